@@ -1,0 +1,508 @@
+"""Plain float64 CPU oracle of the GPTQ layer-quantization pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, header, table
+or constant with the HIP library; it is slow on purpose and written so that
+each step can be read against the pages it follows.
+
+Sources (web pages on the subject; each function cites the passage it follows)
+  [LoRA] "Technical summary: GPTQ-intrinsic LoRA" (gist.science, 2606.01412)
+  [2D]   "GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding" (gist.science,
+         2607.27042), technical summary
+  [Wiki] "GPTQ" encyclopedia entry (wikiprompt.org)
+  [Lat]  "The Lattice Geometry of Neural Network Quantization -- A Short
+         Equivalence Proof of GPTQ and Babai's Algorithm" (gist.science,
+         2508.01077), technical overview
+
+Conventions.  W is stored as a Linear weight, [out, n] (rows = output neurons,
+columns = input dimensions); the pages write XW with W as [n, out].  X is the
+calibration matrix [tokens, n]; bfloat16 inputs arrive as their uint16 bit
+patterns.  H = X^T X is [n, n].
+
+What pins each function (tests/test_oracle_*.py): exact rational Hessians and
+two summation orders; three independent factor routes (Cholesky->inverse->
+Cholesky, reversal, QL of the data matrix [X; mu I]); H = cI reduces to
+round-to-nearest found by brute force over the grid; the exact identities
+W - What = E U and sum(E^2) = tr(D H_lam D^T); blocked == unblocked; GPTQ codes
+== an independently written Babai nearest-plane solver on the QL basis; brute
+force over all 2-bit code vectors for n <= 8; the nearest-plane error bound;
+hand-worked fixtures in tests/golden/; for the LoRA variant the Schur-complement
+and ridge (optimal low-rank compensation) closed forms, r = 0 reduction and
+basis invariance.
+
+Parity unpinned (conventions that only self-consistency fixes; the GPU follows
+them exactly): the min-max grid details of ``grid_fit`` (0 inside the range,
+integer zero point, degenerate range -> s = 1, z = 0), the moment at which a
+group's grid is fitted, and the fp32 precision in which the code and zero-point
+decisions are taken.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import scipy.linalg as sla
+
+F32 = np.float32
+
+
+class NotPositiveDefinite(ValueError):
+    """Raised when the damped Hessian is not positive definite.
+
+    ``info`` follows the library convention: 1 + the index (in H's own
+    numbering) of the first pivot found non-positive when columns are
+    eliminated from n-1 down to 0.
+    """
+
+    def __init__(self, info: int):
+        super().__init__(f"damped Hessian not positive definite (info={info})")
+        self.info = info
+
+
+# --------------------------------------------------------------------------
+# inputs
+# --------------------------------------------------------------------------
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Decode bfloat16 bit patterns (uint16) exactly into float64."""
+    b = np.ascontiguousarray(np.asarray(bits).astype(np.uint16)).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _as_f64(X) -> np.ndarray:
+    X = np.asarray(X)
+    if X.dtype == np.uint16 or X.dtype == np.int16:
+        return bf16_bits_to_f64(X.view(np.uint16))
+    return X.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# a1: calibration Hessian
+# --------------------------------------------------------------------------
+def hessian(X, chunk: int = 2048, H0: np.ndarray | None = None) -> np.ndarray:
+    """H = H0 + sum_t x_t^T x_t, unscaled, in float64, streamed over tokens.
+
+    [Lat] tech. overview section 2 (the output error is a sum over the
+    calibration samples x_1..x_k) and section 3.1 (the Gram matrix X^T X);
+    [2D] section 1 (Gram G = A^T A of the one-sided problem).  bf16 x bf16
+    products are exact in float64.
+    """
+    X = np.asarray(X)
+    tokens, n = X.shape
+    H = np.zeros((n, n)) if H0 is None else np.array(H0, dtype=np.float64, copy=True)
+    for t0 in range(0, tokens, chunk):
+        Xc = _as_f64(X[t0:t0 + chunk])
+        H += Xc.T @ Xc
+    return H
+
+
+# --------------------------------------------------------------------------
+# a2: damping
+# --------------------------------------------------------------------------
+def damp(H: np.ndarray, lam_abs: float = 0.0, lam_rel: float = 0.0):
+    """H_lam = H + lam I with lam = lam_abs + lam_rel * mean(diag H).
+
+    [Lat] section 3.1: stacking mu I under X keeps the lattice basis
+    independent and is the same as the lambda-regularisation X^T X + lam I
+    (lam = mu^2).  Returns (H_lam, lam).
+    """
+    n = H.shape[0]
+    lam = float(lam_abs) + float(lam_rel) * float(np.mean(np.diag(H)))
+    return H + lam * np.eye(n), lam
+
+
+# --------------------------------------------------------------------------
+# a3: upper Cholesky factor of the inverse (three independent routes)
+# --------------------------------------------------------------------------
+def _chol_lower(A: np.ndarray, reversed_order: bool = False) -> np.ndarray:
+    c, info = sla.lapack.dpotrf(np.asarray(A, dtype=np.float64), lower=1, clean=1)
+    if info > 0:
+        n = A.shape[0]
+        # report in H's own numbering, for elimination from n-1 down to 0
+        raise NotPositiveDefinite((n - info + 1) if reversed_order else info)
+    if info < 0:
+        raise ValueError("dpotrf argument error")
+    return c
+
+
+def factor_u(H_lam: np.ndarray) -> np.ndarray:
+    """U upper, positive diagonal, with H_lam^{-1} = U^T U.
+
+    Route: Cholesky of H_lam, triangular inverse, explicit inverse Gram,
+    Cholesky again.  [2D] sections 2 and 4: the feedback factors are the
+    unit-triangular factors of the inverse Gram matrix (its LDL); the unit
+    upper one is diag(U)^{-1} U.
+    """
+    n = H_lam.shape[0]
+    _chol_lower(H_lam[::-1, ::-1], reversed_order=True)  # PD check, library numbering
+    L = _chol_lower(H_lam)
+    Linv = sla.solve_triangular(L, np.eye(n), lower=True)
+    Hinv = Linv.T @ Linv
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    C = _chol_lower(Hinv)
+    return np.triu(C.T)
+
+
+def factor_u_reversal(H_lam: np.ndarray) -> np.ndarray:
+    """Same U by the reversal identity U = P chol(P H_lam P)^{-1} P.
+
+    With P the reversal permutation and C = chol(P H_lam P) lower,
+    H_lam^{-1} = (P C^{-1} P)^T (P C^{-1} P) and P C^{-1} P is upper with a
+    positive diagonal, so it is U (the factor is unique).
+    """
+    n = H_lam.shape[0]
+    C = _chol_lower(H_lam[::-1, ::-1], reversed_order=True)
+    Cinv = sla.solve_triangular(C, np.eye(n), lower=True)
+    return np.triu(Cinv[::-1, ::-1])
+
+
+def ql_lower_from_data(X, mu: float) -> np.ndarray:
+    """Lower L with L^T L = X^T X + mu^2 I, from a QL factorisation of [X; mu I].
+
+    [Lat] section 3.1 (the stacked basis X' = [X; mu I]) and section 3.3
+    (the QL decomposition X = QL links data space and parameter space).
+    QL of X' is the QR of X' with its columns reversed, reversed back.
+    """
+    Xd = _as_f64(X)
+    n = Xd.shape[1]
+    Xs = np.vstack([Xd, mu * np.eye(n)]) if mu else Xd
+    R = np.linalg.qr(Xs[:, ::-1], mode="r")
+    L = R[::-1, ::-1].copy()  # lower triangular
+    sgn = np.sign(np.diag(L))
+    sgn[sgn == 0] = 1.0
+    return np.tril(sgn[:, None] * L)
+
+
+def ql_lower_from_gram(H_lam: np.ndarray) -> np.ndarray:
+    """Lower L with L^T L = H_lam from a QL factorisation of a square root of H_lam."""
+    lam_, V = np.linalg.eigh(H_lam)
+    if np.min(lam_) <= 0:
+        raise NotPositiveDefinite(0)
+    S = np.sqrt(lam_)[:, None] * V.T  # S^T S = H_lam
+    R = np.linalg.qr(S[:, ::-1], mode="r")
+    L = R[::-1, ::-1].copy()
+    sgn = np.sign(np.diag(L))
+    return np.tril(sgn[:, None] * L)
+
+
+# --------------------------------------------------------------------------
+# the asymmetric min-max grid; decisions taken in float32
+# --------------------------------------------------------------------------
+def grid_fit(v: np.ndarray, maxq: int):
+    """Per-row asymmetric min-max grid of 2^b levels over the last axis of v.
+
+    [Wiki] technical approach: weights are split into groups and each group has
+    its own scale.  The grid is lo = min(min v, 0), hi = max(max v, 0),
+    s = (hi - lo)/maxq, r = 1/s, z = rne(-lo * r) in [0, maxq]; a degenerate
+    range (hi == lo) gives s = 1, z = 0.  The zero-point decision is taken in
+    float32 (the library's precision).  Returns float32 arrays (s, r, z, zraw)
+    where zraw is the value that was rounded to z.
+    """
+    v32 = np.asarray(v, dtype=np.float64).astype(F32)
+    lo = np.minimum(v32.min(axis=-1), F32(0))
+    hi = np.maximum(v32.max(axis=-1), F32(0))
+    deg = hi == lo
+    s = np.where(deg, F32(1), (hi - lo) / F32(maxq)).astype(F32)
+    r = (F32(1) / s).astype(F32)
+    zraw = ((-lo * r) + F32(0)).astype(F32)  # + 0 turns -0 into +0
+    z = np.where(deg, F32(0), np.clip(np.rint(zraw), F32(0), F32(maxq))).astype(F32)
+    return s, r, z, zraw
+
+
+def quantize_values(w: np.ndarray, s, r, z, maxq: int):
+    """Round current weights onto the grid (decision in float32).
+
+    x = fl32(fl32(w * r) + z), q = clamp(rne(x), 0, maxq), what = fl32(s (q - z)).
+    Returns (q as float32, what as float64, x).
+    """
+    w32 = np.asarray(w, dtype=np.float64).astype(F32)
+    x = ((w32 * r).astype(F32) + z).astype(F32)
+    q = np.clip(np.rint(x), F32(0), F32(maxq)).astype(F32)
+    what = (s * (q - z)).astype(F32)
+    return q, what.astype(np.float64), x
+
+
+def _near_tie(v, window):
+    f = v.astype(np.float64) - np.floor(v.astype(np.float64))
+    return np.abs(f - 0.5) < window
+
+
+# --------------------------------------------------------------------------
+# a4/a5: the column sweep, unblocked and with lazy block updates
+# --------------------------------------------------------------------------
+def gptq_sweep(W, U, bits: int, group: int = 0, block: int | None = None,
+               n_q: int | None = None, replay: dict | None = None,
+               tie_window: float = 1e-3) -> dict:
+    """GPTQ column sweep of W [out, n_total] against U (H_lam^{-1} = U^T U).
+
+    Each row is independent ([Lat] section 2: the problem splits into one
+    closest-vector problem per neuron).  For each row, for j = 0..n_q-1 in
+    natural order ([2D] section 1: fixed order, error fed forward through a
+    triangular feedback matrix; [Wiki] technical approach: quantise a column,
+    then update the remaining weights to compensate, in closed form):
+      if group and j % group == 0: fit the grid on the current w[j:j+group]
+      q_j = clamp(rne(w_j / s + z)),  what_j = s (q_j - z)
+      E_j = (w_j - what_j) / U_jj,    w[k] -= E_j U_jk for k > j
+    With ``block`` the update of step j only reaches the columns of its own
+    block; after the block, W[:, b1:] -= E[:, b0:b1] U[b0:b1, b1:] ([2D]
+    section 2, GPTQ's lazy block update).  ``block=None`` is the unblocked
+    sweep.  Columns n_q..n_total-1 are never rounded; they only receive
+    updates (the intrinsic-LoRA variant).  group == 0 fits one grid per row on
+    the original row.
+
+    ``replay``: dict(codes=..., zeros=...) from another implementation; at a
+    near-tie (|frac - 0.5| < tie_window of the value being rounded) where it
+    chose the other neighbour, its choice is taken.  Used only by parity tests.
+    """
+    W = np.array(W, dtype=np.float64, copy=True)
+    U = np.asarray(U, dtype=np.float64)
+    out, n_total = W.shape
+    n_q = n_total if n_q is None else int(n_q)
+    maxq = (1 << bits) - 1
+    if group:
+        assert n_q % group == 0, "group must divide the quantised width"
+    B = n_q if block is None else int(block)
+    unblocked = block is None
+    if group and not unblocked:
+        assert group % B == 0 or B % group == 0, "groups must align with blocks"
+    ngroups = n_q // group if group else 1
+    codes = np.zeros((out, n_q), dtype=np.uint8)
+    E = np.zeros((out, n_q))
+    What = np.zeros((out, n_q))
+    scales = np.zeros((out, ngroups), dtype=F32)
+    zeros = np.zeros((out, ngroups), dtype=F32)
+    forced_codes = 0
+    forced_zeros = 0
+    margin = np.full((out, n_q), np.inf)
+
+    def fit(cols, g):
+        nonlocal forced_zeros
+        s, r, z, zraw = grid_fit(cols, maxq)
+        if replay is not None and "zeros" in replay:
+            zr = np.asarray(replay["zeros"])[:, g].astype(F32)
+            lo = np.clip(np.floor(zraw), 0, maxq).astype(F32)
+            hi = np.clip(np.floor(zraw) + 1, 0, maxq).astype(F32)
+            take = _near_tie(zraw, tie_window) & (zr != z) & ((zr == lo) | (zr == hi))
+            forced_zeros += int(take.sum())
+            z = np.where(take, zr, z).astype(F32)
+        scales[:, g] = s
+        zeros[:, g] = z
+        return s, r, z
+
+    if not group:
+        s, r, z = fit(W[:, :n_q], 0)
+    for b0 in range(0, n_q, B):
+        b1 = min(b0 + B, n_q)
+        upd_end = n_total if unblocked else b1
+        for j in range(b0, b1):
+            if group and j % group == 0:
+                s, r, z = fit(W[:, j:j + group], j // group)
+            q, what, x = quantize_values(W[:, j], s, r, z, maxq)
+            margin[:, j] = np.abs((x.astype(np.float64) - np.floor(x.astype(np.float64))) - 0.5)
+            if replay is not None and "codes" in replay:
+                qr = np.asarray(replay["codes"])[:, j].astype(F32)
+                lo = np.clip(np.floor(x), 0, maxq).astype(F32)
+                hi = np.clip(np.floor(x) + 1, 0, maxq).astype(F32)
+                take = _near_tie(x, tie_window) & (qr != q) & ((qr == lo) | (qr == hi))
+                if take.any():
+                    forced_codes += int(take.sum())
+                    q = np.where(take, qr, q).astype(F32)
+                    what = (s * (q - z)).astype(F32).astype(np.float64)
+            codes[:, j] = q.astype(np.uint8)
+            What[:, j] = what
+            e = (W[:, j] - what) / U[j, j]
+            E[:, j] = e
+            W[:, j + 1:upd_end] -= np.outer(e, U[j, j + 1:upd_end])
+        if not unblocked and b1 < n_total:
+            W[:, b1:] -= E[:, b0:b1] @ U[b0:b1, b1:]
+    return dict(codes=codes, scales=scales, zeros=zeros, E=E, What=What,
+                W_final=W, forced_codes=forced_codes, forced_zeros=forced_zeros,
+                margin=margin)
+
+
+def dequantize(codes, scales, zeros, group: int = 0) -> np.ndarray:
+    """What = s (q - z) per group, in float32 arithmetic (as stored)."""
+    codes = np.asarray(codes).astype(F32)
+    out, n = codes.shape
+    g = group if group else n
+    s = np.repeat(np.asarray(scales, dtype=F32), g, axis=1)[:, :n]
+    z = np.repeat(np.asarray(zeros, dtype=F32), g, axis=1)[:, :n]
+    return (s * (codes - z)).astype(F32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# a6: objective
+# --------------------------------------------------------------------------
+def objective(W, What, H) -> float:
+    """J = ||X (W - What)^T||_F^2 = tr(D H D^T), D = W - What.
+
+    [LoRA] problem statement (layer-wise reconstruction error) and [Lat]
+    section 2 (sum over samples of ||W x_j - V x_j||^2).
+    """
+    D = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    return float(np.sum((D @ H) * D))
+
+
+def objective_rows(W, What, H) -> np.ndarray:
+    D = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    return np.sum((D @ H) * D, axis=1)
+
+
+# --------------------------------------------------------------------------
+# the whole pass for one layer
+# --------------------------------------------------------------------------
+def gptq_layer(W, X, bits: int, group: int, block: int, lam_rel: float = 0.01,
+               lam_abs: float = 0.0, H: np.ndarray | None = None) -> dict:
+    """Hessian -> damping -> factor -> blocked sweep -> objective."""
+    if H is None:
+        H = hessian(X)
+    H_lam, lam = damp(H, lam_abs, lam_rel)
+    U = factor_u(H_lam)
+    res = gptq_sweep(W, U, bits, group, block)
+    res.update(H=H, U=U, lam=lam)
+    res["J"] = objective(W, res["What"], H)
+    res["J_lam"] = float(np.sum(res["E"] ** 2))
+    return res
+
+
+# --------------------------------------------------------------------------
+# independent cross-checks
+# --------------------------------------------------------------------------
+def babai(W, L, bits: int, group: int = 0) -> dict:
+    """Box-constrained Babai nearest-plane on the lattice basis L (H_lam = L^T L).
+
+    [Lat] sections 3.2-3.3 and 4: nearest plane with the (lower) QL factor,
+    shown there to take exactly GPTQ's steps.  Coordinate j is rounded at
+    c_j = w_j + L[j, :j] (w - v)[:j] / L_jj; for groups the grid is fitted on
+    the projected targets u = w[j:] + L[j:, j:]^{-1} L[j:, :j] (w - v)[:j].
+    """
+    W = np.asarray(W, dtype=np.float64)
+    L = np.asarray(L, dtype=np.float64)
+    out, n = W.shape
+    maxq = (1 << bits) - 1
+    V = np.zeros((out, n))
+    codes = np.zeros((out, n), dtype=np.uint8)
+    ng = n // group if group else 1
+    scales = np.zeros((out, ng), dtype=F32)
+    zeros = np.zeros((out, ng), dtype=F32)
+    if not group:
+        s, r, z, _ = grid_fit(W, maxq)
+        scales[:, 0], zeros[:, 0] = s, z
+    for j in range(n):
+        D = W[:, :j] - V[:, :j]
+        if group and j % group == 0:
+            rhs = L[j:, :j] @ D.T  # [n-j, out]
+            u = W[:, j:] + sla.solve_triangular(L[j:, j:], rhs, lower=True).T
+            s, r, z, _ = grid_fit(u[:, :group], maxq)
+            scales[:, j // group], zeros[:, j // group] = s, z
+        c = W[:, j] + (D @ L[j, :j]) / L[j, j]
+        q, what, _ = quantize_values(c, s, r, z, maxq)
+        codes[:, j] = q.astype(np.uint8)
+        V[:, j] = what
+    return dict(codes=codes, scales=scales, zeros=zeros, What=V)
+
+
+def brute_force_row(w, H_lam, s: float, z: float, maxq: int):
+    """Exact minimum of (w - what)^T H_lam (w - what) over all code vectors.
+
+    Enumerates every q in {0..maxq}^n (tiny n only) on a fixed grid.
+    Returns (min value, argmin codes).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    n = w.shape[0]
+    Q = np.array(list(itertools.product(range(maxq + 1), repeat=n)), dtype=np.float64)
+    What = (F32(s) * (Q.astype(F32) - F32(z))).astype(F32).astype(np.float64)
+    D = w[None, :] - What
+    vals = np.einsum("ij,jk,ik->i", D, H_lam, D)
+    k = int(np.argmin(vals))
+    return float(vals[k]), Q[k].astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# a7: GPTQ-intrinsic LoRA
+# --------------------------------------------------------------------------
+def top_eigvecs(H: np.ndarray, r: int) -> np.ndarray:
+    """Eigenvectors of the r largest eigenvalues of H (= top right singular
+    vectors of X).  [LoRA] method section 2 (L = V_r)."""
+    lam_, V = np.linalg.eigh(H)
+    idx = np.argsort(lam_)[::-1][:r]
+    return V[:, idx]
+
+
+def augmented_hessian(H: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """H~ = T^T H T with T = [I, V]: the Gram of X~ = [X, X V] without forming X~.
+
+    [LoRA] method section 2 (augmented calibration matrix X~ = [X, XL])."""
+    n = H.shape[0]
+    T = np.hstack([np.eye(n), V])
+    return T.T @ H @ T
+
+
+def factor_u_eig_qr(Ht: np.ndarray, lam: float) -> np.ndarray:
+    """U for the singular augmented Hessian via eigendecomposition and QR.
+
+    [LoRA] method section 2, implementation details: H~ = Q diag(l) Q^T,
+    l clamped at 0, S = diag((l + lam)^{-1/2}) Q^T so S^T S = (H~ + lam I)^{-1};
+    QR of S gives U = R with rows sign-fixed to a positive diagonal.
+    """
+    l, Q = np.linalg.eigh(Ht)
+    l = np.maximum(l, 0.0)
+    S = (1.0 / np.sqrt(l + lam))[:, None] * Q.T
+    R = np.linalg.qr(S, mode="r")
+    sgn = np.sign(np.diag(R))
+    sgn[sgn == 0] = 1.0
+    return np.triu(sgn[:, None] * R)
+
+
+def lora(W, H, r: int, bits: int, group: int = 0, block: int | None = 128,
+         lam_rel: float = 1e-4, lam_abs: float = 0.0, V: np.ndarray | None = None,
+         replay: dict | None = None) -> dict:
+    """GPTQ-intrinsic LoRA: sweep W~ = [W, 0] on the augmented Hessian.
+
+    [LoRA] method section 2: the first n columns are rounded into Q, the r
+    appended columns start at zero and absorb the error, giving R.  lam is
+    relative to the plain H.  Returns codes/scales/zeros, L = V_r [n, r],
+    R [r, out] (pages' convention W^T ~ Q + L R), R_out = R^T, the objective
+    J = ||X (W - What - R_out V^T)^T||^2 and J_lam = sum(E^2).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    out, n = W.shape
+    lam = float(lam_abs) + float(lam_rel) * float(np.mean(np.diag(H)))
+    if V is None:
+        V = top_eigvecs(H, r)
+    if r == 0:
+        V = np.zeros((n, 0))
+    Ht = augmented_hessian(H, V)
+    U = factor_u_eig_qr(Ht, lam)
+    Wt = np.hstack([W, np.zeros((out, r))])
+    res = gptq_sweep(Wt, U, bits, group, block, n_q=n, replay=replay)
+    Rout = res["W_final"][:, n:]
+    D = W - res["What"] - Rout @ V.T
+    res.update(L=V, R=Rout.T.copy(), R_out=Rout, U=U, lam=lam, H_aug=Ht)
+    res["J"] = float(np.sum((D @ H) * D))
+    res["J_lam"] = float(np.sum(res["E"] ** 2))
+    return res
+
+
+def lora_schur(W, H, V, lam: float, bits: int, group: int = 0, block: int | None = 128):
+    """Closed forms the LoRA sweep must reproduce.
+
+    Eliminating the r free columns leaves the Schur complement
+    S = H_lam - H V (V^T H V + lam I)^{-1} V^T H for the rounded columns, and
+    for a fixed Q the optimal compensation is the ridge solution
+    R_out^T = (V^T H V + lam I)^{-1} V^T H (W - What)^T ([LoRA] section 4:
+    OLrC optimises L, R for a fixed Q).
+    """
+    n = H.shape[0]
+    r = V.shape[1]
+    H_lam = H + lam * np.eye(n)
+    HV = H @ V
+    K = V.T @ HV + lam * np.eye(r)
+    S = H_lam - HV @ np.linalg.solve(K, HV.T)
+    S = 0.5 * (S + S.T)
+    U = factor_u(S)
+    res = gptq_sweep(W, U, bits, group, block)
+    D1 = np.asarray(W, dtype=np.float64) - res["What"]
+    Rt = np.linalg.solve(K, HV.T @ D1.T)
+    res.update(R_out=Rt.T, S=S, U=U)
+    return res
