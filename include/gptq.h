@@ -1,0 +1,170 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer-quantization library.
+ *
+ * The library computes, for one linear layer with weight W [out, n] (stored as
+ * a Linear weight: rows = output neurons, columns = input dimensions) and a
+ * calibration matrix X [tokens, n], integer codes Q, per-group scales and zero
+ * points minimising the layer-wise reconstruction error ||X (W - What)^T||_F^2
+ * (GPTQ-intrinsic LoRA technical summary, "problem statement"; Lattice Geometry
+ * of NN Quantization, technical overview section 2, where the problem splits
+ * into one closest-vector problem per output row).
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every
+ *     input and output buffer; the library never frees or keeps them.
+ *   - Row-major throughout.  X holds bfloat16 values as their uint16 bit
+ *     patterns.  Matrices of size [rows, cols] have leading dimension cols
+ *     unless an ld argument is given.
+ *   - A context owns its device workspace (grown on demand, kept until
+ *     gptq_destroy) and the HIP stream it was created with.  Calls are
+ *     asynchronous on that stream except those marked SYNC, which wait for the
+ *     stream before returning.  A context is not thread-safe: one context per
+ *     host thread/stream.
+ *   - Every call returns a gptq_status.  Argument errors are detected on the
+ *     host before anything is launched.  After GPTQ_ERR_HIP the HIP error text
+ *     is available from gptq_last_error().
+ *   - Results are deterministic: repeated calls on the same inputs give the
+ *     same bytes (no floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad bits/group/block */
+  GPTQ_ERR_NOT_PD = 2,      /* damped Hessian not positive definite (see info) */
+  GPTQ_ERR_NONFINITE = 3,   /* non-finite entry in H */
+  GPTQ_ERR_UNSUPPORTED = 4, /* valid but unsupported shape or alignment */
+  GPTQ_ERR_HIP = 5,         /* HIP runtime error (text in gptq_last_error) */
+  GPTQ_ERR_NO_MEMORY = 6    /* workspace allocation failed */
+} gptq_status;
+
+typedef struct gptq_ctx_s* gptq_ctx;
+
+/* Create a context on HIP device `device`, issuing work on `stream` (a
+ * hipStream_t; NULL = the device's null stream).  *ctx [host] receives the
+ * handle.  Allocates only host memory; device workspace is allocated by the
+ * first call that needs it. */
+int gptq_create(gptq_ctx* ctx, int device, void* stream);
+
+/* Wait for the context's stream, free its workspace and the context. */
+int gptq_destroy(gptq_ctx ctx);
+
+/* Static text for a status code. */
+const char* gptq_strerror(int status);
+
+/* Text of the last error recorded in ctx (empty string if none). */
+const char* gptq_last_error(gptq_ctx ctx);
+
+/* Calibration Hessian (GPTQ-2D technical summary section 1, Gram G = A^T A;
+ * Lattice Geometry section 3.1, X^T X):
+ *   H[n][n] (fp32, full symmetric) = (accumulate ? H : 0) + X^T X
+ * X[tokens][ldx] bf16 bit patterns; only the first n columns are read.
+ * The sum is unscaled.  bf16 products are exact in fp32; accumulation is fp32
+ * in a fixed order (split over tokens, partials summed in a fixed order), and
+ * H is exactly symmetric.  Requires ldx % 8 == 0, ldx >= n, X 16-byte aligned
+ * (else GPTQ_ERR_UNSUPPORTED).  tokens == 0 leaves H (accumulate) or zeroes it.
+ * Asynchronous. */
+int gptq_hessian(gptq_ctx ctx, const uint16_t* X, int64_t tokens, int32_t n, int64_t ldx,
+                 float* H, int accumulate);
+
+/* Damping and factor (Lattice Geometry section 3.1: X^T X + lam I; GPTQ-2D
+ * sections 2 and 4: the feedback factors are the unit-triangular factors of
+ * the inverse Gram matrix):
+ *   lam = lam_abs + lam_rel * mean(diag H)
+ *   U[n][n] fp32, upper triangular with positive diagonal, zero below it, with
+ *   (H + lam I)^{-1} = U^T U.
+ * Computed in fp64 by Cholesky of the index-reversed damped matrix and a
+ * triangular inverse (U = P chol(P H_lam P)^{-1} P, P the reversal), so pivots
+ * are eliminated from column n-1 down to 0.
+ * SYNC.  *info [host] = 0 on success, else 1 + the column (in H's numbering)
+ * of the first non-positive pivot met in that order, and GPTQ_ERR_NOT_PD is
+ * returned (U is then undefined).  *lam_used [host] (may be NULL) = lam.
+ * H is not modified.  Non-finite H -> GPTQ_ERR_NONFINITE. */
+int gptq_factor(gptq_ctx ctx, const float* H, int32_t n, double lam_abs, double lam_rel,
+                float* U, int32_t* info, double* lam_used);
+
+/* Blocked column sweep (GPTQ encyclopedia entry, technical approach: quantise
+ * a column, update the remaining weights in closed form, groups with their own
+ * scale; GPTQ-2D sections 1-2: fixed order, triangular feedback, GPTQ's lazy
+ * block update).  For every row, columns j = 0..n-1 in natural order:
+ *   at a group start (or once per row when group == 0, on the original row)
+ *     fit lo = min(min v, 0), hi = max(max v, 0), s = (hi-lo)/maxq (s = 1 if
+ *     hi == lo), r = 1/s, z = rne(-lo*r) on the current weights v of the group;
+ *   x = fl32(fl32(w_j*r) + z), q = clamp(rne(x), 0, maxq), what = s (q - z),
+ *   E_j = (w_j - what)/U_jj, and w_k -= E_j U_jk for k > j
+ * with the in-block part done per column and the rest, after each block of
+ * `block` columns, as W[:, b1:] -= E[:, b0:b1] U[b0:b1, b1:].
+ * Inputs: W[out][n] fp32 (not modified), U[n][n] from gptq_factor, lam (the
+ * damping used for U, for the objective).  Outputs: codes[out][n] uint8 in
+ * [0, 2^bits-1]; scales[out][ng] fp32 and zeros[out][ng] uint8 with
+ * ng = group ? n/group : 1; err[out][n] fp32 the scaled errors E (may be NULL);
+ * obj[2] [host] = {J, J_lam}: J_lam = sum E^2 = tr(D (H+lam I) D^T) and
+ * J = J_lam - lam ||D||^2 = ||X D^T||^2 with D = W - What.
+ * Requirements: 2 <= bits <= 8; group == 0 or (group % 8 == 0, n % group == 0,
+ * and group % block == 0 or block % group == 0); block in {16,32,64,128,256}.
+ * SYNC (objective read back). */
+int gptq_quantize(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const float* U,
+                  int32_t bits, int32_t group, int32_t block, double lam,
+                  uint8_t* codes, float* scales, uint8_t* zeros, float* err, double* obj);
+
+/* GPTQ-intrinsic LoRA (GPTQ-intrinsic LoRA technical summary, method section 2):
+ * X~ = [X, X V_r] with V_r the top-r eigenvectors of H = X^T X; the sweep runs
+ * on W~ = [W, 0] against the factor of X~^T X~ + lam I (lam = lam_abs +
+ * lam_rel * mean(diag H)), rounding only the first n columns; the r appended
+ * columns absorb the error.  Outputs codes/scales/zeros as gptq_quantize (W^T
+ * ~ Q + L R in the pages' convention, i.e. W ~ What + R^T L^T):
+ *   L[n][r] fp32: an orthonormal basis of the top-r eigenspace of H (found by
+ *                 subspace iteration in fp64; any basis gives the same Q and
+ *                 the same product L R);
+ *   R[r][out] fp32;
+ *   obj[2] [host] = {J, J_lam}, J = ||X (W - What - R^T L^T)^T||^2.
+ * X as gptq_hessian; 1 <= r <= 256; requirements on bits/group/block as
+ * gptq_quantize.  SYNC.  *info semantics as gptq_factor (may be NULL). */
+int gptq_lora(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const uint16_t* X,
+              int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,
+              int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
+              uint8_t* zeros, float* L, float* R, double* obj, int32_t* info);
+
+/* One layer of a batch.  X may be NULL: then H must already hold the layer's
+ * Hessian (several layers may point at the same H and X == NULL to share it).
+ * H and U are caller-provided [n][n] fp32 buffers (H is written when X != NULL).
+ * obj and info are outputs written by the call. */
+typedef struct {
+  const uint16_t* X;
+  int64_t tokens;
+  int64_t ldx;
+  const float* W;
+  int32_t out, n;
+  int32_t bits, group, block;
+  int32_t pad0;
+  double lam_abs, lam_rel;
+  float* H;
+  float* U;
+  uint8_t* codes;
+  float* scales;
+  uint8_t* zeros;
+  float* err;      /* may be NULL */
+  double obj[2];   /* out: {J, J_lam} */
+  int32_t info;    /* out: as gptq_factor */
+  int32_t pad1;
+} gptq_layer;
+
+/* Quantise many independent layers at once (Hessians, factors, sweeps and
+ * trailing updates each run as one grouped launch over all layers per step).
+ * layers [host] array of nlayers descriptors; results equal those of calling
+ * gptq_hessian, gptq_factor and gptq_quantize per layer.  SYNC.  Returns the
+ * first error met; per-layer info/obj are filled in for every layer. */
+int gptq_quantize_batched(gptq_ctx ctx, int32_t nlayers, gptq_layer* layers);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

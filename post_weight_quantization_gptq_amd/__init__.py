@@ -1,0 +1,294 @@
+"""MI355X-native GPTQ layer quantization.
+
+A thin Python binding (ctypes) over ``libgptq_mi355x.so``, the HIP/C library
+declared in ``include/gptq.h``.  This module only marshals arguments: it checks
+shapes and dtypes, allocates output tensors with torch (device memory) and
+passes raw pointers and the current HIP stream to the library, where every step
+of the pass runs.  There is no fallback: if the library is missing, every entry
+point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GPTQError",
+    "Context",
+    "library_path",
+    "load_library",
+    "exported_symbols",
+    "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBNAME = "libgptq_mi355x.so"
+_lib = None
+
+STATUS = {
+    0: "GPTQ_OK",
+    1: "GPTQ_ERR_INVALID_ARG",
+    2: "GPTQ_ERR_NOT_PD",
+    3: "GPTQ_ERR_NONFINITE",
+    4: "GPTQ_ERR_UNSUPPORTED",
+    5: "GPTQ_ERR_HIP",
+    6: "GPTQ_ERR_NO_MEMORY",
+}
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), msg))
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIBNAME)
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p),
+        ("tokens", ctypes.c_int64),
+        ("ldx", ctypes.c_int64),
+        ("W", ctypes.c_void_p),
+        ("out", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("pad0", ctypes.c_int32),
+        ("lam_abs", ctypes.c_double),
+        ("lam_rel", ctypes.c_double),
+        ("H", ctypes.c_void_p),
+        ("U", ctypes.c_void_p),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("zeros", ctypes.c_void_p),
+        ("err", ctypes.c_void_p),
+        ("obj", ctypes.c_double * 2),
+        ("info", ctypes.c_int32),
+        ("pad1", ctypes.c_int32),
+    ]
+
+
+def load_library(path: str | None = None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise RuntimeError(
+            "%s is not built; run `python -m post_weight_quantization_gptq_amd.build_lib`" % p)
+    L = ctypes.CDLL(p)
+    vp, i32, i64, d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    L.gptq_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp]
+    L.gptq_destroy.argtypes = [vp]
+    L.gptq_strerror.argtypes = [ctypes.c_int]
+    L.gptq_strerror.restype = ctypes.c_char_p
+    L.gptq_last_error.argtypes = [vp]
+    L.gptq_last_error.restype = ctypes.c_char_p
+    L.gptq_hessian.argtypes = [vp, vp, i64, i32, i64, vp, ctypes.c_int]
+    L.gptq_factor.argtypes = [vp, vp, i32, d, d, vp, ctypes.POINTER(i32), ctypes.POINTER(d)]
+    L.gptq_quantize.argtypes = [vp, vp, i32, i32, vp, i32, i32, i32, d, vp, vp, vp, vp,
+                                ctypes.POINTER(d)]
+    L.gptq_lora.argtypes = [vp, vp, i32, i32, vp, i64, i64, i32, i32, i32, i32, d, d,
+                            vp, vp, vp, vp, vp, ctypes.POINTER(d), ctypes.POINTER(i32)]
+    L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
+    for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
+                 "gptq_lora", "gptq_quantize_batched"):
+        getattr(L, name).restype = ctypes.c_int
+    if path is None:
+        _lib = L
+    return L
+
+
+def exported_symbols(header: str | None = None):
+    """Function names declared in include/gptq.h."""
+    import re
+    header = header or os.path.join(os.path.dirname(_HERE), "include", "gptq.h")
+    txt = open(header).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gptq_[a-z_]+)\s*\(", txt)))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+class Context:
+    """A library context bound to a device and to the current torch stream."""
+
+    def __init__(self, device=None):
+        import torch
+        self.torch = torch
+        self.lib = load_library()
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        if dev.type != "cuda":
+            raise ValueError("the GPTQ library needs a GPU device")
+        self.device = torch.device("cuda", dev.index if dev.index is not None else torch.cuda.current_device())
+        self.stream = torch.cuda.current_stream(self.device)
+        h = ctypes.c_void_p()
+        self._check(self.lib.gptq_create(ctypes.byref(h), self.device.index, ctypes.c_void_p(self.stream.cuda_stream)),
+                    ctx=None)
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.gptq_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    # ------------------------------------------------------------------ util
+    def _check(self, rc, ctx="self"):
+        if rc != 0:
+            msg = ""
+            if ctx is not None and getattr(self, "handle", None):
+                msg = (self.lib.gptq_last_error(self.handle) or b"").decode()
+            if not msg:
+                msg = self.lib.gptq_strerror(rc).decode()
+            raise GPTQError(rc, msg)
+
+    def _dev(self, t, dtype, name):
+        torch = self.torch
+        if t.device != self.device:
+            raise ValueError("%s must be on %s" % (name, self.device))
+        if t.dtype != dtype:
+            raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        return t
+
+    def _xbits(self, X):
+        torch = self.torch
+        if X.dtype == torch.bfloat16:
+            X = X.view(torch.int16)
+        if X.dtype not in (torch.int16, torch.uint16):
+            raise TypeError("X must be bfloat16 (or its int16 bit patterns)")
+        if X.dim() != 2 or X.stride(1) != 1:
+            raise ValueError("X must be a row-major [tokens, ldx] matrix")
+        if X.device != self.device:
+            raise ValueError("X must be on %s" % self.device)
+        return X
+
+    # ----------------------------------------------------------- entry points
+    def hessian(self, X, n: int | None = None, H=None, accumulate: bool = False):
+        """H = (accumulate ? H : 0) + X^T X (fp32 [n, n])."""
+        torch = self.torch
+        X = self._xbits(X)
+        tokens, ldx = X.shape[0], X.stride(0)
+        n = X.shape[1] if n is None else int(n)
+        if H is None:
+            H = torch.empty((n, n), dtype=torch.float32, device=self.device)
+        self._dev(H, torch.float32, "H")
+        self._check(self.lib.gptq_hessian(self.handle, _ptr(X), tokens, n, ldx, _ptr(H), int(bool(accumulate))))
+        return H
+
+    def factor(self, H, lam_abs: float = 0.0, lam_rel: float = 0.01, U=None):
+        """U upper with (H + lam I)^{-1} = U^T U.  Returns (U, info, lam); raises on failure."""
+        torch = self.torch
+        self._dev(H, torch.float32, "H")
+        n = H.shape[0]
+        if U is None:
+            U = torch.empty((n, n), dtype=torch.float32, device=self.device)
+        info = ctypes.c_int32(0)
+        lam = ctypes.c_double(0.0)
+        rc = self.lib.gptq_factor(self.handle, _ptr(H), n, float(lam_abs), float(lam_rel), _ptr(U),
+                                  ctypes.byref(info), ctypes.byref(lam))
+        if rc == 2:
+            err = GPTQError(rc, (self.lib.gptq_last_error(self.handle) or b"").decode())
+            err.info = info.value
+            raise err
+        self._check(rc)
+        return U, info.value, lam.value
+
+    def quantize(self, W, U, bits: int, group: int, block: int, lam: float, want_err: bool = False,
+                 out=None):
+        """Blocked GPTQ sweep.  Returns dict(codes, scales, zeros, err, J, J_lam)."""
+        torch = self.torch
+        self._dev(W, torch.float32, "W")
+        self._dev(U, torch.float32, "U")
+        o, n = W.shape
+        ng = n // group if group else 1
+        if out is None:
+            out = dict(codes=torch.empty((o, n), dtype=torch.uint8, device=self.device),
+                       scales=torch.empty((o, ng), dtype=torch.float32, device=self.device),
+                       zeros=torch.empty((o, ng), dtype=torch.uint8, device=self.device),
+                       err=torch.empty((o, n), dtype=torch.float32, device=self.device) if want_err else None)
+        obj = (ctypes.c_double * 2)()
+        self._check(self.lib.gptq_quantize(self.handle, _ptr(W), o, n, _ptr(U), int(bits), int(group), int(block),
+                                           float(lam), _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["zeros"]),
+                                           _ptr(out.get("err")), obj))
+        res = dict(out)
+        res["J"], res["J_lam"] = obj[0], obj[1]
+        return res
+
+    def lora(self, W, X, r: int, bits: int, group: int, block: int, lam_abs: float = 0.0,
+             lam_rel: float = 1e-4):
+        """GPTQ-intrinsic LoRA.  Returns dict(codes, scales, zeros, L [n, r], R [r, out], J, J_lam)."""
+        torch = self.torch
+        self._dev(W, torch.float32, "W")
+        X = self._xbits(X)
+        o, n = W.shape
+        ng = n // group if group else 1
+        res = dict(codes=torch.empty((o, n), dtype=torch.uint8, device=self.device),
+                   scales=torch.empty((o, ng), dtype=torch.float32, device=self.device),
+                   zeros=torch.empty((o, ng), dtype=torch.uint8, device=self.device),
+                   L=torch.empty((n, r), dtype=torch.float32, device=self.device),
+                   R=torch.empty((r, o), dtype=torch.float32, device=self.device))
+        obj = (ctypes.c_double * 2)()
+        info = ctypes.c_int32(0)
+        self._check(self.lib.gptq_lora(self.handle, _ptr(W), o, n, _ptr(X), X.shape[0], X.stride(0), int(r),
+                                       int(bits), int(group), int(block), float(lam_abs), float(lam_rel),
+                                       _ptr(res["codes"]), _ptr(res["scales"]), _ptr(res["zeros"]),
+                                       _ptr(res["L"]), _ptr(res["R"]), obj, ctypes.byref(info)))
+        res["J"], res["J_lam"], res["info"] = obj[0], obj[1], info.value
+        return res
+
+    def quantize_batched(self, layers):
+        """layers: list of dicts with W, bits, group, block, lam_rel (and X or H, optional lam_abs, err).
+        Fills H/U/codes/scales/zeros per layer (allocating what is missing); returns the list."""
+        torch = self.torch
+        arr = (_Layer * len(layers))()
+        keep = []
+        for i, ly in enumerate(layers):
+            W = self._dev(ly["W"], torch.float32, "W")
+            o, n = W.shape
+            g = int(ly["group"])
+            ng = n // g if g else 1
+            ly.setdefault("H", torch.empty((n, n), dtype=torch.float32, device=self.device))
+            ly.setdefault("U", torch.empty((n, n), dtype=torch.float32, device=self.device))
+            ly.setdefault("codes", torch.empty((o, n), dtype=torch.uint8, device=self.device))
+            ly.setdefault("scales", torch.empty((o, ng), dtype=torch.float32, device=self.device))
+            ly.setdefault("zeros", torch.empty((o, ng), dtype=torch.uint8, device=self.device))
+            X = ly.get("X")
+            if X is not None:
+                X = self._xbits(X)
+            a = arr[i]
+            a.X = X.data_ptr() if X is not None else None
+            a.tokens = X.shape[0] if X is not None else 0
+            a.ldx = X.stride(0) if X is not None else n
+            a.W, a.out, a.n = W.data_ptr(), o, n
+            a.bits, a.group, a.block = int(ly["bits"]), g, int(ly["block"])
+            a.lam_abs, a.lam_rel = float(ly.get("lam_abs", 0.0)), float(ly.get("lam_rel", 0.01))
+            a.H, a.U = ly["H"].data_ptr(), ly["U"].data_ptr()
+            a.codes, a.scales, a.zeros = ly["codes"].data_ptr(), ly["scales"].data_ptr(), ly["zeros"].data_ptr()
+            a.err = ly["err"].data_ptr() if ly.get("err") is not None else None
+            keep.append(X)
+        rc = self.lib.gptq_quantize_batched(self.handle, len(layers), arr)
+        for i, ly in enumerate(layers):
+            ly["J"], ly["J_lam"], ly["info"] = arr[i].obj[0], arr[i].obj[1], arr[i].info
+        self._check(rc)
+        return layers

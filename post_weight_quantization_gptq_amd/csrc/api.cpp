@@ -1,0 +1,792 @@
+// C ABI of the GPTQ library: argument checks, the launch planner and the
+// context's workspace.  The planner turns the shapes of a call into per-launch
+// task tables (packed in one buffer, uploaded with one copy per call) and then
+// issues every kernel on the context's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gptq.h"
+#include "common.h"
+#include "launch.h"
+#include "plan.h"
+
+#define GPTQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+struct DevBuf {
+  void* p = nullptr;
+  size_t cap = 0;
+};
+
+}  // namespace
+
+struct gptq_ctx_s {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  int ncu = 256;
+  int nxcd = 8;
+  std::string err;
+  DevBuf partials, facA, facY, facT, work, eblk, objp, slots, blob, lora;
+  void* hblob = nullptr;  // pinned staging for the task tables
+  size_t hblob_cap = 0;
+  void* hsmall = nullptr;  // pinned read-back area
+  size_t hsmall_cap = 0;
+  hipEvent_t blob_ev = nullptr;
+  bool blob_pending = false;
+};
+
+namespace {
+
+int set_err(gptq_ctx c, int status, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    c->err = buf;
+  }
+  return status;
+}
+
+#define HIPCHK(c, expr)                                                                       \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess)                                                                     \
+      return set_err((c), GPTQ_ERR_HIP, "%s: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, \
+                     __LINE__);                                                               \
+  } while (0)
+
+int ensure(gptq_ctx c, DevBuf& b, size_t bytes) {
+  if (bytes == 0) bytes = 256;
+  if (b.cap >= bytes) return GPTQ_OK;
+  if (b.p) {
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    HIPCHK(c, hipFree(b.p));
+    b.p = nullptr;
+    b.cap = 0;
+  }
+  const size_t want = (bytes + (2u << 20) - 1) & ~((size_t)(2u << 20) - 1);
+  if (hipMalloc(&b.p, want) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(c, GPTQ_ERR_NO_MEMORY, "device allocation of %zu bytes failed", want);
+  }
+  b.cap = want;
+  return GPTQ_OK;
+}
+
+int ensure_pinned(gptq_ctx c, void*& p, size_t& cap, size_t bytes) {
+  if (cap >= bytes) return GPTQ_OK;
+  if (p) {
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    HIPCHK(c, hipHostFree(p));
+    p = nullptr;
+    cap = 0;
+  }
+  const size_t want = std::max<size_t>(bytes, 1 << 16);
+  if (hipHostMalloc(&p, want, hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(c, GPTQ_ERR_NO_MEMORY, "pinned allocation of %zu bytes failed", want);
+  }
+  cap = want;
+  return GPTQ_OK;
+}
+
+// Packed task tables of one call.
+struct Blob {
+  std::vector<uint8_t> h;
+  template <class T>
+  size_t add(const T* p, size_t n) {
+    size_t off = (h.size() + 63) & ~(size_t)63;
+    h.resize(off + sizeof(T) * std::max<size_t>(n, 1));
+    if (n) memcpy(h.data() + off, p, sizeof(T) * n);
+    return off;
+  }
+  template <class T>
+  size_t add(const std::vector<T>& v) {
+    return add(v.data(), v.size());
+  }
+};
+
+// Upload a blob; returns the device base pointer in *dbase.
+int upload(gptq_ctx c, const Blob& b, uint8_t** dbase) {
+  const size_t bytes = b.h.size();
+  int rc = ensure(c, c->blob, bytes);
+  if (rc) return rc;
+  if (c->blob_pending) {
+    HIPCHK(c, hipEventSynchronize(c->blob_ev));
+    c->blob_pending = false;
+  }
+  rc = ensure_pinned(c, c->hblob, c->hblob_cap, bytes);
+  if (rc) return rc;
+  memcpy(c->hblob, b.h.data(), bytes);
+  HIPCHK(c, hipMemcpyAsync(c->blob.p, c->hblob, bytes, hipMemcpyHostToDevice, c->stream));
+  HIPCHK(c, hipEventRecord(c->blob_ev, c->stream));
+  c->blob_pending = true;
+  *dbase = (uint8_t*)c->blob.p;
+  return GPTQ_OK;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int d) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != d) (void)hipSetDevice(d);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// ------------------------------------------------------------ Hessian plan --
+struct HessJob {
+  const uint16_t* X;
+  long long tokens, ldx;
+  int n;
+  float* H;
+  int accumulate;
+};
+
+struct HessPlan {
+  std::vector<SyrkProb> probs;
+  std::vector<SyrkTask> tasks;
+  std::vector<RedProb> rprobs;
+  std::vector<RedTask> rtasks;
+  std::vector<int> partlist;
+  int nparts = 0;
+};
+
+// Split every (problem, upper tile) over token slices so that each XCD works
+// on its own slice, then even out the last, partly filled round of each XCD
+// by cutting its items into shorter token ranges.
+void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, HessPlan& P) {
+  struct Item {
+    int prob, ti, tj, k0, k1;
+  };
+  std::vector<std::vector<Item>> lists(nxcd);
+  std::vector<int> ntile_of(jobs.size());
+  for (size_t p = 0; p < jobs.size(); ++p) {
+    const HessJob& J = jobs[p];
+    P.probs.push_back(SyrkProb{J.X, J.ldx, J.n, (int)J.tokens});
+    P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate});
+    const int nt = cdiv(J.n, 256);
+    ntile_of[p] = nt;
+    if (J.tokens <= 0 || J.n <= 0) continue;
+    const long long chunks = cdiv(J.tokens, 64);
+    const int nsl = (int)std::max<long long>(1, std::min<long long>(nxcd, chunks / 32));
+    int tix = 0;
+    for (int ti = 0; ti < nt; ++ti)
+      for (int tj = ti; tj < nt; ++tj, ++tix)
+        for (int s = 0; s < nsl; ++s) {
+          const long long c0 = chunks * s / nsl, c1 = chunks * (s + 1) / nsl;
+          const int k0 = (int)(c0 * 64), k1 = (int)std::min<long long>(c1 * 64, J.tokens);
+          if (k1 <= k0) continue;
+          const int x = (nsl == nxcd) ? s : (tix + s) % nxcd;
+          lists[x].push_back(Item{(int)p, ti, tj, k0, k1});
+        }
+  }
+  // balance each XCD's last round
+  for (auto& L : lists) {
+    const int M = (int)L.size();
+    if (M == 0) continue;
+    const int rem = M % cus_per_xcd;
+    if (rem == 0) continue;
+    const int first = (M >= cus_per_xcd) ? M - rem : 0;
+    const int cnt = M - first;
+    const int f = std::max(1, cus_per_xcd / cnt);
+    if (f <= 1) continue;
+    std::vector<Item> out(L.begin(), L.begin() + first);
+    for (int i = first; i < M; ++i) {
+      const Item it = L[i];
+      const int ch = cdiv(it.k1 - it.k0, 64);
+      const int pieces = std::min(f, ch);
+      for (int q = 0; q < pieces; ++q) {
+        const int a = it.k0 + (int)((long long)ch * q / pieces) * 64;
+        const int b = std::min(it.k1, it.k0 + (int)((long long)ch * (q + 1) / pieces) * 64);
+        if (b > a) out.push_back(Item{it.prob, it.ti, it.tj, a, b});
+      }
+    }
+    L.swap(out);
+  }
+  size_t maxlen = 0;
+  for (auto& L : lists) maxlen = std::max(maxlen, L.size());
+  P.tasks.assign(maxlen * nxcd, SyrkTask{0, 0, 0, 0, 0, -1, 0, 0});
+  // partial slots; remember each tile's parts in (k0) order
+  struct PartRef {
+    int prob, ti, tj, k0, part;
+  };
+  std::vector<PartRef> refs;
+  int part = 0;
+  for (size_t slot = 0; slot < maxlen; ++slot)
+    for (int x = 0; x < nxcd; ++x) {
+      if (slot >= lists[x].size()) continue;
+      const Item& it = lists[x][slot];
+      P.tasks[slot * nxcd + x] = SyrkTask{it.prob, it.ti, it.tj, it.k0, it.k1, part, 0, 0};
+      refs.push_back(PartRef{it.prob, it.ti, it.tj, it.k0, part});
+      ++part;
+    }
+  P.nparts = part;
+  std::sort(refs.begin(), refs.end(), [](const PartRef& a, const PartRef& b) {
+    if (a.prob != b.prob) return a.prob < b.prob;
+    if (a.ti != b.ti) return a.ti < b.ti;
+    if (a.tj != b.tj) return a.tj < b.tj;
+    return a.k0 < b.k0;
+  });
+  size_t r = 0;
+  for (size_t p = 0; p < jobs.size(); ++p) {
+    const int n = jobs[p].n, nt = ntile_of[p];
+    for (int ti = 0; ti < nt; ++ti)
+      for (int tj = ti; tj < nt; ++tj) {
+        const int part0 = (int)P.partlist.size();
+        while (r < refs.size() && refs[r].prob == (int)p && refs[r].ti == ti && refs[r].tj == tj)
+          P.partlist.push_back(refs[r++].part);
+        const int np = (int)P.partlist.size() - part0;
+        for (int a = 0; a < 4; ++a)
+          for (int b = 0; b < 4; ++b) {
+            if (ti == tj && a > b) continue;
+            const int r0 = ti * 256 + 64 * a, c0 = tj * 256 + 64 * b;
+            if (r0 >= n || c0 >= n) continue;
+            P.rtasks.push_back(RedTask{(int)p, r0, c0, part0, np, 0, 0, 0});
+          }
+      }
+  }
+}
+
+int run_hessian(gptq_ctx c, const std::vector<HessJob>& jobs) {
+  HessPlan P;
+  plan_hessian(jobs, c->nxcd, std::max(1, c->ncu / c->nxcd), P);
+  int rc = ensure(c, c->partials, (size_t)std::max(P.nparts, 1) * 65536 * sizeof(float));
+  if (rc) return rc;
+  Blob b;
+  const size_t o_probs = b.add(P.probs), o_tasks = b.add(P.tasks), o_rprobs = b.add(P.rprobs),
+               o_rtasks = b.add(P.rtasks), o_plist = b.add(P.partlist);
+  uint8_t* d = nullptr;
+  rc = upload(c, b, &d);
+  if (rc) return rc;
+  HIPCHK(c, launch_syrk((const SyrkProb*)(d + o_probs), (const SyrkTask*)(d + o_tasks),
+                        (int)P.tasks.size(), (float*)c->partials.p, c->stream));
+  HIPCHK(c, launch_syrk_reduce((const RedProb*)(d + o_rprobs), (const RedTask*)(d + o_rtasks),
+                               (int)P.rtasks.size(), (const int*)(d + o_plist),
+                               (const float*)c->partials.p, c->stream));
+  return GPTQ_OK;
+}
+
+// ------------------------------------------------------------- factor plan --
+struct FacJob {
+  const float* H;  // null: A (and lam) prepared by an earlier kernel
+  int n, ldh, ldu;
+  double lam_abs, lam_rel;
+  float* U;
+};
+
+size_t inv_scratch_doubles(int n) {
+  size_t best = 64 * 64;
+  for (int s = 64; s < n; s *= 2) {
+    const int npairs = cdiv(n - s, 2LL * s);
+    best = std::max(best, (size_t)npairs * s * s);
+  }
+  return best;
+}
+
+// Enqueue the factor of every job.  A/Y/T offsets (in doubles) into facA/facY/facT.
+int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool assembled_A = false,
+               double** A_out = nullptr) {
+  const int np = (int)jobs.size();
+  std::vector<size_t> oA(np), oT(np);
+  size_t totA = 0, totT = 0;
+  for (int p = 0; p < np; ++p) {
+    oA[p] = totA;
+    totA += (size_t)jobs[p].n * jobs[p].n;
+    oT[p] = totT;
+    totT += inv_scratch_doubles(jobs[p].n);
+  }
+  int rc;
+  if (!assembled_A) {
+    rc = ensure(c, c->facA, totA * sizeof(double));
+    if (rc) return rc;
+  }
+  if ((rc = ensure(c, c->facY, totA * sizeof(double)))) return rc;
+  if ((rc = ensure(c, c->facT, totT * sizeof(double)))) return rc;
+  std::vector<FacProb> probs(np);
+  int maxnb = 0, maxn = 0;
+  for (int p = 0; p < np; ++p) {
+    const FacJob& J = jobs[p];
+    FacProb f;
+    f.H = J.H;
+    f.A = (double*)c->facA.p + oA[p];
+    f.Y = (double*)c->facY.p + oA[p];
+    f.T = (double*)c->facT.p + oT[p];
+    f.U = J.U;
+    f.n = J.n;
+    f.ldh = J.ldh;
+    f.ldu = J.ldu;
+    f.pad0 = 0;
+    f.lam_abs = J.lam_abs;
+    f.lam_rel = J.lam_rel;
+    f.lam = &dslots[p].lam;
+    f.info = &dslots[p].info;
+    f.nonfinite = &dslots[p].nonfinite;
+    probs[p] = f;
+    maxnb = std::max(maxnb, cdiv(J.n, 64));
+    maxn = std::max(maxn, J.n);
+    if (A_out) A_out[p] = f.A;
+  }
+  Blob b;
+  const size_t o_probs = b.add(probs);
+  struct L {
+    int kind;  // 0 fill, 1 panel, 2 gemm, 3 trinv, 4 makeu
+    size_t off;
+    int nseg, nwg;
+  };
+  std::vector<L> launches;
+  auto add_launch = [&](int kind, std::vector<Seg>& segs) {
+    int nwg = 0;
+    for (auto& s : segs) {
+      s.wg0 = nwg;
+      nwg += s.nwg;
+    }
+    if (nwg == 0) return;
+    launches.push_back(L{kind, b.add(segs), (int)segs.size(), nwg});
+  };
+  {
+    std::vector<Seg> s;
+    for (int p = 0; p < np; ++p)
+      if (jobs[p].H) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 4), 0, 0, 0, 0, 0});
+    add_launch(0, s);
+  }
+  for (int k = 0; k < maxnb; ++k) {
+    std::vector<Seg> pan, trl;
+    for (int p = 0; p < np; ++p) {
+      const int n = jobs[p].n, nb = cdiv(n, 64);
+      if (k >= nb) continue;
+      pan.push_back(Seg{p, 0, nb - k, k, 0, 0, 0, 0});
+      const int r0 = 64 * (k + 1);
+      if (r0 < n) {
+        const int m = cdiv(n - r0, 64);
+        trl.push_back(Seg{p, 0, m * (m + 1) / 2, GK_CHOL_TRAIL, 64 * k, std::min(64, n - 64 * k), r0, 0});
+      }
+    }
+    add_launch(1, pan);
+    add_launch(2, trl);
+  }
+  {
+    std::vector<Seg> s;
+    for (int p = 0; p < np; ++p) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 64), 0, 0, 0, 0, 0});
+    add_launch(3, s);
+  }
+  for (int s = 64; s < maxn; s *= 2) {
+    for (int step = 0; step < 2; ++step) {
+      std::vector<Seg> sg;
+      for (int p = 0; p < np; ++p) {
+        const int n = jobs[p].n;
+        if (n <= s) continue;
+        const int npairs = cdiv(n - s, 2LL * s), tj = cdiv(s, 64);
+        sg.push_back(Seg{p, 0, npairs * tj * tj, step == 0 ? GK_INV_STEP1 : GK_INV_STEP2, s, tj * tj, 0, 0});
+      }
+      add_launch(2, sg);
+    }
+  }
+  {
+    std::vector<Seg> s;
+    for (int p = 0; p < np; ++p) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 4), 0, 0, 0, 0, 0});
+    add_launch(4, s);
+  }
+  uint8_t* d = nullptr;
+  if ((rc = upload(c, b, &d))) return rc;
+  const FacProb* dp = (const FacProb*)(d + o_probs);
+  HIPCHK(c, launch_damp_lambda(dp, np, c->stream));
+  for (const L& l : launches) {
+    const Seg* sg = (const Seg*)(d + l.off);
+    switch (l.kind) {
+      case 0: HIPCHK(c, launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 1: HIPCHK(c, launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 2: HIPCHK(c, launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 3: HIPCHK(c, launch_trinv_diag(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 4: HIPCHK(c, launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
+    }
+  }
+  return GPTQ_OK;
+}
+
+// ----------------------------------------------------------- quantize plan --
+int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<float*>* Ww_out = nullptr) {
+  const int nl = (int)jobs.size();
+  size_t totW = 0, totE = 0, totO = 0;
+  std::vector<size_t> oW(nl), oE(nl), oO(nl);
+  for (int p = 0; p < nl; ++p) {
+    const QuantJob& J = jobs[p];
+    oW[p] = totW;
+    if (!J.Ww_ext) totW += (size_t)J.out * J.nt;
+    oE[p] = totE;
+    totE += (size_t)J.out * J.block;
+    oO[p] = totO;
+    totO += (size_t)J.out * cdiv(J.n, J.block) * 2;
+  }
+  int rc;
+  if ((rc = ensure(c, c->work, totW * sizeof(float)))) return rc;
+  if ((rc = ensure(c, c->eblk, totE * sizeof(float)))) return rc;
+  if ((rc = ensure(c, c->objp, totO * sizeof(double)))) return rc;
+  std::vector<QLayer> L(nl);
+  int maxblk = 0;
+  for (int p = 0; p < nl; ++p) {
+    const QuantJob& J = jobs[p];
+    QLayer q;
+    q.W = J.W;
+    q.Ww = J.Ww_ext ? J.Ww_ext : (float*)c->work.p + oW[p];
+    q.U = J.U;
+    q.codes = J.codes;
+    q.scales = J.scales;
+    q.zeros = J.zeros;
+    q.err = J.err;
+    q.Eb = (float*)c->eblk.p + oE[p];
+    q.objp = (double*)c->objp.p + oO[p];
+    q.obj = J.obj;
+    q.lam = J.lam;
+    q.out = J.out;
+    q.n = J.n;
+    q.nt = J.nt;
+    q.bits = J.bits;
+    q.group = J.group;
+    q.block = J.block;
+    q.nblk = cdiv(J.n, J.block);
+    q.ng = J.group ? J.n / J.group : 1;
+    L[p] = q;
+    maxblk = std::max(maxblk, q.nblk);
+    if (Ww_out) Ww_out->push_back(q.Ww);
+  }
+  Blob b;
+  const size_t o_L = b.add(L);
+  struct Lc {
+    int kind;  // 0 init, 1 rowfit, 2 sweep, 3 trail
+    int block;
+    size_t off;
+    int nseg, nwg;
+  };
+  std::vector<Lc> launches;
+  auto add_launch = [&](int kind, int block, std::vector<Seg>& segs) {
+    int nwg = 0;
+    for (auto& s : segs) {
+      s.wg0 = nwg;
+      nwg += s.nwg;
+    }
+    if (nwg == 0) return;
+    launches.push_back(Lc{kind, block, b.add(segs), (int)segs.size(), nwg});
+  };
+  {
+    std::vector<Seg> s, f;
+    for (int p = 0; p < nl; ++p) {
+      s.push_back(Seg{p, 0, cdiv(jobs[p].out, 4), 0, 0, 0, 0, 0});
+      if (jobs[p].group == 0) f.push_back(Seg{p, 0, cdiv(jobs[p].out, 4), 0, 0, 0, 0, 0});
+    }
+    add_launch(0, 0, s);
+    add_launch(1, 0, f);
+  }
+  std::vector<int> blocks;
+  for (auto& J : jobs)
+    if (std::find(blocks.begin(), blocks.end(), J.block) == blocks.end()) blocks.push_back(J.block);
+  for (int k = 0; k < maxblk; ++k) {
+    for (int B : blocks) {
+      std::vector<Seg> s;
+      for (int p = 0; p < nl; ++p)
+        if (jobs[p].block == B && k < L[p].nblk) s.push_back(Seg{p, 0, cdiv(jobs[p].out, 16), k, 0, 0, 0, 0});
+      add_launch(2, B, s);
+    }
+    std::vector<Seg> t;
+    for (int p = 0; p < nl; ++p) {
+      if (k >= L[p].nblk) continue;
+      const int b1 = std::min((k + 1) * jobs[p].block, jobs[p].n);
+      if (b1 >= jobs[p].nt) continue;
+      t.push_back(Seg{p, 0, cdiv(jobs[p].out, 64) * cdiv(jobs[p].nt - b1, 64), k, 0, 0, 0, 0});
+    }
+    add_launch(3, 0, t);
+  }
+  uint8_t* d = nullptr;
+  if ((rc = upload(c, b, &d))) return rc;
+  const QLayer* dL = (const QLayer*)(d + o_L);
+  for (const Lc& l : launches) {
+    const Seg* sg = (const Seg*)(d + l.off);
+    switch (l.kind) {
+      case 0: HIPCHK(c, launch_init_work(dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 1: HIPCHK(c, launch_rowfit(dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 2: HIPCHK(c, launch_sweep(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 3: HIPCHK(c, launch_trail(dL, sg, l.nseg, l.nwg, c->stream)); break;
+    }
+  }
+  HIPCHK(c, launch_objective(dL, nl, c->stream));
+  return GPTQ_OK;
+}
+
+int check_quant_args(gptq_ctx c, int out, int n, int bits, int group, int block) {
+  if (out < 0 || n < 0) return set_err(c, GPTQ_ERR_INVALID_ARG, "negative size");
+  if (bits < 2 || bits > 8) return set_err(c, GPTQ_ERR_INVALID_ARG, "bits must be in 2..8");
+  if (!(block == 16 || block == 32 || block == 64 || block == 128))
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "block must be 16, 32, 64 or 128");
+  if (group < 0) return set_err(c, GPTQ_ERR_INVALID_ARG, "negative group");
+  if (group) {
+    if (group % 8) return set_err(c, GPTQ_ERR_UNSUPPORTED, "group must be a multiple of 8");
+    if (n % group) return set_err(c, GPTQ_ERR_INVALID_ARG, "group must divide n");
+    if (group % block && block % group)
+      return set_err(c, GPTQ_ERR_UNSUPPORTED, "group and block must divide one another");
+  }
+  return GPTQ_OK;
+}
+
+int check_x(gptq_ctx c, const uint16_t* X, long long tokens, int n, long long ldx) {
+  if (tokens < 0 || n < 0 || ldx < n) return set_err(c, GPTQ_ERR_INVALID_ARG, "bad X sizes");
+  if (tokens > 0 && n > 0 && !X) return set_err(c, GPTQ_ERR_INVALID_ARG, "X is null");
+  if (ldx % 8 || ((uintptr_t)X & 15)) return set_err(c, GPTQ_ERR_UNSUPPORTED, "X needs ldx %% 8 == 0 and 16-byte alignment");
+  if (tokens > 0x7fffffffLL) return set_err(c, GPTQ_ERR_UNSUPPORTED, "tokens > 2^31-1");
+  return GPTQ_OK;
+}
+
+int ensure_small(gptq_ctx c, size_t bytes) { return ensure_pinned(c, c->hsmall, c->hsmall_cap, bytes); }
+
+}  // namespace
+
+// ================================================================ C ABI ====
+GPTQ_API const char* gptq_strerror(int status) {
+  switch (status) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_ERR_INVALID_ARG: return "invalid argument";
+    case GPTQ_ERR_NOT_PD: return "damped Hessian is not positive definite";
+    case GPTQ_ERR_NONFINITE: return "non-finite value in the Hessian";
+    case GPTQ_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+    case GPTQ_ERR_HIP: return "HIP runtime error";
+    case GPTQ_ERR_NO_MEMORY: return "out of device memory";
+    default: return "unknown status";
+  }
+}
+
+GPTQ_API const char* gptq_last_error(gptq_ctx ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+GPTQ_API int gptq_create(gptq_ctx* ctx, int device, void* stream) {
+  if (!ctx) return GPTQ_ERR_INVALID_ARG;
+  *ctx = nullptr;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return GPTQ_ERR_INVALID_ARG;
+  gptq_ctx c = new gptq_ctx_s();
+  c->device = device;
+  c->stream = (hipStream_t)stream;
+  DeviceGuard g(device);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
+    c->ncu = prop.multiProcessorCount;
+  if (hipEventCreateWithFlags(&c->blob_ev, hipEventDisableTiming) != hipSuccess) {
+    delete c;
+    return GPTQ_ERR_HIP;
+  }
+  *ctx = c;
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_destroy(gptq_ctx c) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  {
+    DeviceGuard g(c->device);
+    (void)hipStreamSynchronize(c->stream);
+    DevBuf* bufs[] = {&c->partials, &c->facA, &c->facY, &c->facT, &c->work, &c->eblk,
+                      &c->objp, &c->slots, &c->blob, &c->lora};
+    for (DevBuf* b : bufs)
+      if (b->p) (void)hipFree(b->p);
+    if (c->hblob) (void)hipHostFree(c->hblob);
+    if (c->hsmall) (void)hipHostFree(c->hsmall);
+    if (c->blob_ev) (void)hipEventDestroy(c->blob_ev);
+  }
+  delete c;
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_hessian(gptq_ctx c, const uint16_t* X, int64_t tokens, int32_t n, int64_t ldx,
+                          float* H, int accumulate) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  int rc = check_x(c, X, tokens, n, ldx);
+  if (rc) return rc;
+  if (n > 0 && !H) return set_err(c, GPTQ_ERR_INVALID_ARG, "H is null");
+  if (n == 0) return GPTQ_OK;
+  DeviceGuard g(c->device);
+  return run_hessian(c, {HessJob{X, tokens, ldx, n, H, accumulate ? 1 : 0}});
+}
+
+GPTQ_API int gptq_factor(gptq_ctx c, const float* H, int32_t n, double lam_abs, double lam_rel,
+                         float* U, int32_t* info, double* lam_used) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (info) *info = 0;
+  if (n < 0 || (n > 0 && (!H || !U)) || !info) return set_err(c, GPTQ_ERR_INVALID_ARG, "bad factor arguments");
+  if (!std::isfinite(lam_abs) || !std::isfinite(lam_rel)) return set_err(c, GPTQ_ERR_INVALID_ARG, "non-finite damping");
+  if (n == 0) return GPTQ_OK;
+  DeviceGuard g(c->device);
+  int rc = ensure(c, c->slots, sizeof(Slot));
+  if (rc) return rc;
+  Slot* ds = (Slot*)c->slots.p;
+  if ((rc = run_factor(c, {FacJob{H, n, n, n, lam_abs, lam_rel, U}}, ds))) return rc;
+  if ((rc = ensure_small(c, sizeof(Slot)))) return rc;
+  HIPCHK(c, hipMemcpyAsync(c->hsmall, ds, sizeof(Slot), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  const Slot s = *(const Slot*)c->hsmall;
+  if (lam_used) *lam_used = s.lam;
+  if (s.nonfinite) return set_err(c, GPTQ_ERR_NONFINITE, "non-finite entry in H");
+  *info = s.info;
+  if (s.info) return set_err(c, GPTQ_ERR_NOT_PD, "not positive definite at column %d", s.info - 1);
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_quantize(gptq_ctx c, const float* W, int32_t out, int32_t n, const float* U,
+                           int32_t bits, int32_t group, int32_t block, double lam, uint8_t* codes,
+                           float* scales, uint8_t* zeros, float* err, double* obj) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  int rc = check_quant_args(c, out, n, bits, group, block);
+  if (rc) return rc;
+  if (!obj) return set_err(c, GPTQ_ERR_INVALID_ARG, "obj is null");
+  obj[0] = obj[1] = 0.0;
+  if (out == 0 || n == 0) return GPTQ_OK;
+  if (!W || !U || !codes || !scales || !zeros) return set_err(c, GPTQ_ERR_INVALID_ARG, "null pointer");
+  DeviceGuard g(c->device);
+  if ((rc = ensure(c, c->slots, sizeof(Slot)))) return rc;
+  Slot* ds = (Slot*)c->slots.p;
+  Slot hs{};
+  hs.lam = lam;
+  HIPCHK(c, hipMemcpyAsync(ds, &hs, sizeof(Slot), hipMemcpyHostToDevice, c->stream));
+  QuantJob J{W, out, n, n, U, bits, group, block, codes, scales, zeros, err, &ds->lam, ds->obj, nullptr};
+  if ((rc = run_quantize(c, {J}))) return rc;
+  if ((rc = ensure_small(c, sizeof(Slot)))) return rc;
+  HIPCHK(c, hipMemcpyAsync(c->hsmall, ds, sizeof(Slot), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  const Slot s = *(const Slot*)c->hsmall;
+  obj[0] = s.obj[0];
+  obj[1] = s.obj[1];
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_quantize_batched(gptq_ctx c, int32_t nlayers, gptq_layer* layers) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (nlayers < 0 || (nlayers > 0 && !layers)) return set_err(c, GPTQ_ERR_INVALID_ARG, "bad layer list");
+  if (nlayers == 0) return GPTQ_OK;
+  for (int i = 0; i < nlayers; ++i) {
+    gptq_layer& l = layers[i];
+    l.info = 0;
+    l.obj[0] = l.obj[1] = 0.0;
+    int rc = check_quant_args(c, l.out, l.n, l.bits, l.group, l.block);
+    if (rc) return rc;
+    if (l.n <= 0 || l.out <= 0) return set_err(c, GPTQ_ERR_INVALID_ARG, "layer %d: empty", i);
+    if (!l.W || !l.H || !l.U || !l.codes || !l.scales || !l.zeros)
+      return set_err(c, GPTQ_ERR_INVALID_ARG, "layer %d: null pointer", i);
+    if (l.X && (rc = check_x(c, l.X, l.tokens, l.n, l.ldx))) return rc;
+  }
+  DeviceGuard g(c->device);
+  int rc;
+  std::vector<HessJob> hj;
+  for (int i = 0; i < nlayers; ++i)
+    if (layers[i].X) hj.push_back(HessJob{layers[i].X, layers[i].tokens, layers[i].ldx, layers[i].n, layers[i].H, 0});
+  if (!hj.empty() && (rc = run_hessian(c, hj))) return rc;
+  // one factor per distinct (H, U, damping)
+  std::vector<int> fac_of(nlayers, -1);
+  std::vector<FacJob> fj;
+  for (int i = 0; i < nlayers; ++i) {
+    for (int j = 0; j < i; ++j)
+      if (layers[j].H == layers[i].H && layers[j].U == layers[i].U && layers[j].n == layers[i].n &&
+          layers[j].lam_abs == layers[i].lam_abs && layers[j].lam_rel == layers[i].lam_rel) {
+        fac_of[i] = fac_of[j];
+        break;
+      }
+    if (fac_of[i] < 0) {
+      fac_of[i] = (int)fj.size();
+      fj.push_back(FacJob{layers[i].H, layers[i].n, layers[i].n, layers[i].n, layers[i].lam_abs, layers[i].lam_rel, layers[i].U});
+    }
+  }
+  const int nf = (int)fj.size();
+  if ((rc = ensure(c, c->slots, sizeof(Slot) * (nf + nlayers)))) return rc;
+  Slot* ds = (Slot*)c->slots.p;
+  if ((rc = run_factor(c, fj, ds))) return rc;
+  std::vector<QuantJob> qj;
+  for (int i = 0; i < nlayers; ++i) {
+    const gptq_layer& l = layers[i];
+    qj.push_back(QuantJob{l.W, l.out, l.n, l.n, l.U, l.bits, l.group, l.block, l.codes, l.scales, l.zeros,
+                          l.err, &ds[fac_of[i]].lam, ds[nf + i].obj, nullptr});
+  }
+  if ((rc = run_quantize(c, qj))) return rc;
+  const size_t bytes = sizeof(Slot) * (nf + nlayers);
+  if ((rc = ensure_small(c, bytes))) return rc;
+  HIPCHK(c, hipMemcpyAsync(c->hsmall, ds, bytes, hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  const Slot* hs = (const Slot*)c->hsmall;
+  int first = GPTQ_OK;
+  for (int i = 0; i < nlayers; ++i) {
+    const Slot& f = hs[fac_of[i]];
+    layers[i].info = f.info;
+    layers[i].obj[0] = hs[nf + i].obj[0];
+    layers[i].obj[1] = hs[nf + i].obj[1];
+    if (!first && f.nonfinite) first = set_err(c, GPTQ_ERR_NONFINITE, "layer %d: non-finite H", i);
+    if (!first && f.info) first = set_err(c, GPTQ_ERR_NOT_PD, "layer %d: not positive definite", i);
+  }
+  return first;
+}
+
+GPTQ_API int gptq_lora(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t* X,
+                       int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,
+                       int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
+                       uint8_t* zeros, float* L, float* R, double* obj, int32_t* info) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (info) *info = 0;
+  int rc = check_quant_args(c, out, n, bits, group, block);
+  if (rc) return rc;
+  if ((rc = check_x(c, X, tokens, n, ldx))) return rc;
+  if (r < 1 || r > 256 || r > n) return set_err(c, GPTQ_ERR_UNSUPPORTED, "rank must be in 1..min(256, n)");
+  if (!obj || !W || !codes || !scales || !zeros || !L || !R || out <= 0 || n <= 0)
+    return set_err(c, GPTQ_ERR_INVALID_ARG, "null pointer or empty layer");
+  obj[0] = obj[1] = 0.0;
+  DeviceGuard g(c->device);
+  LoraIO io{W, out, n, X, tokens, ldx, r, bits, group, block, lam_abs, lam_rel, codes, scales, zeros, L, R};
+  LoraHooks hooks;
+  hooks.hessian = [&](const uint16_t* X_, long long t_, long long ld_, int n_, float* H_) {
+    return run_hessian(c, {HessJob{X_, t_, ld_, n_, H_, 0}});
+  };
+  hooks.ensure = [&](size_t bytes) -> void* {
+    if (ensure(c, c->lora, bytes)) return nullptr;
+    return c->lora.p;
+  };
+  hooks.factor = [&](double* A, int nt, float* U, Slot* slot) {
+    // A was assembled (damped, reversed, lower) by the LoRA kernels
+    std::vector<FacJob> fj{FacJob{nullptr, nt, nt, nt, 0.0, 0.0, U}};
+    DevBuf save = c->facA;
+    c->facA.p = A;
+    c->facA.cap = (size_t)nt * nt * sizeof(double);
+    int rc2 = run_factor(c, fj, slot, true);
+    c->facA = save;
+    return rc2;
+  };
+  hooks.quantize = [&](const QuantJob& j) { return run_quantize(c, {j}); };
+  hooks.slots = [&](size_t bytes) -> void* {
+    if (ensure(c, c->slots, bytes)) return nullptr;
+    return c->slots.p;
+  };
+  hooks.set_err = [&](int st, const char* msg) { return set_err(c, st, "%s", msg); };
+  rc = run_lora(c->stream, io, hooks);
+  if (rc) return rc;
+  Slot* ds = (Slot*)c->slots.p;
+  if ((rc = ensure_small(c, sizeof(Slot)))) return rc;
+  HIPCHK(c, hipMemcpyAsync(c->hsmall, ds, sizeof(Slot), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  const Slot s = *(const Slot*)c->hsmall;
+  if (s.nonfinite) return set_err(c, GPTQ_ERR_NONFINITE, "non-finite entry in H");
+  if (info) *info = s.info;
+  if (s.info) return set_err(c, GPTQ_ERR_NOT_PD, "augmented Hessian not positive definite");
+  obj[0] = s.obj[0];
+  obj[1] = s.obj[1];
+  return GPTQ_OK;
+}

@@ -1,0 +1,86 @@
+// Internal definitions shared by the HIP kernels and the host planner of the
+// GPTQ library (gfx950 / CDNA4).  Nothing here is part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef double f64x4 __attribute__((__vector_size__(4 * sizeof(double))));
+
+// A grouped launch covers several problems (layers).  Each problem owns a
+// contiguous range [wg0, wg0 + nwg) of the grid; a..d are kernel-specific.
+struct Seg {
+  int prob;
+  int wg0;
+  int nwg;
+  int a, b, c, d, e;
+};
+
+// ---------------------------------------------------------------- Hessian --
+// One 256x256 output tile of H over the token range [k0, k1) -> partial slot.
+struct SyrkProb {
+  const uint16_t* X;
+  long long ldx;
+  int n;
+  int tokens;
+};
+struct SyrkTask {
+  int prob, ti, tj, k0, k1, part, pad0, pad1;
+};
+// One 64x64 sub-block (r0 <= c0 region) of an upper tile: sum of its partials.
+struct RedProb {
+  float* H;
+  int n;
+  int accumulate;
+};
+struct RedTask {
+  int prob, r0, c0, part0, nparts, pad0, pad1, pad2;
+};
+
+// ----------------------------------------------------------------- factor --
+// Work matrices are fp64, row-major with leading dimension n.
+//   A: damped, index-reversed matrix, overwritten by its Cholesky factor C
+//   Y: C^{-1} (lower), T: scratch of the triangular inverse
+struct FacProb {
+  const float* H;  // input [n][ldh] fp32 (null when A was assembled elsewhere)
+  double* A;
+  double* Y;
+  double* T;
+  float* U;        // output [n][ldu]
+  int n;
+  int ldh;
+  int ldu;
+  int pad0;
+  double lam_abs, lam_rel;
+  double* lam;     // device slot: damping used
+  int* info;       // device slot: 0 or 1 + failing column (H numbering)
+  int* nonfinite;  // device slot
+};
+
+enum GemmKind { GK_CHOL_TRAIL = 0, GK_INV_STEP1 = 1, GK_INV_STEP2 = 2 };
+
+// ------------------------------------------------------------------ sweep --
+struct QLayer {
+  const float* W;   // original weights [out][n]
+  float* Ww;        // working weights [out][nt]
+  const float* U;   // factor [nt][nt]
+  uint8_t* codes;   // [out][n]
+  float* scales;    // [out][ng]
+  uint8_t* zeros;   // [out][ng]
+  float* err;       // [out][n] or null
+  float* Eb;        // block errors [out][block]
+  double* objp;     // per (row, block): {sum E^2, sum D^2}
+  double* obj;      // [2] {J, J_lam} (device)
+  const double* lam;  // device slot holding the damping of U
+  int out, n, nt, bits, group, block, nblk, ng;
+};
+
+__device__ __forceinline__ int find_seg(const Seg* __restrict__ segs, int nseg, int wg) {
+  int s = 0;
+  while (s + 1 < nseg && segs[s + 1].wg0 <= wg) ++s;
+  return s;
+}

@@ -1,0 +1,338 @@
+// Damping and the upper Cholesky factor of the inverse damped Hessian, in fp64.
+//
+// lam = lam_abs + lam_rel * mean(diag H) and H_lam = H + lam I (Lattice
+// Geometry of NN Quantization, technical overview section 3.1).  The sweep
+// needs U upper with H_lam^{-1} = U^T U: the unit-upper factor of the LDL of
+// the inverse Gram matrix is diag(U)^{-1} U (GPTQ-2D technical summary,
+// sections 2 and 4).  With P the index reversal and C = chol(P H_lam P),
+// U = P C^{-1} P, so one Cholesky and one triangular inverse suffice
+// (2n^3/3 flops instead of 4n^3/3 for Cholesky -> inverse -> Cholesky).
+//
+// Cholesky: right-looking, 64-wide panels (a panel kernel factors the
+// diagonal block in LDS and solves its rows below, then an fp64 MFMA update of
+// the trailing lower triangle).  Inverse: recursive doubling over the diagonal
+// blocks, [[A,0],[B,C]]^{-1} = [[A^-1,0],[-C^-1 B A^-1, C^-1]], two fp64 MFMA
+// products per level for all block pairs at once.
+#include "common.h"
+#include "launch.h"
+
+#define NB 64
+
+// ------------------------------------------------------------ damping -----
+__global__ __launch_bounds__(256) void k_damp_lambda(const FacProb* __restrict__ probs, int nprob) {
+  __shared__ double red[256];
+  const int p = blockIdx.x;
+  if (p >= nprob) return;
+  const FacProb pb = probs[p];
+  if (pb.H == nullptr) return;  // assembled elsewhere (lam already set)
+  double s = 0.0;
+  for (int i = threadIdx.x; i < pb.n; i += 256) s += (double)pb.H[(size_t)i * pb.ldh + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double mean = pb.n > 0 ? red[0] / (double)pb.n : 0.0;
+    *pb.lam = pb.lam_abs + pb.lam_rel * mean;
+    *pb.info = 0;
+    *pb.nonfinite = 0;
+  }
+}
+
+// A[i][j] = H[n-1-i][n-1-j] + lam delta_ij, lower triangle only (j <= i).
+// Segment: one workgroup per 4 rows.
+__global__ __launch_bounds__(256) void k_damp_fill(const FacProb* __restrict__ probs,
+                                                   const Seg* __restrict__ segs, int nseg) {
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  const int n = pb.n;
+  const int i = (blockIdx.x - sg.wg0) * 4 + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const double lam = *pb.lam;
+  const float* hrow = pb.H + (size_t)(n - 1 - i) * pb.ldh;
+  double* arow = pb.A + (size_t)i * n;
+  bool bad = false;
+  for (int j = threadIdx.x & 63; j <= i; j += 64) {
+    const float h = hrow[n - 1 - j];
+    bad |= !__builtin_isfinite(h);
+    arow[j] = (double)h + (i == j ? lam : 0.0);
+  }
+  if (bad) atomicOr(pb.nonfinite, 1);
+}
+
+// ----------------------------------------------------------- Cholesky -----
+// Panel k: workgroup (k, i) for row blocks i >= k.  Each factors the 64x64
+// diagonal block in LDS (identically), then block k writes it back and every
+// other block solves X C_kk^T = A_ik for its rows.
+__global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ probs,
+                                                    const Seg* __restrict__ segs, int nseg) {
+  __shared__ double D[NB][NB + 1];
+  __shared__ double R[NB][NB + 1];
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  const int n = pb.n, k = sg.a, i = k + (blockIdx.x - sg.wg0);
+  const int k0 = k * NB, m = min(NB, n - k0);
+  const int tid = threadIdx.x;
+  double* A = pb.A;
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    D[r][c] = (r < m && c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
+  }
+  __syncthreads();
+  for (int j = 0; j < m; ++j) {
+    const double d = D[j][j];
+    if (!(d > 0.0) || !__builtin_isfinite(d)) {
+      // first failing pivot in elimination order: step k0 + j, column n-1-(k0+j) of H
+      if (tid == 0 && i == k) atomicMax(pb.info, n - (k0 + j));
+      return;  // uniform: every thread read the same d
+    }
+    const double sd = sqrt(d);
+    const double inv = 1.0 / sd;
+    __syncthreads();
+    if (tid == 0) D[j][j] = sd;
+    for (int r = j + 1 + tid; r < m; r += 256) D[r][j] *= inv;
+    __syncthreads();
+    const int w = m - j - 1;  // trailing size
+    for (int e = tid; e < w * w; e += 256) {
+      const int r = j + 1 + e / w, c = j + 1 + e % w;
+      if (c <= r) D[r][c] -= D[r][j] * D[c][j];
+    }
+    __syncthreads();
+  }
+  if (i == k) {
+    for (int e = tid; e < NB * NB; e += 256) {
+      const int r = e >> 6, c = e & 63;
+      if (r < m && c <= r) A[(size_t)(k0 + r) * n + k0 + c] = D[r][c];
+    }
+    return;
+  }
+  const int r0 = i * NB, mr = min(NB, n - r0);
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    R[r][c] = (r < mr && c < m) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0;
+  }
+  __syncthreads();
+  // X D^T = R, column by column: X[:, c] = R[:, c] / D[c][c]; R[:, c'] -= X[:, c] D[c'][c]
+  const int rr = tid & 63, part = tid >> 6;
+  for (int c = 0; c < m; ++c) {
+    if (part == 0) R[rr][c] = R[rr][c] / D[c][c];
+    __syncthreads();
+    const double x = R[rr][c];
+    for (int c2 = c + 1 + part; c2 < m; c2 += 4) R[rr][c2] -= x * D[c2][c];
+    __syncthreads();
+  }
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    if (r < mr && c < m) A[(size_t)(r0 + r) * n + k0 + c] = R[r][c];
+  }
+}
+
+// --------------------------------------------------- fp64 MFMA products ---
+// One 64x64 output tile per workgroup, 4 waves of 32x32, v_mfma_f64_16x16x4.
+//   C(i, j) = beta C(i, j) + alpha sum_{t in [kb, ke)} Aop(i, t) Bop(t, j)
+// Aop(i, t) = A[i * lda + t]; Bop(t, j) = B[t * sbk + j * sbj] (one of sbk,
+// sbj is 1).  The kind decides the operands from the problem's matrices.
+__global__ __launch_bounds__(256) void k_gemm64(const FacProb* __restrict__ probs,
+                                                const Seg* __restrict__ segs, int nseg) {
+  __shared__ double As[64][17];
+  __shared__ double Bs[16][65];
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  const int n = pb.n;
+  const int t = blockIdx.x - sg.wg0;
+  const double* A;
+  const double* B;
+  double* C;
+  long long lda, sbk, sbj, ldc;
+  int mt, nt, kb, ke;
+  double alpha, beta;
+  if (sg.a == GK_CHOL_TRAIL) {
+    // panel columns [k0, k0 + pw), trailing rows/cols from r0; lower tiles only
+    const int k0 = sg.b, pw = sg.c, r0 = sg.d;
+    int a = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
+    while ((a + 1) * (a + 2) / 2 <= t) ++a;
+    while (a * (a + 1) / 2 > t) --a;
+    const int b = t - a * (a + 1) / 2;
+    const int i0 = r0 + 64 * a, j0 = r0 + 64 * b;
+    A = pb.A + (size_t)i0 * n + k0;
+    lda = n;
+    B = pb.A + (size_t)j0 * n + k0;
+    sbk = 1;
+    sbj = n;
+    C = pb.A + (size_t)i0 * n + j0;
+    ldc = n;
+    mt = min(64, n - i0);
+    nt = min(64, n - j0);
+    kb = 0;
+    ke = pw;
+    alpha = -1.0;
+    beta = 1.0;
+  } else {
+    // level with block size s: pair q = A-block [a0, a0+s), C-block [c0, c0+sC)
+    const int s = sg.b, tiles_j = (s + 63) / 64;
+    const int pair_tiles = sg.c;  // tiles per pair (uniform: ceil(s/64)^2)
+    const int q = t / pair_tiles, tt = t % pair_tiles;
+    const int a0 = 2 * q * s, c0 = a0 + s, sC = min(s, n - c0);
+    const int ti = tt / tiles_j, tj = tt % tiles_j;
+    const int i0 = 64 * ti, j0 = 64 * tj;
+    if (i0 >= sC) return;
+    mt = min(64, sC - i0);
+    nt = min(64, s - j0);
+    double* Tq = pb.T + (size_t)q * s * s;  // one s x s slot per pair
+    if (sg.a == GK_INV_STEP1) {
+      // T = B_blk * Y_A, B_blk = C[c0.., a0..] (stored in A), Y_A lower
+      A = pb.A + (size_t)(c0 + i0) * n + a0;
+      lda = n;
+      B = pb.Y + (size_t)a0 * n + a0 + j0;
+      sbk = n;
+      sbj = 1;
+      C = Tq + (size_t)i0 * s + j0;
+      ldc = s;
+      kb = j0;
+      ke = s;
+      alpha = 1.0;
+      beta = 0.0;
+    } else {
+      // Y_B = -Y_C * T, Y_C lower
+      A = pb.Y + (size_t)(c0 + i0) * n + c0;
+      lda = n;
+      B = Tq + j0;
+      sbk = s;
+      sbj = 1;
+      C = pb.Y + (size_t)(c0 + i0) * n + a0 + j0;
+      ldc = n;
+      kb = 0;
+      ke = min(sC, i0 + 64);
+      alpha = -1.0;
+      beta = 0.0;
+    }
+    // rows of A are offset by i0 already; the k index of Y_C starts at 0
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr = w >> 1, wc = w & 1;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0;
+
+  for (int k0 = kb; k0 < ke; k0 += 16) {
+    {  // A chunk: 64 rows x 16 k
+      const int r = tid >> 2, kq = (tid & 3) * 4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = k0 + kq + u;
+        As[r][kq + u] = (r < mt && kk < ke) ? A[(size_t)r * lda + kk] : 0.0;
+      }
+    }
+    if (sbj == 1) {  // B chunk, j-contiguous: 16 k x 64 j
+      const int kr = tid >> 4, jq = (tid & 15) * 4;
+      const int kk = k0 + kr;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jq + u;
+        Bs[kr][j] = (kk < ke && j < nt) ? B[(size_t)kk * sbk + j] : 0.0;
+      }
+    } else {  // k-contiguous
+      const int j = tid >> 2, kq = (tid & 3) * 4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = k0 + kq + u;
+        Bs[kq + u][j] = (kk < ke && j < nt) ? B[(size_t)j * sbj + kk] : 0.0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      double a[2], b[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) a[mi] = As[32 * wr + 16 * mi + (lane & 15)][4 * kk + (lane >> 4)];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) b[ni] = Bs[4 * kk + (lane >> 4)][32 * wc + 16 * ni + (lane & 15)];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 32 * wr + 16 * mi + (lane >> 4) + 4 * r;
+        const int j = 32 * wc + 16 * ni + (lane & 15);
+        if (i < mt && j < nt) {
+          double* cp = C + (size_t)i * ldc + j;
+          *cp = (beta != 0.0 ? *cp : 0.0) + alpha * acc[mi][ni][r];
+        }
+      }
+}
+
+// ------------------------------------------------ triangular inverse -----
+// Invert every 64x64 diagonal block of C (lower): one thread per column.
+__global__ __launch_bounds__(64) void k_trinv_diag(const FacProb* __restrict__ probs,
+                                                   const Seg* __restrict__ segs, int nseg) {
+  __shared__ double Cs[NB][NB + 1];
+  __shared__ double Ys[NB][NB + 1];
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  const int n = pb.n, b0 = (blockIdx.x - sg.wg0) * NB, m = min(NB, n - b0);
+  const int j = threadIdx.x;
+  for (int r = 0; r < m; ++r) Cs[r][j] = (j <= r && j < m) ? pb.A[(size_t)(b0 + r) * n + b0 + j] : 0.0;
+  __syncthreads();
+  if (j < m) {
+    Ys[j][j] = 1.0 / Cs[j][j];
+    for (int i = j + 1; i < m; ++i) {
+      double s = 0.0;
+      for (int t = j; t < i; ++t) s += Cs[i][t] * Ys[t][j];
+      Ys[i][j] = -s / Cs[i][i];
+    }
+  }
+  __syncthreads();
+  for (int r = 0; r < m; ++r)
+    if (j < m) pb.Y[(size_t)(b0 + r) * n + b0 + j] = (j <= r) ? Ys[r][j] : 0.0;
+}
+
+// U[i][j] = Y[n-1-i][n-1-j] for j >= i (upper), 0 below; fp32.  4 rows per WG.
+__global__ __launch_bounds__(256) void k_make_u(const FacProb* __restrict__ probs,
+                                                const Seg* __restrict__ segs, int nseg) {
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  const int n = pb.n;
+  const int i = (blockIdx.x - sg.wg0) * 4 + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const double* yrow = pb.Y + (size_t)(n - 1 - i) * n;
+  float* urow = pb.U + (size_t)i * pb.ldu;
+  for (int j = threadIdx.x & 63; j < n; j += 64) urow[j] = (j >= i) ? (float)yrow[n - 1 - j] : 0.f;
+}
+
+hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st) {
+  if (nprob <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_damp_lambda, dim3(nprob), dim3(256), 0, st, probs, nprob);
+  return hipGetLastError();
+}
+
+#define SEG_LAUNCH(name, kern, threads)                                                   \
+  hipError_t name(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st) { \
+    if (nwg <= 0) return hipSuccess;                                                      \
+    hipLaunchKernelGGL(kern, dim3(nwg), dim3(threads), 0, st, probs, segs, nseg);         \
+    return hipGetLastError();                                                             \
+  }
+
+SEG_LAUNCH(launch_damp_fill, k_damp_fill, 256)
+SEG_LAUNCH(launch_chol_panel, k_chol_panel, 256)
+SEG_LAUNCH(launch_gemm64, k_gemm64, 256)
+SEG_LAUNCH(launch_trinv_diag, k_trinv_diag, 64)
+SEG_LAUNCH(launch_make_u, k_make_u, 256)

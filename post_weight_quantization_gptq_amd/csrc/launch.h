@@ -1,0 +1,25 @@
+// Host-side launchers of the kernels (internal to the library).
+#pragma once
+#include "common.h"
+
+// Hessian
+hipError_t launch_syrk(const SyrkProb* probs, const SyrkTask* tasks, int ntasks, float* partials,
+                       hipStream_t st);
+hipError_t launch_syrk_reduce(const RedProb* probs, const RedTask* tasks, int ntasks,
+                              const int* partlist, const float* partials, hipStream_t st);
+hipError_t launch_zero_f32(float* p, long long count, hipStream_t st);
+
+// Factor
+hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st);
+hipError_t launch_damp_fill(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_chol_panel(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_gemm64(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_trinv_diag(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_make_u(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
+
+// Sweep
+hipError_t launch_init_work(const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_rowfit(const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_sweep(int block, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_trail(const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_objective(const QLayer* L, int nl, hipStream_t st);

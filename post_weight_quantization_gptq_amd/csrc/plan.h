@@ -1,0 +1,54 @@
+// Host-side planning types shared by the C ABI and the intrinsic-LoRA driver
+// (internal to the library).
+#pragma once
+#include <functional>
+
+#include "common.h"
+
+// Per-call device slot of one factor/quantise job.
+struct Slot {
+  double lam;
+  int info;
+  int nonfinite;
+  double obj[2];
+};
+
+struct QuantJob {
+  const float* W;
+  int out, n, nt;  // nt = n + appended (never rounded) columns
+  const float* U;  // [nt][nt]
+  int bits, group, block;
+  uint8_t* codes;
+  float* scales;
+  uint8_t* zeros;
+  float* err;
+  const double* lam;  // device pointer to the damping of U
+  double* obj;        // device [2]
+  float* Ww_ext;      // optional caller-owned working buffer [out][nt]
+};
+
+struct LoraIO {
+  const float* W;
+  int out, n;
+  const uint16_t* X;
+  long long tokens, ldx;
+  int r, bits, group, block;
+  double lam_abs, lam_rel;
+  uint8_t* codes;
+  float* scales;
+  uint8_t* zeros;
+  float* L;
+  float* R;
+};
+
+// Services the C ABI lends to the LoRA driver (workspace, the shared stages).
+struct LoraHooks {
+  std::function<int(const uint16_t*, long long, long long, int, float*)> hessian;
+  std::function<void*(size_t)> ensure;  // LoRA workspace of at least n bytes
+  std::function<void*(size_t)> slots;   // device slots of at least n bytes
+  std::function<int(double*, int, float*, Slot*)> factor;  // factor an assembled A
+  std::function<int(const QuantJob&)> quantize;
+  std::function<int(int, const char*)> set_err;
+};
+
+int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hooks);
