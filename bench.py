@@ -1,0 +1,186 @@
+"""Benchmark of the GPTQ layer-quantization pass on one MI355X.
+
+One step = the whole pass for one layer on inputs already resident in HBM:
+gptq_hessian (X^T X on bf16 MFMA) -> gptq_factor (damping, fp64 Cholesky and
+triangular inverse) -> gptq_quantize (blocked column sweep, trailing updates,
+objective).  The default workload is the square projection layer: W 4096x4096,
+4-bit, group 128, block 128, 262144 calibration tokens.
+
+Prints one JSON line (rank 0).  Extra objects: `roofline` for the dominant
+kernel (the Hessian contraction, timed live with HIP events on the library's
+stream), `cpu_baseline` (the float64 oracle timed on a bounded sample on the
+host cores), per-stage times and algorithmic TFLOP/s.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # dense MFMA bf16, MI355X
+PEAK_HBM_GBS = 8000.0
+METRIC = "ms per layer + TFLOP/s (frac of MFMA peak), 4096×4096 4-bit g128 GPTQ"
+
+
+def layer_flops(out, n, tokens, block, n_total=None):
+    """Algorithmic flops of one layer (counted as in the design notes)."""
+    nt = n_total or n
+    syrk = tokens * n * (n + 1)
+    factor = 2 * nt ** 3 / 3
+    nblk = -(-n // block)
+    sweep = 0
+    trail = 0
+    for b in range(nblk):
+        b0, b1 = b * block, min((b + 1) * block, n)
+        w = b1 - b0
+        sweep += out * w * (w - 1)
+        trail += 2 * out * w * (nt - b1)
+    return dict(syrk=syrk, factor=factor, sweep=sweep, trail=trail, total=syrk + factor + sweep + trail)
+
+
+def cpu_baseline(spec, lay, max_rows=32, tok_sample=4096):
+    """The float64 oracle, as it stands, on a bounded sample of the same layer,
+    scaled to ms per layer: Hessian on tok_sample tokens (scaled by tokens),
+    the full damping + factor, and the sweep on max_rows rows (scaled by rows)."""
+    import numpy as np
+    from oracle import gptq_ref as o
+    from post_weight_quantization_gptq_amd import synth
+    Xs = synth.bits_to_numpy(lay["X"][:tok_sample].cpu())
+    t0 = time.perf_counter()
+    Hs = o.hessian(Xs)
+    t_h = time.perf_counter() - t0
+    # factor on a full-rank matrix of the same size (the sampled H is rank
+    # deficient only through damping, which keeps it positive definite)
+    t0 = time.perf_counter()
+    Hl, lam = o.damp(Hs, lam_rel=spec.lam_rel)
+    U = o.factor_u(Hl)
+    t_f = time.perf_counter() - t0
+    W = lay["W"][:max_rows].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    o.gptq_sweep(W, U, spec.bits, spec.group, spec.block)
+    t_s = time.perf_counter() - t0
+    total_ms = 1e3 * (t_h * spec.tokens / tok_sample + t_f + t_s * spec.out / max_rows)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    return {"value": round(total_ms, 1), "unit": "ms/layer", "cores": cores, "kind": "oracle",
+            "sample": "Hessian on %d of %d tokens (x%.0f), full damping+factor (n=%d), sweep on %d of %d rows (x%.0f);"
+                      " measured %.1f s + %.1f s + %.1f s" % (tok_sample, spec.tokens, spec.tokens / tok_sample,
+                                                               spec.n, max_rows, spec.out, spec.out / max_rows,
+                                                               t_h, t_f, t_s)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="square", choices=["square", "single", "lora", "mlp", "vit"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs the pass on a single MI355X "
+              "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from post_weight_quantization_gptq_amd import Context, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    specs = synth.FULL[args.workload]
+    print("# generating %s inputs" % args.workload, file=sys.stderr, flush=True)
+    lays = [synth.layer(s, dev) for s in specs]
+    torch.cuda.synchronize()
+    ctx = Context(dev)
+    st = torch.cuda.current_stream(dev)
+
+    def one_step(ev=None):
+        results = []
+        if args.workload == "vit":
+            layers = [dict(W=l["W"], X=l["X"], bits=s.bits, group=s.group, block=s.block, lam_rel=s.lam_rel)
+                      for s, l in zip(specs, lays)]
+            ctx.quantize_batched(layers)
+            return layers
+        for s, l in zip(specs, lays):
+            if s.kind == "lowrank":
+                results.append(ctx.lora(l["W"], l["X"], s.rank, s.bits, s.group, s.block, lam_rel=s.lam_rel))
+                continue
+            if ev is not None:
+                ev[0].record(st)
+            H = ctx.hessian(l["X"])
+            if ev is not None:
+                ev[1].record(st)
+            U, info, lam = ctx.factor(H, lam_rel=s.lam_rel)
+            if ev is not None:
+                ev[2].record(st)
+            r = ctx.quantize(l["W"], U, s.bits, s.group, s.block, lam)
+            if ev is not None:
+                ev[3].record(st)
+            results.append(r)
+        return results
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    stage = {"hessian": 0.0, "factor": 0.0, "quantize": 0.0}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    last = None
+    for k in range(args.steps):
+        last = one_step(evs[k] if args.workload in ("square", "single", "mlp") else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    nlayers = len(specs)
+    ms_layer = ms_step / nlayers
+
+    fl = [layer_flops(s.out, s.n, s.tokens, s.block, s.n + s.rank) for s in specs]
+    total_flops = sum(f["total"] for f in fl)
+    tflops = total_flops / (ms_step * 1e-3) / 1e12
+    line = {"metric": METRIC, "value": round(ms_layer, 4), "unit": "ms/layer", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; shapes, spectra and outliers of the pages' layers)",
+            "config": {"workload": "%s: %s" % (args.workload, ", ".join(
+                "%s W[%d,%d] X[%d,%d] %d-bit g%d B%d" % (s.name, s.out, s.n, s.tokens, s.n, s.bits, s.group, s.block)
+                for s in specs[:4]) + (" ... (%d layers)" % len(specs) if len(specs) > 4 else ""))},
+            "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "dtypes": "X bf16 -> H fp32 (bf16 MFMA, fp32 accumulate); factor fp64; sweep and trailing fp32"}
+    if args.workload in ("square", "single", "mlp"):
+        for k in range(args.steps):
+            e = evs[k]
+            stage["hessian"] += e[0].elapsed_time(e[1])
+            stage["factor"] += e[1].elapsed_time(e[2])
+            stage["quantize"] += e[2].elapsed_time(e[3])
+        for key in stage:
+            stage[key] = round(stage[key] / args.steps / nlayers, 4)
+        line["stages_ms"] = stage
+        syrk_flops = sum(f["syrk"] for f in fl) / nlayers
+        ach = syrk_flops / (stage["hessian"] * 1e-3) / 1e12
+        traffic = None
+        tf_path = os.path.join(ROOT, "profiles", "syrk_%s_traffic.json" % args.workload)
+        if os.path.exists(tf_path):
+            try:
+                traffic = json.load(open(tf_path)).get("bytes_per_launch")
+            except Exception:
+                traffic = None
+        line["roofline"] = {"kernel": "k_syrk (+ k_syrk_reduce in the timed call)", "bound": "mfma",
+                            "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    if args.workload == "lora":
+        line["objective"] = {"J": last[0]["J"], "J_lam": last[0]["J_lam"]}
+    if not args.no_cpu_baseline and args.workload in ("square", "single"):
+        print("# timing the oracle on a host sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(specs[0], {"W": lays[0]["W"], "X": lays[0]["X"]})
+    ctx.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -68,8 +68,9 @@ const char* gptq_last_error(gptq_ctx ctx);
  * X[tokens][ldx] bf16 bit patterns; only the first n columns are read.
  * The sum is unscaled.  bf16 products are exact in fp32; accumulation is fp32
  * in a fixed order (split over tokens, partials summed in a fixed order), and
- * H is exactly symmetric.  Requires ldx % 8 == 0, ldx >= n, X 16-byte aligned
- * (else GPTQ_ERR_UNSUPPORTED).  tokens == 0 leaves H (accumulate) or zeroes it.
+ * H is exactly symmetric.  Requires ldx >= n; rows are read with 16-byte
+ * loads when ldx % 8 == 0 and X is 16-byte aligned, element by element
+ * otherwise.  tokens == 0 leaves H (accumulate) or zeroes it.
  * Asynchronous. */
 int gptq_hessian(gptq_ctx ctx, const uint16_t* X, int64_t tokens, int32_t n, int64_t ldx,
                  float* H, int accumulate);
@@ -108,7 +109,7 @@ int gptq_factor(gptq_ctx ctx, const float* H, int32_t n, double lam_abs, double 
  * obj[2] [host] = {J, J_lam}: J_lam = sum E^2 = tr(D (H+lam I) D^T) and
  * J = J_lam - lam ||D||^2 = ||X D^T||^2 with D = W - What.
  * Requirements: 2 <= bits <= 8; group == 0 or (group % 8 == 0, n % group == 0,
- * and group % block == 0 or block % group == 0); block in {16,32,64,128,256}.
+ * and group % block == 0 or block % group == 0); block in {16,32,64,128}.
  * SYNC (objective read back). */
 int gptq_quantize(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const float* U,
                   int32_t bits, int32_t group, int32_t block, double lam,
@@ -125,7 +126,7 @@ int gptq_quantize(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const fl
  *                 the same product L R);
  *   R[r][out] fp32;
  *   obj[2] [host] = {J, J_lam}, J = ||X (W - What - R^T L^T)^T||^2.
- * X as gptq_hessian; 1 <= r <= 256; requirements on bits/group/block as
+ * X as gptq_hessian; 1 <= r <= min(128, n); requirements on bits/group/block as
  * gptq_quantize.  SYNC.  *info semantics as gptq_factor (may be NULL). */
 int gptq_lora(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const uint16_t* X,
               int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,

@@ -178,7 +178,8 @@ void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, H
   std::vector<int> ntile_of(jobs.size());
   for (size_t p = 0; p < jobs.size(); ++p) {
     const HessJob& J = jobs[p];
-    P.probs.push_back(SyrkProb{J.X, J.ldx, J.n, (int)J.tokens});
+    const int vec = (J.ldx % 8 == 0) && (((uintptr_t)J.X & 15) == 0);
+    P.probs.push_back(SyrkProb{J.X, J.ldx, J.n, vec});
     P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate});
     const int nt = cdiv(J.n, 256);
     ntile_of[p] = nt;
@@ -545,7 +546,7 @@ int check_quant_args(gptq_ctx c, int out, int n, int bits, int group, int block)
 int check_x(gptq_ctx c, const uint16_t* X, long long tokens, int n, long long ldx) {
   if (tokens < 0 || n < 0 || ldx < n) return set_err(c, GPTQ_ERR_INVALID_ARG, "bad X sizes");
   if (tokens > 0 && n > 0 && !X) return set_err(c, GPTQ_ERR_INVALID_ARG, "X is null");
-  if (ldx % 8 || ((uintptr_t)X & 15)) return set_err(c, GPTQ_ERR_UNSUPPORTED, "X needs ldx %% 8 == 0 and 16-byte alignment");
+  if ((uintptr_t)X & 1) return set_err(c, GPTQ_ERR_INVALID_ARG, "X is not 2-byte aligned");
   if (tokens > 0x7fffffffLL) return set_err(c, GPTQ_ERR_UNSUPPORTED, "tokens > 2^31-1");
   return GPTQ_OK;
 }
@@ -746,7 +747,7 @@ GPTQ_API int gptq_lora(gptq_ctx c, const float* W, int32_t out, int32_t n, const
   int rc = check_quant_args(c, out, n, bits, group, block);
   if (rc) return rc;
   if ((rc = check_x(c, X, tokens, n, ldx))) return rc;
-  if (r < 1 || r > 256 || r > n) return set_err(c, GPTQ_ERR_UNSUPPORTED, "rank must be in 1..min(256, n)");
+  if (r < 1 || r > 128 || r > n) return set_err(c, GPTQ_ERR_UNSUPPORTED, "rank must be in 1..min(128, n)");
   if (!obj || !W || !codes || !scales || !zeros || !L || !R || out <= 0 || n <= 0)
     return set_err(c, GPTQ_ERR_INVALID_ARG, "null pointer or empty layer");
   obj[0] = obj[1] = 0.0;

@@ -26,7 +26,7 @@ struct SyrkProb {
   const uint16_t* X;
   long long ldx;
   int n;
-  int tokens;
+  int vec;  // rows are 16-byte aligned (16-byte loads allowed)
 };
 struct SyrkTask {
   int prob, ti, tj, k0, k1, part, pad0, pad1;

@@ -113,10 +113,12 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
     ev[c] = 0.f;
   }
   Grid g = {1.f, 1.f, 0.f};
-  if (G == 0 && rv) {
-    g.s = ly.scales[(size_t)row * ly.ng];
+  if (rv && (G == 0 || (b0 % G) != 0)) {
+    // the row's grid, or the grid of a group that began in an earlier block
+    const size_t gi = (size_t)row * ly.ng + (G ? b0 / G : 0);
+    g.s = ly.scales[gi];
     g.r = 1.f / g.s;
-    g.z = (float)ly.zeros[(size_t)row * ly.ng];
+    g.z = (float)ly.zeros[gi];
   }
   __syncthreads();
 

@@ -19,18 +19,19 @@
 
 // Load this thread's 8 tokens x 8 features patch (zero outside the data).
 __device__ __forceinline__ void syk_load(u32x4 (&r)[8], const uint16_t* __restrict__ X,
-                                         long long ldx, int n, int f, int krow, int k1) {
+                                         long long ldx, int n, int vec, int f, int krow, int k1) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int row = krow + t;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (row < k1) {
       const uint16_t* p = X + (long long)row * ldx + f;
-      if (f + 8 <= n) {
+      if (vec && f + 8 <= n) {
         v = *(const u32x4*)p;
       } else if (f < n) {
         unsigned h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int e = 0; e < n - f; ++e) h[e] = p[e];
+        const int m = min(8, n - f);
+        for (int e = 0; e < m; ++e) h[e] = p[e];
         v.x = h[0] | (h[1] << 16);
         v.y = h[2] | (h[3] << 16);
         v.z = h[4] | (h[5] << 16);
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(256, 1) void k_syrk(const SyrkProb* __restrict__ pr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][q][r] = 0.f;
 
-  syk_load(ra, pb.X, pb.ldx, pb.n, fa, tk.k0 + 8 * g, tk.k1);
-  if (!diag) syk_load(rb, pb.X, pb.ldx, pb.n, fb, tk.k0 + 8 * g, tk.k1);
+  syk_load(ra, pb.X, pb.ldx, pb.n, pb.vec, fa, tk.k0 + 8 * g, tk.k1);
+  if (!diag) syk_load(rb, pb.X, pb.ldx, pb.n, pb.vec, fb, tk.k0 + 8 * g, tk.k1);
   syk_store(lds, ra, c, g);
   if (!diag) syk_store(lds + SYK_OPB, rb, c, g);
   __syncthreads();
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(256, 1) void k_syrk(const SyrkProb* __restrict__ pr
     const bool more = s + 1 < nsteps;
     if (more) {
       const int kr = tk.k0 + (s + 1) * 64 + 8 * g;
-      syk_load(ra, pb.X, pb.ldx, pb.n, fa, kr, tk.k1);
-      if (!diag) syk_load(rb, pb.X, pb.ldx, pb.n, fb, kr, tk.k1);
+      syk_load(ra, pb.X, pb.ldx, pb.n, pb.vec, fa, kr, tk.k1);
+      if (!diag) syk_load(rb, pb.X, pb.ldx, pb.n, pb.vec, fb, kr, tk.k1);
     }
     const uint8_t* As = cur;
     const uint8_t* Bs = diag ? cur : cur + SYK_OPB;

@@ -89,8 +89,8 @@ def _specs_small():
     s["lora"] = [LayerSpec("lora", 160, 384, 8192, 3, 0, 128, 1e-4, kind="lowrank", rank=16, seed=4)]
     vit = []
     for blk in range(2):
-        for j, (nm, o, n) in enumerate([("qkv", 288, 96), ("proj", 96, 96), ("fc1", 384, 96),
-                                        ("fc2", 96, 384)]):
+        for j, (nm, o, n) in enumerate([("qkv", 384, 128), ("proj", 128, 128), ("fc1", 384, 128),
+                                        ("fc2", 128, 384)]):
             vit.append(LayerSpec("b%d.%s" % (blk, nm), o, n, 2000, 2, 64, 64, 0.01, decay=0.5,
                                  seed=500 + 4 * blk + j))
     s["vit"] = vit

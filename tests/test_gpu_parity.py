@@ -67,11 +67,16 @@ def test_hessian_bitwise_repeatable(ctx):
     assert torch.equal(a, b)
 
 
-def test_hessian_rejects_bad_ld(ctx):
-    X = _rand_x(64, 30, 1).cuda()  # ldx = 30, not a multiple of 8
-    with pytest.raises(GPTQError) as e:
-        ctx.hessian(X)
-    assert e.value.status == 4
+def test_hessian_unaligned_rows(ctx):
+    X = _rand_x(999, 30, 1)  # ldx = 30: rows not 16-byte aligned
+    Xpad = torch.zeros((999, 37), dtype=torch.int16)
+    Xpad[:, :30] = X
+    H = ctx.hessian(X.cuda())
+    H2 = ctx.hessian(Xpad.cuda(), n=30)
+    torch.cuda.synchronize()
+    Hr = o.hessian(_bits(X))
+    assert np.linalg.norm(np32(H) - Hr) / np.linalg.norm(Hr) <= 1e-5
+    assert torch.equal(H, H2)
 
 
 # ------------------------------------------------------------------- factor --
@@ -126,7 +131,8 @@ def test_factor_nonfinite(ctx):
     (130, 512, 3, 128, 64),
     (64, 384, 2, 64, 64),
     (33, 256, 3, 32, 128),
-    (40, 384, 4, 256, 128),
+    (40, 512, 4, 256, 128),
+    (57, 512, 3, 128, 32),
     (50, 200, 8, 0, 16),
     (70, 256, 2, 16, 32),
 ])
