@@ -169,7 +169,9 @@ struct HessPlan {
 
 // Split every (problem, upper tile) over token slices so that each XCD works
 // on its own slice, then even out the last, partly filled round of each XCD
-// by cutting its items into shorter token ranges.
+// by cutting its items into shorter token ranges.  The cut points of a problem
+// depend on that problem alone, so a layer gets the same bits whether it is
+// quantised alone or in a batch.
 void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, HessPlan& P) {
   struct Item {
     int prob, ti, tj, k0, k1;
@@ -184,6 +186,7 @@ void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, H
     const int nt = cdiv(J.n, 256);
     ntile_of[p] = nt;
     if (J.tokens <= 0 || J.n <= 0) continue;
+    std::vector<std::vector<Item>> own(nxcd);
     const long long chunks = cdiv(J.tokens, 64);
     const int nsl = (int)std::max<long long>(1, std::min<long long>(nxcd, chunks / 32));
     int tix = 0;
@@ -194,31 +197,33 @@ void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, H
           const int k0 = (int)(c0 * 64), k1 = (int)std::min<long long>(c1 * 64, J.tokens);
           if (k1 <= k0) continue;
           const int x = (nsl == nxcd) ? s : (tix + s) % nxcd;
-          lists[x].push_back(Item{(int)p, ti, tj, k0, k1});
+          own[x].push_back(Item{(int)p, ti, tj, k0, k1});
         }
-  }
-  // balance each XCD's last round
-  for (auto& L : lists) {
-    const int M = (int)L.size();
-    if (M == 0) continue;
-    const int rem = M % cus_per_xcd;
-    if (rem == 0) continue;
-    const int first = (M >= cus_per_xcd) ? M - rem : 0;
-    const int cnt = M - first;
-    const int f = std::max(1, cus_per_xcd / cnt);
-    if (f <= 1) continue;
-    std::vector<Item> out(L.begin(), L.begin() + first);
-    for (int i = first; i < M; ++i) {
-      const Item it = L[i];
-      const int ch = cdiv(it.k1 - it.k0, 64);
-      const int pieces = std::min(f, ch);
-      for (int q = 0; q < pieces; ++q) {
-        const int a = it.k0 + (int)((long long)ch * q / pieces) * 64;
-        const int b = std::min(it.k1, it.k0 + (int)((long long)ch * (q + 1) / pieces) * 64);
-        if (b > a) out.push_back(Item{it.prob, it.ti, it.tj, a, b});
+    for (int x = 0; x < nxcd; ++x) {
+      std::vector<Item>& L = own[x];
+      const int M = (int)L.size();
+      const int rem = M % cus_per_xcd;
+      if (M > 0 && rem != 0) {
+        const int first = (M >= cus_per_xcd) ? M - rem : 0;
+        const int cnt = M - first;
+        const int f = std::max(1, cus_per_xcd / cnt);
+        if (f > 1) {
+          std::vector<Item> out(L.begin(), L.begin() + first);
+          for (int i = first; i < M; ++i) {
+            const Item it = L[i];
+            const int ch = cdiv(it.k1 - it.k0, 64);
+            const int pieces = std::min(f, ch);
+            for (int q = 0; q < pieces; ++q) {
+              const int a = it.k0 + (int)((long long)ch * q / pieces) * 64;
+              const int b = std::min(it.k1, it.k0 + (int)((long long)ch * (q + 1) / pieces) * 64);
+              if (b > a) out.push_back(Item{it.prob, it.ti, it.tj, a, b});
+            }
+          }
+          L.swap(out);
+        }
       }
+      lists[x].insert(lists[x].end(), L.begin(), L.end());
     }
-    L.swap(out);
   }
   size_t maxlen = 0;
   for (auto& L : lists) maxlen = std::max(maxlen, L.size());
