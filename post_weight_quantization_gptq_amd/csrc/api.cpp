@@ -351,7 +351,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   Blob b;
   const size_t o_probs = b.add(probs);
   struct L {
-    int kind;  // 0 fill, 1 panel, 2 gemm, 3 trinv, 4 makeu
+    int kind;  // 0 fill, 1 panel, 2 gemm, 4 makeu
     size_t off;
     int nseg, nwg;
   };
@@ -371,25 +371,27 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
       if (jobs[p].H) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 4), 0, 0, 0, 0, 0});
     add_launch(0, s);
   }
+  // Cholesky: outer panels of 256 columns, four 64-column steps each
   for (int k = 0; k < maxnb; ++k) {
-    std::vector<Seg> pan, trl;
+    std::vector<Seg> pan, inner, outer;
     for (int p = 0; p < np; ++p) {
       const int n = jobs[p].n, nb = cdiv(n, 64);
       if (k >= nb) continue;
       pan.push_back(Seg{p, 0, nb - k, k, 0, 0, 0, 0});
-      const int r0 = 64 * (k + 1);
-      if (r0 < n) {
-        const int m = cdiv(n - r0, 64);
-        trl.push_back(Seg{p, 0, m * (m + 1) / 2, GK_CHOL_TRAIL, 64 * k, std::min(64, n - 64 * k), r0, 0});
+      const int k0 = 64 * k, pw = std::min(64, n - k0);
+      const int P0 = (k0 / 256) * 256, P1 = std::min(P0 + 256, n);
+      const int c0 = k0 + pw;
+      if (c0 < P1) {  // rest of the outer panel
+        const int nrow = cdiv(n - c0, 64), ncol = cdiv(P1 - c0, 64);
+        inner.push_back(Seg{p, 0, ncol * nrow - ncol * (ncol - 1) / 2, GK_CHOL_TRAIL, k0, pw, c0, P1});
+      } else if (P1 < n) {  // end of the outer panel: trailing update with K = P1 - P0
+        const int m = cdiv(n - P1, 64);
+        outer.push_back(Seg{p, 0, m * (m + 1) / 2, GK_CHOL_TRAIL, P0, P1 - P0, P1, n});
       }
     }
     add_launch(1, pan);
-    add_launch(2, trl);
-  }
-  {
-    std::vector<Seg> s;
-    for (int p = 0; p < np; ++p) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 64), 0, 0, 0, 0, 0});
-    add_launch(3, s);
+    add_launch(2, inner);
+    add_launch(2, outer);
   }
   for (int s = 64; s < maxn; s *= 2) {
     for (int step = 0; step < 2; ++step) {
@@ -418,7 +420,6 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
       case 0: HIPCHK(c, launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: HIPCHK(c, launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 2: HIPCHK(c, launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3: HIPCHK(c, launch_trinv_diag(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 4: HIPCHK(c, launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
     }
   }

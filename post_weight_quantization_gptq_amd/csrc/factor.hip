@@ -8,9 +8,14 @@
 // U = P C^{-1} P, so one Cholesky and one triangular inverse suffice
 // (2n^3/3 flops instead of 4n^3/3 for Cholesky -> inverse -> Cholesky).
 //
-// Cholesky: right-looking, 64-wide panels (a panel kernel factors the
-// diagonal block in LDS and solves its rows below, then an fp64 MFMA update of
-// the trailing lower triangle).  Inverse: recursive doubling over the diagonal
+// Cholesky: right-looking over 256-wide outer panels, each factored in four
+// 64-wide steps.  A step factors its 64x64 diagonal block (and inverts it)
+// inside one wave with the block in registers, then computes the panel rows
+// below as A_ik L_kk^{-T} on fp64 MFMA and updates the rest of the outer
+// panel; after the outer panel, one fp64 MFMA update with K = 256 reaches the
+// trailing lower triangle (four times less traffic over the trailing matrix
+// than updating it after every 64 columns).  The diagonal inverses L_kk^{-1}
+// are the base of the triangular inverse.  Inverse: recursive doubling over the diagonal
 // blocks, [[A,0],[B,C]]^{-1} = [[A^-1,0],[-C^-1 B A^-1, C^-1]], two fp64 MFMA
 // products per level for all block pairs at once.
 #include "common.h"
@@ -63,13 +68,66 @@ __global__ __launch_bounds__(256) void k_damp_fill(const FacProb* __restrict__ p
 }
 
 // ----------------------------------------------------------- Cholesky -----
-// Panel k: workgroup (k, i) for row blocks i >= k.  Each factors the 64x64
-// diagonal block in LDS (identically), then block k writes it back and every
-// other block solves X C_kk^T = A_ik for its rows.
+// Cholesky and inverse of one 64x64 diagonal block by the whole group.
+// LT is column-major (LT[c][r] = block[r][c], r >= c used), padded with the
+// identity past the block's size.  On return LT holds L (column-major, lower)
+// and YT holds L^{-1} (column-major), *bad the first failing pivot or -1.
+// Step j: every thread forms its row's multiplier l_i = a_ij / sqrt(a_jj) and
+// updates its share of the columns c > j with l_i l_c; the scaled column j is
+// written one step later (no thread reads it again), so one barrier per step.
+__device__ __forceinline__ void leaf_block(double (*LT)[NB + 1], double (*YT)[NB + 1], int* bad) {
+  const int tid = threadIdx.x, i = tid & 63, cq = tid >> 6;
+  double lprev = 0.0;
+  int fail = -1;
+  for (int j = 0; j < NB; ++j) {
+    const double d = LT[j][j];
+    if (!(d > 0.0) || !__builtin_isfinite(d)) {  // uniform: every thread read the same d
+      fail = j;
+      break;
+    }
+    const double sd = sqrt(d);
+    const double inv = 1.0 / sd;
+    const double li = (i > j) ? LT[j][i] * inv : (i == j ? sd : 0.0);
+    for (int c = j + 1 + cq; c < NB; c += 4) {
+      const double lc = LT[j][c] * inv;
+      if (i >= c) LT[c][i] -= li * lc;
+    }
+    if (cq == 0 && j > 0 && i >= j - 1) LT[j - 1][i] = lprev;
+    lprev = li;
+    __syncthreads();
+  }
+  if (fail >= 0) {
+    if (tid == 0) *bad = fail;
+    __syncthreads();
+    return;
+  }
+  if (cq == 0) LT[NB - 1][i] = (i == NB - 1) ? lprev : LT[NB - 1][i];
+  __syncthreads();
+  // inverse: column c = tid/4 of Y = L^{-1}, four lanes split the sum over t
+  const int c = tid >> 2, p = tid & 3;
+  for (int r = 0; r < NB; ++r) {
+    double s = 0.0;
+    for (int t = c + p; t < r; t += 4) s += LT[t][r] * YT[c][t];
+    s += __shfl_xor(s, 1, 4);
+    s += __shfl_xor(s, 2, 4);
+    const double y = (r < c) ? 0.0 : (((r == c) ? 1.0 : 0.0) - s) / LT[r][r];
+    if (p == 0) YT[c][r] = y;
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (tid == 0) *bad = -1;
+  __syncthreads();
+}
+
+// Panel step k (64 columns starting at k0): workgroup (k, i) for row blocks
+// i >= k.  Every group factors the diagonal block (the same way); group k
+// writes L_kk^{-1}, the others compute their rows of the panel as
+// A_ik L_kk^{-T} on fp64 MFMA.
 __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ probs,
                                                     const Seg* __restrict__ segs, int nseg) {
-  __shared__ double D[NB][NB + 1];
-  __shared__ double R[NB][NB + 1];
+  __shared__ double LT[NB][NB + 1];
+  __shared__ double YT[NB][NB + 1];
+  __shared__ double Rs[NB][NB + 1];
+  __shared__ int bad;
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const FacProb pb = probs[sg.prob];
   if (*pb.info != 0 || *pb.nonfinite != 0) return;
@@ -78,56 +136,68 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
   const int tid = threadIdx.x;
   double* A = pb.A;
   for (int e = tid; e < NB * NB; e += 256) {
+    const int r = e >> 6, c = e & 63;  // coalesced over c
+    double v;
+    if (r < m && c < m) v = (c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
+    else v = (r == c) ? 1.0 : 0.0;
+    LT[c][r] = v;
+    YT[c][r] = 0.0;
+  }
+  const int r0 = i * NB, mr = (i == k) ? 0 : min(NB, n - r0);
+  for (int e = tid; e < NB * NB; e += 256) {
     const int r = e >> 6, c = e & 63;
-    D[r][c] = (r < m && c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
+    Rs[r][c] = (r < mr && c < m) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0;
   }
   __syncthreads();
-  for (int j = 0; j < m; ++j) {
-    const double d = D[j][j];
-    if (!(d > 0.0) || !__builtin_isfinite(d)) {
-      // first failing pivot in elimination order: step k0 + j, column n-1-(k0+j) of H
-      if (tid == 0 && i == k) atomicMax(pb.info, n - (k0 + j));
-      return;  // uniform: every thread read the same d
-    }
-    const double sd = sqrt(d);
-    const double inv = 1.0 / sd;
-    __syncthreads();
-    if (tid == 0) D[j][j] = sd;
-    for (int r = j + 1 + tid; r < m; r += 256) D[r][j] *= inv;
-    __syncthreads();
-    const int w = m - j - 1;  // trailing size
-    for (int e = tid; e < w * w; e += 256) {
-      const int r = j + 1 + e / w, c = j + 1 + e % w;
-      if (c <= r) D[r][c] -= D[r][j] * D[c][j];
-    }
-    __syncthreads();
+  leaf_block(LT, YT, &bad);
+  if (bad >= 0) {
+    if (tid == 0 && i == k) atomicMax(pb.info, n - (k0 + bad));
+    return;
   }
   if (i == k) {
+    // Only L_kk^{-1} is kept: nothing reads the diagonal block of L again (the
+    // updates read the panel rows below it, the inverse reads Y_kk), and the
+    // other groups of this launch are still reading A_kk, so A_kk stays as is.
+    // the whole block, zeros above the diagonal included: the inverse's
+    // products read these tiles in full
     for (int e = tid; e < NB * NB; e += 256) {
       const int r = e >> 6, c = e & 63;
-      if (r < m && c <= r) A[(size_t)(k0 + r) * n + k0 + c] = D[r][c];
+      if (r < m && c < m) pb.Y[(size_t)(k0 + r) * n + k0 + c] = (c <= r) ? YT[c][r] : 0.0;
     }
     return;
   }
-  const int r0 = i * NB, mr = min(NB, n - r0);
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    R[r][c] = (r < mr && c < m) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0;
+  // X = R Y^T: X(r, c) = sum_t R[r][t] Y[c][t] = sum_t R[r][t] YT[t][c]
+  const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[a][b][q] = 0.0;
+#pragma unroll 4
+  for (int kk = 0; kk < NB / 4; ++kk) {
+    double av[2], bv[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) av[mi] = Rs[32 * wr + 16 * mi + (lane & 15)][4 * kk + (lane >> 4)];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) bv[ni] = YT[4 * kk + (lane >> 4)][32 * wc + 16 * ni + (lane & 15)];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
   }
-  __syncthreads();
-  // X D^T = R, column by column: X[:, c] = R[:, c] / D[c][c]; R[:, c'] -= X[:, c] D[c'][c]
-  const int rr = tid & 63, part = tid >> 6;
-  for (int c = 0; c < m; ++c) {
-    if (part == 0) R[rr][c] = R[rr][c] / D[c][c];
-    __syncthreads();
-    const double x = R[rr][c];
-    for (int c2 = c + 1 + part; c2 < m; c2 += 4) R[rr][c2] -= x * D[c2][c];
-    __syncthreads();
-  }
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    if (r < mr && c < m) A[(size_t)(r0 + r) * n + k0 + c] = R[r][c];
-  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 32 * wr + 16 * mi + (lane >> 4) + 4 * q;
+        const int c = 32 * wc + 16 * ni + (lane & 15);
+        if (r < mr && c < m) A[(size_t)(r0 + r) * n + k0 + c] = acc[mi][ni][q];
+      }
 }
 
 // --------------------------------------------------- fp64 MFMA products ---
@@ -151,24 +221,28 @@ __global__ __launch_bounds__(256) void k_gemm64(const FacProb* __restrict__ prob
   int mt, nt, kb, ke;
   double alpha, beta;
   if (sg.a == GK_CHOL_TRAIL) {
-    // panel columns [k0, k0 + pw), trailing rows/cols from r0; lower tiles only
-    const int k0 = sg.b, pw = sg.c, r0 = sg.d;
-    int a = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
-    while ((a + 1) * (a + 2) / 2 <= t) ++a;
-    while (a * (a + 1) / 2 > t) --a;
-    const int b = t - a * (a + 1) / 2;
-    const int i0 = r0 + 64 * a, j0 = r0 + 64 * b;
-    A = pb.A + (size_t)i0 * n + k0;
+    // A[i][j] -= sum_{t in [kb, kb+kw)} A[i][t] A[j][t] for the lower tiles of
+    // rows [c0, n) x columns [c0, c1)
+    const int kb0 = sg.b, kw = sg.c, c0 = sg.d, c1 = sg.e;
+    const int nrow = (n - c0 + 63) / 64, ncol = (c1 - c0 + 63) / 64;
+    int b = 0, tt = t;
+    while (b < ncol && tt >= nrow - b) {
+      tt -= nrow - b;
+      ++b;
+    }
+    const int a = b + tt;
+    const int i0 = c0 + 64 * a, j0 = c0 + 64 * b;
+    A = pb.A + (size_t)i0 * n + kb0;
     lda = n;
-    B = pb.A + (size_t)j0 * n + k0;
+    B = pb.A + (size_t)j0 * n + kb0;
     sbk = 1;
     sbj = n;
     C = pb.A + (size_t)i0 * n + j0;
     ldc = n;
     mt = min(64, n - i0);
-    nt = min(64, n - j0);
+    nt = min(64, c1 - j0);
     kb = 0;
-    ke = pw;
+    ke = kw;
     alpha = -1.0;
     beta = 1.0;
   } else {
@@ -278,32 +352,6 @@ __global__ __launch_bounds__(256) void k_gemm64(const FacProb* __restrict__ prob
       }
 }
 
-// ------------------------------------------------ triangular inverse -----
-// Invert every 64x64 diagonal block of C (lower): one thread per column.
-__global__ __launch_bounds__(64) void k_trinv_diag(const FacProb* __restrict__ probs,
-                                                   const Seg* __restrict__ segs, int nseg) {
-  __shared__ double Cs[NB][NB + 1];
-  __shared__ double Ys[NB][NB + 1];
-  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
-  const FacProb pb = probs[sg.prob];
-  if (*pb.info != 0 || *pb.nonfinite != 0) return;
-  const int n = pb.n, b0 = (blockIdx.x - sg.wg0) * NB, m = min(NB, n - b0);
-  const int j = threadIdx.x;
-  for (int r = 0; r < m; ++r) Cs[r][j] = (j <= r && j < m) ? pb.A[(size_t)(b0 + r) * n + b0 + j] : 0.0;
-  __syncthreads();
-  if (j < m) {
-    Ys[j][j] = 1.0 / Cs[j][j];
-    for (int i = j + 1; i < m; ++i) {
-      double s = 0.0;
-      for (int t = j; t < i; ++t) s += Cs[i][t] * Ys[t][j];
-      Ys[i][j] = -s / Cs[i][i];
-    }
-  }
-  __syncthreads();
-  for (int r = 0; r < m; ++r)
-    if (j < m) pb.Y[(size_t)(b0 + r) * n + b0 + j] = (j <= r) ? Ys[r][j] : 0.0;
-}
-
 // U[i][j] = Y[n-1-i][n-1-j] for j >= i (upper), 0 below; fp32.  4 rows per WG.
 __global__ __launch_bounds__(256) void k_make_u(const FacProb* __restrict__ probs,
                                                 const Seg* __restrict__ segs, int nseg) {
@@ -334,5 +382,4 @@ hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st) {
 SEG_LAUNCH(launch_damp_fill, k_damp_fill, 256)
 SEG_LAUNCH(launch_chol_panel, k_chol_panel, 256)
 SEG_LAUNCH(launch_gemm64, k_gemm64, 256)
-SEG_LAUNCH(launch_trinv_diag, k_trinv_diag, 64)
 SEG_LAUNCH(launch_make_u, k_make_u, 256)
