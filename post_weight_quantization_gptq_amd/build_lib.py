@@ -20,7 +20,7 @@ FLAGS = [
     "-shared",
     "-fvisibility=hidden",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
-    "-ffp-contract=fast",
+    "-ffp-contract=on",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]

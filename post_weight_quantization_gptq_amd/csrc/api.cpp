@@ -429,16 +429,25 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
 // ----------------------------------------------------------- quantize plan --
 int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<float*>* Ww_out = nullptr) {
   const int nl = (int)jobs.size();
+  // Super-blocks: each block's errors reach the rest of its super-block right
+  // away, the columns past it only at the super-block's end (one product with
+  // K = the super-block width), so the far columns of W are rewritten once
+  // per super-block instead of once per block.  Groups must nest in it.
+  std::vector<int> sbk(nl);
   size_t totW = 0, totE = 0, totO = 0;
   std::vector<size_t> oW(nl), oE(nl), oO(nl);
   for (int p = 0; p < nl; ++p) {
     const QuantJob& J = jobs[p];
+    int sb = std::max(1, 512 / J.block);
+    const int sbw = sb * J.block;
+    if (J.group && !(sbw % J.group == 0 || J.group % sbw == 0)) sb = 1;
+    sbk[p] = sb;
     oW[p] = totW;
     if (!J.Ww_ext) totW += (size_t)J.out * J.nt;
     oE[p] = totE;
-    totE += (size_t)J.out * J.block;
+    totE += (size_t)J.out * sb * J.block;
     oO[p] = totO;
-    totO += (size_t)J.out * cdiv(J.n, J.block) * 2;
+    totO += (size_t)J.out * 2;
   }
   int rc;
   if ((rc = ensure(c, c->work, totW * sizeof(float)))) return rc;
@@ -468,6 +477,10 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     q.block = J.block;
     q.nblk = cdiv(J.n, J.block);
     q.ng = J.group ? J.n / J.group : 1;
+    q.ldE = sbk[p] * J.block;
+    q.eoff_blk = J.block;
+    q.sbk = sbk[p];
+    q.pad0 = 0;
     L[p] = q;
     maxblk = std::max(maxblk, q.nblk);
     if (Ww_out) Ww_out->push_back(q.Ww);
@@ -512,9 +525,14 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     std::vector<Seg> t;
     for (int p = 0; p < nl; ++p) {
       if (k >= L[p].nblk) continue;
-      const int b1 = std::min((k + 1) * jobs[p].block, jobs[p].n);
-      if (b1 >= jobs[p].nt) continue;
-      t.push_back(Seg{p, 0, cdiv(jobs[p].out, 64) * cdiv(jobs[p].nt - b1, 64), k, 0, 0, 0, 0});
+      const int B = jobs[p].block, n = jobs[p].n, nt = jobs[p].nt, sb = sbk[p];
+      const int b0 = k * B, b1 = std::min(b0 + B, n);
+      const int sb0 = (k / sb) * sb * B, sb1 = std::min(sb0 + sb * B, n);
+      const int mrow = cdiv(jobs[p].out, 128);
+      if (b1 < sb1)  // rest of the super-block
+        t.push_back(Seg{p, 0, mrow * cdiv(sb1 - b1, 128), (k % sb) * B, b0, b1 - b0, b1, sb1});
+      if (b1 == sb1 && sb1 < nt)  // end of the super-block: all columns past it
+        t.push_back(Seg{p, 0, mrow * cdiv(nt - sb1, 128), 0, sb0, sb1 - sb0, sb1, nt});
     }
     add_launch(3, 0, t);
   }

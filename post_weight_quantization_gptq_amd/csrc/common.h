@@ -73,10 +73,14 @@ struct QLayer {
   uint8_t* zeros;   // [out][ng]
   float* err;       // [out][n] or null
   float* Eb;        // block errors [out][block]
-  double* objp;     // per (row, block): {sum E^2, sum D^2}
+  double* objp;     // per row: {sum E^2, sum D^2}, accumulated block by block
   double* obj;      // [2] {J, J_lam} (device)
   const double* lam;  // device slot holding the damping of U
   int out, n, nt, bits, group, block, nblk, ng;
+  int ldE;          // width of the error buffer (one super-block of columns)
+  int eoff_blk;     // column offset of one block inside it (= block)
+  int sbk;          // blocks per super-block
+  int pad0;
 };
 
 __device__ __forceinline__ int find_seg(const Seg* __restrict__ segs, int nseg, int wg) {

@@ -69,52 +69,94 @@ __global__ __launch_bounds__(256) void k_damp_fill(const FacProb* __restrict__ p
 
 // ----------------------------------------------------------- Cholesky -----
 // Cholesky and inverse of one 64x64 diagonal block by the whole group.
-// LT is column-major (LT[c][r] = block[r][c], r >= c used), padded with the
-// identity past the block's size.  On return LT holds L (column-major, lower)
-// and YT holds L^{-1} (column-major), *bad the first failing pivot or -1.
-// Step j: every thread forms its row's multiplier l_i = a_ij / sqrt(a_jj) and
-// updates its share of the columns c > j with l_i l_c; the scaled column j is
-// written one step later (no thread reads it again), so one barrier per step.
-__device__ __forceinline__ void leaf_block(double (*LT)[NB + 1], double (*YT)[NB + 1], int* bad) {
-  const int tid = threadIdx.x, i = tid & 63, cq = tid >> 6;
-  double lprev = 0.0;
+// Thread (tr, tc) = (tid / 16, tid % 16) keeps the 4x4 block of rows
+// 4tr..4tr+3, columns 4tc..4tc+3 in registers.  In: LT column-major
+// (LT[c][r] = block[r][c], r >= c), padded with the identity.  Out: YT =
+// L^{-1} column-major, *bad = first failing pivot or -1.
+// Iteration j: the owners of column j publish it; after one barrier every
+// thread forms l_r = a_rj / sqrt(a_jj) for its rows and columns and applies
+// the rank-1 update.  The inverse runs one column behind in the same loop
+// (Y row t = Z row t / L_tt, then Z rows r > t -= L_rt Y row t), so both
+// share the barrier; column and row broadcasts are double-buffered.
+__device__ __forceinline__ void leaf_block(double (*LT)[NB + 1], double (*YT)[NB + 1], double (*cbuf)[NB],
+                                           double (*ybuf)[NB], int* bad) {
+  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  double a[4][4], z[4][4], lrp[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci) {
+      const int r = 4 * tr + ri, c = 4 * tc + ci;
+      a[ri][ci] = (c <= r) ? LT[c][r] : 0.0;
+      z[ri][ci] = (r == c) ? 1.0 : 0.0;
+    }
+  double inv_prev = 1.0;
   int fail = -1;
-  for (int j = 0; j < NB; ++j) {
-    const double d = LT[j][j];
-    if (!(d > 0.0) || !__builtin_isfinite(d)) {  // uniform: every thread read the same d
-      fail = j;
-      break;
+#pragma unroll
+  for (int j = 0; j <= NB; ++j) {
+    if (j < NB && tc == (j >> 2)) {
+#pragma unroll
+      for (int ri = 0; ri < 4; ++ri) cbuf[j & 1][4 * tr + ri] = a[ri][j & 3];
     }
-    const double sd = sqrt(d);
-    const double inv = 1.0 / sd;
-    const double li = (i > j) ? LT[j][i] * inv : (i == j ? sd : 0.0);
-    for (int c = j + 1 + cq; c < NB; c += 4) {
-      const double lc = LT[j][c] * inv;
-      if (i >= c) LT[c][i] -= li * lc;
+    if (j >= 1 && tr == ((j - 1) >> 2)) {
+#pragma unroll
+      for (int ci = 0; ci < 4; ++ci) {
+        const double y = z[(j - 1) & 3][ci] * inv_prev;
+        z[(j - 1) & 3][ci] = y;
+        ybuf[(j - 1) & 1][4 * tc + ci] = y;
+      }
     }
-    if (cq == 0 && j > 0 && i >= j - 1) LT[j - 1][i] = lprev;
-    lprev = li;
     __syncthreads();
+    double lr[4] = {0.0, 0.0, 0.0, 0.0};
+    if (j < NB) {
+      double d = cbuf[j & 1][j];
+      if (!(d > 0.0) || !__builtin_isfinite(d)) {  // uniform
+        fail = j;
+        break;
+      }
+      // 1/sqrt(d) from the hardware estimate and two Newton steps; sqrt(d) = d/sqrt(d)
+      double inv = __builtin_amdgcn_rsq(d);
+      inv = inv * (1.5 - 0.5 * d * inv * inv);
+      inv = inv * (1.5 - 0.5 * d * inv * inv);
+      const double sd = d * inv;
+      // multipliers, zero outside rows >= j and columns > j, so that the
+      // rank-1 update below needs no per-element test (entries above the
+      // diagonal are never read)
+      double lc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double vr = cbuf[j & 1][4 * tr + q] * inv;
+        const double vc = cbuf[j & 1][4 * tc + q] * inv;
+        lr[q] = (4 * tr + q >= j) ? vr : 0.0;
+        lc[q] = (4 * tc + q > j) ? vc : 0.0;
+      }
+#pragma unroll
+      for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+        for (int ci = 0; ci < 4; ++ci) a[ri][ci] -= lr[ri] * lc[ci];
+      inv_prev = inv;
+    }
+    if (j >= 1) {
+      const int t = j - 1;
+      double yc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) yc[q] = ybuf[t & 1][4 * tc + q];
+#pragma unroll
+      for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+        for (int ci = 0; ci < 4; ++ci) z[ri][ci] -= lrp[ri] * yc[ci];
+    }
+    // L[r][j] for rows r > j (zero otherwise): the next inverse step's factors
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lrp[q] = (4 * tr + q > j) ? lr[q] : 0.0;
   }
-  if (fail >= 0) {
-    if (tid == 0) *bad = fail;
-    __syncthreads();
-    return;
+  if (tid == 0) *bad = fail;
+  if (fail < 0) {
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+      for (int ci = 0; ci < 4; ++ci) YT[4 * tc + ci][4 * tr + ri] = z[ri][ci];
   }
-  if (cq == 0) LT[NB - 1][i] = (i == NB - 1) ? lprev : LT[NB - 1][i];
-  __syncthreads();
-  // inverse: column c = tid/4 of Y = L^{-1}, four lanes split the sum over t
-  const int c = tid >> 2, p = tid & 3;
-  for (int r = 0; r < NB; ++r) {
-    double s = 0.0;
-    for (int t = c + p; t < r; t += 4) s += LT[t][r] * YT[c][t];
-    s += __shfl_xor(s, 1, 4);
-    s += __shfl_xor(s, 2, 4);
-    const double y = (r < c) ? 0.0 : (((r == c) ? 1.0 : 0.0) - s) / LT[r][r];
-    if (p == 0) YT[c][r] = y;
-    __builtin_amdgcn_wave_barrier();
-  }
-  if (tid == 0) *bad = -1;
   __syncthreads();
 }
 
@@ -127,6 +169,8 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
   __shared__ double LT[NB][NB + 1];
   __shared__ double YT[NB][NB + 1];
   __shared__ double Rs[NB][NB + 1];
+  __shared__ double cbuf[2][NB];
+  __shared__ double ybuf[2][NB];
   __shared__ int bad;
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const FacProb pb = probs[sg.prob];
@@ -135,21 +179,26 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
   const int k0 = k * NB, m = min(NB, n - k0);
   const int tid = threadIdx.x;
   double* A = pb.A;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e >> 6, c = e & 63;  // coalesced over c
-    double v;
-    if (r < m && c < m) v = (c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
-    else v = (r == c) ? 1.0 : 0.0;
-    LT[c][r] = v;
-    YT[c][r] = 0.0;
-  }
   const int r0 = i * NB, mr = (i == k) ? 0 : min(NB, n - r0);
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    Rs[r][c] = (r < mr && c < m) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0;
+  {
+    // both 64x64 blocks: 16 + 16 loads per thread, all in flight together
+    double ta[16], tr[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q, r = e >> 6, c = e & 63;  // coalesced over c
+      ta[q] = (r < m && c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
+      tr[q] = (r < mr && c < m) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q, r = e >> 6, c = e & 63;
+      LT[c][r] = (r < m && c < m) ? ta[q] : ((r == c) ? 1.0 : 0.0);
+      YT[c][r] = 0.0;
+      Rs[r][c] = tr[q];
+    }
   }
   __syncthreads();
-  leaf_block(LT, YT, &bad);
+  leaf_block(LT, YT, cbuf, ybuf, &bad);
   if (bad >= 0) {
     if (tid == 0 && i == k) atomicMax(pb.info, n - (k0 + bad));
     return;

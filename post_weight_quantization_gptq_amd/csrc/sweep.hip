@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void k_init_work(const QLayer* __restrict__ L,
   if (row >= ly.out) return;
   for (int c = threadIdx.x & 63; c < ly.nt; c += 64)
     ly.Ww[(size_t)row * ly.nt + c] = c < ly.n ? ly.W[(size_t)row * ly.n + c] : 0.f;
+  if ((threadIdx.x & 63) < 2) ly.objp[(size_t)row * 2 + (threadIdx.x & 63)] = 0.0;
 }
 
 // One grid per row on the original row (group == 0).  One wave per row.
@@ -79,12 +80,112 @@ __global__ __launch_bounds__(256) void k_rowfit(const QLayer* __restrict__ L,
   }
 }
 
+// Broadcast lane SRC of each 16-lane row to the whole row (DPP row_newbcast).
+template <int SRC>
+__device__ __forceinline__ float bcast16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, false));
+}
+
+template <int CPL>
+struct SweepState {
+  float wv[CPL];  // current weights of this lane's columns
+  float dv[CPL];  // 1/U_jj of this lane's columns
+  float qv[CPL];  // codes
+  float hv[CPL];  // dequantised values
+  float ev[CPL];  // scaled errors
+  Grid g;
+  int nextg;      // next group start inside the block (or a large number)
+};
+
+struct SweepCtx {
+  const float* Us;     // LDS U block
+  const float* Wwrow;  // working row (global)
+  float maxq;
+  int B, bw, b0, G, l16, rv;
+  float* scales;
+  uint8_t* zeros;
+  size_t grow;  // row offset into scales/zeros
+};
+
+// Fit the grid of the group starting at in-block column j on the current
+// values of columns [j, j+G) (registers, and the working row past the block).
+template <int CPL>
+__device__ __forceinline__ void fit_group(SweepState<CPL>& st, const SweepCtx& cx, int j) {
+  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int c2 = 0; c2 < CPL; ++c2) {
+    const int lc = CPL * cx.l16 + c2;
+    if (lc >= j && lc < j + cx.G && lc < cx.bw) {
+      mn = fminf(mn, st.wv[c2]);
+      mx = fmaxf(mx, st.wv[c2]);
+    }
+  }
+  if (j + cx.G > cx.B && cx.rv)  // group extends past this block
+    for (int cc = cx.B + cx.l16; cc < j + cx.G; cc += 16) {
+      const float v = cx.Wwrow[cx.b0 + cc];
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+#pragma unroll
+  for (int m = 8; m > 0; m >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, m, 16));
+  }
+  st.g = grid_from(mn, mx, cx.maxq);
+  if (cx.rv && cx.l16 == 0) {
+    const size_t gi = cx.grow + (cx.b0 + j) / cx.G;
+    cx.scales[gi] = st.g.s;
+    cx.zeros[gi] = (uint8_t)st.g.z;
+  }
+}
+
+// The CPL columns owned by lane O of every row group.
+// Groups are multiples of 8 >= CPL columns, so a group can only start at the
+// first column of an owner lane: the check runs once per owner.
+template <int O, int CPL>
+__device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx& cx) {
+  if (O * CPL == st.nextg && O * CPL < cx.bw) {
+    fit_group<CPL>(st, cx, O * CPL);
+    st.nextg += cx.G;
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int j = O * CPL + c;
+    if (j < cx.bw) {
+      const float wj = bcast16<O>(st.wv[c]);
+      const float x = __fadd_rn(__fmul_rn(wj, st.g.r), st.g.z);
+      const float q = fminf(fmaxf(rintf(x), 0.f), cx.maxq);
+      const float what = st.g.s * (q - st.g.z);
+      const float e = (wj - what) * bcast16<O>(st.dv[c]);
+      if (cx.l16 == O) {
+        st.qv[c] = q;
+        st.hv[c] = what;
+        st.ev[c] = e;
+      }
+      const float* urow = cx.Us + j * cx.B + CPL * cx.l16;
+#pragma unroll
+      for (int c2 = 0; c2 < CPL; ++c2) st.wv[c2] = fmaf(-e, urow[c2], st.wv[c2]);
+    }
+  }
+}
+
+template <int O, int CPL>
+struct SweepAll {
+  __device__ __forceinline__ static void run(SweepState<CPL>& st, const SweepCtx& cx) {
+    sweep_owner<O, CPL>(st, cx);
+    SweepAll<O + 1, CPL>::run(st, cx);
+  }
+};
+template <int CPL>
+struct SweepAll<16, CPL> {
+  __device__ __forceinline__ static void run(SweepState<CPL>&, const SweepCtx&) {}
+};
+
 template <int CPL>
 __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
                                                const Seg* __restrict__ segs, int nseg) {
   constexpr int B = 16 * CPL;
   __shared__ __attribute__((aligned(16))) float Us[B * B];
-  __shared__ float dinv[B];
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const QLayer ly = L[sg.prob];
   const int blk = sg.a;
@@ -94,95 +195,85 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   const int row = (blockIdx.x - sg.wg0) * 16 + w * 4 + (lane >> 4);
   const bool rv = row < ly.out;
   const int nt = ly.nt, G = ly.group;
-  const float maxq = (float)((1 << ly.bits) - 1);
 
-  for (int e = tid; e < B * B; e += 256) {
-    const int j = e / B, k = e % B;
-    Us[e] = (j < bw && k < bw) ? ly.U[(size_t)(b0 + j) * nt + b0 + k] : 0.f;
+  {
+    // U block -> LDS: all loads of a thread in flight at once, 16 B each
+    constexpr int PER = (B * B / 4 + 255) / 256;
+    const bool vec = (nt % 4) == 0 && bw == B;
+    f32x4 tmp[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = tid + 256 * q;
+      const int j = idx / (B / 4), k4 = (idx % (B / 4)) * 4;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (idx < B * B / 4 && j < bw) {
+        const float* src = ly.U + (size_t)(b0 + j) * nt + b0 + k4;
+        if (vec) {
+          v = *(const f32x4*)src;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = (k4 + u < bw) ? src[u] : 0.f;
+        }
+      }
+      tmp[q] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = tid + 256 * q;
+      if (idx < B * B / 4) *(f32x4*)&Us[idx * 4] = tmp[q];
+    }
   }
-  for (int j = tid; j < B; j += 256) dinv[j] = j < bw ? 1.f / ly.U[(size_t)(b0 + j) * nt + b0 + j] : 0.f;
 
-  float wv[CPL], wo[CPL], qv[CPL], ev[CPL];
+  SweepState<CPL> st;
+  float wo[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int lc = CPL * l16 + c;
     const bool in = rv && lc < bw;
-    wv[c] = in ? ly.Ww[(size_t)row * nt + b0 + lc] : 0.f;
+    st.wv[c] = in ? ly.Ww[(size_t)row * nt + b0 + lc] : 0.f;
+    st.dv[c] = (lc < bw) ? 1.f / ly.U[(size_t)(b0 + lc) * nt + b0 + lc] : 0.f;
     wo[c] = in ? ly.W[(size_t)row * ly.n + b0 + lc] : 0.f;
-    qv[c] = 0.f;
-    ev[c] = 0.f;
+    st.qv[c] = 0.f;
+    st.hv[c] = 0.f;
+    st.ev[c] = 0.f;
   }
-  Grid g = {1.f, 1.f, 0.f};
+  st.g = Grid{1.f, 1.f, 0.f};
   if (rv && (G == 0 || (b0 % G) != 0)) {
     // the row's grid, or the grid of a group that began in an earlier block
     const size_t gi = (size_t)row * ly.ng + (G ? b0 / G : 0);
-    g.s = ly.scales[gi];
-    g.r = 1.f / g.s;
-    g.z = (float)ly.zeros[gi];
+    st.g.s = ly.scales[gi];
+    st.g.r = 1.f / st.g.s;
+    st.g.z = (float)ly.zeros[gi];
   }
+  st.nextg = (G == 0) ? (1 << 30) : ((b0 % G) == 0 ? 0 : G - (b0 % G));
+  SweepCtx cx;
+  cx.Us = Us;
+  cx.Wwrow = ly.Ww + (size_t)(rv ? row : 0) * nt;
+  cx.maxq = (float)((1 << ly.bits) - 1);
+  cx.B = B;
+  cx.bw = bw;
+  cx.b0 = b0;
+  cx.G = G;
+  cx.l16 = l16;
+  cx.rv = rv;
+  cx.scales = ly.scales;
+  cx.zeros = ly.zeros;
+  cx.grow = (size_t)(rv ? row : 0) * ly.ng;
   __syncthreads();
 
-  double se = 0.0, sd = 0.0;
-  for (int o = 0; o < 16; ++o) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int j = o * CPL + c;
-      if (j < bw) {
-        if (G != 0 && ((b0 + j) % G) == 0) {
-          // fit the group's grid on its current values [b0+j, b0+j+G)
-          float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-#pragma unroll
-          for (int c2 = 0; c2 < CPL; ++c2) {
-            const int lc = CPL * l16 + c2;
-            if (lc >= j && lc < j + G && lc < bw) {
-              mn = fminf(mn, wv[c2]);
-              mx = fmaxf(mx, wv[c2]);
-            }
-          }
-          if (j + G > B && rv)  // group extends past this block (group > block)
-            for (int cc = B + l16; cc < j + G; cc += 16) {
-              const float v = ly.Ww[(size_t)row * nt + b0 + cc];
-              mn = fminf(mn, v);
-              mx = fmaxf(mx, v);
-            }
-#pragma unroll
-          for (int m = 8; m > 0; m >>= 1) {
-            mn = fminf(mn, __shfl_xor(mn, m, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, m, 16));
-          }
-          g = grid_from(mn, mx, maxq);
-          if (rv && l16 == 0) {
-            const size_t gi = (size_t)row * ly.ng + (b0 + j) / G;
-            ly.scales[gi] = g.s;
-            ly.zeros[gi] = (uint8_t)g.z;
-          }
-        }
-        const float wj = __shfl(wv[c], o, 16);
-        const float x = __fadd_rn(__fmul_rn(wj, g.r), g.z);
-        const float q = fminf(fmaxf(rintf(x), 0.f), maxq);
-        const float what = g.s * (q - g.z);
-        const float e = (wj - what) * dinv[j];
-        if (l16 == o) {
-          qv[c] = q;
-          ev[c] = e;
-          const float d = wo[c] - what;
-          sd += (double)d * (double)d;
-          se += (double)e * (double)e;
-        }
-        const float* urow = Us + j * B + CPL * l16;
-#pragma unroll
-        for (int c2 = 0; c2 < CPL; ++c2) wv[c2] = fmaf(-e, urow[c2], wv[c2]);
-      }
-    }
-  }
+  SweepAll<0, CPL>::run(st, cx);
 
+  double se = 0.0, sd = 0.0;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int lc = CPL * l16 + c;
     if (rv && lc < bw) {
-      ly.codes[(size_t)row * ly.n + b0 + lc] = (uint8_t)qv[c];
-      ly.Eb[(size_t)row * B + lc] = ev[c];
-      if (ly.err) ly.err[(size_t)row * ly.n + b0 + lc] = ev[c];
+      ly.codes[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
+      ly.Eb[(size_t)row * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
+      if (ly.err) ly.err[(size_t)row * ly.n + b0 + lc] = st.ev[c];
+      const double d = (double)wo[c] - (double)st.hv[c];
+      sd += d * d;
+      se += (double)st.ev[c] * (double)st.ev[c];
     }
   }
 #pragma unroll
@@ -191,53 +282,112 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
     sd += __shfl_xor(sd, m, 16);
   }
   if (rv && l16 == 0) {
-    double* op = ly.objp + ((size_t)row * ly.nblk + blk) * 2;
-    op[0] = se;
-    op[1] = sd;
+    // per-row sums, accumulated over the blocks in block order
+    double* op = ly.objp + (size_t)row * 2;
+    op[0] += se;
+    op[1] += sd;
   }
 }
 
-// W[:, b1:nt] -= E[:, 0:K] U[b0:b1, b1:nt] for one 64x64 tile, K <= 128,
-// on v_mfma_f32_32x32x2f32 (4 waves of 32x32).
-__global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L,
-                                               const Seg* __restrict__ segs, int nseg) {
-  __shared__ float As[64][129];
-  __shared__ float Bs[128][65];
+// W[:, j0:j1] -= E[:, eoff:eoff+K] U[kb:kb+K, j0:j1] for one 128x128 tile, in
+// K chunks of 128, on v_mfma_f32_32x32x2f32 (4 waves of 64x64).
+__global__ __launch_bounds__(256, 1) void k_trail(const QLayer* __restrict__ L,
+                                                  const Seg* __restrict__ segs, int nseg) {
+  __shared__ float As[128][129];
+  __shared__ __attribute__((aligned(16))) float Bs[128][132];
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const QLayer ly = L[sg.prob];
-  const int blk = sg.a, B = ly.block;
-  const int b0 = blk * B, b1 = min(b0 + B, ly.n), K = b1 - b0;
+  const int eoff = sg.a, kb = sg.b, K = sg.c, j0 = sg.d, j1 = sg.e;
   const int nt = ly.nt;
-  const int tiles_j = (nt - b1 + 63) / 64;
+  const int tiles_j = (j1 - j0 + 127) / 128;
   const int t = blockIdx.x - sg.wg0;
-  const int i0 = 64 * (t / tiles_j), j0 = b1 + 64 * (t % tiles_j);
-  const int mt = min(64, ly.out - i0), ntc = min(64, nt - j0);
+  const int i0 = 128 * (t / tiles_j), jj0 = j0 + 128 * (t % tiles_j);
+  const int mt = min(128, ly.out - i0), ntc = min(128, j1 - jj0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int e = tid; e < 64 * 128; e += 256) {
-    const int r = e >> 7, k = e & 127;
-    As[r][k] = (r < mt && k < K) ? ly.Eb[(size_t)(i0 + r) * B + k] : 0.f;
-  }
-  for (int e = tid; e < 128 * 64; e += 256) {
-    const int k = e >> 6, j = e & 63;
-    Bs[k][j] = (k < K && j < ntc) ? ly.U[(size_t)(b0 + k) * nt + j0 + j] : 0.f;
-  }
-  __syncthreads();
   const int wr = w >> 1, wc = w & 1;
-  f32x16 acc;
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int ksteps = (K + 1) >> 1;
-  for (int kk = 0; kk < ksteps; ++kk) {
-    const float a = As[32 * wr + (lane & 31)][2 * kk + (lane >> 5)];
-    const float b = Bs[2 * kk + (lane >> 5)][32 * wc + (lane & 31)];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  for (int kc = 0; kc < K; kc += 128) {
+    const int kw = min(128, K - kc);
+    {
+      // E chunk (128 rows x 128 k) and U chunk (128 k x 128 cols): 16 + 16
+      // loads of 16 B per thread, all in flight before any LDS store
+      const bool evec = (ly.ldE % 4) == 0 && ((eoff + kc) % 4) == 0;
+      const bool uvec = (nt % 4) == 0 && (jj0 % 4) == 0;
+      f32x4 ta[16], tb[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int idx = tid + 256 * q;
+        const int r = idx >> 5, k4 = (idx & 31) * 4;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (r < mt) {
+          const float* src = ly.Eb + (size_t)(i0 + r) * ly.ldE + eoff + kc + k4;
+          if (evec && k4 + 4 <= kw) {
+            v = *(const f32x4*)src;
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = (k4 + u < kw) ? src[u] : 0.f;
+          }
+        }
+        ta[q] = v;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int idx = tid + 256 * q;
+        const int k = idx >> 5, jq = (idx & 31) * 4;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (k < kw) {
+          const float* src = ly.U + (size_t)(kb + kc + k) * nt + jj0 + jq;
+          if (uvec && jq + 4 <= ntc) {
+            v = *(const f32x4*)src;
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = (jq + u < ntc) ? src[u] : 0.f;
+          }
+        }
+        tb[q] = v;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int idx = tid + 256 * q;
+        const int r = idx >> 5, k4 = (idx & 31) * 4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) As[r][k4 + u] = ta[q][u];
+        const int k = idx >> 5, jq = (idx & 31) * 4;
+        *(f32x4*)&Bs[k][jq] = tb[q];
+      }
+    }
+    __syncthreads();
+    const int ksteps = (kw + 1) >> 1;
+    for (int kk = 0; kk < ksteps; ++kk) {
+      float av[2], bv[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) av[mi] = As[64 * wr + 32 * mi + (lane & 31)][2 * kk + (lane >> 5)];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) bv[ni] = Bs[2 * kk + (lane >> 5)][64 * wc + 32 * ni + (lane & 31)];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+    }
+    __syncthreads();
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = 32 * wr + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    const int j = 32 * wc + (lane & 31);
-    if (i < mt && j < ntc) ly.Ww[(size_t)(i0 + i) * nt + j0 + j] -= acc[r];
-  }
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = 64 * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int j = 64 * wc + 32 * ni + (lane & 31);
+        if (i < mt && j < ntc) ly.Ww[(size_t)(i0 + i) * nt + jj0 + j] -= acc[mi][ni][r];
+      }
 }
 
 // J_lam = sum E^2, ||D||^2 (plus the appended columns, whose final values are
@@ -249,8 +399,7 @@ __global__ __launch_bounds__(256) void k_objective(const QLayer* __restrict__ L,
   const QLayer ly = L[p];
   const int tid = threadIdx.x;
   double se = 0.0, sd = 0.0;
-  const long long np = (long long)ly.out * ly.nblk;
-  for (long long i = tid; i < np; i += 256) {
+  for (long long i = tid; i < ly.out; i += 256) {
     se += ly.objp[2 * i];
     sd += ly.objp[2 * i + 1];
   }
