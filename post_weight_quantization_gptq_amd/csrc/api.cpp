@@ -34,7 +34,7 @@ struct gptq_ctx_s {
   int ncu = 256;
   int nxcd = 8;
   std::string err;
-  DevBuf partials, facA, facY, facT, work, eblk, objp, slots, blob, lora;
+  DevBuf partials, xt, facA, facY, facT, work, eblk, objp, slots, blob, lora;
   void* hblob = nullptr;  // pinned staging for the task tables
   size_t hblob_cap = 0;
   void* hsmall = nullptr;  // pinned read-back area
@@ -159,6 +159,8 @@ struct HessJob {
 };
 
 struct HessPlan {
+  std::vector<XposeProb> xprobs;
+  std::vector<Seg> xsegs;
   std::vector<SyrkProb> probs;
   std::vector<SyrkTask> tasks;
   std::vector<RedProb> rprobs;
@@ -172,7 +174,7 @@ struct HessPlan {
 // by cutting its items into shorter token ranges.  The cut points of a problem
 // depend on that problem alone, so a layer gets the same bits whether it is
 // quantised alone or in a batch.
-void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, HessPlan& P) {
+void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, uint16_t* xt, HessPlan& P) {
   struct Item {
     int prob, ti, tj, k0, k1;
   };
@@ -181,20 +183,24 @@ void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, H
   for (size_t p = 0; p < jobs.size(); ++p) {
     const HessJob& J = jobs[p];
     const int vec = (J.ldx % 8 == 0) && (((uintptr_t)J.X & 15) == 0);
-    P.probs.push_back(SyrkProb{J.X, J.ldx, J.n, vec});
-    P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate});
     const int nt = cdiv(J.n, 256);
+    const long long chunks = cdiv(J.tokens, 64);
+    const int n_pad = nt * 256, t_pad = (int)(chunks * 64);
+    P.xprobs.push_back(XposeProb{J.X, J.ldx, xt, J.n, (int)J.tokens, n_pad, t_pad, vec, 0});
+    if (t_pad > 0) P.xsegs.push_back(Seg{(int)p, 0, (t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
+    P.probs.push_back(SyrkProb{xt, t_pad});
+    xt += (size_t)n_pad * t_pad;
+    P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate});
     ntile_of[p] = nt;
     if (J.tokens <= 0 || J.n <= 0) continue;
     std::vector<std::vector<Item>> own(nxcd);
-    const long long chunks = cdiv(J.tokens, 64);
     const int nsl = (int)std::max<long long>(1, std::min<long long>(nxcd, chunks / 32));
     int tix = 0;
     for (int ti = 0; ti < nt; ++ti)
       for (int tj = ti; tj < nt; ++tj, ++tix)
         for (int s = 0; s < nsl; ++s) {
           const long long c0 = chunks * s / nsl, c1 = chunks * (s + 1) / nsl;
-          const int k0 = (int)(c0 * 64), k1 = (int)std::min<long long>(c1 * 64, J.tokens);
+          const int k0 = (int)(c0 * 64), k1 = (int)(c1 * 64);  // zero-padded past tokens
           if (k1 <= k0) continue;
           const int x = (nsl == nxcd) ? s : (tix + s) % nxcd;
           own[x].push_back(Item{(int)p, ti, tj, k0, k1});
@@ -270,16 +276,27 @@ void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, H
 }
 
 int run_hessian(gptq_ctx c, const std::vector<HessJob>& jobs) {
-  HessPlan P;
-  plan_hessian(jobs, c->nxcd, std::max(1, c->ncu / c->nxcd), P);
-  int rc = ensure(c, c->partials, (size_t)std::max(P.nparts, 1) * 65536 * sizeof(float));
+  size_t xt_elems = 0;
+  for (const HessJob& J : jobs) xt_elems += (size_t)cdiv(J.n, 256) * 256 * (size_t)cdiv(J.tokens, 64) * 64;
+  int rc = ensure(c, c->xt, xt_elems * sizeof(uint16_t));
   if (rc) return rc;
+  HessPlan P;
+  plan_hessian(jobs, c->nxcd, std::max(1, c->ncu / c->nxcd), (uint16_t*)c->xt.p, P);
+  if ((rc = ensure(c, c->partials, (size_t)std::max(P.nparts, 1) * 65536 * sizeof(float)))) return rc;
+  int nxwg = 0;
+  for (auto& sg : P.xsegs) {
+    sg.wg0 = nxwg;
+    nxwg += sg.nwg;
+  }
   Blob b;
+  const size_t o_xprobs = b.add(P.xprobs), o_xsegs = b.add(P.xsegs);
   const size_t o_probs = b.add(P.probs), o_tasks = b.add(P.tasks), o_rprobs = b.add(P.rprobs),
                o_rtasks = b.add(P.rtasks), o_plist = b.add(P.partlist);
   uint8_t* d = nullptr;
   rc = upload(c, b, &d);
   if (rc) return rc;
+  HIPCHK(c, launch_xpose((const XposeProb*)(d + o_xprobs), (const Seg*)(d + o_xsegs), (int)P.xsegs.size(), nxwg,
+                         c->stream));
   HIPCHK(c, launch_syrk((const SyrkProb*)(d + o_probs), (const SyrkTask*)(d + o_tasks),
                         (int)P.tasks.size(), (float*)c->partials.p, c->stream));
   HIPCHK(c, launch_syrk_reduce((const RedProb*)(d + o_rprobs), (const RedTask*)(d + o_rtasks),
@@ -620,7 +637,7 @@ GPTQ_API int gptq_destroy(gptq_ctx c) {
   {
     DeviceGuard g(c->device);
     (void)hipStreamSynchronize(c->stream);
-    DevBuf* bufs[] = {&c->partials, &c->facA, &c->facY, &c->facT, &c->work, &c->eblk,
+    DevBuf* bufs[] = {&c->partials, &c->xt, &c->facA, &c->facY, &c->facT, &c->work, &c->eblk,
                       &c->objp, &c->slots, &c->blob, &c->lora};
     for (DevBuf* b : bufs)
       if (b->p) (void)hipFree(b->p);

@@ -22,11 +22,17 @@ struct Seg {
 
 // ---------------------------------------------------------------- Hessian --
 // One 256x256 output tile of H over the token range [k0, k1) -> partial slot.
-struct SyrkProb {
+struct XposeProb {
   const uint16_t* X;
   long long ldx;
-  int n;
-  int vec;  // rows are 16-byte aligned (16-byte loads allowed)
+  uint16_t* Xt;  // [n_pad][t_pad]
+  int n, tokens, n_pad, t_pad;
+  int vec;  // rows of X are 16-byte aligned (16-byte loads allowed)
+  int pad0;
+};
+struct SyrkProb {
+  const uint16_t* Xt;  // feature-major copy [n_pad][t_pad], zero-padded
+  long long t_pad;
 };
 struct SyrkTask {
   int prob, ti, tj, k0, k1, part, pad0, pad1;

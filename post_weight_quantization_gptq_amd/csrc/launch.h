@@ -3,6 +3,7 @@
 #include "common.h"
 
 // Hessian
+hipError_t launch_xpose(const XposeProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
 hipError_t launch_syrk(const SyrkProb* probs, const SyrkTask* tasks, int ntasks, float* partials,
                        hipStream_t st);
 hipError_t launch_syrk_reduce(const RedProb* probs, const RedTask* tasks, int ntasks,

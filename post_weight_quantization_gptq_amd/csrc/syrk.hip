@@ -4,8 +4,10 @@
 // Quantization, technical overview section 3.1; GPTQ-2D technical summary
 // section 1) is a dense contraction over tokens with both operands stored
 // feature-contiguous ([tokens, n] rows).  The MFMA wants 8 consecutive tokens
-// per lane, so every 8x8 (token x feature) patch a thread loads is transposed
-// in registers with byte permutes and written to LDS feature-major.
+// per lane, so X is first copied once, transposed and zero-padded, into a
+// feature-major workspace (one bandwidth-bound pass); every tile of the
+// contraction then moves 16-byte rows straight into LDS in the order the
+// MFMA reads them, with no per-tile transposition or bounds checks.
 //
 // Work split: one workgroup = one 256x256 upper tile of H over a token range;
 // the planner gives each XCD its own slice of tokens, so the workgroups that
@@ -14,64 +16,78 @@
 #include "common.h"
 #include "launch.h"
 
-#define SYK_ROW 144              // LDS bytes per feature row: 64 tokens + 16 B pad
-#define SYK_OPB (256 * SYK_ROW)  // LDS bytes per operand tile
 
-// Load this thread's 8 tokens x 8 features patch (zero outside the data).
-__device__ __forceinline__ void syk_load(u32x4 (&r)[8], const uint16_t* __restrict__ X,
-                                         long long ldx, int n, int vec, int f, int krow, int k1) {
+// Transposed, zero-padded copy of X: Xt[f][t] for f < n_pad, t < t_pad (a
+// multiple of 64 tokens).  One 64 x 64 (token x feature) tile per group: rows
+// of X come in with 16-byte loads, go out feature-major with 16-byte stores.
+__global__ __launch_bounds__(256) void k_xpose(const XposeProb* __restrict__ probs,
+                                               const Seg* __restrict__ segs, int nseg) {
+  __shared__ uint16_t T[64][64 + 8];
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const XposeProb pb = probs[sg.prob];
+  const int t = blockIdx.x - sg.wg0;
+  const int fblocks = pb.n_pad / 64;
+  const int t0 = 64 * (t / fblocks), f0 = 64 * (t % fblocks);
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int row = krow + t;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < k1) {
-      const uint16_t* p = X + (long long)row * ldx + f;
-      if (vec && f + 8 <= n) {
-        v = *(const u32x4*)p;
-      } else if (f < n) {
-        unsigned h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        const int m = min(8, n - f);
-        for (int e = 0; e < m; ++e) h[e] = p[e];
-        v.x = h[0] | (h[1] << 16);
-        v.y = h[2] | (h[3] << 16);
-        v.z = h[4] | (h[5] << 16);
-        v.w = h[6] | (h[7] << 16);
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + 256 * q;
+    const int r = idx >> 3, c8 = (idx & 7) * 8;  // token row r, features c8..c8+7
+    const int tok = t0 + r, f = f0 + c8;
+    unsigned h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (tok < pb.tokens && f < pb.n) {
+      const uint16_t* src = pb.X + (long long)tok * pb.ldx + f;
+      if (pb.vec && f + 8 <= pb.n) {
+        const u32x4 v = *(const u32x4*)src;
+        h[0] = v.x & 0xffff; h[1] = v.x >> 16; h[2] = v.y & 0xffff; h[3] = v.y >> 16;
+        h[4] = v.z & 0xffff; h[5] = v.z >> 16; h[6] = v.w & 0xffff; h[7] = v.w >> 16;
+      } else {
+        for (int e = 0; e < 8 && f + e < pb.n; ++e) h[e] = src[e];
       }
     }
-    r[t] = v;
-  }
-}
-
-// Transpose the 8x8 patch (token-major in r[t]) and store feature-major:
-// feature row (8c + e), tokens [8g, 8g + 8).
-__device__ __forceinline__ void syk_store(uint8_t* lds, const u32x4 (&r)[8], int c, int g) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    // low halves of an even/odd token pair for even e, high halves for odd e
-    const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 o;
-    o.x = __builtin_amdgcn_perm(r[1][e >> 1], r[0][e >> 1], sel);
-    o.y = __builtin_amdgcn_perm(r[3][e >> 1], r[2][e >> 1], sel);
-    o.z = __builtin_amdgcn_perm(r[5][e >> 1], r[4][e >> 1], sel);
-    o.w = __builtin_amdgcn_perm(r[7][e >> 1], r[6][e >> 1], sel);
-    *(u32x4*)(lds + (8 * c + e) * SYK_ROW + 16 * g) = o;
+    for (int e = 0; e < 8; ++e) T[c8 + e][r] = (uint16_t)h[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + 256 * q;
+    const int f = idx >> 3, r8 = (idx & 7) * 8;  // feature f, tokens r8..r8+7
+    const u32x4 o = *(const u32x4*)&T[f][r8];
+    *(u32x4*)(pb.Xt + (size_t)(f0 + f) * pb.t_pad + t0 + r8) = o;
   }
 }
 
-__global__ __launch_bounds__(256, 1) void k_syrk(const SyrkProb* __restrict__ probs,
+// One 256x256 upper tile of H over the token range [k0, k1) of Xt (both
+// multiples of 64; the copy is zero-padded, so no bounds are checked).
+// Per 64-token step each operand is a 256-row x 128-byte tile in LDS.  The
+// rows travel from L2 straight into LDS (global_load_lds, 16 B per lane, no
+// registers in between) while the previous step is multiplied; inside a row
+// the 16-byte token chunks are stored XOR-swizzled by (row % 8), so the
+// fragment reads of 32 consecutive rows hit all LDS banks.
+#define SYK_STAGE (2 * 256 * 128)  // bytes per stage (two operands)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_syrk(const SyrkProb* __restrict__ probs,
                                                  const SyrkTask* __restrict__ tasks,
                                                  float* __restrict__ partials) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * SYK_OPB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SYK_STAGE];
   const SyrkTask tk = tasks[blockIdx.x];
   if (tk.part < 0) return;
   const SyrkProb pb = probs[tk.prob];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = tid & 7, c = tid >> 3;
-  const int fa = tk.ti * 256 + 8 * c, fb = tk.tj * 256 + 8 * c;
   const bool diag = tk.ti == tk.tj;
-  const int nsteps = (tk.k1 - tk.k0 + 63) >> 6;
+  const int nsteps = (tk.k1 - tk.k0) >> 6;
+  const size_t tp = (size_t)pb.t_pad;
+  // Load slot of this lane: instruction q of wave w fills LDS rows
+  // 8(4q+w) .. 8(4q+w)+7; lane -> row 8(4q+w) + lane/8, chunk position lane%8,
+  // holding token chunk (lane%8) ^ (row%8).
+  const int lrow = 8 * w + (lane >> 3);
+  const int tchunk = (lane & 7) ^ ((lane >> 3) & 7);
+  const uint16_t* ga = pb.Xt + (size_t)(tk.ti * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
+  const uint16_t* gb = pb.Xt + (size_t)(tk.tj * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
 
-  u32x4 ra[8], rb[8];
   f32x16 acc[4][4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
@@ -80,46 +96,62 @@ __global__ __launch_bounds__(256, 1) void k_syrk(const SyrkProb* __restrict__ pr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][q][r] = 0.f;
 
-  syk_load(ra, pb.X, pb.ldx, pb.n, pb.vec, fa, tk.k0 + 8 * g, tk.k1);
-  if (!diag) syk_load(rb, pb.X, pb.ldx, pb.n, pb.vec, fb, tk.k0 + 8 * g, tk.k1);
-  syk_store(lds, ra, c, g);
-  if (!diag) syk_store(lds + SYK_OPB, rb, c, g);
-  __syncthreads();
-
+  auto issue = [&](int step, int stage) {
+    uint8_t* base = lds + stage * SYK_STAGE;
+    const size_t off = (size_t)step * 64;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(ga + (size_t)(32 * q) * tp + off),
+                                       (lds_void*)(base + (4 * q + w) * 1024), 16, 0, 0);
+    if (!diag) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(gb + (size_t)(32 * q) * tp + off),
+                                         (lds_void*)(base + 256 * 128 + (4 * q + w) * 1024), 16, 0, 0);
+    }
+  };
   const int arow = 128 * (w >> 1) + (lane & 31);
   const int brow = 128 * (w & 1) + (lane & 31);
-  const int koff = 16 * (lane >> 5);
+  const int sw = lane & 7;  // = row % 8 for every fragment row of this lane
+
+  if (nsteps > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
-    const uint8_t* cur = lds + (s & 1) * 2 * SYK_OPB;
-    uint8_t* nxt = lds + ((s + 1) & 1) * 2 * SYK_OPB;
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      const int kr = tk.k0 + (s + 1) * 64 + 8 * g;
-      syk_load(ra, pb.X, pb.ldx, pb.n, pb.vec, fa, kr, tk.k1);
-      if (!diag) syk_load(rb, pb.X, pb.ldx, pb.n, pb.vec, fb, kr, tk.k1);
+    if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
+    const uint8_t* As = lds + (s & 1) * SYK_STAGE;
+    const uint8_t* Bs = diag ? As : As + 256 * 128;
+    // fragments of sub-step ks+1 are requested before the MFMAs of ks
+    bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 5; ++ks) {
+      if (ks < 4) {
+        const int ch = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) fa[ks & 1][m] = *(const bf16x8*)(As + (arow + 32 * m) * 128 + ch);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) fb[ks & 1][q] = *(const bf16x8*)(Bs + (brow + 32 * q) * 128 + ch);
+      }
+      if (ks > 0) {
+        const int u = (ks - 1) & 1;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[m][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[u][m], fb[u][q], acc[m][q], 0, 0, 0);
+      }
     }
-    const uint8_t* As = cur;
-    const uint8_t* Bs = diag ? cur : cur + SYK_OPB;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        a[m] = *(const bf16x8*)(As + (arow + 32 * m) * SYK_ROW + ks * 32 + koff);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        b[q] = *(const bf16x8*)(Bs + (brow + 32 * q) * SYK_ROW + ks * 32 + koff);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc[m][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], b[q], acc[m][q], 0, 0, 0);
-    }
-    if (more) {
-      syk_store(nxt, ra, c, g);
-      if (!diag) syk_store(nxt + SYK_OPB, rb, c, g);
-    }
-    __syncthreads();
+    // keep the order: reads of sub-step 0; then (reads of k+1, MFMAs of k)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of step s+1 have landed
+    __syncthreads();                // ... and everybody's; stage s&1 is free again
   }
 
   float* P = partials + (size_t)tk.part * 65536;
@@ -148,12 +180,22 @@ __global__ __launch_bounds__(256) void k_syrk_reduce(const RedProb* __restrict__
   const int tid = threadIdx.x, n = pb.n;
   const int lr0 = tk.r0 & 255, lc0 = tk.c0 & 255;
   const int cc = tid & 63;
+  float sum[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) sum[q] = 0.f;
+  for (int p = 0; p < tk.nparts; ++p) {  // parts in list order, 16 loads in flight
+    const float* src = partials + (size_t)partlist[tk.part0 + p] * 65536 + (lr0 + (tid >> 6)) * 256 + lc0 + cc;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = src[4 * q * 256];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sum[q] += v[q];
+  }
+#pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int rr = (tid >> 6) + 4 * q;
-    float s = 0.f;
-    for (int p = 0; p < tk.nparts; ++p)
-      s += partials[(size_t)partlist[tk.part0 + p] * 65536 + (lr0 + rr) * 256 + lc0 + cc];
     const int i = tk.r0 + rr, j = tk.c0 + cc;
+    float s = sum[q];
     if (pb.accumulate && i < n && j < n && i <= j) s += pb.H[(size_t)i * n + j];
     S[rr][cc] = s;
   }
@@ -176,6 +218,12 @@ __global__ void k_zero_f32(float* __restrict__ p, long long count) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long stride = (long long)gridDim.x * blockDim.x;
   for (; i < count; i += stride) p[i] = 0.f;
+}
+
+hipError_t launch_xpose(const XposeProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st) {
+  if (nwg <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_xpose, dim3(nwg), dim3(256), 0, st, probs, segs, nseg);
+  return hipGetLastError();
 }
 
 hipError_t launch_syrk(const SyrkProb* probs, const SyrkTask* tasks, int ntasks, float* partials,
