@@ -74,6 +74,21 @@ def cpu_baseline(spec, lay, max_rows=32, tok_sample=4096):
                                                                t_h, t_f, t_s)}
 
 
+def syrk_traffic(workload):
+    """HBM bytes per k_syrk launch from the committed counter summary, or None
+    when absent or taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_syrk_%s_traffic.json" % workload)
+    src = os.path.join(ROOT, "post_weight_quantization_gptq_amd", "csrc", "syrk.hip")
+    try:
+        rec = json.load(open(path))
+        if rec.get("syrk_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return None
+        return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +96,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="square", choices=["square", "single", "lora", "mlp", "vit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (5 times), the reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the pass on a single MI355X "
@@ -92,6 +110,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": 5}), flush=True)
+        return
     specs = synth.FULL[args.workload]
     print("# generating %s inputs" % args.workload, file=sys.stderr, flush=True)
     lays = [synth.layer(s, dev) for s in specs]
@@ -99,23 +126,33 @@ def main():
     ctx = Context(dev)
     st = torch.cuda.current_stream(dev)
 
-    def one_step(ev=None):
+    def one_step(evl=None):
         results = []
         if args.workload == "vit":
             layers = [dict(W=l["W"], X=l["X"], bits=s.bits, group=s.group, block=s.block, lam_rel=s.lam_rel)
                       for s, l in zip(specs, lays)]
             ctx.quantize_batched(layers)
             return layers
-        for s, l in zip(specs, lays):
+        shared = {}
+        for li, (s, l) in enumerate(zip(specs, lays)):
+            ev = evl[li] if evl is not None else None
             if s.kind == "lowrank":
                 results.append(ctx.lora(l["W"], l["X"], s.rank, s.bits, s.group, s.block, lam_rel=s.lam_rel))
                 continue
             if ev is not None:
                 ev[0].record(st)
-            H = ctx.hessian(l["X"])
-            if ev is not None:
-                ev[1].record(st)
-            U, info, lam = ctx.factor(H, lam_rel=s.lam_rel)
+            if s.x_key and s.x_key in shared:
+                # layers fed by the same input share one Hessian and its factor
+                U, lam = shared[s.x_key]
+                if ev is not None:
+                    ev[1].record(st)
+            else:
+                H = ctx.hessian(l["X"])
+                if ev is not None:
+                    ev[1].record(st)
+                U, info, lam = ctx.factor(H, lam_rel=s.lam_rel)
+                if s.x_key:
+                    shared[s.x_key] = (U, lam)
             if ev is not None:
                 ev[2].record(st)
             r = ctx.quantize(l["W"], U, s.bits, s.group, s.block, lam)
@@ -127,8 +164,10 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
+    dominant = "k_syrk"
+    ctx.timing(dominant)
     stage = {"hessian": 0.0, "factor": 0.0, "quantize": 0.0}
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in specs] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     last = None
@@ -136,11 +175,31 @@ def main():
         last = one_step(evs[k] if args.workload in ("square", "single", "mlp") else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    dom_ms, dom_launches = ctx.kernel_time(dominant)
+    # per-kernel breakdown from one more (untimed) step with every launch bracketed
+    ctx.timing("*")
+    one_step()
+    torch.cuda.synchronize()
+    names = ["k_xpose", "k_syrk", "k_syrk_reduce", "k_damp_lambda", "k_damp_fill", "k_chol_panel",
+             "k_gemm64", "k_make_u", "k_init_work", "k_rowfit", "k_sweep", "k_trail", "k_objective"]
+    breakdown = {}
+    for nm in names:
+        ms, cnt = ctx.kernel_time(nm)
+        if cnt:
+            breakdown[nm] = {"ms": round(ms, 4), "launches": cnt}
+    ctx.timing(None)
     ms_step = 1e3 * wall / args.steps
     nlayers = len(specs)
     ms_layer = ms_step / nlayers
 
-    fl = [layer_flops(s.out, s.n, s.tokens, s.block, s.n + s.rank) for s in specs]
+    fl, seen = [], set()
+    for s in specs:
+        f = layer_flops(s.out, s.n, s.tokens, s.block, s.n + s.rank)
+        if s.x_key and s.x_key in seen:  # shared Hessian and factor: counted once
+            f["total"] -= f["syrk"] + f["factor"]
+            f["syrk"] = f["factor"] = 0
+        seen.add(s.x_key)
+        fl.append(f)
     total_flops = sum(f["total"] for f in fl)
     tflops = total_flops / (ms_step * 1e-3) / 1e12
     line = {"metric": METRIC, "value": round(ms_layer, 4), "unit": "ms/layer", "n_gpus": 1,
@@ -154,25 +213,24 @@ def main():
             "dtypes": "X bf16 -> H fp32 (bf16 MFMA, fp32 accumulate); factor fp64; sweep and trailing fp32"}
     if args.workload in ("square", "single", "mlp"):
         for k in range(args.steps):
-            e = evs[k]
-            stage["hessian"] += e[0].elapsed_time(e[1])
-            stage["factor"] += e[1].elapsed_time(e[2])
-            stage["quantize"] += e[2].elapsed_time(e[3])
+            for e in evs[k]:
+                stage["hessian"] += e[0].elapsed_time(e[1])
+                stage["factor"] += e[1].elapsed_time(e[2])
+                stage["quantize"] += e[2].elapsed_time(e[3])
         for key in stage:
             stage[key] = round(stage[key] / args.steps / nlayers, 4)
         line["stages_ms"] = stage
-        syrk_flops = sum(f["syrk"] for f in fl) / nlayers
-        ach = syrk_flops / (stage["hessian"] * 1e-3) / 1e12
-        traffic = None
-        tf_path = os.path.join(ROOT, "profiles", "syrk_%s_traffic.json" % args.workload)
-        if os.path.exists(tf_path):
-            try:
-                traffic = json.load(open(tf_path)).get("bytes_per_launch")
-            except Exception:
-                traffic = None
-        line["roofline"] = {"kernel": "k_syrk (+ k_syrk_reduce in the timed call)", "bound": "mfma",
-                            "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    line["kernels_one_step"] = breakdown
+    if dom_launches:
+        # algorithmic flops of one launch (mean over the step's launches): the
+        # triangle X^T X of every layer the launch covers
+        per_launch = sum(f["syrk"] for f in fl) / dom_launches * args.steps
+        avg_ms = dom_ms / dom_launches
+        ach = per_launch / (avg_ms * 1e-3) / 1e12
+        line["roofline"] = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),
+                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                            "traffic": syrk_traffic(args.workload), "avg_launch_ms": round(avg_ms, 4),
+                            "flops_per_launch": per_launch}
     if args.workload == "lora":
         line["objective"] = {"J": last[0]["J"], "J_lam": last[0]["J_lam"]}
     if not args.no_cpu_baseline and args.workload in ("square", "single"):

@@ -164,6 +164,20 @@ typedef struct {
  * first error met; per-layer info/obj are filled in for every layer. */
 int gptq_quantize_batched(gptq_ctx ctx, int32_t nlayers, gptq_layer* layers);
 
+/* Measurement support (not part of the method).  gptq_timing(ctx, kernels)
+ * clears the totals and from then on brackets each launch of the named
+ * kernels with a pair of HIP events on the context's stream.  kernels [host]
+ * is a comma-separated list of kernel names (e.g. "k_syrk,k_sweep"), "*" for
+ * every kernel the context launches, or NULL to stop recording (totals are
+ * kept until the next gptq_timing call).  Kernel names: k_xpose, k_syrk,
+ * k_syrk_reduce, k_damp_lambda, k_damp_fill, k_chol_panel, k_gemm64, k_make_u,
+ * k_init_work, k_rowfit, k_sweep, k_trail, k_objective.  gptq_kernel_time
+ * waits for the recorded events and returns the summed elapsed milliseconds
+ * and the number of timed launches of kernel `name` (0 and 0 if none).  Each
+ * timed launch costs two event records on the stream. */
+int gptq_timing(gptq_ctx ctx, const char* kernels);
+int gptq_kernel_time(gptq_ctx ctx, const char* name, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -96,8 +96,10 @@ def load_library(path: str | None = None):
     L.gptq_lora.argtypes = [vp, vp, i32, i32, vp, i64, i64, i32, i32, i32, i32, d, d,
                             vp, vp, vp, vp, vp, ctypes.POINTER(d), ctypes.POINTER(i32)]
     L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
+    L.gptq_timing.argtypes = [vp, ctypes.c_char_p]
+    L.gptq_kernel_time.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(d), ctypes.POINTER(i64)]
     for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
-                 "gptq_lora", "gptq_quantize_batched"):
+                 "gptq_lora", "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
         getattr(L, name).restype = ctypes.c_int
     if path is None:
         _lib = L
@@ -133,6 +135,17 @@ class Context:
         self._check(self.lib.gptq_create(ctypes.byref(h), self.device.index, ctypes.c_void_p(self.stream.cuda_stream)),
                     ctx=None)
         self.handle = h
+
+    def timing(self, kernels: str | None = "*"):
+        """Start per-kernel event timing of `kernels` (comma-separated names or
+        "*"), clearing the totals; None stops it."""
+        self._check(self.lib.gptq_timing(self.handle, None if kernels is None else kernels.encode()))
+
+    def kernel_time(self, name: str):
+        """(total ms, launches) of the kernel `name` since timing was enabled."""
+        ms, cnt = ctypes.c_double(0.0), ctypes.c_int64(0)
+        self._check(self.lib.gptq_kernel_time(self.handle, name.encode(), ctypes.byref(ms), ctypes.byref(cnt)))
+        return ms.value, cnt.value
 
     def close(self):
         if getattr(self, "handle", None):

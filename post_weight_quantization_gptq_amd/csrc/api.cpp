@@ -41,6 +41,18 @@ struct gptq_ctx_s {
   size_t hsmall_cap = 0;
   hipEvent_t blob_ev = nullptr;
   bool blob_pending = false;
+  // per-kernel timing (off unless gptq_timing enabled it)
+  struct Timed {
+    const char* name;
+    hipEvent_t a, b;
+  };
+  bool timing = false;
+  std::string tfilter;  // "*" or ",name,name,"
+  std::vector<Timed> tpend;
+  std::vector<hipEvent_t> tpool;
+  std::vector<std::string> tname;
+  std::vector<double> tms;
+  std::vector<long long> tcount;
 };
 
 namespace {
@@ -63,6 +75,60 @@ int set_err(gptq_ctx c, int status, const char* fmt, ...) {
     if (e_ != hipSuccess)                                                                     \
       return set_err((c), GPTQ_ERR_HIP, "%s: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, \
                      __LINE__);                                                               \
+  } while (0)
+
+hipError_t timer_event(gptq_ctx c, hipEvent_t* e) {
+  if (!c->tpool.empty()) {
+    *e = c->tpool.back();
+    c->tpool.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(e);
+}
+
+// Fold the finished event pairs into the per-name totals.
+int timer_collect(gptq_ctx c) {
+  for (const auto& t : c->tpend) {
+    HIPCHK(c, hipEventSynchronize(t.b));
+    float ms = 0.f;
+    HIPCHK(c, hipEventElapsedTime(&ms, t.a, t.b));
+    size_t k = 0;
+    while (k < c->tname.size() && c->tname[k] != t.name) ++k;
+    if (k == c->tname.size()) {
+      c->tname.push_back(t.name);
+      c->tms.push_back(0.0);
+      c->tcount.push_back(0);
+    }
+    c->tms[k] += ms;
+    c->tcount[k] += 1;
+    c->tpool.push_back(t.a);
+    c->tpool.push_back(t.b);
+  }
+  c->tpend.clear();
+  return GPTQ_OK;
+}
+
+bool timer_wants(gptq_ctx c, const char* name) {
+  if (!c->timing) return false;
+  if (c->tfilter == "*") return true;
+  return c->tfilter.find(std::string(",") + name + ",") != std::string::npos;
+}
+
+// Issue one kernel launch; with timing on, bracket it by an event pair.
+#define LAUNCH(c, name, expr)                                \
+  do {                                                       \
+    hipEvent_t ea_ = nullptr, eb_ = nullptr;                 \
+    const bool timed_ = timer_wants(c, name);                \
+    if (timed_) {                                            \
+      HIPCHK(c, timer_event(c, &ea_));                       \
+      HIPCHK(c, timer_event(c, &eb_));                       \
+      HIPCHK(c, hipEventRecord(ea_, (c)->stream));           \
+    }                                                        \
+    HIPCHK(c, expr);                                         \
+    if (timed_) {                                            \
+      HIPCHK(c, hipEventRecord(eb_, (c)->stream));           \
+      (c)->tpend.push_back(gptq_ctx_s::Timed{name, ea_, eb_}); \
+    }                                                        \
   } while (0)
 
 int ensure(gptq_ctx c, DevBuf& b, size_t bytes) {
@@ -295,11 +361,11 @@ int run_hessian(gptq_ctx c, const std::vector<HessJob>& jobs) {
   uint8_t* d = nullptr;
   rc = upload(c, b, &d);
   if (rc) return rc;
-  HIPCHK(c, launch_xpose((const XposeProb*)(d + o_xprobs), (const Seg*)(d + o_xsegs), (int)P.xsegs.size(), nxwg,
+  LAUNCH(c, "k_xpose", launch_xpose((const XposeProb*)(d + o_xprobs), (const Seg*)(d + o_xsegs), (int)P.xsegs.size(), nxwg,
                          c->stream));
-  HIPCHK(c, launch_syrk((const SyrkProb*)(d + o_probs), (const SyrkTask*)(d + o_tasks),
+  LAUNCH(c, "k_syrk", launch_syrk((const SyrkProb*)(d + o_probs), (const SyrkTask*)(d + o_tasks),
                         (int)P.tasks.size(), (float*)c->partials.p, c->stream));
-  HIPCHK(c, launch_syrk_reduce((const RedProb*)(d + o_rprobs), (const RedTask*)(d + o_rtasks),
+  LAUNCH(c, "k_syrk_reduce", launch_syrk_reduce((const RedProb*)(d + o_rprobs), (const RedTask*)(d + o_rtasks),
                                (int)P.rtasks.size(), (const int*)(d + o_plist),
                                (const float*)c->partials.p, c->stream));
   return GPTQ_OK;
@@ -430,14 +496,14 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   uint8_t* d = nullptr;
   if ((rc = upload(c, b, &d))) return rc;
   const FacProb* dp = (const FacProb*)(d + o_probs);
-  HIPCHK(c, launch_damp_lambda(dp, np, c->stream));
+  LAUNCH(c, "k_damp_lambda", launch_damp_lambda(dp, np, c->stream));
   for (const L& l : launches) {
     const Seg* sg = (const Seg*)(d + l.off);
     switch (l.kind) {
-      case 0: HIPCHK(c, launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 1: HIPCHK(c, launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 2: HIPCHK(c, launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 4: HIPCHK(c, launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 0: LAUNCH(c, "k_damp_fill", launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 1: LAUNCH(c, "k_chol_panel", launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 2: LAUNCH(c, "k_gemm64", launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 4: LAUNCH(c, "k_make_u", launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
     }
   }
   return GPTQ_OK;
@@ -559,13 +625,13 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
   for (const Lc& l : launches) {
     const Seg* sg = (const Seg*)(d + l.off);
     switch (l.kind) {
-      case 0: HIPCHK(c, launch_init_work(dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 1: HIPCHK(c, launch_rowfit(dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 2: HIPCHK(c, launch_sweep(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3: HIPCHK(c, launch_trail(dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 0: LAUNCH(c, "k_init_work", launch_init_work(dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 1: LAUNCH(c, "k_rowfit", launch_rowfit(dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 2: LAUNCH(c, "k_sweep", launch_sweep(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 3: LAUNCH(c, "k_trail", launch_trail(dL, sg, l.nseg, l.nwg, c->stream)); break;
     }
   }
-  HIPCHK(c, launch_objective(dL, nl, c->stream));
+  LAUNCH(c, "k_objective", launch_objective(dL, nl, c->stream));
   return GPTQ_OK;
 }
 
@@ -644,8 +710,48 @@ GPTQ_API int gptq_destroy(gptq_ctx c) {
     if (c->hblob) (void)hipHostFree(c->hblob);
     if (c->hsmall) (void)hipHostFree(c->hsmall);
     if (c->blob_ev) (void)hipEventDestroy(c->blob_ev);
+    for (const auto& t : c->tpend) {
+      (void)hipEventDestroy(t.a);
+      (void)hipEventDestroy(t.b);
+    }
+    for (hipEvent_t e : c->tpool) (void)hipEventDestroy(e);
   }
   delete c;
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_timing(gptq_ctx c, const char* kernels) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  DeviceGuard g(c->device);
+  int rc = timer_collect(c);
+  if (rc) return rc;
+  c->tname.clear();
+  c->tms.clear();
+  c->tcount.clear();
+  c->timing = kernels != nullptr;
+  c->tfilter.clear();
+  if (kernels) {
+    std::string k(kernels);
+    k.erase(std::remove(k.begin(), k.end(), ' '), k.end());
+    c->tfilter = (k == "*") ? k : "," + k + ",";
+  }
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_kernel_time(gptq_ctx c, const char* name, double* total_ms, int64_t* launches) {
+  if (!c || !name || !total_ms || !launches) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  DeviceGuard g(c->device);
+  int rc = timer_collect(c);
+  if (rc) return rc;
+  *total_ms = 0.0;
+  *launches = 0;
+  for (size_t k = 0; k < c->tname.size(); ++k)
+    if (c->tname[k] == name) {
+      *total_ms = c->tms[k];
+      *launches = c->tcount[k];
+    }
   return GPTQ_OK;
 }
 

@@ -60,33 +60,70 @@ __global__ __launch_bounds__(256) void k_xpose(const XposeProb* __restrict__ pro
 
 // One 256x256 upper tile of H over the token range [k0, k1) of Xt (both
 // multiples of 64; the copy is zero-padded, so no bounds are checked).
-// Per 64-token step each operand is a 256-row x 128-byte tile in LDS.  The
-// rows travel from L2 straight into LDS (global_load_lds, 16 B per lane, no
-// registers in between) while the previous step is multiplied; inside a row
-// the 16-byte token chunks are stored XOR-swizzled by (row % 8), so the
-// fragment reads of 32 consecutive rows hit all LDS banks.
-#define SYK_STAGE (2 * 256 * 128)  // bytes per stage (two operands)
+//
+// Pipeline: a ring of 4 LDS stages of 32 tokens (each operand a 256-row x
+// 64-byte tile, 16 KB); rows travel from L2 straight into LDS
+// (global_load_lds, 16 B per lane, no registers in between) three stages
+// ahead of the stage being multiplied.  Inside a row the 16-byte token chunks
+// are stored XOR-swizzled by (row / 4) % 4, so a fragment read of 16
+// consecutive rows covers all LDS banks.  Each wave owns a 128x128 quarter of
+// the tile (4 x 4 MFMA 32x32x16 accumulators, 256 AGPRs); the fragment reads
+// of the next 16-token sub-step are interleaved with the MFMAs of the current
+// one, across the stage boundary too.
+#define SYK_KT 32                   // tokens per stage
+#define SYK_OPB (256 * SYK_KT * 2)  // bytes of one operand tile in a stage
+#define SYK_STB (2 * SYK_OPB)       // bytes of a stage
+#define SYK_NST 4                   // stages in the ring
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_syrk(const SyrkProb* __restrict__ probs,
-                                                 const SyrkTask* __restrict__ tasks,
-                                                 float* __restrict__ partials) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SYK_STAGE];
-  const SyrkTask tk = tasks[blockIdx.x];
-  if (tk.part < 0) return;
-  const SyrkProb pb = probs[tk.prob];
+// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding).
+template <int N>
+struct VmWait {
+  static constexpr int value = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+};
+
+template <bool DIAG>
+__device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk, uint8_t* lds,
+                                          float* __restrict__ partials) {
+  constexpr int L = DIAG ? 4 : 8;  // global_load_lds per lane per stage
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool diag = tk.ti == tk.tj;
-  const int nsteps = (tk.k1 - tk.k0) >> 6;
+  const int nsteps = (tk.k1 - tk.k0) / SYK_KT;
   const size_t tp = (size_t)pb.t_pad;
-  // Load slot of this lane: instruction q of wave w fills LDS rows
-  // 8(4q+w) .. 8(4q+w)+7; lane -> row 8(4q+w) + lane/8, chunk position lane%8,
-  // holding token chunk (lane%8) ^ (row%8).
-  const int lrow = 8 * w + (lane >> 3);
-  const int tchunk = (lane & 7) ^ ((lane >> 3) & 7);
+  // Load slot: instruction q of wave w fills the 16 LDS rows 16(4q+w) ..
+  // 16(4q+w)+15 (1 KB); lane -> row 16(4q+w) + lane/4 at chunk position
+  // lane%4, holding token chunk (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16).
+  const int lrow = 16 * w + (lane >> 2);
+  const int tchunk = (lane & 3) ^ (lane >> 4);
   const uint16_t* ga = pb.Xt + (size_t)(tk.ti * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
   const uint16_t* gb = pb.Xt + (size_t)(tk.tj * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
+  auto issue = [&](int step, int stage) {
+    uint8_t* base = lds + stage * SYK_STB;
+    const size_t off = (size_t)step * SYK_KT;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(ga + (size_t)(64 * q) * tp + off),
+                                       (lds_void*)(base + (4 * q + w) * 1024), 16, 0, 0);
+    if (!DIAG) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(gb + (size_t)(64 * q) * tp + off),
+                                         (lds_void*)(base + SYK_OPB + (4 * q + w) * 1024), 16, 0, 0);
+    }
+  };
+  // Fragment rows of this lane: arow + 32m (A), brow + 32q (B); all have
+  // (row/4)%4 == (lane/4)%4.
+  const int arow = 128 * (w >> 1) + (lane & 31);
+  const int brow = 128 * (w & 1) + (lane & 31);
+  const int sw = (lane >> 2) & 3;
+  auto rd = [&](const uint8_t* st, int ks, bf16x8* fa, bf16x8* fb) {
+    const int ch = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) fa[m] = *(const bf16x8*)(st + (arow + 32 * m) * 64 + ch);
+    const uint8_t* sb = DIAG ? st : st + SYK_OPB;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fb[q] = *(const bf16x8*)(sb + (brow + 32 * q) * 64 + ch);
+  };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -95,64 +132,52 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][q][r] = 0.f;
-
-  auto issue = [&](int step, int stage) {
-    uint8_t* base = lds + stage * SYK_STAGE;
-    const size_t off = (size_t)step * 64;
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(ga + (size_t)(32 * q) * tp + off),
-                                       (lds_void*)(base + (4 * q + w) * 1024), 16, 0, 0);
-    if (!diag) {
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(gb + (size_t)(32 * q) * tp + off),
-                                         (lds_void*)(base + 256 * 128 + (4 * q + w) * 1024), 16, 0, 0);
-    }
+      for (int q = 0; q < 4; ++q)
+        acc[m][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[q], acc[m][q], 0, 0, 0);
   };
-  const int arow = 128 * (w >> 1) + (lane & 31);
-  const int brow = 128 * (w & 1) + (lane & 31);
-  const int sw = lane & 7;  // = row % 8 for every fragment row of this lane
 
-  if (nsteps > 0) issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Three stages in flight from the start; past the last step the copies
+  // repeat the last step into stages nobody reads again (keeps the count of
+  // copies in flight uniform).
+  const int last = nsteps - 1;
+  issue(0, 0);
+  issue(min(1, last), 1);
+  issue(min(2, last), 2);
+  __builtin_amdgcn_s_waitcnt(VmWait<2 * L>::value);  // stage 0 has landed
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  rd(lds, 0, a0, b0);
   for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
-    const uint8_t* As = lds + (s & 1) * SYK_STAGE;
-    const uint8_t* Bs = diag ? As : As + 256 * 128;
-    // fragments of sub-step ks+1 are requested before the MFMAs of ks
-    bf16x8 fa[2][4], fb[2][4];
+    rd(lds + (s & 3) * SYK_STB, 1, a1, b1);
+    mma(a0, b0);
 #pragma unroll
-    for (int ks = 0; ks < 5; ++ks) {
-      if (ks < 4) {
-        const int ch = ((2 * ks + (lane >> 5)) ^ sw) * 16;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) fa[ks & 1][m] = *(const bf16x8*)(As + (arow + 32 * m) * 128 + ch);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) fb[ks & 1][q] = *(const bf16x8*)(Bs + (brow + 32 * q) * 128 + ch);
-      }
-      if (ks > 0) {
-        const int u = (ks - 1) & 1;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[m][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[u][m], fb[u][q], acc[m][q], 0, 0, 0);
-      }
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // keep the order: reads of sub-step 0; then (reads of k+1, MFMAs of k)
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of step s+1 have landed
-    __syncthreads();                // ... and everybody's; stage s&1 is free again
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    // stage s+1 has landed (only stage s+2 may still be in flight) for this
+    // wave, and after the barrier for every wave; stage s-1 is free
+    __builtin_amdgcn_s_waitcnt(VmWait<L>::value);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(min(s + 3, last), (s + 3) & 3);
+    rd(lds + ((s + 1) & 3) * SYK_STB, 0, a0, b0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_group_barrier(0x020, L, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::value);  // no copy into LDS outlives the group
 
   float* P = partials + (size_t)tk.part * 65536;
 #pragma unroll
@@ -165,6 +190,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int col = 128 * (w & 1) + 32 * q + (lane & 31);
         P[row * 256 + col] = acc[m][q][r];
       }
+}
+
+__global__ __launch_bounds__(256, 1) void k_syrk(const SyrkProb* __restrict__ probs,
+                                                 const SyrkTask* __restrict__ tasks,
+                                                 float* __restrict__ partials) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SYK_NST * SYK_STB];
+  const SyrkTask tk = tasks[blockIdx.x];
+  if (tk.part < 0) return;
+  const SyrkProb pb = probs[tk.prob];
+  if (tk.ti == tk.tj)
+    syrk_tile<true>(pb, tk, lds, partials);
+  else
+    syrk_tile<false>(pb, tk, lds, partials);
 }
 
 // Sum the partials of one 64x64 sub-block of an upper tile in list order,
