@@ -271,7 +271,8 @@ class Context:
         return res
 
     def quantize_batched(self, layers):
-        """layers: list of dicts with W, bits, group, block, lam_rel (and X or H, optional lam_abs, err).
+        """layers: list of dicts with W, bits, group, block, lam_rel (and X or H, optional lam_abs,
+        err or want_err).
         Fills H/U/codes/scales/zeros per layer (allocating what is missing); returns the list."""
         torch = self.torch
         arr = (_Layer * len(layers))()
@@ -286,6 +287,8 @@ class Context:
             ly.setdefault("codes", torch.empty((o, n), dtype=torch.uint8, device=self.device))
             ly.setdefault("scales", torch.empty((o, ng), dtype=torch.float32, device=self.device))
             ly.setdefault("zeros", torch.empty((o, ng), dtype=torch.uint8, device=self.device))
+            if ly.get("want_err") and ly.get("err") is None:
+                ly["err"] = torch.empty((o, n), dtype=torch.float32, device=self.device)
             X = ly.get("X")
             if X is not None:
                 X = self._xbits(X)

@@ -371,6 +371,88 @@ int run_hessian(gptq_ctx c, const std::vector<HessJob>& jobs) {
   return GPTQ_OK;
 }
 
+// One layer's Gram matrix accurate to float64 rounding ([n][n] doubles, full
+// symmetric): the same transposed copy of X, 128x128 upper tiles on float64
+// MFMA, each tile split over S token slices (S chosen so that the tasks fill
+// whole rounds of the chip), partials summed in slice order.
+int run_hessian64(gptq_ctx c, const uint16_t* X, long long tokens, long long ldx, int n, double* H) {
+  if (n <= 0) return GPTQ_OK;
+  const int n_pad = cdiv(n, 256) * 256;
+  const long long t_pad = cdiv(tokens, 64) * 64;
+  int rc = ensure(c, c->xt, (size_t)n_pad * (size_t)std::max(t_pad, 64LL) * sizeof(uint16_t));
+  if (rc) return rc;
+  uint16_t* xt = (uint16_t*)c->xt.p;
+  const int vec = (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
+  std::vector<XposeProb> xprobs{XposeProb{X, ldx, xt, n, (int)tokens, n_pad, (int)t_pad, vec, 0}};
+  std::vector<Seg> xsegs;
+  if (t_pad > 0) xsegs.push_back(Seg{0, 0, (int)(t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
+  const int nwx = xsegs.empty() ? 0 : xsegs[0].nwg;
+  std::vector<SyrkProb> probs{SyrkProb{xt, t_pad}};
+  std::vector<RedProb64> rprobs{RedProb64{H, n, 0}};
+  const int nt = cdiv(n, 128);
+  const int ntile = nt * (nt + 1) / 2;
+  const long long chunks = t_pad / 32;
+  // slices: minimise rounds x slice length
+  int S = 1;
+  long long best = -1;
+  for (int k = 1; k <= 64 && k <= std::max(1LL, chunks); ++k) {
+    const long long rounds = cdiv((long long)ntile * k, (long long)c->ncu);
+    const long long cost = rounds * cdiv(chunks, (long long)k);
+    if (best < 0 || cost < best) {
+      best = cost;
+      S = k;
+    }
+  }
+  std::vector<SyrkTask> tasks;
+  std::vector<int> partlist;
+  std::vector<RedTask> rtasks;
+  if (chunks > 0) {
+    for (int sl = 0; sl < S; ++sl) {
+      const int k0 = (int)(32 * (chunks * sl / S)), k1 = (int)(32 * (chunks * (sl + 1) / S));
+      int t = 0;
+      for (int ti = 0; ti < nt; ++ti)
+        for (int tj = ti; tj < nt; ++tj, ++t) tasks.push_back(SyrkTask{0, ti, tj, k0, k1, (int)tasks.size(), 0, 0});
+    }
+    int t = 0;
+    for (int ti = 0; ti < nt; ++ti)
+      for (int tj = ti; tj < nt; ++tj, ++t) {
+        const int part0 = (int)partlist.size();
+        for (int sl = 0; sl < S; ++sl) partlist.push_back(sl * ntile + t);
+        for (int a = 0; a < 2; ++a)
+          for (int b = 0; b < 2; ++b) {
+            if (ti == tj && a > b) continue;
+            const int r0 = ti * 128 + 64 * a, c0 = tj * 128 + 64 * b;
+            if (r0 >= n || c0 >= n) continue;
+            rtasks.push_back(RedTask{0, r0, c0, part0, S, 0, 0, 0});
+          }
+      }
+  } else {
+    // no tokens: H = 0 (every sub-block sums zero partials)
+    for (int ti = 0; ti < nt; ++ti)
+      for (int tj = ti; tj < nt; ++tj)
+        for (int a = 0; a < 2; ++a)
+          for (int b = 0; b < 2; ++b) {
+            const int r0 = ti * 128 + 64 * a, c0 = tj * 128 + 64 * b;
+            if ((ti == tj && a > b) || r0 >= n || c0 >= n) continue;
+            rtasks.push_back(RedTask{0, r0, c0, 0, 0, 0, 0, 0});
+          }
+  }
+  if ((rc = ensure(c, c->partials, std::max<size_t>(tasks.size(), 1) * 16384 * sizeof(double)))) return rc;
+  Blob b;
+  const size_t o_xprobs = b.add(xprobs), o_xsegs = b.add(xsegs), o_probs = b.add(probs), o_tasks = b.add(tasks),
+               o_rprobs = b.add(rprobs), o_rtasks = b.add(rtasks), o_plist = b.add(partlist);
+  uint8_t* d = nullptr;
+  if ((rc = upload(c, b, &d))) return rc;
+  LAUNCH(c, "k_xpose", launch_xpose((const XposeProb*)(d + o_xprobs), (const Seg*)(d + o_xsegs), (int)xsegs.size(),
+                                    nwx, c->stream));
+  LAUNCH(c, "k_syrk64", launch_syrk64((const SyrkProb*)(d + o_probs), (const SyrkTask*)(d + o_tasks),
+                                      (int)tasks.size(), (double*)c->partials.p, c->stream));
+  LAUNCH(c, "k_syrk64_reduce", launch_syrk64_reduce((const RedProb64*)(d + o_rprobs), (const RedTask*)(d + o_rtasks),
+                                                    (int)rtasks.size(), (const int*)(d + o_plist),
+                                                    (const double*)c->partials.p, c->stream));
+  return GPTQ_OK;
+}
+
 // ------------------------------------------------------------- factor plan --
 struct FacJob {
   const float* H;  // null: A (and lam) prepared by an earlier kernel
@@ -901,8 +983,8 @@ GPTQ_API int gptq_lora(gptq_ctx c, const float* W, int32_t out, int32_t n, const
   DeviceGuard g(c->device);
   LoraIO io{W, out, n, X, tokens, ldx, r, bits, group, block, lam_abs, lam_rel, codes, scales, zeros, L, R};
   LoraHooks hooks;
-  hooks.hessian = [&](const uint16_t* X_, long long t_, long long ld_, int n_, float* H_) {
-    return run_hessian(c, {HessJob{X_, t_, ld_, n_, H_, 0}});
+  hooks.hessian64 = [&](const uint16_t* X_, long long t_, long long ld_, int n_, double* H_) {
+    return run_hessian64(c, X_, t_, ld_, n_, H_);
   };
   hooks.ensure = [&](size_t bytes) -> void* {
     if (ensure(c, c->lora, bytes)) return nullptr;

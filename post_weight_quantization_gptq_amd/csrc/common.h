@@ -46,6 +46,12 @@ struct RedProb {
 struct RedTask {
   int prob, r0, c0, part0, nparts, pad0, pad1, pad2;
 };
+// fp64 Gram output (full symmetric [n][n]).
+struct RedProb64 {
+  double* H;
+  int n;
+  int pad0;
+};
 
 // ----------------------------------------------------------------- factor --
 // Work matrices are fp64, row-major with leading dimension n.

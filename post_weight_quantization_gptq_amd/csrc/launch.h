@@ -9,6 +9,10 @@ hipError_t launch_syrk(const SyrkProb* probs, const SyrkTask* tasks, int ntasks,
 hipError_t launch_syrk_reduce(const RedProb* probs, const RedTask* tasks, int ntasks,
                               const int* partlist, const float* partials, hipStream_t st);
 hipError_t launch_zero_f32(float* p, long long count, hipStream_t st);
+hipError_t launch_syrk64(const SyrkProb* probs, const SyrkTask* tasks, int ntasks, double* partials,
+                         hipStream_t st);
+hipError_t launch_syrk64_reduce(const RedProb64* probs, const RedTask* tasks, int ntasks, const int* partlist,
+                                const double* partials, hipStream_t st);
 
 // Factor
 hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st);

@@ -122,11 +122,6 @@ __global__ void k_dsum(const double* __restrict__ P, double* __restrict__ C, lon
   C[i] = s;
 }
 
-__global__ void k_h_to_f64(const float* __restrict__ H, double* __restrict__ D, long long count) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) D[i] = (double)H[i];
-}
-
 // Fixed start block: hash of (i, k) mapped to [-1, 1).
 __global__ void k_start_block(double* __restrict__ V, int n, int r) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -179,11 +174,11 @@ __global__ __launch_bounds__(256) void k_chol_inv_small(const double* __restrict
 }
 
 // lam = lam_abs + lam_rel * mean(diag H); clears the slot's flags.
-__global__ __launch_bounds__(256) void k_lora_lambda(const float* __restrict__ H, int n, double lam_abs,
+__global__ __launch_bounds__(256) void k_lora_lambda(const double* __restrict__ H, int n, double lam_abs,
                                                      double lam_rel, Slot* __restrict__ slot) {
   __shared__ double red[256];
   double s = 0.0;
-  for (int i = threadIdx.x; i < n; i += 256) s += (double)H[(size_t)i * n + i];
+  for (int i = threadIdx.x; i < n; i += 256) s += H[(size_t)i * n + i];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int k = 128; k > 0; k >>= 1) {
@@ -259,7 +254,7 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
     return o;
   };
   const int ks_n = std::max(1, std::min(16, n / 256));   // split-K for K = n products
-  const size_t oH = take((size_t)n * n * 4), oH64 = take((size_t)n * n * 8), oV = take((size_t)n * r * 8),
+  const size_t oH64 = take((size_t)n * n * 8), oV = take((size_t)n * r * 8),
                oZ = take((size_t)n * r * 8), oG = take((size_t)r * r * 8), oLi = take((size_t)r * r * 8),
                oM = take((size_t)r * r * 8), oHV = take((size_t)n * r * 8),
                oS = take((size_t)std::max(ks_n * n * r, ks_n * r * r) * 8), oA = take((size_t)nt * nt * 8),
@@ -268,14 +263,15 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
   if (!base) return GPTQ_ERR_NO_MEMORY;
   Slot* slot = (Slot*)hk.slots(sizeof(Slot));
   if (!slot) return GPTQ_ERR_NO_MEMORY;
-  float* H = (float*)(base + oH);
   double *H64 = (double*)(base + oH64), *V = (double*)(base + oV), *Z = (double*)(base + oZ),
          *G = (double*)(base + oG), *Li = (double*)(base + oLi), *M = (double*)(base + oM),
          *HV = (double*)(base + oHV), *S = (double*)(base + oS), *A = (double*)(base + oA);
   float* U = (float*)(base + oU);
   float* Ww = (float*)(base + oW);
 
-  int rc = hk.hessian(io.X, io.tokens, io.ldx, n, H);
+  // H accurate to float64 rounding: the Schur complement below cancels the
+  // top-r eigen-directions of H against a damping far below their size
+  int rc = hk.hessian64(io.X, io.tokens, io.ldx, n, H64);
   if (rc) return rc;
   hipError_t e;
 #define LCHK(x)                                                        \
@@ -283,10 +279,7 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
     e = (x);                                                           \
     if (e != hipSuccess) return hk.set_err(GPTQ_ERR_HIP, hipGetErrorString(e)); \
   } while (0)
-  hipLaunchKernelGGL(k_lora_lambda, dim3(1), dim3(256), 0, st, (const float*)H, n, io.lam_abs, io.lam_rel, slot);
-  LCHK(hipGetLastError());
-  hipLaunchKernelGGL(k_h_to_f64, dim3(cdivl((long long)n * n, 256)), dim3(256), 0, st, (const float*)H, H64,
-                     (long long)n * n);
+  hipLaunchKernelGGL(k_lora_lambda, dim3(1), dim3(256), 0, st, (const double*)H64, n, io.lam_abs, io.lam_rel, slot);
   LCHK(hipGetLastError());
   hipLaunchKernelGGL(k_start_block, dim3(cdivl((long long)n * r, 256)), dim3(256), 0, st, V, n, r);
   LCHK(hipGetLastError());

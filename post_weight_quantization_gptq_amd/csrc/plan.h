@@ -43,7 +43,7 @@ struct LoraIO {
 
 // Services the C ABI lends to the LoRA driver (workspace, the shared stages).
 struct LoraHooks {
-  std::function<int(const uint16_t*, long long, long long, int, float*)> hessian;
+  std::function<int(const uint16_t*, long long, long long, int, double*)> hessian64;
   std::function<void*(size_t)> ensure;  // LoRA workspace of at least n bytes
   std::function<void*(size_t)> slots;   // device slots of at least n bytes
   std::function<int(double*, int, float*, Slot*)> factor;  // factor an assembled A

@@ -252,6 +252,165 @@ __global__ __launch_bounds__(256) void k_syrk_reduce(const RedProb* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// Gram matrix accurate to float64 rounding, for callers whose later steps
+// cancel most of H (the intrinsic-LoRA Schur complement loses the top
+// eigen-directions of H against a damping of 1e-4 of its mean diagonal, so a
+// float32 accumulation error of H is amplified beyond the codes' tolerance).
+// bf16 values are exact in float64, so are their products; the sums run in
+// float64 on v_mfma_f64_16x16x4.  One 128x128 upper tile per workgroup over
+// a token range (multiple of 32), 4 waves of 64x64 (4 x 4 MFMA blocks).  The
+// MFMA's four k-slots of step s take tokens 8k + s of a 32-token stage, so a
+// lane reads its row's 8 consecutive tokens with one 16-byte LDS read and
+// uses them over the stage's 8 steps (A and B use the same token order).
+#define S64_ROWB 64                 // bytes per LDS row (32 tokens)
+#define S64_OPB (128 * S64_ROWB)    // one operand tile per stage (8 KB)
+
+__device__ __forceinline__ double bf16_to_f64(unsigned h) {
+  return (double)__uint_as_float(h << 16);
+}
+
+template <bool DIAG>
+__device__ __forceinline__ void syrk64_tile(const SyrkProb& pb, const SyrkTask& tk, uint8_t* lds,
+                                            double* __restrict__ partials) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nsteps = (tk.k1 - tk.k0) / 32;
+  const size_t tp = (size_t)pb.t_pad;
+  // instruction q of wave w fills LDS rows 16(4q+w)..+15 (1 KB): lane ->
+  // row 16(4q+w) + lane/4 at chunk position lane%4 holding token chunk
+  // (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16)
+  const int lrow = 16 * w + (lane >> 2);
+  const int tchunk = (lane & 3) ^ (lane >> 4);
+  const uint16_t* ga = pb.Xt + (size_t)(tk.ti * 128 + lrow) * tp + tk.k0 + 8 * tchunk;
+  const uint16_t* gb = pb.Xt + (size_t)(tk.tj * 128 + lrow) * tp + tk.k0 + 8 * tchunk;
+  auto issue = [&](int step, int stage) {
+    uint8_t* base = lds + stage * 2 * S64_OPB;
+    const size_t off = (size_t)step * 32;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(ga + (size_t)(64 * q) * tp + off),
+                                       (lds_void*)(base + (4 * q + w) * 1024), 16, 0, 0);
+    if (!DIAG) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(gb + (size_t)(64 * q) * tp + off),
+                                         (lds_void*)(base + S64_OPB + (4 * q + w) * 1024), 16, 0, 0);
+    }
+  };
+  // fragment rows: 64(w/2) + 16 mb + lane%16 (A), 64(w%2) + 16 nb + lane%16 (B);
+  // the lane reads token chunk lane/16, stored at chunk position
+  // (lane/16) ^ ((row/4)%4) = (lane/16) ^ ((lane/4)%4)
+  const int arow = 64 * (w >> 1) + (lane & 15);
+  const int brow = 64 * (w & 1) + (lane & 15);
+  const int ch = ((lane >> 4) ^ ((lane >> 2) & 3)) * 16;
+
+  f64x4 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[m][q][r] = 0.0;
+
+  if (nsteps > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
+    const uint8_t* As = lds + (s & 1) * 2 * S64_OPB;
+    const uint8_t* Bs = DIAG ? As : As + S64_OPB;
+    u32x4 fa[4], fb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) fa[m] = *(const u32x4*)(As + (arow + 16 * m) * S64_ROWB + ch);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fb[q] = *(const u32x4*)(Bs + (brow + 16 * q) * S64_ROWB + ch);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const unsigned word = fa[m][st >> 1];
+        av[m] = bf16_to_f64((st & 1) ? (word >> 16) : (word & 0xffffu));
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const unsigned word = fb[q][st >> 1];
+        bv[q] = bf16_to_f64((st & 1) ? (word >> 16) : (word & 0xffffu));
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[m][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[m], bv[q], acc[m][q], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  double* P = partials + (size_t)tk.part * 16384;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 64 * (w >> 1) + 16 * m + (lane >> 4) + 4 * r;
+        const int col = 64 * (w & 1) + 16 * q + (lane & 15);
+        P[row * 128 + col] = acc[m][q][r];
+      }
+}
+
+__global__ __launch_bounds__(256, 1) void k_syrk64(const SyrkProb* __restrict__ probs,
+                                                   const SyrkTask* __restrict__ tasks,
+                                                   double* __restrict__ partials) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * S64_OPB];
+  const SyrkTask tk = tasks[blockIdx.x];
+  if (tk.part < 0) return;
+  const SyrkProb pb = probs[tk.prob];
+  if (tk.ti == tk.tj)
+    syrk64_tile<true>(pb, tk, lds, partials);
+  else
+    syrk64_tile<false>(pb, tk, lds, partials);
+}
+
+// Sum the float64 partials of one 64x64 sub-block of a 128x128 upper tile in
+// list order; write the upper part and its mirror (exactly symmetric H).
+__global__ __launch_bounds__(256) void k_syrk64_reduce(const RedProb64* __restrict__ probs,
+                                                       const RedTask* __restrict__ tasks,
+                                                       const int* __restrict__ partlist,
+                                                       const double* __restrict__ partials) {
+  __shared__ double S[64][65];
+  const RedTask tk = tasks[blockIdx.x];
+  const RedProb64 pb = probs[tk.prob];
+  const int tid = threadIdx.x, n = pb.n;
+  const int lr0 = tk.r0 & 127, lc0 = tk.c0 & 127;
+  const int cc = tid & 63;
+  double sum[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) sum[q] = 0.0;
+  for (int p = 0; p < tk.nparts; ++p) {
+    const double* src = partials + (size_t)partlist[tk.part0 + p] * 16384 + (lr0 + (tid >> 6)) * 128 + lc0 + cc;
+    double v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = src[4 * q * 128];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sum[q] += v[q];
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) S[(tid >> 6) + 4 * q][cc] = sum[q];
+  __syncthreads();
+  for (int q = 0; q < 16; ++q) {
+    const int rr = (tid >> 6) + 4 * q;
+    const int i = tk.r0 + rr, j = tk.c0 + cc;
+    if (i < n && j < n && i <= j) pb.H[(size_t)i * n + j] = S[rr][cc];
+  }
+  for (int q = 0; q < 16; ++q) {
+    const int ci = (tid >> 6) + 4 * q;
+    const int ri = tid & 63;
+    const int i = tk.r0 + ri, j = tk.c0 + ci;
+    if (i < n && j < n && i < j) pb.H[(size_t)j * n + i] = S[ri][ci];
+  }
+}
+
 __global__ void k_zero_f32(float* __restrict__ p, long long count) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long stride = (long long)gridDim.x * blockDim.x;
@@ -275,6 +434,20 @@ hipError_t launch_syrk_reduce(const RedProb* probs, const RedTask* tasks, int nt
                               const int* partlist, const float* partials, hipStream_t st) {
   if (ntasks <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_syrk_reduce, dim3(ntasks), dim3(256), 0, st, probs, tasks, partlist, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_syrk64(const SyrkProb* probs, const SyrkTask* tasks, int ntasks, double* partials,
+                         hipStream_t st) {
+  if (ntasks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_syrk64, dim3(ntasks), dim3(256), 0, st, probs, tasks, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_syrk64_reduce(const RedProb64* probs, const RedTask* tasks, int ntasks, const int* partlist,
+                                const double* partials, hipStream_t st) {
+  if (ntasks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_syrk64_reduce, dim3(ntasks), dim3(256), 0, st, probs, tasks, partlist, partials);
   return hipGetLastError();
 }
 

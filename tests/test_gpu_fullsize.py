@@ -1,0 +1,184 @@
+"""GPU library vs the oracle at the full sizes of the benchmark layers.
+
+The calls are the ones bench.py times (same shapes, same entry points, same
+launch plans).  Where the oracle finishes in about a minute it runs whole
+(square layer: H, factor, every row of the sweep with forced replay; the
+intrinsic-LoRA layer); elsewhere the checks are sampled outputs the oracle
+computes one by one (principal blocks of H from the same tokens) and
+properties that hold at any size (U H_lam U^T = I to the float32 rounding
+bound, the sweep's defining recurrence on sampled rows).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import gptq_ref as o  # noqa: E402
+from post_weight_quantization_gptq_amd import Context, synth  # noqa: E402
+from parity import check_h_block, check_sweep, check_sweep_recurrence, check_u_rows, np32  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = Context("cuda:0")
+    yield c
+    c.close()
+
+
+def _rows(out, k, seed):
+    """k distinct rows: the first, the last and a seeded sample between."""
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, out - 1), size=k - 2, replace=False)
+    return np.unique(np.concatenate([[0, out - 1], mid]))
+
+
+def _cols(n, k, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    c = rng.choice(n, size=k, replace=False)
+    return np.unique(np.concatenate([c, [0, n - 1], np.asarray(extra, dtype=np.int64)]))
+
+
+@pytest.mark.timeout(900)
+def test_square_layer_full_oracle(ctx):
+    """4096x4096, 4-bit, g128, 262144 tokens: the whole oracle."""
+    spec = synth.FULL["square"][0]
+    print("square: generating", flush=True)
+    lay = synth.layer(spec, "cuda")
+    H = ctx.hessian(lay["X"])
+    U, info, lam = ctx.factor(H, lam_rel=spec.lam_rel)
+    res = ctx.quantize(lay["W"], U, spec.bits, spec.group, spec.block, lam, want_err=True)
+    torch.cuda.synchronize()
+    Xb = synth.bits_to_numpy(lay["X"])
+    print("square: oracle Hessian", flush=True)
+    Hr = o.hessian(Xb)
+    err_h = float(np.linalg.norm(np32(H) - Hr) / np.linalg.norm(Hr))
+    Hl, lam_r = o.damp(Hr, lam_rel=spec.lam_rel)
+    print("square: H rel err %.3e; oracle factor" % err_h, flush=True)
+    Ur = o.factor_u(Hl)
+    assert err_h <= 1e-5
+    assert info == 0 and lam == pytest.approx(lam_r, rel=1e-5)
+    check_u_rows(np32(U), np32(H), lam, _rows(spec.n, 48, 1))
+    print("square: oracle sweep", flush=True)
+    rep = {}
+    Wn = np32(lay["W"]).astype(np.float64)
+    check_sweep(res, Wn, Ur, spec.bits, spec.group, spec.block, Hr, lam_r, report=rep)
+    print("square:", rep, flush=True)
+    # J_lam is the sum of squared scaled errors (exact identity of the sweep)
+    E = np32(res["err"]).astype(np.float64)
+    assert res["J_lam"] == pytest.approx(float(np.sum(E * E)), rel=1e-6)
+
+
+@pytest.mark.timeout(600)
+def test_lora_layer_full_oracle(ctx):
+    """Intrinsic LoRA 2048x2048, 3-bit, r = 64, 65536 tokens: the whole oracle."""
+    spec = synth.FULL["lora"][0]
+    print("lora: generating", flush=True)
+    lay = synth.layer(spec)
+    res = ctx.lora(lay["W"].cuda(), lay["X"].cuda(), spec.rank, spec.bits, spec.group, spec.block,
+                   lam_rel=spec.lam_rel)
+    print("lora: oracle", flush=True)
+    Hr = o.hessian(synth.bits_to_numpy(lay["X"]))
+    Wn = lay["W"].numpy().astype(np.float64)
+    ref = o.lora(Wn, Hr, spec.rank, spec.bits, spec.group, spec.block, lam_rel=spec.lam_rel)
+    codes = np32(res["codes"])
+    zeros = np32(res["zeros"]).astype(np.float32)
+    agree = float(np.mean(codes == ref["codes"]))
+    rep = o.lora(Wn, Hr, spec.rank, spec.bits, spec.group, spec.block, lam_rel=spec.lam_rel,
+                 V=ref["L"], replay=dict(codes=codes, zeros=zeros))
+    L = np32(res["L"]).astype(np.float64)
+    R = np32(res["R"]).astype(np.float64)
+    proj = float(np.abs(L @ L.T - ref["L"] @ ref["L"].T).max())
+    LR_g = R.T @ L.T
+    LR_r = rep["R_out"] @ rep["L"].T
+    lr_err = float(np.linalg.norm(LR_g - LR_r) / np.linalg.norm(LR_r))
+    print("lora:", dict(agree=agree, forced=rep["forced_codes"], J=res["J"], J_ref=ref["J"], proj=proj,
+                        lr_err=lr_err), flush=True)
+    assert np.abs(L.T @ L - np.eye(spec.rank)).max() < 1e-5
+    assert proj < 1e-4
+    assert agree >= 0.995
+    assert np.array_equal(rep["codes"], codes)
+    assert lr_err <= 1e-3
+    assert abs(res["J"] - ref["J"]) <= 5e-3 * ref["J"]
+
+
+@pytest.mark.timeout(900)
+def test_mlp_layers_full(ctx):
+    """MLP of a 1.7B-class decoder: gate/up (6144x2048, one shared Hessian)
+    against the whole oracle; down (2048x6144, 6144-wide Hessian) by sampled
+    blocks of H and the properties of U and the sweep."""
+    specs = synth.FULL["mlp"]
+    gate, up, down = specs
+    print("mlp: generating gate/up input", flush=True)
+    lg = synth.layer(gate, "cuda")
+    Wup = synth.weights(up, "cuda")
+    H = ctx.hessian(lg["X"])
+    U, info, lam = ctx.factor(H, lam_rel=gate.lam_rel)
+    rg = ctx.quantize(lg["W"], U, gate.bits, gate.group, gate.block, lam)
+    ru = ctx.quantize(Wup, U, up.bits, up.group, up.block, lam)
+    torch.cuda.synchronize()
+    print("mlp: oracle gate/up", flush=True)
+    Hr = o.hessian(synth.bits_to_numpy(lg["X"]))
+    assert np.linalg.norm(np32(H) - Hr) / np.linalg.norm(Hr) <= 1e-5
+    Hl, lam_r = o.damp(Hr, lam_rel=gate.lam_rel)
+    Ur = o.factor_u(Hl)
+    for name, r, Wt in (("gate", rg, lg["W"]), ("up", ru, Wup)):
+        rep = {}
+        check_sweep(r, np32(Wt).astype(np.float64), Ur, gate.bits, gate.group, gate.block, Hr, lam_r, report=rep)
+        print("mlp:", name, rep, flush=True)
+    del lg, H, U, Hr, Hl, Ur
+    print("mlp: down", flush=True)
+    ld = synth.layer(down, "cuda")
+    H = ctx.hessian(ld["X"])
+    U, info, lam = ctx.factor(H, lam_rel=down.lam_rel)
+    rd = ctx.quantize(ld["W"], U, down.bits, down.group, down.block, lam, want_err=True)
+    torch.cuda.synchronize()
+    Hn, Un = np32(H), np32(U)
+    Xb = synth.bits_to_numpy(ld["X"])
+    e = check_h_block(Hn, Xb, _cols(down.n, 200, 3))
+    assert np.array_equal(Hn, Hn.T)
+    assert lam == pytest.approx(down.lam_rel * float(np.mean(np.diag(Hn.astype(np.float64)))), rel=1e-6)
+    ratio = check_u_rows(Un, Hn, lam, _rows(down.n, 48, 4))
+    rows = _rows(down.out, 32, 5)
+    w = check_sweep_recurrence(np32(ld["W"])[rows], Un, np32(rd["codes"])[rows], np32(rd["scales"])[rows],
+                               np32(rd["zeros"])[rows], np32(rd["err"])[rows], down.bits, down.group)
+    E = np32(rd["err"]).astype(np.float64)
+    assert rd["J_lam"] == pytest.approx(float(np.sum(E * E)), rel=1e-6)
+    print("mlp: down H block err %.2e, U ratio %.3f, recurrence %s" % (e, ratio, w), flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_vit_batched_full(ctx):
+    """48 ViT-Base layers in one batched call: two layers (a 768-wide and a
+    3072-wide one) against the whole oracle, every layer by sampled blocks of
+    H and the properties of U and the sweep."""
+    specs = synth.FULL["vit"]
+    print("vit: generating %d layers" % len(specs), flush=True)
+    lays = [synth.layer(s, "cuda") for s in specs]
+    layers = [dict(W=l["W"], X=l["X"], bits=s.bits, group=s.group, block=s.block, lam_rel=s.lam_rel, want_err=True)
+              for s, l in zip(specs, lays)]
+    ctx.quantize_batched(layers)
+    torch.cuda.synchronize()
+    full = {0, next(i for i, s in enumerate(specs) if s.n == 3072)}
+    for i, (s, l, b) in enumerate(zip(specs, lays, layers)):
+        assert b["info"] == 0, s.name
+        Hn, Un = np32(b["H"]), np32(b["U"])
+        lam = s.lam_rel * float(np.mean(np.diag(Hn.astype(np.float64))))
+        if i in full:
+            print("vit: oracle", s.name, flush=True)
+            Hr = o.hessian(synth.bits_to_numpy(l["X"]))
+            assert np.linalg.norm(Hn - Hr) / np.linalg.norm(Hr) <= 1e-5
+            Hl, lam_r = o.damp(Hr, lam_rel=s.lam_rel)
+            rep = {}
+            check_sweep(b, np32(l["W"]).astype(np.float64), o.factor_u(Hl), s.bits, s.group, s.block, Hr, lam_r,
+                        report=rep)
+            print("vit:", s.name, rep, flush=True)
+            continue
+        Xb = synth.bits_to_numpy(l["X"])
+        check_h_block(Hn, Xb, _cols(s.n, 48, 10 + i))
+        check_u_rows(Un, Hn, lam, _rows(s.n, 16, 100 + i))
+        rows = _rows(s.out, 8, 200 + i)
+        check_sweep_recurrence(np32(l["W"])[rows], Un, np32(b["codes"])[rows], np32(b["scales"])[rows],
+                               np32(b["zeros"])[rows], np32(b["err"])[rows], s.bits, s.group)
+    print("vit: all layers checked", flush=True)
