@@ -41,7 +41,7 @@ def layer_flops(out, n, tokens, block, n_total=None):
     return dict(syrk=syrk, factor=factor, sweep=sweep, trail=trail, total=syrk + factor + sweep + trail)
 
 
-def cpu_baseline(spec, lay, max_rows=32, tok_sample=4096):
+def cpu_baseline(spec, lay, max_rows=512, tok_sample=32768):
     """The float64 oracle, as it stands, on a bounded sample of the same layer,
     scaled to ms per layer: Hessian on tok_sample tokens (scaled by tokens),
     the full damping + factor, and the sweep on max_rows rows (scaled by rows)."""
