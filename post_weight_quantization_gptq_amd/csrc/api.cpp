@@ -235,119 +235,119 @@ struct HessPlan {
   int nparts = 0;
 };
 
-// Split every (problem, upper tile) over token slices so that each XCD works
-// on its own slice, then even out the last, partly filled round of each XCD
-// by cutting its items into shorter token ranges.  The cut points of a problem
-// depend on that problem alone, so a layer gets the same bits whether it is
-// quantised alone or in a batch.
-void plan_hessian(const std::vector<HessJob>& jobs, int nxcd, int cus_per_xcd, uint16_t* xt, HessPlan& P) {
-  struct Item {
-    int prob, ti, tj, k0, k1;
-  };
-  std::vector<std::vector<Item>> lists(nxcd);
-  std::vector<int> ntile_of(jobs.size());
+// Interleaved bit order of (i, j): tiles close in this order share rows of X.
+static int morton2(int i, int j) {
+  int m = 0;
+  for (int b = 0; b < 10; ++b) m |= (((i >> b) & 1) << (2 * b + 1)) | (((j >> b) & 1) << (2 * b));
+  return m;
+}
+
+// Number of token slices for one layer's tiles: whole rounds of the chip at
+// one tile per CU, each task also paying for writing its partial (about ten
+// 32-token steps of time).  Depends on the layer alone.
+static int hess_slices(int ntile, long long chunks, int ncu) {
+  int best_s = 1;
+  long long best = -1;
+  for (int s = 1; s <= 64 && s <= std::max(1LL, chunks); ++s) {
+    const long long rounds = cdiv((long long)ntile * s, (long long)ncu);
+    const long long cost = rounds * (cdiv(chunks, (long long)s) + 10);
+    if (best < 0 || cost < best) {
+      best = cost;
+      best_s = s;
+    }
+  }
+  return best_s;
+}
+
+// Tasks of every layer: its upper 256x256 tiles times S token slices, slice
+// by slice, so that the whole chip streams one window of tokens at a time and
+// re-reads of X hit the L2/MALL.  Inside a slice the tiles go in Morton order,
+// cut into 8 groups that are dealt out in turn: consecutive workgroups land
+// on the 8 XCDs in turn, so each XCD works on one compact group of tiles that
+// shares rows of X in its own L2.  The cut points of a layer depend on that
+// layer alone, so a layer gets the same bits alone or in a batch.  The rows of
+// the transposed copy are padded by 256 tokens so that rows at the same token
+// offset spread over the L2 channels.
+void plan_hessian(const std::vector<HessJob>& jobs, int ncu, int nxcd, uint16_t* xt, HessPlan& P) {
   for (size_t p = 0; p < jobs.size(); ++p) {
     const HessJob& J = jobs[p];
     const int vec = (J.ldx % 8 == 0) && (((uintptr_t)J.X & 15) == 0);
     const int nt = cdiv(J.n, 256);
     const long long chunks = cdiv(J.tokens, 64);
     const int n_pad = nt * 256, t_pad = (int)(chunks * 64);
-    P.xprobs.push_back(XposeProb{J.X, J.ldx, xt, J.n, (int)J.tokens, n_pad, t_pad, vec, 0});
+    const int ldt = t_pad > 0 ? t_pad + 256 : 0;
+    P.xprobs.push_back(XposeProb{J.X, J.ldx, xt, J.n, (int)J.tokens, n_pad, t_pad, vec, ldt});
     if (t_pad > 0) P.xsegs.push_back(Seg{(int)p, 0, (t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
-    P.probs.push_back(SyrkProb{xt, t_pad});
-    xt += (size_t)n_pad * t_pad;
+    P.probs.push_back(SyrkProb{xt, ldt});
+    xt += (size_t)n_pad * ldt;
     P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate});
-    ntile_of[p] = nt;
-    if (J.tokens <= 0 || J.n <= 0) continue;
-    std::vector<std::vector<Item>> own(nxcd);
-    const int nsl = (int)std::max<long long>(1, std::min<long long>(nxcd, chunks / 32));
-    int tix = 0;
+    if (J.n <= 0) continue;
+    std::vector<std::pair<int, int>> tl;
     for (int ti = 0; ti < nt; ++ti)
-      for (int tj = ti; tj < nt; ++tj, ++tix)
-        for (int s = 0; s < nsl; ++s) {
-          const long long c0 = chunks * s / nsl, c1 = chunks * (s + 1) / nsl;
-          const int k0 = (int)(c0 * 64), k1 = (int)(c1 * 64);  // zero-padded past tokens
-          if (k1 <= k0) continue;
-          const int x = (nsl == nxcd) ? s : (tix + s) % nxcd;
-          own[x].push_back(Item{(int)p, ti, tj, k0, k1});
-        }
-    for (int x = 0; x < nxcd; ++x) {
-      std::vector<Item>& L = own[x];
-      const int M = (int)L.size();
-      const int rem = M % cus_per_xcd;
-      if (M > 0 && rem != 0) {
-        const int first = (M >= cus_per_xcd) ? M - rem : 0;
-        const int cnt = M - first;
-        const int f = std::max(1, cus_per_xcd / cnt);
-        if (f > 1) {
-          std::vector<Item> out(L.begin(), L.begin() + first);
-          for (int i = first; i < M; ++i) {
-            const Item it = L[i];
-            const int ch = cdiv(it.k1 - it.k0, 64);
-            const int pieces = std::min(f, ch);
-            for (int q = 0; q < pieces; ++q) {
-              const int a = it.k0 + (int)((long long)ch * q / pieces) * 64;
-              const int b = std::min(it.k1, it.k0 + (int)((long long)ch * (q + 1) / pieces) * 64);
-              if (b > a) out.push_back(Item{it.prob, it.ti, it.tj, a, b});
-            }
-          }
-          L.swap(out);
+      for (int tj = ti; tj < nt; ++tj) tl.push_back({ti, tj});
+    const int ntile = (int)tl.size();
+    if (J.tokens > 0) {
+      std::vector<std::pair<int, int>> mo = tl;
+      std::stable_sort(mo.begin(), mo.end(), [](const std::pair<int, int>& x, const std::pair<int, int>& y) {
+        return morton2(x.first, x.second) < morton2(y.first, y.second);
+      });
+      std::vector<int> ord;  // dealt order, indices into mo
+      const int G = std::max(1, std::min(nxcd, ntile)), base = ntile / G, rem = ntile % G;
+      for (int idx = 0; idx <= base; ++idx)
+        for (int g = 0; g < G; ++g)
+          if (idx < base + (g < rem ? 1 : 0)) ord.push_back(g * base + std::min(g, rem) + idx);
+      const long long c32 = t_pad / 32;
+      const int S = hess_slices(ntile, c32, ncu);
+      const int first = (int)P.tasks.size();
+      std::vector<int> pos(ntile);  // tile (canonical index) -> position inside a slice
+      for (int q = 0; q < ntile; ++q) {
+        const std::pair<int, int> t = mo[ord[q]];
+        const int ci = t.first * nt - t.first * (t.first - 1) / 2 + (t.second - t.first);
+        pos[ci] = q;
+      }
+      for (int sl = 0; sl < S; ++sl) {
+        const int k0 = (int)(32 * (c32 * sl / S)), k1 = (int)(32 * (c32 * (sl + 1) / S));
+        for (int q = 0; q < ntile; ++q) {
+          const std::pair<int, int> t = mo[ord[q]];
+          P.tasks.push_back(SyrkTask{(int)p, t.first, t.second, k0, k1, (int)P.tasks.size(), 0, 0});
         }
       }
-      lists[x].insert(lists[x].end(), L.begin(), L.end());
-    }
-  }
-  size_t maxlen = 0;
-  for (auto& L : lists) maxlen = std::max(maxlen, L.size());
-  P.tasks.assign(maxlen * nxcd, SyrkTask{0, 0, 0, 0, 0, -1, 0, 0});
-  // partial slots; remember each tile's parts in (k0) order
-  struct PartRef {
-    int prob, ti, tj, k0, part;
-  };
-  std::vector<PartRef> refs;
-  int part = 0;
-  for (size_t slot = 0; slot < maxlen; ++slot)
-    for (int x = 0; x < nxcd; ++x) {
-      if (slot >= lists[x].size()) continue;
-      const Item& it = lists[x][slot];
-      P.tasks[slot * nxcd + x] = SyrkTask{it.prob, it.ti, it.tj, it.k0, it.k1, part, 0, 0};
-      refs.push_back(PartRef{it.prob, it.ti, it.tj, it.k0, part});
-      ++part;
-    }
-  P.nparts = part;
-  std::sort(refs.begin(), refs.end(), [](const PartRef& a, const PartRef& b) {
-    if (a.prob != b.prob) return a.prob < b.prob;
-    if (a.ti != b.ti) return a.ti < b.ti;
-    if (a.tj != b.tj) return a.tj < b.tj;
-    return a.k0 < b.k0;
-  });
-  size_t r = 0;
-  for (size_t p = 0; p < jobs.size(); ++p) {
-    const int n = jobs[p].n, nt = ntile_of[p];
-    for (int ti = 0; ti < nt; ++ti)
-      for (int tj = ti; tj < nt; ++tj) {
+      for (int ci = 0; ci < ntile; ++ci) {
+        const int ti = tl[ci].first, tj = tl[ci].second;
         const int part0 = (int)P.partlist.size();
-        while (r < refs.size() && refs[r].prob == (int)p && refs[r].ti == ti && refs[r].tj == tj)
-          P.partlist.push_back(refs[r++].part);
-        const int np = (int)P.partlist.size() - part0;
+        for (int sl = 0; sl < S; ++sl) P.partlist.push_back(first + sl * ntile + pos[ci]);
         for (int a = 0; a < 4; ++a)
           for (int b = 0; b < 4; ++b) {
             if (ti == tj && a > b) continue;
             const int r0 = ti * 256 + 64 * a, c0 = tj * 256 + 64 * b;
-            if (r0 >= n || c0 >= n) continue;
-            P.rtasks.push_back(RedTask{(int)p, r0, c0, part0, np, 0, 0, 0});
+            if (r0 >= J.n || c0 >= J.n) continue;
+            P.rtasks.push_back(RedTask{(int)p, r0, c0, part0, S, 0, 0, 0});
           }
       }
+    } else {
+      // no tokens: every sub-block sums zero partials (H = 0, or H unchanged)
+      for (int ci = 0; ci < ntile; ++ci) {
+        const int ti = tl[ci].first, tj = tl[ci].second;
+        for (int a = 0; a < 4; ++a)
+          for (int b = 0; b < 4; ++b) {
+            const int r0 = ti * 256 + 64 * a, c0 = tj * 256 + 64 * b;
+            if ((ti == tj && a > b) || r0 >= J.n || c0 >= J.n) continue;
+            P.rtasks.push_back(RedTask{(int)p, r0, c0, 0, 0, 0, 0, 0});
+          }
+      }
+    }
   }
+  P.nparts = (int)P.tasks.size();
 }
 
 int run_hessian(gptq_ctx c, const std::vector<HessJob>& jobs) {
   size_t xt_elems = 0;
-  for (const HessJob& J : jobs) xt_elems += (size_t)cdiv(J.n, 256) * 256 * (size_t)cdiv(J.tokens, 64) * 64;
+  for (const HessJob& J : jobs)
+    if (J.tokens > 0) xt_elems += (size_t)cdiv(J.n, 256) * 256 * ((size_t)cdiv(J.tokens, 64) * 64 + 256);
   int rc = ensure(c, c->xt, xt_elems * sizeof(uint16_t));
   if (rc) return rc;
   HessPlan P;
-  plan_hessian(jobs, c->nxcd, std::max(1, c->ncu / c->nxcd), (uint16_t*)c->xt.p, P);
+  plan_hessian(jobs, c->ncu, c->nxcd, (uint16_t*)c->xt.p, P);
   if ((rc = ensure(c, c->partials, (size_t)std::max(P.nparts, 1) * 65536 * sizeof(float)))) return rc;
   int nxwg = 0;
   for (auto& sg : P.xsegs) {
@@ -383,7 +383,7 @@ int run_hessian64(gptq_ctx c, const uint16_t* X, long long tokens, long long ldx
   if (rc) return rc;
   uint16_t* xt = (uint16_t*)c->xt.p;
   const int vec = (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
-  std::vector<XposeProb> xprobs{XposeProb{X, ldx, xt, n, (int)tokens, n_pad, (int)t_pad, vec, 0}};
+  std::vector<XposeProb> xprobs{XposeProb{X, ldx, xt, n, (int)tokens, n_pad, (int)t_pad, vec, (int)t_pad}};
   std::vector<Seg> xsegs;
   if (t_pad > 0) xsegs.push_back(Seg{0, 0, (int)(t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
   const int nwx = xsegs.empty() ? 0 : xsegs[0].nwg;

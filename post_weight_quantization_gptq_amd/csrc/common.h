@@ -25,14 +25,14 @@ struct Seg {
 struct XposeProb {
   const uint16_t* X;
   long long ldx;
-  uint16_t* Xt;  // [n_pad][t_pad]
+  uint16_t* Xt;  // [n_pad][ldt], tokens [0, t_pad) written
   int n, tokens, n_pad, t_pad;
   int vec;  // rows of X are 16-byte aligned (16-byte loads allowed)
-  int pad0;
+  int ldt;  // row pitch of Xt in tokens (>= t_pad)
 };
 struct SyrkProb {
-  const uint16_t* Xt;  // feature-major copy [n_pad][t_pad], zero-padded
-  long long t_pad;
+  const uint16_t* Xt;  // feature-major copy [n_pad][ldt], zero-padded to t_pad tokens
+  long long ldt;
 };
 struct SyrkTask {
   int prob, ti, tj, k0, k1, part, pad0, pad1;

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void k_xpose(const XposeProb* __restrict__ pro
     const int idx = tid + 256 * q;
     const int f = idx >> 3, r8 = (idx & 7) * 8;  // feature f, tokens r8..r8+7
     const u32x4 o = *(const u32x4*)&T[f][r8];
-    *(u32x4*)(pb.Xt + (size_t)(f0 + f) * pb.t_pad + t0 + r8) = o;
+    *(u32x4*)(pb.Xt + (size_t)(f0 + f) * pb.ldt + t0 + r8) = o;
   }
 }
 
@@ -89,7 +89,7 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
   constexpr int L = DIAG ? 4 : 8;  // global_load_lds per lane per stage
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nsteps = (tk.k1 - tk.k0) / SYK_KT;
-  const size_t tp = (size_t)pb.t_pad;
+  const size_t tp = (size_t)pb.ldt;
   // Load slot: instruction q of wave w fills the 16 LDS rows 16(4q+w) ..
   // 16(4q+w)+15 (1 KB); lane -> row 16(4q+w) + lane/4 at chunk position
   // lane%4, holding token chunk (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16).
@@ -275,7 +275,7 @@ __device__ __forceinline__ void syrk64_tile(const SyrkProb& pb, const SyrkTask& 
                                             double* __restrict__ partials) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nsteps = (tk.k1 - tk.k0) / 32;
-  const size_t tp = (size_t)pb.t_pad;
+  const size_t tp = (size_t)pb.ldt;
   // instruction q of wave w fills LDS rows 16(4q+w)..+15 (1 KB): lane ->
   // row 16(4q+w) + lane/4 at chunk position lane%4 holding token chunk
   // (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16)
