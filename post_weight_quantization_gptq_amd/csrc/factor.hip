@@ -9,10 +9,11 @@
 // (2n^3/3 flops instead of 4n^3/3 for Cholesky -> inverse -> Cholesky).
 //
 // Cholesky: right-looking over 256-wide outer panels, each factored in four
-// 64-wide steps.  A step factors its 64x64 diagonal block (and inverts it)
-// inside one wave with the block in registers, then computes the panel rows
-// below as A_ik L_kk^{-T} on fp64 MFMA and updates the rest of the outer
-// panel; after the outer panel, one fp64 MFMA update with K = 256 reaches the
+// 64-wide steps.  A step factors its 64x64 diagonal block inside one wave
+// with the block's rows in registers (no barriers), inverts it on all four
+// waves (16x16 forward substitutions, then doubling on fp64 MFMA), then
+// computes the panel rows below as A_ik L_kk^{-T} on fp64 MFMA and updates
+// the rest of the outer panel; after the outer panel, one fp64 MFMA update with K = 256 reaches the
 // trailing lower triangle (four times less traffic over the trailing matrix
 // than updating it after every 64 columns).  The diagonal inverses L_kk^{-1}
 // are the base of the triangular inverse.  Inverse: recursive doubling over the diagonal
@@ -68,94 +69,160 @@ __global__ __launch_bounds__(256) void k_damp_fill(const FacProb* __restrict__ p
 }
 
 // ----------------------------------------------------------- Cholesky -----
-// Cholesky and inverse of one 64x64 diagonal block by the whole group.
-// Thread (tr, tc) = (tid / 16, tid % 16) keeps the 4x4 block of rows
-// 4tr..4tr+3, columns 4tc..4tc+3 in registers.  In: LT column-major
-// (LT[c][r] = block[r][c], r >= c), padded with the identity.  Out: YT =
-// L^{-1} column-major, *bad = first failing pivot or -1.
-// Iteration j: the owners of column j publish it; after one barrier every
-// thread forms l_r = a_rj / sqrt(a_jj) for its rows and columns and applies
-// the rank-1 update.  The inverse runs one column behind in the same loop
-// (Y row t = Z row t / L_tt, then Z rows r > t -= L_rt Y row t), so both
-// share the barrier; column and row broadcasts are double-buffered.
-__device__ __forceinline__ void leaf_block(double (*LT)[NB + 1], double (*YT)[NB + 1], double (*cbuf)[NB],
-                                           double (*ybuf)[NB], int* bad) {
-  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
-  double a[4][4], z[4][4], lrp[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-    for (int ci = 0; ci < 4; ++ci) {
-      const int r = 4 * tr + ri, c = 4 * tc + ci;
-      a[ri][ci] = (c <= r) ? LT[c][r] : 0.0;
-      z[ri][ci] = (r == c) ? 1.0 : 0.0;
-    }
-  double inv_prev = 1.0;
-  int fail = -1;
-#pragma unroll
-  for (int j = 0; j <= NB; ++j) {
-    if (j < NB && tc == (j >> 2)) {
-#pragma unroll
-      for (int ri = 0; ri < 4; ++ri) cbuf[j & 1][4 * tr + ri] = a[ri][j & 3];
-    }
-    if (j >= 1 && tr == ((j - 1) >> 2)) {
-#pragma unroll
-      for (int ci = 0; ci < 4; ++ci) {
-        const double y = z[(j - 1) & 3][ci] * inv_prev;
-        z[(j - 1) & 3][ci] = y;
-        ybuf[(j - 1) & 1][4 * tc + ci] = y;
-      }
-    }
-    __syncthreads();
-    double lr[4] = {0.0, 0.0, 0.0, 0.0};
-    if (j < NB) {
-      double d = cbuf[j & 1][j];
-      if (!(d > 0.0) || !__builtin_isfinite(d)) {  // uniform
-        fail = j;
-        break;
-      }
-      // 1/sqrt(d) from the hardware estimate and two Newton steps; sqrt(d) = d/sqrt(d)
-      double inv = __builtin_amdgcn_rsq(d);
-      inv = inv * (1.5 - 0.5 * d * inv * inv);
-      inv = inv * (1.5 - 0.5 * d * inv * inv);
-      const double sd = d * inv;
-      // multipliers, zero outside rows >= j and columns > j, so that the
-      // rank-1 update below needs no per-element test (entries above the
-      // diagonal are never read)
-      double lc[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const double vr = cbuf[j & 1][4 * tr + q] * inv;
-        const double vc = cbuf[j & 1][4 * tc + q] * inv;
-        lr[q] = (4 * tr + q >= j) ? vr : 0.0;
-        lc[q] = (4 * tc + q > j) ? vc : 0.0;
-      }
-#pragma unroll
-      for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-        for (int ci = 0; ci < 4; ++ci) a[ri][ci] -= lr[ri] * lc[ci];
-      inv_prev = inv;
-    }
-    if (j >= 1) {
-      const int t = j - 1;
-      double yc[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) yc[q] = ybuf[t & 1][4 * tc + q];
-#pragma unroll
-      for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-        for (int ci = 0; ci < 4; ++ci) z[ri][ci] -= lrp[ri] * yc[ci];
-    }
-    // L[r][j] for rows r > j (zero otherwise): the next inverse step's factors
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lrp[q] = (4 * tr + q > j) ? lr[q] : 0.0;
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), l);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Cholesky of the 64x64 diagonal block by one wave, without barriers.  Lane r
+// keeps row r in registers; the steps are instantiated one by one (template
+// recursion), so every register index is a constant.  Step j: the pivot comes
+// from lane j (readlane), 1/sqrt by the hardware estimate and two Newton
+// steps, every lane forms its multiplier l_r = a_rj / sqrt(a_jj) and the
+// multipliers go through LDS (broadcast reads, in order inside the wave; 16
+// in flight) for the rank-1 update of columns > j; entries above the
+// diagonal are don't-care.  In: LT[c][r] = block[r][c] (r >= c), padded with
+// the identity.  Out (may alias LT): Ls[r][c] = L[r][c] with zeros above the
+// diagonal, dv[r] = 1 / L[r][r].  Returns the first failing pivot or -1.
+struct CholWave {
+  double a[NB];
+  double dvr;
+  int fail;
+};
+
+template <int J>
+__device__ __forceinline__ void chol_step(CholWave& st, double* lb, int r) {
+  if (st.fail >= 0) return;  // uniform
+  const double d = readlane_f64(st.a[J], J);
+  if (!(d > 0.0) || !__builtin_isfinite(d)) {
+    st.fail = J;
+    return;
   }
-  if (tid == 0) *bad = fail;
-  if (fail < 0) {
+  double rs = __builtin_amdgcn_rsq(d);
+  rs = rs * (1.5 - 0.5 * d * rs * rs);
+  rs = rs * (1.5 - 0.5 * d * rs * rs);
+  const double l = (r > J) ? st.a[J] * rs : ((r == J) ? d * rs : 0.0);
+  st.a[J] = l;
+  if (r == J) st.dvr = rs;
+  if constexpr (J + 1 < NB) {
+    lb[r] = l;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int ri = 0; ri < 4; ++ri)
+    for (int k0 = J + 1; k0 < NB; k0 += 16) {
+      double lk[16];
 #pragma unroll
-      for (int ci = 0; ci < 4; ++ci) YT[4 * tc + ci][4 * tr + ri] = z[ri][ci];
+      for (int t = 0; t < 16; ++t)
+        if (k0 + t < NB) lk[t] = lb[k0 + t];
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        if (k0 + t < NB) st.a[k0 + t] -= l * lk[t];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int J>
+struct CholSteps {
+  __device__ __forceinline__ static void run(CholWave& st, double* lb, int r) {
+    chol_step<J>(st, lb, r);
+    CholSteps<J + 1>::run(st, lb, r);
+  }
+};
+template <>
+struct CholSteps<NB> {
+  __device__ __forceinline__ static void run(CholWave&, double*, int) {}
+};
+
+__device__ __forceinline__ int chol64_wave(double (*LT)[NB + 1], double (*Ls)[NB + 1], double* dv, double* lb) {
+  const int r = threadIdx.x & 63;
+  CholWave st;
+#pragma unroll
+  for (int c = 0; c < NB; ++c) st.a[c] = LT[c][r];
+  __builtin_amdgcn_wave_barrier();
+  st.dvr = 0.0;
+  st.fail = -1;
+  CholSteps<0>::run(st, lb, r);
+#pragma unroll
+  for (int c = 0; c < NB; ++c) Ls[r][c] = (c <= r) ? st.a[c] : 0.0;
+  dv[r] = st.dvr;
+  return st.fail;
+}
+
+// Y = L^{-1} of the 64x64 lower block by the four waves: the diagonal 16x16
+// inverses by forward substitution (wave w, lane = column), then two doubling
+// levels [[A,0],[B,C]]^{-1} = [[A^-1,0],[-C^-1 B A^-1, C^-1]] on fp64 MFMA
+// (16 -> 32: waves 0 and 1; 32 -> 64: one 16x16 output block per wave).
+// Ys is row-major with zeros above the diagonal; Tm is scratch [32][33].
+__device__ __forceinline__ void inv64_waves(double (*Ls)[NB + 1], const double* dv, double (*Ys)[NB + 1],
+                                            double (*Tm)[33]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  {
+    const int c = lane & 15, o = 16 * w;
+    double y[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      double s = (rr == c) ? 1.0 : 0.0;
+#pragma unroll
+      for (int kk = 0; kk < rr; ++kk) s -= Ls[o + rr][o + kk] * y[kk];
+      y[rr] = s * dv[o + rr];
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) Ys[o + rr][o + c] = y[rr];
+    }
+    // zeros above the diagonal blocks (read by the products below and by callers)
+    for (int e = lane; e < 16 * (NB - o - 16); e += 64) Ys[o + (e & 15)][o + 16 + (e >> 4)] = 0.0;
+  }
+  __syncthreads();
+  const int i16 = lane & 15, k4 = lane >> 4;
+  if (w < 2) {
+    // pair (2w, 2w+1): Y[b1][b0] = -Y[b1][b1] L[b1][b0] Y[b0][b0]
+    const int b0 = 32 * w, b1 = b0 + 16;
+    double (*T)[33] = Tm + 16 * w;  // rows 16w..16w+15 of the scratch, 16 columns used
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(Ls[b1 + i16][b0 + 4 * s + k4], Ys[b0 + 4 * s + k4][b0 + i16], acc, 0,
+                                                0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T[k4 + 4 * q][i16] = acc[q];
+    __builtin_amdgcn_wave_barrier();
+    f64x4 acc2 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(Ys[b1 + i16][b1 + 4 * s + k4], T[4 * s + k4][i16], acc2, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Ys[b1 + k4 + 4 * q][b0 + i16] = -acc2[q];
+  }
+  __syncthreads();
+  {
+    // Y[32:64][0:32] = -Y22 (L21 Y11); wave w owns output block (p, q)
+    const int p = w >> 1, q = w & 1;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb < q) continue;  // Y11 is lower triangular
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(Ls[32 + 16 * p + i16][16 * kb + 4 * s + k4],
+                                                  Ys[16 * kb + 4 * s + k4][16 * q + i16], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) Tm[16 * p + k4 + 4 * qq][16 * q + i16] = acc[qq];
+    __syncthreads();
+    f64x4 acc2 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb > p) continue;  // Y22 is lower triangular
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(Ys[32 + 16 * p + i16][32 + 16 * kb + 4 * s + k4],
+                                                   Tm[16 * kb + 4 * s + k4][16 * q + i16], acc2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) Ys[32 + 16 * p + k4 + 4 * qq][16 * q + i16] = -acc2[qq];
   }
   __syncthreads();
 }
@@ -166,11 +233,12 @@ __device__ __forceinline__ void leaf_block(double (*LT)[NB + 1], double (*YT)[NB
 // A_ik L_kk^{-T} on fp64 MFMA.
 __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ probs,
                                                     const Seg* __restrict__ segs, int nseg) {
-  __shared__ double LT[NB][NB + 1];
-  __shared__ double YT[NB][NB + 1];
-  __shared__ double Rs[NB][NB + 1];
-  __shared__ double cbuf[2][NB];
-  __shared__ double ybuf[2][NB];
+  __shared__ double LT[NB][NB + 1];  // the diagonal block, then L (row-major)
+  __shared__ double Ys[NB][NB + 1];  // L^{-1}, row-major
+  __shared__ double Rs[NB][NB + 1];  // this group's panel rows
+  __shared__ double Tm[32][33];
+  __shared__ double lb[NB];
+  __shared__ double dv[NB];
   __shared__ int bad;
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const FacProb pb = probs[sg.prob];
@@ -193,29 +261,33 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
     for (int q = 0; q < 16; ++q) {
       const int e = tid + 256 * q, r = e >> 6, c = e & 63;
       LT[c][r] = (r < m && c < m) ? ta[q] : ((r == c) ? 1.0 : 0.0);
-      YT[c][r] = 0.0;
       Rs[r][c] = tr[q];
     }
   }
   __syncthreads();
-  leaf_block(LT, YT, cbuf, ybuf, &bad);
+  if (tid < 64) {
+    const int f = chol64_wave(LT, LT, dv, lb);
+    if (tid == 0) bad = f;
+  }
+  __syncthreads();
   if (bad >= 0) {
     if (tid == 0 && i == k) atomicMax(pb.info, n - (k0 + bad));
     return;
   }
+  inv64_waves(LT, dv, Ys, Tm);
   if (i == k) {
     // Only L_kk^{-1} is kept: nothing reads the diagonal block of L again (the
     // updates read the panel rows below it, the inverse reads Y_kk), and the
     // other groups of this launch are still reading A_kk, so A_kk stays as is.
-    // the whole block, zeros above the diagonal included: the inverse's
-    // products read these tiles in full
+    // The whole block, zeros above the diagonal included: the inverse's
+    // products read these tiles in full.
     for (int e = tid; e < NB * NB; e += 256) {
       const int r = e >> 6, c = e & 63;
-      if (r < m && c < m) pb.Y[(size_t)(k0 + r) * n + k0 + c] = (c <= r) ? YT[c][r] : 0.0;
+      if (r < m && c < m) pb.Y[(size_t)(k0 + r) * n + k0 + c] = (c <= r) ? Ys[r][c] : 0.0;
     }
     return;
   }
-  // X = R Y^T: X(r, c) = sum_t R[r][t] Y[c][t] = sum_t R[r][t] YT[t][c]
+  // X = R Y^T: X(r, c) = sum_t R[r][t] Y[c][t]
   const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
   f64x4 acc[2][2];
 #pragma unroll
@@ -230,7 +302,7 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) av[mi] = Rs[32 * wr + 16 * mi + (lane & 15)][4 * kk + (lane >> 4)];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) bv[ni] = YT[4 * kk + (lane >> 4)][32 * wc + 16 * ni + (lane & 15)];
+    for (int ni = 0; ni < 2; ++ni) bv[ni] = Ys[32 * wc + 16 * ni + (lane & 15)][4 * kk + (lane >> 4)];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
