@@ -516,7 +516,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   Blob b;
   const size_t o_probs = b.add(probs);
   struct L {
-    int kind;  // 0 fill, 1 panel, 2 gemm, 4 makeu
+    int kind;  // 0 fill, 1 panel, 2 gemm (64 tiles), 3 gemm (128 tiles), 4 makeu
     size_t off;
     int nseg, nwg;
   };
@@ -559,15 +559,16 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
     add_launch(2, outer);
   }
   for (int s = 64; s < maxn; s *= 2) {
+    const int ts = 64;  // tile of the level's products
     for (int step = 0; step < 2; ++step) {
       std::vector<Seg> sg;
       for (int p = 0; p < np; ++p) {
         const int n = jobs[p].n;
         if (n <= s) continue;
-        const int npairs = cdiv(n - s, 2LL * s), tj = cdiv(s, 64);
+        const int npairs = cdiv(n - s, 2LL * s), tj = cdiv(s, ts);
         sg.push_back(Seg{p, 0, npairs * tj * tj, step == 0 ? GK_INV_STEP1 : GK_INV_STEP2, s, tj * tj, 0, 0});
       }
-      add_launch(2, sg);
+      add_launch(ts == 128 ? 3 : 2, sg);
     }
   }
   {
@@ -585,6 +586,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
       case 0: LAUNCH(c, "k_damp_fill", launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: LAUNCH(c, "k_chol_panel", launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 2: LAUNCH(c, "k_gemm64", launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 3: LAUNCH(c, "k_gemm128", launch_gemm128(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 4: LAUNCH(c, "k_make_u", launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
     }
   }

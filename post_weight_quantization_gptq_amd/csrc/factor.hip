@@ -284,6 +284,9 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
     for (int e = tid; e < NB * NB; e += 256) {
       const int r = e >> 6, c = e & 63;
       if (r < m && c < m) pb.Y[(size_t)(k0 + r) * n + k0 + c] = (c <= r) ? Ys[r][c] : 0.0;
+      // the block right of an even diagonal block lies inside the inverse's
+      // 128-wide product tiles and must read as zero
+      if ((k & 1) == 0 && r < m && k0 + NB + c < n) pb.Y[(size_t)(k0 + r) * n + k0 + NB + c] = 0.0;
     }
     return;
   }
@@ -322,14 +325,25 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
 }
 
 // --------------------------------------------------- fp64 MFMA products ---
-// One 64x64 output tile per workgroup, 4 waves of 32x32, v_mfma_f64_16x16x4.
+// One TS x TS output tile per workgroup (TS = 64 or 128), 4 waves of
+// TS/2 x TS/2, v_mfma_f64_16x16x4.
 //   C(i, j) = beta C(i, j) + alpha sum_{t in [kb, ke)} Aop(i, t) Bop(t, j)
 // Aop(i, t) = A[i * lda + t]; Bop(t, j) = B[t * sbk + j * sbj] (one of sbk,
 // sbj is 1).  The kind decides the operands from the problem's matrices.
-__global__ __launch_bounds__(256) void k_gemm64(const FacProb* __restrict__ probs,
-                                                const Seg* __restrict__ segs, int nseg) {
-  __shared__ double As[64][17];
-  __shared__ double Bs[16][65];
+// K chunks (32 for TS = 64, 16 for TS = 128) are staged through registers
+// into a double-buffered LDS pair: the loads of chunk c+1 are in flight while
+// chunk c is multiplied.  128-wide tiles halve the bytes per flop; the narrow
+// updates inside an outer panel use 64-wide tiles for parallelism.
+template <int TS>
+__global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs, const Seg* __restrict__ segs,
+                                              int nseg) {
+  constexpr int KC = (TS == 64) ? 32 : 16;  // k per chunk
+  constexpr int MB = TS / 32;               // 16x16 blocks per wave side
+  constexpr int TPR = 256 / TS;             // threads per row of a k-contiguous operand
+  constexpr int TPK = 256 / KC;             // threads per k row of a j-contiguous operand
+  constexpr int V = KC * TS / 256;          // values per thread per operand (8)
+  __shared__ double As[2][TS][KC + 1];
+  __shared__ double Bs[2][KC][TS + 1];
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const FacProb pb = probs[sg.prob];
   if (*pb.info != 0 || *pb.nonfinite != 0) return;
@@ -345,14 +359,14 @@ __global__ __launch_bounds__(256) void k_gemm64(const FacProb* __restrict__ prob
     // A[i][j] -= sum_{t in [kb, kb+kw)} A[i][t] A[j][t] for the lower tiles of
     // rows [c0, n) x columns [c0, c1)
     const int kb0 = sg.b, kw = sg.c, c0 = sg.d, c1 = sg.e;
-    const int nrow = (n - c0 + 63) / 64, ncol = (c1 - c0 + 63) / 64;
+    const int nrow = (n - c0 + TS - 1) / TS, ncol = (c1 - c0 + TS - 1) / TS;
     int b = 0, tt = t;
     while (b < ncol && tt >= nrow - b) {
       tt -= nrow - b;
       ++b;
     }
     const int a = b + tt;
-    const int i0 = c0 + 64 * a, j0 = c0 + 64 * b;
+    const int i0 = c0 + TS * a, j0 = c0 + TS * b;
     A = pb.A + (size_t)i0 * n + kb0;
     lda = n;
     B = pb.A + (size_t)j0 * n + kb0;
@@ -360,23 +374,23 @@ __global__ __launch_bounds__(256) void k_gemm64(const FacProb* __restrict__ prob
     sbj = n;
     C = pb.A + (size_t)i0 * n + j0;
     ldc = n;
-    mt = min(64, n - i0);
-    nt = min(64, c1 - j0);
+    mt = min(TS, n - i0);
+    nt = min(TS, c1 - j0);
     kb = 0;
     ke = kw;
     alpha = -1.0;
     beta = 1.0;
   } else {
     // level with block size s: pair q = A-block [a0, a0+s), C-block [c0, c0+sC)
-    const int s = sg.b, tiles_j = (s + 63) / 64;
-    const int pair_tiles = sg.c;  // tiles per pair (uniform: ceil(s/64)^2)
+    const int s = sg.b, tiles_j = (s + TS - 1) / TS;
+    const int pair_tiles = sg.c;  // tiles per pair (uniform: ceil(s/TS)^2)
     const int q = t / pair_tiles, tt = t % pair_tiles;
     const int a0 = 2 * q * s, c0 = a0 + s, sC = min(s, n - c0);
     const int ti = tt / tiles_j, tj = tt % tiles_j;
-    const int i0 = 64 * ti, j0 = 64 * tj;
+    const int i0 = TS * ti, j0 = TS * tj;
     if (i0 >= sC) return;
-    mt = min(64, sC - i0);
-    nt = min(64, s - j0);
+    mt = min(TS, sC - i0);
+    nt = min(TS, s - j0);
     double* Tq = pb.T + (size_t)q * s * s;  // one s x s slot per pair
     if (sg.a == GK_INV_STEP1) {
       // T = B_blk * Y_A, B_blk = C[c0.., a0..] (stored in A), Y_A lower
@@ -401,77 +415,127 @@ __global__ __launch_bounds__(256) void k_gemm64(const FacProb* __restrict__ prob
       C = pb.Y + (size_t)(c0 + i0) * n + a0 + j0;
       ldc = n;
       kb = 0;
-      ke = min(sC, i0 + 64);
+      ke = min(sC, i0 + TS);
       alpha = -1.0;
       beta = 0.0;
     }
-    // rows of A are offset by i0 already; the k index of Y_C starts at 0
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1;
-  f64x4 acc[2][2];
+  f64x4 acc[MB][MB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0;
 
-  for (int k0 = kb; k0 < ke; k0 += 16) {
-    {  // A chunk: 64 rows x 16 k
-      const int r = tid >> 2, kq = (tid & 3) * 4;
+  double ra[V], rb[V];
+  // k-contiguous operands: thread -> row tid / TPR, V/4 quads of k at a
+  // stride of KC/(V/4); j-contiguous: k row tid / TPK, V/4 quads of j at a
+  // stride of TS/(V/4).  Loads never branch: an out-of-range element reads a
+  // valid address of the same operand and is replaced by zero.
+  constexpr int NQ = V / 4;
+  const int lr = tid / TPR, lq = (tid % TPR) * 4;
+  const int kr = tid / TPK, jq = (tid % TPK) * 4;
+  auto load = [&](int k0) {
+    const bool rok = lr < mt;
+    const double* ap = A + (size_t)(rok ? lr : 0) * lda;
+#pragma unroll
+    for (int h = 0; h < NQ; ++h)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int kk = k0 + kq + u;
-        As[r][kq + u] = (r < mt && kk < ke) ? A[(size_t)r * lda + kk] : 0.0;
+        const int kk = k0 + lq + (KC / NQ) * h + u;
+        const bool ok = rok && kk < ke;
+        const double v = ap[ok ? kk : kb];
+        ra[4 * h + u] = ok ? v : 0.0;
       }
-    }
-    if (sbj == 1) {  // B chunk, j-contiguous: 16 k x 64 j
-      const int kr = tid >> 4, jq = (tid & 15) * 4;
+    if (sbj == 1) {
       const int kk = k0 + kr;
+      const bool kok = kk < ke;
+      const double* bp = B + (size_t)(kok ? kk : kb) * sbk;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = jq + u;
-        Bs[kr][j] = (kk < ke && j < nt) ? B[(size_t)kk * sbk + j] : 0.0;
-      }
-    } else {  // k-contiguous
-      const int j = tid >> 2, kq = (tid & 3) * 4;
+      for (int h = 0; h < NQ; ++h)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = k0 + kq + u;
-        Bs[kq + u][j] = (kk < ke && j < nt) ? B[(size_t)j * sbj + kk] : 0.0;
-      }
+        for (int u = 0; u < 4; ++u) {
+          const int j = jq + (TS / NQ) * h + u;
+          const bool ok = kok && j < nt;
+          const double v = bp[ok ? j : 0];
+          rb[4 * h + u] = ok ? v : 0.0;
+        }
+    } else {
+      const bool jok = lr < nt;
+      const double* bp = B + (size_t)(jok ? lr : 0) * sbj;
+#pragma unroll
+      for (int h = 0; h < NQ; ++h)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int kk = k0 + lq + (KC / NQ) * h + u;
+          const bool ok = jok && kk < ke;
+          const double v = bp[ok ? kk : kb];
+          rb[4 * h + u] = ok ? v : 0.0;
+        }
     }
-    __syncthreads();
+  };
+  auto store = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      double a[2], b[2];
+    for (int h = 0; h < NQ; ++h)
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) a[mi] = As[32 * wr + 16 * mi + (lane & 15)][4 * kk + (lane >> 4)];
+      for (int u = 0; u < 4; ++u) As[buf][lr][lq + (KC / NQ) * h + u] = ra[4 * h + u];
+    if (sbj == 1) {
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) b[ni] = Bs[4 * kk + (lane >> 4)][32 * wc + 16 * ni + (lane & 15)];
+      for (int h = 0; h < NQ; ++h)
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+        for (int u = 0; u < 4; ++u) Bs[buf][kr][jq + (TS / NQ) * h + u] = rb[4 * h + u];
+    } else {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+      for (int h = 0; h < NQ; ++h)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Bs[buf][lq + (KC / NQ) * h + u][lr] = rb[4 * h + u];
+    }
+  };
+  if (kb < ke) {
+    load(kb);
+    store(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = kb; k0 < ke; k0 += KC) {
+    const bool more = k0 + KC < ke;
+    if (more) load(k0 + KC);
+#pragma unroll
+    for (int kk = 0; kk < KC / 4; ++kk) {
+      double a[MB], b[MB];
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi) a[mi] = As[buf][(TS / 2) * wr + 16 * mi + (lane & 15)][4 * kk + (lane >> 4)];
+#pragma unroll
+      for (int ni = 0; ni < MB; ++ni) b[ni] = Bs[buf][4 * kk + (lane >> 4)][(TS / 2) * wc + 16 * ni + (lane & 15)];
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < MB; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     }
+    if (more) store(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < MB; ++ni)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 32 * wr + 16 * mi + (lane >> 4) + 4 * r;
-        const int j = 32 * wc + 16 * ni + (lane & 15);
+        const int i = (TS / 2) * wr + 16 * mi + (lane >> 4) + 4 * r;
+        const int j = (TS / 2) * wc + 16 * ni + (lane & 15);
         if (i < mt && j < nt) {
           double* cp = C + (size_t)i * ldc + j;
           *cp = (beta != 0.0 ? *cp : 0.0) + alpha * acc[mi][ni][r];
         }
       }
 }
+
+
 
 // U[i][j] = Y[n-1-i][n-1-j] for j >= i (upper), 0 below; fp32.  4 rows per WG.
 __global__ __launch_bounds__(256) void k_make_u(const FacProb* __restrict__ probs,
@@ -502,5 +566,6 @@ hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st) {
 
 SEG_LAUNCH(launch_damp_fill, k_damp_fill, 256)
 SEG_LAUNCH(launch_chol_panel, k_chol_panel, 256)
-SEG_LAUNCH(launch_gemm64, k_gemm64, 256)
+SEG_LAUNCH(launch_gemm64, k_gemm<64>, 256)
+SEG_LAUNCH(launch_gemm128, k_gemm<128>, 256)
 SEG_LAUNCH(launch_make_u, k_make_u, 256)
