@@ -689,19 +689,19 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
         if (jobs[p].block == B && k < L[p].nblk) s.push_back(Seg{p, 0, cdiv(jobs[p].out, 16), k, 0, 0, 0, 0});
       add_launch(2, B, s);
     }
-    std::vector<Seg> t;
+    std::vector<Seg> tn, tf;  // inside the super-block (64 tiles), past it (128 tiles)
     for (int p = 0; p < nl; ++p) {
       if (k >= L[p].nblk) continue;
       const int B = jobs[p].block, n = jobs[p].n, nt = jobs[p].nt, sb = sbk[p];
       const int b0 = k * B, b1 = std::min(b0 + B, n);
       const int sb0 = (k / sb) * sb * B, sb1 = std::min(sb0 + sb * B, n);
-      const int mrow = cdiv(jobs[p].out, 128);
       if (b1 < sb1)  // rest of the super-block
-        t.push_back(Seg{p, 0, mrow * cdiv(sb1 - b1, 128), (k % sb) * B, b0, b1 - b0, b1, sb1});
+        tn.push_back(Seg{p, 0, cdiv(jobs[p].out, 64) * cdiv(sb1 - b1, 64), (k % sb) * B, b0, b1 - b0, b1, sb1});
       if (b1 == sb1 && sb1 < nt)  // end of the super-block: all columns past it
-        t.push_back(Seg{p, 0, mrow * cdiv(nt - sb1, 128), 0, sb0, sb1 - sb0, sb1, nt});
+        tf.push_back(Seg{p, 0, cdiv(jobs[p].out, 128) * cdiv(nt - sb1, 128), 0, sb0, sb1 - sb0, sb1, nt});
     }
-    add_launch(3, 0, t);
+    add_launch(3, 64, tn);
+    add_launch(3, 128, tf);
   }
   uint8_t* d = nullptr;
   if ((rc = upload(c, b, &d))) return rc;
@@ -712,7 +712,7 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
       case 0: LAUNCH(c, "k_init_work", launch_init_work(dL, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: LAUNCH(c, "k_rowfit", launch_rowfit(dL, sg, l.nseg, l.nwg, c->stream)); break;
       case 2: LAUNCH(c, "k_sweep", launch_sweep(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3: LAUNCH(c, "k_trail", launch_trail(dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 3: LAUNCH(c, "k_trail", launch_trail(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
     }
   }
   LAUNCH(c, "k_objective", launch_objective(dL, nl, c->stream));

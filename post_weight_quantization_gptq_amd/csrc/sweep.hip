@@ -289,103 +289,120 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   }
 }
 
-// W[:, j0:j1] -= E[:, eoff:eoff+K] U[kb:kb+K, j0:j1] for one 128x128 tile, in
-// K chunks of 128, on v_mfma_f32_32x32x2f32 (4 waves of 64x64).
-__global__ __launch_bounds__(256, 1) void k_trail(const QLayer* __restrict__ L,
-                                                  const Seg* __restrict__ segs, int nseg) {
-  __shared__ float As[128][129];
-  __shared__ __attribute__((aligned(16))) float Bs[128][132];
+// W[:, j0:j1] -= E[:, eoff:eoff+K] U[kb:kb+K, j0:j1] for one TS x TS tile
+// (TS = 128 for the products past a super-block, 64 for the narrow ones
+// inside it), on v_mfma_f32_32x32x2f32 (4 waves of TS/2 x TS/2).  K chunks of
+// 32 go through registers into a double-buffered LDS pair, so the loads of
+// chunk c+1 are in flight while chunk c is multiplied.
+template <int TS>
+__global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, const Seg* __restrict__ segs, int nseg) {
+  constexpr int KC = 32;
+  constexpr int MB = TS / 64;        // 32x32 blocks per wave side
+  constexpr int TPR = 256 / TS;      // threads per E row
+  constexpr int VA = KC / TPR;       // E values per thread (multiple of 4)
+  constexpr int VB = TS / 8;         // U values per thread (8 threads per k row)
+  __shared__ float As[2][TS][KC + 1];
+  __shared__ __attribute__((aligned(16))) float Bs[2][KC][TS + 4];
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const QLayer ly = L[sg.prob];
   const int eoff = sg.a, kb = sg.b, K = sg.c, j0 = sg.d, j1 = sg.e;
   const int nt = ly.nt;
-  const int tiles_j = (j1 - j0 + 127) / 128;
+  const int tiles_j = (j1 - j0 + TS - 1) / TS;
   const int t = blockIdx.x - sg.wg0;
-  const int i0 = 128 * (t / tiles_j), jj0 = j0 + 128 * (t % tiles_j);
-  const int mt = min(128, ly.out - i0), ntc = min(128, j1 - jj0);
+  const int i0 = TS * (t / tiles_j), jj0 = j0 + TS * (t % tiles_j);
+  const int mt = min(TS, ly.out - i0), ntc = min(TS, j1 - jj0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1;
-  f32x16 acc[2][2];
+  f32x16 acc[MB][MB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  for (int kc = 0; kc < K; kc += 128) {
-    const int kw = min(128, K - kc);
-    {
-      // E chunk (128 rows x 128 k) and U chunk (128 k x 128 cols): 16 + 16
-      // loads of 16 B per thread, all in flight before any LDS store
-      const bool evec = (ly.ldE % 4) == 0 && ((eoff + kc) % 4) == 0;
-      const bool uvec = (nt % 4) == 0 && (jj0 % 4) == 0;
-      f32x4 ta[16], tb[16];
+
+  const int ar = tid / TPR, ak = (tid % TPR) * VA;  // E: row, first k
+  const int bk = tid >> 3, bj = (tid & 7) * VB;     // U: k row, first column
+  const bool arow_ok = ar < mt;
+  const float* ap = ly.Eb + (size_t)(i0 + (arow_ok ? ar : 0)) * ly.ldE + eoff;
+  const bool evec = (ly.ldE % 4) == 0 && (eoff % 4) == 0;
+  const bool uvec = (nt % 4) == 0 && (jj0 % 4) == 0 && (((uintptr_t)ly.U) & 15) == 0;
+  f32x4 ra[VA / 4], rb[VB / 4];
+  auto load = [&](int kc) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int idx = tid + 256 * q;
-        const int r = idx >> 5, k4 = (idx & 31) * 4;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (r < mt) {
-          const float* src = ly.Eb + (size_t)(i0 + r) * ly.ldE + eoff + kc + k4;
-          if (evec && k4 + 4 <= kw) {
-            v = *(const f32x4*)src;
-          } else {
+    for (int q = 0; q < VA / 4; ++q) {
+      const int k = kc + ak + 4 * q;
+      if (evec && arow_ok && k + 4 <= K) {
+        ra[q] = *(const f32x4*)(ap + k);
+      } else {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = (k4 + u < kw) ? src[u] : 0.f;
-          }
+        for (int u = 0; u < 4; ++u) {
+          const bool ok = arow_ok && k + u < K;
+          const float v = ap[ok ? k + u : 0];
+          ra[q][u] = ok ? v : 0.f;
         }
-        ta[q] = v;
-      }
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int idx = tid + 256 * q;
-        const int k = idx >> 5, jq = (idx & 31) * 4;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (k < kw) {
-          const float* src = ly.U + (size_t)(kb + kc + k) * nt + jj0 + jq;
-          if (uvec && jq + 4 <= ntc) {
-            v = *(const f32x4*)src;
-          } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = (jq + u < ntc) ? src[u] : 0.f;
-          }
-        }
-        tb[q] = v;
-      }
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int idx = tid + 256 * q;
-        const int r = idx >> 5, k4 = (idx & 31) * 4;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) As[r][k4 + u] = ta[q][u];
-        const int k = idx >> 5, jq = (idx & 31) * 4;
-        *(f32x4*)&Bs[k][jq] = tb[q];
       }
     }
-    __syncthreads();
-    const int ksteps = (kw + 1) >> 1;
-    for (int kk = 0; kk < ksteps; ++kk) {
-      float av[2], bv[2];
+    const int k = kc + bk;
+    const bool kok = k < K;
+    const float* bp = ly.U + (size_t)(kb + (kok ? k : 0)) * nt + jj0;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) av[mi] = As[64 * wr + 32 * mi + (lane & 31)][2 * kk + (lane >> 5)];
+    for (int q = 0; q < VB / 4; ++q) {
+      const int j = bj + 4 * q;
+      if (uvec && kok && j + 4 <= ntc) {
+        rb[q] = *(const f32x4*)(bp + j);
+      } else {
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) bv[ni] = Bs[2 * kk + (lane >> 5)][64 * wc + 32 * ni + (lane & 31)];
+        for (int u = 0; u < 4; ++u) {
+          const bool ok = kok && j + u < ntc;
+          const float v = bp[ok ? j + u : 0];
+          rb[q][u] = ok ? v : 0.f;
+        }
+      }
+    }
+  };
+  auto store = [&](int buf) {
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+    for (int q = 0; q < VA / 4; ++q)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+      for (int u = 0; u < 4; ++u) As[buf][ar][ak + 4 * q + u] = ra[q][u];
+#pragma unroll
+    for (int q = 0; q < VB / 4; ++q) *(f32x4*)&Bs[buf][bk][bj + 4 * q] = rb[q];
+  };
+  if (K > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int kc = 0; kc < K; kc += KC) {
+    const bool more = kc + KC < K;
+    if (more) load(kc + KC);
+#pragma unroll
+    for (int kk = 0; kk < KC / 2; ++kk) {
+      float av[MB], bv[MB];
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi) av[mi] = As[buf][(TS / 2) * wr + 32 * mi + (lane & 31)][2 * kk + (lane >> 5)];
+#pragma unroll
+      for (int ni = 0; ni < MB; ++ni) bv[ni] = Bs[buf][2 * kk + (lane >> 5)][(TS / 2) * wc + 32 * ni + (lane & 31)];
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < MB; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
     }
+    if (more) store(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < MB; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = 64 * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int j = 64 * wc + 32 * ni + (lane & 31);
+        const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
         if (i < mt && j < ntc) ly.Ww[(size_t)(i0 + i) * nt + jj0 + j] -= acc[mi][ni][r];
       }
 }
@@ -438,7 +455,14 @@ __global__ __launch_bounds__(256) void k_objective(const QLayer* __restrict__ L,
 
 QSEG_LAUNCH(launch_init_work, k_init_work, 256)
 QSEG_LAUNCH(launch_rowfit, k_rowfit, 256)
-QSEG_LAUNCH(launch_trail, k_trail, 256)
+hipError_t launch_trail(int ts, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st) {
+  if (nwg <= 0) return hipSuccess;
+  if (ts == 64)
+    hipLaunchKernelGGL(k_trail<64>, dim3(nwg), dim3(256), 0, st, L, segs, nseg);
+  else
+    hipLaunchKernelGGL(k_trail<128>, dim3(nwg), dim3(256), 0, st, L, segs, nseg);
+  return hipGetLastError();
+}
 
 hipError_t launch_sweep(int block, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st) {
   if (nwg <= 0) return hipSuccess;
