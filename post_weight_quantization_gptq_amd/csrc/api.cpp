@@ -235,6 +235,13 @@ struct HessPlan {
   int nparts = 0;
 };
 
+// The tiles can read X directly (no transposed copy) when its rows are
+// 16-byte aligned and n is a multiple of 8 (16-byte feature chunks never
+// cross the end of a row).
+static bool hess_direct(const HessJob& J) {
+  return J.tokens > 0 && (J.ldx % 8) == 0 && (((uintptr_t)J.X) & 15) == 0 && (J.n % 8) == 0;
+}
+
 // Interleaved bit order of (i, j): tiles close in this order share rows of X.
 static int morton2(int i, int j) {
   int m = 0;
@@ -275,11 +282,17 @@ void plan_hessian(const std::vector<HessJob>& jobs, int ncu, int nxcd, uint16_t*
     const int nt = cdiv(J.n, 256);
     const long long chunks = cdiv(J.tokens, 64);
     const int n_pad = nt * 256, t_pad = (int)(chunks * 64);
-    const int ldt = t_pad > 0 ? t_pad + 256 : 0;
-    P.xprobs.push_back(XposeProb{J.X, J.ldx, xt, J.n, (int)J.tokens, n_pad, t_pad, vec, ldt});
-    if (t_pad > 0) P.xsegs.push_back(Seg{(int)p, 0, (t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
-    P.probs.push_back(SyrkProb{xt, ldt});
-    xt += (size_t)n_pad * ldt;
+    if (hess_direct(J)) {
+      // the tiles read X itself (transposing LDS reads); no copy
+      P.xprobs.push_back(XposeProb{J.X, J.ldx, nullptr, J.n, (int)J.tokens, n_pad, t_pad, vec, 0});
+      P.probs.push_back(SyrkProb{J.X, J.ldx, 1, (int)J.tokens, J.n, 0});
+    } else {
+      const int ldt = t_pad > 0 ? t_pad + 256 : 0;
+      P.xprobs.push_back(XposeProb{J.X, J.ldx, xt, J.n, (int)J.tokens, n_pad, t_pad, vec, ldt});
+      if (t_pad > 0) P.xsegs.push_back(Seg{(int)p, 0, (t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
+      P.probs.push_back(SyrkProb{xt, ldt, 0, (int)J.tokens, J.n, 0});
+      xt += (size_t)n_pad * ldt;
+    }
     P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate});
     if (J.n <= 0) continue;
     std::vector<std::pair<int, int>> tl;
@@ -343,7 +356,7 @@ void plan_hessian(const std::vector<HessJob>& jobs, int ncu, int nxcd, uint16_t*
 int run_hessian(gptq_ctx c, const std::vector<HessJob>& jobs) {
   size_t xt_elems = 0;
   for (const HessJob& J : jobs)
-    if (J.tokens > 0) xt_elems += (size_t)cdiv(J.n, 256) * 256 * ((size_t)cdiv(J.tokens, 64) * 64 + 256);
+    if (J.tokens > 0 && !hess_direct(J)) xt_elems += (size_t)cdiv(J.n, 256) * 256 * ((size_t)cdiv(J.tokens, 64) * 64 + 256);
   int rc = ensure(c, c->xt, xt_elems * sizeof(uint16_t));
   if (rc) return rc;
   HessPlan P;
@@ -387,7 +400,7 @@ int run_hessian64(gptq_ctx c, const uint16_t* X, long long tokens, long long ldx
   std::vector<Seg> xsegs;
   if (t_pad > 0) xsegs.push_back(Seg{0, 0, (int)(t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
   const int nwx = xsegs.empty() ? 0 : xsegs[0].nwg;
-  std::vector<SyrkProb> probs{SyrkProb{xt, t_pad}};
+  std::vector<SyrkProb> probs{SyrkProb{xt, t_pad, 0, (int)tokens, n, 0}};
   std::vector<RedProb64> rprobs{RedProb64{H, n, 0}};
   const int nt = cdiv(n, 128);
   const int ntile = nt * (nt + 1) / 2;

@@ -31,8 +31,16 @@ struct XposeProb {
   int ldt;  // row pitch of Xt in tokens (>= t_pad)
 };
 struct SyrkProb {
-  const uint16_t* Xt;  // feature-major copy [n_pad][ldt], zero-padded to t_pad tokens
+  // direct == 0: Xt is the feature-major copy [n_pad][ldt], zero-padded to
+  // t_pad tokens.  direct == 1: Xt is X itself, token-major [tokens][ldt]
+  // (16-byte aligned rows, n a multiple of 8); rows past `tokens` and
+  // features past n are never read.
+  const uint16_t* Xt;
   long long ldt;
+  int direct;
+  int tokens;
+  int n;
+  int pad0;
 };
 struct SyrkTask {
   int prob, ti, tj, k0, k1, part, pad0, pad1;

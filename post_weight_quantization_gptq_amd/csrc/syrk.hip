@@ -83,32 +83,69 @@ struct VmWait {
   static constexpr int value = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
 };
 
-template <bool DIAG>
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// TR = false: operands from the feature-major copy Xt, one 16-byte row chunk
+// per MFMA lane.  TR = true: operands straight from X (token-major).  A stage
+// then holds 32 token rows of 256 features (512 B each, 16-byte chunks
+// XOR-swizzled by 4 (row % 4)), and the fragments come out of LDS with the
+// transposing read ds_read_b64_tr_b16: in each 16-lane group, lane i points
+// at 4 features of token (i / 4) and receives 4 tokens of one feature, so
+// two such reads give a lane the 8 consecutive tokens of its feature that
+// the 32x32x16 MFMA wants, with no copy of X.
+template <bool DIAG, bool TR>
 __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk, uint8_t* lds,
                                           float* __restrict__ partials) {
   constexpr int L = DIAG ? 4 : 8;  // global_load_lds per lane per stage
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nsteps = (tk.k1 - tk.k0) / SYK_KT;
   const size_t tp = (size_t)pb.ldt;
-  // Load slot: instruction q of wave w fills the 16 LDS rows 16(4q+w) ..
-  // 16(4q+w)+15 (1 KB); lane -> row 16(4q+w) + lane/4 at chunk position
-  // lane%4, holding token chunk (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16).
-  const int lrow = 16 * w + (lane >> 2);
-  const int tchunk = (lane & 3) ^ (lane >> 4);
-  const uint16_t* ga = pb.Xt + (size_t)(tk.ti * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
-  const uint16_t* gb = pb.Xt + (size_t)(tk.tj * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
+  const uint16_t* ga;
+  const uint16_t* gb;
+  size_t gstep, gq;  // element offsets per step and per instruction
+  int tok0 = 0, trow = 0;
+  if (!TR) {
+    // Load slot: instruction q of wave w fills the 16 LDS rows 16(4q+w) ..
+    // 16(4q+w)+15 (1 KB); lane -> row 16(4q+w) + lane/4 at chunk position
+    // lane%4, holding token chunk (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16).
+    const int lrow = 16 * w + (lane >> 2);
+    const int tchunk = (lane & 3) ^ (lane >> 4);
+    ga = pb.Xt + (size_t)(tk.ti * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
+    gb = pb.Xt + (size_t)(tk.tj * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
+    gstep = SYK_KT;
+    gq = 64 * tp;
+  } else {
+    // instruction q of wave w fills token rows 2(4q+w), 2(4q+w)+1 (1 KB);
+    // lane -> row 2(4q+w) + lane/32 at chunk position lane%32, holding
+    // feature chunk (lane%32) ^ 4 (row % 4).  Chunks past n read chunk 0.
+    trow = 2 * w + (lane >> 5);
+    const int chunk = (lane & 31) ^ (4 * (trow & 3));
+    const int fa = tk.ti * 256 + 8 * chunk, fb = tk.tj * 256 + 8 * chunk;
+    ga = pb.Xt + (fa < pb.n ? fa : tk.ti * 256);
+    gb = pb.Xt + (fb < pb.n ? fb : tk.tj * 256);
+    tok0 = tk.k0;
+    gstep = 0;
+    gq = 0;
+  }
   auto issue = [&](int step, int stage) {
     uint8_t* base = lds + stage * SYK_STB;
-    const size_t off = (size_t)step * SYK_KT;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(ga + (size_t)(64 * q) * tp + off),
-                                       (lds_void*)(base + (4 * q + w) * 1024), 16, 0, 0);
-    if (!DIAG) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(gb + (size_t)(64 * q) * tp + off),
-                                         (lds_void*)(base + SYK_OPB + (4 * q + w) * 1024), 16, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      size_t off;
+      if (!TR) {
+        off = (size_t)q * gq + (size_t)step * gstep;
+      } else {
+        // token row of this lane; rows past the end read the last row (the
+        // stage's tail is zeroed in LDS before use)
+        int t = tok0 + step * SYK_KT + 8 * q + trow;
+        t = t < pb.tokens ? t : pb.tokens - 1;
+        off = (size_t)t * tp;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(ga + off), (lds_void*)(base + (4 * q + w) * 1024), 16, 0, 0);
+      if (!DIAG)
+        __builtin_amdgcn_global_load_lds((const void*)(gb + off), (lds_void*)(base + SYK_OPB + (4 * q + w) * 1024), 16,
+                                         0, 0);
     }
   };
   // Fragment rows of this lane: arow + 32m (A), brow + 32q (B); all have
@@ -116,13 +153,53 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
   const int arow = 128 * (w >> 1) + (lane & 31);
   const int brow = 128 * (w & 1) + (lane & 31);
   const int sw = (lane >> 2) & 3;
+  // TR: 16-lane group g = lane/16, i = lane%16: features 16(g%2) + 4(i%4) of
+  // the 32-feature block, tokens 8(g/2) + i/4 (+4 for the second read)
+  const int tg = lane >> 4, ti4 = lane & 15;
+  const int tr_tok = 8 * (tg >> 1) + (ti4 >> 2);
+  const int tr_f = 16 * (tg & 1) + 4 * (ti4 & 3);
+  auto tr_addr = [&](const uint8_t* st, int f, int tok) -> const lds_v4i16* {
+    const int c = f >> 3, half = (f >> 2) & 1;
+    return (const lds_v4i16*)(st + tok * 512 + ((c ^ (4 * (tok & 3))) << 4) + 8 * half);
+  };
   auto rd = [&](const uint8_t* st, int ks, bf16x8* fa, bf16x8* fb) {
-    const int ch = ((2 * ks + (lane >> 5)) ^ sw) * 16;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) fa[m] = *(const bf16x8*)(st + (arow + 32 * m) * 64 + ch);
     const uint8_t* sb = DIAG ? st : st + SYK_OPB;
+    if (!TR) {
+      const int ch = ((2 * ks + (lane >> 5)) ^ sw) * 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) fb[q] = *(const bf16x8*)(sb + (brow + 32 * q) * 64 + ch);
+      for (int m = 0; m < 4; ++m) fa[m] = *(const bf16x8*)(st + (arow + 32 * m) * 64 + ch);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fb[q] = *(const bf16x8*)(sb + (brow + 32 * q) * 64 + ch);
+    } else {
+      const int tok = 16 * ks + tr_tok;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int f = 128 * (w >> 1) + 32 * m + tr_f;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(st, f, tok));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(st, f, tok + 4));
+        const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        fa[m] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = 128 * (w & 1) + 32 * q + tr_f;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(sb, f, tok));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(sb, f, tok + 4));
+        const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        fb[q] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  };
+  // TR: zero the token rows of stage `stage` (step `step`) past the end of X
+  auto zero_tail = [&](int step, int stage) {
+    const int t0 = tok0 + step * SYK_KT;
+    if (!TR || t0 + SYK_KT <= pb.tokens) return;  // uniform
+    const int valid = pb.tokens - t0;  // may be <= 0
+    uint8_t* base = lds + stage * SYK_STB;
+    for (int e = tid; e < (DIAG ? 1 : 2) * SYK_KT * 32; e += 256) {
+      const int op = e / (SYK_KT * 32), row = (e / 32) % SYK_KT, c = e % 32;
+      if (row >= valid) *(u32x4*)(base + op * SYK_OPB + row * 512 + c * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
   };
 
   f32x16 acc[4][4];
@@ -150,6 +227,10 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
   __builtin_amdgcn_s_waitcnt(VmWait<2 * L>::value);  // stage 0 has landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+  if (TR && tok0 + SYK_KT > pb.tokens) {  // uniform: a tail already in stage 0
+    zero_tail(0, 0);
+    __syncthreads();
+  }
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   rd(lds, 0, a0, b0);
   for (int s = 0; s < nsteps; ++s) {
@@ -166,6 +247,10 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     __builtin_amdgcn_s_waitcnt(VmWait<L>::value);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    if (TR && s + 1 < nsteps && tok0 + (s + 2) * SYK_KT > pb.tokens) {  // uniform
+      zero_tail(s + 1, (s + 1) & 3);
+      __syncthreads();
+    }
     issue(min(s + 3, last), (s + 3) & 3);
     rd(lds + ((s + 1) & 3) * SYK_STB, 0, a0, b0);
     mma(a1, b1);
@@ -199,10 +284,17 @@ __global__ __launch_bounds__(256, 1) void k_syrk(const SyrkProb* __restrict__ pr
   const SyrkTask tk = tasks[blockIdx.x];
   if (tk.part < 0) return;
   const SyrkProb pb = probs[tk.prob];
-  if (tk.ti == tk.tj)
-    syrk_tile<true>(pb, tk, lds, partials);
-  else
-    syrk_tile<false>(pb, tk, lds, partials);
+  if (pb.direct) {
+    if (tk.ti == tk.tj)
+      syrk_tile<true, true>(pb, tk, lds, partials);
+    else
+      syrk_tile<false, true>(pb, tk, lds, partials);
+  } else {
+    if (tk.ti == tk.tj)
+      syrk_tile<true, false>(pb, tk, lds, partials);
+    else
+      syrk_tile<false, false>(pb, tk, lds, partials);
+  }
 }
 
 // Sum the partials of one 64x64 sub-block of an upper tile in list order,
