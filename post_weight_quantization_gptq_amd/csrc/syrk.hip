@@ -94,10 +94,14 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // at 4 features of token (i / 4) and receives 4 tokens of one feature, so
 // two such reads give a lane the 8 consecutive tokens of its feature that
 // the 32x32x16 MFMA wants, with no copy of X.
-template <bool DIAG, bool TR>
+template <bool DIAG, bool TR, int NW>
 __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk, uint8_t* lds,
                                           float* __restrict__ partials) {
-  constexpr int L = DIAG ? 4 : 8;  // global_load_lds per lane per stage
+  constexpr int NI = 16 / NW;                 // global_load_lds per operand per lane per stage
+  constexpr int L = DIAG ? NI : 2 * NI;       // ... for both operands
+  constexpr int WC = NW / 2;                  // waves across the tile's columns (2 down)
+  constexpr int NBF = 8 / WC;                 // 32-column B fragments per wave
+  constexpr int NTH = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nsteps = (tk.k1 - tk.k0) / SYK_KT;
   const size_t tp = (size_t)pb.ldt;
@@ -106,18 +110,19 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
   size_t gstep, gq;  // element offsets per step and per instruction
   int tok0 = 0, trow = 0;
   if (!TR) {
-    // Load slot: instruction q of wave w fills the 16 LDS rows 16(4q+w) ..
-    // 16(4q+w)+15 (1 KB); lane -> row 16(4q+w) + lane/4 at chunk position
-    // lane%4, holding token chunk (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16).
+    // Load slot: instruction q of wave w fills the 16 LDS rows 16(NW q+w) ..
+    // 16(NW q+w)+15 (1 KB); lane -> row 16(NW q+w) + lane/4 at chunk
+    // position lane%4, holding token chunk (lane%4) ^ ((row/4)%4) =
+    // (lane%4) ^ (lane/16).
     const int lrow = 16 * w + (lane >> 2);
     const int tchunk = (lane & 3) ^ (lane >> 4);
     ga = pb.Xt + (size_t)(tk.ti * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
     gb = pb.Xt + (size_t)(tk.tj * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
     gstep = SYK_KT;
-    gq = 64 * tp;
+    gq = 16 * NW * tp;
   } else {
-    // instruction q of wave w fills token rows 2(4q+w), 2(4q+w)+1 (1 KB);
-    // lane -> row 2(4q+w) + lane/32 at chunk position lane%32, holding
+    // instruction q of wave w fills token rows 2(NW q+w), 2(NW q+w)+1 (1 KB);
+    // lane -> row 2(NW q+w) + lane/32 at chunk position lane%32, holding
     // feature chunk (lane%32) ^ 4 (row % 4).  Chunks past n read chunk 0.
     trow = 2 * w + (lane >> 5);
     const int chunk = (lane & 31) ^ (4 * (trow & 3));
@@ -131,27 +136,28 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
   auto issue = [&](int step, int stage) {
     uint8_t* base = lds + stage * SYK_STB;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NI; ++q) {
       size_t off;
       if (!TR) {
         off = (size_t)q * gq + (size_t)step * gstep;
       } else {
         // token row of this lane; rows past the end read the last row (the
         // stage's tail is zeroed in LDS before use)
-        int t = tok0 + step * SYK_KT + 8 * q + trow;
+        int t = tok0 + step * SYK_KT + 2 * NW * q + trow;
         t = t < pb.tokens ? t : pb.tokens - 1;
         off = (size_t)t * tp;
       }
-      __builtin_amdgcn_global_load_lds((const void*)(ga + off), (lds_void*)(base + (4 * q + w) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ga + off), (lds_void*)(base + (NW * q + w) * 1024), 16, 0, 0);
       if (!DIAG)
-        __builtin_amdgcn_global_load_lds((const void*)(gb + off), (lds_void*)(base + SYK_OPB + (4 * q + w) * 1024), 16,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(gb + off), (lds_void*)(base + SYK_OPB + (NW * q + w) * 1024),
+                                         16, 0, 0);
     }
   };
   // Fragment rows of this lane: arow + 32m (A), brow + 32q (B); all have
-  // (row/4)%4 == (lane/4)%4.
-  const int arow = 128 * (w >> 1) + (lane & 31);
-  const int brow = 128 * (w & 1) + (lane & 31);
+  // (row/4)%4 == (lane/4)%4.  Wave w: rows 128 (w / WC), columns
+  // (256 / WC) (w % WC) of the tile.
+  const int arow = 128 * (w / WC) + (lane & 31);
+  const int brow = (256 / WC) * (w % WC) + (lane & 31);
   const int sw = (lane >> 2) & 3;
   // TR: 16-lane group g = lane/16, i = lane%16: features 16(g%2) + 4(i%4) of
   // the 32-feature block, tokens 8(g/2) + i/4 (+4 for the second read)
@@ -169,20 +175,20 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
 #pragma unroll
       for (int m = 0; m < 4; ++m) fa[m] = *(const bf16x8*)(st + (arow + 32 * m) * 64 + ch);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) fb[q] = *(const bf16x8*)(sb + (brow + 32 * q) * 64 + ch);
+      for (int q = 0; q < NBF; ++q) fb[q] = *(const bf16x8*)(sb + (brow + 32 * q) * 64 + ch);
     } else {
       const int tok = 16 * ks + tr_tok;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int f = 128 * (w >> 1) + 32 * m + tr_f;
+        const int f = 128 * (w / WC) + 32 * m + tr_f;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(st, f, tok));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(st, f, tok + 4));
         const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         fa[m] = __builtin_bit_cast(bf16x8, v);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = 128 * (w & 1) + 32 * q + tr_f;
+      for (int q = 0; q < NBF; ++q) {
+        const int f = (256 / WC) * (w % WC) + 32 * q + tr_f;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(sb, f, tok));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(sb, f, tok + 4));
         const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -196,24 +202,24 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     if (!TR || t0 + SYK_KT <= pb.tokens) return;  // uniform
     const int valid = pb.tokens - t0;  // may be <= 0
     uint8_t* base = lds + stage * SYK_STB;
-    for (int e = tid; e < (DIAG ? 1 : 2) * SYK_KT * 32; e += 256) {
+    for (int e = tid; e < (DIAG ? 1 : 2) * SYK_KT * 32; e += NTH) {
       const int op = e / (SYK_KT * 32), row = (e / 32) % SYK_KT, c = e % 32;
       if (row >= valid) *(u32x4*)(base + op * SYK_OPB + row * 512 + c * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NBF];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < NBF; ++q)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][q][r] = 0.f;
   auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < NBF; ++q)
         acc[m][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[q], acc[m][q], 0, 0, 0);
   };
 
@@ -231,17 +237,21 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     zero_tail(0, 0);
     __syncthreads();
   }
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  bf16x8 a0[4], b0[NBF], a1[4], b1[NBF];
+  constexpr int NRD = (4 + NBF) * (TR ? 2 : 1);  // LDS reads per sub-step
+  constexpr int NMF = 4 * NBF;                   // MFMAs per sub-step
+  constexpr int NIL = NRD < NMF ? NRD : NMF;     // interleaved pairs
   rd(lds, 0, a0, b0);
   for (int s = 0; s < nsteps; ++s) {
     rd(lds + (s & 3) * SYK_STB, 1, a1, b1);
     mma(a0, b0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NIL; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if constexpr (NMF > NIL) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NIL, 0);
+    if constexpr (NRD > NIL) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
     // stage s+1 has landed (only stage s+2 may still be in flight) for this
     // wave, and after the barrier for every wave; stage s-1 is free
     __builtin_amdgcn_s_waitcnt(VmWait<L>::value);
@@ -256,11 +266,12 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     mma(a1, b1);
     __builtin_amdgcn_sched_group_barrier(0x020, L, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NIL; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if constexpr (NMF > NIL) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NIL, 0);
+    if constexpr (NRD > NIL) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
   }
   __builtin_amdgcn_s_waitcnt(VmWait<0>::value);  // no copy into LDS outlives the group
 
@@ -268,32 +279,33 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < NBF; ++q)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 128 * (w >> 1) + 32 * m + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = 128 * (w & 1) + 32 * q + (lane & 31);
+        const int row = 128 * (w / WC) + 32 * m + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = (256 / WC) * (w % WC) + 32 * q + (lane & 31);
         P[row * 256 + col] = acc[m][q][r];
       }
 }
 
-__global__ __launch_bounds__(256, 1) void k_syrk(const SyrkProb* __restrict__ probs,
-                                                 const SyrkTask* __restrict__ tasks,
-                                                 float* __restrict__ partials) {
+#define SYK_NW 8  // waves per workgroup (2 per SIMD)
+__global__ __launch_bounds__(64 * SYK_NW, 1) void k_syrk(const SyrkProb* __restrict__ probs,
+                                                         const SyrkTask* __restrict__ tasks,
+                                                         float* __restrict__ partials) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[SYK_NST * SYK_STB];
   const SyrkTask tk = tasks[blockIdx.x];
   if (tk.part < 0) return;
   const SyrkProb pb = probs[tk.prob];
   if (pb.direct) {
     if (tk.ti == tk.tj)
-      syrk_tile<true, true>(pb, tk, lds, partials);
+      syrk_tile<true, true, SYK_NW>(pb, tk, lds, partials);
     else
-      syrk_tile<false, true>(pb, tk, lds, partials);
+      syrk_tile<false, true, SYK_NW>(pb, tk, lds, partials);
   } else {
     if (tk.ti == tk.tj)
-      syrk_tile<true, false>(pb, tk, lds, partials);
+      syrk_tile<true, false, SYK_NW>(pb, tk, lds, partials);
     else
-      syrk_tile<false, false>(pb, tk, lds, partials);
+      syrk_tile<false, false, SYK_NW>(pb, tk, lds, partials);
   }
 }
 
@@ -518,7 +530,7 @@ hipError_t launch_xpose(const XposeProb* probs, const Seg* segs, int nseg, int n
 hipError_t launch_syrk(const SyrkProb* probs, const SyrkTask* tasks, int ntasks, float* partials,
                        hipStream_t st) {
   if (ntasks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_syrk, dim3(ntasks), dim3(256), 0, st, probs, tasks, partials);
+  hipLaunchKernelGGL(k_syrk, dim3(ntasks), dim3(64 * SYK_NW), 0, st, probs, tasks, partials);
   return hipGetLastError();
 }
 
