@@ -245,13 +245,7 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
   for (int s = 0; s < nsteps; ++s) {
     rd(lds + (s & 3) * SYK_STB, 1, a1, b1);
     mma(a0, b0);
-#pragma unroll
-    for (int i = 0; i < NIL; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if constexpr (NMF > NIL) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NIL, 0);
-    if constexpr (NRD > NIL) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
+
     // stage s+1 has landed (only stage s+2 may still be in flight) for this
     // wave, and after the barrier for every wave; stage s-1 is free
     __builtin_amdgcn_s_waitcnt(VmWait<L>::value);
@@ -264,14 +258,7 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     issue(min(s + 3, last), (s + 3) & 3);
     rd(lds + ((s + 1) & 3) * SYK_STB, 0, a0, b0);
     mma(a1, b1);
-    __builtin_amdgcn_sched_group_barrier(0x020, L, 0);
-#pragma unroll
-    for (int i = 0; i < NIL; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if constexpr (NMF > NIL) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NIL, 0);
-    if constexpr (NRD > NIL) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
+
   }
   __builtin_amdgcn_s_waitcnt(VmWait<0>::value);  // no copy into LDS outlives the group
 
