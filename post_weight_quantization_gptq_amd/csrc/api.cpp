@@ -374,8 +374,9 @@ int run_hessian(gptq_ctx c, const std::vector<HessJob>& jobs) {
   uint8_t* d = nullptr;
   rc = upload(c, b, &d);
   if (rc) return rc;
-  LAUNCH(c, "k_xpose", launch_xpose((const XposeProb*)(d + o_xprobs), (const Seg*)(d + o_xsegs), (int)P.xsegs.size(), nxwg,
-                         c->stream));
+  if (nxwg > 0)  // no transposed copy when every X is read in place
+    LAUNCH(c, "k_xpose", launch_xpose((const XposeProb*)(d + o_xprobs), (const Seg*)(d + o_xsegs), (int)P.xsegs.size(),
+                                      nxwg, c->stream));
   LAUNCH(c, "k_syrk", launch_syrk((const SyrkProb*)(d + o_probs), (const SyrkTask*)(d + o_tasks),
                         (int)P.tasks.size(), (float*)c->partials.p, c->stream));
   LAUNCH(c, "k_syrk_reduce", launch_syrk_reduce((const RedProb*)(d + o_rprobs), (const RedTask*)(d + o_rtasks),
