@@ -34,7 +34,7 @@ struct gptq_ctx_s {
   int ncu = 256;
   int nxcd = 8;
   std::string err;
-  DevBuf partials, xt, facA, facY, facT, work, eblk, objp, slots, blob, lora;
+  DevBuf partials, xt, facA, facY, work, eblk, objp, slots, blob, lora;
   void* hblob = nullptr;  // pinned staging for the task tables
   size_t hblob_cap = 0;
   void* hsmall = nullptr;  // pinned read-back area
@@ -475,26 +475,15 @@ struct FacJob {
   float* U;
 };
 
-size_t inv_scratch_doubles(int n) {
-  size_t best = 64 * 64;
-  for (int s = 64; s < n; s *= 2) {
-    const int npairs = cdiv(n - s, 2LL * s);
-    best = std::max(best, (size_t)npairs * s * s);
-  }
-  return best;
-}
-
-// Enqueue the factor of every job.  A/Y/T offsets (in doubles) into facA/facY/facT.
+// Enqueue the factor of every job.  A/Y offsets (in doubles) into facA/facY.
 int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool assembled_A = false,
                double** A_out = nullptr) {
   const int np = (int)jobs.size();
-  std::vector<size_t> oA(np), oT(np);
-  size_t totA = 0, totT = 0;
+  std::vector<size_t> oA(np);
+  size_t totA = 0;
   for (int p = 0; p < np; ++p) {
     oA[p] = totA;
     totA += (size_t)jobs[p].n * jobs[p].n;
-    oT[p] = totT;
-    totT += inv_scratch_doubles(jobs[p].n);
   }
   int rc;
   if (!assembled_A) {
@@ -502,7 +491,6 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
     if (rc) return rc;
   }
   if ((rc = ensure(c, c->facY, totA * sizeof(double)))) return rc;
-  if ((rc = ensure(c, c->facT, totT * sizeof(double)))) return rc;
   std::vector<FacProb> probs(np);
   int maxnb = 0, maxn = 0;
   for (int p = 0; p < np; ++p) {
@@ -511,7 +499,6 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
     f.H = J.H;
     f.A = (double*)c->facA.p + oA[p];
     f.Y = (double*)c->facY.p + oA[p];
-    f.T = (double*)c->facT.p + oT[p];
     f.U = J.U;
     f.n = J.n;
     f.ldh = J.ldh;
@@ -530,7 +517,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   Blob b;
   const size_t o_probs = b.add(probs);
   struct L {
-    int kind;  // 0 fill, 1 panel, 2 gemm (64 tiles), 3 gemm (128 tiles), 4 makeu
+    int kind;  // 0 fill, 1 panel, 2 gemm (general, 64 tiles), 3 ring gemm 64, 4 ring gemm 128, 5 makeu
     size_t off;
     int nseg, nwg;
   };
@@ -544,51 +531,60 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
     if (nwg == 0) return;
     launches.push_back(L{kind, b.add(segs), (int)segs.size(), nwg});
   };
+  // The ring-staged products need every K range and row pitch to be a
+  // multiple of 64 (16-byte aligned chunks of 16 doubles).
+  bool ring = true;
+  for (const FacJob& J : jobs) ring = ring && (J.n % 64) == 0;
   {
     std::vector<Seg> s;
     for (int p = 0; p < np; ++p)
       if (jobs[p].H) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 4), 0, 0, 0, 0, 0});
     add_launch(0, s);
   }
-  // Cholesky: outer panels of 256 columns, four 64-column steps each
+  // Cholesky and Y = L^{-1}: outer panels of 256 columns, four 64-column
+  // steps each.  Step k: the panel launch (every 64-block of the problem),
+  // then the updates of the rest of the outer panel (L columns [c0, P1) of
+  // every row below; Y rows [c0, P1)), or at the end of the outer panel the
+  // trailing updates with K = P1 - P0 (L's trailing triangle; Y rows past P1).
   for (int k = 0; k < maxnb; ++k) {
     std::vector<Seg> pan, inner, outer;
+    int outer_rows = 0;
     for (int p = 0; p < np; ++p) {
       const int n = jobs[p].n, nb = cdiv(n, 64);
       if (k >= nb) continue;
-      pan.push_back(Seg{p, 0, nb - k, k, 0, 0, 0, 0});
+      pan.push_back(Seg{p, 0, nb, k, 0, 0, 0, 0});
       const int k0 = 64 * k, pw = std::min(64, n - k0);
       const int P0 = (k0 / 256) * 256, P1 = std::min(P0 + 256, n);
       const int c0 = k0 + pw;
       if (c0 < P1) {  // rest of the outer panel
         const int nrow = cdiv(n - c0, 64), ncol = cdiv(P1 - c0, 64);
         inner.push_back(Seg{p, 0, ncol * nrow - ncol * (ncol - 1) / 2, GK_CHOL_TRAIL, k0, pw, c0, P1});
-      } else if (P1 < n) {  // end of the outer panel: trailing update with K = P1 - P0
-        const int m = cdiv(n - P1, 64);
-        outer.push_back(Seg{p, 0, m * (m + 1) / 2, GK_CHOL_TRAIL, P0, P1 - P0, P1, n});
+        inner.push_back(Seg{p, 0, cdiv(P1 - c0, 64) * cdiv(c0, 64), GK_ZUPD, k0, pw, c0, P1});
+      } else if (P1 < n) {  // end of the outer panel: trailing updates with K = P1 - P0
+        outer.push_back(Seg{p, 0, 0, GK_CHOL_TRAIL, P0, P1 - P0, P1, n});
+        outer.push_back(Seg{p, 0, 0, GK_ZUPD, P0, P1 - P0, P1, n});
+        outer_rows = std::max(outer_rows, n - P1);
+      }
+    }
+    // 128-wide tiles while the trailing part gives about two tiles per CU
+    const int ots = (ring && outer_rows >= 1024) ? 128 : 64;
+    for (Seg& sg : outer) {
+      const int n = jobs[sg.prob].n;
+      if (sg.a == GK_CHOL_TRAIL) {
+        const int m = cdiv(n - sg.d, ots);
+        sg.nwg = m * (m + 1) / 2;
+      } else {
+        sg.nwg = cdiv(n - sg.d, ots) * cdiv(sg.b + sg.c, ots);
       }
     }
     add_launch(1, pan);
-    add_launch(2, inner);
-    add_launch(2, outer);
-  }
-  for (int s = 64; s < maxn; s *= 2) {
-    const int ts = 64;  // tile of the level's products
-    for (int step = 0; step < 2; ++step) {
-      std::vector<Seg> sg;
-      for (int p = 0; p < np; ++p) {
-        const int n = jobs[p].n;
-        if (n <= s) continue;
-        const int npairs = cdiv(n - s, 2LL * s), tj = cdiv(s, ts);
-        sg.push_back(Seg{p, 0, npairs * tj * tj, step == 0 ? GK_INV_STEP1 : GK_INV_STEP2, s, tj * tj, 0, 0});
-      }
-      add_launch(ts == 128 ? 3 : 2, sg);
-    }
+    add_launch(ring ? 3 : 2, inner);
+    add_launch(!ring ? 2 : (ots == 128 ? 4 : 3), outer);
   }
   {
     std::vector<Seg> s;
     for (int p = 0; p < np; ++p) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 4), 0, 0, 0, 0, 0});
-    add_launch(4, s);
+    add_launch(5, s);
   }
   uint8_t* d = nullptr;
   if ((rc = upload(c, b, &d))) return rc;
@@ -600,8 +596,9 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
       case 0: LAUNCH(c, "k_damp_fill", launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: LAUNCH(c, "k_chol_panel", launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 2: LAUNCH(c, "k_gemm64", launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3: LAUNCH(c, "k_gemm128", launch_gemm128(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 4: LAUNCH(c, "k_make_u", launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 3: LAUNCH(c, "k_gemm_ring64", launch_gemm_ring64(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 4: LAUNCH(c, "k_gemm_ring128", launch_gemm_ring128(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 5: LAUNCH(c, "k_make_u", launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
     }
   }
   return GPTQ_OK;
@@ -801,7 +798,7 @@ GPTQ_API int gptq_destroy(gptq_ctx c) {
   {
     DeviceGuard g(c->device);
     (void)hipStreamSynchronize(c->stream);
-    DevBuf* bufs[] = {&c->partials, &c->xt, &c->facA, &c->facY, &c->facT, &c->work, &c->eblk,
+    DevBuf* bufs[] = {&c->partials, &c->xt, &c->facA, &c->facY, &c->work, &c->eblk,
                       &c->objp, &c->slots, &c->blob, &c->lora};
     for (DevBuf* b : bufs)
       if (b->p) (void)hipFree(b->p);

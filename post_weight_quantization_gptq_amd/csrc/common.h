@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef double f64x4 __attribute__((__vector_size__(4 * sizeof(double))));
+typedef double f64x2 __attribute__((__vector_size__(2 * sizeof(double))));
 
 // A grouped launch covers several problems (layers).  Each problem owns a
 // contiguous range [wg0, wg0 + nwg) of the grid; a..d are kernel-specific.
@@ -67,9 +68,8 @@ struct RedProb64 {
 //   Y: C^{-1} (lower), T: scratch of the triangular inverse
 struct FacProb {
   const float* H;  // input [n][ldh] fp32 (null when A was assembled elsewhere)
-  double* A;
-  double* Y;
-  double* T;
+  double* A;       // [n][n]: P H_lam P (lower), overwritten by L
+  double* Y;       // [n][n]: L^{-1}, built row block by row block
   float* U;        // output [n][ldu]
   int n;
   int ldh;
@@ -81,7 +81,12 @@ struct FacProb {
   int* nonfinite;  // device slot
 };
 
-enum GemmKind { GK_CHOL_TRAIL = 0, GK_INV_STEP1 = 1, GK_INV_STEP2 = 2 };
+// GK_CHOL_TRAIL: A(i, j) -= sum_t L(i, t) L(j, t) on the lower tiles of rows
+//   [d, n) x columns [d, e), t in [b, b + c).
+// GK_ZUPD: Y(i, j) -= sum_t L(i, t) Y(t, j) on rows [d, e) x columns
+//   [0, b + c), t in [b, b + c); columns from b on are written for the first
+//   time (no accumulate).
+enum GemmKind { GK_CHOL_TRAIL = 0, GK_ZUPD = 1 };
 
 // ------------------------------------------------------------------ sweep --
 struct QLayer {
@@ -101,6 +106,14 @@ struct QLayer {
   int eoff_blk;     // column offset of one block inside it (= block)
   int sbk;          // blocks per super-block
   int pad0;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding).
+template <int N>
+struct VmWait {
+  static constexpr int value = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
 };
 
 __device__ __forceinline__ int find_seg(const Seg* __restrict__ segs, int nseg, int wg) {

@@ -13,12 +13,16 @@
 // with the block's rows in registers (no barriers), inverts it on all four
 // waves (16x16 forward substitutions, then doubling on fp64 MFMA), then
 // computes the panel rows below as A_ik L_kk^{-T} on fp64 MFMA and updates
-// the rest of the outer panel; after the outer panel, one fp64 MFMA update with K = 256 reaches the
-// trailing lower triangle (four times less traffic over the trailing matrix
-// than updating it after every 64 columns).  The diagonal inverses L_kk^{-1}
-// are the base of the triangular inverse.  Inverse: recursive doubling over the diagonal
-// blocks, [[A,0],[B,C]]^{-1} = [[A^-1,0],[-C^-1 B A^-1, C^-1]], two fp64 MFMA
-// products per level for all block pairs at once.
+// the rest of the outer panel; after the outer panel, one fp64 MFMA update
+// with K = 256 reaches the trailing lower triangle (four times less traffic
+// over the trailing matrix than updating it after every 64 columns).
+// Inverse: Y = L^{-1} by blocked forward substitution of L Y = I run in step
+// with the factorization.  Step k finishes block row k of Y
+// (Y_kj = L_kk^{-1} B_kj, B_kj = -sum_{t<k} L_kt Y_tj) in the same launch as
+// the panel, and B_ik -= L_ik Y_k: joins the Cholesky updates: the rows of
+// the outer panel right away, the rows past it in the outer update (K = 256
+// again).  So the inverse adds no serial steps and no long-K products, and
+// its n^3/3 flops ride in launches that are there anyway.
 #include "common.h"
 #include "launch.h"
 
@@ -227,15 +231,22 @@ __device__ __forceinline__ void inv64_waves(double (*Ls)[NB + 1], const double* 
   __syncthreads();
 }
 
-// Panel step k (64 columns starting at k0): workgroup (k, i) for row blocks
-// i >= k.  Every group factors the diagonal block (the same way); group k
-// writes L_kk^{-1}, the others compute their rows of the panel as
-// A_ik L_kk^{-T} on fp64 MFMA.
+// Panel step k (64 columns starting at k0), one workgroup per 64-block of
+// the problem.  Every group factors the diagonal block the same way and
+// inverts it; then
+//   - group for row block i > k: its rows of the panel, L_ik = A_ik L_kk^{-T};
+//   - group for row block k: writes L_kk^{-1} as Y_kk and zeros the rest of
+//     its rows of the 256-wide diagonal block of Y (read as a whole by the
+//     products of the outer step);
+//   - group for column block j < k: Y_kj = L_kk^{-1} B_kj, where B_kj holds
+//     -sum_{t<k} L_kt Y_tj from the updates of the earlier steps (forward
+//     substitution of L Y = I, one block row per step).
+// The products run on fp64 MFMA, 4 waves of 32 x 32.
 __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ probs,
                                                     const Seg* __restrict__ segs, int nseg) {
   __shared__ double LT[NB][NB + 1];  // the diagonal block, then L (row-major)
   __shared__ double Ys[NB][NB + 1];  // L^{-1}, row-major
-  __shared__ double Rs[NB][NB + 1];  // this group's panel rows
+  __shared__ double Rs[NB][NB + 1];  // this group's panel rows, or B_kj
   __shared__ double Tm[32][33];
   __shared__ double lb[NB];
   __shared__ double dv[NB];
@@ -243,11 +254,13 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const FacProb pb = probs[sg.prob];
   if (*pb.info != 0 || *pb.nonfinite != 0) return;
-  const int n = pb.n, k = sg.a, i = k + (blockIdx.x - sg.wg0);
+  const int n = pb.n, k = sg.a, nb = (n + NB - 1) / NB, g = blockIdx.x - sg.wg0;
   const int k0 = k * NB, m = min(NB, n - k0);
+  const bool yrole = g >= nb - k;                 // Y_kj for column block j
+  const int i = yrole ? k : k + g, j = yrole ? g - (nb - k) : 0;
   const int tid = threadIdx.x;
   double* A = pb.A;
-  const int r0 = i * NB, mr = (i == k) ? 0 : min(NB, n - r0);
+  const int r0 = i * NB, mr = yrole ? m : ((i == k) ? 0 : min(NB, n - r0));
   {
     // both 64x64 blocks: 16 + 16 loads per thread, all in flight together
     double ta[16], tr[16];
@@ -255,7 +268,10 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
     for (int q = 0; q < 16; ++q) {
       const int e = tid + 256 * q, r = e >> 6, c = e & 63;  // coalesced over c
       ta[q] = (r < m && c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
-      tr[q] = (r < mr && c < m) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0;
+      if (yrole)
+        tr[q] = (r < m) ? pb.Y[(size_t)(k0 + r) * n + NB * j + c] : 0.0;
+      else
+        tr[q] = (r < mr && c < m) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0;
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -271,26 +287,26 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
   }
   __syncthreads();
   if (bad >= 0) {
-    if (tid == 0 && i == k) atomicMax(pb.info, n - (k0 + bad));
+    if (tid == 0 && g == 0) atomicMax(pb.info, n - (k0 + bad));
     return;
   }
   inv64_waves(LT, dv, Ys, Tm);
-  if (i == k) {
+  if (!yrole && i == k) {
     // Only L_kk^{-1} is kept: nothing reads the diagonal block of L again (the
-    // updates read the panel rows below it, the inverse reads Y_kk), and the
-    // other groups of this launch are still reading A_kk, so A_kk stays as is.
-    // The whole block, zeros above the diagonal included: the inverse's
-    // products read these tiles in full.
-    for (int e = tid; e < NB * NB; e += 256) {
-      const int r = e >> 6, c = e & 63;
-      if (r < m && c < m) pb.Y[(size_t)(k0 + r) * n + k0 + c] = (c <= r) ? Ys[r][c] : 0.0;
-      // the block right of an even diagonal block lies inside the inverse's
-      // 128-wide product tiles and must read as zero
-      if ((k & 1) == 0 && r < m && k0 + NB + c < n) pb.Y[(size_t)(k0 + r) * n + k0 + NB + c] = 0.0;
+    // updates read the panel rows below it), and the other groups of this
+    // launch are still reading A_kk, so A_kk stays as is.  The whole block,
+    // zeros above the diagonal included, then zeros up to the end of the
+    // 256-wide diagonal block.
+    const int P1 = min((k0 / 256) * 256 + 256, n);
+    const int wz = P1 - k0;  // 64 .. 256 columns
+    for (int e = tid; e < NB * wz; e += 256) {
+      const int r = e / wz, c = e % wz;
+      if (r < m) pb.Y[(size_t)(k0 + r) * n + k0 + c] = (c < m && c <= r) ? Ys[r][c] : 0.0;
     }
     return;
   }
-  // X = R Y^T: X(r, c) = sum_t R[r][t] Y[c][t]
+  // yrole: Out(r, c) = sum_t Ys[r][t] Rs[t][c]   (Y_kj = L_kk^{-1} B_kj)
+  // else:  Out(r, c) = sum_t Rs[r][t] Ys[c][t]   (L_ik = A_ik L_kk^{-T})
   const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
   f64x4 acc[2][2];
 #pragma unroll
@@ -302,16 +318,25 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
 #pragma unroll 4
   for (int kk = 0; kk < NB / 4; ++kk) {
     double av[2], bv[2];
+    const int t = 4 * kk + (lane >> 4);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) av[mi] = Rs[32 * wr + 16 * mi + (lane & 15)][4 * kk + (lane >> 4)];
+    for (int mi = 0; mi < 2; ++mi) {
+      const int r = 32 * wr + 16 * mi + (lane & 15);
+      av[mi] = yrole ? Ys[r][t] : Rs[r][t];
+    }
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) bv[ni] = Ys[32 * wc + 16 * ni + (lane & 15)][4 * kk + (lane >> 4)];
+    for (int ni = 0; ni < 2; ++ni) {
+      const int c = 32 * wc + 16 * ni + (lane & 15);
+      bv[ni] = yrole ? Rs[t][c] : Ys[c][t];
+    }
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
   }
+  double* out = yrole ? pb.Y + (size_t)k0 * n + NB * j : A + (size_t)r0 * n + k0;
+  const int mc = yrole ? NB : m;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -320,20 +345,19 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
       for (int q = 0; q < 4; ++q) {
         const int r = 32 * wr + 16 * mi + (lane >> 4) + 4 * q;
         const int c = 32 * wc + 16 * ni + (lane & 15);
-        if (r < mr && c < m) A[(size_t)(r0 + r) * n + k0 + c] = acc[mi][ni][q];
+        if (r < mr && c < mc) out[(size_t)r * n + c] = acc[mi][ni][q];
       }
 }
 
 // --------------------------------------------------- fp64 MFMA products ---
-// One TS x TS output tile per workgroup (TS = 64 or 128), 4 waves of
-// TS/2 x TS/2, v_mfma_f64_16x16x4.
+// General form (any n): one 64 x 64 output tile per workgroup, 4 waves of
+// 32 x 32, v_mfma_f64_16x16x4.
 //   C(i, j) = beta C(i, j) + alpha sum_{t in [kb, ke)} Aop(i, t) Bop(t, j)
 // Aop(i, t) = A[i * lda + t]; Bop(t, j) = B[t * sbk + j * sbj] (one of sbk,
 // sbj is 1).  The kind decides the operands from the problem's matrices.
-// K chunks (32 for TS = 64, 16 for TS = 128) are staged through registers
-// into a double-buffered LDS pair: the loads of chunk c+1 are in flight while
-// chunk c is multiplied.  128-wide tiles halve the bytes per flop; the narrow
-// updates inside an outer panel use 64-wide tiles for parallelism.
+// K chunks of 32 are staged through registers into a double-buffered LDS
+// pair: the loads of chunk c+1 are in flight while chunk c is multiplied.
+// Problems with n % 64 == 0 take k_gemm_ring below instead.
 template <int TS>
 __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs, const Seg* __restrict__ segs,
                                               int nseg) {
@@ -381,44 +405,23 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
     alpha = -1.0;
     beta = 1.0;
   } else {
-    // level with block size s: pair q = A-block [a0, a0+s), C-block [c0, c0+sC)
-    const int s = sg.b, tiles_j = (s + TS - 1) / TS;
-    const int pair_tiles = sg.c;  // tiles per pair (uniform: ceil(s/TS)^2)
-    const int q = t / pair_tiles, tt = t % pair_tiles;
-    const int a0 = 2 * q * s, c0 = a0 + s, sC = min(s, n - c0);
-    const int ti = tt / tiles_j, tj = tt % tiles_j;
-    const int i0 = TS * ti, j0 = TS * tj;
-    if (i0 >= sC) return;
-    mt = min(TS, sC - i0);
-    nt = min(TS, s - j0);
-    double* Tq = pb.T + (size_t)q * s * s;  // one s x s slot per pair
-    if (sg.a == GK_INV_STEP1) {
-      // T = B_blk * Y_A, B_blk = C[c0.., a0..] (stored in A), Y_A lower
-      A = pb.A + (size_t)(c0 + i0) * n + a0;
-      lda = n;
-      B = pb.Y + (size_t)a0 * n + a0 + j0;
-      sbk = n;
-      sbj = 1;
-      C = Tq + (size_t)i0 * s + j0;
-      ldc = s;
-      kb = j0;
-      ke = s;
-      alpha = 1.0;
-      beta = 0.0;
-    } else {
-      // Y_B = -Y_C * T, Y_C lower
-      A = pb.Y + (size_t)(c0 + i0) * n + c0;
-      lda = n;
-      B = Tq + j0;
-      sbk = s;
-      sbj = 1;
-      C = pb.Y + (size_t)(c0 + i0) * n + a0 + j0;
-      ldc = n;
-      kb = 0;
-      ke = min(sC, i0 + TS);
-      alpha = -1.0;
-      beta = 0.0;
-    }
+    // Y(i, j) -= sum_t L(i, t) Y(t, j): rows [r0, r1) x columns [0, kb0 + kw)
+    const int kb0 = sg.b, kw = sg.c, r0 = sg.d, r1 = sg.e;
+    const int ncol = (kb0 + kw + TS - 1) / TS;
+    const int i0 = r0 + TS * (t / ncol), j0 = TS * (t % ncol);
+    A = pb.A + (size_t)i0 * n + kb0;
+    lda = n;
+    B = pb.Y + (size_t)kb0 * n + j0;
+    sbk = n;
+    sbj = 1;
+    C = pb.Y + (size_t)i0 * n + j0;
+    ldc = n;
+    mt = min(TS, r1 - i0);
+    nt = min(TS, kb0 + kw - j0);
+    kb = 0;
+    ke = kw;
+    alpha = -1.0;
+    beta = j0 < kb0 ? 1.0 : 0.0;  // columns from kb0 on: first write
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1;
@@ -520,6 +523,8 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
     __syncthreads();
     buf ^= 1;
   }
+  // every load of C before any store (one memory round trip, not one per element)
+  double cur[MB][MB][4];
 #pragma unroll
   for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
@@ -528,14 +533,218 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
       for (int r = 0; r < 4; ++r) {
         const int i = (TS / 2) * wr + 16 * mi + (lane >> 4) + 4 * r;
         const int j = (TS / 2) * wc + 16 * ni + (lane & 15);
-        if (i < mt && j < nt) {
-          double* cp = C + (size_t)i * ldc + j;
-          *cp = (beta != 0.0 ? *cp : 0.0) + alpha * acc[mi][ni][r];
-        }
+        cur[mi][ni][r] = (beta != 0.0 && i < mt && j < nt) ? C[(size_t)i * ldc + j] : 0.0;
+      }
+#pragma unroll
+  for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < MB; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = (TS / 2) * wr + 16 * mi + (lane >> 4) + 4 * r;
+        const int j = (TS / 2) * wc + 16 * ni + (lane & 15);
+        if (i < mt && j < nt) C[(size_t)i * ldc + j] = cur[mi][ni][r] + alpha * acc[mi][ni][r];
       }
 }
 
 
+// Products of the factor when n % 64 == 0 (every K range, row offset and
+// pitch is then a multiple of 64): one TS x TS tile per workgroup (TS = 128
+// on 8 waves of 64 x 32, or TS = 64 on 4 waves of 32 x 32), fp64 MFMA
+// 16x16x4.  K chunks of 16 go from global memory straight into a 3-stage
+// LDS ring (global_load_lds, 16 B per lane), two chunks ahead, so no
+// register staging and no load latency on the critical path.
+//   - k-contiguous operands (L always, and L again as B in the Cholesky
+//     update) sit row-major, 128 B per row and chunk, the 16-byte k-pairs
+//     XOR-swizzled by (row / 2) % 8: a lane reads its two k values with one
+//     ds_read_b128 and 16 lanes on 16 rows hit 16 distinct bank groups;
+//   - j-contiguous B (Y in the inverse's updates) sits k-major, the j-pairs
+//     of a row XOR-swizzled by 8 ((k / 2) % 2).
+// K order: MFMA lane group g holds k = 8p + 2g + u in sub-step u of pair
+// step p, the same for both operands, so each pair step sums the 8 k's of
+// its range once.  Rows past the tile's edge read a valid row whose
+// results are never stored.
+template <int TS>
+struct RingCfg {
+  static constexpr int NW = TS == 128 ? 8 : 4;  // waves
+  static constexpr int WGC = NW / 2;            // wave grid 2 x WGC
+  static constexpr int WM = TS / 2, WN = TS / WGC;
+  static constexpr int MI = WM / 16, NI = WN / 16;
+  static constexpr int KC = 16, NST = 3;
+  static constexpr int OPB = TS * KC * 8;       // bytes per operand per stage
+  static constexpr int STB = 2 * OPB;
+  static constexpr int NQ = OPB / 1024 / NW;    // global_load_lds per operand per wave per stage
+};
+
+template <int TS>
+__global__ __launch_bounds__(RingCfg<TS>::NW * 64) void k_gemm_ring(const FacProb* __restrict__ probs,
+                                                                     const Seg* __restrict__ segs, int nseg) {
+  using C_ = RingCfg<TS>;
+  constexpr int NW = C_::NW, MI = C_::MI, NI = C_::NI, KC = C_::KC, NST = C_::NST;
+  constexpr int OPB = C_::OPB, STB = C_::STB, NQ = C_::NQ;
+  static_assert(NQ >= 1 && NQ * NW * 1024 == OPB, "load split");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STB];
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  const int n = pb.n;
+  const int t = blockIdx.x - sg.wg0;
+  const double* A;
+  const double* B;
+  double* C;
+  long long lda, ldb, ldc;  // ldb: pitch between B's k-contiguous rows (j) or k rows
+  bool bkc;                 // B k-contiguous
+  int mt, nt, kb, ke;
+  double alpha, beta;
+  if (sg.a == GK_CHOL_TRAIL) {
+    const int kb0 = sg.b, kw = sg.c, c0 = sg.d, c1 = sg.e;
+    const int nrow = (n - c0 + TS - 1) / TS, ncol = (c1 - c0 + TS - 1) / TS;
+    int b = 0, tt = t;
+    while (b < ncol && tt >= nrow - b) {
+      tt -= nrow - b;
+      ++b;
+    }
+    const int i0 = c0 + TS * (b + tt), j0 = c0 + TS * b;
+    A = pb.A + (size_t)i0 * n + kb0;
+    B = pb.A + (size_t)j0 * n + kb0;
+    lda = ldb = n;
+    bkc = true;
+    C = pb.A + (size_t)i0 * n + j0;
+    ldc = n;
+    mt = min(TS, n - i0);
+    nt = min(TS, c1 - j0);
+    kb = 0;
+    ke = kw;
+    alpha = -1.0;
+    beta = 1.0;
+  } else {
+    // Y(i, j) -= sum_t L(i, t) Y(t, j): rows [r0, r1) x columns [0, kb0 + kw)
+    const int kb0 = sg.b, kw = sg.c, r0 = sg.d, r1 = sg.e;
+    const int ncol = (kb0 + kw + TS - 1) / TS;
+    const int i0 = r0 + TS * (t / ncol), j0 = TS * (t % ncol);
+    A = pb.A + (size_t)i0 * n + kb0;
+    lda = n;
+    B = pb.Y + (size_t)kb0 * n + j0;
+    ldb = n;
+    bkc = false;
+    C = pb.Y + (size_t)i0 * n + j0;
+    ldc = n;
+    mt = min(TS, r1 - i0);
+    nt = min(TS, kb0 + kw - j0);
+    kb = 0;
+    ke = kw;
+    alpha = -1.0;
+    beta = j0 < kb0 ? 1.0 : 0.0;  // columns from kb0 on: first write
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr = w / C_::WGC, wc = w % C_::WGC;
+  const int nst = (ke - kb) / KC;
+
+  // global sources of this lane, per instruction q (k offset added per stage)
+  const double* asrc[NQ];
+  const double* bsrc[NQ];
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    const int slot = (NW * qi + w) * 64 + lane;  // 16-byte slot of the stage
+    const int r = slot >> 3, p = slot & 7;       // k-contiguous: row, pair slot
+    const int kp = p ^ ((r >> 1) & 7);
+    asrc[qi] = A + (size_t)(r < mt ? r : 0) * lda + kb + 2 * kp;
+    if (bkc) {
+      bsrc[qi] = B + (size_t)(r < nt ? r : 0) * ldb + kb + 2 * kp;
+    } else {
+      const int k = slot / (TS / 2), jp = (slot % (TS / 2)) ^ (8 * ((k >> 1) & 1));
+      bsrc[qi] = B + (size_t)(kb + k) * ldb + (2 * jp < nt ? 2 * jp : 0);
+    }
+  }
+  auto issue = [&](int st, int buf) {
+    uint8_t* base = lds + buf * STB;
+    const size_t ka = (size_t)st * KC, kbo = bkc ? (size_t)st * KC : (size_t)st * KC * ldb;
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[qi] + ka), (lds_void*)(base + (NW * qi + w) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[qi] + kbo), (lds_void*)(base + OPB + (NW * qi + w) * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  f64x4 acc[MI][NI];
+#pragma unroll
+  for (int a = 0; a < MI; ++a)
+#pragma unroll
+    for (int b = 0; b < NI; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0;
+
+  const int li = lane & 15, g = lane >> 4;
+  if (nst > 0) issue(0, 0);
+  if (nst > 1) issue(1, 1);
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst)
+      __builtin_amdgcn_s_waitcnt(VmWait<2 * NQ>::value);
+    else
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::value);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 2 < nst) issue(st + 2, (st + 2) % NST);
+    const uint8_t* sa = lds + (st % NST) * STB;
+    const uint8_t* sb = sa + OPB;
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      double av[MI][2], bv[NI][2];
+      const int kp = 4 * ps + g;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int r = wr * C_::WM + 16 * mi + li;
+        const f64x2 v = *(const f64x2*)(sa + r * 128 + ((kp ^ ((r >> 1) & 7)) << 4));
+        av[mi][0] = v[0];
+        av[mi][1] = v[1];
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int j = wc * C_::WN + 16 * ni + li;
+        if (bkc) {
+          const f64x2 v = *(const f64x2*)(sb + j * 128 + ((kp ^ ((j >> 1) & 7)) << 4));
+          bv[ni][0] = v[0];
+          bv[ni][1] = v[1];
+        } else {
+          const int k = 2 * kp;  // and k + 1: same swizzle
+          const int off = (((j >> 1) ^ (8 * ((k >> 1) & 1))) << 4) + 8 * (j & 1);
+          bv[ni][0] = *(const double*)(sb + k * (TS * 8) + off);
+          bv[ni][1] = *(const double*)(sb + (k + 1) * (TS * 8) + off);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mi][u], bv[ni][u], acc[mi][ni], 0, 0, 0);
+    }
+  }
+  // every load of C before any store (one memory round trip, not one per element)
+  double cur[MI][NI][4];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = wr * C_::WM + 16 * mi + g + 4 * r;
+        const int j = wc * C_::WN + 16 * ni + li;
+        cur[mi][ni][r] = (beta != 0.0 && i < mt && j < nt) ? C[(size_t)i * ldc + j] : 0.0;
+      }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = wr * C_::WM + 16 * mi + g + 4 * r;
+        const int j = wc * C_::WN + 16 * ni + li;
+        if (i < mt && j < nt) C[(size_t)i * ldc + j] = cur[mi][ni][r] + alpha * acc[mi][ni][r];
+      }
+}
 
 // U[i][j] = Y[n-1-i][n-1-j] for j >= i (upper), 0 below; fp32.  4 rows per WG.
 __global__ __launch_bounds__(256) void k_make_u(const FacProb* __restrict__ probs,
@@ -567,5 +776,6 @@ hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st) {
 SEG_LAUNCH(launch_damp_fill, k_damp_fill, 256)
 SEG_LAUNCH(launch_chol_panel, k_chol_panel, 256)
 SEG_LAUNCH(launch_gemm64, k_gemm<64>, 256)
-SEG_LAUNCH(launch_gemm128, k_gemm<128>, 256)
+SEG_LAUNCH(launch_gemm_ring64, k_gemm_ring<64>, 256)
+SEG_LAUNCH(launch_gemm_ring128, k_gemm_ring<128>, 512)
 SEG_LAUNCH(launch_make_u, k_make_u, 256)

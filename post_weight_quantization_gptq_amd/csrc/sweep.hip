@@ -395,6 +395,11 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
     __syncthreads();
     buf ^= 1;
   }
+  // All loads of the tile's W before any store: the stores could alias the
+  // loads as far as the compiler knows, so interleaving them would cost one
+  // memory round trip per element.
+  float* wbase = ly.Ww + (size_t)i0 * nt + jj0;
+  float cur[MB][MB][16];
 #pragma unroll
   for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
@@ -403,7 +408,17 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
       for (int r = 0; r < 16; ++r) {
         const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
-        if (i < mt && j < ntc) ly.Ww[(size_t)(i0 + i) * nt + jj0 + j] -= acc[mi][ni][r];
+        cur[mi][ni][r] = (i < mt && j < ntc) ? wbase[(size_t)i * nt + j] : 0.f;
+      }
+#pragma unroll
+  for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < MB; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
+        if (i < mt && j < ntc) wbase[(size_t)i * nt + j] = cur[mi][ni][r] - acc[mi][ni][r];
       }
 }
 

@@ -75,14 +75,6 @@ __global__ __launch_bounds__(256) void k_xpose(const XposeProb* __restrict__ pro
 #define SYK_STB (2 * SYK_OPB)       // bytes of a stage
 #define SYK_NST 4                   // stages in the ring
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding).
-template <int N>
-struct VmWait {
-  static constexpr int value = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-};
-
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 

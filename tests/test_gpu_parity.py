@@ -86,7 +86,7 @@ def _spd(n, seed, decay=0.8, tokens=None):
     return Xf.T @ Xf
 
 
-@pytest.mark.parametrize("n", [64, 100, 200, 517, 1024])
+@pytest.mark.parametrize("n", [64, 100, 200, 517, 1024, 2560])
 def test_factor_matches_oracle(ctx, n):
     print("factor", n, flush=True)
     H32 = _spd(n, n).astype(np.float32)
