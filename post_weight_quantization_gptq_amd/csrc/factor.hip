@@ -80,78 +80,124 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
-// Cholesky of the 64x64 diagonal block by one wave, without barriers.  Lane r
-// keeps row r in registers; the steps are instantiated one by one (template
-// recursion), so every register index is a constant.  Step j: the pivot comes
-// from lane j (readlane), 1/sqrt by the hardware estimate and two Newton
-// steps, every lane forms its multiplier l_r = a_rj / sqrt(a_jj) and the
-// multipliers go through LDS (broadcast reads, in order inside the wave; 16
-// in flight) for the rank-1 update of columns > j; entries above the
-// diagonal are don't-care.  In: LT[c][r] = block[r][c] (r >= c), padded with
-// the identity.  Out (may alias LT): Ls[r][c] = L[r][c] with zeros above the
-// diagonal, dv[r] = 1 / L[r][r].  Returns the first failing pivot or -1.
-struct CholWave {
-  double a[NB];
+// Cholesky of the 64x64 diagonal block by the workgroup's four waves,
+// blocked by 16 columns.  For each 16-column sub-panel, wave 0 runs the
+// column steps with lane r holding row r's 16 entries of the sub-panel (at
+// most 15 FMAs per step), then the four waves apply the rank-16 update to the
+// lower 16x16 tiles right of it on fp64 MFMA.
+// Column step j: 1/sqrt of the pivot by the hardware estimate and one Newton
+// step (the estimate is good to about 2^-26, so one step reaches double
+// precision), l = a_j * rs on every lane (lane j: sqrt of the pivot; lanes
+// below: the multipliers; lanes above: values above the diagonal that
+// nothing reads); lane j+1 forms the next pivot from its own multiplier (the
+// same fma as the rank-1 update performs there) and hands it over by
+// readlane, so the serial chain never waits for LDS; the multipliers reach
+// the other lanes through LDS (two alternating rows of broadcast reads).
+// The steps contain no branch: a failed pivot (not positive or not finite) is
+// recorded and replaced by 1, so the rest stays finite and is discarded.  A
+// scheduling fence ends every step, so the compiler interleaves the next
+// pivot's chain with the step's FMAs and no more.
+// In: M[r][c] row-major, lower triangle valid (padded with the identity).
+// Out: M lower = L (entries above the diagonal are don't-care), dv[r] =
+// 1 / L[r][r].  Returns the first failing pivot or -1, the same on every
+// thread.  lb: 2 NB doubles of LDS; flag: one int of LDS.
+struct PanelWave {
+  double a[16];
   double dvr;
   int fail;
 };
 
-template <int J>
-__device__ __forceinline__ void chol_step(CholWave& st, double* lb, int r) {
-  if (st.fail >= 0) return;  // uniform
-  const double d = readlane_f64(st.a[J], J);
-  if (!(d > 0.0) || !__builtin_isfinite(d)) {
-    st.fail = J;
-    return;
+template <int C>
+__device__ __forceinline__ double sub_step(PanelWave& st, double* lb, int r, int c0, double rs) {
+  const int J = c0 + C;
+  const double l = st.a[C] * rs;
+  st.a[C] = l;
+  st.dvr = (r == J) ? rs : st.dvr;
+  double rsn = 0.0;
+  if constexpr (C + 1 < 16) {
+    // next pivot from lane J+1's own update (same fma as the rank-1 update)
+    const int J1 = J + 1;
+    const double dn = readlane_f64(st.a[C + 1] - l * l, J1);
+    const bool ok = dn > 0.0 && __builtin_isfinite(dn);
+    st.fail = (st.fail < 0 && !ok) ? J1 : st.fail;
+    const double dd = ok ? dn : 1.0;
+    rsn = __builtin_amdgcn_rsq(dd);
+    rsn = rsn * (1.5 - 0.5 * dd * rsn * rsn);
+    double* row = lb + NB * (C & 1);
+    row[r] = l;
+    double lk[16];
+#pragma unroll
+    for (int t = C + 1; t < 16; ++t) lk[t] = row[c0 + t];
+#pragma unroll
+    for (int t = C + 1; t < 16; ++t) st.a[t] -= l * lk[t];
   }
-  double rs = __builtin_amdgcn_rsq(d);
-  rs = rs * (1.5 - 0.5 * d * rs * rs);
-  rs = rs * (1.5 - 0.5 * d * rs * rs);
-  const double l = (r > J) ? st.a[J] * rs : ((r == J) ? d * rs : 0.0);
-  st.a[J] = l;
-  if (r == J) st.dvr = rs;
-  if constexpr (J + 1 < NB) {
-    lb[r] = l;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int k0 = J + 1; k0 < NB; k0 += 16) {
-      double lk[16];
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        if (k0 + t < NB) lk[t] = lb[k0 + t];
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        if (k0 + t < NB) st.a[k0 + t] -= l * lk[t];
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
+  __builtin_amdgcn_sched_barrier(0);
+  return rsn;
 }
 
-template <int J>
-struct CholSteps {
-  __device__ __forceinline__ static void run(CholWave& st, double* lb, int r) {
-    chol_step<J>(st, lb, r);
-    CholSteps<J + 1>::run(st, lb, r);
+template <int C>
+struct SubSteps {
+  __device__ __forceinline__ static void run(PanelWave& st, double* lb, int r, int c0, double rs) {
+    const double rsn = sub_step<C>(st, lb, r, c0, rs);
+    SubSteps<C + 1>::run(st, lb, r, c0, rsn);
   }
 };
 template <>
-struct CholSteps<NB> {
-  __device__ __forceinline__ static void run(CholWave&, double*, int) {}
+struct SubSteps<16> {
+  __device__ __forceinline__ static void run(PanelWave&, double*, int, int, double) {}
 };
 
-__device__ __forceinline__ int chol64_wave(double (*LT)[NB + 1], double (*Ls)[NB + 1], double* dv, double* lb) {
-  const int r = threadIdx.x & 63;
-  CholWave st;
-#pragma unroll
-  for (int c = 0; c < NB; ++c) st.a[c] = LT[c][r];
-  __builtin_amdgcn_wave_barrier();
+__device__ __forceinline__ int chol64_blocked(double (*M)[NB + 1], double* dv, double* lb, int* flag) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  PanelWave st;
   st.dvr = 0.0;
   st.fail = -1;
-  CholSteps<0>::run(st, lb, r);
+#pragma unroll 1
+  for (int p = 0; p < 4; ++p) {
+    const int c0 = 16 * p;
+    if (w == 0) {
 #pragma unroll
-  for (int c = 0; c < NB; ++c) Ls[r][c] = (c <= r) ? st.a[c] : 0.0;
-  dv[r] = st.dvr;
-  return st.fail;
+      for (int t = 0; t < 16; ++t) st.a[t] = M[lane][c0 + t];
+      const double d = readlane_f64(st.a[0], c0);
+      const bool ok = d > 0.0 && __builtin_isfinite(d);
+      st.fail = (st.fail < 0 && !ok) ? c0 : st.fail;
+      const double dd = ok ? d : 1.0;
+      double rs = __builtin_amdgcn_rsq(dd);
+      rs = rs * (1.5 - 0.5 * dd * rs * rs);
+      SubSteps<0>::run(st, lb, lane, c0, rs);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) M[lane][c0 + t] = st.a[t];
+    }
+    __syncthreads();
+    if (p < 3) {
+      // M[i][j] -= sum_{t<16} M[i][c0+t] M[j][c0+t] on the lower 16x16 tiles
+      // of rows / columns [c0 + 16, 64)
+      const int nt = 3 - p, ntiles = nt * (nt + 1) / 2;
+      const int i16 = lane & 15, k4 = lane >> 4;
+      for (int tile = w; tile < ntiles; tile += 4) {
+        int ti = 0, rem = tile;
+        while (rem > ti) {
+          rem -= ti + 1;
+          ++ti;
+        }
+        const int i0 = c0 + 16 + 16 * ti, j0 = c0 + 16 + 16 * rem;
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(M[i0 + i16][c0 + 4 * s4 + k4], M[j0 + i16][c0 + 4 * s4 + k4], acc, 0,
+                                                    0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) M[i0 + k4 + 4 * q][j0 + i16] -= acc[q];
+      }
+      __syncthreads();
+    }
+  }
+  if (w == 0) {
+    dv[lane] = st.dvr;
+    if (lane == 0) *flag = st.fail;
+  }
+  __syncthreads();
+  return *flag;
 }
 
 // Y = L^{-1} of the 64x64 lower block by the four waves: the diagonal 16x16
@@ -248,9 +294,9 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
   __shared__ double Ys[NB][NB + 1];  // L^{-1}, row-major
   __shared__ double Rs[NB][NB + 1];  // this group's panel rows, or B_kj
   __shared__ double Tm[32][33];
-  __shared__ double lb[NB];
+  __shared__ double lb[2 * NB];
   __shared__ double dv[NB];
-  __shared__ int bad;
+  __shared__ int flag;
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const FacProb pb = probs[sg.prob];
   if (*pb.info != 0 || *pb.nonfinite != 0) return;
@@ -276,16 +322,12 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int e = tid + 256 * q, r = e >> 6, c = e & 63;
-      LT[c][r] = (r < m && c < m) ? ta[q] : ((r == c) ? 1.0 : 0.0);
+      LT[r][c] = (r < m && c < m) ? ta[q] : ((r == c) ? 1.0 : 0.0);
       Rs[r][c] = tr[q];
     }
   }
   __syncthreads();
-  if (tid < 64) {
-    const int f = chol64_wave(LT, LT, dv, lb);
-    if (tid == 0) bad = f;
-  }
-  __syncthreads();
+  const int bad = chol64_blocked(LT, dv, lb, &flag);
   if (bad >= 0) {
     if (tid == 0 && g == 0) atomicMax(pb.info, n - (k0 + bad));
     return;
