@@ -34,7 +34,7 @@ struct gptq_ctx_s {
   int ncu = 256;
   int nxcd = 8;
   std::string err;
-  DevBuf partials, xt, facA, facY, work, eblk, objp, slots, blob, lora;
+  DevBuf partials, xt, facA, facY, work, eblk, objp, dinv, slots, blob, lora;
   void* hblob = nullptr;  // pinned staging for the task tables
   size_t hblob_cap = 0;
   void* hsmall = nullptr;  // pinned read-back area
@@ -612,8 +612,8 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
   // K = the super-block width), so the far columns of W are rewritten once
   // per super-block instead of once per block.  Groups must nest in it.
   std::vector<int> sbk(nl);
-  size_t totW = 0, totE = 0, totO = 0;
-  std::vector<size_t> oW(nl), oE(nl), oO(nl);
+  size_t totW = 0, totE = 0, totO = 0, totD = 0;
+  std::vector<size_t> oW(nl), oE(nl), oO(nl), oD(nl);
   for (int p = 0; p < nl; ++p) {
     const QuantJob& J = jobs[p];
     int sb = std::max(1, 512 / J.block);
@@ -626,11 +626,14 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     totE += (size_t)J.out * sb * J.block;
     oO[p] = totO;
     totO += (size_t)J.out * 2;
+    oD[p] = totD;
+    totD += (size_t)(J.nt + 63) / 64 * 64;
   }
   int rc;
   if ((rc = ensure(c, c->work, totW * sizeof(float)))) return rc;
   if ((rc = ensure(c, c->eblk, totE * sizeof(float)))) return rc;
   if ((rc = ensure(c, c->objp, totO * sizeof(double)))) return rc;
+  if ((rc = ensure(c, c->dinv, totD * sizeof(float)))) return rc;
   std::vector<QLayer> L(nl);
   int maxblk = 0;
   for (int p = 0; p < nl; ++p) {
@@ -645,6 +648,7 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     q.err = J.err;
     q.Eb = (float*)c->eblk.p + oE[p];
     q.objp = (double*)c->objp.p + oO[p];
+    q.dinv = (const float*)c->dinv.p + oD[p];
     q.obj = J.obj;
     q.lam = J.lam;
     q.out = J.out;
@@ -798,7 +802,7 @@ GPTQ_API int gptq_destroy(gptq_ctx c) {
   {
     DeviceGuard g(c->device);
     (void)hipStreamSynchronize(c->stream);
-    DevBuf* bufs[] = {&c->partials, &c->xt, &c->facA, &c->facY, &c->work, &c->eblk,
+    DevBuf* bufs[] = {&c->partials, &c->xt, &c->facA, &c->facY, &c->work, &c->eblk, &c->dinv,
                       &c->objp, &c->slots, &c->blob, &c->lora};
     for (DevBuf* b : bufs)
       if (b->p) (void)hipFree(b->p);

@@ -98,6 +98,7 @@ struct QLayer {
   uint8_t* zeros;   // [out][ng]
   float* err;       // [out][n] or null
   float* Eb;        // block errors [out][block]
+  const float* dinv;  // 1 / U_jj [nt], filled by k_init_work
   double* objp;     // per row: {sum E^2, sum D^2}, accumulated block by block
   double* obj;      // [2] {J, J_lam} (device)
   const double* lam;  // device slot holding the damping of U

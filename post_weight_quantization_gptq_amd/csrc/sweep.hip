@@ -42,12 +42,16 @@ __device__ __forceinline__ Grid grid_from(float mn, float mx, float maxq) {
   return g;
 }
 
-// Working copy of W (and zero columns n..nt-1 for the augmented variant).
+// Working copy of W (and zero columns n..nt-1 for the augmented variant),
+// and 1 / U_jj for every column (the sweep's error scale), once per layer.
 __global__ __launch_bounds__(256) void k_init_work(const QLayer* __restrict__ L,
                                                    const Seg* __restrict__ segs, int nseg) {
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const QLayer ly = L[sg.prob];
-  const int row = (blockIdx.x - sg.wg0) * 4 + (threadIdx.x >> 6);
+  const int wi = blockIdx.x - sg.wg0;
+  for (int c = wi * 256 + threadIdx.x; c < ly.nt; c += sg.nwg * 256)
+    ((float*)ly.dinv)[c] = 1.f / ly.U[(size_t)c * ly.nt + c];
+  const int row = wi * 4 + (threadIdx.x >> 6);
   if (row >= ly.out) return;
   for (int c = threadIdx.x & 63; c < ly.nt; c += 64)
     ly.Ww[(size_t)row * ly.nt + c] = c < ly.n ? ly.W[(size_t)row * ly.n + c] : 0.f;
@@ -142,8 +146,13 @@ __device__ __forceinline__ void fit_group(SweepState<CPL>& st, const SweepCtx& c
 // The CPL columns owned by lane O of every row group.
 // Groups are multiples of 8 >= CPL columns, so a group can only start at the
 // first column of an owner lane: the check runs once per owner.
+// Columns past the end of a ragged block need no test: their weights, U rows
+// and 1/U_jj are zero, so they produce e = 0 and change nothing (their codes
+// are never written).  Each step loads the next column's U row before its
+// own chain starts, so the LDS latency stays off the serial path.
 template <int O, int CPL>
-__device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx& cx) {
+__device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx& cx, float (&ucur)[CPL]) {
+  constexpr int B = 16 * CPL;
   if (O * CPL == st.nextg && O * CPL < cx.bw) {
     fit_group<CPL>(st, cx, O * CPL);
     st.nextg += cx.G;
@@ -151,34 +160,41 @@ __device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx&
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int j = O * CPL + c;
-    if (j < cx.bw) {
-      const float wj = bcast16<O>(st.wv[c]);
-      const float x = __fadd_rn(__fmul_rn(wj, st.g.r), st.g.z);
-      const float q = fminf(fmaxf(rintf(x), 0.f), cx.maxq);
-      const float what = st.g.s * (q - st.g.z);
-      const float e = (wj - what) * bcast16<O>(st.dv[c]);
-      if (cx.l16 == O) {
-        st.qv[c] = q;
-        st.hv[c] = what;
-        st.ev[c] = e;
-      }
-      const float* urow = cx.Us + j * cx.B + CPL * cx.l16;
+    float unext[CPL];
+    if (j + 1 < B) {
+      const float* un = cx.Us + (j + 1) * B + CPL * cx.l16;
 #pragma unroll
-      for (int c2 = 0; c2 < CPL; ++c2) st.wv[c2] = fmaf(-e, urow[c2], st.wv[c2]);
+      for (int v = 0; v < CPL; ++v) unext[v] = un[v];
+    }
+    const float wj = bcast16<O>(st.wv[c]);
+    const float x = __fadd_rn(__fmul_rn(wj, st.g.r), st.g.z);
+    const float q = fminf(fmaxf(rintf(x), 0.f), cx.maxq);
+    const float what = st.g.s * (q - st.g.z);
+    const float e = (wj - what) * bcast16<O>(st.dv[c]);
+    if (cx.l16 == O) {
+      st.qv[c] = q;
+      st.hv[c] = what;
+      st.ev[c] = e;
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < CPL; ++c2) st.wv[c2] = fmaf(-e, ucur[c2], st.wv[c2]);
+    if (j + 1 < B) {
+#pragma unroll
+      for (int v = 0; v < CPL; ++v) ucur[v] = unext[v];
     }
   }
 }
 
 template <int O, int CPL>
 struct SweepAll {
-  __device__ __forceinline__ static void run(SweepState<CPL>& st, const SweepCtx& cx) {
-    sweep_owner<O, CPL>(st, cx);
-    SweepAll<O + 1, CPL>::run(st, cx);
+  __device__ __forceinline__ static void run(SweepState<CPL>& st, const SweepCtx& cx, float (&ucur)[CPL]) {
+    sweep_owner<O, CPL>(st, cx, ucur);
+    SweepAll<O + 1, CPL>::run(st, cx, ucur);
   }
 };
 template <int CPL>
 struct SweepAll<16, CPL> {
-  __device__ __forceinline__ static void run(SweepState<CPL>&, const SweepCtx&) {}
+  __device__ __forceinline__ static void run(SweepState<CPL>&, const SweepCtx&, float (&)[CPL]) {}
 };
 
 template <int CPL>
@@ -196,6 +212,34 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   const bool rv = row < ly.out;
   const int nt = ly.nt, G = ly.group;
 
+  // the row's loads first, then the U block, all in flight together
+  SweepState<CPL> st;
+  float wo[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int lc = CPL * l16 + c;
+    const bool in = rv && lc < bw;
+    st.wv[c] = in ? ly.Ww[(size_t)row * nt + b0 + lc] : 0.f;
+    st.dv[c] = (lc < bw) ? ly.dinv[b0 + lc] : 0.f;
+    wo[c] = in ? ly.W[(size_t)row * ly.n + b0 + lc] : 0.f;
+    st.qv[c] = 0.f;
+    st.hv[c] = 0.f;
+    st.ev[c] = 0.f;
+  }
+  // the row's objective sums so far (added to at the end)
+  double obj_e = 0.0, obj_d = 0.0;
+  if (rv && l16 == 0) {
+    obj_e = ly.objp[(size_t)row * 2];
+    obj_d = ly.objp[(size_t)row * 2 + 1];
+  }
+  st.g = Grid{1.f, 1.f, 0.f};
+  if (rv && (G == 0 || (b0 % G) != 0)) {
+    // the row's grid, or the grid of a group that began in an earlier block
+    const size_t gi = (size_t)row * ly.ng + (G ? b0 / G : 0);
+    st.g.s = ly.scales[gi];
+    st.g.r = 1.f / st.g.s;
+    st.g.z = (float)ly.zeros[gi];
+  }
   {
     // U block -> LDS: all loads of a thread in flight at once, 16 B each
     constexpr int PER = (B * B / 4 + 255) / 256;
@@ -223,28 +267,6 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
       if (idx < B * B / 4) *(f32x4*)&Us[idx * 4] = tmp[q];
     }
   }
-
-  SweepState<CPL> st;
-  float wo[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int lc = CPL * l16 + c;
-    const bool in = rv && lc < bw;
-    st.wv[c] = in ? ly.Ww[(size_t)row * nt + b0 + lc] : 0.f;
-    st.dv[c] = (lc < bw) ? 1.f / ly.U[(size_t)(b0 + lc) * nt + b0 + lc] : 0.f;
-    wo[c] = in ? ly.W[(size_t)row * ly.n + b0 + lc] : 0.f;
-    st.qv[c] = 0.f;
-    st.hv[c] = 0.f;
-    st.ev[c] = 0.f;
-  }
-  st.g = Grid{1.f, 1.f, 0.f};
-  if (rv && (G == 0 || (b0 % G) != 0)) {
-    // the row's grid, or the grid of a group that began in an earlier block
-    const size_t gi = (size_t)row * ly.ng + (G ? b0 / G : 0);
-    st.g.s = ly.scales[gi];
-    st.g.r = 1.f / st.g.s;
-    st.g.z = (float)ly.zeros[gi];
-  }
   st.nextg = (G == 0) ? (1 << 30) : ((b0 % G) == 0 ? 0 : G - (b0 % G));
   SweepCtx cx;
   cx.Us = Us;
@@ -261,7 +283,10 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   cx.grow = (size_t)(rv ? row : 0) * ly.ng;
   __syncthreads();
 
-  SweepAll<0, CPL>::run(st, cx);
+  float ucur[CPL];
+#pragma unroll
+  for (int v = 0; v < CPL; ++v) ucur[v] = Us[CPL * l16 + v];
+  SweepAll<0, CPL>::run(st, cx, ucur);
 
   double se = 0.0, sd = 0.0;
 #pragma unroll
@@ -284,8 +309,8 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   if (rv && l16 == 0) {
     // per-row sums, accumulated over the blocks in block order
     double* op = ly.objp + (size_t)row * 2;
-    op[0] += se;
-    op[1] += sd;
+    op[0] = obj_e + se;
+    op[1] = obj_d + sd;
   }
 }
 
