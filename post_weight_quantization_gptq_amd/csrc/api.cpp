@@ -41,6 +41,10 @@ struct gptq_ctx_s {
   size_t hsmall_cap = 0;
   hipEvent_t blob_ev = nullptr;
   bool blob_pending = false;
+  // second stream (default priority) for the factor's trailing updates that
+  // run beside its serial chain; fork / join events order it against stream
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   // per-kernel timing (off unless gptq_timing enabled it)
   struct Timed {
     const char* name;
@@ -114,22 +118,24 @@ bool timer_wants(gptq_ctx c, const char* name) {
   return c->tfilter.find(std::string(",") + name + ",") != std::string::npos;
 }
 
-// Issue one kernel launch; with timing on, bracket it by an event pair.
-#define LAUNCH(c, name, expr)                                \
-  do {                                                       \
-    hipEvent_t ea_ = nullptr, eb_ = nullptr;                 \
-    const bool timed_ = timer_wants(c, name);                \
-    if (timed_) {                                            \
-      HIPCHK(c, timer_event(c, &ea_));                       \
-      HIPCHK(c, timer_event(c, &eb_));                       \
-      HIPCHK(c, hipEventRecord(ea_, (c)->stream));           \
-    }                                                        \
-    HIPCHK(c, expr);                                         \
-    if (timed_) {                                            \
-      HIPCHK(c, hipEventRecord(eb_, (c)->stream));           \
+// Issue one kernel launch on stream st; with timing on, bracket it by an
+// event pair on that stream.
+#define LAUNCH_ON(c, st, name, expr)                           \
+  do {                                                         \
+    hipEvent_t ea_ = nullptr, eb_ = nullptr;                   \
+    const bool timed_ = timer_wants(c, name);                  \
+    if (timed_) {                                              \
+      HIPCHK(c, timer_event(c, &ea_));                         \
+      HIPCHK(c, timer_event(c, &eb_));                         \
+      HIPCHK(c, hipEventRecord(ea_, st));                      \
+    }                                                          \
+    HIPCHK(c, expr);                                           \
+    if (timed_) {                                              \
+      HIPCHK(c, hipEventRecord(eb_, st));                      \
       (c)->tpend.push_back(gptq_ctx_s::Timed{name, ea_, eb_}); \
-    }                                                        \
+    }                                                          \
   } while (0)
+#define LAUNCH(c, name, expr) LAUNCH_ON(c, (c)->stream, name, expr)
 
 int ensure(gptq_ctx c, DevBuf& b, size_t bytes) {
   if (bytes == 0) bytes = 256;
@@ -517,20 +523,23 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   Blob b;
   const size_t o_probs = b.add(probs);
   struct L {
-    int kind;  // 0 fill, 1 panel, 2 gemm (general, 64 tiles), 3 ring gemm 64, 4 ring gemm 128, 5 makeu
+    int kind;  // 0 fill, 1 panel, 2 gemm (general, 64 tiles), 3 ring gemm 64, 4 ring gemm 128, 5 makeu,
+               // 6 fork (side stream waits for the main stream), 7 join (main waits for the side stream)
+    bool side;  // launch on the side stream
     size_t off;
     int nseg, nwg;
   };
   std::vector<L> launches;
-  auto add_launch = [&](int kind, std::vector<Seg>& segs) {
+  auto add_launch = [&](int kind, std::vector<Seg>& segs, bool side = false) {
     int nwg = 0;
     for (auto& s : segs) {
       s.wg0 = nwg;
       nwg += s.nwg;
     }
     if (nwg == 0) return;
-    launches.push_back(L{kind, b.add(segs), (int)segs.size(), nwg});
+    launches.push_back(L{kind, side, b.add(segs), (int)segs.size(), nwg});
   };
+  auto add_sync = [&](int kind) { launches.push_back(L{kind, false, 0, 0, 0}); };
   // The ring-staged products need every K range and row pitch to be a
   // multiple of 64 (16-byte aligned chunks of 16 doubles).
   bool ring = true;
@@ -544,11 +553,17 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   // Cholesky and Y = L^{-1}: outer panels of 256 columns, four 64-column
   // steps each.  Step k: the panel launch (every 64-block of the problem),
   // then the updates of the rest of the outer panel (L columns [c0, P1) of
-  // every row below; Y rows [c0, P1)), or at the end of the outer panel the
-  // trailing updates with K = P1 - P0 (L's trailing triangle; Y rows past P1).
+  // every row below; Y rows [c0, P1)).  At the end of an outer panel the
+  // trailing updates with K = P1 - P0 split in two: the part the next outer
+  // panel reads (L columns [P1, S), S = P1 + 256; Y rows [P1, S)) on the main
+  // stream, and the rest (L's trailing triangle from S on; Y rows from S on)
+  // on the side stream, where it overlaps the next outer panel's steps (which
+  // neither read nor write it) and is joined before the next outer update.
+  // With the general products (n % 64 != 0) everything stays on one stream.
+  bool side_busy = false;
   for (int k = 0; k < maxnb; ++k) {
-    std::vector<Seg> pan, inner, outer;
-    int outer_rows = 0;
+    std::vector<Seg> pan, inner, crit, bulk;
+    int bulk_rows = 0;
     for (int p = 0; p < np; ++p) {
       const int n = jobs[p].n, nb = cdiv(n, 64);
       if (k >= nb) continue;
@@ -561,26 +576,42 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
         inner.push_back(Seg{p, 0, ncol * nrow - ncol * (ncol - 1) / 2, GK_CHOL_TRAIL, k0, pw, c0, P1});
         inner.push_back(Seg{p, 0, cdiv(P1 - c0, 64) * cdiv(c0, 64), GK_ZUPD, k0, pw, c0, P1});
       } else if (P1 < n) {  // end of the outer panel: trailing updates with K = P1 - P0
-        outer.push_back(Seg{p, 0, 0, GK_CHOL_TRAIL, P0, P1 - P0, P1, n});
-        outer.push_back(Seg{p, 0, 0, GK_ZUPD, P0, P1 - P0, P1, n});
-        outer_rows = std::max(outer_rows, n - P1);
-      }
-    }
-    // 128-wide tiles while the trailing part gives about two tiles per CU
-    const int ots = (ring && outer_rows >= 1024) ? 128 : 64;
-    for (Seg& sg : outer) {
-      const int n = jobs[sg.prob].n;
-      if (sg.a == GK_CHOL_TRAIL) {
-        const int m = cdiv(n - sg.d, ots);
-        sg.nwg = m * (m + 1) / 2;
-      } else {
-        sg.nwg = cdiv(n - sg.d, ots) * cdiv(sg.b + sg.c, ots);
+        const int S = ring ? std::min(P1 + 256, n) : n;
+        {
+          const int nrow = cdiv(n - P1, 64), ncol = cdiv(S - P1, 64);
+          crit.push_back(Seg{p, 0, ncol * nrow - ncol * (ncol - 1) / 2, GK_CHOL_TRAIL, P0, P1 - P0, P1, S});
+          crit.push_back(Seg{p, 0, cdiv(S - P1, 64) * cdiv(P1, 64), GK_ZUPD, P0, P1 - P0, P1, S});
+        }
+        if (S < n) {
+          const int m = cdiv(n - S, 128);
+          bulk.push_back(Seg{p, 0, m * (m + 1) / 2, GK_CHOL_TRAIL, P0, P1 - P0, S, n});
+          bulk.push_back(Seg{p, 0, m * cdiv(P1, 128), GK_ZUPD, P0, P1 - P0, S, n});
+          bulk_rows = std::max(bulk_rows, n - S);
+        }
       }
     }
     add_launch(1, pan);
     add_launch(ring ? 3 : 2, inner);
-    add_launch(!ring ? 2 : (ots == 128 ? 4 : 3), outer);
+    if (!crit.empty()) {
+      if (side_busy) add_sync(7);  // the previous bulk update touches the columns updated now
+      side_busy = false;
+      if (!bulk.empty()) {
+        if (bulk_rows < 1024) {  // small: 64-wide tiles, on the main stream
+          for (Seg& sg : bulk) {
+            const int n = jobs[sg.prob].n, m = cdiv(n - sg.d, 64);
+            sg.nwg = (sg.a == GK_CHOL_TRAIL) ? m * (m + 1) / 2 : m * cdiv(sg.b + sg.c, 64);
+          }
+          for (Seg& sg : bulk) crit.push_back(sg);
+        } else {
+          add_sync(6);
+          add_launch(4, bulk, true);
+          side_busy = true;
+        }
+      }
+      add_launch(ring ? 3 : 2, crit);
+    }
   }
+  if (side_busy) add_sync(7);
   {
     std::vector<Seg> s;
     for (int p = 0; p < np; ++p) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 4), 0, 0, 0, 0, 0});
@@ -590,15 +621,29 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   if ((rc = upload(c, b, &d))) return rc;
   const FacProb* dp = (const FacProb*)(d + o_probs);
   LAUNCH(c, "k_damp_lambda", launch_damp_lambda(dp, np, c->stream));
+  // the side stream's updates take at most this many CUs (one workgroup per
+  // CU), leaving the rest to the panels and the narrow updates
+  const int side_wg = std::max(1, c->ncu * 5 / 8);
   for (const L& l : launches) {
     const Seg* sg = (const Seg*)(d + l.off);
+    hipStream_t st = l.side ? c->side : c->stream;
     switch (l.kind) {
       case 0: LAUNCH(c, "k_damp_fill", launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: LAUNCH(c, "k_chol_panel", launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 2: LAUNCH(c, "k_gemm64", launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3: LAUNCH(c, "k_gemm_ring64", launch_gemm_ring64(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 4: LAUNCH(c, "k_gemm_ring128", launch_gemm_ring128(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 3: LAUNCH_ON(c, st, "k_gemm_ring64", launch_gemm_ring(64, dp, sg, l.nseg, l.nwg, 0, st)); break;
+      case 4:
+        LAUNCH_ON(c, st, "k_gemm_ring128", launch_gemm_ring(128, dp, sg, l.nseg, l.nwg, l.side ? side_wg : 0, st));
+        break;
       case 5: LAUNCH(c, "k_make_u", launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 6:
+        HIPCHK(c, hipEventRecord(c->fork_ev, c->stream));
+        HIPCHK(c, hipStreamWaitEvent(c->side, c->fork_ev, 0));
+        break;
+      case 7:
+        HIPCHK(c, hipEventRecord(c->join_ev, c->side));
+        HIPCHK(c, hipStreamWaitEvent(c->stream, c->join_ev, 0));
+        break;
     }
   }
   return GPTQ_OK;
@@ -789,7 +834,13 @@ GPTQ_API int gptq_create(gptq_ctx* ctx, int device, void* stream) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
     c->ncu = prop.multiProcessorCount;
-  if (hipEventCreateWithFlags(&c->blob_ev, hipEventDisableTiming) != hipSuccess) {
+  if (hipEventCreateWithFlags(&c->blob_ev, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming) != hipSuccess ||
+      hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) {
+    if (c->blob_ev) (void)hipEventDestroy(c->blob_ev);
+    if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
+    if (c->join_ev) (void)hipEventDestroy(c->join_ev);
     delete c;
     return GPTQ_ERR_HIP;
   }
@@ -802,6 +853,7 @@ GPTQ_API int gptq_destroy(gptq_ctx c) {
   {
     DeviceGuard g(c->device);
     (void)hipStreamSynchronize(c->stream);
+    if (c->side) (void)hipStreamSynchronize(c->side);
     DevBuf* bufs[] = {&c->partials, &c->xt, &c->facA, &c->facY, &c->work, &c->eblk, &c->dinv,
                       &c->objp, &c->slots, &c->blob, &c->lora};
     for (DevBuf* b : bufs)
@@ -809,6 +861,9 @@ GPTQ_API int gptq_destroy(gptq_ctx c) {
     if (c->hblob) (void)hipHostFree(c->hblob);
     if (c->hsmall) (void)hipHostFree(c->hsmall);
     if (c->blob_ev) (void)hipEventDestroy(c->blob_ev);
+    if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
+    if (c->join_ev) (void)hipEventDestroy(c->join_ev);
+    if (c->side) (void)hipStreamDestroy(c->side);
     for (const auto& t : c->tpend) {
       (void)hipEventDestroy(t.a);
       (void)hipEventDestroy(t.b);

@@ -619,18 +619,17 @@ struct RingCfg {
 };
 
 template <int TS>
-__global__ __launch_bounds__(RingCfg<TS>::NW * 64) void k_gemm_ring(const FacProb* __restrict__ probs,
-                                                                     const Seg* __restrict__ segs, int nseg) {
+__device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, const Seg* __restrict__ segs, int nseg,
+                                          int vt, uint8_t* lds) {
   using C_ = RingCfg<TS>;
   constexpr int NW = C_::NW, MI = C_::MI, NI = C_::NI, KC = C_::KC, NST = C_::NST;
   constexpr int OPB = C_::OPB, STB = C_::STB, NQ = C_::NQ;
   static_assert(NQ >= 1 && NQ * NW * 1024 == OPB, "load split");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STB];
-  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const Seg sg = segs[find_seg(segs, nseg, vt)];
   const FacProb pb = probs[sg.prob];
   if (*pb.info != 0 || *pb.nonfinite != 0) return;
   const int n = pb.n;
-  const int t = blockIdx.x - sg.wg0;
+  const int t = vt - sg.wg0;
   const double* A;
   const double* B;
   double* C;
@@ -788,6 +787,20 @@ __global__ __launch_bounds__(RingCfg<TS>::NW * 64) void k_gemm_ring(const FacPro
       }
 }
 
+// Tiles vt = blockIdx.x, blockIdx.x + gridDim.x, ... < ntot: a grid smaller
+// than the tile count makes the launch persistent, so it can run beside the
+// factorization's serial chain without taking every CU.
+template <int TS>
+__global__ __launch_bounds__(RingCfg<TS>::NW * 64) void k_gemm_ring(const FacProb* __restrict__ probs,
+                                                                     const Seg* __restrict__ segs, int nseg,
+                                                                     int ntot) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RingCfg<TS>::NST * RingCfg<TS>::STB];
+  for (int vt = blockIdx.x; vt < ntot; vt += gridDim.x) {
+    ring_tile<TS>(probs, segs, nseg, vt, lds);
+    __syncthreads();  // the next tile refills the ring
+  }
+}
+
 // U[i][j] = Y[n-1-i][n-1-j] for j >= i (upper), 0 below; fp32.  4 rows per WG.
 __global__ __launch_bounds__(256) void k_make_u(const FacProb* __restrict__ probs,
                                                 const Seg* __restrict__ segs, int nseg) {
@@ -818,6 +831,14 @@ hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st) {
 SEG_LAUNCH(launch_damp_fill, k_damp_fill, 256)
 SEG_LAUNCH(launch_chol_panel, k_chol_panel, 256)
 SEG_LAUNCH(launch_gemm64, k_gemm<64>, 256)
-SEG_LAUNCH(launch_gemm_ring64, k_gemm_ring<64>, 256)
-SEG_LAUNCH(launch_gemm_ring128, k_gemm_ring<128>, 512)
+hipError_t launch_gemm_ring(int ts, const FacProb* probs, const Seg* segs, int nseg, int ntot, int maxwg,
+                            hipStream_t st) {
+  if (ntot <= 0) return hipSuccess;
+  const int grid = (maxwg > 0 && maxwg < ntot) ? maxwg : ntot;
+  if (ts == 128)
+    hipLaunchKernelGGL(k_gemm_ring<128>, dim3(grid), dim3(512), 0, st, probs, segs, nseg, ntot);
+  else
+    hipLaunchKernelGGL(k_gemm_ring<64>, dim3(grid), dim3(256), 0, st, probs, segs, nseg, ntot);
+  return hipGetLastError();
+}
 SEG_LAUNCH(launch_make_u, k_make_u, 256)

@@ -19,8 +19,9 @@ hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st);
 hipError_t launch_damp_fill(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
 hipError_t launch_chol_panel(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
 hipError_t launch_gemm64(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
-hipError_t launch_gemm_ring64(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
-hipError_t launch_gemm_ring128(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
+// ts = 64 or 128; at most maxwg workgroups (0: one per tile), persistent over the ntot tiles
+hipError_t launch_gemm_ring(int ts, const FacProb* probs, const Seg* segs, int nseg, int ntot, int maxwg,
+                            hipStream_t st);
 hipError_t launch_make_u(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
 
 // Sweep
