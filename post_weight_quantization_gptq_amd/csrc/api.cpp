@@ -622,8 +622,10 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   const FacProb* dp = (const FacProb*)(d + o_probs);
   LAUNCH(c, "k_damp_lambda", launch_damp_lambda(dp, np, c->stream));
   // the side stream's updates take at most this many CUs (one workgroup per
-  // CU), leaving the rest to the panels and the narrow updates
-  const int side_wg = std::max(1, c->ncu * 5 / 8);
+  // CU, whose registers fill the CU), leaving about 96 to the serial chain:
+  // the 64 panel workgroups of a 4096-wide problem and its narrow updates
+  // (measured best at n = 4096 among caps of 128 to 256 CUs)
+  const int side_wg = std::max(1, c->ncu - std::min(96, c->ncu / 2));
   for (const L& l : launches) {
     const Seg* sg = (const Seg*)(d + l.off);
     hipStream_t st = l.side ? c->side : c->stream;

@@ -593,9 +593,9 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
 // Products of the factor when n % 64 == 0 (every K range, row offset and
 // pitch is then a multiple of 64): one TS x TS tile per workgroup (TS = 128
 // on 8 waves of 64 x 32, or TS = 64 on 4 waves of 32 x 32), fp64 MFMA
-// 16x16x4.  K chunks of 16 go from global memory straight into a 3-stage
-// LDS ring (global_load_lds, 16 B per lane), two chunks ahead, so no
-// register staging and no load latency on the critical path.
+// 16x16x4.  K chunks of 16 go from global memory straight into an LDS ring
+// (global_load_lds, 16 B per lane; 3 stages for 128-wide tiles, 6 for 64-wide
+// ones), so no register staging and no load latency on the critical path.
 //   - k-contiguous operands (L always, and L again as B in the Cholesky
 //     update) sit row-major, 128 B per row and chunk, the 16-byte k-pairs
 //     XOR-swizzled by (row / 2) % 8: a lane reads its two k values with one
@@ -606,13 +606,29 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
 // step p, the same for both operands, so each pair step sums the 8 k's of
 // its range once.  Rows past the tile's edge read a valid row whose
 // results are never stored.
+// s_waitcnt vmcnt(ahead * PER) for a runtime ahead in [0, NST - 2]
+template <int NST, int PER>
+__device__ __forceinline__ void ring_wait(int ahead) {
+  if constexpr (NST > 2) {
+    if (ahead >= NST - 2) {
+      __builtin_amdgcn_s_waitcnt(VmWait<(NST - 2) * PER>::value);
+      return;
+    }
+    ring_wait<NST - 1, PER>(ahead);
+  } else {
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::value);
+  }
+}
+
 template <int TS>
 struct RingCfg {
   static constexpr int NW = TS == 128 ? 8 : 4;  // waves
   static constexpr int WGC = NW / 2;            // wave grid 2 x WGC
   static constexpr int WM = TS / 2, WN = TS / WGC;
   static constexpr int MI = WM / 16, NI = WN / 16;
-  static constexpr int KC = 16, NST = 3;
+  // 64-wide tiles compute a stage in about 1000 cycles, 128-wide ones in
+  // about 4000: the narrow ring keeps five stages in flight, the wide one two
+  static constexpr int KC = 16, NST = TS == 128 ? 3 : 6;
   static constexpr int OPB = TS * KC * 8;       // bytes per operand per stage
   static constexpr int STB = 2 * OPB;
   static constexpr int NQ = OPB / 1024 / NW;    // global_load_lds per operand per wave per stage
@@ -717,16 +733,15 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
       for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0;
 
   const int li = lane & 15, g = lane >> 4;
-  if (nst > 0) issue(0, 0);
-  if (nst > 1) issue(1, 1);
+#pragma unroll
+  for (int q = 0; q < NST - 1; ++q)
+    if (q < nst) issue(q, q);
   for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst)
-      __builtin_amdgcn_s_waitcnt(VmWait<2 * NQ>::value);
-    else
-      __builtin_amdgcn_s_waitcnt(VmWait<0>::value);
+    // stage st has landed once at most (stages issued after it) x 2 NQ loads remain
+    ring_wait<NST, 2 * NQ>(min(NST - 2, nst - 1 - st));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (st + 2 < nst) issue(st + 2, (st + 2) % NST);
+    if (st + NST - 1 < nst) issue(st + NST - 1, (st + NST - 1) % NST);
     const uint8_t* sa = lds + (st % NST) * STB;
     const uint8_t* sb = sa + OPB;
 #pragma unroll
