@@ -18,8 +18,11 @@
  *   - A context owns its device workspace (grown on demand, kept until
  *     gptq_destroy) and the HIP stream it was created with.  Calls are
  *     asynchronous on that stream except those marked SYNC, which wait for the
- *     stream before returning.  A context is not thread-safe: one context per
- *     host thread/stream.
+ *     stream before returning.  The context also owns a second stream (default
+ *     priority) on which the factor runs part of its trailing updates; every
+ *     call joins it back into the context's stream by event before its last
+ *     launch, so work later enqueued on the context's stream sees all results.
+ *     A context is not thread-safe: one context per host thread/stream.
  *   - Every call returns a gptq_status.  Argument errors are detected on the
  *     host before anything is launched.  After GPTQ_ERR_HIP the HIP error text
  *     is available from gptq_last_error().
@@ -49,11 +52,11 @@ typedef struct gptq_ctx_s* gptq_ctx;
 
 /* Create a context on HIP device `device`, issuing work on `stream` (a
  * hipStream_t; NULL = the device's null stream).  *ctx [host] receives the
- * handle.  Allocates only host memory; device workspace is allocated by the
- * first call that needs it. */
+ * handle.  Creates the context's second stream and two events; device
+ * workspace is allocated by the first call that needs it. */
 int gptq_create(gptq_ctx* ctx, int device, void* stream);
 
-/* Wait for the context's stream, free its workspace and the context. */
+/* Wait for the context's streams, free its workspace and the context. */
 int gptq_destroy(gptq_ctx ctx);
 
 /* Static text for a status code. */
