@@ -670,7 +670,7 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     oW[p] = totW;
     if (!J.Ww_ext) totW += (size_t)J.out * J.nt;
     oE[p] = totE;
-    totE += (size_t)J.out * sb * J.block;
+    totE += 2 * (size_t)J.out * sb * J.block;  // two super-blocks: one swept while the other's far update runs
     oO[p] = totO;
     totO += (size_t)J.out * 2;
     oD[p] = totD;
@@ -717,21 +717,23 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
   Blob b;
   const size_t o_L = b.add(L);
   struct Lc {
-    int kind;  // 0 init, 1 rowfit, 2 sweep, 3 trail
+    int kind;  // 0 init, 1 rowfit, 2 sweep, 3 trail, 6 fork, 7 join (as in the factor)
     int block;
+    bool side;
     size_t off;
     int nseg, nwg;
   };
   std::vector<Lc> launches;
-  auto add_launch = [&](int kind, int block, std::vector<Seg>& segs) {
+  auto add_launch = [&](int kind, int block, std::vector<Seg>& segs, bool side = false) {
     int nwg = 0;
     for (auto& s : segs) {
       s.wg0 = nwg;
       nwg += s.nwg;
     }
     if (nwg == 0) return;
-    launches.push_back(Lc{kind, block, b.add(segs), (int)segs.size(), nwg});
+    launches.push_back(Lc{kind, block, side, b.add(segs), (int)segs.size(), nwg});
   };
+  auto add_sync = [&](int kind) { launches.push_back(Lc{kind, 0, false, 0, 0, 0}); };
   {
     std::vector<Seg> s, f;
     for (int p = 0; p < nl; ++p) {
@@ -744,6 +746,13 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
   std::vector<int> blocks;
   for (auto& J : jobs)
     if (std::find(blocks.begin(), blocks.end(), J.block) == blocks.end()) blocks.push_back(J.block);
+  // At a super-block's end, the next super-block's columns are updated on
+  // the main stream (its sweeps read them); the columns past it on the side
+  // stream, beside the next super-block's sweeps (which neither read nor
+  // write them; the errors sit in the other half of the two-super-block
+  // buffer), joined before the next far update.  Needs the groups to nest in
+  // a super-block (a group fit reads its whole group).
+  bool side_busy = false;
   for (int k = 0; k < maxblk; ++k) {
     for (int B : blocks) {
       std::vector<Seg> s;
@@ -751,30 +760,54 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
         if (jobs[p].block == B && k < L[p].nblk) s.push_back(Seg{p, 0, cdiv(jobs[p].out, 16), k, 0, 0, 0, 0});
       add_launch(2, B, s);
     }
-    std::vector<Seg> tn, tf;  // inside the super-block (64 tiles), past it (128 tiles)
+    std::vector<Seg> tn, crit, bulk;  // inside the super-block (64 tiles), past it (64 / 128 tiles)
     for (int p = 0; p < nl; ++p) {
       if (k >= L[p].nblk) continue;
-      const int B = jobs[p].block, n = jobs[p].n, nt = jobs[p].nt, sb = sbk[p];
+      const int B = jobs[p].block, n = jobs[p].n, nt = jobs[p].nt, sb = sbk[p], sbw = sb * B;
       const int b0 = k * B, b1 = std::min(b0 + B, n);
-      const int sb0 = (k / sb) * sb * B, sb1 = std::min(sb0 + sb * B, n);
+      const int sb0 = (k / sb) * sbw, sb1 = std::min(sb0 + sbw, n);
+      const int par = ((k / sb) & 1) * jobs[p].out * L[p].ldE;  // this super-block's half of the error buffer
       if (b1 < sb1)  // rest of the super-block
-        tn.push_back(Seg{p, 0, cdiv(jobs[p].out, 64) * cdiv(sb1 - b1, 64), (k % sb) * B, b0, b1 - b0, b1, sb1});
-      if (b1 == sb1 && sb1 < nt)  // end of the super-block: all columns past it
-        tf.push_back(Seg{p, 0, cdiv(jobs[p].out, 128) * cdiv(nt - sb1, 128), 0, sb0, sb1 - sb0, sb1, nt});
+        tn.push_back(Seg{p, 0, cdiv(jobs[p].out, 64) * cdiv(sb1 - b1, 64), par + (k % sb) * B, b0, b1 - b0, b1, sb1});
+      if (b1 == sb1 && sb1 < nt) {  // end of the super-block: all columns past it
+        const bool nest = jobs[p].group == 0 || sbw % jobs[p].group == 0;
+        const int S = nest ? std::min(sb1 + sbw, nt) : nt;
+        crit.push_back(Seg{p, 0, cdiv(jobs[p].out, 64) * cdiv(S - sb1, 64), par, sb0, sb1 - sb0, sb1, S});
+        if (S < nt) bulk.push_back(Seg{p, 0, cdiv(jobs[p].out, 128) * cdiv(nt - S, 128), par, sb0, sb1 - sb0, S, nt});
+      }
     }
     add_launch(3, 64, tn);
-    add_launch(3, 128, tf);
+    if (!crit.empty()) {
+      if (side_busy) add_sync(7);  // the previous far update covers the columns updated now
+      side_busy = false;
+      if (!bulk.empty()) {
+        add_sync(6);
+        add_launch(3, 128, bulk, true);
+        side_busy = true;
+      }
+      add_launch(3, 64, crit);
+    }
   }
+  if (side_busy) add_sync(7);
   uint8_t* d = nullptr;
   if ((rc = upload(c, b, &d))) return rc;
   const QLayer* dL = (const QLayer*)(d + o_L);
   for (const Lc& l : launches) {
     const Seg* sg = (const Seg*)(d + l.off);
+    hipStream_t st = l.side ? c->side : c->stream;
     switch (l.kind) {
       case 0: LAUNCH(c, "k_init_work", launch_init_work(dL, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: LAUNCH(c, "k_rowfit", launch_rowfit(dL, sg, l.nseg, l.nwg, c->stream)); break;
       case 2: LAUNCH(c, "k_sweep", launch_sweep(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3: LAUNCH(c, "k_trail", launch_trail(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 3: LAUNCH_ON(c, st, "k_trail", launch_trail(l.block, dL, sg, l.nseg, l.nwg, st)); break;
+      case 6:
+        HIPCHK(c, hipEventRecord(c->fork_ev, c->stream));
+        HIPCHK(c, hipStreamWaitEvent(c->side, c->fork_ev, 0));
+        break;
+      case 7:
+        HIPCHK(c, hipEventRecord(c->join_ev, c->side));
+        HIPCHK(c, hipStreamWaitEvent(c->stream, c->join_ev, 0));
+        break;
     }
   }
   LAUNCH(c, "k_objective", launch_objective(dL, nl, c->stream));

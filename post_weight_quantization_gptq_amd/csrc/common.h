@@ -97,7 +97,7 @@ struct QLayer {
   float* scales;    // [out][ng]
   uint8_t* zeros;   // [out][ng]
   float* err;       // [out][n] or null
-  float* Eb;        // block errors [out][block]
+  float* Eb;        // errors of a super-block [2][out][ldE], by super-block parity
   const float* dinv;  // 1 / U_jj [nt], filled by k_init_work
   double* objp;     // per row: {sum E^2, sum D^2}, accumulated block by block
   double* obj;      // [2] {J, J_lam} (device)

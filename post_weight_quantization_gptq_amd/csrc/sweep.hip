@@ -176,6 +176,10 @@ __device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx&
       st.hv[c] = what;
       st.ev[c] = e;
     }
+    // take the owner's values now (an empty asm pins them), so the 16 owners'
+    // candidates do not all stay live to the end of the block: 138 registers
+    // instead of 439, which lets other kernels share the CU
+    __asm__ volatile("" : "+v"(st.qv[c]), "+v"(st.hv[c]), "+v"(st.ev[c]));
 #pragma unroll
     for (int c2 = 0; c2 < CPL; ++c2) st.wv[c2] = fmaf(-e, ucur[c2], st.wv[c2]);
     if (j + 1 < B) {
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
     const int lc = CPL * l16 + c;
     if (rv && lc < bw) {
       ly.codes[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
-      ly.Eb[(size_t)row * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
+      ly.Eb[((size_t)((blk / ly.sbk) & 1) * ly.out + row) * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
       if (ly.err) ly.err[(size_t)row * ly.n + b0 + lc] = st.ev[c];
       const double d = (double)wo[c] - (double)st.hv[c];
       sd += d * d;
