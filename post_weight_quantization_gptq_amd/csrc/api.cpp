@@ -799,7 +799,9 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
       case 0: LAUNCH(c, "k_init_work", launch_init_work(dL, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: LAUNCH(c, "k_rowfit", launch_rowfit(dL, sg, l.nseg, l.nwg, c->stream)); break;
       case 2: LAUNCH(c, "k_sweep", launch_sweep(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3: LAUNCH_ON(c, st, "k_trail", launch_trail(l.block, dL, sg, l.nseg, l.nwg, st)); break;
+      case 3:  // beside the sweeps: one workgroup per CU, which leaves room on each CU for a sweep's
+        LAUNCH_ON(c, st, "k_trail", launch_trail(l.block, dL, sg, l.nseg, l.nwg, l.side ? c->ncu : 0, st));
+        break;
       case 6:
         HIPCHK(c, hipEventRecord(c->fork_ev, c->stream));
         HIPCHK(c, hipStreamWaitEvent(c->side, c->fork_ev, 0));

@@ -110,6 +110,11 @@ struct QLayer {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+// global-memory views: loads through them count only against vmcnt (a
+// generic pointer's flat loads also count against lgkmcnt, which LDS waits
+// would then have to drain)
+typedef const __attribute__((address_space(1))) double gdouble;
+typedef const __attribute__((address_space(1))) float gfloat;
 
 // s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding).
 template <int N>

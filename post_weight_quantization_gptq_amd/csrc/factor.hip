@@ -733,6 +733,21 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
       for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0;
 
   const int li = lane & 15, g = lane >> 4;
+  // C's current values, loaded first so their latency hides behind the
+  // ring's (vector loads complete in issue order, so the waits below, which
+  // count only the ring's loads, are only stricter for them), and all of them
+  // before any store: one round trip, not one per element
+  double cur[MI][NI][4];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = wr * C_::WM + 16 * mi + g + 4 * r;
+        const int j = wc * C_::WN + 16 * ni + li;
+        cur[mi][ni][r] = (beta != 0.0 && i < mt && j < nt) ? ((const gdouble*)C)[(size_t)i * ldc + j] : 0.0;
+      }
 #pragma unroll
   for (int q = 0; q < NST - 1; ++q)
     if (q < nst) issue(q, q);
@@ -778,18 +793,6 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
             acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mi][u], bv[ni][u], acc[mi][ni], 0, 0, 0);
     }
   }
-  // every load of C before any store (one memory round trip, not one per element)
-  double cur[MI][NI][4];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = wr * C_::WM + 16 * mi + g + 4 * r;
-        const int j = wc * C_::WN + 16 * ni + li;
-        cur[mi][ni][r] = (beta != 0.0 && i < mt && j < nt) ? C[(size_t)i * ldc + j] : 0.0;
-      }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll

@@ -28,5 +28,6 @@ hipError_t launch_make_u(const FacProb* probs, const Seg* segs, int nseg, int nw
 hipError_t launch_init_work(const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
 hipError_t launch_rowfit(const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
 hipError_t launch_sweep(int block, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
-hipError_t launch_trail(int ts, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
+// at most maxwg workgroups (0: one per tile), persistent over the nwg tiles
+hipError_t launch_trail(int ts, const QLayer* L, const Seg* segs, int nseg, int nwg, int maxwg, hipStream_t st);
 hipError_t launch_objective(const QLayer* L, int nl, hipStream_t st);

@@ -324,7 +324,8 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
 // 32 go through registers into a double-buffered LDS pair, so the loads of
 // chunk c+1 are in flight while chunk c is multiplied.
 template <int TS>
-__global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, const Seg* __restrict__ segs, int nseg) {
+__global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, const Seg* __restrict__ segs, int nseg,
+                                               int ntot) {
   constexpr int KC = 32;
   constexpr int MB = TS / 64;        // 32x32 blocks per wave side
   constexpr int TPR = 256 / TS;      // threads per E row
@@ -332,12 +333,15 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
   constexpr int VB = TS / 8;         // U values per thread (8 threads per k row)
   __shared__ float As[2][TS][KC + 1];
   __shared__ __attribute__((aligned(16))) float Bs[2][KC][TS + 4];
-  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  // tiles vt = blockIdx.x, blockIdx.x + gridDim.x, ... < ntot (persistent when
+  // the grid is smaller than the tile count)
+  for (int vt = blockIdx.x; vt < ntot; vt += gridDim.x) {
+  const Seg sg = segs[find_seg(segs, nseg, vt)];
   const QLayer ly = L[sg.prob];
   const int eoff = sg.a, kb = sg.b, K = sg.c, j0 = sg.d, j1 = sg.e;
   const int nt = ly.nt;
   const int tiles_j = (j1 - j0 + TS - 1) / TS;
-  const int t = blockIdx.x - sg.wg0;
+  const int t = vt - sg.wg0;
   const int i0 = TS * (t / tiles_j), jj0 = j0 + TS * (t % tiles_j);
   const int mt = min(TS, ly.out - i0), ntc = min(TS, j1 - jj0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -356,6 +360,22 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
   const float* ap = ly.Eb + (size_t)(i0 + (arow_ok ? ar : 0)) * ly.ldE + eoff;
   const bool evec = (ly.ldE % 4) == 0 && (eoff % 4) == 0;
   const bool uvec = (nt % 4) == 0 && (jj0 % 4) == 0 && (((uintptr_t)ly.U) & 15) == 0;
+  // The tile's W, loaded first so its latency hides behind the K loop, and
+  // all of it before any store (the stores could alias the loads as far as
+  // the compiler knows, so interleaving them would cost one memory round
+  // trip per element).  Global-space loads: they count only against vmcnt.
+  float* wbase = ly.Ww + (size_t)i0 * nt + jj0;
+  float cur[MB][MB][16];
+#pragma unroll
+  for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < MB; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
+        cur[mi][ni][r] = (i < mt && j < ntc) ? ((const gfloat*)wbase)[(size_t)i * nt + j] : 0.f;
+      }
   f32x4 ra[VA / 4], rb[VB / 4];
   auto load = [&](int kc) {
 #pragma unroll
@@ -424,21 +444,6 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
     __syncthreads();
     buf ^= 1;
   }
-  // All loads of the tile's W before any store: the stores could alias the
-  // loads as far as the compiler knows, so interleaving them would cost one
-  // memory round trip per element.
-  float* wbase = ly.Ww + (size_t)i0 * nt + jj0;
-  float cur[MB][MB][16];
-#pragma unroll
-  for (int mi = 0; mi < MB; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < MB; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
-        cur[mi][ni][r] = (i < mt && j < ntc) ? wbase[(size_t)i * nt + j] : 0.f;
-      }
 #pragma unroll
   for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
@@ -449,6 +454,8 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
         const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
         if (i < mt && j < ntc) wbase[(size_t)i * nt + j] = cur[mi][ni][r] - acc[mi][ni][r];
       }
+  __syncthreads();  // the next tile refills the LDS pair
+  }
 }
 
 // J_lam = sum E^2, ||D||^2 (plus the appended columns, whose final values are
@@ -499,12 +506,13 @@ __global__ __launch_bounds__(256) void k_objective(const QLayer* __restrict__ L,
 
 QSEG_LAUNCH(launch_init_work, k_init_work, 256)
 QSEG_LAUNCH(launch_rowfit, k_rowfit, 256)
-hipError_t launch_trail(int ts, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st) {
+hipError_t launch_trail(int ts, const QLayer* L, const Seg* segs, int nseg, int nwg, int maxwg, hipStream_t st) {
   if (nwg <= 0) return hipSuccess;
+  const int grid = (maxwg > 0 && maxwg < nwg) ? maxwg : nwg;
   if (ts == 64)
-    hipLaunchKernelGGL(k_trail<64>, dim3(nwg), dim3(256), 0, st, L, segs, nseg);
+    hipLaunchKernelGGL(k_trail<64>, dim3(grid), dim3(256), 0, st, L, segs, nseg, nwg);
   else
-    hipLaunchKernelGGL(k_trail<128>, dim3(nwg), dim3(256), 0, st, L, segs, nseg);
+    hipLaunchKernelGGL(k_trail<128>, dim3(grid), dim3(256), 0, st, L, segs, nseg, nwg);
   return hipGetLastError();
 }
 
