@@ -524,7 +524,8 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   const size_t o_probs = b.add(probs);
   struct L {
     int kind;  // 0 fill, 1 panel, 2 gemm (general, 64 tiles), 3 ring gemm 64, 4 ring gemm 128, 5 makeu,
-               // 6 fork (side stream waits for the main stream), 7 join (main waits for the side stream)
+               // 6 fork (side stream waits for the main stream), 7 join (main waits for the side stream),
+               // 8 panel pair
     bool side;  // launch on the side stream
     size_t off;
     int nseg, nwg;
@@ -561,14 +562,18 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   // neither read nor write it) and is joined before the next outer update.
   // With the general products (n % 64 != 0) everything stays on one stream.
   bool side_busy = false;
-  for (int k = 0; k < maxnb; ++k) {
-    std::vector<Seg> pan, inner, crit, bulk;
+  // Steps go in pairs (k, k+1) inside an outer panel: one launch of
+  // k_chol_panel2 (kind 8) does both; a last block without a partner takes
+  // the single-step k_chol_panel.
+  for (int k = 0; k < maxnb; k += 2) {
+    std::vector<Seg> pan, pan2, inner, crit, bulk;
     int bulk_rows = 0;
     for (int p = 0; p < np; ++p) {
       const int n = jobs[p].n, nb = cdiv(n, 64);
       if (k >= nb) continue;
-      pan.push_back(Seg{p, 0, nb, k, 0, 0, 0, 0});
-      const int k0 = 64 * k, pw = std::min(64, n - k0);
+      const bool pair = k + 1 < nb;
+      (pair ? pan2 : pan).push_back(Seg{p, 0, nb, k, 0, 0, 0, 0});
+      const int k0 = 64 * k, pw = std::min(pair ? 128 : 64, n - k0);
       const int P0 = (k0 / 256) * 256, P1 = std::min(P0 + 256, n);
       const int c0 = k0 + pw;
       if (c0 < P1) {  // rest of the outer panel
@@ -590,6 +595,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
         }
       }
     }
+    add_launch(8, pan2);
     add_launch(1, pan);
     add_launch(ring ? 3 : 2, inner);
     if (!crit.empty()) {
@@ -632,6 +638,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
     switch (l.kind) {
       case 0: LAUNCH(c, "k_damp_fill", launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: LAUNCH(c, "k_chol_panel", launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
+      case 8: LAUNCH(c, "k_chol_panel2", launch_chol_panel2(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 2: LAUNCH(c, "k_gemm64", launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
       case 3: LAUNCH_ON(c, st, "k_gemm_ring64", launch_gemm_ring(64, dp, sg, l.nseg, l.nwg, 0, st)); break;
       case 4:

@@ -27,6 +27,9 @@
 #include "launch.h"
 
 #define NB 64
+// LDS pitch of a 64x64 fp64 block: rows 16-byte aligned (one ds_read_b128
+// gives a lane two k values) and 16 rows of a column read hit distinct banks
+#define LDP (NB + 2)
 
 // ------------------------------------------------------------ damping -----
 __global__ __launch_bounds__(256) void k_damp_lambda(const FacProb* __restrict__ probs, int nprob) {
@@ -147,7 +150,7 @@ struct SubSteps<16> {
   __device__ __forceinline__ static void run(PanelWave&, double*, int, int, double) {}
 };
 
-__device__ __forceinline__ int chol64_blocked(double (*M)[NB + 1], double* dv, double* lb, int* flag) {
+__device__ __forceinline__ int chol64_blocked(double (*M)[LDP], double* dv, double* lb, int* flag) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   PanelWave st;
   st.dvr = 0.0;
@@ -205,7 +208,7 @@ __device__ __forceinline__ int chol64_blocked(double (*M)[NB + 1], double* dv, d
 // levels [[A,0],[B,C]]^{-1} = [[A^-1,0],[-C^-1 B A^-1, C^-1]] on fp64 MFMA
 // (16 -> 32: waves 0 and 1; 32 -> 64: one 16x16 output block per wave).
 // Ys is row-major with zeros above the diagonal; Tm is scratch [32][33].
-__device__ __forceinline__ void inv64_waves(double (*Ls)[NB + 1], const double* dv, double (*Ys)[NB + 1],
+__device__ __forceinline__ void inv64_waves(double (*Ls)[LDP], const double* dv, double (*Ys)[LDP],
                                             double (*Tm)[33]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   {
@@ -277,6 +280,72 @@ __device__ __forceinline__ void inv64_waves(double (*Ls)[NB + 1], const double* 
   __syncthreads();
 }
 
+// 64x64x64 block products on the four waves (each wave a 32x32 quarter of
+// the result, fp64 MFMA 16x16x4), operands in LDS:
+//   acc += sum_t Aop(r, t) Bop(t, c),  Aop(r, t) = A[r][t],
+//   Bop(t, c) = B[t][c] (BT = false) or B[c][t] (BT = true).
+// K order: in pair step p, lane group g holds t = 8p + 2g + u in sub-step u
+// (the same for both operands), so a row operand is one ds_read_b128.
+// The accumulator layout: wave w holds rows 32 (w / 2) + 16 mi + (lane / 16)
+// + 4 q and columns 32 (w % 2) + 16 ni + lane % 16.
+template <bool BT>
+__device__ __forceinline__ void blk_mma(f64x4 (&acc)[2][2], const double (*A)[LDP], const double (*B)[LDP]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1;
+  const int li = lane & 15, g = lane >> 4;
+  // fully unrolled: a loop back-edge makes the compiler move the
+  // accumulators between AGPRs and VGPRs (and drain the MFMA pipe) each trip
+#pragma unroll
+  for (int ps = 0; ps < NB / 8; ++ps) {
+    const int t = 8 * ps + 2 * g;
+    f64x2 av[2], bv[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) av[mi] = *(const f64x2*)&A[32 * wr + 16 * mi + li][t];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int c = 32 * wc + 16 * ni + li;
+      if (BT) {
+        bv[ni] = *(const f64x2*)&B[c][t];
+      } else {
+        bv[ni][0] = B[t][c];
+        bv[ni][1] = B[t + 1][c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mi][u], bv[ni][u], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void blk_neg(f64x4 (&acc)[2][2]) {
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[mi][ni][q] = -acc[mi][ni][q];
+}
+
+// visit the accumulator's elements: f(mi, ni, q, row, col)
+template <class F>
+__device__ __forceinline__ void blk_each(F&& f) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        f(mi, ni, q, 32 * wr + 16 * mi + (lane >> 4) + 4 * q, 32 * wc + 16 * ni + (lane & 15));
+}
+
+__device__ __forceinline__ void blk_zero(f64x4 (&acc)[2][2]) {
+  blk_each([&](int mi, int ni, int q, int, int) { acc[mi][ni][q] = 0.0; });
+}
+
 // Panel step k (64 columns starting at k0), one workgroup per 64-block of
 // the problem.  Every group factors the diagonal block the same way and
 // inverts it; then
@@ -290,9 +359,9 @@ __device__ __forceinline__ void inv64_waves(double (*Ls)[NB + 1], const double* 
 // The products run on fp64 MFMA, 4 waves of 32 x 32.
 __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ probs,
                                                     const Seg* __restrict__ segs, int nseg) {
-  __shared__ double LT[NB][NB + 1];  // the diagonal block, then L (row-major)
-  __shared__ double Ys[NB][NB + 1];  // L^{-1}, row-major
-  __shared__ double Rs[NB][NB + 1];  // this group's panel rows, or B_kj
+  __shared__ __attribute__((aligned(16))) double LT[NB][LDP];  // the diagonal block, then L (row-major)
+  __shared__ __attribute__((aligned(16))) double Ys[NB][LDP];  // L^{-1}, row-major
+  __shared__ __attribute__((aligned(16))) double Rs[NB][LDP];  // this group's panel rows, or B_kj
   __shared__ double Tm[32][33];
   __shared__ double lb[2 * NB];
   __shared__ double dv[NB];
@@ -351,32 +420,11 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
   // else:  Out(r, c) = sum_t Rs[r][t] Ys[c][t]   (L_ik = A_ik L_kk^{-T})
   const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
   f64x4 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[a][b][q] = 0.0;
-#pragma unroll 4
-  for (int kk = 0; kk < NB / 4; ++kk) {
-    double av[2], bv[2];
-    const int t = 4 * kk + (lane >> 4);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int r = 32 * wr + 16 * mi + (lane & 15);
-      av[mi] = yrole ? Ys[r][t] : Rs[r][t];
-    }
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int c = 32 * wc + 16 * ni + (lane & 15);
-      bv[ni] = yrole ? Rs[t][c] : Ys[c][t];
-    }
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
-  }
+  blk_zero(acc);
+  if (yrole)
+    blk_mma<false>(acc, Ys, Rs);
+  else
+    blk_mma<true>(acc, Rs, Ys);
   double* out = yrole ? pb.Y + (size_t)k0 * n + NB * j : A + (size_t)r0 * n + k0;
   const int mc = yrole ? NB : m;
 #pragma unroll
@@ -389,6 +437,174 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
         const int c = 32 * wc + 16 * ni + (lane & 15);
         if (r < mr && c < mc) out[(size_t)r * n + c] = acc[mi][ni][q];
       }
+}
+
+// Two 64-column steps k, k+1 of one outer panel in a single launch.  Every
+// workgroup first runs the pair's diagonal chain itself: the leaf Cholesky
+// and inverse of D0 = A_kk, L10 = A_{k+1,k} L_kk^{-T}, D1 = A_{k+1,k+1} -
+// L10 L10^T, its leaf and inverse; then its own part:
+//   - row block i >= k+2: L_ik = A_ik L_kk^{-T}, then
+//     L_{i,k+1} = (A_{i,k+1} - L_ik L10^T) L_{k+1,k+1}^{-T};
+//   - row block k: writes Y_kk = L_kk^{-1}, Y_{k+1,k} = -Y_{k+1,k+1} L10 Y_kk,
+//     Y_{k+1,k+1}, and zeros to the end of the 256-wide diagonal block;
+//   - row block k+1: nothing (L10 is read by no later step, and writing it
+//     would race with the other groups' loads of A_{k+1,k});
+//   - column block j < k: Y_kj = Y_kk B_kj, then
+//     Y_{k+1,j} = Y_{k+1,k+1} (B_{k+1,j} - L10 Y_kj).
+// This replaces two panel launches and the narrow update between them; the
+// repeated diagonal work is parallel and costs less than the launches.
+// Needs k + 1 < nb (block k is then full; block k+1 may be partial).
+__global__ __launch_bounds__(256) void k_chol_panel2(const FacProb* __restrict__ probs,
+                                                     const Seg* __restrict__ segs, int nseg) {
+  __shared__ __attribute__((aligned(16))) double LT[NB][LDP];   // leaf workspace (D0, then D1), then the operand stage
+  __shared__ __attribute__((aligned(16))) double Y0[NB][LDP];   // L_kk^{-1}
+  __shared__ __attribute__((aligned(16))) double Y1[NB][LDP];   // L_{k+1,k+1}^{-1}
+  __shared__ __attribute__((aligned(16))) double L10[NB][LDP];  // A_{k+1,k}, then L10
+  __shared__ double Tm[32][33];
+  __shared__ double lb[2 * NB];
+  __shared__ double dv[NB];
+  __shared__ int flag;
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  const int n = pb.n, k = sg.a, nb = (n + NB - 1) / NB, g = blockIdx.x - sg.wg0;
+  const int k0 = k * NB, k1 = k0 + NB, m1 = min(NB, n - k1);
+  const bool yrole = g >= nb - k;
+  const int i = yrole ? k : k + g, j = yrole ? g - (nb - k) : 0;
+  const int tid = threadIdx.x;
+  double* A = pb.A;
+  double* Y = pb.Y;
+  const int r0 = i * NB, mr = min(NB, n - r0);
+  const bool own = yrole || i >= k + 2;
+  // loads: the pair's diagonal region and this group's two blocks
+  f64x4 d1[2][2], x1[2][2];  // D1 and (A_{i,k+1} or B_{k+1,j}), accumulator layout
+  double tx[16];             // A_ik or B_kj, row-major by thread
+  {
+    double ta[16], tb[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q, r = e >> 6, c = e & 63;
+      ta[q] = (c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
+      tb[q] = (r < m1) ? A[(size_t)(k1 + r) * n + k0 + c] : 0.0;
+      tx[q] = !own ? 0.0 : yrole ? Y[(size_t)(k0 + r) * n + NB * j + c]
+                                 : ((r < mr) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0);
+    }
+    blk_each([&](int mi, int ni, int q, int r, int c) {
+      d1[mi][ni][q] = (r < m1 && c <= r) ? A[(size_t)(k1 + r) * n + k1 + c] : 0.0;
+      x1[mi][ni][q] = !own ? 0.0 : yrole ? ((r < m1) ? Y[(size_t)(k1 + r) * n + NB * j + c] : 0.0)
+                                         : ((r < mr && c < m1) ? A[(size_t)(r0 + r) * n + k1 + c] : 0.0);
+    });
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q, r = e >> 6, c = e & 63;
+      LT[r][c] = ta[q];
+      L10[r][c] = tb[q];
+    }
+  }
+  __syncthreads();
+  int bad = chol64_blocked(LT, dv, lb, &flag);
+  if (bad >= 0) {
+    if (tid == 0 && g == 0) atomicMax(pb.info, n - (k0 + bad));
+    return;
+  }
+  inv64_waves(LT, dv, Y0, Tm);
+  f64x4 acc[2][2];
+  // L10 = A_{k+1,k} Y0^T
+  blk_zero(acc);
+  blk_mma<true>(acc, L10, Y0);
+  __syncthreads();
+  blk_each([&](int mi, int ni, int q, int r, int c) { L10[r][c] = acc[mi][ni][q]; });
+  __syncthreads();
+  // D1 - L10 L10^T, padded with the identity past m1
+  blk_neg(d1);
+  blk_mma<true>(d1, L10, L10);
+  blk_neg(d1);
+  blk_each([&](int mi, int ni, int q, int r, int c) {
+    LT[r][c] = (r < m1 && c < m1) ? d1[mi][ni][q] : ((r == c) ? 1.0 : 0.0);
+  });
+  __syncthreads();
+  bad = chol64_blocked(LT, dv, lb, &flag);
+  if (bad >= 0) {
+    if (tid == 0 && g == 0) atomicMax(pb.info, n - (k1 + bad));
+    return;
+  }
+  inv64_waves(LT, dv, Y1, Tm);  // LT is free from here on
+  const int P1 = min((k0 / 256) * 256 + 256, n);
+  if (!yrole && i == k) {
+    // Y rows of the pair: Y_kk, Y_{k+1,k} = -Y1 (L10 Y0), Y_{k+1,k+1}, zeros
+    // to the end of the outer panel's diagonal block
+    for (int e = tid; e < NB * (P1 - k0); e += 256) {
+      const int r = e / (P1 - k0), c = e % (P1 - k0);
+      Y[(size_t)(k0 + r) * n + k0 + c] = (c < NB && c <= r) ? Y0[r][c] : 0.0;
+    }
+    for (int e = tid; e < NB * (P1 - k1); e += 256) {
+      const int r = e / (P1 - k1), c = e % (P1 - k1);
+      if (r < m1) Y[(size_t)(k1 + r) * n + k1 + c] = (c < m1 && c <= r) ? Y1[r][c] : 0.0;
+    }
+    blk_zero(acc);
+    blk_mma<false>(acc, L10, Y0);
+    blk_each([&](int mi, int ni, int q, int r, int c) { LT[r][c] = acc[mi][ni][q]; });
+    __syncthreads();
+    blk_zero(acc);
+    blk_mma<false>(acc, Y1, LT);
+    blk_neg(acc);
+    blk_each([&](int mi, int ni, int q, int r, int c) {
+      if (r < m1) Y[(size_t)(k1 + r) * n + k0 + c] = acc[mi][ni][q];
+    });
+    return;
+  }
+  // Row block k+1 keeps A_{k+1,k} as it is: every group of this launch
+  // loads it at its start, and nothing after this launch reads L10 (the
+  // next updates read L's rows from k+2 on).
+  if (!yrole && i == k + 1) return;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    LT[e >> 6][e & 63] = tx[q];
+  }
+  __syncthreads();
+  blk_zero(acc);
+  if (!yrole) {
+    // L_ik = A_ik Y0^T
+    blk_mma<true>(acc, LT, Y0);
+    blk_each([&](int mi, int ni, int q, int r, int c) {
+      if (r < mr) A[(size_t)(r0 + r) * n + k0 + c] = acc[mi][ni][q];
+    });
+    __syncthreads();
+    blk_each([&](int mi, int ni, int q, int r, int c) { LT[r][c] = acc[mi][ni][q]; });
+    __syncthreads();
+    // A_{i,k+1} - L_ik L10^T, then times Y1^T
+    blk_neg(x1);
+    blk_mma<true>(x1, LT, L10);
+    blk_neg(x1);
+    __syncthreads();
+    blk_each([&](int mi, int ni, int q, int r, int c) { LT[r][c] = x1[mi][ni][q]; });
+    __syncthreads();
+    blk_zero(acc);
+    blk_mma<true>(acc, LT, Y1);
+    blk_each([&](int mi, int ni, int q, int r, int c) {
+      if (r < mr && c < m1) A[(size_t)(r0 + r) * n + k1 + c] = acc[mi][ni][q];
+    });
+  } else {
+    // Y_kj = Y0 B_kj
+    blk_mma<false>(acc, Y0, LT);
+    blk_each([&](int mi, int ni, int q, int r, int c) { Y[(size_t)(k0 + r) * n + NB * j + c] = acc[mi][ni][q]; });
+    __syncthreads();
+    blk_each([&](int mi, int ni, int q, int r, int c) { LT[r][c] = acc[mi][ni][q]; });
+    __syncthreads();
+    // B_{k+1,j} - L10 Y_kj, then Y1 times it
+    blk_neg(x1);
+    blk_mma<false>(x1, L10, LT);
+    blk_neg(x1);
+    __syncthreads();
+    blk_each([&](int mi, int ni, int q, int r, int c) { LT[r][c] = x1[mi][ni][q]; });
+    __syncthreads();
+    blk_zero(acc);
+    blk_mma<false>(acc, Y1, LT);
+    blk_each([&](int mi, int ni, int q, int r, int c) {
+      if (r < m1) Y[(size_t)(k1 + r) * n + NB * j + c] = acc[mi][ni][q];
+    });
+  }
 }
 
 // --------------------------------------------------- fp64 MFMA products ---
@@ -848,6 +1064,7 @@ hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st) {
 
 SEG_LAUNCH(launch_damp_fill, k_damp_fill, 256)
 SEG_LAUNCH(launch_chol_panel, k_chol_panel, 256)
+SEG_LAUNCH(launch_chol_panel2, k_chol_panel2, 256)
 SEG_LAUNCH(launch_gemm64, k_gemm<64>, 256)
 hipError_t launch_gemm_ring(int ts, const FacProb* probs, const Seg* segs, int nseg, int ntot, int maxwg,
                             hipStream_t st) {

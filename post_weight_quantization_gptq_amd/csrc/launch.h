@@ -18,6 +18,7 @@ hipError_t launch_syrk64_reduce(const RedProb64* probs, const RedTask* tasks, in
 hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st);
 hipError_t launch_damp_fill(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
 hipError_t launch_chol_panel(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
+hipError_t launch_chol_panel2(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
 hipError_t launch_gemm64(const FacProb* probs, const Seg* segs, int nseg, int nwg, hipStream_t st);
 // ts = 64 or 128; at most maxwg workgroups (0: one per tile), persistent over the ntot tiles
 hipError_t launch_gemm_ring(int ts, const FacProb* probs, const Seg* segs, int nseg, int ntot, int maxwg,

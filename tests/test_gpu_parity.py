@@ -282,3 +282,26 @@ def test_batched_matches_oracle(ctx):
         Hr = o.hessian(_bits(l["X"]))
         Hl, lam = o.damp(Hr, lam_rel=s.lam_rel)
         check_sweep(b, l["W"].numpy().astype(np.float64), o.factor_u(Hl), s.bits, s.group, s.block, Hr, lam)
+
+
+def test_batched_factor_more_groups_than_cus(ctx):
+    """24 layers of n = 768 in one batched call: each step's panel launch has
+    24 x 12 = 288 workgroups (one per CU), so late groups start after early
+    ones have finished and written their outputs.  Every U must match the
+    oracle's factor of its own H (a group reading another group's output of
+    the same launch would break this)."""
+    n, out, tokens = 768, 32, 1536
+    layers = []
+    for i in range(24):
+        X = _rand_x(tokens, n, 500 + i)
+        W = torch.from_numpy(np.random.default_rng(600 + i).normal(0.0, 0.02, size=(out, n)).astype(np.float32))
+        layers.append(dict(W=W.cuda(), X=X.cuda(), bits=4, group=64, block=64, lam_rel=0.01))
+    ctx.quantize_batched(layers)
+    torch.cuda.synchronize()
+    for i, b in enumerate(layers):
+        assert b["info"] == 0, i
+        Hn = np32(b["H"]).astype(np.float64)
+        Hl, lam = o.damp(Hn, lam_rel=0.01)
+        Ur = o.factor_u(Hl)
+        Ug = np32(b["U"]).astype(np.float64)
+        assert np.abs(Ug - Ur).max() <= 2e-6 * np.abs(Ur).max(), i
