@@ -181,7 +181,9 @@ def main():
     one_step()
     torch.cuda.synchronize()
     names = ["k_xpose", "k_syrk", "k_syrk_reduce", "k_syrk64", "k_syrk64_reduce", "k_damp_lambda", "k_damp_fill", "k_chol_panel", "k_chol_panel2",
-             "k_gemm64", "k_gemm_ring64", "k_gemm_ring128", "k_make_u", "k_init_work", "k_rowfit", "k_sweep", "k_trail", "k_objective"]
+             "k_gemm64", "k_gemm_ring64", "k_gemm_ring128", "k_make_u", "k_init_work", "k_rowfit", "k_sweep", "k_trail", "k_objective",
+             "k_lora_lambda", "k_start_block", "k_dgemm", "k_dsum", "k_gram_chol", "k_apply", "k_lora_assemble",
+             "k_lora_extract"]
     breakdown = {}
     for nm in names:
         ms, cnt = ctx.kernel_time(nm)

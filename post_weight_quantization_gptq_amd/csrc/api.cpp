@@ -1122,6 +1122,10 @@ GPTQ_API int gptq_lora(gptq_ctx c, const float* W, int32_t out, int32_t n, const
     return c->slots.p;
   };
   hooks.set_err = [&](int st, const char* msg) { return set_err(c, st, "%s", msg); };
+  hooks.launch = [&](const char* name, const std::function<hipError_t()>& f) -> int {
+    LAUNCH(c, name, f());
+    return GPTQ_OK;
+  };
   rc = run_lora(c->stream, io, hooks);
   if (rc) return rc;
   Slot* ds = (Slot*)c->slots.p;

@@ -19,6 +19,7 @@
 #include <vector>
 
 #include "../../include/gptq.h"
+#include "blk64.h"
 #include "common.h"
 #include "launch.h"
 #include "plan.h"
@@ -135,47 +136,216 @@ __global__ void k_start_block(double* __restrict__ V, int n, int r) {
   V[i] = (double)(x >> 11) * (2.0 / 9007199254740992.0) - 1.0;
 }
 
-// G (r x r, symmetric PD) = L L^T -> Linv = L^{-1} (lower); then Z L^{-T} has
-// orthonormal columns.  One workgroup, r <= 128 (L in LDS, the inverse is
-// built column by column in global memory, one thread per column).
-__global__ __launch_bounds__(256) void k_chol_inv_small(const double* __restrict__ G, double* __restrict__ Linv, int r) {
-  __shared__ double Ls[128 * 128];
+// ------------------------------------------------ Cholesky-QR pieces -----
+// One Cholesky-QR pass turns Z (n x r, r <= 128) into V = Z L^{-T} with
+// G = Z^T Z = L L^T, so V^T V = I.  Two kernels:
+//   k_gram_chol: G by row chunks (each workgroup the Gram of its rows, 64 at
+//     a time, on fp64 MFMA), then the last workgroup to finish sums the
+//     partials in chunk order and factors G, as 64x64 blocks: the leaf
+//     Cholesky and inverse of G00, L10 = G10 L00^{-T}, the leaf of
+//     G11 - L10 L10^T and its inverse, Li10 = -Li11 L10 Li00; it writes
+//     Li = L^{-1} (r x r row-major, zeros above the diagonal).
+//   k_apply: V = Z Li^T, 64 rows per workgroup.
+// A relative jitter of 1e-15 max diag(G) on the diagonal keeps a (nearly)
+// rank-deficient G factorable; a pivot that still fails is replaced by 1, so
+// the result stays finite (the second pass re-orthonormalises).
+constexpr int kGramParts = 8;  // at most this many row chunks per Gram
+
+// ZTb[c][t] = Z[i0 + t][64 b + c] for t < 64, zeros past n and r
+__device__ __forceinline__ void load_zt(const double* __restrict__ Z, int n, int r, int i0, double (*ZT0)[LDP],
+                                        double (*ZT1)[LDP]) {
   const int tid = threadIdx.x;
-  double dmax = 0.0;
-  for (int i = 0; i < r; ++i) dmax = fmax(dmax, G[i * r + i]);
-  for (int e = tid; e < r * r; e += 256) {
-    const int i = e / r, j = e % r;
-    Ls[e] = (j <= i) ? G[e] + (i == j ? 1e-15 * dmax : 0.0) : 0.0;
+  const int rc = r > NB ? 2 * NB : NB;  // columns staged
+  double v[32];
+#pragma unroll
+  for (int q = 0; q < 32; ++q) {
+    const int e = tid + 256 * q, t = e / rc, c = e % rc;
+    v[q] = (e < NB * rc && i0 + t < n && c < r) ? Z[(size_t)(i0 + t) * r + c] : 0.0;
   }
-  __syncthreads();
-  for (int j = 0; j < r; ++j) {
-    const double d = Ls[j * r + j];
-    const double sd = sqrt(d > 0.0 ? d : 1e-300);
-    __syncthreads();
-    if (tid == 0) Ls[j * r + j] = sd;
-    for (int i = j + 1 + tid; i < r; i += 256) Ls[i * r + j] /= sd;
-    __syncthreads();
-    const int w = r - j - 1;
-    for (int e = tid; e < w * w; e += 256) {
-      const int i = j + 1 + e / w, k = j + 1 + e % w;
-      if (k <= i) Ls[i * r + k] -= Ls[i * r + j] * Ls[k * r + j];
-    }
-    __syncthreads();
-  }
-  for (int j = tid; j < r; j += 256) {
-    for (int i = 0; i < j; ++i) Linv[i * r + j] = 0.0;
-    Linv[j * r + j] = 1.0 / Ls[j * r + j];
-    for (int i = j + 1; i < r; ++i) {
-      double s = 0.0;
-      for (int t = j; t < i; ++t) s += Ls[i * r + t] * Linv[t * r + j];
-      Linv[i * r + j] = -s / Ls[i * r + i];
+#pragma unroll
+  for (int q = 0; q < 32; ++q) {
+    const int e = tid + 256 * q, t = e / rc, c = e % rc;
+    if (e < NB * rc) {
+      if (c < NB) ZT0[c][t] = v[q];
+      else ZT1[c - NB][t] = v[q];
     }
   }
 }
 
-// lam = lam_abs + lam_rel * mean(diag H); clears the slot's flags.
+__global__ __launch_bounds__(256) void k_gram_chol(const double* __restrict__ Z, int n, int r, int rows_per,
+                                                   double* __restrict__ Gp, double* __restrict__ Li,
+                                                   unsigned* __restrict__ counter) {
+  __shared__ __attribute__((aligned(16))) double LT[NB][LDP];   // Z^T chunk (cols 0-63), then leaf workspace
+  __shared__ __attribute__((aligned(16))) double L10[NB][LDP];  // Z^T chunk (cols 64-127), then G10 / L10
+  __shared__ __attribute__((aligned(16))) double Y0[NB][LDP];
+  __shared__ __attribute__((aligned(16))) double Y1[NB][LDP];   // G11 until its leaf, then Li11
+  __shared__ double Tm[32][33];
+  __shared__ double lb[2 * NB];
+  __shared__ double dv[NB];
+  __shared__ double jit;
+  __shared__ int flag, last;
+  const int tid = threadIdx.x, nz = gridDim.x, z = blockIdx.x;
+  const bool two = r > NB;
+  const int nblk = two ? 3 : 1;
+  {
+    f64x4 g00[2][2], g10[2][2], g11[2][2];
+    blk_zero(g00);
+    blk_zero(g10);
+    blk_zero(g11);
+    const int ie = min(n, (z + 1) * rows_per);
+    for (int i0 = z * rows_per; i0 < ie; i0 += NB) {
+      load_zt(Z, n, r, i0, LT, L10);
+      __syncthreads();
+      blk_mma<true>(g00, LT, LT);
+      if (two) {
+        blk_mma<true>(g10, L10, LT);
+        blk_mma<true>(g11, L10, L10);
+      }
+      __syncthreads();
+    }
+    double* P = Gp + (size_t)z * 3 * NB * NB;
+    blk_each([&](int mi, int ni, int q, int rr, int c) {
+      P[rr * NB + c] = g00[mi][ni][q];
+      if (two) {
+        P[NB * NB + rr * NB + c] = g10[mi][ni][q];
+        P[2 * NB * NB + rr * NB + c] = g11[mi][ni][q];
+      }
+    });
+  }
+  // the last workgroup to finish reduces and factors
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(counter, 1u) == (unsigned)(nz - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  const int m0 = min(r, NB), m1 = r - m0;
+  for (int b = 0; b < nblk; ++b) {
+    double s[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s[q] = 0.0;
+    for (int zz = 0; zz < nz; ++zz) {
+      const double* P = Gp + ((size_t)zz * 3 + b) * NB * NB;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) s[q] += P[tid + 256 * q];
+    }
+    double (*D)[LDP] = b == 0 ? LT : b == 1 ? L10 : Y1;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;
+      D[e >> 6][e & 63] = s[q];
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    double d = tid < m0 ? LT[tid][tid] : 0.0;
+    if (tid < m1) d = fmax(d, Y1[tid][tid]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) d = fmax(d, __shfl_xor(d, o));
+    if (tid == 0) jit = 1e-15 * d;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    LT[tid][tid] = tid < m0 ? LT[tid][tid] + jit : 1.0;
+    if (two) Y1[tid][tid] += jit;
+  }
+  __syncthreads();
+  chol64_blocked(LT, dv, lb, &flag);  // a failed pivot is replaced by 1
+  inv64_waves(LT, dv, Y0, Tm);
+  f64x4 acc[2][2];
+  if (two) {
+    // L10 = G10 Li00^T
+    blk_zero(acc);
+    blk_mma<true>(acc, L10, Y0);
+    __syncthreads();
+    blk_each([&](int mi, int ni, int q, int rr, int c) { L10[rr][c] = acc[mi][ni][q]; });
+    f64x4 d1[2][2];
+    blk_each([&](int mi, int ni, int q, int rr, int c) { d1[mi][ni][q] = Y1[rr][c]; });
+    __syncthreads();
+    // G11 - L10 L10^T, padded with the identity past m1
+    blk_neg(d1);
+    blk_mma<true>(d1, L10, L10);
+    blk_neg(d1);
+    blk_each([&](int mi, int ni, int q, int rr, int c) {
+      LT[rr][c] = (rr < m1 && c < m1) ? d1[mi][ni][q] : ((rr == c) ? 1.0 : 0.0);
+    });
+    __syncthreads();
+    chol64_blocked(LT, dv, lb, &flag);
+    inv64_waves(LT, dv, Y1, Tm);
+    // Li10 = -Li11 (L10 Li00)
+    blk_zero(acc);
+    blk_mma<false>(acc, L10, Y0);
+    blk_each([&](int mi, int ni, int q, int rr, int c) { LT[rr][c] = acc[mi][ni][q]; });
+    __syncthreads();
+    blk_zero(acc);
+    blk_mma<false>(acc, Y1, LT);
+    blk_each([&](int mi, int ni, int q, int rr, int c) {
+      if (rr < m1) {
+        Li[(size_t)(NB + rr) * r + c] = -acc[mi][ni][q];
+        if (c < m1) Li[(size_t)(NB + rr) * r + NB + c] = Y1[rr][c];
+      }
+    });
+  }
+  blk_each([&](int mi, int ni, int q, int rr, int c) {
+    if (rr < m0 && c < m0) Li[(size_t)rr * r + c] = Y0[rr][c];
+    if (rr < m0 && c < m1) Li[(size_t)rr * r + NB + c] = 0.0;
+  });
+  if (tid == 0) *counter = 0u;  // ready for the next launch
+}
+
+// V[i][c] = sum_t Z[i][t] Li[c][t] (V = Z Li^T), rows [64 blockIdx.x, +64)
+__global__ __launch_bounds__(256) void k_apply(const double* __restrict__ Z, int n, int r,
+                                               const double* __restrict__ Li, double* __restrict__ V) {
+  __shared__ __attribute__((aligned(16))) double Zs0[NB][LDP];
+  __shared__ __attribute__((aligned(16))) double Zs1[NB][LDP];
+  __shared__ __attribute__((aligned(16))) double Lb0[NB][LDP];
+  __shared__ __attribute__((aligned(16))) double Lb1[NB][LDP];
+  const int tid = threadIdx.x, i0 = NB * blockIdx.x;
+  const bool two = r > NB;
+  auto load = [&](double (*D)[LDP], const double* S, int ld, int r0, int c0, int rmax, int cmax) {
+    double v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q, rr = e >> 6, c = e & 63;
+      v[q] = (r0 + rr < rmax && c0 + c < cmax) ? S[(size_t)(r0 + rr) * ld + c0 + c] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;
+      D[e >> 6][e & 63] = v[q];
+    }
+  };
+  load(Zs0, Z, r, i0, 0, n, r);
+  load(Lb0, Li, r, 0, 0, r, r);
+  if (two) {
+    load(Zs1, Z, r, i0, NB, n, r);
+    load(Lb1, Li, r, NB, 0, r, r);
+  }
+  __syncthreads();
+  f64x4 acc0[2][2], acc1[2][2];
+  blk_zero(acc0);
+  blk_mma<true>(acc0, Zs0, Lb0);
+  if (two) {
+    blk_zero(acc1);
+    blk_mma<true>(acc1, Zs0, Lb1);
+    __syncthreads();
+    load(Lb0, Li, r, NB, NB, r, r);
+    __syncthreads();
+    blk_mma<true>(acc1, Zs1, Lb0);
+  }
+  blk_each([&](int mi, int ni, int q, int rr, int c) {
+    if (i0 + rr < n) {
+      if (c < r) V[(size_t)(i0 + rr) * r + c] = acc0[mi][ni][q];
+      if (two && NB + c < r) V[(size_t)(i0 + rr) * r + NB + c] = acc1[mi][ni][q];
+    }
+  });
+}
+
+// lam = lam_abs + lam_rel * mean(diag H); clears the slot's flags and the
+// Gram kernels' arrival counter.
 __global__ __launch_bounds__(256) void k_lora_lambda(const double* __restrict__ H, int n, double lam_abs,
-                                                     double lam_rel, Slot* __restrict__ slot) {
+                                                     double lam_rel, Slot* __restrict__ slot,
+                                                     unsigned* __restrict__ counter) {
   __shared__ double red[256];
   double s = 0.0;
   for (int i = threadIdx.x; i < n; i += 256) s += H[(size_t)i * n + i];
@@ -189,6 +359,7 @@ __global__ __launch_bounds__(256) void k_lora_lambda(const double* __restrict__ 
     slot->lam = lam_abs + lam_rel * red[0] / (double)n;
     slot->info = 0;
     slot->nonfinite = 0;
+    *counter = 0u;
   }
 }
 
@@ -228,17 +399,22 @@ __global__ void k_lora_extract(const double* __restrict__ V, const float* __rest
 
 inline int cdivl(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-hipError_t dgemm(hipStream_t st, const DGemm& g0, double* C, double* scratch) {
+// C = the product; split-K partials go to scratch and are summed by k_dsum
+int dgemm(hipStream_t st, const LoraHooks& hk, const DGemm& g0, double* C, double* scratch) {
   DGemm g = g0;
   const int tiles = cdivl(g.M, 64) * cdivl(g.N, 64);
   if (g.ksplit < 1) g.ksplit = 1;
   g.P = (g.ksplit == 1) ? C : scratch;
-  hipLaunchKernelGGL(k_dgemm, dim3(tiles, g.ksplit), dim3(256), 0, st, g);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || g.ksplit == 1) return e;
+  int rc = hk.launch("k_dgemm", [&] {
+    hipLaunchKernelGGL(k_dgemm, dim3(tiles, g.ksplit), dim3(256), 0, st, g);
+    return hipGetLastError();
+  });
+  if (rc || g.ksplit == 1) return rc;
   const long long MN = (long long)g.M * g.N;
-  hipLaunchKernelGGL(k_dsum, dim3(cdivl(MN, 256)), dim3(256), 0, st, (const double*)scratch, C, MN, g.ksplit);
-  return hipGetLastError();
+  return hk.launch("k_dsum", [&] {
+    hipLaunchKernelGGL(k_dsum, dim3(cdivl(MN, 256)), dim3(256), 0, st, (const double*)scratch, C, MN, g.ksplit);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace
@@ -254,18 +430,23 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
     return o;
   };
   const int ks_n = std::max(1, std::min(16, n / 256));   // split-K for K = n products
+  // Gram row chunks: at most kGramParts workgroups, whole 64-row blocks each
+  const int nrb = cdivl(n, 64), rows_per = 64 * cdivl(nrb, std::min(kGramParts, nrb));
+  const int nparts = cdivl(n, rows_per);
   const size_t oH64 = take((size_t)n * n * 8), oV = take((size_t)n * r * 8),
-               oZ = take((size_t)n * r * 8), oG = take((size_t)r * r * 8), oLi = take((size_t)r * r * 8),
+               oZ = take((size_t)n * r * 8), oLi = take((size_t)r * r * 8),
                oM = take((size_t)r * r * 8), oHV = take((size_t)n * r * 8),
-               oS = take((size_t)std::max(ks_n * n * r, ks_n * r * r) * 8), oA = take((size_t)nt * nt * 8),
-               oU = take((size_t)nt * nt * 4), oW = take((size_t)out * nt * 4);
+               oS = take((size_t)std::max(ks_n * n * r, ks_n * r * r) * 8),
+               oGp = take((size_t)kGramParts * 3 * 64 * 64 * 8), oCnt = take(sizeof(unsigned)),
+               oA = take((size_t)nt * nt * 8), oU = take((size_t)nt * nt * 4), oW = take((size_t)out * nt * 4);
   uint8_t* base = (uint8_t*)hk.ensure(off);
   if (!base) return GPTQ_ERR_NO_MEMORY;
   Slot* slot = (Slot*)hk.slots(sizeof(Slot));
   if (!slot) return GPTQ_ERR_NO_MEMORY;
   double *H64 = (double*)(base + oH64), *V = (double*)(base + oV), *Z = (double*)(base + oZ),
-         *G = (double*)(base + oG), *Li = (double*)(base + oLi), *M = (double*)(base + oM),
-         *HV = (double*)(base + oHV), *S = (double*)(base + oS), *A = (double*)(base + oA);
+         *Li = (double*)(base + oLi), *M = (double*)(base + oM), *HV = (double*)(base + oHV),
+         *S = (double*)(base + oS), *Gp = (double*)(base + oGp), *A = (double*)(base + oA);
+  unsigned* cnt = (unsigned*)(base + oCnt);
   float* U = (float*)(base + oU);
   float* Ww = (float*)(base + oW);
 
@@ -273,50 +454,42 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
   // top-r eigen-directions of H against a damping far below their size
   int rc = hk.hessian64(io.X, io.tokens, io.ldx, n, H64);
   if (rc) return rc;
-  hipError_t e;
-#define LCHK(x)                                                        \
-  do {                                                                 \
-    e = (x);                                                           \
-    if (e != hipSuccess) return hk.set_err(GPTQ_ERR_HIP, hipGetErrorString(e)); \
+#define LLAUNCH(name, ...)                                                                  \
+  do {                                                                                      \
+    if ((rc = hk.launch(name, [&] { hipLaunchKernelGGL(__VA_ARGS__); return hipGetLastError(); }))) \
+      return rc;                                                                            \
   } while (0)
-  hipLaunchKernelGGL(k_lora_lambda, dim3(1), dim3(256), 0, st, (const double*)H64, n, io.lam_abs, io.lam_rel, slot);
-  LCHK(hipGetLastError());
-  hipLaunchKernelGGL(k_start_block, dim3(cdivl((long long)n * r, 256)), dim3(256), 0, st, V, n, r);
-  LCHK(hipGetLastError());
-  auto orth = [&](const double* Zin, double* Vout) -> hipError_t {
-    // G = Z^T Z ; Z L^{-T} -> Vout
-    DGemm g{Zin, 1, r, Zin, r, 1, nullptr, r, r, n, ks_n};
-    hipError_t e2 = dgemm(st, g, G, S);
-    if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL(k_chol_inv_small, dim3(1), dim3(256), 0, st, (const double*)G, Li, r);
-    if ((e2 = hipGetLastError()) != hipSuccess) return e2;
-    DGemm h{Zin, r, 1, Li, 1, r, nullptr, n, r, r, 1};
-    return dgemm(st, h, Vout, S);
+  LLAUNCH("k_lora_lambda", k_lora_lambda, dim3(1), dim3(256), 0, st, (const double*)H64, n, io.lam_abs, io.lam_rel,
+          slot, cnt);
+  LLAUNCH("k_start_block", k_start_block, dim3(cdivl((long long)n * r, 256)), dim3(256), 0, st, V, n, r);
+  // one Cholesky-QR pass: Vout = Zin L^{-T}, Zin^T Zin = L L^T
+  auto orth = [&](const double* Zin, double* Vout) -> int {
+    LLAUNCH("k_gram_chol", k_gram_chol, dim3(nparts), dim3(256), 0, st, Zin, n, r, rows_per, Gp, Li, cnt);
+    LLAUNCH("k_apply", k_apply, dim3(nrb), dim3(256), 0, st, Zin, n, r, (const double*)Li, Vout);
+    return 0;
   };
   for (int it = 0; it < kIters; ++it) {
     DGemm g{H64, n, 1, V, r, 1, nullptr, n, r, n, ks_n};  // Z = H V
-    LCHK(dgemm(st, g, Z, S));
-    LCHK(orth(Z, V));  // Cholesky-QR, twice
-    LCHK(orth(V, Z));
+    if ((rc = dgemm(st, hk, g, Z, S))) return rc;
+    if ((rc = orth(Z, V))) return rc;  // Cholesky-QR, twice
+    if ((rc = orth(V, Z))) return rc;
     std::swap(V, Z);
   }
   {
     DGemm g{H64, n, 1, V, r, 1, nullptr, n, r, n, ks_n};  // HV = H V
-    LCHK(dgemm(st, g, HV, S));
+    if ((rc = dgemm(st, hk, g, HV, S))) return rc;
     DGemm m{V, 1, r, HV, r, 1, nullptr, r, r, n, ks_n};  // M = V^T H V
-    LCHK(dgemm(st, m, M, S));
+    if ((rc = dgemm(st, hk, m, M, S))) return rc;
   }
-  hipLaunchKernelGGL(k_lora_assemble, dim3(cdivl(nt, 4)), dim3(256), 0, st, (const double*)H64, (const double*)HV,
-                     (const double*)M, n, r, A, slot);
-  LCHK(hipGetLastError());
+  LLAUNCH("k_lora_assemble", k_lora_assemble, dim3(cdivl(nt, 4)), dim3(256), 0, st, (const double*)H64,
+          (const double*)HV, (const double*)M, n, r, A, slot);
   if ((rc = hk.factor(A, nt, U, slot))) return rc;
   QuantJob J{io.W, out, n, nt, U, io.bits, io.group, io.block, io.codes, io.scales, io.zeros, nullptr,
              &slot->lam, slot->obj, Ww};
   if ((rc = hk.quantize(J))) return rc;
-  const long long cnt = std::max((long long)n * r, (long long)r * out);
-  hipLaunchKernelGGL(k_lora_extract, dim3(cdivl(cnt, 256)), dim3(256), 0, st, (const double*)V, (const float*)Ww,
-                     out, n, r, io.L, io.R);
-  LCHK(hipGetLastError());
-#undef LCHK
+  const long long ne = std::max((long long)n * r, (long long)r * out);
+  LLAUNCH("k_lora_extract", k_lora_extract, dim3(cdivl(ne, 256)), dim3(256), 0, st, (const double*)V,
+          (const float*)Ww, out, n, r, io.L, io.R);
+#undef LLAUNCH
   return 0;
 }

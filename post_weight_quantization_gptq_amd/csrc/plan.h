@@ -49,6 +49,9 @@ struct LoraHooks {
   std::function<int(double*, int, float*, Slot*)> factor;  // factor an assembled A
   std::function<int(const QuantJob&)> quantize;
   std::function<int(int, const char*)> set_err;
+  // issue one launch (the function) on the context's stream under the given
+  // kernel name (a string literal), timed when timing is on
+  std::function<int(const char*, const std::function<hipError_t()>&)> launch;
 };
 
 int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hooks);

@@ -218,8 +218,17 @@ def test_layer_repeatable_bitwise(ctx):
 
 
 # ------------------------------------------------------------------- LoRA ---
-def test_lora_matches_oracle(ctx):
-    spec = synth.SMALL["lora"][0]
+LORA_SPECS = [synth.SMALL["lora"][0],
+              # two 64-blocks in the Gram factorization (the second partial),
+              # ragged last row block (400 = 6 * 64 + 16)
+              synth.LayerSpec("lora96", 160, 400, 8192, 3, 0, 128, 1e-4, kind="lowrank", rank=96, seed=5),
+              # rank at the limit, two full 64-blocks
+              synth.LayerSpec("lora128", 96, 640, 8192, 3, 0, 128, 1e-4, kind="lowrank", rank=128, seed=6)]
+
+
+@pytest.mark.parametrize("spec", LORA_SPECS, ids=lambda s: s.name)
+def test_lora_matches_oracle(ctx, spec):
+    print("lora", spec.name, spec.n, spec.rank, flush=True)
     lay = synth.layer(spec)
     res = ctx.lora(lay["W"].cuda(), lay["X"].cuda(), spec.rank, spec.bits, spec.group, spec.block,
                    lam_rel=spec.lam_rel)
