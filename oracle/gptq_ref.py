@@ -29,7 +29,10 @@ W - What = E U and sum(E^2) = tr(D H_lam D^T); blocked == unblocked; GPTQ codes
 force over all 2-bit code vectors for n <= 8; the nearest-plane error bound;
 hand-worked fixtures in tests/golden/; for the LoRA variant the Schur-complement
 and ridge (optimal low-rank compensation) closed forms, r = 0 reduction and
-basis invariance.
+basis invariance; for the refinement loop (tests/test_oracle_refine.py) the
+truncated SVD at H = I, a matrix-square-root route to the same OLrC optimum,
+brute force over the grid for every Bid-Up coordinate decision, the decoupled
+(diagonal H) case reducing to round-to-nearest, and a non-increasing trace.
 
 Parity unpinned (conventions that only self-consistency fixes; the GPU follows
 them exactly): the min-max grid details of ``grid_fit`` (0 inside the range,
@@ -506,3 +509,122 @@ def lora_schur(W, H, V, lam: float, bits: int, group: int = 0, block: int | None
     Rt = np.linalg.solve(K, HV.T @ D1.T)
     res.update(R_out=Rt.T, S=S, U=U)
     return res
+
+
+# --------------------------------------------------------------------------
+# refinement after the intrinsic LoRA: OLrC <-> Bid-Up
+# --------------------------------------------------------------------------
+def olrc(W, What, H, r: int) -> dict:
+    """Optimal low-rank compensation for a fixed Q ([LoRA] section 4, OLrC).
+
+    Minimises J(C) = tr((E - C) H (E - C)^T), E = W - What, over rank(C) <= r
+    (the layer objective with What + C in place of What).  With any H = F F^T,
+    J = ||(E - C) F||_F^2, so by Eckart-Young the best C F is the rank-r
+    truncation of E F, P_r P_r^T E F with P_r the top-r left singular vectors
+    of E F, i.e. the top-r eigenvectors of E H E^T; hence C = P_r P_r^T E
+    (no square root or inverse of H is needed, and a singular H is fine).
+    Factors: R_out = P_r [out, r] and L = E^T P_r [n, r], C = R_out L^T
+    (the pages' W^T ~ Q + L R with R = R_out^T).  J = tr((E - C) H (E - C)^T).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    E = W - np.asarray(What, dtype=np.float64)
+    M = E @ H @ E.T
+    lam_, P = np.linalg.eigh(M)
+    P = P[:, np.argsort(lam_)[::-1][:r]]
+    L = E.T @ P
+    C = P @ L.T
+    D = E - C
+    return dict(R_out=P, L=L, C=C, J=float(np.sum((D @ H) * D)), eig=np.sort(lam_)[::-1])
+
+
+def bid_up(W, C, codes, scales, zeros, H, bits: int, group: int = 0,
+           replay=None, tie_window: float = 1e-3) -> dict:
+    """One Bid-Up pass: coordinate moves of Q on its fixed grid for fixed L, R.
+
+    [LoRA] section 4, Bid-Up: with the low-rank part C = R_out L^T fixed and
+    the grid (scales, zeros) fixed, each row's objective
+    J_i(q) = d H d^T, d = w - c - what(q), is lowered one coordinate at a
+    time.  Along coordinate j, J_i is a parabola in what_j with its vertex at
+    t = what_j + g_j / H_jj, g = d H (the gradient is -2 g), so the best grid
+    value is the one nearest t: q* = clamp(rne(x)), x = fl32(fl32(t r) + z)
+    (the sweep's rounding, in float32); the code moves to q* only when that
+    strictly lowers J_i, |x - q*| < |x - q_j|, and the move delta = what(q*)
+    - what(q_j) changes d_j by -delta and g by -delta H_j:.  Coordinates are
+    visited once, j = 0..n-1 (plain reading: one cyclic pass per Bid-Up step).
+
+    ``replay``: codes from another implementation of the same pass; where x
+    is within tie_window of the midpoint between its choice and ours (the
+    choices differ by one level), its choice is taken.  Returns the new codes,
+    What, the per-move objective changes and J before and after.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    H = np.asarray(H, dtype=np.float64)
+    out, n = W.shape
+    maxq = (1 << bits) - 1
+    codes = np.array(codes, dtype=np.uint8, copy=True)
+    What = dequantize(codes, scales, zeros, group)
+    g = (W - np.asarray(C, dtype=np.float64) - What) @ H
+    J0 = float(np.sum(g * (W - C - What)))
+    gs = group if group else n
+    dJ = np.zeros(out)
+    moves = 0
+    forced = 0
+    for j in range(n):
+        s = np.asarray(scales, dtype=F32)[:, j // gs]
+        z = np.asarray(zeros, dtype=F32)[:, j // gs]
+        rr = (F32(1) / s).astype(F32)
+        qo = codes[:, j].astype(F32)
+        ho = What[:, j]
+        t = (ho + g[:, j] / H[j, j]).astype(F32)
+        x = ((t * rr).astype(F32) + z).astype(F32)
+        qs = np.clip(np.rint(x), F32(0), F32(maxq)).astype(F32)
+        mv = np.abs(x - qs) < np.abs(x - qo)
+        qn = np.where(mv, qs, qo).astype(F32)
+        if replay is not None:
+            qr = np.asarray(replay)[:, j].astype(F32)
+            mid = F32(0.5) * (qr + qn)
+            take = (qr != qn) & (np.abs(qr - qn) == 1) & (np.abs(x.astype(np.float64) - mid) < tie_window)
+            forced += int(take.sum())
+            qn = np.where(take, qr, qn).astype(F32)
+        hn = (s * (qn - z)).astype(F32).astype(np.float64)
+        delta = hn - ho
+        moves += int(np.count_nonzero(delta))
+        dJ += delta * (delta * H[j, j] - 2.0 * g[:, j])
+        codes[:, j] = qn.astype(np.uint8)
+        What[:, j] = hn
+        g -= np.outer(delta, H[j])
+    D = W - C - What
+    return dict(codes=codes, What=What, dJ=dJ, J0=J0, J=float(np.sum((D @ H) * D)),
+                moves=moves, forced=forced)
+
+
+def lora_refine(W, H, r: int, bits: int, group: int = 0, block: int | None = 128,
+                lam_rel: float = 1e-4, lam_abs: float = 0.0, rounds: int = 1,
+                replay: list | None = None) -> dict:
+    """Intrinsic LoRA, then ``rounds`` of OLrC followed by Bid-Up, then a last
+    OLrC so that L, R are optimal for the final Q ([LoRA] section 4: the two
+    steps alternate; each minimises the objective over its own variables, so
+    the objective never increases).  trace = [J after the sweep, then J after
+    every step] (2 rounds + 2 values).  ``replay[t]``: codes of another
+    implementation after Bid-Up pass t.
+    """
+    res = lora(W, H, r, bits, group, block, lam_rel=lam_rel, lam_abs=lam_abs)
+    codes, What = res["codes"], res["What"]
+    trace = [res["J"]]
+    steps = []
+    for t in range(rounds):
+        oc = olrc(W, What, H, r)
+        trace.append(oc["J"])
+        bu = bid_up(W, oc["C"], codes, res["scales"], res["zeros"], H, bits, group,
+                    replay=None if replay is None else replay[t])
+        codes, What = bu["codes"], bu["What"]
+        trace.append(bu["J"])
+        steps.append(dict(olrc=oc, bid_up=bu))
+    if rounds:
+        oc = olrc(W, What, H, r)
+        trace.append(oc["J"])
+        L, R_out = oc["L"], oc["R_out"]
+    else:
+        L, R_out = res["L"], res["R_out"]
+    return dict(codes=codes, scales=res["scales"], zeros=res["zeros"], What=What, L=L,
+                R=R_out.T.copy(), R_out=R_out, trace=trace, steps=steps, sweep=res)
