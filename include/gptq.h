@@ -136,6 +136,56 @@ int gptq_lora(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const uint16
               int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
               uint8_t* zeros, float* L, float* R, double* obj, int32_t* info);
 
+/* Gram matrix accurate to float64 rounding, H = X^T X in fp64 (the products
+ * of bf16 values are exact in fp64 and the sums run in fp64 on fp64 MFMA).  X
+ * as gptq_hessian; H[n][n] fp64, device, caller-owned, fully written.  The
+ * Hessian the refinement steps below take.  ASYNC on the context's stream. */
+int gptq_hessian64(gptq_ctx ctx, const uint16_t* X, int64_t tokens, int32_t n, int64_t ldx, double* H);
+
+/* Refinement after the intrinsic LoRA (GPTQ-intrinsic LoRA technical summary,
+ * section 4, Bid-Up refinement: OLrC fits L, R for a fixed Q, Bid-Up moves Q
+ * on its fixed grid for fixed L, R, the two alternate and the layer objective
+ * never increases).  Objective: J = tr(D H D^T), D = W - What - R^T L^T,
+ * What = s (q - z) per group (fp32 as stored), H from gptq_hessian64.
+ *
+ * gptq_olrc: for the given codes, the rank-r correction C minimising J is
+ * C = P P^T E with E = W - What and P the top-r eigenvectors of E H E^T
+ * (found by subspace iteration in fp64, Cholesky-QR twice per step; where
+ * the r-th and (r+1)-th eigenvalues are close, any near-optimal subspace may
+ * come out).  Writes L[n][r] = E^T P and R[r][out] = P^T (fp32, device) and
+ * J (host, the objective with that correction).  codes/scales/zeros as
+ * gptq_quantize's outputs (read only); bits is checked only.
+ *
+ * gptq_bid_up: one pass over the columns j = 0..n-1 of every row: with
+ * g = D H (gradient of the row objective up to the factor -2), the code
+ * moves to q* = clamp(rne(x)), x = fl32(fl32(t / s) + z) (t / s as
+ * t * fl32(1/s)), t = fl32(what_j + g_j / H_jj), only when that is strictly
+ * nearer, |x - q*| < |x - q_j|; the move updates g for the later columns.
+ * codes [out][n] are read and rewritten in place (device); L, R as written by
+ * gptq_olrc; J (host) = the objective after the pass (its value before plus
+ * the summed change of the moves).  The moves run on fp32 with the sweep's
+ * lazy block updates (block as gptq_quantize).
+ *
+ * Both: W[out][n] fp32 and H[n][n] fp64 device; 1 <= r <= min(128, out, n);
+ * requirements on bits/group/block as gptq_quantize.  SYNC. */
+int gptq_olrc(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const double* H, int32_t r,
+              int32_t bits, int32_t group, const uint8_t* codes, const float* scales,
+              const uint8_t* zeros, float* L, float* R, double* J);
+int gptq_bid_up(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const double* H, int32_t r,
+                const float* L, const float* R, int32_t bits, int32_t group, int32_t block,
+                uint8_t* codes, const float* scales, const uint8_t* zeros, double* J);
+
+/* gptq_lora followed by `rounds` >= 1 rounds of gptq_olrc then gptq_bid_up,
+ * and a last gptq_olrc, all on the fp64 Hessian the LoRA computes (shared,
+ * not recomputed).  Outputs codes/scales/zeros (the grid stays the sweep's),
+ * L, R from the last OLrC, and trace[2 rounds + 2] (host): J after the
+ * sweep, then after every step (non-increasing up to rounding).  Arguments
+ * otherwise as gptq_lora (also r <= out).  SYNC. */
+int gptq_lora_refine(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const uint16_t* X,
+                     int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,
+                     int32_t block, double lam_abs, double lam_rel, int32_t rounds, uint8_t* codes,
+                     float* scales, uint8_t* zeros, float* L, float* R, double* trace, int32_t* info);
+
 /* One layer of a batch.  X may be NULL: then H must already hold the layer's
  * Hessian (several layers may point at the same H and X == NULL to share it).
  * H and U are caller-provided [n][n] fp32 buffers (H is written when X != NULL).
@@ -173,8 +223,12 @@ int gptq_quantize_batched(gptq_ctx ctx, int32_t nlayers, gptq_layer* layers);
  * is a comma-separated list of kernel names (e.g. "k_syrk,k_sweep"), "*" for
  * every kernel the context launches, or NULL to stop recording (totals are
  * kept until the next gptq_timing call).  Kernel names: k_xpose, k_syrk,
- * k_syrk_reduce, k_damp_lambda, k_damp_fill, k_chol_panel, k_gemm64, k_make_u,
- * k_init_work, k_rowfit, k_sweep, k_trail, k_objective.  gptq_kernel_time
+ * k_syrk_reduce, k_syrk64, k_syrk64_reduce, k_damp_lambda, k_damp_fill,
+ * k_chol_panel, k_chol_panel2, k_gemm64, k_gemm_ring64, k_gemm_ring128,
+ * k_make_u, k_init_work, k_rowfit, k_sweep, k_trail, k_objective, and for the
+ * LoRA and refinement paths k_lora_lambda, k_start_block, k_dgemm, k_dsum,
+ * k_gram_chol, k_apply, k_lora_assemble, k_lora_extract, k_ref_init, k_resid,
+ * k_gfinal, k_sum_parts, k_f32_to_f64, k_f64_to_f32, k_olrc_out.  gptq_kernel_time
  * waits for the recorded events and returns the summed elapsed milliseconds
  * and the number of timed launches of kernel `name` (0 and 0 if none).  Each
  * timed launch costs two event records on the stream. */

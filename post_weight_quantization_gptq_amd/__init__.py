@@ -95,11 +95,18 @@ def load_library(path: str | None = None):
                                 ctypes.POINTER(d)]
     L.gptq_lora.argtypes = [vp, vp, i32, i32, vp, i64, i64, i32, i32, i32, i32, d, d,
                             vp, vp, vp, vp, vp, ctypes.POINTER(d), ctypes.POINTER(i32)]
+    L.gptq_lora_refine.argtypes = [vp, vp, i32, i32, vp, i64, i64, i32, i32, i32, i32, d, d, i32,
+                                   vp, vp, vp, vp, vp, ctypes.POINTER(d), ctypes.POINTER(i32)]
+    L.gptq_hessian64.argtypes = [vp, vp, i64, i32, i64, vp]
+    L.gptq_olrc.argtypes = [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(d)]
+    L.gptq_bid_up.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp,
+                              ctypes.POINTER(d)]
     L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
     L.gptq_timing.argtypes = [vp, ctypes.c_char_p]
     L.gptq_kernel_time.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(d), ctypes.POINTER(i64)]
     for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
-                 "gptq_lora", "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
+                 "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up",
+                 "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
         getattr(L, name).restype = ctypes.c_int
     if path is None:
         _lib = L
@@ -112,7 +119,7 @@ def exported_symbols(header: str | None = None):
     header = header or os.path.join(os.path.dirname(_HERE), "include", "gptq.h")
     txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(gptq_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(gptq_[a-z0-9_]+)\s*\(", txt)))
 
 
 def _ptr(t):
@@ -269,6 +276,76 @@ class Context:
                                        _ptr(res["L"]), _ptr(res["R"]), obj, ctypes.byref(info)))
         res["J"], res["J_lam"], res["info"] = obj[0], obj[1], info.value
         return res
+
+    def lora_refine(self, W, X, r: int, bits: int, group: int, block: int, rounds: int = 1,
+                    lam_abs: float = 0.0, lam_rel: float = 1e-4):
+        """Intrinsic LoRA, then `rounds` of OLrC + Bid-Up and a last OLrC.
+        Returns dict(codes, scales, zeros, L [n, r], R [r, out], trace [2 rounds + 2])."""
+        torch = self.torch
+        self._dev(W, torch.float32, "W")
+        X = self._xbits(X)
+        o, n = W.shape
+        ng = n // group if group else 1
+        res = dict(codes=torch.empty((o, n), dtype=torch.uint8, device=self.device),
+                   scales=torch.empty((o, ng), dtype=torch.float32, device=self.device),
+                   zeros=torch.empty((o, ng), dtype=torch.uint8, device=self.device),
+                   L=torch.empty((n, r), dtype=torch.float32, device=self.device),
+                   R=torch.empty((r, o), dtype=torch.float32, device=self.device))
+        tr = (ctypes.c_double * (2 * int(rounds) + 2))()
+        info = ctypes.c_int32(0)
+        self._check(self.lib.gptq_lora_refine(self.handle, _ptr(W), o, n, _ptr(X), X.shape[0], X.stride(0), int(r),
+                                              int(bits), int(group), int(block), float(lam_abs), float(lam_rel),
+                                              int(rounds), _ptr(res["codes"]), _ptr(res["scales"]),
+                                              _ptr(res["zeros"]), _ptr(res["L"]), _ptr(res["R"]), tr,
+                                              ctypes.byref(info)))
+        res["trace"], res["info"] = list(tr), info.value
+        return res
+
+    def hessian64(self, X, n: int | None = None, H=None):
+        """H = X^T X accurate to fp64 rounding (fp64 [n, n])."""
+        torch = self.torch
+        X = self._xbits(X)
+        n = X.shape[1] if n is None else int(n)
+        if H is None:
+            H = torch.empty((n, n), dtype=torch.float64, device=self.device)
+        self._dev(H, torch.float64, "H")
+        self._check(self.lib.gptq_hessian64(self.handle, _ptr(X), X.shape[0], n, X.stride(0), _ptr(H)))
+        return H
+
+    def olrc(self, W, H, r: int, bits: int, group: int, codes, scales, zeros):
+        """Optimal rank-r compensation for fixed codes.  Returns dict(L [n, r], R [r, out], J)."""
+        torch = self.torch
+        self._dev(W, torch.float32, "W")
+        self._dev(H, torch.float64, "H")
+        self._dev(codes, torch.uint8, "codes")
+        self._dev(scales, torch.float32, "scales")
+        self._dev(zeros, torch.uint8, "zeros")
+        o, n = W.shape
+        res = dict(L=torch.empty((n, r), dtype=torch.float32, device=self.device),
+                   R=torch.empty((r, o), dtype=torch.float32, device=self.device))
+        J = ctypes.c_double(0.0)
+        self._check(self.lib.gptq_olrc(self.handle, _ptr(W), o, n, _ptr(H), int(r), int(bits), int(group),
+                                       _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(res["L"]), _ptr(res["R"]),
+                                       ctypes.byref(J)))
+        res["J"] = J.value
+        return res
+
+    def bid_up(self, W, H, L, R, bits: int, group: int, block: int, codes, scales, zeros):
+        """One Bid-Up pass; rewrites codes in place.  Returns the objective after the pass."""
+        torch = self.torch
+        self._dev(W, torch.float32, "W")
+        self._dev(H, torch.float64, "H")
+        self._dev(L, torch.float32, "L")
+        self._dev(R, torch.float32, "R")
+        self._dev(codes, torch.uint8, "codes")
+        self._dev(scales, torch.float32, "scales")
+        self._dev(zeros, torch.uint8, "zeros")
+        o, n = W.shape
+        J = ctypes.c_double(0.0)
+        self._check(self.lib.gptq_bid_up(self.handle, _ptr(W), o, n, _ptr(H), int(L.shape[1]), _ptr(L), _ptr(R),
+                                         int(bits), int(group), int(block), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                         ctypes.byref(J)))
+        return J.value
 
     def quantize_batched(self, layers):
         """layers: list of dicts with W, bits, group, block, lam_rel (and X or H, optional lam_abs,

@@ -716,7 +716,7 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     q.ldE = sbk[p] * J.block;
     q.eoff_blk = J.block;
     q.sbk = sbk[p];
-    q.pad0 = 0;
+    q.mode = J.mode;
     L[p] = q;
     maxblk = std::max(maxblk, q.nblk);
     if (Ww_out) Ww_out->push_back(q.Ww);
@@ -729,23 +729,24 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     bool side;
     size_t off;
     int nseg, nwg;
+    int mode;  // sweeps: 0 GPTQ, 1 Bid-Up
   };
   std::vector<Lc> launches;
-  auto add_launch = [&](int kind, int block, std::vector<Seg>& segs, bool side = false) {
+  auto add_launch = [&](int kind, int block, std::vector<Seg>& segs, bool side = false, int mode = 0) {
     int nwg = 0;
     for (auto& s : segs) {
       s.wg0 = nwg;
       nwg += s.nwg;
     }
     if (nwg == 0) return;
-    launches.push_back(Lc{kind, block, side, b.add(segs), (int)segs.size(), nwg});
+    launches.push_back(Lc{kind, block, side, b.add(segs), (int)segs.size(), nwg, mode});
   };
-  auto add_sync = [&](int kind) { launches.push_back(Lc{kind, 0, false, 0, 0, 0}); };
+  auto add_sync = [&](int kind) { launches.push_back(Lc{kind, 0, false, 0, 0, 0, 0}); };
   {
     std::vector<Seg> s, f;
     for (int p = 0; p < nl; ++p) {
       s.push_back(Seg{p, 0, cdiv(jobs[p].out, 4), 0, 0, 0, 0, 0});
-      if (jobs[p].group == 0) f.push_back(Seg{p, 0, cdiv(jobs[p].out, 4), 0, 0, 0, 0, 0});
+      if (jobs[p].group == 0 && !jobs[p].mode) f.push_back(Seg{p, 0, cdiv(jobs[p].out, 4), 0, 0, 0, 0, 0});
     }
     add_launch(0, 0, s);
     add_launch(1, 0, f);
@@ -761,12 +762,14 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
   // a super-block (a group fit reads its whole group).
   bool side_busy = false;
   for (int k = 0; k < maxblk; ++k) {
-    for (int B : blocks) {
-      std::vector<Seg> s;
-      for (int p = 0; p < nl; ++p)
-        if (jobs[p].block == B && k < L[p].nblk) s.push_back(Seg{p, 0, cdiv(jobs[p].out, 16), k, 0, 0, 0, 0});
-      add_launch(2, B, s);
-    }
+    for (int B : blocks)
+      for (int mode = 0; mode < 2; ++mode) {
+        std::vector<Seg> s;
+        for (int p = 0; p < nl; ++p)
+          if (jobs[p].block == B && jobs[p].mode == mode && k < L[p].nblk)
+            s.push_back(Seg{p, 0, cdiv(jobs[p].out, 16), k, 0, 0, 0, 0});
+        add_launch(2, B, s, false, mode);
+      }
     std::vector<Seg> tn, crit, bulk;  // inside the super-block (64 tiles), past it (64 / 128 tiles)
     for (int p = 0; p < nl; ++p) {
       if (k >= L[p].nblk) continue;
@@ -805,7 +808,7 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     switch (l.kind) {
       case 0: LAUNCH(c, "k_init_work", launch_init_work(dL, sg, l.nseg, l.nwg, c->stream)); break;
       case 1: LAUNCH(c, "k_rowfit", launch_rowfit(dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 2: LAUNCH(c, "k_sweep", launch_sweep(l.block, dL, sg, l.nseg, l.nwg, c->stream)); break;
+      case 2: LAUNCH(c, "k_sweep", launch_sweep(l.block, l.mode, dL, sg, l.nseg, l.nwg, c->stream)); break;
       case 3:  // beside the sweeps: one workgroup per CU, which leaves room on each CU for a sweep's
         LAUNCH_ON(c, st, "k_trail", launch_trail(l.block, dL, sg, l.nseg, l.nwg, l.side ? c->ncu : 0, st));
         break;
@@ -1082,31 +1085,19 @@ GPTQ_API int gptq_quantize_batched(gptq_ctx c, int32_t nlayers, gptq_layer* laye
   return first;
 }
 
-GPTQ_API int gptq_lora(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t* X,
-                       int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,
-                       int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
-                       uint8_t* zeros, float* L, float* R, double* obj, int32_t* info) {
-  if (!c) return GPTQ_ERR_INVALID_ARG;
-  c->err.clear();
-  if (info) *info = 0;
-  int rc = check_quant_args(c, out, n, bits, group, block);
-  if (rc) return rc;
-  if ((rc = check_x(c, X, tokens, n, ldx))) return rc;
-  if (r < 1 || r > 128 || r > n) return set_err(c, GPTQ_ERR_UNSUPPORTED, "rank must be in 1..min(128, n)");
-  if (!obj || !W || !codes || !scales || !zeros || !L || !R || out <= 0 || n <= 0)
-    return set_err(c, GPTQ_ERR_INVALID_ARG, "null pointer or empty layer");
-  obj[0] = obj[1] = 0.0;
-  DeviceGuard g(c->device);
-  LoraIO io{W, out, n, X, tokens, ldx, r, bits, group, block, lam_abs, lam_rel, codes, scales, zeros, L, R};
+namespace {
+
+// Services the LoRA and refinement drivers borrow from the context.
+LoraHooks lora_hooks(gptq_ctx c) {
   LoraHooks hooks;
-  hooks.hessian64 = [&](const uint16_t* X_, long long t_, long long ld_, int n_, double* H_) {
+  hooks.hessian64 = [c](const uint16_t* X_, long long t_, long long ld_, int n_, double* H_) {
     return run_hessian64(c, X_, t_, ld_, n_, H_);
   };
-  hooks.ensure = [&](size_t bytes) -> void* {
+  hooks.ensure = [c](size_t bytes) -> void* {
     if (ensure(c, c->lora, bytes)) return nullptr;
     return c->lora.p;
   };
-  hooks.factor = [&](double* A, int nt, float* U, Slot* slot) {
+  hooks.factor = [c](double* A, int nt, float* U, Slot* slot) {
     // A was assembled (damped, reversed, lower) by the LoRA kernels
     std::vector<FacJob> fj{FacJob{nullptr, nt, nt, nt, 0.0, 0.0, U}};
     DevBuf save = c->facA;
@@ -1116,27 +1107,128 @@ GPTQ_API int gptq_lora(gptq_ctx c, const float* W, int32_t out, int32_t n, const
     c->facA = save;
     return rc2;
   };
-  hooks.quantize = [&](const QuantJob& j) { return run_quantize(c, {j}); };
-  hooks.slots = [&](size_t bytes) -> void* {
+  hooks.quantize = [c](const QuantJob& j) { return run_quantize(c, {j}); };
+  hooks.slots = [c](size_t bytes) -> void* {
     if (ensure(c, c->slots, bytes)) return nullptr;
     return c->slots.p;
   };
-  hooks.set_err = [&](int st, const char* msg) { return set_err(c, st, "%s", msg); };
-  hooks.launch = [&](const char* name, const std::function<hipError_t()>& f) -> int {
+  hooks.set_err = [c](int st, const char* msg) { return set_err(c, st, "%s", msg); };
+  hooks.launch = [c](const char* name, const std::function<hipError_t()>& f) -> int {
     LAUNCH(c, name, f());
     return GPTQ_OK;
   };
+  return hooks;
+}
+
+// gptq_lora and gptq_lora_refine: the sweep on the augmented Hessian, then
+// `rounds` refinement rounds; obj (rounds == 0: {J, J_lam}) or the trace
+// (rounds > 0: 2 rounds + 2 values) is copied to res.
+int lora_impl(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t* X, int64_t tokens, int64_t ldx,
+              int32_t r, int32_t bits, int32_t group, int32_t block, double lam_abs, double lam_rel, int32_t rounds,
+              uint8_t* codes, float* scales, uint8_t* zeros, float* L, float* R, double* res, int32_t* info) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (info) *info = 0;
+  int rc = check_quant_args(c, out, n, bits, group, block);
+  if (rc) return rc;
+  if ((rc = check_x(c, X, tokens, n, ldx))) return rc;
+  if (r < 1 || r > 128 || r > n) return set_err(c, GPTQ_ERR_UNSUPPORTED, "rank must be in 1..min(128, n)");
+  if (!res || !W || !codes || !scales || !zeros || !L || !R || out <= 0 || n <= 0)
+    return set_err(c, GPTQ_ERR_INVALID_ARG, "null pointer or empty layer");
+  if (rounds > 0 && r > out) return set_err(c, GPTQ_ERR_UNSUPPORTED, "refinement needs rank <= out");
+  const int nres = rounds > 0 ? 2 * rounds + 2 : 2;
+  for (int k = 0; k < nres; ++k) res[k] = 0.0;
+  DeviceGuard g(c->device);
+  LoraIO io{W, out, n, X, tokens, ldx, r, bits, group, block, lam_abs, lam_rel, codes, scales, zeros, L, R};
+  io.rounds = rounds;
+  const LoraHooks hooks = lora_hooks(c);
   rc = run_lora(c->stream, io, hooks);
   if (rc) return rc;
-  Slot* ds = (Slot*)c->slots.p;
-  if ((rc = ensure_small(c, sizeof(Slot)))) return rc;
-  HIPCHK(c, hipMemcpyAsync(c->hsmall, ds, sizeof(Slot), hipMemcpyDeviceToHost, c->stream));
+  const size_t bytes = sizeof(Slot) + (rounds > 0 ? (size_t)nres * sizeof(double) : 0);
+  if ((rc = ensure_small(c, bytes))) return rc;
+  HIPCHK(c, hipMemcpyAsync(c->hsmall, c->slots.p, bytes, hipMemcpyDeviceToHost, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
   const Slot s = *(const Slot*)c->hsmall;
   if (s.nonfinite) return set_err(c, GPTQ_ERR_NONFINITE, "non-finite entry in H");
   if (info) *info = s.info;
   if (s.info) return set_err(c, GPTQ_ERR_NOT_PD, "augmented Hessian not positive definite");
-  obj[0] = s.obj[0];
-  obj[1] = s.obj[1];
+  if (rounds > 0) {
+    const double* tr = (const double*)((const Slot*)c->hsmall + 1);
+    for (int k = 0; k < nres; ++k) res[k] = tr[k];
+  } else {
+    res[0] = s.obj[0];
+    res[1] = s.obj[1];
+  }
   return GPTQ_OK;
+}
+
+// gptq_olrc / gptq_bid_up: one refinement step on caller-held state.
+int refine_step(gptq_ctx c, bool bid, const float* W, int32_t out, int32_t n, const double* H, int32_t r,
+                int32_t bits, int32_t group, int32_t block, uint8_t* codes, float* scales, uint8_t* zeros, float* L,
+                float* R, double* J) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  int rc = check_quant_args(c, out, n, bits, group, block);
+  if (rc) return rc;
+  if (!J || !W || !H || !codes || !scales || !zeros || !L || !R || out <= 0 || n <= 0)
+    return set_err(c, GPTQ_ERR_INVALID_ARG, "null pointer or empty layer");
+  if (r < 1 || r > 128 || r > n || r > out)
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "rank must be in 1..min(128, out, n)");
+  *J = 0.0;
+  DeviceGuard g(c->device);
+  if ((rc = ensure(c, c->slots, sizeof(double)))) return rc;
+  double* dJ = (double*)c->slots.p;
+  RefineIO io{W, out, n, H, r, bits, group, block, codes, scales, zeros, L, R};
+  const LoraHooks hooks = lora_hooks(c);
+  rc = bid ? run_bid_up(c->stream, io, hooks, dJ) : run_olrc(c->stream, io, hooks, dJ);
+  if (rc) return rc;
+  if ((rc = ensure_small(c, sizeof(double)))) return rc;
+  HIPCHK(c, hipMemcpyAsync(c->hsmall, dJ, sizeof(double), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  *J = *(const double*)c->hsmall;
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+GPTQ_API int gptq_lora(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t* X,
+                       int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,
+                       int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
+                       uint8_t* zeros, float* L, float* R, double* obj, int32_t* info) {
+  return lora_impl(c, W, out, n, X, tokens, ldx, r, bits, group, block, lam_abs, lam_rel, 0, codes, scales, zeros,
+                   L, R, obj, info);
+}
+
+GPTQ_API int gptq_lora_refine(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t* X,
+                              int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,
+                              int32_t block, double lam_abs, double lam_rel, int32_t rounds, uint8_t* codes,
+                              float* scales, uint8_t* zeros, float* L, float* R, double* trace, int32_t* info) {
+  if (rounds < 1) return set_err(c, GPTQ_ERR_INVALID_ARG, "rounds must be at least 1");
+  return lora_impl(c, W, out, n, X, tokens, ldx, r, bits, group, block, lam_abs, lam_rel, rounds, codes, scales,
+                   zeros, L, R, trace, info);
+}
+
+GPTQ_API int gptq_hessian64(gptq_ctx c, const uint16_t* X, int64_t tokens, int32_t n, int64_t ldx, double* H) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  int rc = check_x(c, X, tokens, n, ldx);
+  if (rc) return rc;
+  if (n > 0 && !H) return set_err(c, GPTQ_ERR_INVALID_ARG, "H is null");
+  if (n == 0) return GPTQ_OK;
+  DeviceGuard g(c->device);
+  return run_hessian64(c, X, tokens, ldx, n, H);
+}
+
+GPTQ_API int gptq_olrc(gptq_ctx c, const float* W, int32_t out, int32_t n, const double* H, int32_t r,
+                       int32_t bits, int32_t group, const uint8_t* codes, const float* scales,
+                       const uint8_t* zeros, float* L, float* R, double* J) {
+  return refine_step(c, false, W, out, n, H, r, bits, group, 128, (uint8_t*)codes, (float*)scales,
+                     (uint8_t*)zeros, L, R, J);
+}
+
+GPTQ_API int gptq_bid_up(gptq_ctx c, const float* W, int32_t out, int32_t n, const double* H, int32_t r,
+                         const float* L, const float* R, int32_t bits, int32_t group, int32_t block,
+                         uint8_t* codes, const float* scales, const uint8_t* zeros, double* J) {
+  return refine_step(c, true, W, out, n, H, r, bits, group, block, codes, (float*)scales, (uint8_t*)zeros,
+                     (float*)L, (float*)R, J);
 }

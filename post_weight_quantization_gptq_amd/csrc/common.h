@@ -106,7 +106,7 @@ struct QLayer {
   int ldE;          // width of the error buffer (one super-block of columns)
   int eoff_blk;     // column offset of one block inside it (= block)
   int sbk;          // blocks per super-block
-  int pad0;
+  int mode;         // 0: GPTQ sweep; 1: Bid-Up pass (W = g, U = H, codes in/out, grid given)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;

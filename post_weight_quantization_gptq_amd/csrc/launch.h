@@ -28,7 +28,8 @@ hipError_t launch_make_u(const FacProb* probs, const Seg* segs, int nseg, int nw
 // Sweep
 hipError_t launch_init_work(const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
 hipError_t launch_rowfit(const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
-hipError_t launch_sweep(int block, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
+// mode 0: the GPTQ sweep; mode 1: one Bid-Up pass (see the QLayer mode field)
+hipError_t launch_sweep(int block, int mode, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st);
 // at most maxwg workgroups (0: one per tile), persistent over the nwg tiles
 hipError_t launch_trail(int ts, const QLayer* L, const Seg* segs, int nseg, int nwg, int maxwg, hipStream_t st);
 hipError_t launch_objective(const QLayer* L, int nl, hipStream_t st);

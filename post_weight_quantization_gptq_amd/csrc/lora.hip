@@ -399,29 +399,290 @@ __global__ void k_lora_extract(const double* __restrict__ V, const float* __rest
 
 inline int cdivl(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+#define LLAUNCH(name, ...)                                                                          \
+  do {                                                                                              \
+    if ((rc = hk.launch(name, [&] { hipLaunchKernelGGL(__VA_ARGS__); return hipGetLastError(); }))) \
+      return rc;                                                                                    \
+  } while (0)
+
 // C = the product; split-K partials go to scratch and are summed by k_dsum
 int dgemm(hipStream_t st, const LoraHooks& hk, const DGemm& g0, double* C, double* scratch) {
   DGemm g = g0;
   const int tiles = cdivl(g.M, 64) * cdivl(g.N, 64);
   if (g.ksplit < 1) g.ksplit = 1;
   g.P = (g.ksplit == 1) ? C : scratch;
-  int rc = hk.launch("k_dgemm", [&] {
-    hipLaunchKernelGGL(k_dgemm, dim3(tiles, g.ksplit), dim3(256), 0, st, g);
-    return hipGetLastError();
-  });
-  if (rc || g.ksplit == 1) return rc;
+  int rc;
+  LLAUNCH("k_dgemm", k_dgemm, dim3(tiles, g.ksplit), dim3(256), 0, st, g);
+  if (g.ksplit == 1) return 0;
   const long long MN = (long long)g.M * g.N;
-  return hk.launch("k_dsum", [&] {
-    hipLaunchKernelGGL(k_dsum, dim3(cdivl(MN, 256)), dim3(256), 0, st, (const double*)scratch, C, MN, g.ksplit);
-    return hipGetLastError();
-  });
+  LLAUNCH("k_dsum", k_dsum, dim3(cdivl(MN, 256)), dim3(256), 0, st, (const double*)scratch, C, MN, g.ksplit);
+  return 0;
+}
+
+inline int ksplit_for(int K) { return std::max(1, std::min(16, K / 256)); }
+
+// one Cholesky-QR pass over nrows x r: Vout = Zin L^{-T}, Zin^T Zin = L L^T
+int orth(hipStream_t st, const LoraHooks& hk, const double* Zin, double* Vout, int nrows, int r, double* Gp,
+         double* Li, unsigned* cnt) {
+  const int nrb = cdivl(nrows, 64), rows_per = 64 * cdivl(nrb, std::min(kGramParts, nrb));
+  const int nparts = cdivl(nrows, rows_per);
+  int rc;
+  LLAUNCH("k_gram_chol", k_gram_chol, dim3(nparts), dim3(256), 0, st, Zin, nrows, r, rows_per, Gp, Li, cnt);
+  LLAUNCH("k_apply", k_apply, dim3(nrb), dim3(256), 0, st, Zin, nrows, r, (const double*)Li, Vout);
+  return 0;
+}
+
+// ----------------------------------------------- refinement: OLrC, Bid-Up -----
+// (GPTQ-intrinsic LoRA technical summary, section 4: OLrC re-fits L, R for a
+// fixed Q, Bid-Up moves Q on its fixed grid for fixed L, R; they alternate
+// and the layer objective never increases.)
+//
+// OLrC: with E = W - What, the rank-r correction C minimising
+// tr((E - C) H (E - C)^T) is C = P P^T E, P the top-r eigenvectors of
+// E H E^T (Eckart-Young on E F for any H = F F^T), so no square root or
+// inverse of H is needed.  P comes from subspace iteration in fp64,
+// P <- orth(EH (E^T P)) with EH = E H formed once, Cholesky-QR twice per
+// step; then L = E^T P, R = P^T (C = R^T L^T).  Its objective is
+// J = sum(g * E) with g = (E - C) H = EH - P (P^T EH), which is also the
+// gradient Bid-Up starts from.
+// Bid-Up: one pass of the column sweep in its Bid-Up mode, on g (fp32) with
+// U = H (fp32): the sweep's lazy block updates carry the moves forward.
+
+// E = W - What - C (C may be null); What = s (q - z) in fp32 as stored
+__global__ void k_resid(const float* __restrict__ W, const uint8_t* __restrict__ codes,
+                        const float* __restrict__ scales, const uint8_t* __restrict__ zeros, int out, int n,
+                        int group, const double* __restrict__ C, double* __restrict__ E) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)out * n) return;
+  const int row = (int)(i / n), col = (int)(i % n);
+  const int ng = group ? n / group : 1;
+  const size_t gi = (size_t)row * ng + (group ? col / group : 0);
+  const float s = scales[gi], z = (float)zeros[gi];
+  const float wh = s * ((float)codes[i] - z);
+  E[i] = (double)W[i] - (double)wh - (C ? C[i] : 0.0);
+}
+
+// g = EH - Y (Y may be null), g32 = fl32(g); part[b] = this block's share of
+// sum(g * E), each thread over a fixed stride of the elements (fixed order)
+__global__ __launch_bounds__(256) void k_gfinal(const double* __restrict__ EH, const double* __restrict__ Y,
+                                                const double* __restrict__ E, long long cnt,
+                                                float* __restrict__ g32, double* __restrict__ part) {
+  __shared__ double red[256];
+  const long long stride = (long long)gridDim.x * 256;
+  double acc = 0.0;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < cnt; i += stride) {
+    const double g = EH[i] - (Y ? Y[i] : 0.0);
+    g32[i] = (float)g;
+    acc += g * E[i];
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// dst[0] = sum of part[0..np) (fixed order) + (add ? add[0] : 0)
+__global__ __launch_bounds__(256) void k_sum_parts(const double* __restrict__ part, int np,
+                                                   const double* __restrict__ add, double* __restrict__ dst) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < np; i += 256) acc += part[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dst[0] = red[0] + (add ? add[0] : 0.0);
+}
+
+__global__ void k_f64_to_f32(const double* __restrict__ a, float* __restrict__ b, long long cnt) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < cnt) b[i] = (float)a[i];
+}
+
+__global__ void k_f32_to_f64(const float* __restrict__ a, double* __restrict__ b, long long cnt) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < cnt) b[i] = (double)a[i];
+}
+
+// L[n][r] = T (fp32); R[k][i] = P[i][k]
+__global__ void k_olrc_out(const double* __restrict__ T, const double* __restrict__ P, int n, int out, int r,
+                           float* __restrict__ L, float* __restrict__ R) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (long long)n * r) L[i] = (float)T[i];
+  if (i < (long long)r * out) {
+    const long long k = i / out, row = i % out;
+    R[i] = (float)P[row * r + k];
+  }
+}
+
+// the arrival counter of the Gram kernels and the device constant 0
+__global__ void k_ref_init(unsigned* __restrict__ cnt, double* __restrict__ dev) {
+  if (threadIdx.x == 0) {
+    *cnt = 0u;
+    dev[0] = 0.0;
+  }
+}
+
+constexpr int kParts = 512;  // partial sums of the objective dot product
+
+struct RefBufs {
+  double *E, *EH, *Y, *P, *Pz, *T, *X, *S, *Gp, *Li, *parts, *Ld, *Rd, *dev;
+  unsigned* cnt;
+  float *g32, *H32;
+};
+
+// Lay the refinement buffers out from offset off of base (base may be null
+// to size them); returns the end offset.
+size_t ref_layout(int out, int n, int r, uint8_t* base, size_t off, RefBufs* b) {
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return base ? base + o : nullptr;
+  };
+  const size_t on = (size_t)out * n;
+  const int ks = std::max(ksplit_for(n), ksplit_for(out));
+  b->E = (double*)take(on * 8);
+  b->EH = (double*)take(on * 8);
+  b->Y = (double*)take(on * 8);
+  b->P = (double*)take((size_t)out * r * 8);
+  b->Pz = (double*)take((size_t)out * r * 8);
+  b->T = (double*)take((size_t)n * r * 8);
+  b->X = (double*)take((size_t)r * n * 8);
+  b->S = (double*)take((size_t)ks * std::max(out, n) * r * 8);
+  b->Gp = (double*)take((size_t)kGramParts * 3 * 64 * 64 * 8);
+  b->Li = (double*)take((size_t)r * r * 8);
+  b->parts = (double*)take((size_t)kParts * 8);
+  b->Ld = (double*)take((size_t)n * r * 8);
+  b->Rd = (double*)take((size_t)r * out * 8);
+  b->dev = (double*)take(8 * 8);
+  b->cnt = (unsigned*)take(sizeof(unsigned));
+  b->g32 = (float*)take(on * 4);
+  b->H32 = (float*)take((size_t)n * n * 4);
+  return off;
+}
+
+int run_gfinal(hipStream_t st, const LoraHooks& hk, const RefBufs& b, const double* EH, const double* Y,
+               const double* E, long long cnt, const double* add, double* J) {
+  int rc;
+  LLAUNCH("k_gfinal", k_gfinal, dim3(kParts), dim3(256), 0, st, EH, Y, E, cnt, b.g32, b.parts);
+  LLAUNCH("k_sum_parts", k_sum_parts, dim3(1), dim3(256), 0, st, (const double*)b.parts, kParts, add, J);
+  return 0;
+}
+
+// OLrC for the current codes: leaves g (fp32) for a Bid-Up pass in b.g32,
+// J in *J (device), and (if L, R are given) the factors.
+int olrc(hipStream_t st, const RefineIO& io, const LoraHooks& hk, const RefBufs& b, double* J, float* L, float* R) {
+  const int out = io.out, n = io.n, r = io.r;
+  const long long on = (long long)out * n;
+  int rc;
+  LLAUNCH("k_resid", k_resid, dim3(cdivl(on, 256)), dim3(256), 0, st, io.W, io.codes, io.scales, io.zeros, out, n,
+          io.group, (const double*)nullptr, b.E);
+  {
+    DGemm g{b.E, n, 1, io.H64, n, 1, nullptr, out, n, n, 1};  // EH = E H
+    if ((rc = dgemm(st, hk, g, b.EH, b.S))) return rc;
+  }
+  double *P = b.P, *Pz = b.Pz;
+  LLAUNCH("k_start_block", k_start_block, dim3(cdivl((long long)out * r, 256)), dim3(256), 0, st, P, out, r);
+  for (int it = 0; it < kIters; ++it) {
+    DGemm t{b.E, 1, n, P, r, 1, nullptr, n, r, out, ksplit_for(out)};  // T = E^T P
+    if ((rc = dgemm(st, hk, t, b.T, b.S))) return rc;
+    DGemm z{b.EH, n, 1, b.T, r, 1, nullptr, out, r, n, ksplit_for(n)};  // Z = EH T
+    if ((rc = dgemm(st, hk, z, Pz, b.S))) return rc;
+    if ((rc = orth(st, hk, Pz, P, out, r, b.Gp, b.Li, b.cnt))) return rc;  // Cholesky-QR, twice
+    if ((rc = orth(st, hk, P, Pz, out, r, b.Gp, b.Li, b.cnt))) return rc;
+    std::swap(P, Pz);
+  }
+  {
+    DGemm t{b.E, 1, n, P, r, 1, nullptr, n, r, out, ksplit_for(out)};  // L = E^T P
+    if ((rc = dgemm(st, hk, t, b.T, b.S))) return rc;
+    DGemm x{P, 1, r, b.EH, n, 1, nullptr, r, n, out, ksplit_for(out)};  // X = P^T EH
+    if ((rc = dgemm(st, hk, x, b.X, b.S))) return rc;
+    DGemm y{P, r, 1, b.X, n, 1, nullptr, out, n, r, 1};  // Y = P X
+    if ((rc = dgemm(st, hk, y, b.Y, b.S))) return rc;
+  }
+  if ((rc = run_gfinal(st, hk, b, b.EH, b.Y, b.E, on, nullptr, J))) return rc;
+  if (L && R) {
+    const long long ne = std::max((long long)n * r, (long long)r * out);
+    LLAUNCH("k_olrc_out", k_olrc_out, dim3(cdivl(ne, 256)), dim3(256), 0, st, (const double*)b.T, (const double*)P, n,
+            out, r, L, R);
+  }
+  return 0;
+}
+
+// One Bid-Up pass from b.g32 (g of the current codes) with H in b.H32;
+// *J = *J0 + the summed objective change of the moves (device values).
+int bid_up_pass(hipStream_t st, const RefineIO& io, const LoraHooks& hk, const RefBufs& b, const double* J0,
+                double* J) {
+  QuantJob q{b.g32, io.out, io.n, io.n, b.H32, io.bits, io.group, io.block, io.codes, io.scales, io.zeros,
+             nullptr, b.dev, b.dev + 2, nullptr};
+  q.mode = 1;
+  int rc = hk.quantize(q);
+  if (rc) return rc;
+  LLAUNCH("k_sum_parts", k_sum_parts, dim3(1), dim3(256), 0, st, (const double*)(b.dev + 2), 1, J0, J);
+  return 0;
+}
+
+int check_refine(const RefineIO& io, const LoraHooks& hk) {
+  if (io.r < 1 || io.r > 128 || io.r > io.out || io.r > io.n)
+    return hk.set_err(GPTQ_ERR_UNSUPPORTED, "rank must be in 1..min(128, out, n)");
+  return 0;
 }
 
 }  // namespace
 
+int run_olrc(hipStream_t st, const RefineIO& io, const LoraHooks& hk, double* J) {
+  int rc = check_refine(io, hk);
+  if (rc) return rc;
+  RefBufs b;
+  const size_t bytes = ref_layout(io.out, io.n, io.r, nullptr, 0, &b);
+  uint8_t* base = (uint8_t*)hk.ensure(bytes);
+  if (!base) return GPTQ_ERR_NO_MEMORY;
+  ref_layout(io.out, io.n, io.r, base, 0, &b);
+  LLAUNCH("k_ref_init", k_ref_init, dim3(1), dim3(64), 0, st, b.cnt, b.dev);
+  return olrc(st, io, hk, b, J, io.L, io.R);
+}
+
+int run_bid_up(hipStream_t st, const RefineIO& io, const LoraHooks& hk, double* J) {
+  int rc = check_refine(io, hk);
+  if (rc) return rc;
+  const int out = io.out, n = io.n, r = io.r;
+  const long long on = (long long)out * n;
+  RefBufs b;
+  const size_t bytes = ref_layout(out, n, r, nullptr, 0, &b);
+  uint8_t* base = (uint8_t*)hk.ensure(bytes);
+  if (!base) return GPTQ_ERR_NO_MEMORY;
+  ref_layout(out, n, r, base, 0, &b);
+  LLAUNCH("k_ref_init", k_ref_init, dim3(1), dim3(64), 0, st, b.cnt, b.dev);
+  // C = R^T L^T in fp64, D = W - What - C, g = D H, J0 = sum(g * D)
+  LLAUNCH("k_f32_to_f64", k_f32_to_f64, dim3(cdivl((long long)n * r, 256)), dim3(256), 0, st, (const float*)io.L,
+          b.Ld, (long long)n * r);
+  LLAUNCH("k_f32_to_f64", k_f32_to_f64, dim3(cdivl((long long)r * out, 256)), dim3(256), 0, st, (const float*)io.R,
+          b.Rd, (long long)r * out);
+  {
+    DGemm c{b.Rd, 1, out, b.Ld, 1, r, nullptr, out, n, r, 1};
+    if ((rc = dgemm(st, hk, c, b.Y, b.S))) return rc;
+  }
+  LLAUNCH("k_resid", k_resid, dim3(cdivl(on, 256)), dim3(256), 0, st, io.W, io.codes, io.scales, io.zeros, out, n,
+          io.group, (const double*)b.Y, b.E);
+  {
+    DGemm g{b.E, n, 1, io.H64, n, 1, nullptr, out, n, n, 1};
+    if ((rc = dgemm(st, hk, g, b.EH, b.S))) return rc;
+  }
+  if ((rc = run_gfinal(st, hk, b, b.EH, nullptr, b.E, on, nullptr, b.dev + 4))) return rc;
+  LLAUNCH("k_f64_to_f32", k_f64_to_f32, dim3(cdivl((long long)n * n, 256)), dim3(256), 0, st, io.H64, b.H32,
+          (long long)n * n);
+  return bid_up_pass(st, io, hk, b, b.dev + 4, J);
+}
+
 int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
   const int n = io.n, r = io.r, nt = n + r, out = io.out;
   if (r > 128) return hk.set_err(GPTQ_ERR_UNSUPPORTED, "rank above 128 is not supported");
+  if (io.rounds > 0 && r > out) return hk.set_err(GPTQ_ERR_UNSUPPORTED, "refinement needs rank <= out");
   // workspace layout
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -429,20 +690,23 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
     off += (bytes + 255) & ~(size_t)255;
     return o;
   };
-  const int ks_n = std::max(1, std::min(16, n / 256));   // split-K for K = n products
-  // Gram row chunks: at most kGramParts workgroups, whole 64-row blocks each
-  const int nrb = cdivl(n, 64), rows_per = 64 * cdivl(nrb, std::min(kGramParts, nrb));
-  const int nparts = cdivl(n, rows_per);
+  const int ks_n = ksplit_for(n);  // split-K for K = n products
   const size_t oH64 = take((size_t)n * n * 8), oV = take((size_t)n * r * 8),
                oZ = take((size_t)n * r * 8), oLi = take((size_t)r * r * 8),
                oM = take((size_t)r * r * 8), oHV = take((size_t)n * r * 8),
                oS = take((size_t)std::max(ks_n * n * r, ks_n * r * r) * 8),
                oGp = take((size_t)kGramParts * 3 * 64 * 64 * 8), oCnt = take(sizeof(unsigned)),
                oA = take((size_t)nt * nt * 8), oU = take((size_t)nt * nt * 4), oW = take((size_t)out * nt * 4);
+  RefBufs rb;
+  const size_t oRef = off;
+  if (io.rounds > 0) off = ref_layout(out, n, r, nullptr, off, &rb);
   uint8_t* base = (uint8_t*)hk.ensure(off);
   if (!base) return GPTQ_ERR_NO_MEMORY;
-  Slot* slot = (Slot*)hk.slots(sizeof(Slot));
+  if (io.rounds > 0) ref_layout(out, n, r, base, oRef, &rb);
+  // slots: the call's Slot, then the refinement trace
+  Slot* slot = (Slot*)hk.slots(sizeof(Slot) + (size_t)(2 * std::max(io.rounds, 0) + 2) * sizeof(double));
   if (!slot) return GPTQ_ERR_NO_MEMORY;
+  double* trace = (double*)(slot + 1);
   double *H64 = (double*)(base + oH64), *V = (double*)(base + oV), *Z = (double*)(base + oZ),
          *Li = (double*)(base + oLi), *M = (double*)(base + oM), *HV = (double*)(base + oHV),
          *S = (double*)(base + oS), *Gp = (double*)(base + oGp), *A = (double*)(base + oA);
@@ -454,25 +718,14 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
   // top-r eigen-directions of H against a damping far below their size
   int rc = hk.hessian64(io.X, io.tokens, io.ldx, n, H64);
   if (rc) return rc;
-#define LLAUNCH(name, ...)                                                                  \
-  do {                                                                                      \
-    if ((rc = hk.launch(name, [&] { hipLaunchKernelGGL(__VA_ARGS__); return hipGetLastError(); }))) \
-      return rc;                                                                            \
-  } while (0)
   LLAUNCH("k_lora_lambda", k_lora_lambda, dim3(1), dim3(256), 0, st, (const double*)H64, n, io.lam_abs, io.lam_rel,
           slot, cnt);
   LLAUNCH("k_start_block", k_start_block, dim3(cdivl((long long)n * r, 256)), dim3(256), 0, st, V, n, r);
-  // one Cholesky-QR pass: Vout = Zin L^{-T}, Zin^T Zin = L L^T
-  auto orth = [&](const double* Zin, double* Vout) -> int {
-    LLAUNCH("k_gram_chol", k_gram_chol, dim3(nparts), dim3(256), 0, st, Zin, n, r, rows_per, Gp, Li, cnt);
-    LLAUNCH("k_apply", k_apply, dim3(nrb), dim3(256), 0, st, Zin, n, r, (const double*)Li, Vout);
-    return 0;
-  };
   for (int it = 0; it < kIters; ++it) {
     DGemm g{H64, n, 1, V, r, 1, nullptr, n, r, n, ks_n};  // Z = H V
     if ((rc = dgemm(st, hk, g, Z, S))) return rc;
-    if ((rc = orth(Z, V))) return rc;  // Cholesky-QR, twice
-    if ((rc = orth(V, Z))) return rc;
+    if ((rc = orth(st, hk, Z, V, n, r, Gp, Li, cnt))) return rc;  // Cholesky-QR, twice
+    if ((rc = orth(st, hk, V, Z, n, r, Gp, Li, cnt))) return rc;
     std::swap(V, Z);
   }
   {
@@ -487,9 +740,23 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
   QuantJob J{io.W, out, n, nt, U, io.bits, io.group, io.block, io.codes, io.scales, io.zeros, nullptr,
              &slot->lam, slot->obj, Ww};
   if ((rc = hk.quantize(J))) return rc;
-  const long long ne = std::max((long long)n * r, (long long)r * out);
-  LLAUNCH("k_lora_extract", k_lora_extract, dim3(cdivl(ne, 256)), dim3(256), 0, st, (const double*)V,
-          (const float*)Ww, out, n, r, io.L, io.R);
-#undef LLAUNCH
-  return 0;
+  if (io.rounds <= 0) {
+    const long long ne = std::max((long long)n * r, (long long)r * out);
+    LLAUNCH("k_lora_extract", k_lora_extract, dim3(cdivl(ne, 256)), dim3(256), 0, st, (const double*)V,
+            (const float*)Ww, out, n, r, io.L, io.R);
+    return 0;
+  }
+  // refinement: rounds of OLrC then Bid-Up, and a last OLrC for L, R
+  RefineIO ri{io.W, out, n, H64, r, io.bits, io.group, io.block, io.codes, io.scales, io.zeros, io.L, io.R};
+  LLAUNCH("k_ref_init", k_ref_init, dim3(1), dim3(64), 0, st, rb.cnt, rb.dev);
+  LLAUNCH("k_sum_parts", k_sum_parts, dim3(1), dim3(256), 0, st, (const double*)slot->obj, 1,
+          (const double*)nullptr, trace);
+  LLAUNCH("k_f64_to_f32", k_f64_to_f32, dim3(cdivl((long long)n * n, 256)), dim3(256), 0, st,
+          (const double*)H64, rb.H32, (long long)n * n);
+  for (int t = 0; t < io.rounds; ++t) {
+    if ((rc = olrc(st, ri, hk, rb, trace + 1 + 2 * t, nullptr, nullptr))) return rc;
+    if ((rc = bid_up_pass(st, ri, hk, rb, trace + 1 + 2 * t, trace + 2 + 2 * t))) return rc;
+  }
+  return olrc(st, ri, hk, rb, trace + 1 + 2 * io.rounds, io.L, io.R);
 }
+#undef LLAUNCH

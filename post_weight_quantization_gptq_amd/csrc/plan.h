@@ -25,6 +25,10 @@ struct QuantJob {
   const double* lam;  // device pointer to the damping of U
   double* obj;        // device [2]
   float* Ww_ext;      // optional caller-owned working buffer [out][nt]
+  // 0: GPTQ sweep.  1: one Bid-Up pass: W holds g = (W - C - What) H, U holds
+  // H, codes are read and rewritten on the given grid (scales, zeros), obj[0]
+  // receives the summed objective change of the moves.
+  int mode = 0;
 };
 
 struct LoraIO {
@@ -34,6 +38,22 @@ struct LoraIO {
   long long tokens, ldx;
   int r, bits, group, block;
   double lam_abs, lam_rel;
+  uint8_t* codes;
+  float* scales;
+  uint8_t* zeros;
+  float* L;
+  float* R;
+  int rounds = 0;  // refinement rounds (OLrC then Bid-Up) after the sweep
+};
+
+// One refinement step's operands: the layer, H in fp64 [n][n] (device), the
+// current codes on their fixed grid, and L [n][r], R [r][out] (OLrC writes
+// them; Bid-Up reads them).
+struct RefineIO {
+  const float* W;
+  int out, n;
+  const double* H64;
+  int r, bits, group, block;
   uint8_t* codes;
   float* scales;
   uint8_t* zeros;
@@ -54,4 +74,10 @@ struct LoraHooks {
   std::function<int(const char*, const std::function<hipError_t()>&)> launch;
 };
 
+// With io.rounds > 0 the slots hold, after the Slot, the objective trace
+// (2 rounds + 2 doubles: after the sweep, then after every step).
 int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hooks);
+// OLrC for the given codes: L, R and the objective into *J (device).
+int run_olrc(hipStream_t st, const RefineIO& io, const LoraHooks& hooks, double* J);
+// One Bid-Up pass for the given L, R: codes rewritten, objective into *J (device).
+int run_bid_up(hipStream_t st, const RefineIO& io, const LoraHooks& hooks, double* J);

@@ -143,6 +143,15 @@ __device__ __forceinline__ void fit_group(SweepState<CPL>& st, const SweepCtx& c
   }
 }
 
+// Bid-Up: the grid of the group starting at in-block column j, as given.
+template <int CPL>
+__device__ __forceinline__ void load_group(SweepState<CPL>& st, const SweepCtx& cx, int j) {
+  const size_t gi = cx.grow + (cx.b0 + j) / cx.G;
+  st.g.s = cx.scales[gi];
+  st.g.r = 1.f / st.g.s;
+  st.g.z = (float)cx.zeros[gi];
+}
+
 // The CPL columns owned by lane O of every row group.
 // Groups are multiples of 8 >= CPL columns, so a group can only start at the
 // first column of an owner lane: the check runs once per owner.
@@ -150,11 +159,22 @@ __device__ __forceinline__ void fit_group(SweepState<CPL>& st, const SweepCtx& c
 // and 1/U_jj are zero, so they produce e = 0 and change nothing (their codes
 // are never written).  Each step loads the next column's U row before its
 // own chain starts, so the LDS latency stays off the serial path.
-template <int O, int CPL>
+//
+// Bid-Up (BID): the working row holds g = d H (d = w - c - what) and "U" is
+// H itself.  Column j moves its code to the grid point nearest
+// t = what_j + g_j / H_jj when that is strictly nearer (in the rounded
+// coordinate x) than the current code; the move e = what_new - what_old is
+// fed forward exactly as the sweep's error (g_k -= e H_jk), and the owner
+// keeps the objective change e (e H_jj - 2 g_j) where the sweep keeps what.
+// H_jj is the owner's own entry of row j of the block (ucur[c]).
+template <int O, int CPL, bool BID>
 __device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx& cx, float (&ucur)[CPL]) {
   constexpr int B = 16 * CPL;
   if (O * CPL == st.nextg && O * CPL < cx.bw) {
-    fit_group<CPL>(st, cx, O * CPL);
+    if constexpr (BID)
+      load_group<CPL>(st, cx, O * CPL);
+    else
+      fit_group<CPL>(st, cx, O * CPL);
     st.nextg += cx.G;
   }
 #pragma unroll
@@ -167,14 +187,32 @@ __device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx&
       for (int v = 0; v < CPL; ++v) unext[v] = un[v];
     }
     const float wj = bcast16<O>(st.wv[c]);
-    const float x = __fadd_rn(__fmul_rn(wj, st.g.r), st.g.z);
-    const float q = fminf(fmaxf(rintf(x), 0.f), cx.maxq);
-    const float what = st.g.s * (q - st.g.z);
-    const float e = (wj - what) * bcast16<O>(st.dv[c]);
-    if (cx.l16 == O) {
-      st.qv[c] = q;
-      st.hv[c] = what;
-      st.ev[c] = e;
+    float e;
+    if constexpr (BID) {
+      // dequantised values rounded as stored (__fmul_rn: no fusion into the
+      // subtraction), so a code that stays put moves by exactly 0
+      const float qo = bcast16<O>(st.qv[c]);
+      const float ho = __fmul_rn(st.g.s, qo - st.g.z);
+      const float t = fmaf(wj, bcast16<O>(st.dv[c]), ho);
+      const float x = __fadd_rn(__fmul_rn(t, st.g.r), st.g.z);
+      const float qs = fminf(fmaxf(rintf(x), 0.f), cx.maxq);
+      const float qn = (fabsf(x - qs) < fabsf(x - qo)) ? qs : qo;
+      e = __fmul_rn(st.g.s, qn - st.g.z) - ho;
+      if (cx.l16 == O) {
+        st.qv[c] = qn;
+        st.hv[c] = e * fmaf(e, ucur[c], -2.f * wj);
+        st.ev[c] = e;
+      }
+    } else {
+      const float x = __fadd_rn(__fmul_rn(wj, st.g.r), st.g.z);
+      const float q = fminf(fmaxf(rintf(x), 0.f), cx.maxq);
+      const float what = __fmul_rn(st.g.s, q - st.g.z);  // as stored, not fused into the error
+      e = (wj - what) * bcast16<O>(st.dv[c]);
+      if (cx.l16 == O) {
+        st.qv[c] = q;
+        st.hv[c] = what;
+        st.ev[c] = e;
+      }
     }
     // take the owner's values now (an empty asm pins them), so the 16 owners'
     // candidates do not all stay live to the end of the block: 138 registers
@@ -189,19 +227,22 @@ __device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx&
   }
 }
 
-template <int O, int CPL>
+template <int O, int CPL, bool BID>
 struct SweepAll {
   __device__ __forceinline__ static void run(SweepState<CPL>& st, const SweepCtx& cx, float (&ucur)[CPL]) {
-    sweep_owner<O, CPL>(st, cx, ucur);
-    SweepAll<O + 1, CPL>::run(st, cx, ucur);
+    sweep_owner<O, CPL, BID>(st, cx, ucur);
+    SweepAll<O + 1, CPL, BID>::run(st, cx, ucur);
   }
 };
-template <int CPL>
-struct SweepAll<16, CPL> {
+template <int CPL, bool BID>
+struct SweepAll<16, CPL, BID> {
   __device__ __forceinline__ static void run(SweepState<CPL>&, const SweepCtx&, float (&)[CPL]) {}
 };
 
-template <int CPL>
+// BID: one Bid-Up pass instead of the GPTQ sweep (codes are read as the
+// starting point, the grid is the one given, and the per-row sums are the
+// objective changes of the moves).
+template <int CPL, bool BID>
 __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
                                                const Seg* __restrict__ segs, int nseg) {
   constexpr int B = 16 * CPL;
@@ -225,8 +266,8 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
     const bool in = rv && lc < bw;
     st.wv[c] = in ? ly.Ww[(size_t)row * nt + b0 + lc] : 0.f;
     st.dv[c] = (lc < bw) ? ly.dinv[b0 + lc] : 0.f;
-    wo[c] = in ? ly.W[(size_t)row * ly.n + b0 + lc] : 0.f;
-    st.qv[c] = 0.f;
+    wo[c] = (in && !BID) ? ly.W[(size_t)row * ly.n + b0 + lc] : 0.f;
+    st.qv[c] = (in && BID) ? (float)ly.codes[(size_t)row * ly.n + b0 + lc] : 0.f;
     st.hv[c] = 0.f;
     st.ev[c] = 0.f;
   }
@@ -290,7 +331,7 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   float ucur[CPL];
 #pragma unroll
   for (int v = 0; v < CPL; ++v) ucur[v] = Us[CPL * l16 + v];
-  SweepAll<0, CPL>::run(st, cx, ucur);
+  SweepAll<0, CPL, BID>::run(st, cx, ucur);
 
   double se = 0.0, sd = 0.0;
 #pragma unroll
@@ -300,9 +341,13 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
       ly.codes[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
       ly.Eb[((size_t)((blk / ly.sbk) & 1) * ly.out + row) * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
       if (ly.err) ly.err[(size_t)row * ly.n + b0 + lc] = st.ev[c];
-      const double d = (double)wo[c] - (double)st.hv[c];
-      sd += d * d;
-      se += (double)st.ev[c] * (double)st.ev[c];
+      if (BID) {
+        se += (double)st.hv[c];
+      } else {
+        const double d = (double)wo[c] - (double)st.hv[c];
+        sd += d * d;
+        se += (double)st.ev[c] * (double)st.ev[c];
+      }
     }
   }
 #pragma unroll
@@ -516,16 +561,21 @@ hipError_t launch_trail(int ts, const QLayer* L, const Seg* segs, int nseg, int 
   return hipGetLastError();
 }
 
-hipError_t launch_sweep(int block, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st) {
-  if (nwg <= 0) return hipSuccess;
+template <bool BID>
+hipError_t launch_sweep_t(int block, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st) {
   switch (block) {
-    case 16: hipLaunchKernelGGL(k_sweep<1>, dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
-    case 32: hipLaunchKernelGGL(k_sweep<2>, dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
-    case 64: hipLaunchKernelGGL(k_sweep<4>, dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
-    case 128: hipLaunchKernelGGL(k_sweep<8>, dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
+    case 16: hipLaunchKernelGGL((k_sweep<1, BID>), dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
+    case 32: hipLaunchKernelGGL((k_sweep<2, BID>), dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
+    case 64: hipLaunchKernelGGL((k_sweep<4, BID>), dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
+    case 128: hipLaunchKernelGGL((k_sweep<8, BID>), dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_sweep(int block, int mode, const QLayer* L, const Seg* segs, int nseg, int nwg, hipStream_t st) {
+  if (nwg <= 0) return hipSuccess;
+  return mode ? launch_sweep_t<true>(block, L, segs, nseg, nwg, st) : launch_sweep_t<false>(block, L, segs, nseg, nwg, st);
 }
 
 hipError_t launch_objective(const QLayer* L, int nl, hipStream_t st) {
