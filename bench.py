@@ -94,7 +94,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="square", choices=["square", "single", "lora", "mlp", "vit"])
+    ap.add_argument("--workload", default="square", choices=["square", "single", "lora", "lora_refine", "mlp", "vit"])
+    ap.add_argument("--rounds", type=int, default=1, help="refinement rounds of the lora_refine workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), the reference kernel for "
@@ -119,7 +120,7 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "launches": 5}), flush=True)
         return
-    specs = synth.FULL[args.workload]
+    specs = synth.FULL["lora" if args.workload == "lora_refine" else args.workload]
     print("# generating %s inputs" % args.workload, file=sys.stderr, flush=True)
     lays = [synth.layer(s, dev) for s in specs]
     torch.cuda.synchronize()
@@ -137,7 +138,11 @@ def main():
         for li, (s, l) in enumerate(zip(specs, lays)):
             ev = evl[li] if evl is not None else None
             if s.kind == "lowrank":
-                results.append(ctx.lora(l["W"], l["X"], s.rank, s.bits, s.group, s.block, lam_rel=s.lam_rel))
+                if args.workload == "lora_refine":
+                    results.append(ctx.lora_refine(l["W"], l["X"], s.rank, s.bits, s.group, s.block,
+                                                   rounds=args.rounds, lam_rel=s.lam_rel))
+                else:
+                    results.append(ctx.lora(l["W"], l["X"], s.rank, s.bits, s.group, s.block, lam_rel=s.lam_rel))
                 continue
             if ev is not None:
                 ev[0].record(st)
@@ -183,7 +188,8 @@ def main():
     names = ["k_xpose", "k_syrk", "k_syrk_reduce", "k_syrk64", "k_syrk64_reduce", "k_damp_lambda", "k_damp_fill", "k_chol_panel", "k_chol_panel2",
              "k_gemm64", "k_gemm_ring64", "k_gemm_ring128", "k_make_u", "k_init_work", "k_rowfit", "k_sweep", "k_trail", "k_objective",
              "k_lora_lambda", "k_start_block", "k_dgemm", "k_dsum", "k_gram_chol", "k_apply", "k_lora_assemble",
-             "k_lora_extract"]
+             "k_lora_extract", "k_ref_init", "k_resid", "k_gfinal", "k_sum_parts", "k_f32_to_f64", "k_f64_to_f32",
+             "k_olrc_out"]
     breakdown = {}
     for nm in names:
         ms, cnt = ctx.kernel_time(nm)
@@ -235,6 +241,8 @@ def main():
                             "flops_per_launch": per_launch}
     if args.workload == "lora":
         line["objective"] = {"J": last[0]["J"], "J_lam": last[0]["J_lam"]}
+    if args.workload == "lora_refine":
+        line["objective"] = {"trace": last[0]["trace"], "rounds": args.rounds}
     if not args.no_cpu_baseline and args.workload in ("square", "single"):
         print("# timing the oracle on a host sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(specs[0], {"W": lays[0]["W"], "X": lays[0]["X"]})

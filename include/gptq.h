@@ -150,7 +150,8 @@ int gptq_hessian64(gptq_ctx ctx, const uint16_t* X, int64_t tokens, int32_t n, i
  *
  * gptq_olrc: for the given codes, the rank-r correction C minimising J is
  * C = P P^T E with E = W - What and P the top-r eigenvectors of E H E^T
- * (found by subspace iteration in fp64, Cholesky-QR twice per step; where
+ * (found by subspace iteration in fp64, Cholesky-QR once per step and twice
+ * on the last; where
  * the r-th and (r+1)-th eigenvalues are close, any near-optimal subspace may
  * come out).  Writes L[n][r] = E^T P and R[r][out] = P^T (fp32, device) and
  * J (host, the objective with that correction).  codes/scales/zeros as

@@ -592,7 +592,8 @@ def bid_up(W, C, codes, scales, zeros, H, bits: int, group: int = 0,
         dJ += delta * (delta * H[j, j] - 2.0 * g[:, j])
         codes[:, j] = qn.astype(np.uint8)
         What[:, j] = hn
-        g -= np.outer(delta, H[j])
+        mv_rows = delta != 0  # rows that did not move keep their g
+        g[mv_rows] -= np.outer(delta[mv_rows], H[j])
     D = W - C - What
     return dict(codes=codes, What=What, dJ=dJ, J0=J0, J=float(np.sum((D @ H) * D)),
                 moves=moves, forced=forced)

@@ -1087,6 +1087,25 @@ GPTQ_API int gptq_quantize_batched(gptq_ctx c, int32_t nlayers, gptq_layer* laye
 
 namespace {
 
+// C[M][N] = A[M][K] B[N][K]^T (pitch ld) on the fp64 MFMA ring, 128 tiles.
+int run_gemm_nt(gptq_ctx c, const double* A, const double* B, double* C, int M, int N, int K, int ld) {
+  FacProb p{};
+  p.A = (double*)A;
+  p.Y = (double*)B;
+  p.C = C;
+  p.n = ld;
+  const int ntiles = cdiv(M, 128) * cdiv(N, 128);
+  std::vector<Seg> segs{Seg{0, 0, ntiles, GK_NT, M, N, K, 0}};
+  Blob b;
+  const size_t op = b.add(&p, 1), os = b.add(segs);
+  uint8_t* d = nullptr;
+  int rc = upload(c, b, &d);
+  if (rc) return rc;
+  LAUNCH(c, "k_gemm_ring128",
+         launch_gemm_ring(128, (const FacProb*)(d + op), (const Seg*)(d + os), 1, ntiles, 0, c->stream));
+  return GPTQ_OK;
+}
+
 // Services the LoRA and refinement drivers borrow from the context.
 LoraHooks lora_hooks(gptq_ctx c) {
   LoraHooks hooks;
@@ -1116,6 +1135,9 @@ LoraHooks lora_hooks(gptq_ctx c) {
   hooks.launch = [c](const char* name, const std::function<hipError_t()>& f) -> int {
     LAUNCH(c, name, f());
     return GPTQ_OK;
+  };
+  hooks.gemm_nt = [c](const double* A, const double* B, double* C, int M, int N, int K, int ld) {
+    return run_gemm_nt(c, A, B, C, M, N, K, ld);
   };
   return hooks;
 }

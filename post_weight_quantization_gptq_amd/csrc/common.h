@@ -71,6 +71,7 @@ struct FacProb {
   double* A;       // [n][n]: P H_lam P (lower), overwritten by L
   double* Y;       // [n][n]: L^{-1}, built row block by row block
   float* U;        // output [n][ldu]
+  double* C;       // GK_NT only: the product's output
   int n;
   int ldh;
   int ldu;
@@ -86,7 +87,10 @@ struct FacProb {
 // GK_ZUPD: Y(i, j) -= sum_t L(i, t) Y(t, j) on rows [d, e) x columns
 //   [0, b + c), t in [b, b + c); columns from b on are written for the first
 //   time (no accumulate).
-enum GemmKind { GK_CHOL_TRAIL = 0, GK_ZUPD = 1 };
+// GK_NT: C(i, j) = sum_t A(i, t) B(j, t) with A = A [b][d], B = Y [c][d] and
+//   C [b][c], all of pitch n (a plain product of two k-contiguous operands;
+//   the flags info / nonfinite are not consulted).
+enum GemmKind { GK_CHOL_TRAIL = 0, GK_ZUPD = 1, GK_NT = 2 };
 
 // ------------------------------------------------------------------ sweep --
 struct QLayer {

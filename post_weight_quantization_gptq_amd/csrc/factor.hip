@@ -585,7 +585,7 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
   static_assert(NQ >= 1 && NQ * NW * 1024 == OPB, "load split");
   const Seg sg = segs[find_seg(segs, nseg, vt)];
   const FacProb pb = probs[sg.prob];
-  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  if (sg.a != GK_NT && (*pb.info != 0 || *pb.nonfinite != 0)) return;
   const int n = pb.n;
   const int t = vt - sg.wg0;
   const double* A;
@@ -616,6 +616,22 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
     ke = kw;
     alpha = -1.0;
     beta = 1.0;
+  } else if (sg.a == GK_NT) {
+    const int M = sg.b, N = sg.c, K = sg.d;
+    const int ncol = (N + TS - 1) / TS;
+    const int i0 = TS * (t / ncol), j0 = TS * (t % ncol);
+    A = pb.A + (size_t)i0 * n;
+    B = pb.Y + (size_t)j0 * n;
+    lda = ldb = n;
+    bkc = true;
+    C = pb.C + (size_t)i0 * n + j0;
+    ldc = n;
+    mt = min(TS, M - i0);
+    nt = min(TS, N - j0);
+    kb = 0;
+    ke = K;
+    alpha = 1.0;
+    beta = 0.0;
   } else {
     // Y(i, j) -= sum_t L(i, t) Y(t, j): rows [r0, r1) x columns [0, kb0 + kw)
     const int kb0 = sg.b, kw = sg.c, r0 = sg.d, r1 = sg.e;

@@ -11,8 +11,10 @@
 // here, in fp64 (the damped matrix stays positive definite, and fp64 keeps
 // the condition number of ~1e6 at lam = 1e-4 mean(diag H) harmless).
 //
-// V_r comes from subspace iteration in fp64 (V <- orth(H V), orthonormalised
-// by Cholesky-QR applied twice), started from a fixed hash-generated block.
+// V_r comes from subspace iteration in fp64 (V <- orth(H V) by Cholesky-QR;
+// an intermediate basis only has to stay well conditioned, so one pass per
+// step, and a second pass on the last iterate makes it orthonormal to
+// rounding), started from a fixed hash-generated block.
 // Only span(V_r) matters: Q and the product L R do not depend on the basis.
 #include <algorithm>
 #include <utility>
@@ -39,67 +41,78 @@ struct DGemm {
   int M, N, K, ksplit;
 };
 
+// One 64x64 tile per workgroup over its split's k range, 4 waves of 32x32 on
+// v_mfma_f64_16x16x4f64.  K chunks of 32 go through registers into a
+// double-buffered LDS pair: the loads of chunk c+1 are in flight while chunk c
+// is multiplied (the products here are thin and latency-bound).
 __global__ __launch_bounds__(256) void k_dgemm(DGemm g) {
-  __shared__ double As[64][17];
-  __shared__ double Bs[16][65];
+  constexpr int KC = 32;
+  __shared__ double As[2][64][KC + 1];
+  __shared__ double Bs[2][KC][65];
   const int tiles_n = (g.N + 63) / 64;
   const int i0 = 64 * (blockIdx.x / tiles_n), j0 = 64 * (blockIdx.x % tiles_n);
   const int z = blockIdx.y;
   const int kb = (int)((long long)g.K * z / g.ksplit), ke = (int)((long long)g.K * (z + 1) / g.ksplit);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
+  // this thread's 8 A and 8 B values of a chunk
+  const bool ak = g.sak == 1, bj = g.sbj == 1;
+  const int ar = ak ? tid >> 2 : tid & 63, akq = ak ? (tid & 3) * 8 : (tid >> 6) * 8;
+  const int bk = bj ? tid >> 3 : (tid & 3) * 8, bjq = bj ? (tid & 7) * 8 : tid >> 2;
+  const bool arow = i0 + ar < g.M;
+  double ra[8], rb[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kk = k0 + akq + u;
+      ra[u] = (arow && kk < ke) ? g.A[(long long)(i0 + ar) * g.sai + (long long)kk * g.sak] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kk = bj ? k0 + bk : k0 + bk + u, j = bj ? j0 + bjq + u : j0 + bjq;
+      rb[u] = (kk < ke && j < g.N) ? g.B[(long long)kk * g.sbk + (long long)j * g.sbj] : 0.0;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) As[buf][ar][akq + u] = ra[u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (bj) Bs[buf][bk][bjq + u] = rb[u];
+      else Bs[buf][bk + u][bjq] = rb[u];
+    }
+  };
   f64x4 acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0;
-  for (int k0 = kb; k0 < ke; k0 += 16) {
-    if (g.sak == 1) {
-      const int r = tid >> 2, kq = (tid & 3) * 4;
+      for (int r = 0; r < 4; ++r) acc[a][c][r] = 0.0;
+  if (kb < ke) {
+    load(kb);
+    store(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = kb; k0 < ke; k0 += KC) {
+    const bool more = k0 + KC < ke;
+    if (more) load(k0 + KC);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = k0 + kq + u, i = i0 + r;
-        As[r][kq + u] = (i < g.M && kk < ke) ? g.A[i * g.sai + kk] : 0.0;
-      }
-    } else {
-      const int r = tid & 63, kq = (tid >> 6) * 4;
+    for (int kk = 0; kk < KC / 4; ++kk) {
+      double av[2], bv[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = k0 + kq + u, i = i0 + r;
-        As[r][kq + u] = (i < g.M && kk < ke) ? g.A[i * g.sai + kk * g.sak] : 0.0;
-      }
-    }
-    if (g.sbj == 1) {
-      const int kr = tid >> 4, jq = (tid & 15) * 4;
+      for (int mi = 0; mi < 2; ++mi) av[mi] = As[buf][32 * wr + 16 * mi + (lane & 15)][4 * kk + (lane >> 4)];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = k0 + kr, j = j0 + jq + u;
-        Bs[kr][jq + u] = (kk < ke && j < g.N) ? g.B[kk * g.sbk + j] : 0.0;
-      }
-    } else {
-      const int jl = tid >> 2, kq = (tid & 3) * 4;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = k0 + kq + u, j = j0 + jl;
-        Bs[kq + u][jl] = (kk < ke && j < g.N) ? g.B[kk * g.sbk + j * g.sbj] : 0.0;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      double a[2], b[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) a[mi] = As[32 * wr + 16 * mi + (lane & 15)][4 * kk + (lane >> 4)];
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) b[ni] = Bs[4 * kk + (lane >> 4)][32 * wc + 16 * ni + (lane & 15)];
+      for (int ni = 0; ni < 2; ++ni) bv[ni] = Bs[buf][4 * kk + (lane >> 4)][32 * wc + 16 * ni + (lane & 15)];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
     }
+    if (more) store(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
   double* P = g.P + (size_t)z * g.M * g.N;
 #pragma unroll
@@ -151,17 +164,22 @@ __global__ void k_start_block(double* __restrict__ V, int n, int r) {
 // the result stays finite (the second pass re-orthonormalises).
 constexpr int kGramParts = 8;  // at most this many row chunks per Gram
 
-// ZTb[c][t] = Z[i0 + t][64 b + c] for t < 64, zeros past n and r
-__device__ __forceinline__ void load_zt(const double* __restrict__ Z, int n, int r, int i0, double (*ZT0)[LDP],
-                                        double (*ZT1)[LDP]) {
+// ZTb[c][t] = Z[i0 + t][64 b + c] for t < 64, zeros past n and r: the
+// values go to registers first (zt_load), then to LDS transposed (zt_store),
+// so the next chunk's loads can be in flight while this one is multiplied
+__device__ __forceinline__ void zt_load(const double* __restrict__ Z, int n, int r, int i0, double (&v)[32]) {
   const int tid = threadIdx.x;
   const int rc = r > NB ? 2 * NB : NB;  // columns staged
-  double v[32];
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     const int e = tid + 256 * q, t = e / rc, c = e % rc;
     v[q] = (e < NB * rc && i0 + t < n && c < r) ? Z[(size_t)(i0 + t) * r + c] : 0.0;
   }
+}
+
+__device__ __forceinline__ void zt_store(int r, const double (&v)[32], double (*ZT0)[LDP], double (*ZT1)[LDP]) {
+  const int tid = threadIdx.x;
+  const int rc = r > NB ? 2 * NB : NB;
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     const int e = tid + 256 * q, t = e / rc, c = e % rc;
@@ -193,9 +211,12 @@ __global__ __launch_bounds__(256) void k_gram_chol(const double* __restrict__ Z,
     blk_zero(g10);
     blk_zero(g11);
     const int ie = min(n, (z + 1) * rows_per);
+    double v[32];
+    zt_load(Z, n, r, z * rows_per, v);
     for (int i0 = z * rows_per; i0 < ie; i0 += NB) {
-      load_zt(Z, n, r, i0, LT, L10);
+      zt_store(r, v, LT, L10);
       __syncthreads();
+      if (i0 + NB < ie) zt_load(Z, n, r, i0 + NB, v);  // next chunk, in flight during the products
       blk_mma<true>(g00, LT, LT);
       if (two) {
         blk_mma<true>(g10, L10, LT);
@@ -224,7 +245,22 @@ __global__ __launch_bounds__(256) void k_gram_chol(const double* __restrict__ Z,
     double s[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) s[q] = 0.0;
-    for (int zz = 0; zz < nz; ++zz) {
+    // in chunk order; four partials' loads in flight at a time
+    int zz = 0;
+    for (; zz + 4 <= nz; zz += 4) {
+      double t4[4][16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const double* P = Gp + ((size_t)(zz + u) * 3 + b) * NB * NB;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) t4[u][q] = P[tid + 256 * q];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s[q] += t4[u][q];
+    }
+    for (; zz < nz; ++zz) {
       const double* P = Gp + ((size_t)zz * 3 + b) * NB * NB;
 #pragma unroll
       for (int q = 0; q < 16; ++q) s[q] += P[tid + 256 * q];
@@ -419,7 +455,8 @@ int dgemm(hipStream_t st, const LoraHooks& hk, const DGemm& g0, double* C, doubl
   return 0;
 }
 
-inline int ksplit_for(int K) { return std::max(1, std::min(16, K / 256)); }
+// split-K: about 128 of K per workgroup (4 chunks), at most 16 partials
+inline int ksplit_for(int K) { return std::max(1, std::min(16, K / 128)); }
 
 // one Cholesky-QR pass over nrows x r: Vout = Zin L^{-T}, Zin^T Zin = L L^T
 int orth(hipStream_t st, const LoraHooks& hk, const double* Zin, double* Vout, int nrows, int r, double* Gp,
@@ -441,8 +478,8 @@ int orth(hipStream_t st, const LoraHooks& hk, const double* Zin, double* Vout, i
 // tr((E - C) H (E - C)^T) is C = P P^T E, P the top-r eigenvectors of
 // E H E^T (Eckart-Young on E F for any H = F F^T), so no square root or
 // inverse of H is needed.  P comes from subspace iteration in fp64,
-// P <- orth(EH (E^T P)) with EH = E H formed once, Cholesky-QR twice per
-// step; then L = E^T P, R = P^T (C = R^T L^T).  Its objective is
+// P <- orth(EH (E^T P)) with EH = E H formed once (one Cholesky-QR pass per
+// step, a second on the last iterate); then L = E^T P, R = P^T (C = R^T L^T).  Its objective is
 // J = sum(g * E) with g = (E - C) H = EH - P (P^T EH), which is also the
 // gradient Bid-Up starts from.
 // Bid-Up: one pass of the column sweep in its Bid-Up mode, on g (fp32) with
@@ -566,6 +603,16 @@ size_t ref_layout(int out, int n, int r, uint8_t* base, size_t off, RefBufs* b) 
   return off;
 }
 
+// EH[out][n] = E[out][n] H[n][n] (H symmetric, so E H = E H^T: both operands
+// k-contiguous) on the fp64 MFMA ring when the shapes allow, else k_dgemm
+int e_times_h(hipStream_t st, const LoraHooks& hk, const double* E, const double* H, double* EH, double* S, int out,
+              int n) {
+  const bool ring = n % 16 == 0 && ((uintptr_t)E & 15) == 0 && ((uintptr_t)H & 15) == 0 && ((uintptr_t)EH & 15) == 0;
+  if (ring) return hk.gemm_nt(E, H, EH, out, n, n, n);
+  DGemm g{E, n, 1, H, n, 1, nullptr, out, n, n, 1};
+  return dgemm(st, hk, g, EH, S);
+}
+
 int run_gfinal(hipStream_t st, const LoraHooks& hk, const RefBufs& b, const double* EH, const double* Y,
                const double* E, long long cnt, const double* add, double* J) {
   int rc;
@@ -582,10 +629,7 @@ int olrc(hipStream_t st, const RefineIO& io, const LoraHooks& hk, const RefBufs&
   int rc;
   LLAUNCH("k_resid", k_resid, dim3(cdivl(on, 256)), dim3(256), 0, st, io.W, io.codes, io.scales, io.zeros, out, n,
           io.group, (const double*)nullptr, b.E);
-  {
-    DGemm g{b.E, n, 1, io.H64, n, 1, nullptr, out, n, n, 1};  // EH = E H
-    if ((rc = dgemm(st, hk, g, b.EH, b.S))) return rc;
-  }
+  if ((rc = e_times_h(st, hk, b.E, io.H64, b.EH, b.S, out, n))) return rc;  // EH = E H
   double *P = b.P, *Pz = b.Pz;
   LLAUNCH("k_start_block", k_start_block, dim3(cdivl((long long)out * r, 256)), dim3(256), 0, st, P, out, r);
   for (int it = 0; it < kIters; ++it) {
@@ -593,10 +637,10 @@ int olrc(hipStream_t st, const RefineIO& io, const LoraHooks& hk, const RefBufs&
     if ((rc = dgemm(st, hk, t, b.T, b.S))) return rc;
     DGemm z{b.EH, n, 1, b.T, r, 1, nullptr, out, r, n, ksplit_for(n)};  // Z = EH T
     if ((rc = dgemm(st, hk, z, Pz, b.S))) return rc;
-    if ((rc = orth(st, hk, Pz, P, out, r, b.Gp, b.Li, b.cnt))) return rc;  // Cholesky-QR, twice
-    if ((rc = orth(st, hk, P, Pz, out, r, b.Gp, b.Li, b.cnt))) return rc;
-    std::swap(P, Pz);
+    if ((rc = orth(st, hk, Pz, P, out, r, b.Gp, b.Li, b.cnt))) return rc;
   }
+  if ((rc = orth(st, hk, P, Pz, out, r, b.Gp, b.Li, b.cnt))) return rc;  // second pass on the last iterate
+  std::swap(P, Pz);
   {
     DGemm t{b.E, 1, n, P, r, 1, nullptr, n, r, out, ksplit_for(out)};  // L = E^T P
     if ((rc = dgemm(st, hk, t, b.T, b.S))) return rc;
@@ -669,10 +713,7 @@ int run_bid_up(hipStream_t st, const RefineIO& io, const LoraHooks& hk, double* 
   }
   LLAUNCH("k_resid", k_resid, dim3(cdivl(on, 256)), dim3(256), 0, st, io.W, io.codes, io.scales, io.zeros, out, n,
           io.group, (const double*)b.Y, b.E);
-  {
-    DGemm g{b.E, n, 1, io.H64, n, 1, nullptr, out, n, n, 1};
-    if ((rc = dgemm(st, hk, g, b.EH, b.S))) return rc;
-  }
+  if ((rc = e_times_h(st, hk, b.E, io.H64, b.EH, b.S, out, n))) return rc;  // g = D H
   if ((rc = run_gfinal(st, hk, b, b.EH, nullptr, b.E, on, nullptr, b.dev + 4))) return rc;
   LLAUNCH("k_f64_to_f32", k_f64_to_f32, dim3(cdivl((long long)n * n, 256)), dim3(256), 0, st, io.H64, b.H32,
           (long long)n * n);
@@ -724,10 +765,10 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
   for (int it = 0; it < kIters; ++it) {
     DGemm g{H64, n, 1, V, r, 1, nullptr, n, r, n, ks_n};  // Z = H V
     if ((rc = dgemm(st, hk, g, Z, S))) return rc;
-    if ((rc = orth(st, hk, Z, V, n, r, Gp, Li, cnt))) return rc;  // Cholesky-QR, twice
-    if ((rc = orth(st, hk, V, Z, n, r, Gp, Li, cnt))) return rc;
-    std::swap(V, Z);
+    if ((rc = orth(st, hk, Z, V, n, r, Gp, Li, cnt))) return rc;
   }
+  if ((rc = orth(st, hk, V, Z, n, r, Gp, Li, cnt))) return rc;  // second pass on the last iterate
+  std::swap(V, Z);
   {
     DGemm g{H64, n, 1, V, r, 1, nullptr, n, r, n, ks_n};  // HV = H V
     if ((rc = dgemm(st, hk, g, HV, S))) return rc;

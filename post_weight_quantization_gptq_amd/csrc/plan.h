@@ -72,6 +72,9 @@ struct LoraHooks {
   // issue one launch (the function) on the context's stream under the given
   // kernel name (a string literal), timed when timing is on
   std::function<int(const char*, const std::function<hipError_t()>&)> launch;
+  // C[M][N] = A[M][K] B[N][K]^T in fp64, all of pitch ld, on the factor's
+  // fp64 MFMA ring (needs K % 16 == 0, even ld and 16-byte aligned bases)
+  std::function<int(const double*, const double*, double*, int, int, int, int)> gemm_nt;
 };
 
 // With io.rounds > 0 the slots hold, after the Slot, the objective trace

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 
 from oracle import gptq_ref as o  # noqa: E402
 from post_weight_quantization_gptq_amd import Context, synth  # noqa: E402
-from parity import check_h_block, check_sweep, check_sweep_recurrence, check_u_rows, np32  # noqa: E402
+from parity import TIE, check_h_block, check_sweep, check_sweep_recurrence, check_u_rows, np32  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -101,6 +101,56 @@ def test_lora_layer_full_oracle(ctx):
     assert np.array_equal(rep["codes"], codes)
     assert lr_err <= 1e-3
     assert abs(res["J"] - ref["J"]) <= 5e-3 * ref["J"]
+
+
+@pytest.mark.timeout(900)
+def test_lora_refine_full_oracle(ctx):
+    """One refinement round on the 2048x2048, r = 64 LoRA layer, step by step:
+    OLrC on the sweep's codes, Bid-Up from there, OLrC on the result, each
+    against the oracle fed the GPU's own inputs; the one-call loop must give
+    the same bits as the steps."""
+    spec = synth.FULL["lora"][0]
+    print("lora_refine: generating", flush=True)
+    lay = synth.layer(spec)
+    Wd, Xd = lay["W"].cuda(), lay["X"].cuda()
+    base = ctx.lora(Wd, Xd, spec.rank, spec.bits, spec.group, spec.block, lam_rel=spec.lam_rel)
+    H64 = ctx.hessian64(Xd)
+    r = spec.rank
+    o1 = ctx.olrc(Wd, H64, r, spec.bits, spec.group, base["codes"], base["scales"], base["zeros"])
+    codes = base["codes"].clone()
+    Jb = ctx.bid_up(Wd, H64, o1["L"], o1["R"], spec.bits, spec.group, spec.block, codes, base["scales"],
+                    base["zeros"])
+    o2 = ctx.olrc(Wd, H64, r, spec.bits, spec.group, codes, base["scales"], base["zeros"])
+    loop = ctx.lora_refine(Wd, Xd, r, spec.bits, spec.group, spec.block, rounds=1, lam_rel=spec.lam_rel)
+    assert torch.equal(loop["codes"], codes)
+    assert torch.equal(loop["L"], o2["L"]) and torch.equal(loop["R"], o2["R"])
+    # the loop's Bid-Up objective starts from OLrC's J; the separate call
+    # recomputes it from the fp32 L, R it is given (same value to rounding)
+    assert loop["trace"][1] == o1["J"] and loop["trace"][3] == o2["J"]
+    assert abs(loop["trace"][2] - Jb) <= 1e-9 * Jb
+    print("lora_refine: oracle", flush=True)
+    H = o.hessian(synth.bits_to_numpy(lay["X"]))
+    Wn = lay["W"].numpy().astype(np.float64)
+    scales = np32(base["scales"])
+    zeros = np32(base["zeros"]).astype(np.float32)
+    c0 = np32(base["codes"])
+    ref1 = o.olrc(Wn, o.dequantize(c0, scales, zeros, spec.group), H, r)
+    C1 = np32(o1["R"]).astype(np.float64).T @ np32(o1["L"]).astype(np.float64).T
+    c1 = np32(codes)
+    bu = o.bid_up(Wn, C1, c0, scales, zeros, H, spec.bits, spec.group, replay=c1, tie_window=TIE)
+    ref2 = o.olrc(Wn, o.dequantize(c1, scales, zeros, spec.group), H, r)
+    C2 = np32(o2["R"]).astype(np.float64).T @ np32(o2["L"]).astype(np.float64).T
+    info = dict(J1=o1["J"], J1_ref=ref1["J"], moves=bu["moves"], forced=bu["forced"], Jb=Jb, Jb_ref=bu["J"],
+                J2=o2["J"], J2_ref=ref2["J"], gap=ref1["eig"][r - 1] / ref1["eig"][r],
+                C1_err=float(np.abs(C1 - ref1["C"]).max() / np.abs(ref1["C"]).max()))
+    print("lora_refine:", info, flush=True)
+    assert abs(o1["J"] - ref1["J"]) <= 1e-6 * ref1["J"]
+    assert info["C1_err"] <= 1e-5
+    assert np.array_equal(bu["codes"], c1) and bu["forced"] <= 2
+    assert abs(Jb - bu["J"]) <= 1e-5 * bu["J"]
+    assert abs(o2["J"] - ref2["J"]) <= 1e-6 * ref2["J"]
+    assert np.abs(C2 - ref2["C"]).max() <= 1e-5 * np.abs(ref2["C"]).max()
+    assert o2["J"] <= Jb * (1 + 1e-9) and Jb <= o1["J"] * (1 + 1e-9) and o1["J"] <= base["J"] * (1 + 1e-9)
 
 
 @pytest.mark.timeout(900)
