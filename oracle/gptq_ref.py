@@ -32,7 +32,12 @@ and ridge (optimal low-rank compensation) closed forms, r = 0 reduction and
 basis invariance; for the refinement loop (tests/test_oracle_refine.py) the
 truncated SVD at H = I, a matrix-square-root route to the same OLrC optimum,
 brute force over the grid for every Bid-Up coordinate decision, the decoupled
-(diagonal H) case reducing to round-to-nearest, and a non-increasing trace.
+(diagonal H) case reducing to round-to-nearest, and a non-increasing trace;
+for two-sided rounding (tests/test_oracle_2d.py) the vectorized sweep with the
+Kronecker Gram ([2D] Theorem 2), a second topological order (Theorem 1), the
+one-sided reductions B = I and A = I, an independently written nearest-plane
+solver on the integer lattice, the identity metric and the objective formed
+from A and B directly.
 
 Parity unpinned (conventions that only self-consistency fixes; the GPU follows
 them exactly): the min-max grid details of ``grid_fit`` (0 inside the range,
@@ -629,3 +634,104 @@ def lora_refine(W, H, r: int, bits: int, group: int = 0, block: int | None = 128
         L, R_out = res["L"], res["R_out"]
     return dict(codes=codes, scales=res["scales"], zeros=res["zeros"], What=What, L=L,
                 R=R_out.T.copy(), R_out=R_out, trace=trace, steps=steps, sweep=res)
+
+
+# --------------------------------------------------------------------------
+# GPTQ-2D: two-sided adaptive rounding
+# --------------------------------------------------------------------------
+def round_1d(x, U, qmin: int, qmax: int, replay=None, tie_window: float = 1e-3) -> dict:
+    """One-sided adaptive rounding of a vector to integers ([2D] section 1:
+    fixed order, rounding error fed forward through a triangular feedback
+    matrix).  U upper with K^{-1} = U^T U for the metric K.  For p in order:
+    z_p = clamp(rne(fl32(w_p)), qmin, qmax), e_p = (w_p - z_p) / U_pp,
+    w[q] -= e_p U_pq for q > p.  sum(e^2) = (x - z)^T K (x - z).
+    ``replay``: integers of another implementation, taken at near-ties.
+    """
+    w = np.array(x, dtype=np.float64, copy=True).ravel()
+    U = np.asarray(U, dtype=np.float64)
+    N = w.size
+    z = np.zeros(N)
+    e = np.zeros(N)
+    forced = 0
+    for p in range(N):
+        v = F32(w[p])
+        q = float(np.clip(np.rint(v), qmin, qmax))
+        if replay is not None:
+            qr = float(np.asarray(replay).ravel()[p])
+            if qr != q and abs(qr - q) == 1 and abs(abs(float(v) - min(qr, q)) - 0.5) < tie_window:
+                q = qr
+                forced += 1
+        z[p] = q
+        e[p] = (w[p] - q) / U[p, p]
+        w[p + 1:] -= e[p] * U[p, p + 1:]
+    return dict(z=z, e=e, J=float(np.sum(e * e)), forced=forced)
+
+
+def round_2d_vectorized(X, UG, UH, qmin: int, qmax: int) -> dict:
+    """Two-sided rounding as the 1D sweep on vec(X) ([2D] section 1):
+    ||A (Z - X) B||_F^2 = ||(B^T kron A)(vec Z - vec X)||^2 has the Gram
+    H kron G (H = B B^T, G = A^T A), and with G^{-1} = UG^T UG,
+    H^{-1} = UH^T UH the feedback factor of (H kron G)^{-1} is UH kron UG.
+    vec stacks columns, so the order is column-major.  O(m^2 n^2): the
+    reference definition, small sizes only.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    m, n = X.shape
+    UK = np.kron(np.asarray(UH, dtype=np.float64), np.asarray(UG, dtype=np.float64))
+    r = round_1d(X.T.ravel(), UK, qmin, qmax)
+    return dict(Z=r["z"].reshape(n, m).T, E=r["e"].reshape(n, m).T, J=r["J"])
+
+
+def round_2d(X, UG, UH, qmin: int, qmax: int, replay=None, tie_window: float = 1e-3) -> dict:
+    """GPTQ-2D: the same rounding trajectory in anti-diagonal stages with lazy
+    buffers, O(mn max(m, n)) ([2D] section 2: Kronecker feedback, rank-1
+    updates on the lower-right rectangle, anti-diagonal independence, the
+    buffer C = L E pushed down columns and then to the right along rows).
+
+    Unit factors: Lg[k, i] = UG[i, k] / UG[i, i] (lower), Uh[j, l] = UH[j, l]
+    / UH[j, j] (upper).  Rounding entry (i, j) with delta = w_ij - z_ij
+    changes w_kl by -Lg[k, i] delta Uh[j, l] for k >= i, l >= j.  Entry (k, l)
+    is reached after every (i, j) with i <= k, j <= l, so its value is
+    x_kl - R_kl - C_kl with
+      C_kl = sum_{i<k} Lg[k, i] delta_il            (pushed down column l)
+      R_kl = sum_{j<l} Cfin_kj Uh[j, l],  Cfin_kj = C_kj + delta_kj
+                                                    (pushed right along row k).
+    Entries on one anti-diagonal k + l = s touch disjoint columns of C and
+    disjoint rows of R, so a stage is parallel.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    UG = np.asarray(UG, dtype=np.float64)
+    UH = np.asarray(UH, dtype=np.float64)
+    m, n = X.shape
+    Lg = (UG / np.diag(UG)[:, None]).T
+    Uh = UH / np.diag(UH)[:, None]
+    C = np.zeros((m, n))
+    R = np.zeros((m, n))
+    Z = np.zeros((m, n))
+    D = np.zeros((m, n))
+    forced = 0
+    for s in range(m + n - 1):
+        for k in range(max(0, s - n + 1), min(m, s + 1)):
+            l = s - k
+            w = X[k, l] - R[k, l] - C[k, l]
+            v = F32(w)
+            q = float(np.clip(np.rint(v), qmin, qmax))
+            if replay is not None:
+                qr = float(np.asarray(replay)[k, l])
+                if qr != q and abs(qr - q) == 1 and abs(abs(float(v) - min(qr, q)) - 0.5) < tie_window:
+                    q = qr
+                    forced += 1
+            d = w - q
+            Z[k, l] = q
+            D[k, l] = d
+            C[k + 1:, l] += Lg[k + 1:, k] * d
+            cfin = C[k, l] + d
+            R[k, l + 1:] += cfin * Uh[l, l + 1:]
+    E = D / np.outer(np.diag(UG), np.diag(UH))
+    return dict(Z=Z, E=E, delta=D, J=float(np.sum(E * E)), forced=forced)
+
+
+def objective_2d(X, Z, G, H) -> float:
+    """||A (Z - X) B||_F^2 = tr((Z - X)^T G (Z - X) H) for G = A^T A, H = B B^T."""
+    D = np.asarray(Z, dtype=np.float64) - np.asarray(X, dtype=np.float64)
+    return float(np.sum((G @ D @ H) * D))
