@@ -187,6 +187,25 @@ int gptq_lora_refine(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const
                      int32_t block, double lam_abs, double lam_rel, int32_t rounds, uint8_t* codes,
                      float* scales, uint8_t* zeros, float* L, float* R, double* trace, int32_t* info);
 
+/* Two-sided adaptive rounding, GPTQ-2D (GPTQ-2D technical summary): integers
+ * Z minimising ||A (Z - X) B||_F^2 greedily, with exactly the trajectory of
+ * the one-sided sweep over vec(X) (column-major) under the Gram H kron G,
+ * G = A^T A, H = B B^T (section 1; Theorem 2: same result in any order that
+ * respects the dependencies, here anti-diagonals).  Rounding entry (i, j)
+ * with delta = w_ij - z_ij, z_ij = clamp(rne(fl32(w_ij)), qmin, qmax), feeds
+ * -Lg[k][i] delta Uh[j][l] to the entries k >= i, l >= j, with the unit
+ * factors Lg[k][i] = UG[i][k] / UG[i][i], Uh[j][l] = UH[j][l] / UH[j][j]
+ * (section 2: Kronecker feedback, rank-1 updates, the lazy buffer C = L E).
+ * Inputs (device, fp32, row-major): X[m][n] the real target; UG[m][m] and
+ * UH[n][n] upper with G^{-1} = UG^T UG, H^{-1} = UH^T UH (gptq_factor of G
+ * and of H, with or without damping).  Outputs: Z[m][n] int32 in [qmin,
+ * qmax]; delta[m][n] fp32 the rounding residuals w - z (may be NULL);
+ * J [host] = sum of (delta_ij / (UG_ii UH_jj))^2 = ||A (Z - X) B||_F^2 for
+ * the G, H the factors belong to.  The rounding decisions are taken in fp32
+ * and the feedback accumulates in fp32.  SYNC. */
+int gptq_round_2d(gptq_ctx ctx, const float* X, int32_t m, int32_t n, const float* UG, const float* UH,
+                  int32_t qmin, int32_t qmax, int32_t* Z, float* delta, double* J);
+
 /* One layer of a batch.  X may be NULL: then H must already hold the layer's
  * Hessian (several layers may point at the same H and X == NULL to share it).
  * H and U are caller-provided [n][n] fp32 buffers (H is written when X != NULL).
@@ -229,7 +248,8 @@ int gptq_quantize_batched(gptq_ctx ctx, int32_t nlayers, gptq_layer* layers);
  * k_make_u, k_init_work, k_rowfit, k_sweep, k_trail, k_objective, and for the
  * LoRA and refinement paths k_lora_lambda, k_start_block, k_dgemm, k_dsum,
  * k_gram_chol, k_apply, k_lora_assemble, k_lora_extract, k_ref_init, k_resid,
- * k_gfinal, k_sum_parts, k_f32_to_f64, k_f64_to_f32, k_olrc_out.  gptq_kernel_time
+ * k_gfinal, k_sum_parts, k_f32_to_f64, k_f64_to_f32, k_olrc_out, and for the
+ * two-sided rounding k_r2d_unit, k_r2d_fill, k_r2d_tile, k_r2d_push, k_r2d_obj.  gptq_kernel_time
  * waits for the recorded events and returns the summed elapsed milliseconds
  * and the number of timed launches of kernel `name` (0 and 0 if none).  Each
  * timed launch costs two event records on the stream. */

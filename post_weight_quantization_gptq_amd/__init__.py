@@ -101,11 +101,12 @@ def load_library(path: str | None = None):
     L.gptq_olrc.argtypes = [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(d)]
     L.gptq_bid_up.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp,
                               ctypes.POINTER(d)]
+    L.gptq_round_2d.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, vp, vp, ctypes.POINTER(d)]
     L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
     L.gptq_timing.argtypes = [vp, ctypes.c_char_p]
     L.gptq_kernel_time.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(d), ctypes.POINTER(i64)]
     for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
-                 "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up",
+                 "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up", "gptq_round_2d",
                  "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
         getattr(L, name).restype = ctypes.c_int
     if path is None:
@@ -346,6 +347,21 @@ class Context:
                                          int(bits), int(group), int(block), _ptr(codes), _ptr(scales), _ptr(zeros),
                                          ctypes.byref(J)))
         return J.value
+
+    def round_2d(self, X, UG, UH, qmin: int, qmax: int, want_delta: bool = False):
+        """GPTQ-2D two-sided rounding of X [m, n] with the factors UG [m, m], UH [n, n].
+        Returns dict(Z int32 [m, n], delta fp32 [m, n] or None, J)."""
+        torch = self.torch
+        self._dev(X, torch.float32, "X")
+        self._dev(UG, torch.float32, "UG")
+        self._dev(UH, torch.float32, "UH")
+        m, n = X.shape
+        Z = torch.empty((m, n), dtype=torch.int32, device=self.device)
+        D = torch.empty((m, n), dtype=torch.float32, device=self.device) if want_delta else None
+        J = ctypes.c_double(0.0)
+        self._check(self.lib.gptq_round_2d(self.handle, _ptr(X), m, n, _ptr(UG), _ptr(UH), int(qmin), int(qmax),
+                                           _ptr(Z), _ptr(D), ctypes.byref(J)))
+        return dict(Z=Z, delta=D, J=J.value)
 
     def quantize_batched(self, layers):
         """layers: list of dicts with W, bits, group, block, lam_rel (and X or H, optional lam_abs,

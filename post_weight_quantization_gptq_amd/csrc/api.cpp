@@ -34,7 +34,7 @@ struct gptq_ctx_s {
   int ncu = 256;
   int nxcd = 8;
   std::string err;
-  DevBuf partials, xt, facA, facY, work, eblk, objp, dinv, slots, blob, lora;
+  DevBuf partials, xt, facA, facY, work, eblk, objp, dinv, slots, blob, lora, r2d;
   void* hblob = nullptr;  // pinned staging for the task tables
   size_t hblob_cap = 0;
   void* hsmall = nullptr;  // pinned read-back area
@@ -902,7 +902,7 @@ GPTQ_API int gptq_destroy(gptq_ctx c) {
     (void)hipStreamSynchronize(c->stream);
     if (c->side) (void)hipStreamSynchronize(c->side);
     DevBuf* bufs[] = {&c->partials, &c->xt, &c->facA, &c->facY, &c->work, &c->eblk, &c->dinv,
-                      &c->objp, &c->slots, &c->blob, &c->lora};
+                      &c->objp, &c->slots, &c->blob, &c->lora, &c->r2d};
     for (DevBuf* b : bufs)
       if (b->p) (void)hipFree(b->p);
     if (c->hblob) (void)hipHostFree(c->hblob);
@@ -1212,6 +1212,66 @@ int refine_step(gptq_ctx c, bool bid, const float* W, int32_t out, int32_t n, co
 }
 
 }  // namespace
+
+GPTQ_API int gptq_round_2d(gptq_ctx c, const float* X, int32_t m, int32_t n, const float* UG, const float* UH,
+                           int32_t qmin, int32_t qmax, int32_t* Z, float* delta, double* J) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (J) *J = 0.0;
+  if (m < 0 || n < 0 || !J || (m > 0 && n > 0 && (!X || !UG || !UH || !Z)))
+    return set_err(c, GPTQ_ERR_INVALID_ARG, "bad two-sided rounding arguments");
+  if (qmin > qmax) return set_err(c, GPTQ_ERR_INVALID_ARG, "qmin > qmax");
+  if (m == 0 || n == 0) return GPTQ_OK;
+  DeviceGuard g(c->device);
+  const int TM = cdiv(m, 64), TN = cdiv(n, 64);
+  const size_t mn = (size_t)m * n;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t oL = take((size_t)m * m * 4), oU = take((size_t)n * n * 4), odG = take((size_t)m * 4),
+               odH = take((size_t)n * 4), oC = take(mn * 4), oR = take(mn * 4), oD = take(mn * 4), oCf = take(mn * 4),
+               oO = take((size_t)TM * TN * 8), oJ = take(8);
+  int rc = ensure(c, c->r2d, off);
+  if (rc) return rc;
+  uint8_t* base = (uint8_t*)c->r2d.p;
+  R2dProb p;
+  p.X = X;
+  p.Lgt = (const float*)(base + oL);
+  p.Uh1 = (const float*)(base + oU);
+  p.dG = (const float*)(base + odG);
+  p.dH = (const float*)(base + odH);
+  p.C = (float*)(base + oC);
+  p.R = (float*)(base + oR);
+  p.D = delta ? delta : (float*)(base + oD);
+  p.Cf = (float*)(base + oCf);
+  p.Z = Z;
+  p.objp = (double*)(base + oO);
+  p.m = m;
+  p.n = n;
+  p.qmin = qmin;
+  p.qmax = qmax;
+  double* dJ = (double*)(base + oJ);
+  LAUNCH(c, "k_r2d_unit", launch_r2d_unit(UG, m, (float*)p.Lgt, (float*)p.dG, c->stream));
+  LAUNCH(c, "k_r2d_unit", launch_r2d_unit(UH, n, (float*)p.Uh1, (float*)p.dH, c->stream));
+  LAUNCH(c, "k_r2d_fill", launch_r2d_fill(p.C, p.R, (long long)mn, c->stream));
+  // anti-diagonals of 64 x 64 tiles: the stage's tiles, then their pushes
+  for (int S = 0; S < TM + TN - 1; ++S) {
+    const int Ib = std::max(0, S - TN + 1), Ie = std::min(TM - 1, S);
+    LAUNCH(c, "k_r2d_tile", launch_r2d_tile(p, S, Ib, Ie - Ib + 1, c->stream));
+    int items = 0;
+    for (int I = Ib; I <= Ie; ++I) items += (TM - I - 1) + (TN - (S - I) - 1);
+    LAUNCH(c, "k_r2d_push", launch_r2d_push(p, S, Ib, Ie, items, c->stream));
+  }
+  LAUNCH(c, "k_r2d_obj", launch_r2d_obj(p.objp, TM * TN, dJ, c->stream));
+  if ((rc = ensure_small(c, sizeof(double)))) return rc;
+  HIPCHK(c, hipMemcpyAsync(c->hsmall, dJ, sizeof(double), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  *J = *(const double*)c->hsmall;
+  return GPTQ_OK;
+}
 
 GPTQ_API int gptq_lora(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t* X,
                        int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,

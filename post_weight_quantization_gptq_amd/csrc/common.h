@@ -92,6 +92,23 @@ struct FacProb {
 //   the flags info / nonfinite are not consulted).
 enum GemmKind { GK_CHOL_TRAIL = 0, GK_ZUPD = 1, GK_NT = 2 };
 
+// -------------------------------------------------------- two-sided round --
+// GPTQ-2D state (all [m][n] row-major unless noted); see round2d.hip.
+struct R2dProb {
+  const float* X;    // target
+  const float* Lgt;  // [m][m]: UG[i][k] / UG[i][i] for k >= i (row i = column i of the unit lower Lg)
+  const float* Uh1;  // [n][n]: UH[j][l] / UH[j][j] for l >= j
+  const float* dG;   // [m] UG[i][i]
+  const float* dH;   // [n] UH[j][j]
+  float* C;          // pushes down the columns from the tiles above
+  float* R;          // pushes along the rows from the tiles to the left
+  float* D;          // delta = w - z
+  float* Cf;         // C + delta, what a finished entry pushes right
+  int* Z;            // the integers
+  double* objp;      // [TM][TN] per-tile sums of squared scaled errors
+  int m, n, qmin, qmax;
+};
+
 // ------------------------------------------------------------------ sweep --
 struct QLayer {
   const float* W;   // original weights [out][n]

@@ -33,3 +33,10 @@ hipError_t launch_sweep(int block, int mode, const QLayer* L, const Seg* segs, i
 // at most maxwg workgroups (0: one per tile), persistent over the nwg tiles
 hipError_t launch_trail(int ts, const QLayer* L, const Seg* segs, int nseg, int nwg, int maxwg, hipStream_t st);
 hipError_t launch_objective(const QLayer* L, int nl, hipStream_t st);
+
+// two-sided rounding (round2d.hip)
+hipError_t launch_r2d_unit(const float* U, int n, float* U1, float* d, hipStream_t st);
+hipError_t launch_r2d_fill(float* a, float* b, long long cnt, hipStream_t st);
+hipError_t launch_r2d_tile(const R2dProb& p, int S, int Ibeg, int ntiles, hipStream_t st);
+hipError_t launch_r2d_push(const R2dProb& p, int S, int Ibeg, int Iend, int nitems, hipStream_t st);
+hipError_t launch_r2d_obj(const double* objp, int nt, double* J, hipStream_t st);

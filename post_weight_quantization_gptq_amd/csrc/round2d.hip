@@ -1,0 +1,232 @@
+// Two-sided adaptive rounding, GPTQ-2D (GPTQ-2D technical summary).
+//
+// Problem (section 1): integers Z minimising ||A (Z - X) B||_F^2, i.e. the
+// one-sided sweep over vec(X) with the Gram H kron G (G = A^T A, H = B B^T),
+// whose feedback factor is UH kron UG (G^{-1} = UG^T UG, H^{-1} = UH^T UH).
+// Rounding entry (i, j) with delta = w_ij - z_ij changes w_kl by
+// -Lg[k][i] delta Uh[j][l] on the lower-right rectangle k >= i, l >= j, with
+// the unit factors Lg[k][i] = UG[i][k] / UG[i][i] and Uh[j][l] = UH[j][l] /
+// UH[j][j] (section 2: Kronecker feedback, rank-1 updates).  Entry (k, l) is
+// reached after every (i, j) with i <= k, j <= l, so its value is
+// x_kl - R_kl - C_kl with the lazy buffers (section 2: C = L E pushed down
+// the columns, then to the right along the rows)
+//   C_kl = sum_{i<k} Lg[k][i] delta_il,
+//   R_kl = sum_{j<l} Cf_kj Uh[j][l],   Cf_kj = C_kj + delta_kj,
+// and every entry is pushed once down its column and once along its row:
+// O(mn max(m, n)) work.  Entries on one anti-diagonal are independent.
+//
+// On the GPU the matrix is cut into 64 x 64 tiles processed by anti-diagonals
+// of tiles (the blocked form of section 2 / Algorithm 4: groups of
+// anti-diagonals, the rest of the matrix updated by products):
+//   k_r2d_tile: one workgroup per tile of the stage; the tile's C, R, the
+//     target and the diagonal blocks of Lg and Uh sit in LDS, and the
+//     workgroup walks the tile's own anti-diagonals (4 threads per entry),
+//     pushing inside the tile only;
+//   k_r2d_push: the stage's deltas pushed down to every tile below
+//     (C += Lg Delta) and its final C to every tile on the right
+//     (R += Cf Uh), one 64 x 64 output tile per workgroup on fp32 MFMA.
+// Tiles of one stage write disjoint column blocks of C and disjoint row
+// blocks of R, so nothing races; the next stage's tiles read only finished
+// pushes (stream order).
+#include "common.h"
+#include "launch.h"
+
+#define T2 64
+#define T2P (T2 + 1)
+
+// U1[i][k] = U[i][k] / U[i][i] for k >= i, 0 below; d[i] = U[i][i]
+__global__ __launch_bounds__(256) void k_r2d_unit(const float* __restrict__ U, int n, float* __restrict__ U1,
+                                                  float* __restrict__ d) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)n * n) return;
+  const int i = (int)(e / n), k = (int)(e % n);
+  const float di = U[(size_t)i * n + i];
+  U1[e] = k >= i ? U[e] / di : 0.f;
+  if (k == i) d[i] = di;
+}
+
+__global__ __launch_bounds__(256) void k_r2d_fill(float* __restrict__ a, float* __restrict__ b, long long cnt) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e < cnt) {
+    a[e] = 0.f;
+    b[e] = 0.f;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_r2d_tile(R2dProb p, int S, int Ibeg) {
+  __shared__ float Xs[T2][T2P], Cl[T2][T2P], Rl[T2][T2P], Lk[T2][T2P], Uk[T2][T2P];
+  __shared__ double red[256];
+  const int TN = (p.n + T2 - 1) / T2;
+  const int I = Ibeg + blockIdx.x, J = S - I;
+  const int r0 = I * T2, c0 = J * T2;
+  const int mt = min(T2, p.m - r0), nt = min(T2, p.n - c0);
+  const int tid = threadIdx.x;
+  // Lk[i][k] = Lg[r0 + k][r0 + i] (row i: what entry row i pushes down);
+  // Uk[j][l] = Uh[c0 + j][c0 + l] (row j: what column j pushes right)
+  for (int e = tid; e < T2 * T2; e += 256) {
+    const int a = e >> 6, b = e & 63;
+    const bool in = a < mt && b < nt;
+    const size_t g = (size_t)(r0 + a) * p.n + c0 + b;
+    Xs[a][b] = in ? p.X[g] : 0.f;
+    Cl[a][b] = in ? p.C[g] : 0.f;
+    Rl[a][b] = in ? p.R[g] : 0.f;
+    Lk[a][b] = (a < mt && b < mt) ? p.Lgt[(size_t)(r0 + a) * p.m + r0 + b] : 0.f;
+    Uk[a][b] = (a < nt && b < nt) ? p.Uh1[(size_t)(c0 + a) * p.n + c0 + b] : 0.f;
+  }
+  __syncthreads();
+  const int ent = tid >> 2, part = tid & 3;
+  const float qmin = (float)p.qmin, qmax = (float)p.qmax;
+  double se = 0.0;
+  for (int s = 0; s < mt + nt - 1; ++s) {
+    const int k = max(0, s - nt + 1) + ent;
+    if (k <= min(mt - 1, s)) {
+      const int l = s - k;
+      const float c = Cl[k][l];
+      const float w = Xs[k][l] - (Rl[k][l] + c);
+      const float q = fminf(fmaxf(rintf(w), qmin), qmax);
+      const float d = w - q;
+      const float cf = c + d;
+      for (int k2 = k + 1 + part; k2 < mt; k2 += 4) Cl[k2][l] = fmaf(Lk[k][k2], d, Cl[k2][l]);
+      for (int l2 = l + 1 + part; l2 < nt; l2 += 4) Rl[k][l2] = fmaf(cf, Uk[l][l2], Rl[k][l2]);
+      if (part == 0) {
+        const size_t g = (size_t)(r0 + k) * p.n + c0 + l;
+        p.Z[g] = (int)q;
+        p.D[g] = d;
+        p.Cf[g] = cf;
+        const double es = (double)d / ((double)p.dG[r0 + k] * (double)p.dH[c0 + l]);
+        se += es * es;
+      }
+    }
+    __syncthreads();
+  }
+  red[tid] = se;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (tid < k) red[tid] += red[tid + k];
+    __syncthreads();
+  }
+  if (tid == 0) p.objp[(size_t)I * TN + J] = red[0];
+}
+
+// One 64 x 64 output tile of a push of stage S:
+//   kind 0, tile (I, J), row block K > I:    C[K][J] += Lg[K][I] D[I][J]
+//   kind 1, tile (I, J), column block L > J: R[I][L] += Cf[I][J] Uh[J][L]
+// K = 64 on v_mfma_f32_32x32x2f32, 4 waves of 32 x 32.
+__global__ __launch_bounds__(256) void k_r2d_push(R2dProb p, int S, int Ibeg, int Iend) {
+  __shared__ float As[T2][T2P];  // [t][r]
+  __shared__ float Bs[T2][T2P];  // [t][c]
+  const int TM = (p.m + T2 - 1) / T2, TN = (p.n + T2 - 1) / T2;
+  int item = blockIdx.x, I = Ibeg, kind = 0, blk = 0;
+  for (; I <= Iend; ++I) {
+    const int nc = TM - I - 1, nr = TN - (S - I) - 1;
+    if (item < nc) {
+      kind = 0;
+      blk = I + 1 + item;
+      break;
+    }
+    item -= nc;
+    if (item < nr) {
+      kind = 1;
+      blk = S - I + 1 + item;
+      break;
+    }
+    item -= nr;
+  }
+  if (I > Iend) return;
+  const int J = S - I;
+  const int r0 = I * T2, c0 = J * T2;
+  const int mtI = min(T2, p.m - r0), ntJ = min(T2, p.n - c0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
+  float* out;
+  int orows, ocols;  // output tile extent
+  if (kind == 0) {
+    const int k0 = blk * T2;
+    orows = min(T2, p.m - k0);
+    ocols = ntJ;
+    // A(r, t) = Lg[k0 + r][r0 + t] = Lgt[r0 + t][k0 + r]; B(t, c) = D[r0 + t][c0 + c]
+    for (int e = tid; e < T2 * T2; e += 256) {
+      const int t = e >> 6, x = e & 63;
+      As[t][x] = (t < mtI && x < orows) ? p.Lgt[(size_t)(r0 + t) * p.m + k0 + x] : 0.f;
+      Bs[t][x] = (t < mtI && x < ocols) ? p.D[(size_t)(r0 + t) * p.n + c0 + x] : 0.f;
+    }
+    out = p.C + (size_t)k0 * p.n + c0;
+  } else {
+    const int l0 = blk * T2;
+    orows = mtI;
+    ocols = min(T2, p.n - l0);
+    // A(r, t) = Cf[r0 + r][c0 + t]; B(t, c) = Uh[c0 + t][l0 + c]
+    for (int e = tid; e < T2 * T2; e += 256) {
+      const int a = e >> 6, b = e & 63;
+      As[b][a] = (a < orows && b < ntJ) ? p.Cf[(size_t)(r0 + a) * p.n + c0 + b] : 0.f;
+      Bs[a][b] = (a < ntJ && b < ocols) ? p.Uh1[(size_t)(c0 + a) * p.n + l0 + b] : 0.f;
+    }
+    out = p.R + (size_t)r0 * p.n + l0;
+  }
+  __syncthreads();
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll 8
+  for (int kk = 0; kk < T2 / 2; ++kk) {
+    const float a = As[2 * kk + (lane >> 5)][32 * wr + (lane & 31)];
+    const float b = Bs[2 * kk + (lane >> 5)][32 * wc + (lane & 31)];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+  }
+  float cur[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 32 * wr + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    const int j = 32 * wc + (lane & 31);
+    cur[r] = (i < orows && j < ocols) ? out[(size_t)i * p.n + j] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 32 * wr + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    const int j = 32 * wc + (lane & 31);
+    if (i < orows && j < ocols) out[(size_t)i * p.n + j] = cur[r] + acc[r];
+  }
+}
+
+// J = sum of the tiles' partial sums, in tile order
+__global__ __launch_bounds__(256) void k_r2d_obj(const double* __restrict__ objp, int nt, double* __restrict__ J) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < nt; i += 256) s += objp[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *J = red[0];
+}
+
+hipError_t launch_r2d_unit(const float* U, int n, float* U1, float* d, hipStream_t st) {
+  const long long cnt = (long long)n * n;
+  if (cnt == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_r2d_unit, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, U, n, U1, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_r2d_fill(float* a, float* b, long long cnt, hipStream_t st) {
+  if (cnt == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_r2d_fill, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, a, b, cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_r2d_tile(const R2dProb& p, int S, int Ibeg, int ntiles, hipStream_t st) {
+  if (ntiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_r2d_tile, dim3(ntiles), dim3(256), 0, st, p, S, Ibeg);
+  return hipGetLastError();
+}
+
+hipError_t launch_r2d_push(const R2dProb& p, int S, int Ibeg, int Iend, int nitems, hipStream_t st) {
+  if (nitems <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_r2d_push, dim3(nitems), dim3(256), 0, st, p, S, Ibeg, Iend);
+  return hipGetLastError();
+}
+
+hipError_t launch_r2d_obj(const double* objp, int nt, double* J, hipStream_t st) {
+  hipLaunchKernelGGL(k_r2d_obj, dim3(1), dim3(256), 0, st, objp, nt, J);
+  return hipGetLastError();
+}
