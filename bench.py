@@ -89,12 +89,101 @@ def syrk_traffic(workload):
         return None
 
 
+PEAK_FP32_MATRIX_TFLOPS = 157.3  # dense fp32 MFMA, MI355X
+R2D_KERNELS = ["k_damp_lambda", "k_damp_fill", "k_chol_panel", "k_chol_panel2", "k_gemm64", "k_gemm_ring64",
+               "k_gemm_ring128", "k_make_u", "k_r2d_unit", "k_r2d_fill", "k_r2d_tile", "k_r2d_push", "k_r2d_obj"]
+
+
+def bench_r2d(args, torch, Context, synth, dev):
+    """Two-sided rounding (GPTQ-2D) of the square layer: target W / s on a
+    signed 4-bit range, H = the layer's input Gram on the right, G = the Gram
+    of a second seeded 4096-wide matrix on the left.  A step is both damped
+    factors plus the rounding; the Grams are formed once before timing."""
+    sq, og = synth.FULL["r2d"]
+    print("# generating r2d inputs", file=sys.stderr, flush=True)
+    lay = synth.layer(sq, dev)
+    Xo = synth.calibration(og, dev)
+    torch.cuda.synchronize()
+    ctx = Context(dev)
+    H = ctx.hessian(lay["X"])
+    G = ctx.hessian(Xo)
+    del Xo
+    W = lay["W"]
+    X2 = (W / (W.abs().max() / 7.5)).contiguous()
+    m, n = X2.shape
+    st = torch.cuda.current_stream(dev)
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record(st)
+        UG, _, _ = ctx.factor(G, lam_rel=0.01)
+        UH, _, _ = ctx.factor(H, lam_rel=0.01)
+        if ev is not None:
+            ev[1].record(st)
+        r = ctx.round_2d(X2, UG, UH, -8, 7)
+        if ev is not None:
+            ev[2].record(st)
+        return r
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ctx.timing("k_r2d_push,k_r2d_tile")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    last = None
+    for k in range(args.steps):
+        last = one_step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    push_ms, push_n = ctx.kernel_time("k_r2d_push")
+    tile_ms, tile_n = ctx.kernel_time("k_r2d_tile")
+    ctx.timing("*")
+    one_step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for nm in R2D_KERNELS:
+        ms, cnt = ctx.kernel_time(nm)
+        if cnt:
+            breakdown[nm] = {"ms": round(ms, 4), "launches": cnt}
+    ctx.timing(None)
+    ms_step = 1e3 * wall / args.steps
+    fac = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    rnd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    # algorithmic work of the pushes between tiles: every (tile, tile below)
+    # and (tile, tile to the right) pair is one dense 64x64x64 product
+    TM, TN = (m + 63) // 64, (n + 63) // 64
+    pairs = sum((TM - I - 1) + (TN - J - 1) for I in range(TM) for J in range(TN))
+    push_flops = pairs * 2 * 64 ** 3
+    ach = push_flops * args.steps / (push_ms * 1e-3) / 1e12 if push_ms else 0.0
+    line = {"metric": "ms per layer, two-sided rounding (GPTQ-2D) of a 4096x4096 layer", "value": round(ms_step, 4),
+            "unit": "ms/layer", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic (seeded; the square layer and a second 4096-wide input)",
+            "config": {"workload": "r2d: X = W/s [4096,4096] -> Z in [-8,7]; G from Y[65536,4096], "
+                                   "H from X[262144,4096], lam 0.01 mean diag"},
+            "stages_ms": {"factors": round(fac, 4), "round_2d": round(rnd, 4)},
+            "kernels_one_step": breakdown,
+            "roofline": {"kernel": "k_r2d_push", "bound": "mfma", "achieved": round(ach, 2),
+                         "peak": PEAK_FP32_MATRIX_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / PEAK_FP32_MATRIX_TFLOPS, 4), "traffic": None,
+                         "avg_launch_ms": round(push_ms / max(push_n, 1), 4),
+                         "flops_per_step": push_flops},
+            "tile_kernel": {"launches_per_step": tile_n // max(args.steps, 1),
+                            "avg_launch_ms": round(tile_ms / max(tile_n, 1), 4)},
+            "objective": {"J": last["J"]}}
+    ctx.close()
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="square", choices=["square", "single", "lora", "lora_refine", "mlp", "vit"])
+    ap.add_argument("--workload", default="square",
+                    choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d"])
     ap.add_argument("--rounds", type=int, default=1, help="refinement rounds of the lora_refine workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -119,6 +208,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "launches": 5}), flush=True)
+        return
+    if args.workload == "r2d":
+        bench_r2d(args, torch, Context, synth, dev)
         return
     specs = synth.FULL["lora" if args.workload == "lora_refine" else args.workload]
     print("# generating %s inputs" % args.workload, file=sys.stderr, flush=True)

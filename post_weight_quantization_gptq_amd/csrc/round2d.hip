@@ -18,10 +18,9 @@
 // On the GPU the matrix is cut into 64 x 64 tiles processed by anti-diagonals
 // of tiles (the blocked form of section 2 / Algorithm 4: groups of
 // anti-diagonals, the rest of the matrix updated by products):
-//   k_r2d_tile: one workgroup per tile of the stage; the tile's C, R, the
-//     target and the diagonal blocks of Lg and Uh sit in LDS, and the
-//     workgroup walks the tile's own anti-diagonals (4 threads per entry),
-//     pushing inside the tile only;
+//   k_r2d_tile: one workgroup per tile of the stage, four lanes per row of
+//     the tile; the workgroup walks the tile's own anti-diagonals, pushing
+//     inside the tile only;
 //   k_r2d_push: the stage's deltas pushed down to every tile below
 //     (C += Lg Delta) and its final C to every tile on the right
 //     (R += Cf Uh), one 64 x 64 output tile per workgroup on fp32 MFMA.
@@ -53,56 +52,98 @@ __global__ __launch_bounds__(256) void k_r2d_fill(float* __restrict__ a, float* 
   }
 }
 
+// In-tile layout: the four lanes of row group k own row k of the tile.  At
+// inner stage s the row processes column l = s - k (anti-diagonal order).
+// What only row k reads stays in its registers: lane p holds the row's R
+// for columns p + 4u and the row's column-push multipliers Lg[r0 + k2][r0 +
+// k] for k2 = k + 1 + p + 4u.  What passes between rows sits in LDS: the
+// column buffer C (column-major, Ct[l][k]), the target and row l of Uh.  All
+// LDS arrays have a pitch of 69 words: along an anti-diagonal the addresses
+// step by 68 = 4 * 17 words, which spreads a wave's 16 rows x 4 lanes over
+// the banks (a pitch of 65 would put all 16 rows on one bank).  Indices past
+// a ragged tile are clamped to column 64, the padding, which no decision
+// reads, so the pushes are branch-free.
+#define T2L 69
+
 __global__ __launch_bounds__(256) void k_r2d_tile(R2dProb p, int S, int Ibeg) {
-  __shared__ float Xs[T2][T2P], Cl[T2][T2P], Rl[T2][T2P], Lk[T2][T2P], Uk[T2][T2P];
+  __shared__ float Xs[T2][T2L], Ct[T2][T2L], Uk[T2][T2L];
+  // the tile's results stay in LDS until the walk ends: a barrier waits for
+  // every outstanding memory operation, so a global store inside the walk
+  // would add a memory round trip to each of its stages
+  __shared__ float Qs[T2][T2L], Ds[T2][T2L], Fs[T2][T2L];
   __shared__ double red[256];
   const int TN = (p.n + T2 - 1) / T2;
   const int I = Ibeg + blockIdx.x, J = S - I;
   const int r0 = I * T2, c0 = J * T2;
   const int mt = min(T2, p.m - r0), nt = min(T2, p.n - c0);
-  const int tid = threadIdx.x;
-  // Lk[i][k] = Lg[r0 + k][r0 + i] (row i: what entry row i pushes down);
-  // Uk[j][l] = Uh[c0 + j][c0 + l] (row j: what column j pushes right)
+  const int tid = threadIdx.x, lane = tid & 63;
   for (int e = tid; e < T2 * T2; e += 256) {
     const int a = e >> 6, b = e & 63;
     const bool in = a < mt && b < nt;
     const size_t g = (size_t)(r0 + a) * p.n + c0 + b;
     Xs[a][b] = in ? p.X[g] : 0.f;
-    Cl[a][b] = in ? p.C[g] : 0.f;
-    Rl[a][b] = in ? p.R[g] : 0.f;
-    Lk[a][b] = (a < mt && b < mt) ? p.Lgt[(size_t)(r0 + a) * p.m + r0 + b] : 0.f;
+    Ct[b][a] = in ? p.C[g] : 0.f;
     Uk[a][b] = (a < nt && b < nt) ? p.Uh1[(size_t)(c0 + a) * p.n + c0 + b] : 0.f;
   }
+  const int k = tid >> 2, part = tid & 3;
+  float rrow[16], lrow[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int c = part + 4 * u, k2 = k + 1 + part + 4 * u;
+    rrow[u] = (k < mt && c < nt) ? p.R[(size_t)(r0 + k) * p.n + c0 + c] : 0.f;
+    lrow[u] = (k < mt && k2 < mt) ? p.Lgt[(size_t)(r0 + k) * p.m + r0 + k2] : 0.f;
+  }
   __syncthreads();
-  const int ent = tid >> 2, part = tid & 3;
   const float qmin = (float)p.qmin, qmax = (float)p.qmax;
-  double se = 0.0;
   for (int s = 0; s < mt + nt - 1; ++s) {
-    const int k = max(0, s - nt + 1) + ent;
-    if (k <= min(mt - 1, s)) {
-      const int l = s - k;
-      const float c = Cl[k][l];
-      const float w = Xs[k][l] - (Rl[k][l] + c);
-      const float q = fminf(fmaxf(rintf(w), qmin), qmax);
-      const float d = w - q;
+    const int l = s - k;
+    if (k < mt && l >= 0 && l < nt) {
+      // R_kl from the owner lane (l % 4) of the row group
+      float rs = rrow[0];
+#pragma unroll
+      for (int u = 1; u < 16; ++u) rs = (u == (l >> 2)) ? rrow[u] : rs;
+      const float r = __shfl(rs, (lane & ~3) | (l & 3), 64);
+      const float c = Ct[l][k];
+      const float wv = Xs[k][l] - (r + c);
+      const float q = fminf(fmaxf(rintf(wv), qmin), qmax);
+      const float d = wv - q;
       const float cf = c + d;
-      for (int k2 = k + 1 + part; k2 < mt; k2 += 4) Cl[k2][l] = fmaf(Lk[k][k2], d, Cl[k2][l]);
-      for (int l2 = l + 1 + part; l2 < nt; l2 += 4) Rl[k][l2] = fmaf(cf, Uk[l][l2], Rl[k][l2]);
+      // column push: C[k2][l] += Lg[k2][k] d for the rows below
+      float cv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) cv[u] = Ct[l][min(k + 1 + part + 4 * u, T2)];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) Ct[l][min(k + 1 + part + 4 * u, T2)] = fmaf(lrow[u], d, cv[u]);
+      // row push: R[k][c] += Cf_kl Uh[l][c] for the columns right of l.
+      // Applied to every column of the row: Uh[l][c] is 0 left of l, and
+      // column l itself (Uh[l][l] = 1) has just been read for the last time.
+#pragma unroll
+      for (int u = 0; u < 16; ++u) rrow[u] = fmaf(cf, Uk[l][part + 4 * u], rrow[u]);
       if (part == 0) {
-        const size_t g = (size_t)(r0 + k) * p.n + c0 + l;
-        p.Z[g] = (int)q;
-        p.D[g] = d;
-        p.Cf[g] = cf;
-        const double es = (double)d / ((double)p.dG[r0 + k] * (double)p.dH[c0 + l]);
-        se += es * es;
+        Qs[k][l] = q;
+        Ds[k][l] = d;
+        Fs[k][l] = cf;
       }
     }
     __syncthreads();
   }
+  double se = 0.0;
+  for (int e = tid; e < T2 * T2; e += 256) {
+    const int a = e >> 6, b = e & 63;
+    if (a < mt && b < nt) {
+      const size_t g = (size_t)(r0 + a) * p.n + c0 + b;
+      const float d = Ds[a][b];
+      p.Z[g] = (int)Qs[a][b];
+      p.D[g] = d;
+      p.Cf[g] = Fs[a][b];
+      const double es = (double)d / ((double)p.dG[r0 + a] * (double)p.dH[c0 + b]);
+      se += es * es;
+    }
+  }
   red[tid] = se;
   __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (tid < k) red[tid] += red[tid + k];
+  for (int kk = 128; kk > 0; kk >>= 1) {
+    if (tid < kk) red[tid] += red[tid + kk];
     __syncthreads();
   }
   if (tid == 0) p.objp[(size_t)I * TN + J] = red[0];

@@ -21,6 +21,8 @@ columns sign-fixed by sign(diag R)):
   vit       12 x {qkv [2304, 768], proj [768, 768], fc1 [3072, 768],
             fc2 [768, 3072]}; one X per layer, [50176, 768] or [50176, 3072],
             (Z * i^-1/2) Q^T                                         (2-bit, g64)
+  r2d       the square layer, plus Y [65536, 4096] = (Z * i^-1/2) Q^T for
+            the second (output-side) Gram of the two-sided rounding
 where Z has i.i.d. N(0, 1) entries and i = 1..n indexes the input channels.
 """
 from __future__ import annotations
@@ -62,6 +64,11 @@ def _specs_full():
                 LayerSpec("up", 6144, 2048, 262144, 3, 128, 128, 0.01, decay=0.5, seed=32, x_key="mlp_in"),
                 LayerSpec("down", 2048, 6144, 262144, 3, 128, 128, 0.01, kind="relu2", decay=0.5, seed=33)]
     s["lora"] = [LayerSpec("lora", 2048, 2048, 65536, 3, 0, 128, 1e-4, kind="lowrank", rank=64, seed=4)]
+    # two-sided rounding: the square layer (its W as the target, its input
+    # Gram on the right) and a second 4096-wide seeded matrix whose Gram
+    # stands for the output-side factor on the left
+    s["r2d"] = [s["square"][0],
+                LayerSpec("r2d_out", 4096, 4096, 65536, 4, 0, 128, 0.01, decay=0.5, seed=5)]
     vit = []
     for blk in range(12):
         for j, (nm, o, n) in enumerate([("qkv", 2304, 768), ("proj", 768, 768), ("fc1", 3072, 768),

@@ -232,3 +232,73 @@ def test_vit_batched_full(ctx):
         check_sweep_recurrence(np32(l["W"])[rows], Un, np32(b["codes"])[rows], np32(b["scales"])[rows],
                                np32(b["zeros"])[rows], np32(b["err"])[rows], s.bits, s.group)
     print("vit: all layers checked", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_round_2d_full(ctx):
+    """Two-sided rounding of the 4096 x 4096 layer (the r2d bench workload):
+    the objective against tr(D G D H) formed directly, and sampled entries
+    against the defining recurrence rebuilt from the GPU's residuals."""
+    sq, og = synth.FULL["r2d"]
+    print("r2d: generating", flush=True)
+    lay = synth.layer(sq, "cuda")
+    H = ctx.hessian(lay["X"])
+    G = ctx.hessian(synth.calibration(og, "cuda"))
+    W = lay["W"]
+    X2 = (W / (W.abs().max() / 7.5)).contiguous()
+    UG, _, lg = ctx.factor(G, lam_rel=0.01)
+    UH, _, lh = ctx.factor(H, lam_rel=0.01)
+    res = ctx.round_2d(X2, UG, UH, -8, 7, want_delta=True)
+    print("r2d: checking", flush=True)
+    Z = np32(res["Z"]).astype(np.float64)
+    D = np32(res["delta"]).astype(np.float64)
+    X = np32(X2).astype(np.float64)
+    m, n = X.shape
+    Gl = np32(G).astype(np.float64) + lg * np.eye(m)
+    Hl = np32(H).astype(np.float64) + lh * np.eye(n)
+    J = o.objective_2d(X, Z, Gl, Hl)
+    print("r2d:", dict(J=res["J"], J_direct=J), flush=True)
+    assert abs(res["J"] - J) <= 2e-3 * J
+    ug, uh = np32(UG).astype(np.float64), np32(UH).astype(np.float64)
+    Lg = (ug / np.diag(ug)[:, None]).T
+    Uh = uh / np.diag(uh)[:, None]
+    rng = np.random.default_rng(0)
+    pts = [(0, 0), (m - 1, n - 1), (63, 64), (64, 63), (m - 1, 0), (0, n - 1)]
+    pts += [tuple(p) for p in rng.integers(0, [m, n], size=(18, 2))]
+    worst = 0.0
+    for k, l in pts:
+        Ck = Lg[k, :k] @ D[:k, :l + 1]  # C_kj for j <= l
+        R = (Ck[:l] + D[k, :l]) @ Uh[:l, l]
+        w = X[k, l] - R - Ck[l]
+        q = float(np.clip(np.rint(np.float32(w)), -8, 7))
+        near = abs(abs(np.float32(w) - np.floor(np.float32(w))) - 0.5) < TIE
+        assert Z[k, l] == q or (near and abs(Z[k, l] - q) == 1), (k, l, w, Z[k, l])
+        worst = max(worst, abs(D[k, l] - (w - Z[k, l])))
+    print("r2d: worst residual error", worst, flush=True)
+    assert worst <= 2e-3
+
+
+@pytest.mark.timeout(900)
+def test_round_2d_1024_whole_oracle(ctx):
+    """1024 x 1024 against the oracle's whole anti-diagonal algorithm."""
+    m = n = 1024
+    r = np.random.default_rng(7)
+    Q, _ = np.linalg.qr(r.standard_normal((m, m)))
+    Y = (r.standard_normal((4 * m, m)) * np.arange(1, m + 1) ** -0.5) @ Q.T
+    G = (Y.T @ Y).astype(np.float32)
+    Q2, _ = np.linalg.qr(r.standard_normal((n, n)))
+    Y2 = (r.standard_normal((4 * n, n)) * np.arange(1, n + 1) ** -0.4) @ Q2.T
+    H = (Y2.T @ Y2).astype(np.float32)
+    X = r.normal(0.0, 2.5, (m, n)).astype(np.float32)
+    UG, _, _ = ctx.factor(torch.from_numpy(G).cuda(), lam_rel=0.01)
+    UH, _, _ = ctx.factor(torch.from_numpy(H).cuda(), lam_rel=0.01)
+    res = ctx.round_2d(torch.from_numpy(X).cuda(), UG, UH, -8, 7)
+    Z = np32(res["Z"]).astype(np.float64)
+    print("r2d1024: oracle", flush=True)
+    rep = o.round_2d(X, np32(UG).astype(np.float64), np32(UH).astype(np.float64), -8, 7, replay=Z,
+                     tie_window=TIE)
+    info = dict(forced=rep["forced"], bad=int(np.sum(rep["Z"] != Z)), J=res["J"], J_ref=rep["J"])
+    print("r2d1024:", info, flush=True)
+    assert info["bad"] == 0 and rep["forced"] <= 1e-4 * Z.size
+    assert abs(res["J"] - rep["J"]) <= 1e-4 * rep["J"]
+
