@@ -1257,13 +1257,26 @@ GPTQ_API int gptq_round_2d(gptq_ctx c, const float* X, int32_t m, int32_t n, con
   LAUNCH(c, "k_r2d_unit", launch_r2d_unit(UG, m, (float*)p.Lgt, (float*)p.dG, c->stream));
   LAUNCH(c, "k_r2d_unit", launch_r2d_unit(UH, n, (float*)p.Uh1, (float*)p.dH, c->stream));
   LAUNCH(c, "k_r2d_fill", launch_r2d_fill(p.C, p.R, (long long)mn, c->stream));
-  // anti-diagonals of 64 x 64 tiles: the stage's tiles, then their pushes
+  // anti-diagonals of 64 x 64 tiles: the stage's tiles, the pushes into the
+  // next row / column block on the main stream, the rest on the side stream
+  // beside the next stage's tiles (joined before the next near pushes)
+  bool side_busy = false;
   for (int S = 0; S < TM + TN - 1; ++S) {
     const int Ib = std::max(0, S - TN + 1), Ie = std::min(TM - 1, S);
     LAUNCH(c, "k_r2d_tile", launch_r2d_tile(p, S, Ib, Ie - Ib + 1, c->stream));
-    int items = 0;
-    for (int I = Ib; I <= Ie; ++I) items += (TM - I - 1) + (TN - (S - I) - 1);
-    LAUNCH(c, "k_r2d_push", launch_r2d_push(p, S, Ib, Ie, items, c->stream));
+    if (side_busy) {
+      HIPCHK(c, hipEventRecord(c->join_ev, c->side));
+      HIPCHK(c, hipStreamWaitEvent(c->stream, c->join_ev, 0));
+    }
+    LAUNCH(c, "k_r2d_push", launch_r2d_push(p, S, Ib, Ie, false, 0, c->stream));
+    HIPCHK(c, hipEventRecord(c->fork_ev, c->stream));
+    HIPCHK(c, hipStreamWaitEvent(c->side, c->fork_ev, 0));
+    LAUNCH_ON(c, c->side, "k_r2d_push", launch_r2d_push(p, S, Ib, Ie, true, 0, c->side));
+    side_busy = true;
+  }
+  if (side_busy) {
+    HIPCHK(c, hipEventRecord(c->join_ev, c->side));
+    HIPCHK(c, hipStreamWaitEvent(c->stream, c->join_ev, 0));
   }
   LAUNCH(c, "k_r2d_obj", launch_r2d_obj(p.objp, TM * TN, dJ, c->stream));
   if ((rc = ensure_small(c, sizeof(double)))) return rc;

@@ -38,5 +38,7 @@ hipError_t launch_objective(const QLayer* L, int nl, hipStream_t st);
 hipError_t launch_r2d_unit(const float* U, int n, float* U1, float* d, hipStream_t st);
 hipError_t launch_r2d_fill(float* a, float* b, long long cnt, hipStream_t st);
 hipError_t launch_r2d_tile(const R2dProb& p, int S, int Ibeg, int ntiles, hipStream_t st);
-hipError_t launch_r2d_push(const R2dProb& p, int S, int Ibeg, int Iend, int nitems, hipStream_t st);
+// far = false: the pushes into the next row / column block; true: the rest
+// (at most maxwg workgroups, 0: one per item; persistent over the items)
+hipError_t launch_r2d_push(const R2dProb& p, int S, int Ibeg, int Iend, bool far, int maxwg, hipStream_t st);
 hipError_t launch_r2d_obj(const double* objp, int nt, double* J, hipStream_t st);

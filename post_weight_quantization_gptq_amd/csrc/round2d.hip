@@ -24,9 +24,13 @@
 //   k_r2d_push: the stage's deltas pushed down to every tile below
 //     (C += Lg Delta) and its final C to every tile on the right
 //     (R += Cf Uh), one 64 x 64 output tile per workgroup on fp32 MFMA.
+//     The pushes into the next row block and the next column block (all the
+//     next stage's tiles read) run on the main stream; the rest runs on a
+//     second stream beside the next stage's tiles, which neither read nor
+//     write those blocks, and is joined before the next stage's near pushes
+//     (which update blocks it also updates).
 // Tiles of one stage write disjoint column blocks of C and disjoint row
-// blocks of R, so nothing races; the next stage's tiles read only finished
-// pushes (stream order).
+// blocks of R, so nothing within a push races.
 #include "common.h"
 #include "launch.h"
 
@@ -67,9 +71,8 @@ __global__ __launch_bounds__(256) void k_r2d_fill(float* __restrict__ a, float* 
 
 __global__ __launch_bounds__(256) void k_r2d_tile(R2dProb p, int S, int Ibeg) {
   __shared__ float Xs[T2][T2L], Ct[T2][T2L], Uk[T2][T2L];
-  // the tile's results stay in LDS until the walk ends: a barrier waits for
-  // every outstanding memory operation, so a global store inside the walk
-  // would add a memory round trip to each of its stages
+  // the tile's results stay in LDS until the walk ends (measured: stores
+  // from inside the walk cost a quarter more time per stage)
   __shared__ float Qs[T2][T2L], Ds[T2][T2L], Fs[T2][T2L];
   __shared__ double red[256];
   const int TN = (p.n + T2 - 1) / T2;
@@ -86,6 +89,7 @@ __global__ __launch_bounds__(256) void k_r2d_tile(R2dProb p, int S, int Ibeg) {
     Uk[a][b] = (a < nt && b < nt) ? p.Uh1[(size_t)(c0 + a) * p.n + c0 + b] : 0.f;
   }
   const int k = tid >> 2, part = tid & 3;
+  double se = 0.0;
   float rrow[16], lrow[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
@@ -127,7 +131,6 @@ __global__ __launch_bounds__(256) void k_r2d_tile(R2dProb p, int S, int Ibeg) {
     }
     __syncthreads();
   }
-  double se = 0.0;
   for (int e = tid; e < T2 * T2; e += 256) {
     const int a = e >> 6, b = e & 63;
     if (a < mt && b < nt) {
@@ -149,31 +152,47 @@ __global__ __launch_bounds__(256) void k_r2d_tile(R2dProb p, int S, int Ibeg) {
   if (tid == 0) p.objp[(size_t)I * TN + J] = red[0];
 }
 
+// Push items of tile (I, J) on the near (far = false) or far side: the
+// next row block / column block only, or every block past it.
+__host__ __device__ inline int r2d_items(int TM, int TN, int I, int J, bool far, int* nc, int* nr) {
+  *nc = far ? max(0, TM - I - 2) : (I + 1 < TM ? 1 : 0);
+  *nr = far ? max(0, TN - J - 2) : (J + 1 < TN ? 1 : 0);
+  return *nc + *nr;
+}
+
 // One 64 x 64 output tile of a push of stage S:
 //   kind 0, tile (I, J), row block K > I:    C[K][J] += Lg[K][I] D[I][J]
 //   kind 1, tile (I, J), column block L > J: R[I][L] += Cf[I][J] Uh[J][L]
+// near: K = I + 1 and L = J + 1 (what the next stage's tiles read); far:
+// the blocks past those (read two or more stages later).
 // K = 64 on v_mfma_f32_32x32x2f32, 4 waves of 32 x 32.
-__global__ __launch_bounds__(256) void k_r2d_push(R2dProb p, int S, int Ibeg, int Iend) {
+// Items vt = blockIdx.x, blockIdx.x + gridDim.x, ... < ntot: a grid smaller
+// than the item count makes the launch persistent, so the far pushes leave
+// CUs free for the next stage's tiles.
+__global__ __launch_bounds__(256) void k_r2d_push(R2dProb p, int S, int Ibeg, int Iend, int far, int ntot) {
   __shared__ float As[T2][T2P];  // [t][r]
   __shared__ float Bs[T2][T2P];  // [t][c]
   const int TM = (p.m + T2 - 1) / T2, TN = (p.n + T2 - 1) / T2;
-  int item = blockIdx.x, I = Ibeg, kind = 0, blk = 0;
+  const int skip = far ? 2 : 1;
+  for (int vt = blockIdx.x; vt < ntot; vt += gridDim.x) {
+  int item = vt, I = Ibeg, kind = 0, blk = 0;
   for (; I <= Iend; ++I) {
-    const int nc = TM - I - 1, nr = TN - (S - I) - 1;
+    int nc, nr;
+    r2d_items(TM, TN, I, S - I, far != 0, &nc, &nr);
     if (item < nc) {
       kind = 0;
-      blk = I + 1 + item;
+      blk = I + skip + item;
       break;
     }
     item -= nc;
     if (item < nr) {
       kind = 1;
-      blk = S - I + 1 + item;
+      blk = S - I + skip + item;
       break;
     }
     item -= nr;
   }
-  if (I > Iend) return;
+  if (I > Iend) return;  // never: vt < ntot
   const int J = S - I;
   const int r0 = I * T2, c0 = J * T2;
   const int mtI = min(T2, p.m - r0), ntJ = min(T2, p.n - c0);
@@ -226,6 +245,8 @@ __global__ __launch_bounds__(256) void k_r2d_push(R2dProb p, int S, int Ibeg, in
     const int j = 32 * wc + (lane & 31);
     if (i < orows && j < ocols) out[(size_t)i * p.n + j] = cur[r] + acc[r];
   }
+  __syncthreads();  // the next item refills As, Bs
+  }
 }
 
 // J = sum of the tiles' partial sums, in tile order
@@ -261,9 +282,19 @@ hipError_t launch_r2d_tile(const R2dProb& p, int S, int Ibeg, int ntiles, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_r2d_push(const R2dProb& p, int S, int Ibeg, int Iend, int nitems, hipStream_t st) {
+int r2d_push_items(int m, int n, int S, bool far) {
+  const int TM = (m + T2 - 1) / T2, TN = (n + T2 - 1) / T2;
+  const int Ib = max(0, S - TN + 1), Ie = min(TM - 1, S);
+  int total = 0, nc, nr;
+  for (int I = Ib; I <= Ie; ++I) total += r2d_items(TM, TN, I, S - I, far, &nc, &nr);
+  return total;
+}
+
+hipError_t launch_r2d_push(const R2dProb& p, int S, int Ibeg, int Iend, bool far, int maxwg, hipStream_t st) {
+  const int nitems = r2d_push_items(p.m, p.n, S, far);
   if (nitems <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_r2d_push, dim3(nitems), dim3(256), 0, st, p, S, Ibeg, Iend);
+  const int grid = (maxwg > 0 && maxwg < nitems) ? maxwg : nitems;
+  hipLaunchKernelGGL(k_r2d_push, dim3(grid), dim3(256), 0, st, p, S, Ibeg, Iend, far ? 1 : 0, nitems);
   return hipGetLastError();
 }
 
