@@ -37,7 +37,11 @@ for two-sided rounding (tests/test_oracle_2d.py) the vectorized sweep with the
 Kronecker Gram ([2D] Theorem 2), a second topological order (Theorem 1), the
 one-sided reductions B = I and A = I, an independently written nearest-plane
 solver on the integer lattice, the identity metric and the objective formed
-from A and B directly.
+from A and B directly; for the quantised-input target
+(tests/test_oracle_qronos.py) the X_q = X reduction to GPTQ, the
+completed-square identity over random codes, a least-squares route to the
+target, the nearest-plane solver on the target and the objective formed from
+the data.
 
 Parity unpinned (conventions that only self-consistency fixes; the GPU follows
 them exactly): the min-max grid details of ``grid_fit`` (0 inside the range,
@@ -735,3 +739,53 @@ def objective_2d(X, Z, G, H) -> float:
     """||A (Z - X) B||_F^2 = tr((Z - X)^T G (Z - X) H) for G = A^T A, H = B B^T."""
     D = np.asarray(Z, dtype=np.float64) - np.asarray(X, dtype=np.float64)
     return float(np.sum((G @ D @ H) * D))
+
+
+# --------------------------------------------------------------------------
+# quantised-input calibration target (Qronos-style)
+# --------------------------------------------------------------------------
+def cross_gram(Xa, Xb, chunk: int = 2048) -> np.ndarray:
+    """Xa^T Xb in float64 (bf16 bit patterns or floats), summed over token
+    chunks in order; the two-input form of ``hessian``."""
+    A = _as_f64(Xa)
+    B = _as_f64(Xb)
+    n = A.shape[1]
+    G = np.zeros((n, B.shape[1]))
+    for t0 in range(0, A.shape[0], chunk):
+        G += A[t0:t0 + chunk].T @ B[t0:t0 + chunk]
+    return G
+
+
+def qronos_target(W, Hq, G, lam: float) -> np.ndarray:
+    """Target rows w* = (Hq + lam I)^{-1} (G + lam I) w.
+
+    [Lat] section 5.1: when the layer's inputs come from already-quantised
+    layers (Xq instead of X), only the target changes.  For every row,
+    ||Xq q - X w||^2 + lam ||q - w||^2 = (q - w*)^T (Hq + lam I) (q - w*) +
+    const with Hq = Xq^T Xq and G = Xq^T X, so the sweep runs on w* with the
+    factor of Hq + lam I.  Damping is a ridge towards w (our reading); with
+    Xq = X the target is w itself.
+    """
+    n = Hq.shape[0]
+    Hl = Hq + lam * np.eye(n)
+    return np.linalg.solve(Hl, (G + lam * np.eye(n)) @ np.asarray(W, dtype=np.float64).T).T
+
+
+def gptq_qronos(W, X, Xq, bits: int, group: int, block: int, lam_rel: float = 0.01,
+                lam_abs: float = 0.0, replay: dict | None = None) -> dict:
+    """GPTQ with the quantised-input target: Hq = Xq^T Xq, G = Xq^T X,
+    lam from Hq, W* = qronos_target, U = factor of Hq + lam I, then the sweep
+    on W*.  Returns the sweep's result plus W_target, lam, J (the surrogate,
+    tr((W* - What) Hq (W* - What)^T)) and J_q = ||Xq What^T - X W^T||_F^2."""
+    Hq = hessian(Xq)
+    G = cross_gram(Xq, X)
+    H = hessian(X)
+    Hl, lam = damp(Hq, lam_abs, lam_rel)
+    Wst = qronos_target(W, Hq, G, lam)
+    U = factor_u(Hl)
+    res = gptq_sweep(Wst, U, bits, group, block, replay=replay)
+    Q = res["What"]
+    Wd = np.asarray(W, dtype=np.float64)
+    J_q = float(np.sum((Q @ Hq) * Q) - 2.0 * np.sum((Q @ G) * Wd) + np.sum((Wd @ H) * Wd))
+    res.update(W_target=Wst, U=U, lam=lam, Hq=Hq, G=G, J=objective(Wst, Q, Hq), J_q=J_q)
+    return res
