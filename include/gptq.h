@@ -187,6 +187,28 @@ int gptq_lora_refine(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const
                      int32_t block, double lam_abs, double lam_rel, int32_t rounds, uint8_t* codes,
                      float* scales, uint8_t* zeros, float* L, float* R, double* trace, int32_t* info);
 
+/* GPTQ with the quantised-input target (Lattice Geometry of NN Quantization,
+ * section 5.1: when the layer's inputs come from already-quantised layers,
+ * Xq instead of X, only the target of the nearest-plane problem changes).
+ * Every row minimises ||Xq q - X w||^2 + lam ||q - w||^2 (damping as a ridge
+ * towards w), which is the GPTQ sweep of gptq_quantize on the target
+ *   W* = W (G + lam I)^T Hq_lam^{-1},  G = Xq^T X,  Hq_lam = Xq^T Xq + lam I,
+ * lam = lam_abs + lam_rel * mean(diag(Xq^T Xq)), with the factor of Hq_lam.
+ * With Xq = X the target is W.  The Grams run as gptq_hessian (fp32, bf16
+ * MFMA; G over all tiles), the three products forming W* in fp64.
+ * Inputs: W[out][n] fp32; X, Xq [tokens][ldx] bf16 bits (device), the same
+ * tokens and pitch, rows 16-byte aligned, n % 16 == 0.  Outputs as
+ * gptq_quantize (codes, scales, zeros; the grid is fitted on W*'s
+ * error-updated values), Wt[out][n] fp32 the target W* (may be NULL), obj[2]
+ * [host] = {J, J_lam} of the sweep relative to W* and Hq (J = tr((W* - What)
+ * Hq (W* - What)^T); ||Xq What^T - X W^T||^2 differs from it by a constant of
+ * W).  *info as gptq_factor.  Requirements on bits/group/block as
+ * gptq_quantize.  SYNC. */
+int gptq_quantize_qronos(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const uint16_t* X,
+                         const uint16_t* Xq, int64_t tokens, int64_t ldx, int32_t bits, int32_t group,
+                         int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
+                         uint8_t* zeros, float* Wt, double* obj, int32_t* info);
+
 /* Two-sided adaptive rounding, GPTQ-2D (GPTQ-2D technical summary): integers
  * Z minimising ||A (Z - X) B||_F^2 greedily, with exactly the trajectory of
  * the one-sided sweep over vec(X) (column-major) under the Gram H kron G,
@@ -249,7 +271,8 @@ int gptq_quantize_batched(gptq_ctx ctx, int32_t nlayers, gptq_layer* layers);
  * LoRA and refinement paths k_lora_lambda, k_start_block, k_dgemm, k_dsum,
  * k_gram_chol, k_apply, k_lora_assemble, k_lora_extract, k_ref_init, k_resid,
  * k_gfinal, k_sum_parts, k_f32_to_f64, k_f64_to_f32, k_olrc_out, and for the
- * two-sided rounding k_r2d_unit, k_r2d_fill, k_r2d_tile, k_r2d_push, k_r2d_obj.  gptq_kernel_time
+ * two-sided rounding k_r2d_unit, k_r2d_fill, k_r2d_tile, k_r2d_push, k_r2d_obj,
+ * and for the quantised-input target k_qr_prep, k_qr_out.  gptq_kernel_time
  * waits for the recorded events and returns the summed elapsed milliseconds
  * and the number of timed launches of kernel `name` (0 and 0 if none).  Each
  * timed launch costs two event records on the stream. */

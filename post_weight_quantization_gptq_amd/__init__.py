@@ -102,11 +102,14 @@ def load_library(path: str | None = None):
     L.gptq_bid_up.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp,
                               ctypes.POINTER(d)]
     L.gptq_round_2d.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, vp, vp, ctypes.POINTER(d)]
+    L.gptq_quantize_qronos.argtypes = [vp, vp, i32, i32, vp, vp, i64, i64, i32, i32, i32, d, d, vp, vp, vp, vp,
+                                       ctypes.POINTER(d), ctypes.POINTER(i32)]
     L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
     L.gptq_timing.argtypes = [vp, ctypes.c_char_p]
     L.gptq_kernel_time.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(d), ctypes.POINTER(i64)]
     for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
                  "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up", "gptq_round_2d",
+                 "gptq_quantize_qronos",
                  "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
         getattr(L, name).restype = ctypes.c_int
     if path is None:
@@ -347,6 +350,30 @@ class Context:
                                          int(bits), int(group), int(block), _ptr(codes), _ptr(scales), _ptr(zeros),
                                          ctypes.byref(J)))
         return J.value
+
+    def quantize_qronos(self, W, X, Xq, bits: int, group: int, block: int, lam_abs: float = 0.0,
+                        lam_rel: float = 0.01, want_target: bool = False):
+        """GPTQ with the quantised-input target.  Returns dict(codes, scales, zeros, Wt or None, J, J_lam, info)."""
+        torch = self.torch
+        self._dev(W, torch.float32, "W")
+        X = self._xbits(X)
+        Xq = self._xbits(Xq)
+        if Xq.shape != X.shape or Xq.stride(0) != X.stride(0):
+            raise ValueError("X and Xq must have the same shape and row pitch")
+        o, n = W.shape
+        ng = n // group if group else 1
+        res = dict(codes=torch.empty((o, n), dtype=torch.uint8, device=self.device),
+                   scales=torch.empty((o, ng), dtype=torch.float32, device=self.device),
+                   zeros=torch.empty((o, ng), dtype=torch.uint8, device=self.device),
+                   Wt=torch.empty((o, n), dtype=torch.float32, device=self.device) if want_target else None)
+        obj = (ctypes.c_double * 2)()
+        info = ctypes.c_int32(0)
+        self._check(self.lib.gptq_quantize_qronos(self.handle, _ptr(W), o, n, _ptr(X), _ptr(Xq), X.shape[0],
+                                                  X.stride(0), int(bits), int(group), int(block), float(lam_abs),
+                                                  float(lam_rel), _ptr(res["codes"]), _ptr(res["scales"]),
+                                                  _ptr(res["zeros"]), _ptr(res["Wt"]), obj, ctypes.byref(info)))
+        res["J"], res["J_lam"], res["info"] = obj[0], obj[1], info.value
+        return res
 
     def round_2d(self, X, UG, UH, qmin: int, qmax: int, want_delta: bool = False):
         """GPTQ-2D two-sided rounding of X [m, n] with the factors UG [m, m], UH [n, n].

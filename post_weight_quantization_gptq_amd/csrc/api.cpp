@@ -34,7 +34,7 @@ struct gptq_ctx_s {
   int ncu = 256;
   int nxcd = 8;
   std::string err;
-  DevBuf partials, xt, facA, facY, work, eblk, objp, dinv, slots, blob, lora, r2d;
+  DevBuf partials, xt, facA, facY, work, eblk, objp, dinv, slots, blob, lora, r2d, qr;
   void* hblob = nullptr;  // pinned staging for the task tables
   size_t hblob_cap = 0;
   void* hsmall = nullptr;  // pinned read-back area
@@ -228,6 +228,9 @@ struct HessJob {
   int n;
   float* H;
   int accumulate;
+  // non-null: the cross Gram X^T Y (Y as X: [tokens][ldx]; direct layout
+  // only), written in full
+  const uint16_t* Y = nullptr;
 };
 
 struct HessPlan {
@@ -291,19 +294,20 @@ void plan_hessian(const std::vector<HessJob>& jobs, int ncu, int nxcd, uint16_t*
     if (hess_direct(J)) {
       // the tiles read X itself (transposing LDS reads); no copy
       P.xprobs.push_back(XposeProb{J.X, J.ldx, nullptr, J.n, (int)J.tokens, n_pad, t_pad, vec, 0});
-      P.probs.push_back(SyrkProb{J.X, J.ldx, 1, (int)J.tokens, J.n, 0});
+      P.probs.push_back(SyrkProb{J.X, J.ldx, 1, (int)J.tokens, J.n, 0, J.Y});
     } else {
       const int ldt = t_pad > 0 ? t_pad + 256 : 0;
       P.xprobs.push_back(XposeProb{J.X, J.ldx, xt, J.n, (int)J.tokens, n_pad, t_pad, vec, ldt});
       if (t_pad > 0) P.xsegs.push_back(Seg{(int)p, 0, (t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
-      P.probs.push_back(SyrkProb{xt, ldt, 0, (int)J.tokens, J.n, 0});
+      P.probs.push_back(SyrkProb{xt, ldt, 0, (int)J.tokens, J.n, 0, nullptr});
       xt += (size_t)n_pad * ldt;
     }
-    P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate});
+    const bool full = J.Y != nullptr;
+    P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate, full ? 1 : 0, 0});
     if (J.n <= 0) continue;
-    std::vector<std::pair<int, int>> tl;
+    std::vector<std::pair<int, int>> tl;  // upper tiles, or every tile of a cross Gram
     for (int ti = 0; ti < nt; ++ti)
-      for (int tj = ti; tj < nt; ++tj) tl.push_back({ti, tj});
+      for (int tj = full ? 0 : ti; tj < nt; ++tj) tl.push_back({ti, tj});
     const int ntile = (int)tl.size();
     if (J.tokens > 0) {
       std::vector<std::pair<int, int>> mo = tl;
@@ -321,7 +325,8 @@ void plan_hessian(const std::vector<HessJob>& jobs, int ncu, int nxcd, uint16_t*
       std::vector<int> pos(ntile);  // tile (canonical index) -> position inside a slice
       for (int q = 0; q < ntile; ++q) {
         const std::pair<int, int> t = mo[ord[q]];
-        const int ci = t.first * nt - t.first * (t.first - 1) / 2 + (t.second - t.first);
+        const int ci = full ? t.first * nt + t.second
+                            : t.first * nt - t.first * (t.first - 1) / 2 + (t.second - t.first);
         pos[ci] = q;
       }
       for (int sl = 0; sl < S; ++sl) {
@@ -337,7 +342,7 @@ void plan_hessian(const std::vector<HessJob>& jobs, int ncu, int nxcd, uint16_t*
         for (int sl = 0; sl < S; ++sl) P.partlist.push_back(first + sl * ntile + pos[ci]);
         for (int a = 0; a < 4; ++a)
           for (int b = 0; b < 4; ++b) {
-            if (ti == tj && a > b) continue;
+            if (ti == tj && a > b && !full) continue;
             const int r0 = ti * 256 + 64 * a, c0 = tj * 256 + 64 * b;
             if (r0 >= J.n || c0 >= J.n) continue;
             P.rtasks.push_back(RedTask{(int)p, r0, c0, part0, S, 0, 0, 0});
@@ -350,7 +355,7 @@ void plan_hessian(const std::vector<HessJob>& jobs, int ncu, int nxcd, uint16_t*
         for (int a = 0; a < 4; ++a)
           for (int b = 0; b < 4; ++b) {
             const int r0 = ti * 256 + 64 * a, c0 = tj * 256 + 64 * b;
-            if ((ti == tj && a > b) || r0 >= J.n || c0 >= J.n) continue;
+            if ((ti == tj && a > b && !full) || r0 >= J.n || c0 >= J.n) continue;
             P.rtasks.push_back(RedTask{(int)p, r0, c0, 0, 0, 0, 0, 0});
           }
       }
@@ -902,7 +907,7 @@ GPTQ_API int gptq_destroy(gptq_ctx c) {
     (void)hipStreamSynchronize(c->stream);
     if (c->side) (void)hipStreamSynchronize(c->side);
     DevBuf* bufs[] = {&c->partials, &c->xt, &c->facA, &c->facY, &c->work, &c->eblk, &c->dinv,
-                      &c->objp, &c->slots, &c->blob, &c->lora, &c->r2d};
+                      &c->objp, &c->slots, &c->blob, &c->lora, &c->r2d, &c->qr};
     for (DevBuf* b : bufs)
       if (b->p) (void)hipFree(b->p);
     if (c->hblob) (void)hipHostFree(c->hblob);
@@ -1283,6 +1288,68 @@ GPTQ_API int gptq_round_2d(gptq_ctx c, const float* X, int32_t m, int32_t n, con
   HIPCHK(c, hipMemcpyAsync(c->hsmall, dJ, sizeof(double), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
   *J = *(const double*)c->hsmall;
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_quantize_qronos(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t* X,
+                                  const uint16_t* Xq, int64_t tokens, int64_t ldx, int32_t bits, int32_t group,
+                                  int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
+                                  uint8_t* zeros, float* Wt, double* obj, int32_t* info) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (info) *info = 0;
+  int rc = check_quant_args(c, out, n, bits, group, block);
+  if (rc) return rc;
+  if ((rc = check_x(c, X, tokens, n, ldx))) return rc;
+  if ((rc = check_x(c, Xq, tokens, n, ldx))) return rc;
+  if (!obj || !W || !codes || !scales || !zeros || out <= 0 || n <= 0)
+    return set_err(c, GPTQ_ERR_INVALID_ARG, "null pointer or empty layer");
+  if (n % 16 || ldx % 8 || ((uintptr_t)X & 15) || ((uintptr_t)Xq & 15) || tokens <= 0)
+    return set_err(c, GPTQ_ERR_UNSUPPORTED,
+                   "quantised-input target needs n % 16 == 0, 16-byte aligned rows of X and Xq, tokens > 0");
+  if (!std::isfinite(lam_abs) || !std::isfinite(lam_rel)) return set_err(c, GPTQ_ERR_INVALID_ARG, "non-finite damping");
+  obj[0] = obj[1] = 0.0;
+  DeviceGuard g(c->device);
+  const size_t nn = (size_t)n * n, on = (size_t)out * n;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t oH = take(nn * 4), oG = take(nn * 4), oU = take(nn * 4), oWd = take(on * 8), oGd = take(nn * 8),
+               oUd = take(nn * 8), oUt = take(nn * 8), oT1 = take(on * 8), oT2 = take(on * 8),
+               oWs = take(Wt ? 0 : on * 4);
+  if ((rc = ensure(c, c->qr, off))) return rc;
+  uint8_t* base = (uint8_t*)c->qr.p;
+  float *Hq = (float*)(base + oH), *G = (float*)(base + oG), *U = (float*)(base + oU);
+  double *Wd = (double*)(base + oWd), *Gd = (double*)(base + oGd), *Ud = (double*)(base + oUd),
+         *UdT = (double*)(base + oUt), *T1 = (double*)(base + oT1), *T2 = (double*)(base + oT2);
+  float* Ws = Wt ? Wt : (float*)(base + oWs);
+  // Hq = Xq^T Xq and G = Xq^T X in one grouped Hessian launch
+  std::vector<HessJob> hj{HessJob{Xq, tokens, ldx, n, Hq, 0}, HessJob{Xq, tokens, ldx, n, G, 0}};
+  hj[1].Y = X;
+  if ((rc = run_hessian(c, hj))) return rc;
+  if ((rc = ensure(c, c->slots, sizeof(Slot)))) return rc;
+  Slot* ds = (Slot*)c->slots.p;
+  if ((rc = run_factor(c, {FacJob{Hq, n, n, n, lam_abs, lam_rel, U}}, ds))) return rc;
+  // W* = ((W (G + lam I)^T) U^T) U in fp64
+  LAUNCH(c, "k_qr_prep", launch_qr_prep(W, G, U, &ds->lam, out, n, Wd, Gd, Ud, UdT, c->stream));
+  if ((rc = run_gemm_nt(c, Wd, Gd, T1, out, n, n, n))) return rc;
+  if ((rc = run_gemm_nt(c, T1, Ud, T2, out, n, n, n))) return rc;
+  if ((rc = run_gemm_nt(c, T2, UdT, Wd, out, n, n, n))) return rc;
+  LAUNCH(c, "k_qr_out", launch_qr_out(Wd, Ws, (long long)on, c->stream));
+  QuantJob J{Ws, out, n, n, U, bits, group, block, codes, scales, zeros, nullptr, &ds->lam, ds->obj, nullptr};
+  if ((rc = run_quantize(c, {J}))) return rc;
+  if ((rc = ensure_small(c, sizeof(Slot)))) return rc;
+  HIPCHK(c, hipMemcpyAsync(c->hsmall, ds, sizeof(Slot), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  const Slot s = *(const Slot*)c->hsmall;
+  if (s.nonfinite) return set_err(c, GPTQ_ERR_NONFINITE, "non-finite entry in the quantised-input Gram");
+  if (info) *info = s.info;
+  if (s.info) return set_err(c, GPTQ_ERR_NOT_PD, "damped quantised-input Gram not positive definite");
+  obj[0] = s.obj[0];
+  obj[1] = s.obj[1];
   return GPTQ_OK;
 }
 

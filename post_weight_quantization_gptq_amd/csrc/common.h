@@ -42,6 +42,9 @@ struct SyrkProb {
   int tokens;
   int n;
   int pad0;
+  // cross Gram X^T Y: the B operand's rows come from Yt (same layout and
+  // pitch as Xt, direct mode only); null for X^T X
+  const uint16_t* Yt;
 };
 struct SyrkTask {
   int prob, ti, tj, k0, k1, part, pad0, pad1;
@@ -51,6 +54,8 @@ struct RedProb {
   float* H;
   int n;
   int accumulate;
+  int full;  // 1: a cross Gram, every sub-block written as is (no mirror)
+  int pad0;
 };
 struct RedTask {
   int prob, r0, c0, part0, nparts, pad0, pad1, pad2;

@@ -42,3 +42,8 @@ hipError_t launch_r2d_tile(const R2dProb& p, int S, int Ibeg, int ntiles, hipStr
 // (at most maxwg workgroups, 0: one per item; persistent over the items)
 hipError_t launch_r2d_push(const R2dProb& p, int S, int Ibeg, int Iend, bool far, int maxwg, hipStream_t st);
 hipError_t launch_r2d_obj(const double* objp, int nt, double* J, hipStream_t st);
+
+// quantised-input target (qronos.hip)
+hipError_t launch_qr_prep(const float* W, const float* G, const float* U, const double* lam, int out, int n,
+                          double* Wd, double* Gd, double* Ud, double* UdT, hipStream_t st);
+hipError_t launch_qr_out(const double* a, float* b, long long cnt, hipStream_t st);

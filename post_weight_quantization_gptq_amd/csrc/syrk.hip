@@ -109,7 +109,7 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     const int lrow = 16 * w + (lane >> 2);
     const int tchunk = (lane & 3) ^ (lane >> 4);
     ga = pb.Xt + (size_t)(tk.ti * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
-    gb = pb.Xt + (size_t)(tk.tj * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
+    gb = (pb.Yt ? pb.Yt : pb.Xt) + (size_t)(tk.tj * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
     gstep = SYK_KT;
     gq = 16 * NW * tp;
   } else {
@@ -120,7 +120,7 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     const int chunk = (lane & 31) ^ (4 * (trow & 3));
     const int fa = tk.ti * 256 + 8 * chunk, fb = tk.tj * 256 + 8 * chunk;
     ga = pb.Xt + (fa < pb.n ? fa : tk.ti * 256);
-    gb = pb.Xt + (fb < pb.n ? fb : tk.tj * 256);
+    gb = (pb.Yt ? pb.Yt : pb.Xt) + (fb < pb.n ? fb : tk.tj * 256);
     tok0 = tk.k0;
     gstep = 0;
     gq = 0;
@@ -275,13 +275,14 @@ __global__ __launch_bounds__(64 * SYK_NW, 1) void k_syrk(const SyrkProb* __restr
   const SyrkTask tk = tasks[blockIdx.x];
   if (tk.part < 0) return;
   const SyrkProb pb = probs[tk.prob];
+  const bool diag = tk.ti == tk.tj && !pb.Yt;  // one operand serves both sides
   if (pb.direct) {
-    if (tk.ti == tk.tj)
+    if (diag)
       syrk_tile<true, true, SYK_NW>(pb, tk, lds, partials);
     else
       syrk_tile<false, true, SYK_NW>(pb, tk, lds, partials);
   } else {
-    if (tk.ti == tk.tj)
+    if (diag)
       syrk_tile<true, false, SYK_NW>(pb, tk, lds, partials);
     else
       syrk_tile<false, false, SYK_NW>(pb, tk, lds, partials);
@@ -317,15 +318,16 @@ __global__ __launch_bounds__(256) void k_syrk_reduce(const RedProb* __restrict__
     const int rr = (tid >> 6) + 4 * q;
     const int i = tk.r0 + rr, j = tk.c0 + cc;
     float s = sum[q];
-    if (pb.accumulate && i < n && j < n && i <= j) s += pb.H[(size_t)i * n + j];
+    if (pb.accumulate && i < n && j < n && (i <= j || pb.full)) s += pb.H[(size_t)i * n + j];
     S[rr][cc] = s;
   }
   __syncthreads();
   for (int q = 0; q < 16; ++q) {
     const int rr = (tid >> 6) + 4 * q;
     const int i = tk.r0 + rr, j = tk.c0 + cc;
-    if (i < n && j < n && i <= j) pb.H[(size_t)i * n + j] = S[rr][cc];
+    if (i < n && j < n && (i <= j || pb.full)) pb.H[(size_t)i * n + j] = S[rr][cc];
   }
+  if (pb.full) return;  // a cross Gram has no mirror
   // mirror: H[j][i] = S[i][j] for i < j, written along contiguous rows of H
   for (int q = 0; q < 16; ++q) {
     const int ci = (tid >> 6) + 4 * q;  // column index inside the sub-block

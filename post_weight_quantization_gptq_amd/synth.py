@@ -23,6 +23,8 @@ columns sign-fixed by sign(diag R)):
             (Z * i^-1/2) Q^T                                         (2-bit, g64)
   r2d       the square layer, plus Y [65536, 4096] = (Z * i^-1/2) Q^T for
             the second (output-side) Gram of the two-sided rounding
+  qronos    the square layer, its X and Xq = bf16(X + N(0, (0.05 std X)^2))
+            standing in for the inputs of an already-quantised network
 where Z has i.i.d. N(0, 1) entries and i = 1..n indexes the input channels.
 """
 from __future__ import annotations
@@ -170,6 +172,23 @@ def calibration(spec: LayerSpec, device="cpu", chunk: int = 16384) -> torch.Tens
             blk[:, ch] *= math.sqrt(20.0)
         X[t0:t0 + m] = _to_bits(blk)
     return X
+
+
+def perturbed(X: torch.Tensor, seed: int, scale: float = 0.05, chunk: int = 16384) -> torch.Tensor:
+    """A seeded stand-in for the inputs an already-quantised network feeds the
+    layer: X (bf16 bits) plus N(0, (scale * std(X))^2) noise, rounded back to
+    bf16, chunk by chunk on X's device."""
+    dev = X.device
+    gen = torch.Generator(device=dev).manual_seed(60_000 + seed)
+    out = torch.empty_like(X)
+    s = None
+    for t0 in range(0, X.shape[0], chunk):
+        blk = X[t0:t0 + chunk].view(torch.bfloat16).to(torch.float32)
+        if s is None:
+            s = scale * float(blk.std())
+        noise = torch.randn(blk.shape, generator=gen, device=dev, dtype=torch.float32) * s
+        out[t0:t0 + chunk] = _to_bits(blk + noise)
+    return out
 
 
 def layer(spec: LayerSpec, device="cpu"):
