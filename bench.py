@@ -177,13 +177,75 @@ def bench_r2d(args, torch, Context, synth, dev):
     print(json.dumps(line), flush=True)
 
 
+QR_KERNELS = ["k_syrk", "k_syrk_reduce", "k_damp_lambda", "k_damp_fill", "k_chol_panel2", "k_gemm_ring64",
+              "k_gemm_ring128", "k_make_u", "k_qr_prep", "k_qr_out", "k_init_work", "k_sweep", "k_trail",
+              "k_objective"]
+
+
+def bench_qronos(args, torch, Context, synth, dev):
+    """GPTQ with the quantised-input target on the square layer: Xq = X plus
+    seeded noise (a stand-in for the inputs an already-quantised network
+    feeds the layer).  A step is the whole call: Xq^T Xq and Xq^T X (one
+    grouped SYRK launch), the factor, the target's three fp64 products and
+    the sweep."""
+    sq = synth.FULL["square"][0]
+    print("# generating qronos inputs", file=sys.stderr, flush=True)
+    lay = synth.layer(sq, dev)
+    Xq = synth.perturbed(lay["X"], sq.seed)
+    torch.cuda.synchronize()
+    ctx = Context(dev)
+
+    def one_step():
+        return ctx.quantize_qronos(lay["W"], lay["X"], Xq, sq.bits, sq.group, sq.block, lam_rel=sq.lam_rel)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ctx.timing("k_syrk")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    last = None
+    for _ in range(args.steps):
+        last = one_step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    syrk_ms, syrk_n = ctx.kernel_time("k_syrk")
+    ctx.timing("*")
+    one_step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for nm in QR_KERNELS:
+        ms, cnt = ctx.kernel_time(nm)
+        if cnt:
+            breakdown[nm] = {"ms": round(ms, 4), "launches": cnt}
+    ctx.timing(None)
+    ms_step = 1e3 * wall / args.steps
+    t, n = sq.tokens, sq.n
+    flops = t * n * (n + 1) + 2 * t * n * n  # Xq^T Xq (triangle) + Xq^T X (full), one launch
+    avg = syrk_ms / max(syrk_n, 1)
+    ach = flops / (avg * 1e-3) / 1e12 if syrk_n else 0.0
+    line = {"metric": "ms per layer, GPTQ with the quantised-input target, 4096x4096 4-bit g128",
+            "value": round(ms_step, 4), "unit": "ms/layer", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; the square layer, Xq = bf16(X + 0.05 std(X) noise))",
+            "config": {"workload": "qronos: W[4096,4096] X,Xq[262144,4096] 4-bit g128 B128"},
+            "kernels_one_step": breakdown,
+            "roofline": {"kernel": "k_syrk", "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "avg_launch_ms": round(avg, 4), "flops_per_launch": flops},
+            "objective": {"J": last["J"], "J_lam": last["J_lam"]}}
+    ctx.close()
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="square",
-                    choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d"])
+                    choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d", "qronos"])
     ap.add_argument("--rounds", type=int, default=1, help="refinement rounds of the lora_refine workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,6 +273,9 @@ def main():
         return
     if args.workload == "r2d":
         bench_r2d(args, torch, Context, synth, dev)
+        return
+    if args.workload == "qronos":
+        bench_qronos(args, torch, Context, synth, dev)
         return
     specs = synth.FULL["lora" if args.workload == "lora_refine" else args.workload]
     print("# generating %s inputs" % args.workload, file=sys.stderr, flush=True)

@@ -187,6 +187,14 @@ int gptq_lora_refine(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const
                      int32_t block, double lam_abs, double lam_rel, int32_t rounds, uint8_t* codes,
                      float* scales, uint8_t* zeros, float* L, float* R, double* trace, int32_t* info);
 
+/* Cross Gram G = X^T Y (sum over tokens of x_t^T y_t), fp32 [n][n] written in
+ * full (not symmetric), on the same bf16 MFMA tiles as gptq_hessian.  X and
+ * Y are [tokens][ldx] bf16 bits with the same tokens and pitch; rows 16-byte
+ * aligned and n % 8 == 0 (else GPTQ_ERR_UNSUPPORTED).  tokens == 0 writes
+ * zeros.  ASYNC on the context's stream. */
+int gptq_cross_gram(gptq_ctx ctx, const uint16_t* X, const uint16_t* Y, int64_t tokens, int32_t n,
+                    int64_t ldx, float* G);
+
 /* GPTQ with the quantised-input target (Lattice Geometry of NN Quantization,
  * section 5.1: when the layer's inputs come from already-quantised layers,
  * Xq instead of X, only the target of the nearest-plane problem changes).

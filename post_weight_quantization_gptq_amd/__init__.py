@@ -102,6 +102,7 @@ def load_library(path: str | None = None):
     L.gptq_bid_up.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp,
                               ctypes.POINTER(d)]
     L.gptq_round_2d.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, vp, vp, ctypes.POINTER(d)]
+    L.gptq_cross_gram.argtypes = [vp, vp, vp, i64, i32, i64, vp]
     L.gptq_quantize_qronos.argtypes = [vp, vp, i32, i32, vp, vp, i64, i64, i32, i32, i32, d, d, vp, vp, vp, vp,
                                        ctypes.POINTER(d), ctypes.POINTER(i32)]
     L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
@@ -109,7 +110,7 @@ def load_library(path: str | None = None):
     L.gptq_kernel_time.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(d), ctypes.POINTER(i64)]
     for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
                  "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up", "gptq_round_2d",
-                 "gptq_quantize_qronos",
+                 "gptq_quantize_qronos", "gptq_cross_gram",
                  "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
         getattr(L, name).restype = ctypes.c_int
     if path is None:
@@ -350,6 +351,20 @@ class Context:
                                          int(bits), int(group), int(block), _ptr(codes), _ptr(scales), _ptr(zeros),
                                          ctypes.byref(J)))
         return J.value
+
+    def cross_gram(self, X, Y, G=None):
+        """G = X^T Y (fp32 [n, n])."""
+        torch = self.torch
+        X = self._xbits(X)
+        Y = self._xbits(Y)
+        if Y.shape != X.shape or Y.stride(0) != X.stride(0):
+            raise ValueError("X and Y must have the same shape and row pitch")
+        n = X.shape[1]
+        if G is None:
+            G = torch.empty((n, n), dtype=torch.float32, device=self.device)
+        self._dev(G, torch.float32, "G")
+        self._check(self.lib.gptq_cross_gram(self.handle, _ptr(X), _ptr(Y), X.shape[0], n, X.stride(0), _ptr(G)))
+        return G
 
     def quantize_qronos(self, W, X, Xq, bits: int, group: int, block: int, lam_abs: float = 0.0,
                         lam_rel: float = 0.01, want_target: bool = False):

@@ -973,6 +973,23 @@ GPTQ_API int gptq_hessian(gptq_ctx c, const uint16_t* X, int64_t tokens, int32_t
   return run_hessian(c, {HessJob{X, tokens, ldx, n, H, accumulate ? 1 : 0}});
 }
 
+GPTQ_API int gptq_cross_gram(gptq_ctx c, const uint16_t* X, const uint16_t* Y, int64_t tokens, int32_t n,
+                             int64_t ldx, float* G) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  int rc = check_x(c, X, tokens, n, ldx);
+  if (rc) return rc;
+  if ((rc = check_x(c, Y, tokens, n, ldx))) return rc;
+  if (n > 0 && !G) return set_err(c, GPTQ_ERR_INVALID_ARG, "G is null");
+  if (n == 0) return GPTQ_OK;
+  HessJob J{X, tokens, ldx, n, G, 0};
+  J.Y = Y;
+  if (tokens > 0 && !(hess_direct(J) && ((uintptr_t)Y & 15) == 0))
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "cross Gram needs 16-byte aligned rows and n % 8 == 0");
+  DeviceGuard g(c->device);
+  return run_hessian(c, {J});
+}
+
 GPTQ_API int gptq_factor(gptq_ctx c, const float* H, int32_t n, double lam_abs, double lam_rel,
                          float* U, int32_t* info, double* lam_used) {
   if (!c) return GPTQ_ERR_INVALID_ARG;

@@ -23,7 +23,8 @@ def test_header_declares_the_pass():
     names = g.exported_symbols()
     for need in ("gptq_create", "gptq_destroy", "gptq_strerror", "gptq_last_error", "gptq_hessian",
                  "gptq_factor", "gptq_quantize", "gptq_lora", "gptq_quantize_batched", "gptq_hessian64",
-                 "gptq_olrc", "gptq_bid_up", "gptq_lora_refine", "gptq_round_2d", "gptq_quantize_qronos"):
+                 "gptq_olrc", "gptq_bid_up", "gptq_lora_refine", "gptq_round_2d", "gptq_quantize_qronos",
+                 "gptq_cross_gram"):
         assert need in names
 
 

@@ -302,3 +302,48 @@ def test_round_2d_1024_whole_oracle(ctx):
     assert info["bad"] == 0 and rep["forced"] <= 1e-4 * Z.size
     assert abs(res["J"] - rep["J"]) <= 1e-4 * rep["J"]
 
+
+@pytest.mark.timeout(900)
+def test_qronos_full(ctx):
+    """Quantised-input target on the square layer (X 262144 x 4096 and a seeded
+    perturbed Xq): sampled principal blocks of Xq^T Xq and Xq^T X against the
+    oracle's Grams of those columns, the target against the normal equations
+    on sampled rows, and the one-call path against the same steps composed
+    by hand (same bits)."""
+    sq = synth.FULL["square"][0]
+    print("qronos: generating", flush=True)
+    lay = synth.layer(sq, "cuda")
+    X = lay["X"]
+    Xq = synth.perturbed(X, sq.seed)
+    W = lay["W"]
+    res = ctx.quantize_qronos(W, X, Xq, sq.bits, sq.group, sq.block, lam_rel=sq.lam_rel, want_target=True)
+    Hq = ctx.hessian(Xq)
+    G = ctx.cross_gram(Xq, X)
+    U, _, lam = ctx.factor(Hq, lam_rel=sq.lam_rel)
+    g = ctx.quantize(res["Wt"], U, sq.bits, sq.group, sq.block, lam)
+    assert torch.equal(g["codes"], res["codes"]) and torch.equal(g["scales"], res["scales"])
+    print("qronos: checking", flush=True)
+    n = sq.n
+    cols = _rows(n, 96, 3)
+    Xb = synth.bits_to_numpy(X.cpu())
+    Xqb = synth.bits_to_numpy(Xq.cpu())
+    e_h = check_h_block(np32(Hq), Xqb, cols)
+    Gb = o.cross_gram(np.ascontiguousarray(Xqb[:, cols]), np.ascontiguousarray(Xb[:, cols]))
+    e_g = float(np.linalg.norm(np32(G).astype(np.float64)[np.ix_(cols, cols)] - Gb) / np.linalg.norm(Gb))
+    del Xb, Xqb
+    Hd = np32(Hq).astype(np.float64)
+    Gd = np32(G).astype(np.float64)
+    Hl = Hd + lam * np.eye(n)
+    ev = np.linalg.eigvalsh(Hl)
+    kappa = ev[-1] / ev[0]
+    Wd = np32(W).astype(np.float64)
+    Wt = np32(res["Wt"]).astype(np.float64)
+    worst = 0.0
+    for i in _rows(sq.out, 16, 4):
+        rhs = Gd @ Wd[i] + lam * Wd[i]
+        r = Hl @ Wt[i] - rhs
+        worst = max(worst, float(np.linalg.norm(r) / np.linalg.norm(rhs)))
+    print("qronos:", dict(h_err=e_h, g_err=e_g, kappa=kappa, normal_eq=worst, J=res["J"]), flush=True)
+    assert e_g <= 1e-5
+    assert worst <= 1e-7 * kappa + 1e-6
+
