@@ -1109,15 +1109,16 @@ GPTQ_API int gptq_quantize_batched(gptq_ctx c, int32_t nlayers, gptq_layer* laye
 
 namespace {
 
-// C[M][N] = A[M][K] B[N][K]^T (pitch ld) on the fp64 MFMA ring, 128 tiles.
-int run_gemm_nt(gptq_ctx c, const double* A, const double* B, double* C, int M, int N, int K, int ld) {
+// C[M][N] = A[M][K] B[N][K]^T (pitch ld) on the fp64 MFMA ring, 128 tiles;
+// tri = 1 / 2: B upper / lower triangular (zero part of K skipped).
+int run_gemm_nt(gptq_ctx c, const double* A, const double* B, double* C, int M, int N, int K, int ld, int tri = 0) {
   FacProb p{};
   p.A = (double*)A;
   p.Y = (double*)B;
   p.C = C;
   p.n = ld;
   const int ntiles = cdiv(M, 128) * cdiv(N, 128);
-  std::vector<Seg> segs{Seg{0, 0, ntiles, GK_NT, M, N, K, 0}};
+  std::vector<Seg> segs{Seg{0, 0, ntiles, GK_NT, M, N, K, tri}};
   Blob b;
   const size_t op = b.add(&p, 1), os = b.add(segs);
   uint8_t* d = nullptr;
@@ -1353,8 +1354,8 @@ GPTQ_API int gptq_quantize_qronos(gptq_ctx c, const float* W, int32_t out, int32
   // W* = ((W (G + lam I)^T) U^T) U in fp64
   LAUNCH(c, "k_qr_prep", launch_qr_prep(W, G, U, &ds->lam, out, n, Wd, Gd, Ud, UdT, c->stream));
   if ((rc = run_gemm_nt(c, Wd, Gd, T1, out, n, n, n))) return rc;
-  if ((rc = run_gemm_nt(c, T1, Ud, T2, out, n, n, n))) return rc;
-  if ((rc = run_gemm_nt(c, T2, UdT, Wd, out, n, n, n))) return rc;
+  if ((rc = run_gemm_nt(c, T1, Ud, T2, out, n, n, n, 1))) return rc;   // T1 U^T: U upper
+  if ((rc = run_gemm_nt(c, T2, UdT, Wd, out, n, n, n, 2))) return rc;  // T2 U = T2 (U^T)^T: U^T lower
   LAUNCH(c, "k_qr_out", launch_qr_out(Wd, Ws, (long long)on, c->stream));
   QuantJob J{Ws, out, n, n, U, bits, group, block, codes, scales, zeros, nullptr, &ds->lam, ds->obj, nullptr};
   if ((rc = run_quantize(c, {J}))) return rc;

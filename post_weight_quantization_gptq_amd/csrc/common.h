@@ -94,7 +94,9 @@ struct FacProb {
 //   time (no accumulate).
 // GK_NT: C(i, j) = sum_t A(i, t) B(j, t) with A = A [b][d], B = Y [c][d] and
 //   C [b][c], all of pitch n (a plain product of two k-contiguous operands;
-//   the flags info / nonfinite are not consulted).
+//   the flags info / nonfinite are not consulted); e = 1 or 2 declares B
+//   upper or lower triangular, so a column tile skips the zero part of K
+//   (K and the tile size multiples of 16).
 enum GemmKind { GK_CHOL_TRAIL = 0, GK_ZUPD = 1, GK_NT = 2 };
 
 // -------------------------------------------------------- two-sided round --

@@ -628,8 +628,10 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
     ldc = n;
     mt = min(TS, M - i0);
     nt = min(TS, N - j0);
-    kb = 0;
-    ke = K;
+    // e = 1: B upper triangular (B[j][t] = 0 for t < j): t from j0;
+    // e = 2: B lower triangular (B[j][t] = 0 for t > j): t below j0 + TS
+    kb = sg.e == 1 ? j0 : 0;
+    ke = sg.e == 2 ? min(K, j0 + TS) : K;
     alpha = 1.0;
     beta = 0.0;
   } else {
