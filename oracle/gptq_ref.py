@@ -41,7 +41,11 @@ from A and B directly; for the quantised-input target
 (tests/test_oracle_qronos.py) the X_q = X reduction to GPTQ, the
 completed-square identity over random codes, a least-squares route to the
 target, the nearest-plane solver on the target and the objective formed from
-the data.
+the data; for the deployable outputs (tests/test_oracle_deploy.py) the round
+trip of packed codes, the nibble and byte layouts at 4 and 8 bits, a
+hand-worked 3-bit row, per-vector round-to-nearest of L and R against the
+nearest grid level, and the dequant GEMM against the dequantised weights.
+Parity unpinned: the packed layout is a storage convention of ours.
 
 Parity unpinned (conventions that only self-consistency fixes; the GPU follows
 them exactly): the min-max grid details of ``grid_fit`` (0 inside the range,
@@ -789,3 +793,66 @@ def gptq_qronos(W, X, Xq, bits: int, group: int, block: int, lam_rel: float = 0.
     J_q = float(np.sum((Q @ Hq) * Q) - 2.0 * np.sum((Q @ G) * Wd) + np.sum((Wd @ H) * Wd))
     res.update(W_target=Wst, U=U, lam=lam, Hq=Hq, G=G, J=objective(Wst, Q, Hq), J_q=J_q)
     return res
+
+
+# --------------------------------------------------------------------------
+# deployable outputs: packed codes, low-precision L and R, the dequant GEMM
+# --------------------------------------------------------------------------
+def pack_codes(codes, bits: int) -> np.ndarray:
+    """Rows of codes as little-endian bitstreams in uint32 words: code k of a
+    row occupies bits [k bits, (k + 1) bits) of the row's stream (bit b in
+    word b // 32 at position b % 32); the row is padded to whole words with
+    zero bits.  (A storage convention: the pages give no format.)"""
+    codes = np.asarray(codes, dtype=np.int64)
+    out, n = codes.shape
+    words = (n * bits + 31) // 32
+    packed = np.zeros((out, words), dtype=np.uint32)
+    for i in range(out):
+        stream = 0
+        for k in range(n):
+            stream |= int(codes[i, k]) << (k * bits)
+        for w in range(words):
+            packed[i, w] = (stream >> (32 * w)) & 0xFFFFFFFF
+    return packed
+
+
+def unpack_codes(packed, n: int, bits: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint64)
+    out = packed.shape[0]
+    codes = np.zeros((out, n), dtype=np.uint8)
+    for i in range(out):
+        stream = 0
+        for w in range(packed.shape[1]):
+            stream |= int(packed[i, w]) << (32 * w)
+        for k in range(n):
+            codes[i, k] = (stream >> (k * bits)) & ((1 << bits) - 1)
+    return codes
+
+
+def quantize_lowrank(L, R, bits: int) -> dict:
+    """Round-to-nearest of the low-rank factors on their own grids ([LoRA]
+    results: L and R themselves at 4 and 8 bits): each rank component - a
+    column of L [n, r], a row of R [r, out] - gets the min-max grid of
+    ``grid_fit`` and the rounding of ``quantize_values`` (decisions in fp32).
+    Returns codes, scales, zeros and the dequantised L, R."""
+    maxq = (1 << bits) - 1
+    Lt = np.asarray(L, dtype=np.float64).T  # [r, n]: one component per row
+    R = np.asarray(R, dtype=np.float64)
+    res = {}
+    for name, M in (("L", Lt), ("R", R)):
+        s, rr, z, _ = grid_fit(M, maxq)
+        q, what, _ = quantize_values(M, s[:, None], rr[:, None], z[:, None], maxq)
+        res[name + "_codes"] = q.astype(np.uint8)
+        res[name + "_scales"] = s
+        res[name + "_zeros"] = z
+        res[name + "_hat"] = what
+    res["L_codes"] = res["L_codes"].T.copy()  # back to [n, r]
+    res["L_hat"] = res["L_hat"].T.copy()
+    return res
+
+
+def gemm_w4a16(X, codes, scales, zeros, group: int = 0) -> np.ndarray:
+    """Y = X What^T in float64 with What = s (q - z) per group as stored
+    (``dequantize``): the product a deployed 4-bit layer computes on bf16
+    activations (X as bf16 bit patterns or floats)."""
+    return _as_f64(X) @ dequantize(codes, scales, zeros, group).T

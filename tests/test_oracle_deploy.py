@@ -1,0 +1,77 @@
+"""Pins of the oracle's deployable outputs: packed codes against independent
+layouts (nibbles at 4 bits, bytes at 8 bits, a hand-worked 3-bit row) and the
+round trip; low-precision L and R against per-vector round-to-nearest; the
+dequant GEMM against the dequantised weights' product.  CPU only.
+"""
+import numpy as np
+import pytest
+
+from oracle import gptq_ref as o
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_pack_round_trip(bits):
+    r = np.random.default_rng(bits)
+    for n in (1, 7, 32, 61, 130):
+        q = r.integers(0, 1 << bits, (3, n)).astype(np.uint8)
+        p = o.pack_codes(q, bits)
+        assert p.shape == (3, (n * bits + 31) // 32)
+        assert np.array_equal(o.unpack_codes(p, n, bits), q)
+
+
+def test_pack_4bit_is_nibbles_and_8bit_is_bytes():
+    r = np.random.default_rng(9)
+    q4 = r.integers(0, 16, (2, 40)).astype(np.uint8)
+    p4 = o.pack_codes(q4, 4)
+    for k in range(40):
+        assert np.array_equal((p4[:, k // 8] >> (4 * (k % 8))) & 0xF, q4[:, k])
+    q8 = r.integers(0, 256, (2, 12)).astype(np.uint8)
+    assert np.array_equal(o.pack_codes(q8, 8).view(np.uint8).reshape(2, 12), q8)  # little-endian bytes
+
+
+def test_pack_3bit_hand_worked_row():
+    # codes 1..7, 0, 1, 2, 3 at 3 bits: bit offsets 0, 3, ..., 30; the last
+    # code (3 = 0b011) straddles the word boundary (bits 30, 31 | 32)
+    q = np.array([[1, 2, 3, 4, 5, 6, 7, 0, 1, 2, 3]], dtype=np.uint8)
+    w0 = (1 | 2 << 3 | 3 << 6 | 4 << 9 | 5 << 12 | 6 << 15 | 7 << 18 | 0 << 21 | 1 << 24 | 2 << 27
+          | (3 & 0b11) << 30)
+    assert o.pack_codes(q, 3).tolist() == [[w0, 0]]
+    q[0, 10] = 4  # 0b100: only bit 32 set
+    assert o.pack_codes(q, 3).tolist() == [[w0 & 0x3FFFFFFF, 1]]
+
+
+def test_lowrank_quantisation_is_per_vector_rounding():
+    r = np.random.default_rng(10)
+    L = r.normal(0, 0.1, (40, 6))
+    R = r.normal(0, 0.02, (6, 30))
+    for bits in (4, 8):
+        res = o.quantize_lowrank(L, R, bits)
+        maxq = (1 << bits) - 1
+        for k in range(6):
+            for vec, codes, s, z in ((L[:, k], res["L_codes"][:, k], res["L_scales"][k], res["L_zeros"][k]),
+                                     (R[k], res["R_codes"][k], res["R_scales"][k], res["R_zeros"][k])):
+                # the grid spans [min(v, 0), max(v, 0)] and every value goes to
+                # its nearest level (fp32)
+                lo, hi = min(vec.min(), 0), max(vec.max(), 0)
+                assert np.float32(s) == np.float32((np.float32(hi) - np.float32(lo)) / np.float32(maxq))
+                levels = (np.float32(s) * (np.arange(maxq + 1, dtype=np.float32) - np.float32(z))).astype(np.float64)
+                best = np.abs(vec[:, None] - levels[None, :]).argmin(axis=1)
+                near = np.abs(np.abs(vec[:, None] - levels[None, :]).min(axis=1) - s / 2) < 1e-6 * s
+                assert np.all((codes == best) | near)
+        err8 = np.abs(res["L_hat"] - L).max() if bits == 8 else None
+    assert err8 is not None and err8 <= 0.5 * (L.max() - min(L.min(), 0)) / 255 * 1.001
+
+
+def test_dequant_gemm_is_the_product_of_the_dequantised_weights():
+    r = np.random.default_rng(11)
+    X = r.normal(0, 1, (9, 64)).astype(np.float32).astype(np.float64)
+    q = r.integers(0, 16, (5, 64)).astype(np.uint8)
+    s = r.uniform(0.01, 0.1, (5, 2)).astype(np.float32)
+    z = r.integers(0, 16, (5, 2)).astype(np.float32)
+    Y = o.gemm_w4a16(X, q, s, z, group=32)
+    Wd = np.zeros((5, 64))
+    for i in range(5):
+        for k in range(64):
+            g = k // 32
+            Wd[i, k] = float(np.float32(s[i, g]) * np.float32(float(q[i, k]) - z[i, g]))
+    assert np.abs(Y - X @ Wd.T).max() <= 1e-12 * np.abs(Y).max()
