@@ -44,8 +44,10 @@ target, the nearest-plane solver on the target and the objective formed from
 the data; for the deployable outputs (tests/test_oracle_deploy.py) the round
 trip of packed codes, the nibble and byte layouts at 4 and 8 bits, a
 hand-worked 3-bit row, per-vector round-to-nearest of L and R against the
-nearest grid level, and the dequant GEMM against the dequantised weights.
-Parity unpinned: the packed layout is a storage convention of ours.
+nearest grid level, the dequant GEMM against the dequantised weights, and
+the bf16 rounding against torch's float32 -> bfloat16 conversion and
+hand-worked ties.  Parity unpinned: the packed layout is a storage convention
+of ours.
 
 Parity unpinned (conventions that only self-consistency fixes; the GPU follows
 them exactly): the min-max grid details of ``grid_fit`` (0 inside the range,
@@ -851,8 +853,23 @@ def quantize_lowrank(L, R, bits: int) -> dict:
     return res
 
 
-def gemm_w4a16(X, codes, scales, zeros, group: int = 0) -> np.ndarray:
+def bf16_round(v) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (ties to even), returned
+    as float32: keep the upper 16 bits of the binary32 pattern after adding
+    0x7FFF plus the lowest kept bit (finite inputs)."""
+    u = np.asarray(v, dtype=F32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(F32)
+
+
+def gemm_w4a16(X, codes, scales, zeros, group: int = 0, weight_bf16: bool = False) -> np.ndarray:
     """Y = X What^T in float64 with What = s (q - z) per group as stored
     (``dequantize``): the product a deployed 4-bit layer computes on bf16
-    activations (X as bf16 bit patterns or floats)."""
-    return _as_f64(X) @ dequantize(codes, scales, zeros, group).T
+    activations (X as bf16 bit patterns or floats).  With weight_bf16 the
+    dequantised weights are first rounded to bf16 (``bf16_round``), the
+    operand a matrix unit that multiplies bf16 by bf16 is given (our reading:
+    the pages fix no arithmetic for the product)."""
+    What = dequantize(codes, scales, zeros, group)
+    if weight_bf16:
+        What = bf16_round(What.astype(F32)).astype(np.float64)
+    return _as_f64(X) @ What.T

@@ -75,3 +75,33 @@ def test_dequant_gemm_is_the_product_of_the_dequantised_weights():
             g = k // 32
             Wd[i, k] = float(np.float32(s[i, g]) * np.float32(float(q[i, k]) - z[i, g]))
     assert np.abs(Y - X @ Wd.T).max() <= 1e-12 * np.abs(Y).max()
+
+
+def test_bf16_round_matches_torch_and_hand_worked_ties():
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(12)
+    v = np.concatenate([r.normal(0, 1, 4000), r.normal(0, 1e-30, 500), r.normal(0, 1e30, 500),
+                        [0.0, -0.0, 1.0, -2.5, 3.0e38]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(o.bf16_round(v).view(np.uint32), ref.view(np.uint32))
+    # the spacing of bf16 at 1 is 2^-7: 1 + 2^-8 is a tie going to the even 1;
+    # 1 + 3 2^-8 a tie going to the even 1 + 2^-6; just above a tie rounds up
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -(1 + 2.0 ** -8)], dtype=np.float32)
+    assert o.bf16_round(ties).tolist() == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -1.0]
+
+
+def test_dequant_gemm_with_bf16_weights():
+    # weights of the form s (q - z) with s a power of two are exact in bf16,
+    # so both forms agree exactly; otherwise each weight moves by at most half
+    # a bf16 spacing (2^-8 relative)
+    r = np.random.default_rng(13)
+    X = r.normal(0, 1, (7, 64))
+    q = r.integers(0, 16, (6, 64)).astype(np.uint8)
+    z = r.integers(0, 16, (6, 2)).astype(np.float32)
+    s2 = (2.0 ** r.integers(-8, 0, (6, 2))).astype(np.float32)
+    assert np.array_equal(o.gemm_w4a16(X, q, s2, z, 32, weight_bf16=True), o.gemm_w4a16(X, q, s2, z, 32))
+    s = r.uniform(0.01, 0.1, (6, 2)).astype(np.float32)
+    Wd = o.dequantize(q, s, z, 32)
+    Wb = (o.gemm_w4a16(np.eye(64), q, s, z, 32, weight_bf16=True)).T
+    assert np.all(np.abs(Wb - Wd) <= 2.0 ** -8 * np.abs(Wd))
+    assert np.abs(Wb - Wd).max() > 0
