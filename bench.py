@@ -239,13 +239,78 @@ def bench_qronos(args, torch, Context, synth, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_w4a16(args, torch, Context, synth, dev):
+    """The W4A16 product of a deployed 4-bit square layer: Y = X What^T with X
+    [8192, 4096] bf16 (the square layer's input recipe) and the stored form of
+    a [4096, 4096] 4-bit g128 layer (seeded codes, scales, zero points), packed
+    by the library before timing.  A step is one gptq_gemm_w4a16 call."""
+    cfg = synth.W4A16
+    M, N, K, group = cfg["M"], cfg["N"], cfg["K"], cfg["group"]
+    print("# generating w4a16 inputs", file=sys.stderr, flush=True)
+    X = synth.w4a16_inputs(M, K, 92, dev)
+    codes, scales, zeros = synth.w4_stored(N, K, group, 92)
+    ctx = Context(dev)
+    P = ctx.pack_codes(codes.to(dev), 4)
+    S, Z = scales.to(dev), zeros.to(dev)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def one_step():
+        ctx.gemm_w4a16(X, P, S, Z, group, Y=Y)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ctx.timing("k_gemm_w4a16")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms, k_n = ctx.kernel_time("k_gemm_w4a16")
+    ctx.timing(None)
+    ms_step = 1e3 * wall / args.steps
+    flops = 2.0 * M * N * K
+    avg = k_ms / max(k_n, 1)
+    ach = flops / (avg * 1e-3) / 1e12
+    line = {"metric": "TFLOP/s of the W4A16 product Y = X What^T, X [8192, 4096] bf16, 4-bit g128 [4096, 4096]",
+            "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; X from the square layer's input recipe, uniform 4-bit codes)",
+            "config": {"workload": "w4a16: X[8192,4096] bf16 x W[4096,4096] 4-bit g128 -> Y fp32"},
+            "roofline": {"kernel": "k_gemm_w4a16", "bound": "mfma", "achieved": round(ach, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None, "avg_launch_ms": round(avg, 4), "flops_per_launch": flops}}
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle import gptq_ref as o
+        rows = M  # the whole product (about 7 s on the host cores)
+        Xs = synth.bits_to_numpy(X[:rows].cpu())
+        c, sc, zf = codes.numpy(), scales.numpy(), zeros.numpy().astype(np.float32)
+        t0 = time.perf_counter()
+        o.gemm_w4a16(Xs, c, sc, zf, group, weight_bf16=True)
+        t_s = time.perf_counter() - t0
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except Exception:
+            cores = os.cpu_count()
+        line["cpu_baseline"] = {"value": round(2.0 * rows * N * K / t_s / 1e12, 4), "unit": "TFLOP/s",
+                                "cores": cores, "kind": "oracle",
+                                "sample": "the float64 product on %d of %d rows of X (dequantisation "
+                                          "included); measured %.2f s" % (rows, M, t_s)}
+    ctx.close()
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="square",
-                    choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d", "qronos"])
+                    choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d", "qronos", "w4a16"])
     ap.add_argument("--rounds", type=int, default=1, help="refinement rounds of the lora_refine workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -276,6 +341,9 @@ def main():
         return
     if args.workload == "qronos":
         bench_qronos(args, torch, Context, synth, dev)
+        return
+    if args.workload == "w4a16":
+        bench_w4a16(args, torch, Context, synth, dev)
         return
     specs = synth.FULL["lora" if args.workload == "lora_refine" else args.workload]
     print("# generating %s inputs" % args.workload, file=sys.stderr, flush=True)

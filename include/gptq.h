@@ -267,6 +267,48 @@ typedef struct {
  * first error met; per-layer info/obj are filled in for every layer. */
 int gptq_quantize_batched(gptq_ctx ctx, int32_t nlayers, gptq_layer* layers);
 
+/* Deployable outputs (GPTQ encyclopedia entry, implementations: 4-bit weights
+ * cut memory to a quarter and run through matrix kernels at inference;
+ * GPTQ-intrinsic LoRA technical summary, results: L and R themselves at 4 or
+ * 8 bits).  The pages fix no storage format; ours follows.  All ASYNC on the
+ * context's stream; device buffers, caller-owned.
+ *
+ * gptq_pack_codes: codes[rows][n] uint8 -> packed[rows][words], words =
+ * ceil(n bits / 32) uint32: each row is a little-endian bitstream, code k at
+ * stream bits [k bits, (k + 1) bits), stream bit b in word b / 32 at position
+ * b % 32, zero bits up to the end of the last word (at 4 bits: code k is the
+ * nibble 4 (k % 8) of word k / 8; at 8 bits: byte k).  Code bits above `bits`
+ * are ignored.  1 <= bits <= 8.  gptq_unpack_codes is the inverse (codes
+ * written in [0, 2^bits - 1]). */
+int gptq_pack_codes(gptq_ctx ctx, const uint8_t* codes, int32_t rows, int32_t n, int32_t bits,
+                    uint32_t* packed);
+int gptq_unpack_codes(gptq_ctx ctx, const uint32_t* packed, int32_t rows, int32_t n, int32_t bits,
+                      uint8_t* codes);
+
+/* Round-to-nearest of the low-rank factors of gptq_lora / gptq_olrc (L[n][r],
+ * R[r][out] fp32) at 2 <= bits <= 8: every rank component, a column of L and
+ * a row of R, gets its own grid fitted as in gptq_quantize (lo = min(min v,
+ * 0), hi = max(max v, 0), s = (hi - lo)/maxq, z = rne(-lo/s) in [0, maxq]),
+ * then q = clamp(rne(fl32(fl32(v * fl32(1/s)) + z))), vhat = fl32(s (q - z)).
+ * Outputs: Lcodes[n][r], Lscales[r], Lzeros[r], Rcodes[r][out], Rscales[r],
+ * Rzeros[r]; Lhat[n][r] and Rhat[r][out] the dequantised factors (each may
+ * be NULL).  r == 0 writes nothing. */
+int gptq_quantize_lowrank(gptq_ctx ctx, const float* L, const float* R, int32_t n, int32_t r, int32_t out,
+                          int32_t bits, uint8_t* Lcodes, float* Lscales, uint8_t* Lzeros, float* Lhat,
+                          uint8_t* Rcodes, float* Rscales, uint8_t* Rzeros, float* Rhat);
+
+/* W4A16 product Y = X What^T of a 4-bit layer: X[M][ldx] bf16 bits (16-byte
+ * aligned rows), packed[N][K/8] from gptq_pack_codes at 4 bits, scales[N][G]
+ * fp32 and zeros[N][G] uint8 as gptq_quantize writes them (G = K/group, or 1
+ * for group 0), What = s (q - z) per group.  Every weight enters the bf16
+ * matrix unit as bf16(fl32(s (q - z))) (nearest, ties to even); products are
+ * exact and summed in fp32.  Y[M][ldy] fp32, fully written in its M x N part.
+ * Requirements: K % 32 == 0; group 0, K, or a power of two >= 16 dividing K;
+ * ldx % 8 == 0, packed 8-byte aligned (else GPTQ_ERR_UNSUPPORTED). */
+int gptq_gemm_w4a16(gptq_ctx ctx, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
+                    const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group, float* Y,
+                    int64_t ldy);
+
 /* Measurement support (not part of the method).  gptq_timing(ctx, kernels)
  * clears the totals and from then on brackets each launch of the named
  * kernels with a pair of HIP events on the context's stream.  kernels [host]
@@ -280,7 +322,8 @@ int gptq_quantize_batched(gptq_ctx ctx, int32_t nlayers, gptq_layer* layers);
  * k_gram_chol, k_apply, k_lora_assemble, k_lora_extract, k_ref_init, k_resid,
  * k_gfinal, k_sum_parts, k_f32_to_f64, k_f64_to_f32, k_olrc_out, and for the
  * two-sided rounding k_r2d_unit, k_r2d_fill, k_r2d_tile, k_r2d_push, k_r2d_obj,
- * and for the quantised-input target k_qr_prep, k_qr_out.  gptq_kernel_time
+ * and for the quantised-input target k_qr_prep, k_qr_out, and for the
+ * deployable outputs k_pack, k_unpack, k_lr_quant, k_gemm_w4a16.  gptq_kernel_time
  * waits for the recorded events and returns the summed elapsed milliseconds
  * and the number of timed launches of kernel `name` (0 and 0 if none).  Each
  * timed launch costs two event records on the stream. */

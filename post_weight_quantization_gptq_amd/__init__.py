@@ -105,12 +105,17 @@ def load_library(path: str | None = None):
     L.gptq_cross_gram.argtypes = [vp, vp, vp, i64, i32, i64, vp]
     L.gptq_quantize_qronos.argtypes = [vp, vp, i32, i32, vp, vp, i64, i64, i32, i32, i32, d, d, vp, vp, vp, vp,
                                        ctypes.POINTER(d), ctypes.POINTER(i32)]
+    L.gptq_pack_codes.argtypes = [vp, vp, i32, i32, i32, vp]
+    L.gptq_unpack_codes.argtypes = [vp, vp, i32, i32, i32, vp]
+    L.gptq_quantize_lowrank.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.gptq_gemm_w4a16.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, vp, i64]
     L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
     L.gptq_timing.argtypes = [vp, ctypes.c_char_p]
     L.gptq_kernel_time.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(d), ctypes.POINTER(i64)]
     for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
                  "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up", "gptq_round_2d",
-                 "gptq_quantize_qronos", "gptq_cross_gram",
+                 "gptq_quantize_qronos", "gptq_cross_gram", "gptq_pack_codes", "gptq_unpack_codes",
+                 "gptq_quantize_lowrank", "gptq_gemm_w4a16",
                  "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
         getattr(L, name).restype = ctypes.c_int
     if path is None:
@@ -404,6 +409,70 @@ class Context:
         self._check(self.lib.gptq_round_2d(self.handle, _ptr(X), m, n, _ptr(UG), _ptr(UH), int(qmin), int(qmax),
                                            _ptr(Z), _ptr(D), ctypes.byref(J)))
         return dict(Z=Z, delta=D, J=J.value)
+
+    def pack_codes(self, codes, bits: int):
+        """codes uint8 [rows, n] -> int32 [rows, ceil(n bits / 32)] holding the
+        uint32 code words (little-endian bitstream per row)."""
+        torch = self.torch
+        self._dev(codes, torch.uint8, "codes")
+        rows, n = codes.shape
+        P = torch.empty((rows, (n * bits + 31) // 32), dtype=torch.int32, device=self.device)
+        self._check(self.lib.gptq_pack_codes(self.handle, _ptr(codes), rows, n, int(bits), _ptr(P)))
+        return P
+
+    def unpack_codes(self, packed, n: int, bits: int):
+        torch = self.torch
+        self._dev(packed, torch.int32, "packed")
+        rows = packed.shape[0]
+        if packed.shape[1] != (n * bits + 31) // 32:
+            raise ValueError("packed has the wrong number of words per row")
+        codes = torch.empty((rows, n), dtype=torch.uint8, device=self.device)
+        self._check(self.lib.gptq_unpack_codes(self.handle, _ptr(packed), rows, int(n), int(bits), _ptr(codes)))
+        return codes
+
+    def quantize_lowrank(self, L, R, bits: int, want_hat: bool = True):
+        """Round-to-nearest of L [n, r] and R [r, out], one grid per rank component.
+        Returns dict(L_codes, L_scales, L_zeros, L_hat, R_codes, R_scales, R_zeros, R_hat)."""
+        torch = self.torch
+        self._dev(L, torch.float32, "L")
+        self._dev(R, torch.float32, "R")
+        n, r = L.shape
+        if R.shape[0] != r:
+            raise ValueError("L and R have different ranks")
+        out = R.shape[1]
+        dev = self.device
+        res = dict(L_codes=torch.empty((n, r), dtype=torch.uint8, device=dev),
+                   L_scales=torch.empty(r, dtype=torch.float32, device=dev),
+                   L_zeros=torch.empty(r, dtype=torch.uint8, device=dev),
+                   L_hat=torch.empty((n, r), dtype=torch.float32, device=dev) if want_hat else None,
+                   R_codes=torch.empty((r, out), dtype=torch.uint8, device=dev),
+                   R_scales=torch.empty(r, dtype=torch.float32, device=dev),
+                   R_zeros=torch.empty(r, dtype=torch.uint8, device=dev),
+                   R_hat=torch.empty((r, out), dtype=torch.float32, device=dev) if want_hat else None)
+        self._check(self.lib.gptq_quantize_lowrank(
+            self.handle, _ptr(L), _ptr(R), n, r, out, int(bits), _ptr(res["L_codes"]), _ptr(res["L_scales"]),
+            _ptr(res["L_zeros"]), _ptr(res["L_hat"]), _ptr(res["R_codes"]), _ptr(res["R_scales"]),
+            _ptr(res["R_zeros"]), _ptr(res["R_hat"])))
+        return res
+
+    def gemm_w4a16(self, X, packed, scales, zeros, group: int, K: int | None = None, Y=None):
+        """Y = X What^T (fp32 [M, N]) from bf16 X [M, K] and 4-bit packed codes [N, K/8]."""
+        torch = self.torch
+        X = self._xbits(X)
+        self._dev(packed, torch.int32, "packed")
+        self._dev(scales, torch.float32, "scales")
+        self._dev(zeros, torch.uint8, "zeros")
+        M = X.shape[0]
+        K = int(K if K is not None else X.shape[1])
+        N = packed.shape[0]
+        if packed.shape[1] != K // 8:
+            raise ValueError("packed must hold K/8 words per row")
+        if Y is None:
+            Y = torch.empty((M, N), dtype=torch.float32, device=self.device)
+        self._dev(Y, torch.float32, "Y")
+        self._check(self.lib.gptq_gemm_w4a16(self.handle, _ptr(X), M, X.stride(0), _ptr(packed), _ptr(scales),
+                                             _ptr(zeros), N, K, int(group), _ptr(Y), Y.stride(0)))
+        return Y
 
     def quantize_batched(self, layers):
         """layers: list of dicts with W, bits, group, block, lam_rel (and X or H, optional lam_abs,

@@ -1412,3 +1412,83 @@ GPTQ_API int gptq_bid_up(gptq_ctx c, const float* W, int32_t out, int32_t n, con
   return refine_step(c, true, W, out, n, H, r, bits, group, block, codes, (float*)scales, (uint8_t*)zeros,
                      (float*)L, (float*)R, J);
 }
+
+// ------------------------------------------------------ deployable outputs --
+GPTQ_API int gptq_pack_codes(gptq_ctx c, const uint8_t* codes, int32_t rows, int32_t n, int32_t bits,
+                             uint32_t* packed) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (rows < 0 || n < 0 || bits < 1 || bits > 8) return set_err(c, GPTQ_ERR_INVALID_ARG, "bad packing arguments");
+  if ((int64_t)n * bits > INT32_MAX - 32) return set_err(c, GPTQ_ERR_UNSUPPORTED, "row too long to pack");
+  if (rows == 0 || n == 0) return GPTQ_OK;
+  if (!codes || !packed) return set_err(c, GPTQ_ERR_INVALID_ARG, "null buffer");
+  DeviceGuard g(c->device);
+  LAUNCH(c, "k_pack", launch_pack(codes, rows, n, bits, packed, c->stream));
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_unpack_codes(gptq_ctx c, const uint32_t* packed, int32_t rows, int32_t n, int32_t bits,
+                               uint8_t* codes) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (rows < 0 || n < 0 || bits < 1 || bits > 8) return set_err(c, GPTQ_ERR_INVALID_ARG, "bad packing arguments");
+  if ((int64_t)n * bits > INT32_MAX - 32) return set_err(c, GPTQ_ERR_UNSUPPORTED, "row too long to pack");
+  if (rows == 0 || n == 0) return GPTQ_OK;
+  if (!codes || !packed) return set_err(c, GPTQ_ERR_INVALID_ARG, "null buffer");
+  DeviceGuard g(c->device);
+  LAUNCH(c, "k_unpack", launch_unpack(packed, rows, n, bits, codes, c->stream));
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_quantize_lowrank(gptq_ctx c, const float* L, const float* R, int32_t n, int32_t r, int32_t out,
+                                   int32_t bits, uint8_t* Lcodes, float* Lscales, uint8_t* Lzeros, float* Lhat,
+                                   uint8_t* Rcodes, float* Rscales, uint8_t* Rzeros, float* Rhat) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (n < 0 || r < 0 || out < 0 || bits < 2 || bits > 8)
+    return set_err(c, GPTQ_ERR_INVALID_ARG, "bad low-rank quantisation arguments");
+  if (r == 0) return GPTQ_OK;
+  if (n == 0 || out == 0) return set_err(c, GPTQ_ERR_INVALID_ARG, "empty factor with r > 0");
+  if (!L || !R || !Lcodes || !Lscales || !Lzeros || !Rcodes || !Rscales || !Rzeros)
+    return set_err(c, GPTQ_ERR_INVALID_ARG, "null buffer");
+  DeviceGuard g(c->device);
+  LrProb p{L, R, Lcodes, Lscales, Lzeros, Lhat, Rcodes, Rscales, Rzeros, Rhat, n, r, out, (1 << bits) - 1};
+  LAUNCH(c, "k_lr_quant", launch_lr_quant(p, c->stream));
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
+                             const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group,
+                             float* Y, int64_t ldy) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  if (M < 0 || N < 0 || K < 0 || group < 0) return set_err(c, GPTQ_ERR_INVALID_ARG, "negative size");
+  if (M > INT32_MAX - 512) return set_err(c, GPTQ_ERR_UNSUPPORTED, "M too large");
+  if (M == 0 || N == 0) return GPTQ_OK;
+  if (!X || !packed || !scales || !zeros || !Y) return set_err(c, GPTQ_ERR_INVALID_ARG, "null buffer");
+  if (ldx < K || ldy < N) return set_err(c, GPTQ_ERR_INVALID_ARG, "pitch smaller than the row");
+  if (K == 0 || K % 32 != 0 || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0 || ((uintptr_t)packed & 7) != 0)
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs K %% 32 == 0 and 16-byte aligned rows of X");
+  int gshift = 31;
+  if (group != 0 && group != K) {
+    if (group < 16 || (group & (group - 1)) != 0 || K % group != 0)
+      return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs group 0 or a power of two >= 16 dividing K");
+    gshift = __builtin_ctz((unsigned)group);
+  }
+  DeviceGuard g(c->device);
+  W4Prob p{};
+  p.X = X;
+  p.P = packed;
+  p.S = scales;
+  p.Z = zeros;
+  p.Y = Y;
+  p.ldx = ldx;
+  p.ldy = ldy;
+  p.M = (int)M;
+  p.N = N;
+  p.K = K;
+  p.G = gshift == 31 ? 1 : K / group;
+  p.gshift = gshift;
+  LAUNCH(c, "k_gemm_w4a16", launch_gemm_w4a16(p, c->stream));
+  return GPTQ_OK;
+}

@@ -116,6 +116,35 @@ struct R2dProb {
   int m, n, qmin, qmax;
 };
 
+// Round-to-nearest of the low-rank factors: components 0..r-1 are the columns
+// of L [n][r], r..2r-1 the rows of R [r][out]; each gets its own grid.
+struct LrProb {
+  const float* L;
+  const float* R;
+  uint8_t* Lc;  // [n][r]
+  float* Ls;    // [r]
+  uint8_t* Lz;  // [r]
+  float* Lh;    // [n][r] dequantised (may be null)
+  uint8_t* Rc;  // [r][out]
+  float* Rs;
+  uint8_t* Rz;
+  float* Rh;    // [r][out] (may be null)
+  int n, r, out, maxq;
+};
+
+// Y[M][N] = X[M][K] What^T with What = s (q - z) from packed 4-bit codes.
+struct W4Prob {
+  const uint16_t* X;  // bf16 bits, row pitch ldx
+  const uint32_t* P;  // [N][K/8] code words (code k at bits 4(k%8) of word k/8)
+  const float* S;     // [N][G]
+  const uint8_t* Z;   // [N][G]
+  float* Y;           // row pitch ldy
+  long long ldx, ldy;
+  int M, N, K, G;
+  int gshift;  // group = 2^gshift (31: one group per row)
+  int tiles_m, tiles_n;
+};
+
 // ------------------------------------------------------------------ sweep --
 struct QLayer {
   const float* W;   // original weights [out][n]

@@ -1,0 +1,300 @@
+// Deployable outputs of a quantised layer (gfx950): packed code words, the
+// low-rank factors on low-precision grids, and the product of bf16
+// activations with 4-bit weights (W4A16).
+//
+// GPTQ encyclopedia entry, implementations: 4-bit weights cut a model's
+// memory to a quarter and are used through matrix kernels at inference;
+// GPTQ-intrinsic LoRA technical summary, results: L and R themselves stored
+// at 4 or 8 bits.  The pages fix no storage format; ours is stated per kernel.
+#include "common.h"
+#include "grid.h"
+#include "launch.h"
+
+typedef const __attribute__((address_space(1))) uint32_t gu32;
+typedef const __attribute__((address_space(1))) uint8_t gu8;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------- packing --
+// Rows of codes as little-endian bitstreams in 32-bit words: code k of a row
+// occupies stream bits [k bits, (k + 1) bits), stream bit b sits in word b/32
+// at position b%32, and the row ends in zero bits up to a whole word.  One
+// thread per output word; bits of a code above `bits` are ignored.
+__global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ codes, int rows, int n, int bits,
+                                              int words, uint32_t* __restrict__ out) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)rows * words) return;
+  const int i = (int)(idx / words), w = (int)(idx % words);
+  const uint8_t* c = codes + (size_t)i * n;
+  const int b0 = 32 * w;
+  const int kend = min(n, (b0 + 31) / bits + 1);
+  const uint32_t mask = (1u << bits) - 1u;
+  uint32_t v = 0;
+  for (int k = b0 / bits; k < kend; ++k) {
+    const int off = k * bits - b0;  // negative for a code begun in the previous word
+    const uint32_t q = c[k] & mask;
+    v |= off >= 0 ? (q << off) : (q >> -off);
+  }
+  out[idx] = v;
+}
+
+// The inverse: one thread per code.
+__global__ __launch_bounds__(256) void k_unpack(const uint32_t* __restrict__ packed, int rows, int n, int bits,
+                                                int words, uint8_t* __restrict__ codes) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)rows * n) return;
+  const int i = (int)(idx / n), k = (int)(idx % n);
+  const uint32_t* p = packed + (size_t)i * words;
+  const int b = k * bits, w = b >> 5, off = b & 31;
+  uint32_t v = p[w] >> off;
+  if (off + bits > 32) v |= p[w + 1] << (32 - off);
+  codes[idx] = (uint8_t)(v & ((1u << bits) - 1u));
+}
+
+// ------------------------------------------------- low-rank factors --
+// One workgroup per rank component (a column of L, then a row of R): the
+// min-max grid of the sweep over the component, then round-to-nearest with
+// the sweep's fp32 steps, x = fl32(fl32(v r) + z), q = clamp(rne(x)),
+// vhat = fl32(s (q - z)).
+__global__ __launch_bounds__(256) void k_lr_quant(const LrProb p) {
+  __shared__ float red[2][4];
+  const int c = blockIdx.x, tid = threadIdx.x;
+  const bool isL = c < p.r;
+  const int comp = isL ? c : c - p.r;
+  const int len = isL ? p.n : p.out;
+  const size_t stride = isL ? (size_t)p.r : 1;
+  const size_t base = isL ? (size_t)comp : (size_t)comp * p.out;
+  const float* src = (isL ? p.L : p.R) + base;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = tid; i < len; i += 256) {
+    const float v = src[i * stride];
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = mn;
+    red[1][tid >> 6] = mx;
+  }
+  __syncthreads();
+  mn = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
+  mx = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  const float maxq = (float)p.maxq;
+  const Grid g = grid_from(mn, mx, maxq);
+  uint8_t* codes = (isL ? p.Lc : p.Rc) + base;
+  float* hat = isL ? p.Lh : p.Rh;
+  if (tid == 0) {
+    (isL ? p.Ls : p.Rs)[comp] = g.s;
+    (isL ? p.Lz : p.Rz)[comp] = (uint8_t)g.z;
+  }
+  for (int i = tid; i < len; i += 256) {
+    const float v = src[i * stride];
+    const float x = __fadd_rn(__fmul_rn(v, g.r), g.z);
+    const float q = fminf(fmaxf(rintf(x), 0.f), maxq);
+    codes[i * stride] = (uint8_t)q;
+    if (hat) hat[base + i * stride] = __fmul_rn(g.s, q - g.z);
+  }
+}
+
+// ------------------------------------------------------ W4A16 product --
+// Y = X What^T, X [M][K] bf16, What = s (q - z) per (row, group) from the
+// packed 4-bit codes, on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// The matrix unit multiplies bf16 by bf16, so each weight enters as
+// bf16(fl32(s (q - z))) (round to nearest even); the activations are exact.
+//
+// Tile: 256 rows of X x 128 rows of the codes per workgroup, four waves of
+// 128 x 64 (4 x 2 MFMA accumulators, 128 AGPRs); K in steps of 32.
+//   A: X rows go from L2 straight into LDS (global_load_lds, 16 B per lane)
+//      two steps ahead, in a ring of three 16 KB stages.  Each 64-byte LDS
+//      row holds its four 16-byte k-chunks XOR-swizzled by (row / 4) % 4, so
+//      a fragment read of 16 consecutive rows covers all 64 banks.
+//   B: every thread loads two code words (16 codes of one row) one step
+//      ahead into registers, dequantises them with the group's s, z and
+//      writes the bf16 values into a double-buffered 8 KB LDS stage in the
+//      same swizzled layout; the MFMA lanes then read A and B fragments alike.
+// One barrier per step.  Code rows past N and X rows past M are read clamped
+// (valid memory) and never stored.
+#define W4_BM 256
+#define W4_BN 128
+#define W4_KS 32
+#define W4_AST (W4_BM * W4_KS * 2)
+#define W4_BST (W4_BN * W4_KS * 2)
+#define W4_NA 3
+
+// eight codes of one word -> eight bf16 of fl32(s (q - z)), codes in order
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float z) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x2 v;
+    v.x = __fmul_rn((float)((w >> (8 * j)) & 15u) - z, s);
+    v.y = __fmul_rn((float)((w >> (8 * j + 4)) & 15u) - z, s);
+    o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+__global__ __launch_bounds__(256, 1) void k_gemm_w4a16(const W4Prob p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[W4_NA * W4_AST + 2 * W4_BST];
+  uint8_t* const As = lds;
+  uint8_t* const Bs = lds + W4_NA * W4_AST;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // Consecutive workgroups go to the eight XCDs in turn; give XCD x a
+  // contiguous run of tiles (row-panel major), so the workgroups resident on
+  // one XCD share the X panel through its L2.
+  const int nt = p.tiles_m * p.tiles_n;
+  const int xcd = blockIdx.x & 7;
+  const int T = xcd * (nt >> 3) + min(xcd, nt & 7) + (blockIdx.x >> 3);
+  const int m0 = (T / p.tiles_n) * W4_BM, n0 = (T % p.tiles_n) * W4_BN;
+  const int nsteps = p.K / W4_KS, last = nsteps - 1;
+
+  // A copy: instruction q of wave w fills LDS rows 16 (4q + w) .. +15 of a
+  // stage; lane -> row 16 (4q + w) + lane / 4 at chunk position lane % 4,
+  // holding k-chunk (lane % 4) ^ (lane / 16).
+  const uint16_t* ga[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = min(m0 + 16 * (4 * q + w) + (lane >> 2), p.M - 1);
+    ga[q] = p.X + (size_t)row * p.ldx + 8 * ((lane & 3) ^ (lane >> 4));
+  }
+  auto issue_a = [&](int step, int stage) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(ga[q] + step * W4_KS),
+                                       (lds_void*)(As + stage * W4_AST + (4 * q + w) * 1024), 16, 0, 0);
+  };
+  // B: thread -> code row n0 + tid / 2, words 2 (tid % 2) and 2 (tid % 2) + 1
+  // of each step (codes 16 (tid % 2) .. +15), k-chunks 2 (tid % 2), +1.
+  const int nl = tid >> 1, bp = tid & 1;
+  const int nrow = min(n0 + nl, p.N - 1);
+  gu32* gb = (gu32*)(p.P + (size_t)nrow * (p.K >> 3) + 2 * bp);
+  gfloat* gs = (gfloat*)(p.S + (size_t)nrow * p.G);
+  gu8* gz = (gu8*)(p.Z + (size_t)nrow * p.G);
+  const int bsw = (nl >> 2) & 3;
+  uint8_t* const bdst0 = Bs + nl * 64 + (((2 * bp) ^ bsw) << 4);
+  uint8_t* const bdst1 = Bs + nl * 64 + (((2 * bp + 1) ^ bsw) << 4);
+  // groups are powers of two >= 16 (or the whole row), so the 16 codes of a
+  // thread share one (s, z)
+  uint32_t bw0, bw1;
+  float bsc, bzp;
+  auto load_b = [&](int step) {
+    const int g = (step * W4_KS + 16 * bp) >> p.gshift;
+    bw0 = gb[4 * step];
+    bw1 = gb[4 * step + 1];
+    bsc = gs[g];
+    bzp = (float)gz[g];
+  };
+  auto store_b = [&](int stage) {
+    *(u32x4*)(bdst0 + stage * W4_BST) = dequant8(bw0, bsc, bzp);
+    *(u32x4*)(bdst1 + stage * W4_BST) = dequant8(bw1, bsc, bzp);
+  };
+
+  // fragments: wave w owns rows 128 (w / 2) and columns 64 (w % 2) of the
+  // tile; lane -> fragment row lane % 32, k-chunk 2 ks + lane / 32
+  const int sw = (lane >> 2) & 3, hh = lane >> 5, r31 = lane & 31;
+  const int wm0 = 128 * (w >> 1), wn0 = 64 * (w & 1);
+  auto rd = [&](int sa, int sb, int ks, bf16x8* fa, bf16x8* fb) {
+    const int ch = ((2 * ks + hh) ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(As + sa * W4_AST + (wm0 + 32 * i + r31) * 64 + ch);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = *(const bf16x8*)(Bs + sb * W4_BST + (wn0 + 32 * j + r31) * 64 + ch);
+  };
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Prologue: step 0 in LDS (A copied, B dequantised), step 1 in flight.
+  // Past the last step the copies repeat the last step into stages nobody
+  // reads again, so every step ends with the same four copies outstanding.
+  load_b(0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  store_b(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_b(min(1, last));
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a(min(1, last), 1);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 fa[4], fb[2];
+  for (int s = 0; s < nsteps; ++s) {
+    // A(s) and the code words of step s + 1 have landed (only A(s + 1) may
+    // be in flight); after the barrier B(s) is visible and the stages of
+    // step s - 1 are free.
+    __builtin_amdgcn_s_waitcnt(VmWait<4>::value);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int sa = s % W4_NA, sb = s & 1;
+    rd(sa, sb, 0, fa, fb);
+    mma(fa, fb);
+    // dequantise the code words of step s + 1 beside the MFMAs, then reuse
+    // their registers for step s + 2
+    if (s < last) store_b(sb ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(min(s + 2, last));
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(min(s + 2, last), (s + 2) % W4_NA);
+    __builtin_amdgcn_sched_barrier(0);
+    rd(sa, sb, 1, fa, fb);
+    mma(fa, fb);
+  }
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::value);  // no copy into LDS outlives the group
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn0 + 32 * j + r31;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (row < p.M && col < p.N) p.Y[(size_t)row * p.ldy + col] = acc[i][j][r];
+      }
+    }
+}
+
+// ------------------------------------------------------------ launchers --
+hipError_t launch_pack(const uint8_t* codes, int rows, int n, int bits, uint32_t* out, hipStream_t st) {
+  const int words = (int)(((long long)n * bits + 31) / 32);
+  const long long cnt = (long long)rows * words;
+  if (cnt == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, codes, rows, n, bits, words,
+                     out);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint32_t* packed, int rows, int n, int bits, uint8_t* codes, hipStream_t st) {
+  const int words = (int)(((long long)n * bits + 31) / 32);
+  const long long cnt = (long long)rows * n;
+  if (cnt == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_unpack, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, packed, rows, n, bits,
+                     words, codes);
+  return hipGetLastError();
+}
+
+hipError_t launch_lr_quant(const LrProb& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_lr_quant, dim3(2 * p.r), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a16(W4Prob p, hipStream_t st) {
+  p.tiles_m = (p.M + W4_BM - 1) / W4_BM;
+  p.tiles_n = (p.N + W4_BN - 1) / W4_BN;
+  hipLaunchKernelGGL(k_gemm_w4a16, dim3(p.tiles_m * p.tiles_n), dim3(256), 0, st, p);
+  return hipGetLastError();
+}

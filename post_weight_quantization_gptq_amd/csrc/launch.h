@@ -47,3 +47,10 @@ hipError_t launch_r2d_obj(const double* objp, int nt, double* J, hipStream_t st)
 hipError_t launch_qr_prep(const float* W, const float* G, const float* U, const double* lam, int out, int n,
                           double* Wd, double* Gd, double* Ud, double* UdT, hipStream_t st);
 hipError_t launch_qr_out(const double* a, float* b, long long cnt, hipStream_t st);
+
+// deployable outputs (deploy.hip)
+hipError_t launch_pack(const uint8_t* codes, int rows, int n, int bits, uint32_t* out, hipStream_t st);
+hipError_t launch_unpack(const uint32_t* packed, int rows, int n, int bits, uint8_t* codes, hipStream_t st);
+hipError_t launch_lr_quant(const LrProb& p, hipStream_t st);
+// sets the tile counts itself; K % 32 == 0
+hipError_t launch_gemm_w4a16(W4Prob p, hipStream_t st);

@@ -25,6 +25,11 @@ columns sign-fixed by sign(diag R)):
             the second (output-side) Gram of the two-sided rounding
   qronos    the square layer, its X and Xq = bf16(X + N(0, (0.05 std X)^2))
             standing in for the inputs of an already-quantised network
+  w4a16     the stored form of a 4-bit [4096, 4096] layer (codes uniform on
+            0..15, per-(row, group of 128) scales U(0.005, 0.01) and zero
+            points uniform on 0..15, the ranges a min-max grid gives on
+            N(0, 0.02^2) weights) applied to 8192 tokens of the square layer's
+            input recipe
 where Z has i.i.d. N(0, 1) entries and i = 1..n indexes the input channels.
 """
 from __future__ import annotations
@@ -199,3 +204,25 @@ def layer(spec: LayerSpec, device="cpu"):
 def bits_to_numpy(X: torch.Tensor) -> np.ndarray:
     """bf16 bit patterns (int16 tensor) -> uint16 numpy array (for the oracle)."""
     return X.detach().cpu().numpy().view(np.uint16)
+
+
+def w4_stored(N: int, K: int, group: int, seed: int):
+    """Seeded stand-in for a 4-bit layer's stored form: codes [N, K] uint8
+    uniform on 0..15, scales [N, G] float32 U(0.005, 0.01), zeros [N, G] uint8
+    uniform on 0..15 (G = K / group, 1 for group 0)."""
+    g = torch.Generator().manual_seed(70_000 + seed)
+    G = K // group if group else 1
+    codes = torch.randint(0, 16, (N, K), generator=g, dtype=torch.int64).to(torch.uint8)
+    scales = (0.005 + 0.005 * torch.rand((N, G), generator=g, dtype=torch.float64)).to(torch.float32)
+    zeros = torch.randint(0, 16, (N, G), generator=g, dtype=torch.int64).to(torch.uint8)
+    return codes, scales, zeros
+
+
+W4A16 = dict(M=8192, N=4096, K=4096, group=128)
+
+
+def w4a16_inputs(M: int, K: int, seed: int, device="cpu") -> torch.Tensor:
+    """Activations X [M, K] (bf16 bits) from the square layer's input recipe."""
+    spec = LayerSpec("w4a16_x", K, K, M, 4, 128, 128, 0.01, decay=0.4, outlier_channels=8 if K >= 64 else 0,
+                     seed=seed)
+    return calibration(spec, device)

@@ -24,7 +24,8 @@ def test_header_declares_the_pass():
     for need in ("gptq_create", "gptq_destroy", "gptq_strerror", "gptq_last_error", "gptq_hessian",
                  "gptq_factor", "gptq_quantize", "gptq_lora", "gptq_quantize_batched", "gptq_hessian64",
                  "gptq_olrc", "gptq_bid_up", "gptq_lora_refine", "gptq_round_2d", "gptq_quantize_qronos",
-                 "gptq_cross_gram"):
+                 "gptq_cross_gram", "gptq_pack_codes", "gptq_unpack_codes", "gptq_quantize_lowrank",
+                 "gptq_gemm_w4a16"):
         assert need in names
 
 
@@ -46,6 +47,8 @@ def test_null_context_is_rejected_without_a_gpu(lib):
     assert lib.gptq_quantize(None, None, 0, 0, None, 4, 0, 128, 0.0, None, None, None, None, None) == 1
     info = ctypes.c_int32(0)
     assert lib.gptq_factor(None, None, 0, 0.0, 0.0, None, ctypes.byref(info), None) == 1
+    assert lib.gptq_gemm_w4a16(None, None, 0, 0, None, None, None, 0, 0, 0, None, 0) == 1
+    assert lib.gptq_pack_codes(None, None, 0, 0, 4, None) == 1
     assert lib.gptq_destroy(None) == 1
     assert lib.gptq_create(None, 0, None) == 1
     assert lib.gptq_strerror(2) == b"damped Hessian is not positive definite"

@@ -347,3 +347,29 @@ def test_qronos_full(ctx):
     assert e_g <= 1e-5
     assert worst <= 1e-7 * kappa + 1e-6
 
+
+
+def test_w4a16_full(ctx):
+    # the product bench.py times: X [8192, 4096], 4-bit g128 [4096, 4096];
+    # sampled rows of Y against the oracle's float64 product on bf16-rounded
+    # weights, to the fp32 summation bound gamma_K sum |x w|
+    cfg = synth.W4A16
+    M, N, K, group = cfg["M"], cfg["N"], cfg["K"], cfg["group"]
+    print("w4a16 full", M, N, K, group, flush=True)
+    X = synth.w4a16_inputs(M, K, 92, "cuda")
+    codes, scales, zeros = synth.w4_stored(N, K, group, 92)
+    P = ctx.pack_codes(codes.cuda(), 4)
+    assert np.array_equal(np32(P).view(np.uint32)[:8], o.pack_codes(codes[:8].numpy(), 4))
+    Y = ctx.gemm_w4a16(X, P, scales.cuda(), zeros.cuda(), group)
+    rows = _rows(M, 48, 93)
+    Xs = o._as_f64(synth.bits_to_numpy(X[torch.from_numpy(rows).cuda()]))
+    zf = zeros.numpy().astype(np.float32)
+    Wb = o.bf16_round(o.dequantize(codes.numpy(), scales.numpy(), zf, group).astype(np.float32)).astype(np.float64)
+    ref = Xs @ Wb.T
+    mag = np.abs(Xs) @ np.abs(Wb).T
+    gam = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+    err = np.abs(np32(Y)[rows].astype(np.float64) - ref)
+    info = dict(max_err_over_mag=float((err / mag).max()), gamma_K=gam,
+                rel_fro=float(np.linalg.norm(err) / np.linalg.norm(ref)))
+    print(info, flush=True)
+    assert np.all(err <= gam * mag), info
