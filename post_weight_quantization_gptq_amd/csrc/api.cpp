@@ -1471,8 +1471,8 @@ GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t l
     return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs K %% 32 == 0 and 16-byte aligned rows of X");
   int gshift = 31;
   if (group != 0 && group != K) {
-    if (group < 16 || (group & (group - 1)) != 0 || K % group != 0)
-      return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs group 0 or a power of two >= 16 dividing K");
+    if (group < 8 || (group & (group - 1)) != 0 || K % group != 0)
+      return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs group 0 or a power of two >= 8 dividing K");
     gshift = __builtin_ctz((unsigned)group);
   }
   DeviceGuard g(c->device);
@@ -1489,6 +1489,8 @@ GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t l
   p.K = K;
   p.G = gshift == 31 ? 1 : K / group;
   p.gshift = gshift;
-  LAUNCH(c, "k_gemm_w4a16", launch_gemm_w4a16(p, c->stream));
+  // 512-row tiles (8 waves: each dequantised code tile feeds twice the
+  // MFMAs) once X has more than 256 rows, else 256 x 128 (4 waves)
+  LAUNCH(c, "k_gemm_w4a16", launch_gemm_w4a16(p, M > 256 ? 1 : 0, c->stream));
   return GPTQ_OK;
 }

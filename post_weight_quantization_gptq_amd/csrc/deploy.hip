@@ -106,24 +106,25 @@ __global__ __launch_bounds__(256) void k_lr_quant(const LrProb p) {
 // The matrix unit multiplies bf16 by bf16, so each weight enters as
 // bf16(fl32(s (q - z))) (round to nearest even); the activations are exact.
 //
-// Tile: 256 rows of X x 128 rows of the codes per workgroup, four waves of
-// 128 x 64 (4 x 2 MFMA accumulators, 128 AGPRs); K in steps of 32.
+// Tile: BM rows of X x BN rows of the codes per workgroup, one wave per
+// 128 x 64 block of it (4 x 2 MFMA accumulators); K in steps of 32.  The
+// large-M shape is 512 x 128 (8 waves): each dequantised code tile then
+// feeds twice the MFMAs of a 256-row tile.
 //   A: X rows go from L2 straight into LDS (global_load_lds, 16 B per lane)
-//      two steps ahead, in a ring of three 16 KB stages.  Each 64-byte LDS
-//      row holds its four 16-byte k-chunks XOR-swizzled by (row / 4) % 4, so
-//      a fragment read of 16 consecutive rows covers all 64 banks.
-//   B: every thread loads two code words (16 codes of one row) one step
-//      ahead into registers, dequantises them with the group's s, z and
-//      writes the bf16 values into a double-buffered 8 KB LDS stage in the
-//      same swizzled layout; the MFMA lanes then read A and B fragments alike.
-// One barrier per step.  Code rows past N and X rows past M are read clamped
-// (valid memory) and never stored.
-#define W4_BM 256
-#define W4_BN 128
+//      three steps ahead, in a ring of four stages.  Each 64-byte LDS row
+//      holds its four 16-byte k-chunks XOR-swizzled by (row / 4) % 4, so a
+//      fragment read of 16 consecutive rows covers all 64 banks.
+//   B: every thread loads WPT code words one step ahead into registers,
+//      dequantises them with the group's s, z (reloaded only where a group
+//      starts) and writes the bf16 values into a double-buffered LDS stage in
+//      the same swizzled layout; the MFMA lanes then read A and B alike.
+// One barrier per step.  The fragments of the first 16-k sub-step of a step
+// are read right after the barrier, beside the previous step's last MFMAs;
+// the second sub-step's are read beside the first sub-step's MFMAs, which
+// also hide the dequantisation of the next step.  Code rows past N and X
+// rows past M are read clamped (valid memory) and never stored.
 #define W4_KS 32
-#define W4_AST (W4_BM * W4_KS * 2)
-#define W4_BST (W4_BN * W4_KS * 2)
-#define W4_NA 3
+#define W4_NA 4
 
 // eight codes of one word -> eight bf16 of fl32(s (q - z)), codes in order
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float z) {
@@ -138,71 +139,86 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float z) {
   return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-__global__ __launch_bounds__(256, 1) void k_gemm_w4a16(const W4Prob p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[W4_NA * W4_AST + 2 * W4_BST];
+template <int BM, int BN>
+__global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4Prob p) {
+  constexpr int WN = BN / 64;               // waves across the codes (each 128 x 64)
+  constexpr int NW = (BM / 128) * WN;       // waves
+  constexpr int AST = BM * W4_KS * 2;       // bytes of an A stage
+  constexpr int BST = BN * W4_KS * 2;       // bytes of a B stage
+  constexpr int NQ = BM / 16 / NW;          // global_load_lds per lane per stage
+  constexpr int WPT = BN * 4 / (64 * NW);   // code words per thread per step
+  constexpr int TPR = 4 / WPT;              // threads per code row
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[W4_NA * AST + 2 * BST];
   uint8_t* const As = lds;
-  uint8_t* const Bs = lds + W4_NA * W4_AST;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint8_t* const Bs = lds + W4_NA * AST;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets on the scalar unit
   // Consecutive workgroups go to the eight XCDs in turn; give XCD x a
   // contiguous run of tiles (row-panel major), so the workgroups resident on
   // one XCD share the X panel through its L2.
   const int nt = p.tiles_m * p.tiles_n;
   const int xcd = blockIdx.x & 7;
   const int T = xcd * (nt >> 3) + min(xcd, nt & 7) + (blockIdx.x >> 3);
-  const int m0 = (T / p.tiles_n) * W4_BM, n0 = (T % p.tiles_n) * W4_BN;
+  const int m0 = (T / p.tiles_n) * BM, n0 = (T % p.tiles_n) * BN;
   const int nsteps = p.K / W4_KS, last = nsteps - 1;
 
-  // A copy: instruction q of wave w fills LDS rows 16 (4q + w) .. +15 of a
-  // stage; lane -> row 16 (4q + w) + lane / 4 at chunk position lane % 4,
+  // A copy: instruction q of wave w fills LDS rows 16 (NW q + w) .. +15 of a
+  // stage; lane -> row 16 (NW q + w) + lane / 4 at chunk position lane % 4,
   // holding k-chunk (lane % 4) ^ (lane / 16).
-  const uint16_t* ga[4];
+  const uint16_t* ga[NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = min(m0 + 16 * (4 * q + w) + (lane >> 2), p.M - 1);
+  for (int q = 0; q < NQ; ++q) {
+    const int row = min(m0 + 16 * (NW * q + w) + (lane >> 2), p.M - 1);
     ga[q] = p.X + (size_t)row * p.ldx + 8 * ((lane & 3) ^ (lane >> 4));
   }
   auto issue_a = [&](int step, int stage) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < NQ; ++q)
       __builtin_amdgcn_global_load_lds((const void*)(ga[q] + step * W4_KS),
-                                       (lds_void*)(As + stage * W4_AST + (4 * q + w) * 1024), 16, 0, 0);
+                                       (lds_void*)(As + stage * AST + (NW * q + w) * 1024), 16, 0, 0);
   };
-  // B: thread -> code row n0 + tid / 2, words 2 (tid % 2) and 2 (tid % 2) + 1
-  // of each step (codes 16 (tid % 2) .. +15), k-chunks 2 (tid % 2), +1.
-  const int nl = tid >> 1, bp = tid & 1;
+  // B: thread -> code row n0 + tid / TPR, words WPT (tid % TPR) .. +WPT-1 of
+  // each step (k-chunks of the same numbers).  Groups are powers of two of
+  // at least 8 codes (or the whole row), so one (s, z) serves a word.
+  const int nl = tid / TPR, c0 = WPT * (tid % TPR);
   const int nrow = min(n0 + nl, p.N - 1);
-  gu32* gb = (gu32*)(p.P + (size_t)nrow * (p.K >> 3) + 2 * bp);
+  gu32* gb = (gu32*)(p.P + (size_t)nrow * (p.K >> 3) + c0);
   gfloat* gs = (gfloat*)(p.S + (size_t)nrow * p.G);
   gu8* gz = (gu8*)(p.Z + (size_t)nrow * p.G);
   const int bsw = (nl >> 2) & 3;
-  uint8_t* const bdst0 = Bs + nl * 64 + (((2 * bp) ^ bsw) << 4);
-  uint8_t* const bdst1 = Bs + nl * 64 + (((2 * bp + 1) ^ bsw) << 4);
-  // groups are powers of two >= 16 (or the whole row), so the 16 codes of a
-  // thread share one (s, z)
-  uint32_t bw0, bw1;
-  float bsc, bzp;
+  uint32_t bw[WPT];
+  float bsc[WPT], bzp[WPT];
+  // s, z are reloaded only where a group starts (every step for groups
+  // shorter than a step); they stay in registers in between
+  const unsigned gmask = (1u << p.gshift) - 1u;
   auto load_b = [&](int step) {
-    const int g = (step * W4_KS + 16 * bp) >> p.gshift;
-    bw0 = gb[4 * step];
-    bw1 = gb[4 * step + 1];
-    bsc = gs[g];
-    bzp = (float)gz[g];
+    const bool fresh = p.gshift < 5 || ((unsigned)(step * W4_KS) & gmask) == 0;  // uniform
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+      bw[u] = gb[4 * step + u];
+      if (fresh) {
+        const int g = (step * W4_KS + 8 * (c0 + u)) >> p.gshift;
+        bsc[u] = gs[g];
+        bzp[u] = (float)gz[g];
+      }
+    }
   };
   auto store_b = [&](int stage) {
-    *(u32x4*)(bdst0 + stage * W4_BST) = dequant8(bw0, bsc, bzp);
-    *(u32x4*)(bdst1 + stage * W4_BST) = dequant8(bw1, bsc, bzp);
+#pragma unroll
+    for (int u = 0; u < WPT; ++u)
+      *(u32x4*)(Bs + stage * BST + nl * 64 + (((c0 + u) ^ bsw) << 4)) = dequant8(bw[u], bsc[u], bzp[u]);
   };
 
-  // fragments: wave w owns rows 128 (w / 2) and columns 64 (w % 2) of the
+  // fragments: wave w owns rows 128 (w / WN) and columns 64 (w % WN) of the
   // tile; lane -> fragment row lane % 32, k-chunk 2 ks + lane / 32
   const int sw = (lane >> 2) & 3, hh = lane >> 5, r31 = lane & 31;
-  const int wm0 = 128 * (w >> 1), wn0 = 64 * (w & 1);
+  const int wm0 = 128 * (w / WN), wn0 = 64 * (w % WN);
   auto rd = [&](int sa, int sb, int ks, bf16x8* fa, bf16x8* fb) {
     const int ch = ((2 * ks + hh) ^ sw) << 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(As + sa * W4_AST + (wm0 + 32 * i + r31) * 64 + ch);
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(As + sa * AST + (wm0 + 32 * i + r31) * 64 + ch);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[j] = *(const bf16x8*)(Bs + sb * W4_BST + (wn0 + 32 * j + r31) * 64 + ch);
+    for (int j = 0; j < 2; ++j) fb[j] = *(const bf16x8*)(Bs + sb * BST + (wn0 + 32 * j + r31) * 64 + ch);
   };
   f32x16 acc[4][2];
 #pragma unroll
@@ -218,9 +234,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(const W4Prob p) {
       for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
 
-  // Prologue: step 0 in LDS (A copied, B dequantised), step 1 in flight.
-  // Past the last step the copies repeat the last step into stages nobody
-  // reads again, so every step ends with the same four copies outstanding.
+  // Prologue: step 0 in LDS (A copied, B dequantised), steps 1 and 2 in
+  // flight, the first sub-step's fragments read.  Past the last step the
+  // copies repeat the last step into stages nobody reads again, so copies
+  // keep flowing at the same rate to the end.
   load_b(0);
   __builtin_amdgcn_sched_barrier(0);
   issue_a(0, 0);
@@ -230,28 +247,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(const W4Prob p) {
   load_b(min(1, last));
   __builtin_amdgcn_sched_barrier(0);
   issue_a(min(1, last), 1);
+  issue_a(min(2, last), 2);
   __builtin_amdgcn_sched_barrier(0);
-  bf16x8 fa[4], fb[2];
+  __builtin_amdgcn_s_waitcnt(VmWait<2 * NQ>::value);  // A(0) (only A(1), A(2) may be in flight)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+  rd(0, 0, 0, fa0, fb0);
+  // Step s: the second sub-step's fragments are read while the first
+  // sub-step's MFMAs run beside the dequantisation of step s + 1; then the
+  // code words of step s + 2 and the X copy of step s + 3 go out, the
+  // barrier publishes step s + 1, and the next step's first fragments are
+  // read while the second sub-step's MFMAs run.  Before the barrier every
+  // wave has its own LDS reads back (lgkmcnt 0), so the stages it read may be
+  // overwritten after it.
   for (int s = 0; s < nsteps; ++s) {
-    // A(s) and the code words of step s + 1 have landed (only A(s + 1) may
-    // be in flight); after the barrier B(s) is visible and the stages of
-    // step s - 1 are free.
-    __builtin_amdgcn_s_waitcnt(VmWait<4>::value);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
     const int sa = s % W4_NA, sb = s & 1;
-    rd(sa, sb, 0, fa, fb);
-    mma(fa, fb);
-    // dequantise the code words of step s + 1 beside the MFMAs, then reuse
-    // their registers for step s + 2
-    if (s < last) store_b(sb ^ 1);
+    rd(sa, sb, 1, fa1, fb1);
+    mma(fa0, fb0);
+    store_b(sb ^ 1);  // at the last step: rewrites the stage of step s - 1, read by no one
     __builtin_amdgcn_sched_barrier(0);
     load_b(min(s + 2, last));
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(min(s + 2, last), (s + 2) % W4_NA);
+    issue_a(min(s + 3, last), (s + 3) % W4_NA);
     __builtin_amdgcn_sched_barrier(0);
-    rd(sa, sb, 1, fa, fb);
-    mma(fa, fb);
+    // A(s + 1) has landed: at least the NQ copies of each of A(s + 2),
+    // A(s + 3) and the code-word load of step s + 2 were issued after it
+    // (vmcnt counts loads in issue order)
+    __builtin_amdgcn_s_waitcnt(VmWait<2 * NQ + 1>::value & ~(15 << 8));  // and lgkmcnt == 0
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (s < last) rd((s + 1) % W4_NA, sb ^ 1, 0, fa0, fb0);
+    mma(fa1, fb1);
   }
   __builtin_amdgcn_s_waitcnt(VmWait<0>::value);  // no copy into LDS outlives the group
 
@@ -292,9 +319,16 @@ hipError_t launch_lr_quant(const LrProb& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_w4a16(W4Prob p, hipStream_t st) {
-  p.tiles_m = (p.M + W4_BM - 1) / W4_BM;
-  p.tiles_n = (p.N + W4_BN - 1) / W4_BN;
-  hipLaunchKernelGGL(k_gemm_w4a16, dim3(p.tiles_m * p.tiles_n), dim3(256), 0, st, p);
+hipError_t launch_gemm_w4a16(W4Prob p, int shape, hipStream_t st) {
+  const int bm = shape == 1 ? 512 : 256, bn = shape == 2 ? 256 : 128;
+  p.tiles_m = (p.M + bm - 1) / bm;
+  p.tiles_n = (p.N + bn - 1) / bn;
+  const dim3 grid(p.tiles_m * p.tiles_n);
+  if (shape == 1)
+    hipLaunchKernelGGL((k_gemm_w4a16<512, 128>), grid, dim3(512), 0, st, p);
+  else if (shape == 2)
+    hipLaunchKernelGGL((k_gemm_w4a16<256, 256>), grid, dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_gemm_w4a16<256, 128>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
