@@ -74,19 +74,24 @@ def cpu_baseline(spec, lay, max_rows=512, tok_sample=32768):
                                                                t_h, t_f, t_s)}
 
 
-def syrk_traffic(workload):
-    """HBM bytes per k_syrk launch from the committed counter summary, or None
-    when absent or taken on a different kernel source."""
+def kernel_traffic(kernel, workload, source):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>_<workload>_traffic.json, or None when absent or taken on
+    a different version of its source file."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "k_syrk_%s_traffic.json" % workload)
-    src = os.path.join(ROOT, "post_weight_quantization_gptq_amd", "csrc", "syrk.hip")
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kernel, workload))
+    src = os.path.join(ROOT, "post_weight_quantization_gptq_amd", "csrc", source)
     try:
         rec = json.load(open(path))
-        if rec.get("syrk_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
             return None
         return rec.get("bytes_per_launch")
     except Exception:
         return None
+
+
+def syrk_traffic(workload):
+    return kernel_traffic("k_syrk", workload, "syrk.hip")
 
 
 PEAK_FP32_MATRIX_TFLOPS = 157.3  # dense fp32 MFMA, MI355X
@@ -282,7 +287,9 @@ def bench_w4a16(args, torch, Context, synth, dev):
             "config": {"workload": "w4a16: X[8192,4096] bf16 x W[4096,4096] 4-bit g128 -> Y fp32"},
             "roofline": {"kernel": "k_gemm_w4a16", "bound": "mfma", "achieved": round(ach, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None, "avg_launch_ms": round(avg, 4), "flops_per_launch": flops}}
+                         "traffic": kernel_traffic("k_gemm_w4a16", "w4a16", "deploy.hip"),
+                         "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
+                         "algorithmic_bytes_per_launch": M * K * 2 + N * K // 2 + N * (K // group) * 5 + M * N * 4}}
     if not args.no_cpu_baseline:
         import numpy as np
         from oracle import gptq_ref as o

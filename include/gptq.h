@@ -267,11 +267,12 @@ typedef struct {
  * first error met; per-layer info/obj are filled in for every layer. */
 int gptq_quantize_batched(gptq_ctx ctx, int32_t nlayers, gptq_layer* layers);
 
-/* Deployable outputs (GPTQ encyclopedia entry, implementations: 4-bit weights
- * cut memory to a quarter and run through matrix kernels at inference;
- * GPTQ-intrinsic LoRA technical summary, results: L and R themselves at 4 or
- * 8 bits).  The pages fix no storage format; ours follows.  All ASYNC on the
- * context's stream; device buffers, caller-owned.
+/* Deployable outputs (GPTQ encyclopedia entry, technical approach: the
+ * quantised weights are used through GPU matrix kernels at inference;
+ * performance and accuracy: 4-bit weights take a quarter of the fp32 memory;
+ * GPTQ-intrinsic LoRA technical summary, results: L and R themselves at low
+ * precision, 4 and 8 bits).  The pages fix no storage format; ours follows.
+ * All ASYNC on the context's stream; device buffers, caller-owned.
  *
  * gptq_pack_codes: codes[rows][n] uint8 -> packed[rows][words], words =
  * ceil(n bits / 32) uint32: each row is a little-endian bitstream, code k at
@@ -286,16 +287,17 @@ int gptq_unpack_codes(gptq_ctx ctx, const uint32_t* packed, int32_t rows, int32_
                       uint8_t* codes);
 
 /* Round-to-nearest of the low-rank factors of gptq_lora / gptq_olrc (L[n][r],
- * R[r][out] fp32) at 2 <= bits <= 8: every rank component, a column of L and
- * a row of R, gets its own grid fitted as in gptq_quantize (lo = min(min v,
- * 0), hi = max(max v, 0), s = (hi - lo)/maxq, z = rne(-lo/s) in [0, maxq]),
+ * R[r][out] fp32), L at bits_L and R at bits_R (each 2..8): every rank
+ * component, a column of L and a row of R, gets its own grid fitted as in
+ * gptq_quantize (lo = min(min v, 0), hi = max(max v, 0), s = (hi - lo)/maxq,
+ * z = rne(-lo/s) in [0, maxq], maxq = 2^bits - 1 of its factor),
  * then q = clamp(rne(fl32(fl32(v * fl32(1/s)) + z))), vhat = fl32(s (q - z)).
  * Outputs: Lcodes[n][r], Lscales[r], Lzeros[r], Rcodes[r][out], Rscales[r],
  * Rzeros[r]; Lhat[n][r] and Rhat[r][out] the dequantised factors (each may
  * be NULL).  r == 0 writes nothing. */
 int gptq_quantize_lowrank(gptq_ctx ctx, const float* L, const float* R, int32_t n, int32_t r, int32_t out,
-                          int32_t bits, uint8_t* Lcodes, float* Lscales, uint8_t* Lzeros, float* Lhat,
-                          uint8_t* Rcodes, float* Rscales, uint8_t* Rzeros, float* Rhat);
+                          int32_t bits_L, int32_t bits_R, uint8_t* Lcodes, float* Lscales, uint8_t* Lzeros,
+                          float* Lhat, uint8_t* Rcodes, float* Rscales, uint8_t* Rzeros, float* Rhat);
 
 /* W4A16 product Y = X What^T of a 4-bit layer: X[M][ldx] bf16 bits (16-byte
  * aligned rows), packed[N][K/8] from gptq_pack_codes at 4 bits, scales[N][G]

@@ -831,17 +831,18 @@ def unpack_codes(packed, n: int, bits: int) -> np.ndarray:
     return codes
 
 
-def quantize_lowrank(L, R, bits: int) -> dict:
+def quantize_lowrank(L, R, bits: int, bits_R: int | None = None) -> dict:
     """Round-to-nearest of the low-rank factors on their own grids ([LoRA]
-    results: L and R themselves at 4 and 8 bits): each rank component - a
-    column of L [n, r], a row of R [r, out] - gets the min-max grid of
-    ``grid_fit`` and the rounding of ``quantize_values`` (decisions in fp32).
+    results: L and R themselves at low precision, 4 and 8 bits; L at `bits`,
+    R at `bits_R`, by default the same): each rank component - a column of L
+    [n, r], a row of R [r, out] - gets the min-max grid of ``grid_fit`` and the
+    rounding of ``quantize_values`` (decisions in fp32).
     Returns codes, scales, zeros and the dequantised L, R."""
-    maxq = (1 << bits) - 1
     Lt = np.asarray(L, dtype=np.float64).T  # [r, n]: one component per row
     R = np.asarray(R, dtype=np.float64)
     res = {}
-    for name, M in (("L", Lt), ("R", R)):
+    for name, M, b in (("L", Lt, bits), ("R", R, bits if bits_R is None else bits_R)):
+        maxq = (1 << b) - 1
         s, rr, z, _ = grid_fit(M, maxq)
         q, what, _ = quantize_values(M, s[:, None], rr[:, None], z[:, None], maxq)
         res[name + "_codes"] = q.astype(np.uint8)

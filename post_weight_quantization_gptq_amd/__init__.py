@@ -107,7 +107,7 @@ def load_library(path: str | None = None):
                                        ctypes.POINTER(d), ctypes.POINTER(i32)]
     L.gptq_pack_codes.argtypes = [vp, vp, i32, i32, i32, vp]
     L.gptq_unpack_codes.argtypes = [vp, vp, i32, i32, i32, vp]
-    L.gptq_quantize_lowrank.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.gptq_quantize_lowrank.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gptq_gemm_w4a16.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, vp, i64]
     L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
     L.gptq_timing.argtypes = [vp, ctypes.c_char_p]
@@ -430,8 +430,9 @@ class Context:
         self._check(self.lib.gptq_unpack_codes(self.handle, _ptr(packed), rows, int(n), int(bits), _ptr(codes)))
         return codes
 
-    def quantize_lowrank(self, L, R, bits: int, want_hat: bool = True):
-        """Round-to-nearest of L [n, r] and R [r, out], one grid per rank component.
+    def quantize_lowrank(self, L, R, bits: int, bits_R: int | None = None, want_hat: bool = True):
+        """Round-to-nearest of L [n, r] at `bits` and R [r, out] at `bits_R` (default: the
+        same), one grid per rank component.
         Returns dict(L_codes, L_scales, L_zeros, L_hat, R_codes, R_scales, R_zeros, R_hat)."""
         torch = self.torch
         self._dev(L, torch.float32, "L")
@@ -450,7 +451,8 @@ class Context:
                    R_zeros=torch.empty(r, dtype=torch.uint8, device=dev),
                    R_hat=torch.empty((r, out), dtype=torch.float32, device=dev) if want_hat else None)
         self._check(self.lib.gptq_quantize_lowrank(
-            self.handle, _ptr(L), _ptr(R), n, r, out, int(bits), _ptr(res["L_codes"]), _ptr(res["L_scales"]),
+            self.handle, _ptr(L), _ptr(R), n, r, out, int(bits), int(bits if bits_R is None else bits_R),
+            _ptr(res["L_codes"]), _ptr(res["L_scales"]),
             _ptr(res["L_zeros"]), _ptr(res["L_hat"]), _ptr(res["R_codes"]), _ptr(res["R_scales"]),
             _ptr(res["R_zeros"]), _ptr(res["R_hat"])))
         return res

@@ -1441,18 +1441,19 @@ GPTQ_API int gptq_unpack_codes(gptq_ctx c, const uint32_t* packed, int32_t rows,
 }
 
 GPTQ_API int gptq_quantize_lowrank(gptq_ctx c, const float* L, const float* R, int32_t n, int32_t r, int32_t out,
-                                   int32_t bits, uint8_t* Lcodes, float* Lscales, uint8_t* Lzeros, float* Lhat,
-                                   uint8_t* Rcodes, float* Rscales, uint8_t* Rzeros, float* Rhat) {
+                                   int32_t bits_L, int32_t bits_R, uint8_t* Lcodes, float* Lscales, uint8_t* Lzeros,
+                                   float* Lhat, uint8_t* Rcodes, float* Rscales, uint8_t* Rzeros, float* Rhat) {
   if (!c) return GPTQ_ERR_INVALID_ARG;
   c->err.clear();
-  if (n < 0 || r < 0 || out < 0 || bits < 2 || bits > 8)
+  if (n < 0 || r < 0 || out < 0 || bits_L < 2 || bits_L > 8 || bits_R < 2 || bits_R > 8)
     return set_err(c, GPTQ_ERR_INVALID_ARG, "bad low-rank quantisation arguments");
   if (r == 0) return GPTQ_OK;
   if (n == 0 || out == 0) return set_err(c, GPTQ_ERR_INVALID_ARG, "empty factor with r > 0");
   if (!L || !R || !Lcodes || !Lscales || !Lzeros || !Rcodes || !Rscales || !Rzeros)
     return set_err(c, GPTQ_ERR_INVALID_ARG, "null buffer");
   DeviceGuard g(c->device);
-  LrProb p{L, R, Lcodes, Lscales, Lzeros, Lhat, Rcodes, Rscales, Rzeros, Rhat, n, r, out, (1 << bits) - 1};
+  LrProb p{L, R, Lcodes, Lscales, Lzeros, Lhat, Rcodes, Rscales, Rzeros, Rhat, n, r, out, (1 << bits_L) - 1,
+           (1 << bits_R) - 1, 0};
   LAUNCH(c, "k_lr_quant", launch_lr_quant(p, c->stream));
   return GPTQ_OK;
 }

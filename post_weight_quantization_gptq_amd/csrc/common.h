@@ -129,7 +129,8 @@ struct LrProb {
   float* Rs;
   uint8_t* Rz;
   float* Rh;    // [r][out] (may be null)
-  int n, r, out, maxq;
+  int n, r, out, maxqL, maxqR;
+  int pad0;
 };
 
 // Y[M][N] = X[M][K] What^T with What = s (q - z) from packed 4-bit codes.

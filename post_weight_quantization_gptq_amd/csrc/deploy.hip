@@ -2,10 +2,11 @@
 // low-rank factors on low-precision grids, and the product of bf16
 // activations with 4-bit weights (W4A16).
 //
-// GPTQ encyclopedia entry, implementations: 4-bit weights cut a model's
-// memory to a quarter and are used through matrix kernels at inference;
-// GPTQ-intrinsic LoRA technical summary, results: L and R themselves stored
-// at 4 or 8 bits.  The pages fix no storage format; ours is stated per kernel.
+// GPTQ encyclopedia entry, technical approach (the quantised weights are used
+// through GPU matrix kernels at inference) and performance and accuracy
+// (4-bit weights take a quarter of the fp32 memory); GPTQ-intrinsic LoRA
+// technical summary, results: L and R themselves stored at low precision (4
+// and 8 bits).  The pages fix no storage format; ours is stated per kernel.
 #include "common.h"
 #include "grid.h"
 #include "launch.h"
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void k_lr_quant(const LrProb p) {
   __syncthreads();
   mn = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
   mx = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-  const float maxq = (float)p.maxq;
+  const float maxq = (float)(isL ? p.maxqL : p.maxqR);
   const Grid g = grid_from(mn, mx, maxq);
   uint8_t* codes = (isL ? p.Lc : p.Rc) + base;
   float* hat = isL ? p.Lh : p.Rh;

@@ -61,13 +61,13 @@ def _lowrank_case(n, r, out, seed):
     return L, R
 
 
-@pytest.mark.parametrize("n,r,out,bits", [(64, 4, 48, 4), (300, 16, 257, 8), (2048, 64, 2048, 4), (1, 1, 1, 8),
-                                          (513, 3, 9, 2)])
-def test_lowrank_quantisation_bit_exact(ctx, n, r, out, bits):
-    print("lowrank", n, r, out, bits, flush=True)
+@pytest.mark.parametrize("n,r,out,bits,bits_R", [(64, 4, 48, 4, 4), (300, 16, 257, 8, 8), (2048, 64, 2048, 4, 8),
+                                                 (1, 1, 1, 8, 8), (513, 3, 9, 2, 2), (96, 5, 200, 8, 3)])
+def test_lowrank_quantisation_bit_exact(ctx, n, r, out, bits, bits_R):
+    print("lowrank", n, r, out, bits, bits_R, flush=True)
     L, R = _lowrank_case(n, r, out, n + r + out)
-    res = ctx.quantize_lowrank(torch.from_numpy(L).cuda(), torch.from_numpy(R).cuda(), bits)
-    ref = o.quantize_lowrank(L, R, bits)
+    res = ctx.quantize_lowrank(torch.from_numpy(L).cuda(), torch.from_numpy(R).cuda(), bits, bits_R)
+    ref = o.quantize_lowrank(L, R, bits, bits_R)
     for side in ("L", "R"):
         assert np.array_equal(np32(res[side + "_codes"]), ref[side + "_codes"]), side
         assert np.array_equal(np32(res[side + "_scales"]), ref[side + "_scales"].astype(np.float32)), side
@@ -86,6 +86,10 @@ def test_lowrank_of_a_lora_run(ctx):
     for bits in (4, 8):
         q = ctx.quantize_lowrank(res["L"], res["R"], bits)
         ref = o.quantize_lowrank(L, R, bits)
+        if bits == 4:  # and the pages' pairing, L at 4 bits with R at 8
+            qm = ctx.quantize_lowrank(res["L"], res["R"], 4, 8)
+            rm = o.quantize_lowrank(L, R, 4, 8)
+            assert np.array_equal(np32(qm["R_codes"]), rm["R_codes"]) and np.array_equal(np32(qm["L_codes"]), rm["L_codes"])
         assert np.array_equal(np32(q["L_codes"]), ref["L_codes"]) and np.array_equal(np32(q["R_codes"]), ref["R_codes"])
         LR = L.astype(np.float64) @ R
         errs.append(np.abs(np32(q["L_hat"]).astype(np.float64) @ np32(q["R_hat"]) - LR).max() / np.abs(LR).max())

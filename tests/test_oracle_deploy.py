@@ -105,3 +105,13 @@ def test_dequant_gemm_with_bf16_weights():
     Wb = (o.gemm_w4a16(np.eye(64), q, s, z, 32, weight_bf16=True)).T
     assert np.all(np.abs(Wb - Wd) <= 2.0 ** -8 * np.abs(Wd))
     assert np.abs(Wb - Wd).max() > 0
+
+
+def test_lowrank_mixed_widths_take_each_factor_at_its_own_width():
+    # [LoRA] results: L and R at 4 and 8 bits respectively
+    r = np.random.default_rng(14)
+    L, R = r.normal(0, 0.1, (30, 5)), r.normal(0, 0.02, (5, 20))
+    mixed, a, b = o.quantize_lowrank(L, R, 4, 8), o.quantize_lowrank(L, R, 4), o.quantize_lowrank(L, R, 8)
+    for k in ("codes", "scales", "zeros", "hat"):
+        assert np.array_equal(mixed["L_" + k], a["L_" + k]) and np.array_equal(mixed["R_" + k], b["R_" + k])
+    assert mixed["L_codes"].max() <= 15 and mixed["R_codes"].max() > 15
