@@ -442,7 +442,9 @@ def main():
         fl.append(f)
     total_flops = sum(f["total"] for f in fl)
     tflops = total_flops / (ms_step * 1e-3) / 1e12
-    line = {"metric": METRIC, "value": round(ms_layer, 4), "unit": "ms/layer", "n_gpus": 1,
+    metric = METRIC if args.workload == "square" else (
+        "ms per layer + TFLOP/s (frac of MFMA peak), GPTQ, %s workload (%d layers per step)" % (args.workload, len(specs)))
+    line = {"metric": metric, "value": round(ms_layer, 4), "unit": "ms/layer", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
             "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded; shapes, spectra and outliers of the pages' layers)",
