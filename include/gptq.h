@@ -305,8 +305,9 @@ int gptq_quantize_lowrank(gptq_ctx ctx, const float* L, const float* R, int32_t 
  * for group 0), What = s (q - z) per group.  Every weight enters the bf16
  * matrix unit as bf16(fl32(s (q - z))) (nearest, ties to even); products are
  * exact and summed in fp32.  Y[M][ldy] fp32, fully written in its M x N part.
- * Requirements: K % 32 == 0; group 0, K, or a power of two >= 8 dividing K;
- * ldx % 8 == 0, packed 8-byte aligned (else GPTQ_ERR_UNSUPPORTED). */
+ * K == 0 writes zeros.  Requirements: K % 32 == 0; group 0, K, or a power of
+ * two >= 8 dividing K; ldx % 8 == 0, packed 8-byte aligned (else
+ * GPTQ_ERR_UNSUPPORTED). */
 int gptq_gemm_w4a16(gptq_ctx ctx, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
                     const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group, float* Y,
                     int64_t ldy);

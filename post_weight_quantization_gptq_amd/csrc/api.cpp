@@ -220,6 +220,7 @@ struct DeviceGuard {
 };
 
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+inline long long cdiv64(long long a, long long b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------ Hessian plan --
 struct HessJob {
@@ -1466,10 +1467,17 @@ GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t l
   if (M < 0 || N < 0 || K < 0 || group < 0) return set_err(c, GPTQ_ERR_INVALID_ARG, "negative size");
   if (M > INT32_MAX - 512) return set_err(c, GPTQ_ERR_UNSUPPORTED, "M too large");
   if (M == 0 || N == 0) return GPTQ_OK;
-  if (!X || !packed || !scales || !zeros || !Y) return set_err(c, GPTQ_ERR_INVALID_ARG, "null buffer");
+  if (!Y || (K > 0 && (!X || !packed || !scales || !zeros))) return set_err(c, GPTQ_ERR_INVALID_ARG, "null buffer");
   if (ldx < K || ldy < N) return set_err(c, GPTQ_ERR_INVALID_ARG, "pitch smaller than the row");
-  if (K == 0 || K % 32 != 0 || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0 || ((uintptr_t)packed & 7) != 0)
+  if (K == 0) {  // an empty sum: Y = 0 (the other operands are not read)
+    DeviceGuard g(c->device);
+    HIPCHK(c, hipMemset2DAsync(Y, (size_t)ldy * sizeof(float), 0, (size_t)N * sizeof(float), (size_t)M, c->stream));
+    return GPTQ_OK;
+  }
+  if (K % 32 != 0 || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0 || ((uintptr_t)packed & 7) != 0)
     return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs K %% 32 == 0 and 16-byte aligned rows of X");
+  if ((long long)cdiv64(M, 256) * cdiv64(N, 128) > INT32_MAX)
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 product too large for one launch");
   int gshift = 31;
   if (group != 0 && group != K) {
     if (group < 8 || (group & (group - 1)) != 0 || K % group != 0)

@@ -125,7 +125,7 @@ def _check_gemm(Y, Xb, codes, scales, zeros, group, rows=None):
 
 @pytest.mark.parametrize("M,N,K,group", [(1, 1, 32, 0), (100, 70, 96, 32), (300, 200, 256, 128), (257, 129, 512, 0),
                                          (513, 384, 1024, 64), (256, 128, 64, 16), (70, 260, 128, 128), (600, 130, 64, 8),
-                                         (1100, 256, 256, 0)])
+                                         (1100, 256, 256, 0), (64, 40, 96, 96)])
 def test_gemm_w4a16_matches_oracle(ctx, M, N, K, group):
     print("gemm", M, N, K, group, flush=True)
     X, codes, scales, zeros = _gemm_case(M, N, K, group, M + N + K)
@@ -170,6 +170,15 @@ def test_gemm_w4a16_of_a_gptq_layer(ctx):
     Y = ctx.gemm_w4a16(X[:1000], P, q["scales"], q["zeros"], 128)
     codes, scales, zeros = np32(q["codes"]), np32(q["scales"]), np32(q["zeros"])
     _check_gemm(np32(Y), synth.bits_to_numpy(lay["X"][:1000]), codes, scales, zeros, 128)
+
+
+def test_gemm_w4a16_empty_sum_is_zero(ctx):
+    X = torch.zeros((5, 8), dtype=torch.int16, device="cuda")
+    P = torch.zeros((3, 0), dtype=torch.int32, device="cuda")
+    Y = torch.full((5, 3), 9.0, device="cuda")
+    ctx.gemm_w4a16(X, P, torch.ones((3, 1), device="cuda"), torch.zeros((3, 1), dtype=torch.uint8, device="cuda"), 0,
+                   K=0, Y=Y)
+    assert torch.count_nonzero(Y).item() == 0
 
 
 def test_gemm_w4a16_rejects_unsupported(ctx):
