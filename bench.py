@@ -249,9 +249,14 @@ def bench_w4a16(args, torch, Context, synth, dev):
     """The W4A16 product of a deployed 4-bit square layer: Y = X What^T with X
     [8192, 4096] bf16 (the square layer's input recipe) and the stored form of
     a [4096, 4096] 4-bit g128 layer (seeded codes, scales, zero points), packed
-    by the library before timing.  A step is one gptq_gemm_w4a16 call."""
+    by the library before timing.  A step is one gptq_gemm_w4a16 call.  The
+    w4a16_decode workload applies the same layer to 16 tokens (the few-row
+    kernel), reported in microseconds against the HBM roof."""
     cfg = synth.W4A16
     M, N, K, group = cfg["M"], cfg["N"], cfg["K"], cfg["group"]
+    decode = args.workload == "w4a16_decode"
+    if decode:
+        M = synth.W4A16_DECODE_M
     print("# generating w4a16 inputs", file=sys.stderr, flush=True)
     X = synth.w4a16_inputs(M, K, 92, dev)
     codes, scales, zeros = synth.w4_stored(N, K, group, 92)
@@ -267,19 +272,35 @@ def bench_w4a16(args, torch, Context, synth, dev):
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    ctx.timing("k_gemm_w4a16")
+    ctx.timing("k_gemv_w4a16" if decode else "k_gemm_w4a16")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         one_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    k_ms, k_n = ctx.kernel_time("k_gemm_w4a16")
+    kname = "k_gemv_w4a16" if decode else "k_gemm_w4a16"
+    k_ms, k_n = ctx.kernel_time(kname)
     ctx.timing(None)
     ms_step = 1e3 * wall / args.steps
     flops = 2.0 * M * N * K
     avg = k_ms / max(k_n, 1)
     ach = flops / (avg * 1e-3) / 1e12
+    alg_bytes = M * K * 2 + N * K // 2 + N * (K // group) * 5 + M * N * 4
+    if decode:
+        gbs = alg_bytes / (avg * 1e-3) / 1e9
+        line = {"metric": "us per W4A16 product at decode size, X [%d, 4096] bf16, 4-bit g128 [4096, 4096]" % M,
+                "value": round(ms_step * 1e3, 2), "unit": "us/product", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": False, "scaling": "weak",
+                "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic (seeded; X from the square layer's input recipe, uniform 4-bit codes)",
+                "config": {"workload": "w4a16_decode: X[%d,4096] bf16 x W[4096,4096] 4-bit g128 -> Y fp32" % M},
+                "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                             "avg_launch_ms": round(avg, 5), "bytes_per_launch": alg_bytes}}
+        ctx.close()
+        print(json.dumps(line), flush=True)
+        return
     line = {"metric": "TFLOP/s of the W4A16 product Y = X What^T, X [8192, 4096] bf16, 4-bit g128 [4096, 4096]",
             "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -290,7 +311,7 @@ def bench_w4a16(args, torch, Context, synth, dev):
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                          "traffic": kernel_traffic("k_gemm_w4a16", "w4a16", "deploy.hip"),
                          "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
-                         "algorithmic_bytes_per_launch": M * K * 2 + N * K // 2 + N * (K // group) * 5 + M * N * 4}}
+                         "algorithmic_bytes_per_launch": alg_bytes}}
     if not args.no_cpu_baseline:
         import numpy as np
         from oracle import gptq_ref as o
@@ -318,7 +339,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="square",
-                    choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d", "qronos", "w4a16"])
+                    choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d", "qronos", "w4a16",
+                             "w4a16_decode"])
     ap.add_argument("--rounds", type=int, default=1, help="refinement rounds of the lora_refine workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -350,7 +372,7 @@ def main():
     if args.workload == "qronos":
         bench_qronos(args, torch, Context, synth, dev)
         return
-    if args.workload == "w4a16":
+    if args.workload in ("w4a16", "w4a16_decode"):
         bench_w4a16(args, torch, Context, synth, dev)
         return
     specs = synth.FULL["lora" if args.workload == "lora_refine" else args.workload]

@@ -304,7 +304,8 @@ int gptq_quantize_lowrank(gptq_ctx ctx, const float* L, const float* R, int32_t 
  * fp32 and zeros[N][G] uint8 as gptq_quantize writes them (G = K/group, or 1
  * for group 0), What = s (q - z) per group.  Every weight enters the bf16
  * matrix unit as bf16(fl32(s (q - z))) (nearest, ties to even); products are
- * exact and summed in fp32.  Y[M][ldy] fp32, fully written in its M x N part.
+ * exact and summed in fp32 (for M <= 16 a split-K kernel sums in another
+ * order).  Y[M][ldy] fp32, fully written in its M x N part.
  * K == 0 writes zeros.  Requirements: K % 32 == 0; group 0, K, or a power of
  * two >= 8 dividing K; ldx % 8 == 0, packed 8-byte aligned (else
  * GPTQ_ERR_UNSUPPORTED). */
@@ -326,7 +327,8 @@ int gptq_gemm_w4a16(gptq_ctx ctx, const uint16_t* X, int64_t M, int64_t ldx, con
  * k_gfinal, k_sum_parts, k_f32_to_f64, k_f64_to_f32, k_olrc_out, and for the
  * two-sided rounding k_r2d_unit, k_r2d_fill, k_r2d_tile, k_r2d_push, k_r2d_obj,
  * and for the quantised-input target k_qr_prep, k_qr_out, and for the
- * deployable outputs k_pack, k_unpack, k_lr_quant, k_gemm_w4a16.  gptq_kernel_time
+ * deployable outputs k_pack, k_unpack, k_lr_quant, k_gemm_w4a16,
+ * k_gemv_w4a16.  gptq_kernel_time
  * waits for the recorded events and returns the summed elapsed milliseconds
  * and the number of timed launches of kernel `name` (0 and 0 if none).  Each
  * timed launch costs two event records on the stream. */

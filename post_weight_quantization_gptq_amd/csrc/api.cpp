@@ -1498,6 +1498,10 @@ GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t l
   p.K = K;
   p.G = gshift == 31 ? 1 : K / group;
   p.gshift = gshift;
+  if (M <= 16) {  // decode-sized: split K over 16 x 16 blocks, bound by reading the codes
+    LAUNCH(c, "k_gemv_w4a16", launch_gemv_w4a16(p, c->stream));
+    return GPTQ_OK;
+  }
   // 512-row tiles (8 waves: each dequantised code tile feeds twice the
   // MFMAs) once X has more than 256 rows, else 256 x 128 (4 waves)
   LAUNCH(c, "k_gemm_w4a16", launch_gemm_w4a16(p, M > 256 ? 1 : 0, c->stream));

@@ -296,6 +296,63 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
     }
 }
 
+// ------------------------------------------------ W4A16 product, few rows --
+// The same product for M <= 16 rows of X (decode-sized batches), where the
+// tiled kernel would run almost empty: the work is reading the codes.  One
+// workgroup of 8 waves per 16 rows of the codes (16 columns of Y); the waves
+// split K in eight.  Per 32-k step, lane (j = lane % 16, c = lane / 16)
+// dequantises code word (row n0 + j, k-chunk c) into its B operand and takes
+// X[j][k + 8c .. +7] (row j clamped to M - 1) as its A operand, and
+// v_mfma_f32_16x16x32_bf16 accumulates the 16 x 16 block of Y.  The eight
+// partial blocks are summed in LDS in a fixed order.  The arithmetic per
+// entry is that of the tiled kernel (bf16 weights, exact products, fp32
+// sums); only the order of the sums differs.
+#define W4V_NW 8
+__global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
+  __shared__ f32x4 red[W4V_NW][64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int j = lane & 15, c = lane >> 4;
+  const int nrow = min(n0 + j, p.N - 1);
+  const int nsteps = p.K / 32;
+  const int s0 = (int)((long long)nsteps * w / W4V_NW), s1 = (int)((long long)nsteps * (w + 1) / W4V_NW);
+  gu32* gb = (gu32*)(p.P + (size_t)nrow * (p.K >> 3) + c);
+  gfloat* gs = (gfloat*)(p.S + (size_t)nrow * p.G);
+  gu8* gz = (gu8*)(p.Z + (size_t)nrow * p.G);
+  const u32x4* xr = (const u32x4*)(p.X + (size_t)min(j, p.M - 1) * p.ldx + 8 * c);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // groups of 32 codes or more hold the same (s, z) for the whole 32-k step
+  // of every lane, so they are reloaded only where a group starts (a uniform
+  // test); smaller groups reload every step
+  const unsigned gmask = (1u << p.gshift) - 1u;
+  float sc = 0.f, zp = 0.f;
+  for (int s = s0; s < s1; ++s) {
+    if (p.gshift < 5 || s == s0 || ((unsigned)(32 * s) & gmask) == 0) {
+      const int g = (32 * s + 8 * c) >> p.gshift;
+      sc = gs[g];
+      zp = (float)gz[g];
+    }
+    const u32x4 bq = dequant8(gb[4 * s], sc, zp);
+    const u32x4 xa = xr[4 * s];
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa), __builtin_bit_cast(bf16x8, bq), acc,
+                                                  0, 0, 0);
+  }
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+    f32x4 t = red[0][lane];
+#pragma unroll
+    for (int q = 1; q < W4V_NW; ++q) t += red[q][lane];
+    // lane holds rows 4 (lane / 16) + r of the block, column lane % 16
+    const int col = n0 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * (lane >> 4) + r;
+      if (row < p.M && col < p.N) p.Y[(size_t)row * p.ldy + col] = t[r];
+    }
+  }
+}
+
 // ------------------------------------------------------------ launchers --
 hipError_t launch_pack(const uint8_t* codes, int rows, int n, int bits, uint32_t* out, hipStream_t st) {
   const int words = (int)(((long long)n * bits + 31) / 32);
@@ -317,6 +374,13 @@ hipError_t launch_unpack(const uint32_t* packed, int rows, int n, int bits, uint
 
 hipError_t launch_lr_quant(const LrProb& p, hipStream_t st) {
   hipLaunchKernelGGL(k_lr_quant, dim3(2 * p.r), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_w4a16(W4Prob p, hipStream_t st) {
+  p.tiles_m = 1;
+  p.tiles_n = (p.N + 15) / 16;
+  hipLaunchKernelGGL(k_gemv_w4a16, dim3(p.tiles_n), dim3(64 * W4V_NW), 0, st, p);
   return hipGetLastError();
 }
 

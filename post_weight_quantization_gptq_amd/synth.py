@@ -219,6 +219,7 @@ def w4_stored(N: int, K: int, group: int, seed: int):
 
 
 W4A16 = dict(M=8192, N=4096, K=4096, group=128)
+W4A16_DECODE_M = 16  # the same layer applied to 16 tokens (a decode-sized batch)
 
 
 def w4a16_inputs(M: int, K: int, seed: int, device="cpu") -> torch.Tensor:

@@ -125,7 +125,10 @@ def _check_gemm(Y, Xb, codes, scales, zeros, group, rows=None):
 
 @pytest.mark.parametrize("M,N,K,group", [(1, 1, 32, 0), (100, 70, 96, 32), (300, 200, 256, 128), (257, 129, 512, 0),
                                          (513, 384, 1024, 64), (256, 128, 64, 16), (70, 260, 128, 128), (600, 130, 64, 8),
-                                         (1100, 256, 256, 0), (64, 40, 96, 96)])
+                                         (1100, 256, 256, 0), (64, 40, 96, 96),
+                                         # up to 16 rows: the split-K few-row kernel
+                                         (2, 300, 512, 128), (5, 129, 256, 8), (16, 100, 64, 0), (3, 17, 32, 32),
+                                         (16, 1024, 4096, 128), (17, 64, 128, 64)])
 def test_gemm_w4a16_matches_oracle(ctx, M, N, K, group):
     print("gemm", M, N, K, group, flush=True)
     X, codes, scales, zeros = _gemm_case(M, N, K, group, M + N + K)

@@ -373,3 +373,11 @@ def test_w4a16_full(ctx):
                 rel_fro=float(np.linalg.norm(err) / np.linalg.norm(ref)))
     print(info, flush=True)
     assert np.all(err <= gam * mag), info
+    # the decode-sized call (16 rows, the few-row kernel) on the same layer:
+    # every entry
+    Y16 = ctx.gemm_w4a16(X[:16], P, scales.cuda(), zeros.cuda(), group)
+    X16 = o._as_f64(synth.bits_to_numpy(X[:16]))
+    e16 = np.abs(np32(Y16).astype(np.float64) - X16 @ Wb.T)
+    m16 = np.abs(X16) @ np.abs(Wb).T
+    print(dict(decode_max_err_over_mag=float((e16 / m16).max())), flush=True)
+    assert np.all(e16 <= gam * m16)
