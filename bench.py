@@ -296,7 +296,8 @@ def bench_w4a16(args, torch, Context, synth, dev):
                 "data": "synthetic (seeded; X from the square layer's input recipe, uniform 4-bit codes)",
                 "config": {"workload": "w4a16_decode: X[%d,4096] bf16 x W[4096,4096] 4-bit g128 -> Y fp32" % M},
                 "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "traffic": kernel_traffic(kname, "w4a16_decode", "deploy.hip"),
                              "avg_launch_ms": round(avg, 5), "bytes_per_launch": alg_bytes}}
         ctx.close()
         print(json.dumps(line), flush=True)
