@@ -307,7 +307,7 @@ int gptq_quantize_lowrank(gptq_ctx ctx, const float* L, const float* R, int32_t 
  * exact and summed in fp32 (for M <= 16 a split-K kernel sums in another
  * order).  Y[M][ldy] fp32, fully written in its M x N part.
  * K == 0 writes zeros.  Requirements: K % 32 == 0; group 0, K, or a power of
- * two >= 8 dividing K; ldx % 8 == 0, packed 8-byte aligned (else
+ * two >= 8 dividing K; ldx % 8 == 0, X and packed 16-byte aligned (else
  * GPTQ_ERR_UNSUPPORTED). */
 int gptq_gemm_w4a16(gptq_ctx ctx, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
                     const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group, float* Y,

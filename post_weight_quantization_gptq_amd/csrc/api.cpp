@@ -1474,8 +1474,8 @@ GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t l
     HIPCHK(c, hipMemset2DAsync(Y, (size_t)ldy * sizeof(float), 0, (size_t)N * sizeof(float), (size_t)M, c->stream));
     return GPTQ_OK;
   }
-  if (K % 32 != 0 || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0 || ((uintptr_t)packed & 7) != 0)
-    return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs K %% 32 == 0 and 16-byte aligned rows of X");
+  if (K % 32 != 0 || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0 || ((uintptr_t)packed & 15) != 0)
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs K %% 32 == 0 and 16-byte aligned rows of X and codes");
   if ((long long)cdiv64(M, 256) * cdiv64(N, 128) > INT32_MAX)
     return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 product too large for one launch");
   int gshift = 31;

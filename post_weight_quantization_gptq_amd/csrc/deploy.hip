@@ -12,6 +12,7 @@
 #include "launch.h"
 
 typedef const __attribute__((address_space(1))) uint32_t gu32;
+typedef const __attribute__((address_space(1))) u32x4 gu32x4;
 typedef const __attribute__((address_space(1))) uint8_t gu8;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -300,10 +301,10 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
 // The same product for M <= 16 rows of X (decode-sized batches), where the
 // tiled kernel would run almost empty: the work is reading the codes.  One
 // workgroup of 8 waves per 16 rows of the codes (16 columns of Y); the waves
-// split K in eight.  Per 32-k step, lane (j = lane % 16, c = lane / 16)
-// dequantises code word (row n0 + j, k-chunk c) into its B operand and takes
-// X[j][k + 8c .. +7] (row j clamped to M - 1) as its A operand, and
-// v_mfma_f32_16x16x32_bf16 accumulates the 16 x 16 block of Y.  The eight
+// split K in eight.  Lane (j = lane % 16, c = lane / 16) dequantises code
+// words of row n0 + j into its B operand and takes the same k of X[j] (row j
+// clamped to M - 1) as its A operand, and v_mfma_f32_16x16x32_bf16
+// accumulates the 16 x 16 block of Y.  The eight
 // partial blocks are summed in LDS in a fixed order.  The arithmetic per
 // entry is that of the tiled kernel (bf16 weights, exact products, fp32
 // sums); only the order of the sums differs.
@@ -314,28 +315,56 @@ __global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
   const int n0 = blockIdx.x * 16;
   const int j = lane & 15, c = lane >> 4;
   const int nrow = min(n0 + j, p.N - 1);
-  const int nsteps = p.K / 32;
-  const int s0 = (int)((long long)nsteps * w / W4V_NW), s1 = (int)((long long)nsteps * (w + 1) / W4V_NW);
-  gu32* gb = (gu32*)(p.P + (size_t)nrow * (p.K >> 3) + c);
+  const uint32_t* crow = p.P + (size_t)nrow * (p.K >> 3);
   gfloat* gs = (gfloat*)(p.S + (size_t)nrow * p.G);
   gu8* gz = (gu8*)(p.Z + (size_t)nrow * p.G);
-  const u32x4* xr = (const u32x4*)(p.X + (size_t)min(j, p.M - 1) * p.ldx + 8 * c);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  // groups of 32 codes or more hold the same (s, z) for the whole 32-k step
-  // of every lane, so they are reloaded only where a group starts (a uniform
-  // test); smaller groups reload every step
+  const uint16_t* xrow = p.X + (size_t)min(j, p.M - 1) * p.ldx;
   const unsigned gmask = (1u << p.gshift) - 1u;
-  float sc = 0.f, zp = 0.f;
-  for (int s = s0; s < s1; ++s) {
-    if (p.gshift < 5 || s == s0 || ((unsigned)(32 * s) & gmask) == 0) {
-      const int g = (32 * s + 8 * c) >> p.gshift;
-      sc = gs[g];
-      zp = (float)gz[g];
-    }
-    const u32x4 bq = dequant8(gb[4 * s], sc, zp);
-    const u32x4 xa = xr[4 * s];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const u32x4& xa, const u32x4& bq) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa), __builtin_bit_cast(bf16x8, bq), acc,
                                                   0, 0, 0);
+  };
+  // Blocks of 128 k, split among the waves.  In block t the lane loads the
+  // four code words of k = 128 t + 32 c .. +31 at once (16 bytes); its 16-k
+  // sub-step u multiplies the 8 of them at 128 t + 32 c + 8 u with the same
+  // k of X (the 32 k of one MFMA are then {128 t + 32 c' + 8 u + e}, every
+  // k of the block once over u).  Groups of 128 codes or more hold one (s, z)
+  // per block for every lane, reloaded only where a group starts (a uniform
+  // test); smaller groups load theirs per sub-step.
+  const int nblk = p.K >> 7;
+  const int t0 = (int)((long long)nblk * w / W4V_NW), t1 = (int)((long long)nblk * (w + 1) / W4V_NW);
+  const bool big = p.gshift >= 7;
+  float sc = 0.f, zp = 0.f;
+  for (int t = t0; t < t1; ++t) {
+    const int kb = 128 * t + 32 * c;
+    const u32x4 wq = *(const gu32x4*)(crow + (kb >> 3));
+    u32x4 xa[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) xa[u] = *(const u32x4*)(xrow + kb + 8 * u);
+    if (big) {
+      if (t == t0 || ((unsigned)(128 * t) & gmask) == 0) {  // uniform
+        const int g = (128 * t) >> p.gshift;
+        sc = gs[g];
+        zp = (float)gz[g];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mma(xa[u], dequant8(wq[u], sc, zp));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = (kb + 8 * u) >> p.gshift;
+        mma(xa[u], dequant8(wq[u], gs[g], (float)gz[g]));
+      }
+    }
+  }
+  // K % 128: up to three 32-k steps left, one per wave, in the layout of a
+  // 32-k MFMA step (lane k-chunk c)
+  const int s_tail = 4 * nblk + w;
+  if (s_tail < (p.K >> 5)) {  // uniform
+    const int k = 32 * s_tail + 8 * c;
+    const int g = k >> p.gshift;
+    mma(*(const u32x4*)(xrow + k), dequant8(((const gu32*)crow)[k >> 3], gs[g], (float)gz[g]));
   }
   red[w][lane] = acc;
   __syncthreads();

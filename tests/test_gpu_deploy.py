@@ -128,7 +128,7 @@ def _check_gemm(Y, Xb, codes, scales, zeros, group, rows=None):
                                          (1100, 256, 256, 0), (64, 40, 96, 96),
                                          # up to 16 rows: the split-K few-row kernel
                                          (2, 300, 512, 128), (5, 129, 256, 8), (16, 100, 64, 0), (3, 17, 32, 32),
-                                         (16, 1024, 4096, 128), (17, 64, 128, 64)])
+                                         (16, 1024, 4096, 128), (17, 64, 128, 64), (8, 64, 256, 0), (4, 48, 416, 32)])
 def test_gemm_w4a16_matches_oracle(ctx, M, N, K, group):
     print("gemm", M, N, K, group, flush=True)
     X, codes, scales, zeros = _gemm_case(M, N, K, group, M + N + K)
