@@ -74,16 +74,26 @@ def cpu_baseline(spec, lay, max_rows=512, tok_sample=32768):
                                                                t_h, t_f, t_s)}
 
 
+def code_digest(path):
+    """SHA-256 of a C/HIP source with its comments and whitespace removed, so
+    that a counter record stays valid across edits of comments only."""
+    import hashlib
+    import re
+    txt = open(path, encoding="utf-8").read()
+    txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+    txt = re.sub(r"//[^\n]*", " ", txt)
+    return hashlib.sha256(" ".join(txt.split()).encode()).hexdigest()
+
+
 def kernel_traffic(kernel, workload, source):
     """HBM bytes per launch of `kernel` from the committed counter summary
     profiles/<kernel>_<workload>_traffic.json, or None when absent or taken on
-    a different version of its source file."""
-    import hashlib
+    a different version of its source file's code."""
     path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kernel, workload))
     src = os.path.join(ROOT, "post_weight_quantization_gptq_amd", "csrc", source)
     try:
         rec = json.load(open(path))
-        if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        if rec.get("source_code_sha256") != code_digest(src):
             return None
         return rec.get("bytes_per_launch")
     except Exception:

@@ -304,10 +304,10 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
 // split K in eight.  Lane (j = lane % 16, c = lane / 16) dequantises code
 // words of row n0 + j into its B operand and takes the same k of X[j] (row j
 // clamped to M - 1) as its A operand, and v_mfma_f32_16x16x32_bf16
-// accumulates the 16 x 16 block of Y.  The eight
-// partial blocks are summed in LDS in a fixed order.  The arithmetic per
-// entry is that of the tiled kernel (bf16 weights, exact products, fp32
-// sums); only the order of the sums differs.
+// accumulates the 16 x 16 block of Y.  The eight partial blocks are summed in
+// LDS in a fixed order.  The arithmetic per entry is that of the tiled kernel
+// (bf16 weights, exact products, fp32 sums); only the order of the sums
+// differs.
 #define W4V_NW 8
 __global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
   __shared__ f32x4 red[W4V_NW][64];
