@@ -175,6 +175,18 @@ def test_gemm_w4a16_of_a_gptq_layer(ctx):
     _check_gemm(np32(Y), synth.bits_to_numpy(lay["X"][:1000]), codes, scales, zeros, 128)
 
 
+@pytest.mark.parametrize("M", [16, 600])
+def test_gemm_w4a16_is_bitwise_repeatable(ctx, M):
+    # fixed summation orders in both kernels (no atomics): repeated calls
+    # give the same bits
+    X, codes, scales, zeros = _gemm_case(M, 256, 512, 64, 3)
+    P = torch.from_numpy(o.pack_codes(codes, 4).view(np.int32)).cuda()
+    S, Z, Xd = torch.from_numpy(scales).cuda(), torch.from_numpy(zeros).cuda(), X.cuda()
+    Y1 = ctx.gemm_w4a16(Xd, P, S, Z, 64)
+    for _ in range(3):
+        assert torch.equal(ctx.gemm_w4a16(Xd, P, S, Z, 64), Y1)
+
+
 def test_gemm_w4a16_empty_sum_is_zero(ctx):
     X = torch.zeros((5, 8), dtype=torch.int16, device="cuda")
     P = torch.zeros((3, 0), dtype=torch.int32, device="cuda")
