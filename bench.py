@@ -359,7 +359,7 @@ def main():
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the pass on a single MI355X "
+        print("bench.py measures one GPU: the pass runs on a single MI355X "
               "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
