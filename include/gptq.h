@@ -304,7 +304,7 @@ int gptq_quantize_lowrank(gptq_ctx ctx, const float* L, const float* R, int32_t 
  * fp32 and zeros[N][G] uint8 as gptq_quantize writes them (G = K/group, or 1
  * for group 0), What = s (q - z) per group.  Every weight enters the bf16
  * matrix unit as bf16(fl32(s (q - z))) (nearest, ties to even); products are
- * exact and summed in fp32 (for M <= 16 a split-K kernel sums in another
+ * exact and summed in fp32 (for M <= 128 a split-K kernel sums in another
  * order).  Y[M][ldy] fp32, fully written in its M x N part.
  * K == 0 writes zeros.  Requirements: K % 32 == 0; group 0, K, or a power of
  * two >= 8 dividing K; ldx % 8 == 0, X and packed 16-byte aligned (else

@@ -1498,7 +1498,7 @@ GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t l
   p.K = K;
   p.G = gshift == 31 ? 1 : K / group;
   p.gshift = gshift;
-  if (M <= 16) {  // decode-sized: split K over 16 x 16 blocks, bound by reading the codes
+  if (M <= 128) {  // decode-sized: split K over 16 x 16 blocks, bound by reading the codes
     LAUNCH(c, "k_gemv_w4a16", launch_gemv_w4a16(p, c->stream));
     return GPTQ_OK;
   }

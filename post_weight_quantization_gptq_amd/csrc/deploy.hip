@@ -298,10 +298,11 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
 }
 
 // ------------------------------------------------ W4A16 product, few rows --
-// The same product for M <= 16 rows of X (decode-sized batches), where the
-// tiled kernel would run almost empty: the work is reading the codes.  One
-// workgroup of 8 waves per 16 rows of the codes (16 columns of Y); the waves
-// split K in eight.  Lane (j = lane % 16, c = lane / 16) dequantises code
+// The same product for few rows of X (decode-sized batches), where the tiled
+// kernel would run almost empty: the work is reading the codes.  One
+// workgroup of 8 waves per 16 rows of the codes (16 columns of Y) and 16 rows
+// of X (grid y; more rows of X re-read the codes from L2); the waves split K
+// in eight.  Lane (j = lane % 16, c = lane / 16) dequantises code
 // words of row n0 + j into its B operand and takes the same k of X[j] (row j
 // clamped to M - 1) as its A operand, and v_mfma_f32_16x16x32_bf16
 // accumulates the 16 x 16 block of Y.  The eight partial blocks are summed in
@@ -312,13 +313,13 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
 __global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
   __shared__ f32x4 red[W4V_NW][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;  // code rows; rows of X
   const int j = lane & 15, c = lane >> 4;
   const int nrow = min(n0 + j, p.N - 1);
   const uint32_t* crow = p.P + (size_t)nrow * (p.K >> 3);
   gfloat* gs = (gfloat*)(p.S + (size_t)nrow * p.G);
   gu8* gz = (gu8*)(p.Z + (size_t)nrow * p.G);
-  const uint16_t* xrow = p.X + (size_t)min(j, p.M - 1) * p.ldx;
+  const uint16_t* xrow = p.X + (size_t)min(m0 + j, p.M - 1) * p.ldx;
   const unsigned gmask = (1u << p.gshift) - 1u;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto mma = [&](const u32x4& xa, const u32x4& bq) {
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
     const int col = n0 + (lane & 15);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 4 * (lane >> 4) + r;
+      const int row = m0 + 4 * (lane >> 4) + r;
       if (row < p.M && col < p.N) p.Y[(size_t)row * p.ldy + col] = t[r];
     }
   }
@@ -407,9 +408,9 @@ hipError_t launch_lr_quant(const LrProb& p, hipStream_t st) {
 }
 
 hipError_t launch_gemv_w4a16(W4Prob p, hipStream_t st) {
-  p.tiles_m = 1;
+  p.tiles_m = (p.M + 15) / 16;
   p.tiles_n = (p.N + 15) / 16;
-  hipLaunchKernelGGL(k_gemv_w4a16, dim3(p.tiles_n), dim3(64 * W4V_NW), 0, st, p);
+  hipLaunchKernelGGL(k_gemv_w4a16, dim3(p.tiles_n, p.tiles_m), dim3(64 * W4V_NW), 0, st, p);
   return hipGetLastError();
 }
 

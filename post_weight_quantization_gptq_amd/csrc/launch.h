@@ -55,5 +55,5 @@ hipError_t launch_lr_quant(const LrProb& p, hipStream_t st);
 // sets the tile counts itself; K % 32 == 0
 // tile shape 0: 256 x 128 (4 waves), 1: 512 x 128 (8 waves), 2: 256 x 256 (8 waves)
 hipError_t launch_gemm_w4a16(W4Prob p, int shape, hipStream_t st);
-// M <= 16 rows of X: split-K product on 16 x 16 MFMA blocks
+// few rows of X (up to 128): split-K product on 16 x 16 MFMA blocks
 hipError_t launch_gemv_w4a16(W4Prob p, hipStream_t st);

@@ -126,9 +126,10 @@ def _check_gemm(Y, Xb, codes, scales, zeros, group, rows=None):
 @pytest.mark.parametrize("M,N,K,group", [(1, 1, 32, 0), (100, 70, 96, 32), (300, 200, 256, 128), (257, 129, 512, 0),
                                          (513, 384, 1024, 64), (256, 128, 64, 16), (70, 260, 128, 128), (600, 130, 64, 8),
                                          (1100, 256, 256, 0), (64, 40, 96, 96),
-                                         # up to 16 rows: the split-K few-row kernel
+                                         # up to 128 rows: the split-K few-row kernel
                                          (2, 300, 512, 128), (5, 129, 256, 8), (16, 100, 64, 0), (3, 17, 32, 32),
-                                         (16, 1024, 4096, 128), (17, 64, 128, 64), (8, 64, 256, 0), (4, 48, 416, 32)])
+                                         (16, 1024, 4096, 128), (17, 64, 128, 64), (8, 64, 256, 0), (4, 48, 416, 32),
+                                         (40, 200, 512, 128), (128, 96, 256, 16), (129, 64, 128, 0)])
 def test_gemm_w4a16_matches_oracle(ctx, M, N, K, group):
     print("gemm", M, N, K, group, flush=True)
     X, codes, scales, zeros = _gemm_case(M, N, K, group, M + N + K)
@@ -175,7 +176,7 @@ def test_gemm_w4a16_of_a_gptq_layer(ctx):
     _check_gemm(np32(Y), synth.bits_to_numpy(lay["X"][:1000]), codes, scales, zeros, 128)
 
 
-@pytest.mark.parametrize("M", [16, 600])
+@pytest.mark.parametrize("M", [16, 100, 600])
 def test_gemm_w4a16_is_bitwise_repeatable(ctx, M):
     # fixed summation orders in both kernels (no atomics): repeated calls
     # give the same bits
