@@ -209,3 +209,7 @@ def test_gemm_w4a16_rejects_unsupported(ctx):
     with pytest.raises(GPTQError):
         ctx.gemm_w4a16(X, P, torch.ones((4, 2), device="cuda"), torch.zeros((4, 2), dtype=torch.uint8, device="cuda"),
                        48)  # group not a power of two
+    # code rows not 16-byte aligned (a view one word into its buffer)
+    Pw = torch.zeros((4 * 12 + 1,), dtype=torch.int32, device="cuda")[1:].view(4, 12)
+    with pytest.raises(GPTQError):
+        ctx.gemm_w4a16(X, Pw, torch.ones((4, 1), device="cuda"), torch.zeros((4, 1), dtype=torch.uint8, device="cuda"), 0)
