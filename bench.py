@@ -498,6 +498,19 @@ def main():
             stage[key] = round(stage[key] / args.steps / nlayers, 4)
         line["stages_ms"] = stage
     line["kernels_one_step"] = breakdown
+    if args.workload in ("square", "single", "mlp") and "k_trail" in breakdown and "k_sweep" in breakdown:
+        # secondary rates from the breakdown step (event-bracketed kernel time,
+        # wide updates overlapping the sweeps included): the trailing update
+        # against the fp32 matrix roof, the sweep's bytes against HBM
+        trail_fl = sum(f["trail"] for f in fl)
+        sweep_bytes = sum(s.out * s.n * (4 + 4 + 1 + 4) + s.n * s.block * 4 for s in specs)  # W, W_orig, codes, E; U blocks
+        t_tr = breakdown["k_trail"]["ms"] * 1e-3
+        t_sw = breakdown["k_sweep"]["ms"] * 1e-3
+        line["secondary"] = {
+            "k_trail": {"tflops": round(trail_fl / t_tr / 1e12, 2), "peak": PEAK_FP32_MATRIX_TFLOPS,
+                        "frac": round(trail_fl / t_tr / 1e12 / PEAK_FP32_MATRIX_TFLOPS, 4)},
+            "k_sweep": {"gb_s": round(sweep_bytes / t_sw / 1e9, 1), "peak": PEAK_HBM_GBS,
+                        "frac": round(sweep_bytes / t_sw / 1e9 / PEAK_HBM_GBS, 4), "bound": "latency"}}
     if dom_launches:
         # algorithmic flops of one launch (mean over the step's launches): the
         # triangle X^T X of every layer the launch covers
