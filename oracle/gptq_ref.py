@@ -51,9 +51,16 @@ of ours.
 
 Parity unpinned (conventions that only self-consistency fixes; the GPU follows
 them exactly): the min-max grid details of ``grid_fit`` (0 inside the range,
-integer zero point, degenerate range -> s = 1, z = 0), the moment at which a
-group's grid is fitted, and the fp32 precision in which the code and zero-point
-decisions are taken.
+integer zero point, degenerate range -> s = 1, z = 0) and the moment at which a
+group's grid is fitted.
+
+Decision precision.  The pages fix no precision for the rounding decisions, so
+they are taken in the library's float32 form x = fl32(fl32(w * fl32(1/s)) + z).
+A pin (tests/test_oracle_pins.py) shows that this equals the plain float64
+definitions s = (hi - lo)/maxq, z = rne(-lo/s), q = clamp(rne(w/s + z))
+everywhere except within the float32 rounding bound of a tie (a few 1e-6),
+far inside the 1e-3 near-tie window of the parity protocol.  The top-r
+eigenvectors of H are pinned against the SVD of the data matrix.
 """
 from __future__ import annotations
 
@@ -260,6 +267,8 @@ def gptq_sweep(W, U, bits: int, group: int = 0, block: int | None = None,
     then update the remaining weights to compensate, in closed form):
       if group and j % group == 0: fit the grid on the current w[j:j+group]
       q_j = clamp(rne(w_j / s + z)),  what_j = s (q_j - z)
+        (the decision taken in float32 as fl32(fl32(w_j * fl32(1/s)) + z);
+        see the module docstring)
       E_j = (w_j - what_j) / U_jj,    w[k] -= E_j U_jk for k > j
     With ``block`` the update of step j only reaches the columns of its own
     block; after the block, W[:, b1:] -= E[:, b0:b1] U[b0:b1, b1:] ([2D]

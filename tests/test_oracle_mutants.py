@@ -34,6 +34,9 @@ MUTANTS = {
                               "lam = float(lam_abs) + float(lam_rel)"),
     "static_group_grid": ("s, r, z = fit(W[:, j:j + group], j // group)",
                           "s, r, z = fit(W0[:, j:j + group], j // group)"),
+    "bottom_eigvecs": ("idx = np.argsort(lam_)[::-1][:r]", "idx = np.argsort(lam_)[:r]"),
+    "eigvecs_rows": ("    return V[:, idx]\n", "    return V[idx, :].T\n"),
+    "code_truncated": ("q = np.clip(np.rint(x), F32(0), F32(maxq))", "q = np.clip(np.floor(x), F32(0), F32(maxq))"),
 }
 
 
@@ -106,6 +109,11 @@ def _pins(m):
                 fails.append("rtn")
             if (np.abs(-z * s - lo) > 0.5001 * s).any():
                 fails.append("grid-zero")
+    # L = V_r spans the top-r right singular subspace of X, by the SVD of the data
+    V = m.top_eigvecs(H, 3)
+    _, _, Vt = np.linalg.svd(Xf, full_matrices=False)
+    if V.shape != (n, 3) or np.abs(V @ V.T - Vt[:3].T @ Vt[:3]).max() > 1e-8:
+        fails.append("top-subspace")
     # golden group example
     Hg = np.array([[1, 0.5, 0, 0], [0.5, 1, 0, 0], [0, 0, 1, 0], [0, 0, 0, 1.0]])
     wg = np.array([[0.25, 0.10, -0.20, 0.40]])

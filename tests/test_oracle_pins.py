@@ -147,6 +147,49 @@ def test_rounding_is_nearest_grid_point_by_brute_force():
         assert np.array_equal(q[clear].astype(int), best[clear])
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_fp32_decisions_equal_plain_fp64_division_away_from_ties(bits):
+    """The grid and code decisions, taken in float32 with a reciprocal
+    multiply, equal the plain float64 definitions s = (hi - lo)/maxq,
+    z = rne(-lo/s), q = clamp(rne(w/s + z)) everywhere except within the
+    float32 rounding bound of a tie (|frac - 1/2| below a few ulps of the
+    operands: under 8e-6 at 4 bits and 1.3e-4 at 8 bits for values inside
+    the grid)."""
+    rng = _rng(40 + bits)
+    maxq = 2 ** bits - 1
+    rows, g = 4000, 64
+    V = rng.standard_normal((rows, g)) * 10.0 ** rng.uniform(-3, 1, (rows, 1))
+    V[:100] = np.abs(V[:100])       # all-positive groups: lo = 0, z = 0
+    V[100:200] = -np.abs(V[100:200])  # all-negative groups: hi = 0, z = maxq
+    s, r, z, zraw = o.grid_fit(V, maxq)
+    v32 = V.astype(np.float32).astype(np.float64)
+    lo = np.minimum(v32.min(1), 0.0)
+    hi = np.maximum(v32.max(1), 0.0)
+    s64 = (hi - lo) / maxq
+    u = 2.0 ** -24
+    # the stored scale is the float64 scale to within two float32 roundings
+    assert (np.abs(s.astype(np.float64) - s64) <= 2.001 * u * s64).all()
+    # zero points: equal to rne(-lo/s) away from a tie
+    x64 = -lo / s64
+    z64 = np.clip(np.rint(x64), 0, maxq)
+    bound = (x64 + 1.0) * 8 * u
+    tie = np.abs(x64 - np.floor(x64) - 0.5) <= bound
+    assert np.array_equal(z.astype(np.float64)[~tie], z64[~tie])
+    # codes of the group's own values and of values past the grid's ends
+    for w in (v32, 1.5 * v32 - 0.3 * s64[:, None]):
+        q, what, x = o.quantize_values(w, s[:, None], r[:, None], z[:, None], maxq)
+        xd = w / s64[:, None] + z[:, None].astype(np.float64)
+        qd = np.clip(np.rint(xd), 0, maxq)
+        bound = (3.0 * np.abs(w / s64[:, None]) + np.abs(xd) + 1.0) * 2 * u
+        tie = np.abs(xd - np.floor(xd) - 0.5) <= bound
+        assert np.array_equal(q.astype(np.float64)[~tie], qd[~tie])
+        assert tie.mean() < 1e-3
+        if w is v32:  # inside the grid: |w/s| and |x| at most maxq
+            assert bound.max() <= (4 * maxq + 1) * 2 * u * 1.001
+    # the decision's window is far inside the 1e-3 near-tie replay window of the parity tests
+    assert bound.max() < 1e-3
+
+
 # ---------------------------------------------------------------- sweep ----
 @pytest.mark.parametrize("group", [0, 8])
 def test_identity_hessian_reduces_to_round_to_nearest(group):
@@ -303,6 +346,39 @@ def _lowrank_problem(seed, n=48, r=4, tokens=400, out=10):
     X = _to_bf16_bits(((A * sig) @ V.T).astype(np.float32))
     W = 0.02 * rng.standard_normal((out, n))
     return X, W
+
+
+@pytest.mark.parametrize("seed,r,gap", [(30, 4, "wide"), (31, 7, "wide"), (32, 5, "narrow")])
+def test_top_eigvecs_span_top_right_singular_subspace(seed, r, gap):
+    """[LoRA] method section 2: L = V_r holds the top-r right singular vectors
+    of X.  Checked against the SVD of the data matrix itself (not an
+    eigendecomposition of H): same projector, Ritz values equal to the r
+    largest squared singular values, and the captured energy ||X V||^2 equal
+    to their sum (Ky Fan: the maximum over r-dimensional subspaces)."""
+    rng = _rng(seed)
+    n, tokens = 40, 300
+    A, _ = np.linalg.qr(rng.standard_normal((tokens, n)))
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    if gap == "wide":
+        sig = np.concatenate([rng.normal(1.0, 0.1, r), 0.05 * np.arange(1, n - r + 1) ** -0.5])
+    else:  # power law: sigma_r / sigma_{r+1} about 1.1
+        sig = np.arange(1, n + 1) ** -0.5
+    X = _to_bf16_bits(((A * sig) @ Q.T).astype(np.float32))
+    Xf = o.bf16_bits_to_f64(X)
+    H = o.hessian(X)
+    V = o.top_eigvecs(H, r)
+    _, sv, Vt = np.linalg.svd(Xf, full_matrices=False)
+    Vs = Vt[:r].T
+    assert np.abs(V.T @ V - np.eye(r)).max() < 1e-12
+    g = (sv[r - 1] ** 2 - sv[r] ** 2) / sv[0] ** 2  # relative spectral gap
+    assert np.abs(V @ V.T - Vs @ Vs.T).max() < 1e-12 / g
+    ritz = np.sort(np.diag(V.T @ H @ V))[::-1]
+    assert np.allclose(ritz, sv[:r] ** 2, rtol=1e-10, atol=0)
+    assert np.sum((Xf @ V) ** 2) == pytest.approx(np.sum(sv[:r] ** 2), rel=1e-12)
+    # and no other r-dimensional subspace captures more energy
+    for _ in range(5):
+        B, _ = np.linalg.qr(Vs + 0.05 * rng.standard_normal((n, r)))
+        assert np.sum((Xf @ B) ** 2) < np.sum((Xf @ V) ** 2)
 
 
 def test_lora_matches_schur_and_ridge_closed_forms():
