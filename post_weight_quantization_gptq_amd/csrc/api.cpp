@@ -247,9 +247,11 @@ struct HessPlan {
 
 // The tiles can read X directly (no transposed copy) when its rows are
 // 16-byte aligned and n is a multiple of 8 (16-byte feature chunks never
-// cross the end of a row).
+// cross the end of a row).  A stage's per-lane byte offsets (32 rows of the
+// pitch) are 32-bit, which bounds the pitch.
 static bool hess_direct(const HessJob& J) {
-  return J.tokens > 0 && (J.ldx % 8) == 0 && (((uintptr_t)J.X) & 15) == 0 && (J.n % 8) == 0;
+  return J.tokens > 0 && (J.ldx % 8) == 0 && (((uintptr_t)J.X) & 15) == 0 && (J.n % 8) == 0 &&
+         J.ldx < (1LL << 25);
 }
 
 // Interleaved bit order of (i, j): tiles close in this order share rows of X.

@@ -4,10 +4,10 @@
 // Quantization, technical overview section 3.1; GPTQ-2D technical summary
 // section 1) is a dense contraction over tokens with both operands stored
 // feature-contiguous ([tokens, n] rows).  The MFMA wants 8 consecutive tokens
-// per lane, so X is first copied once, transposed and zero-padded, into a
-// feature-major workspace (one bandwidth-bound pass); every tile of the
-// contraction then moves 16-byte rows straight into LDS in the order the
-// MFMA reads them, with no per-tile transposition or bounds checks.
+// per lane.  When X's rows are 16-byte aligned the tiles read X in place and
+// transpose in the LDS read (ds_read_b64_tr_b16); otherwise X is first copied
+// once, transposed and zero-padded, into a feature-major workspace (k_xpose)
+// whose rows the tiles read directly.
 //
 // Work split: one workgroup = one 256x256 upper tile of H over a token range;
 // the planner gives each XCD its own slice of tokens, so the workgroups that
@@ -58,43 +58,56 @@ __global__ __launch_bounds__(256) void k_xpose(const XposeProb* __restrict__ pro
   }
 }
 
-// One 256x256 upper tile of H over the token range [k0, k1) of Xt (both
-// multiples of 64; the copy is zero-padded, so no bounds are checked).
+// One 256x256 upper tile of H over the token range [k0, k1) (a multiple of
+// 32 tokens; TR mode clamps and zeroes rows past the end of X).
 //
-// Pipeline: a ring of 4 LDS stages of 32 tokens (each operand a 256-row x
-// 64-byte tile, 16 KB); rows travel from L2 straight into LDS
-// (global_load_lds, 16 B per lane, no registers in between) three stages
-// ahead of the stage being multiplied.  Inside a row the 16-byte token chunks
-// are stored XOR-swizzled by (row / 4) % 4, so a fragment read of 16
-// consecutive rows covers all LDS banks.  Each wave owns a 128x128 quarter of
-// the tile (4 x 4 MFMA 32x32x16 accumulators, 256 AGPRs); the fragment reads
-// of the next 16-token sub-step are interleaved with the MFMAs of the current
-// one, across the stage boundary too.
+// Four waves, one per SIMD; wave w owns the 128x128 quarter at rows
+// 128 (w / 2), columns 128 (w % 2) of the tile: 4 x 4 accumulators of
+// v_mfma_f32_32x32x16_bf16 (256 AGPRs).  A 128x128 block per wave is the
+// largest the register file allows and needs the fewest LDS bytes per MFMA:
+// each 16-token sub-step reads 8 operand fragments (16 transposing reads of
+// 512 B) for 16 MFMAs, against 12 reads for 8 MFMAs with 128x64 blocks.
+//
+// Pipeline: a ring of 4 LDS stages of 32 tokens (each operand a 256-feature
+// x 32-token tile, 16 KB); rows travel from L2 straight into LDS
+// (global_load_lds, 16 B per lane) three stages ahead of the stage being
+// multiplied.  The fragments of sub-step j+1 are read while the MFMAs of
+// sub-step j run, one read issued after each MFMA, so the LDS port and the
+// matrix pipe work side by side; a stage's copies are issued between the
+// MFMAs of its second sub-step.
+//
+// TR = false: operands from the feature-major copy Xt ([feature][token]),
+// one 16-byte row chunk per MFMA lane.  A stage holds 256 rows of 64 B, the
+// 16-byte token chunks XOR-swizzled by (row / 4) % 4.
+// TR = true: operands straight from X (token-major).  A stage holds 32 token
+// rows of 256 features (512 B each, 16-byte chunks XOR-swizzled by
+// 4 (row % 4)), and the fragments come out of LDS with the transposing read
+// ds_read_b64_tr_b16: in each 16-lane group, lane i points at 4 features of
+// token (i / 4) and receives 4 tokens of one feature, so two such reads give
+// a lane the 8 consecutive tokens of its feature that the 32x32x16 MFMA
+// wants, with no copy of X.
 #define SYK_KT 32                   // tokens per stage
 #define SYK_OPB (256 * SYK_KT * 2)  // bytes of one operand tile in a stage
 #define SYK_STB (2 * SYK_OPB)       // bytes of a stage
 #define SYK_NST 4                   // stages in the ring
+#define SYK_NW 4                    // waves per workgroup (one per SIMD)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// TR = false: operands from the feature-major copy Xt, one 16-byte row chunk
-// per MFMA lane.  TR = true: operands straight from X (token-major).  A stage
-// then holds 32 token rows of 256 features (512 B each, 16-byte chunks
-// XOR-swizzled by 4 (row % 4)), and the fragments come out of LDS with the
-// transposing read ds_read_b64_tr_b16: in each 16-lane group, lane i points
-// at 4 features of token (i / 4) and receives 4 tokens of one feature, so
-// two such reads give a lane the 8 consecutive tokens of its feature that
-// the 32x32x16 MFMA wants, with no copy of X.
-template <bool DIAG, bool TR, int NW>
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+#define SG_MFMA 0x008
+#define SG_VMEM_RD 0x020
+#define SG_DS_RD 0x100
+
+template <bool DIAG, bool TR>
 __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk, uint8_t* lds,
                                           float* __restrict__ partials) {
-  constexpr int NI = 16 / NW;                 // global_load_lds per operand per lane per stage
-  constexpr int L = DIAG ? NI : 2 * NI;       // ... for both operands
-  constexpr int WC = NW / 2;                  // waves across the tile's columns (2 down)
-  constexpr int NBF = 8 / WC;                 // 32-column B fragments per wave
-  constexpr int NTH = 64 * NW;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NI = 4;                  // global_load_lds per operand per wave per stage (16 KB / 4 / 1 KB)
+  constexpr int L = DIAG ? NI : 2 * NI;  // ... for both operands
+  constexpr int NTH = 64 * SYK_NW;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets on the scalar unit
   const int nsteps = (tk.k1 - tk.k0) / SYK_KT;
   const size_t tp = (size_t)pb.ldt;
   const uint16_t* ga;
@@ -102,19 +115,18 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
   size_t gstep, gq;  // element offsets per step and per instruction
   int tok0 = 0, trow = 0;
   if (!TR) {
-    // Load slot: instruction q of wave w fills the 16 LDS rows 16(NW q+w) ..
-    // 16(NW q+w)+15 (1 KB); lane -> row 16(NW q+w) + lane/4 at chunk
-    // position lane%4, holding token chunk (lane%4) ^ ((row/4)%4) =
-    // (lane%4) ^ (lane/16).
+    // instruction q of wave w fills the 16 LDS rows 16(4q+w) .. +15 (1 KB);
+    // lane -> row 16(4q+w) + lane/4 at chunk position lane%4, holding token
+    // chunk (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16)
     const int lrow = 16 * w + (lane >> 2);
     const int tchunk = (lane & 3) ^ (lane >> 4);
     ga = pb.Xt + (size_t)(tk.ti * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
     gb = (pb.Yt ? pb.Yt : pb.Xt) + (size_t)(tk.tj * 256 + lrow) * tp + tk.k0 + 8 * tchunk;
     gstep = SYK_KT;
-    gq = 16 * NW * tp;
+    gq = 16 * SYK_NW * tp;
   } else {
-    // instruction q of wave w fills token rows 2(NW q+w), 2(NW q+w)+1 (1 KB);
-    // lane -> row 2(NW q+w) + lane/32 at chunk position lane%32, holding
+    // instruction q of wave w fills token rows 2(4q+w), 2(4q+w)+1 (1 KB);
+    // lane -> row 2(4q+w) + lane/32 at chunk position lane%32, holding
     // feature chunk (lane%32) ^ 4 (row % 4).  Chunks past n read chunk 0.
     trow = 2 * w + (lane >> 5);
     const int chunk = (lane & 31) ^ (4 * (trow & 3));
@@ -125,67 +137,152 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     gstep = 0;
     gq = 0;
   }
-  auto issue = [&](int step, int stage) {
-    uint8_t* base = lds + stage * SYK_STB;
+  // TR copies: a stage's rows start at a uniform (scalar) address, and each
+  // lane adds a 32-bit byte offset: its row 8q + trow and its feature chunk.
+  // Rows past the end of X take the last row's offset instead (the stage's
+  // tail is zeroed in LDS before use); cur[] holds the offsets of the stage
+  // being copied.
+  const unsigned rowb = (unsigned)pb.ldt * 2u;
+  const unsigned lbA = TR ? 2u * (unsigned)(ga - pb.Xt) : 0u;
+  const unsigned lbB = TR ? 2u * (unsigned)(gb - (pb.Yt ? pb.Yt : pb.Xt)) : 0u;
+  const char* xa = (const char*)pb.Xt;
+  const char* xb = (const char*)(pb.Yt ? pb.Yt : pb.Xt);
+  unsigned curA[NI], curB[NI];
+  // A stage that starts past the end of X (the last 32-token stage of a
+  // 64-token chunk) reads row tokens-1 throughout; its rows are all zeroed.
+  auto stage_row0 = [&](int step) {  // uniform: first token row read by the stage
+    const int t0 = tok0 + step * SYK_KT;
+    return t0 < pb.tokens ? t0 : pb.tokens - 1;
+  };
+  auto prep = [&](int step) {
+    const int valid = pb.tokens - stage_row0(step);  // uniform; >= 1
+    const unsigned lastrow = (unsigned)(valid - 1) * rowb;
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
-      size_t off;
-      if (!TR) {
-        off = (size_t)q * gq + (size_t)step * gstep;
-      } else {
-        // token row of this lane; rows past the end read the last row (the
-        // stage's tail is zeroed in LDS before use)
-        int t = tok0 + step * SYK_KT + 2 * NW * q + trow;
-        t = t < pb.tokens ? t : pb.tokens - 1;
-        off = (size_t)t * tp;
-      }
-      __builtin_amdgcn_global_load_lds((const void*)(ga + off), (lds_void*)(base + (NW * q + w) * 1024), 16, 0, 0);
-      if (!DIAG)
-        __builtin_amdgcn_global_load_lds((const void*)(gb + off), (lds_void*)(base + SYK_OPB + (NW * q + w) * 1024),
-                                         16, 0, 0);
+      const int r = 2 * SYK_NW * q + trow;
+      const unsigned ro = r < valid ? (unsigned)r * rowb : lastrow;
+      curA[q] = ro + lbA;
+      curB[q] = ro + lbB;
     }
   };
-  // Fragment rows of this lane: arow + 32m (A), brow + 32q (B); all have
-  // (row/4)%4 == (lane/4)%4.  Wave w: rows 128 (w / WC), columns
-  // (256 / WC) (w % WC) of the tile.
-  const int arow = 128 * (w / WC) + (lane & 31);
-  const int brow = (256 / WC) * (w % WC) + (lane & 31);
+  auto issue_one = [&](int step, int stage, int q, bool bop) {
+    uint8_t* base = lds + stage * SYK_STB + (bop ? SYK_OPB : 0);
+    const void* src;
+    if (!TR) {
+      src = (bop ? gb : ga) + (size_t)q * gq + (size_t)step * gstep;
+    } else {
+      const size_t t0b = (size_t)stage_row0(step) * rowb;  // uniform
+      src = (bop ? xb : xa) + t0b + (bop ? curB[q] : curA[q]);
+    }
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (SYK_NW * q + w) * 1024), 16, 0, 0);
+  };
+  auto issue = [&](int step, int stage) {
+    if (TR) prep(step);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      issue_one(step, stage, q, false);
+      if (!DIAG) issue_one(step, stage, q, true);
+    }
+  };
+  // Fragment rows of this lane: 128 (w/2) + 32 m + lane%32 (A) and
+  // 128 (w%2) + 32 q + lane%32 (B); all have (row/4)%4 == (lane/4)%4.
+  const int arow = 128 * (w >> 1) + (lane & 31);
+  const int brow = 128 * (w & 1) + (lane & 31);
   const int sw = (lane >> 2) & 3;
   // TR: 16-lane group g = lane/16, i = lane%16: features 16(g%2) + 4(i%4) of
   // the 32-feature block, tokens 8(g/2) + i/4 (+4 for the second read)
   const int tg = lane >> 4, ti4 = lane & 15;
   const int tr_tok = 8 * (tg >> 1) + (ti4 >> 2);
   const int tr_f = 16 * (tg & 1) + 4 * (ti4 & 3);
-  auto tr_addr = [&](const uint8_t* st, int f, int tok) -> const lds_v4i16* {
-    const int c = f >> 3, half = (f >> 2) & 1;
-    return (const lds_v4i16*)(st + tok * 512 + ((c ^ (4 * (tok & 3))) << 4) + 8 * half);
-  };
-  auto rd = [&](const uint8_t* st, int ks, bf16x8* fa, bf16x8* fb) {
-    const uint8_t* sb = DIAG ? st : st + SYK_OPB;
+  // byte offset inside a stage of fragment k's first read (k < 4: A block m = k,
+  // else B block q = k - 4), for token sub-step 0; sub-step 1 adds 16 token rows
+  // (TR) or 32 bytes (!TR), the second TR read 4 token rows
+  int foff[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int bop = k >= 4 && !DIAG;
+    const int r = (k < 4 ? arow + 32 * k : brow + 32 * (k - 4));
     if (!TR) {
-      const int ch = ((2 * ks + (lane >> 5)) ^ sw) * 16;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) fa[m] = *(const bf16x8*)(st + (arow + 32 * m) * 64 + ch);
-#pragma unroll
-      for (int q = 0; q < NBF; ++q) fb[q] = *(const bf16x8*)(sb + (brow + 32 * q) * 64 + ch);
+      foff[k] = bop * SYK_OPB + r * 64 + (((lane >> 5) ^ sw) << 4);
     } else {
-      const int tok = 16 * ks + tr_tok;
+      const int f = (k < 4 ? 128 * (w >> 1) + 32 * k : 128 * (w & 1) + 32 * (k - 4)) + tr_f;
+      const int c = f >> 3, half = (f >> 2) & 1;
+      foff[k] = bop * SYK_OPB + tr_tok * 512 + ((c ^ (4 * (tr_tok & 3))) << 4) + 8 * half;
+    }
+  }
+  (void)arow;
+  (void)brow;
+  // The two reads (TR) or the one read (!TR) of fragment k of sub-step ks in
+  // the stage at st.
+  auto rd_lo = [&](const uint8_t* st, int ks, int k) -> v4i16 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + foff[k] + ks * 16 * 512));
+  };
+  auto rd_hi = [&](const uint8_t* st, int ks, int k) -> v4i16 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + foff[k] + ks * 16 * 512 + 4 * 512));
+  };
+  auto rd_b128 = [&](const uint8_t* st, int ks, int k) -> bf16x8 {
+    // sub-step ks: token chunk 2 ks + lane/32, stored at (2 ks + lane/32) ^ sw
+    const int off = foff[k] ^ ((2 * ks) << 4);
+    return *(const bf16x8*)(st + off);
+  };
+  auto join = [](v4i16 lo, v4i16 hi) -> bf16x8 {
+    const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  f32x16 acc[4][4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int f = 128 * (w / WC) + 32 * m + tr_f;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(st, f, tok));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(st, f, tok + 4));
-        const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        fa[m] = __builtin_bit_cast(bf16x8, v);
-      }
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int q = 0; q < NBF; ++q) {
-        const int f = (256 / WC) * (w % WC) + 32 * q + tr_f;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(sb, f, tok));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tr_addr(sb, f, tok + 4));
-        const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        fb[q] = __builtin_bit_cast(bf16x8, v);
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][q][r] = 0.f;
+
+  // MFMA order of a sub-step: new fragments come in gradually, in the order
+  // they are read (A0 B0 B1 A1 B2 A2 B3 A3).
+  constexpr int MORD[16][2] = {{0, 0}, {0, 1}, {1, 0}, {1, 1}, {0, 2}, {1, 2}, {2, 0}, {2, 1},
+                               {2, 2}, {0, 3}, {1, 3}, {2, 3}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
+  constexpr int RORD[8] = {0, 4, 5, 1, 6, 2, 7, 3};  // fragment read order (k: A m = k, B q = k - 4)
+
+  // One sub-step: the 16 MFMAs on cur[] with the 8 fragments of the next
+  // sub-step (stage nst, sub-step nks) read into nxt[] in between; with
+  // `loads`, the copies of stage `lstep` into slot `lslot` go between the
+  // MFMAs too.  The reads are issued behind the first 12 MFMAs (two behind
+  // each of the first four), so that they have landed when the next
+  // sub-step starts: its first MFMA waits for every LDS read of this one.
+  // The copies go behind the last 8 MFMAs.
+  auto substep = [&](const bf16x8* cur, bf16x8* nxt, const uint8_t* nst, int nks, bool loads, int lstep,
+                     int lslot) {
+    const bf16x8* ca = cur;
+    const bf16x8* cb = cur + 4;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = MORD[i][0], q = MORD[i][1];
+      acc[m][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[m], cb[q], acc[m][q], 0, 0, 0);
+      if ((i & 1) == 0) {
+        const int k = RORD[i >> 1];
+        if (TR) {
+          const v4i16 lo = rd_lo(nst, nks, k);
+          const v4i16 hi = rd_hi(nst, nks, k);
+          nxt[k] = join(lo, hi);
+        } else {
+          nxt[k] = rd_b128(nst, nks, k);
+        }
       }
+      if (loads && i >= 8 && (!DIAG || (i & 1) == 0)) {
+        issue_one(lstep, lslot, (i - 8) >> 1, !DIAG && (i & 1));
+      }
+    }
+    // TR: 16 reads of 8 bytes per lane; !TR: 8 reads of 16 bytes
+    constexpr int NR = TR ? 16 : 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      // TR: two reads behind MFMAs 0-3, one behind 4-11; !TR: one behind 0-7
+      const int nr = NR == 16 ? (i < 4 ? 2 : (i < 12 ? 1 : 0)) : (i < 8 ? 1 : 0);
+      if (nr == 2) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 2, 0);
+      if (nr == 1) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+      if (loads && i >= 8 && (!DIAG || (i & 1) == 0)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
     }
   };
   // TR: zero the token rows of stage `stage` (step `step`) past the end of X
@@ -198,21 +295,6 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
       const int op = e / (SYK_KT * 32), row = (e / 32) % SYK_KT, c = e % 32;
       if (row >= valid) *(u32x4*)(base + op * SYK_OPB + row * 512 + c * 16) = u32x4{0u, 0u, 0u, 0u};
     }
-  };
-
-  f32x16 acc[4][NBF];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int q = 0; q < NBF; ++q)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[m][q][r] = 0.f;
-  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int q = 0; q < NBF; ++q)
-        acc[m][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[q], acc[m][q], 0, 0, 0);
   };
 
   // Three stages in flight from the start; past the last step the copies
@@ -229,15 +311,16 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
     zero_tail(0, 0);
     __syncthreads();
   }
-  bf16x8 a0[4], b0[NBF], a1[4], b1[NBF];
-  constexpr int NRD = (4 + NBF) * (TR ? 2 : 1);  // LDS reads per sub-step
-  constexpr int NMF = 4 * NBF;                   // MFMAs per sub-step
-  constexpr int NIL = NRD < NMF ? NRD : NMF;     // interleaved pairs
-  rd(lds, 0, a0, b0);
+  bf16x8 f0[8], f1[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    f0[k] = TR ? join(rd_lo(lds, 0, k), rd_hi(lds, 0, k)) : rd_b128(lds, 0, k);
+  }
   for (int s = 0; s < nsteps; ++s) {
-    rd(lds + (s & 3) * SYK_STB, 1, a1, b1);
-    mma(a0, b0);
-
+    const uint8_t* st = lds + (s & 3) * SYK_STB;
+    // sub-step 2s on f0, reading sub-step 2s+1 (same stage) into f1
+    substep(f0, f1, st, 1, false, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // stage s+1 has landed (only stage s+2 may still be in flight) for this
     // wave, and after the barrier for every wave; stage s-1 is free
     __builtin_amdgcn_s_waitcnt(VmWait<L>::value);
@@ -247,10 +330,11 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
       zero_tail(s + 1, (s + 1) & 3);
       __syncthreads();
     }
-    issue(min(s + 3, last), (s + 3) & 3);
-    rd(lds + ((s + 1) & 3) * SYK_STB, 0, a0, b0);
-    mma(a1, b1);
-
+    // sub-step 2s+1 on f1, reading sub-step 2s+2 (stage s+1) into f0; the
+    // copies of stage s+3 go into the slot of stage s-1
+    if (TR) prep(min(s + 3, last));
+    substep(f1, f0, lds + ((s + 1) & 3) * SYK_STB, 0, true, min(s + 3, last), (s + 3) & 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(VmWait<0>::value);  // no copy into LDS outlives the group
 
@@ -258,16 +342,15 @@ __device__ __forceinline__ void syrk_tile(const SyrkProb& pb, const SyrkTask& tk
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int q = 0; q < NBF; ++q)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 128 * (w / WC) + 32 * m + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = (256 / WC) * (w % WC) + 32 * q + (lane & 31);
+        const int row = 128 * (w >> 1) + 32 * m + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = 128 * (w & 1) + 32 * q + (lane & 31);
         P[row * 256 + col] = acc[m][q][r];
       }
 }
 
-#define SYK_NW 8  // waves per workgroup (2 per SIMD)
 __global__ __launch_bounds__(64 * SYK_NW, 1) void k_syrk(const SyrkProb* __restrict__ probs,
                                                          const SyrkTask* __restrict__ tasks,
                                                          float* __restrict__ partials) {
@@ -278,14 +361,14 @@ __global__ __launch_bounds__(64 * SYK_NW, 1) void k_syrk(const SyrkProb* __restr
   const bool diag = tk.ti == tk.tj && !pb.Yt;  // one operand serves both sides
   if (pb.direct) {
     if (diag)
-      syrk_tile<true, true, SYK_NW>(pb, tk, lds, partials);
+      syrk_tile<true, true>(pb, tk, lds, partials);
     else
-      syrk_tile<false, true, SYK_NW>(pb, tk, lds, partials);
+      syrk_tile<false, true>(pb, tk, lds, partials);
   } else {
     if (diag)
-      syrk_tile<true, false, SYK_NW>(pb, tk, lds, partials);
+      syrk_tile<true, false>(pb, tk, lds, partials);
     else
-      syrk_tile<false, false, SYK_NW>(pb, tk, lds, partials);
+      syrk_tile<false, false>(pb, tk, lds, partials);
   }
 }
 
