@@ -769,24 +769,24 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
   // buffer), joined before the next far update.  Needs the groups to nest in
   // a super-block (a group fit reads its whole group).
   bool side_busy = false;
+  // One sweep launch per super-block (the sweep kernel applies each block's
+  // errors to the rest of its super-block itself).
   for (int k = 0; k < maxblk; ++k) {
     for (int B : blocks)
       for (int mode = 0; mode < 2; ++mode) {
         std::vector<Seg> s;
         for (int p = 0; p < nl; ++p)
-          if (jobs[p].block == B && jobs[p].mode == mode && k < L[p].nblk)
-            s.push_back(Seg{p, 0, cdiv(jobs[p].out, 16), k, 0, 0, 0, 0});
+          if (jobs[p].block == B && jobs[p].mode == mode && k < L[p].nblk && k % sbk[p] == 0)
+            s.push_back(Seg{p, 0, cdiv(jobs[p].out, 16), k / sbk[p], 0, 0, 0, 0});
         add_launch(2, B, s, false, mode);
       }
-    std::vector<Seg> tn, crit, bulk;  // inside the super-block (64 tiles), past it (64 / 128 tiles)
+    std::vector<Seg> crit, bulk;  // past the super-block (64 / 128 tiles)
     for (int p = 0; p < nl; ++p) {
       if (k >= L[p].nblk) continue;
       const int B = jobs[p].block, n = jobs[p].n, nt = jobs[p].nt, sb = sbk[p], sbw = sb * B;
       const int b0 = k * B, b1 = std::min(b0 + B, n);
       const int sb0 = (k / sb) * sbw, sb1 = std::min(sb0 + sbw, n);
       const int par = ((k / sb) & 1) * jobs[p].out * L[p].ldE;  // this super-block's half of the error buffer
-      if (b1 < sb1)  // rest of the super-block
-        tn.push_back(Seg{p, 0, cdiv(jobs[p].out, 64) * cdiv(sb1 - b1, 64), par + (k % sb) * B, b0, b1 - b0, b1, sb1});
       if (b1 == sb1 && sb1 < nt) {  // end of the super-block: all columns past it
         const bool nest = jobs[p].group == 0 || sbw % jobs[p].group == 0;
         const int S = nest ? std::min(sb1 + sbw, nt) : nt;
@@ -794,7 +794,6 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
         if (S < nt) bulk.push_back(Seg{p, 0, cdiv(jobs[p].out, 128) * cdiv(nt - S, 128), par, sb0, sb1 - sb0, S, nt});
       }
     }
-    add_launch(3, 64, tn);
     if (!crit.empty()) {
       if (side_busy) add_sync(7);  // the previous far update covers the columns updated now
       side_busy = false;

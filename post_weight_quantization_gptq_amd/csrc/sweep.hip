@@ -82,16 +82,20 @@ struct SweepState {
 
 struct SweepCtx {
   const float* Us;     // LDS U block
-  const float* Wwrow;  // working row (global)
+  const float* Wwrow;  // working row (global), columns past the super-block
+  const float* Wsrow;  // the row's columns of the super-block in LDS, indexed by column - sb0
   float maxq;
   int B, bw, b0, G, l16, rv;
+  int sb0, sb1;        // the super-block's columns [sb0, sb1)
   float* scales;
   uint8_t* zeros;
   size_t grow;  // row offset into scales/zeros
 };
 
 // Fit the grid of the group starting at in-block column j on the current
-// values of columns [j, j+G) (registers, and the working row past the block).
+// values of columns [j, j+G): registers for the block, the super-block's
+// rows in LDS past it, the working row in global memory past the
+// super-block.
 template <int CPL>
 __device__ __forceinline__ void fit_group(SweepState<CPL>& st, const SweepCtx& cx, int j) {
   float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
@@ -105,7 +109,8 @@ __device__ __forceinline__ void fit_group(SweepState<CPL>& st, const SweepCtx& c
   }
   if (j + cx.G > cx.B && cx.rv)  // group extends past this block
     for (int cc = cx.B + cx.l16; cc < j + cx.G; cc += 16) {
-      const float v = cx.Wwrow[cx.b0 + cc];
+      const int col = cx.b0 + cc;
+      const float v = col < cx.sb1 ? cx.Wsrow[col - cx.sb0] : cx.Wwrow[col];
       mn = fminf(mn, v);
       mx = fmaxf(mx, v);
     }
@@ -218,69 +223,66 @@ struct SweepAll<16, CPL, BID> {
   __device__ __forceinline__ static void run(SweepState<CPL>&, const SweepCtx&, float (&)[CPL]) {}
 };
 
+// One super-block of sbk consecutive blocks for 16 rows per workgroup (4
+// rows per wave, 16 lanes per row).  The rows' columns of the super-block
+// stay in LDS for the whole launch; after each block is swept, the block's
+// errors reach the rest of the super-block at once, W[rows, b1:sb1] -=
+// E[rows, blk] U[blk, b1:sb1], on the workgroup's own fp32 MFMAs
+// (v_mfma_f32_16x16x4f32, one 16-column tile per wave at a time), with U
+// staged through LDS one B x B chunk at a time.  Columns past the
+// super-block get one product per super-block afterwards (k_trail), from
+// the errors stored in the super-block's half of the error buffer.
+//
 // BID: one Bid-Up pass instead of the GPTQ sweep (codes are read as the
 // starting point, the grid is the one given, and the per-row sums are the
 // objective changes of the moves).
+#define SWEEP_SBW 512  // widest super-block (blocks x block width)
+template <int B>
+struct SweepLds {
+  static constexpr int WP = SWEEP_SBW + 4;
+  static constexpr int EP = B + 4;
+  float us[B * B];   // the diagonal block of U
+  float ws[16 * WP];  // the rows' columns of the super-block
+  float es[16 * EP];  // the block's errors
+};
+
 template <int CPL, bool BID>
 __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
                                                const Seg* __restrict__ segs, int nseg) {
   constexpr int B = 16 * CPL;
-  __shared__ __attribute__((aligned(16))) float Us[B * B];
+  using LD = SweepLds<B>;
+  __shared__ __attribute__((aligned(16))) LD lds;
+  float* Us = lds.us;
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
   const QLayer ly = L[sg.prob];
-  const int blk = sg.a;
-  const int b0 = blk * B, b1 = min(b0 + B, ly.n), bw = b1 - b0;
+  const int sbi = sg.a;  // super-block index
+  const int kb0 = sbi * ly.sbk, kb1 = min(kb0 + ly.sbk, ly.nblk);
+  const int sb0 = kb0 * B, sb1 = min(kb1 * B, ly.n), sbw = sb1 - sb0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15;
-  const int row = (blockIdx.x - sg.wg0) * 16 + w * 4 + (lane >> 4);
+  const int l16 = lane & 15, rr = w * 4 + (lane >> 4);
+  const int r0 = (blockIdx.x - sg.wg0) * 16;
+  const int row = r0 + rr;
   const bool rv = row < ly.out;
   const int nt = ly.nt, G = ly.group;
 
-  // the row's loads first, then the U block, all in flight together
-  SweepState<CPL> st;
-  float wo[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int lc = CPL * l16 + c;
-    const bool in = rv && lc < bw;
-    st.wv[c] = in ? ly.Ww[(size_t)row * nt + b0 + lc] : 0.f;
-    st.dv[c] = (lc < bw) ? ly.dinv[b0 + lc] : 0.f;
-    wo[c] = (in && !BID) ? ly.W[(size_t)row * ly.n + b0 + lc] : 0.f;
-    st.qv[c] = (in && BID) ? (float)ly.codes[(size_t)row * ly.n + b0 + lc] : 0.f;
-    st.hv[c] = 0.f;
-    st.ev[c] = 0.f;
-  }
-  // the row's objective sums so far (added to at the end)
-  double obj_e = 0.0, obj_d = 0.0;
-  if (rv && l16 == 0) {
-    obj_e = ly.objp[(size_t)row * 2];
-    obj_d = ly.objp[(size_t)row * 2 + 1];
-  }
-  st.g = Grid{1.f, 1.f, 0.f};
-  if (rv && (G == 0 || (b0 % G) != 0)) {
-    // the row's grid, or the grid of a group that began in an earlier block
-    const size_t gi = (size_t)row * ly.ng + (G ? b0 / G : 0);
-    st.g.s = ly.scales[gi];
-    st.g.r = 1.f / st.g.s;
-    st.g.z = (float)ly.zeros[gi];
-  }
-  {
-    // U block -> LDS: all loads of a thread in flight at once, 16 B each
-    constexpr int PER = (B * B / 4 + 255) / 256;
-    const bool vec = (nt % 4) == 0 && bw == B;
+  // the diagonal block U[b0r:b0r+bwr, c0:c0+cw] (c0 = b0r, cw = bwr) -> LDS at
+  // pitch B, zero past the ragged edge; all loads of a thread in flight at once
+  auto load_u = [&](int b0r, int bwr, int c0, int cw, int pitch) {
+    constexpr int PER = B * B / 4 / 256 > 0 ? B * B / 4 / 256 : 1;
+    const bool vec = (nt % 4) == 0 && (c0 % 4) == 0 && cw == B;
     f32x4 tmp[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int idx = tid + 256 * q;
       const int j = idx / (B / 4), k4 = (idx % (B / 4)) * 4;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (idx < B * B / 4 && j < bw) {
-        const float* src = ly.U + (size_t)(b0 + j) * nt + b0 + k4;
+      if (idx < B * B / 4 && j < bwr) {
+        const float* src = ly.U + (size_t)(b0r + j) * nt + c0 + k4;
         if (vec) {
           v = *(const f32x4*)src;
         } else {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = (k4 + u < bw) ? src[u] : 0.f;
+          for (int u = 0; u < 4; ++u) v[u] = (k4 + u < cw) ? src[u] : 0.f;
         }
       }
       tmp[q] = v;
@@ -288,54 +290,243 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int idx = tid + 256 * q;
-      if (idx < B * B / 4) *(f32x4*)&Us[idx * 4] = tmp[q];
+      const int j = idx / (B / 4), k4 = (idx % (B / 4)) * 4;
+      if (idx < B * B / 4) *(f32x4*)&Us[j * pitch + k4] = tmp[q];
+    }
+  };
+
+  // the rows' super-block columns -> LDS (zeros for rows past the end), the
+  // first diagonal block of U, and the rows' objective sums so far
+  {
+    const bool vec = (nt % 4) == 0 && (sbw % 4) == 0;
+    const int per_row = (sbw + 3) / 4;
+    for (int e = tid; e < 16 * per_row; e += 256) {
+      const int r = e / per_row, c4 = (e % per_row) * 4;
+      const int gr = r0 + r;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (gr < ly.out) {
+        const float* src = ly.Ww + (size_t)gr * nt + sb0 + c4;
+        if (vec) {
+          v = *(const f32x4*)src;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = (c4 + u < sbw) ? src[u] : 0.f;
+        }
+      }
+      *(f32x4*)&lds.ws[r * LD::WP + c4] = v;
     }
   }
-  st.nextg = (G == 0) ? (1 << 30) : ((b0 % G) == 0 ? 0 : G - (b0 % G));
+  load_u(sb0, min(B, ly.n - sb0), sb0, min(B, ly.n - sb0), B);
+  double obj_e = 0.0, obj_d = 0.0;
+  if (rv && l16 == 0) {
+    obj_e = ly.objp[(size_t)row * 2];
+    obj_d = ly.objp[(size_t)row * 2 + 1];
+  }
+  SweepState<CPL> st;
+  st.g = Grid{1.f, 1.f, 0.f};
+  if (rv && (G == 0 || (sb0 % G) != 0)) {
+    // the row's grid, or the grid of a group that began in an earlier super-block
+    const size_t gi = (size_t)row * ly.ng + (G ? sb0 / G : 0);
+    st.g.s = ly.scales[gi];
+    st.g.r = 1.f / st.g.s;
+    st.g.z = (float)ly.zeros[gi];
+  }
   SweepCtx cx;
   cx.Us = Us;
   cx.Wwrow = ly.Ww + (size_t)(rv ? row : 0) * nt;
+  cx.Wsrow = lds.ws + rr * LD::WP;
   cx.maxq = (float)((1 << ly.bits) - 1);
   cx.B = B;
-  cx.bw = bw;
-  cx.b0 = b0;
   cx.G = G;
   cx.l16 = l16;
   cx.rv = rv;
+  cx.sb0 = sb0;
+  cx.sb1 = sb1;
   cx.scales = ly.scales;
   cx.zeros = ly.zeros;
   cx.grow = (size_t)(rv ? row : 0) * ly.ng;
-  __syncthreads();
-
-  float ucur[CPL];
+  double se = 0.0, sd = 0.0;  // this lane's sums over the super-block, in block order
+  // the next block's per-column inputs, loaded ahead (their latency hides
+  // behind the previous block's update)
+  float pdv[CPL], pwo[CPL], pqv[CPL];
+  auto prefetch = [&](int blk) {
+    const int b0 = blk * B, bw = min(B, ly.n - b0);
 #pragma unroll
-  for (int v = 0; v < CPL; ++v) ucur[v] = Us[CPL * l16 + v];
-  SweepAll<0, CPL, BID>::run(st, cx, ucur);
-
-  double se = 0.0, sd = 0.0;
+    for (int c = 0; c < CPL; ++c) {
+      const int lc = CPL * l16 + c;
+      const bool in = rv && lc < bw;
+      pdv[c] = (lc < bw) ? ly.dinv[b0 + lc] : 0.f;
+      pwo[c] = (in && !BID) ? ly.W[(size_t)row * ly.n + b0 + lc] : 0.f;
+      pqv[c] = (in && BID) ? (float)ly.codes[(size_t)row * ly.n + b0 + lc] : 0.f;
+    }
+  };
+  // a whole B x B diagonal block of U straight into LDS (pitch B), 1 KB per
+  // instruction, without registers; in flight during the update
+  const bool u_dma = (nt % 4) == 0 && (((uintptr_t)ly.U) & 15) == 0;
+  auto dma_u = [&](int nb0) {
+    constexpr int NINST = B * B / 256;  // 1 KB instructions for the block
+    constexpr int RPI = 256 / B;        // rows per instruction
+    const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int lc = CPL * l16 + c;
-    if (rv && lc < bw) {
-      ly.codes[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
-      ly.Eb[((size_t)((blk / ly.sbk) & 1) * ly.out + row) * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
-      if (ly.err) ly.err[(size_t)row * ly.n + b0 + lc] = st.ev[c];
-      if (BID) {
-        se += (double)st.hv[c];
-      } else {
-        const double d = (double)wo[c] - (double)st.hv[c];
-        sd += d * d;
-        se += (double)st.ev[c] * (double)st.ev[c];
+    for (int q = 0; q < (NINST + 3) / 4; ++q) {
+      const int inst = 4 * q + wu;
+      if (inst < NINST) {
+        const int r = inst * RPI + (4 * lane) / B, cc = (4 * lane) % B;
+        __builtin_amdgcn_global_load_lds((const void*)(ly.U + (size_t)(nb0 + r) * nt + nb0 + cc),
+                                         (lds_void*)(Us + inst * 256), 16, 0, 0);
       }
     }
+  };
+  prefetch(kb0);
+  __syncthreads();
+
+  for (int blk = kb0; blk < kb1; ++blk) {
+    const int b0 = blk * B, b1 = min(b0 + B, ly.n), bw = b1 - b0;
+    cx.bw = bw;
+    cx.b0 = b0;
+    float wo[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int lc = CPL * l16 + c;
+      st.wv[c] = lc < bw ? lds.ws[rr * LD::WP + b0 - sb0 + lc] : 0.f;
+      st.dv[c] = pdv[c];
+      wo[c] = pwo[c];
+      st.qv[c] = pqv[c];
+      st.hv[c] = 0.f;
+      st.ev[c] = 0.f;
+    }
+    st.nextg = (G == 0) ? (1 << 30) : ((b0 % G) == 0 ? 0 : G - (b0 % G));
+
+    float ucur[CPL];
+#pragma unroll
+    for (int v = 0; v < CPL; ++v) ucur[v] = Us[CPL * l16 + v];
+    SweepAll<0, CPL, BID>::run(st, cx, ucur);
+
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int lc = CPL * l16 + c;
+      lds.es[rr * LD::EP + lc] = st.ev[c];  // zero past bw (the sweep leaves ev = 0 there)
+      if (rv && lc < bw) {
+        ly.codes[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
+        ly.Eb[((size_t)((blk / ly.sbk) & 1) * ly.out + row) * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
+        if (ly.err) ly.err[(size_t)row * ly.n + b0 + lc] = st.ev[c];
+        if (BID) {
+          se += (double)st.hv[c];
+        } else {
+          const double d = (double)wo[c] - (double)st.hv[c];
+          sd += d * d;
+          se += (double)st.ev[c] * (double)st.ev[c];
+        }
+      }
+    }
+    __syncthreads();  // the errors are in LDS; the diagonal U block is free
+    const bool more = blk + 1 < kb1;
+    const int nb0 = b1, nbw = more ? min(B, ly.n - nb0) : 0;
+    const bool dma = more && u_dma && nbw == B;
+    if (more) {
+      prefetch(blk + 1);
+      if (dma) dma_u(nb0);
+    }
+    // The block's errors reach the rest of the super-block:
+    // W[rows, b1:sb1] -= E[rows, blk] U[blk, b1:sb1] on v_mfma_f32_16x16x4f32,
+    // one tile of 16 rows x 64 columns per wave at a time.  K order: lane
+    // group g = lane / 16 takes k = (B / 4) g + kk at step kk (the same in
+    // both operands), so a lane's E values are contiguous in LDS; the four
+    // MFMAs of a step take columns 4 (lane % 16) + u, u = 0..3, of the tile,
+    // so a lane's U values are one 16-byte load per step.  bw == B whenever
+    // columns follow the block (only the layer's last block is ragged).
+    {
+      constexpr int KQ = B / 4;
+      constexpr int KH = KQ > 8 ? 8 : KQ;  // K steps per work item
+      constexpr int NH = KQ / KH;          // items per 64-column tile
+      const int li = lane & 15, g = lane >> 4;
+      const bool uvec = (nt % 4) == 0 && (((uintptr_t)ly.U) & 15) == 0;
+      // this wave's work items: tiles c0 = b1 + 64 (w + 4 i), each in NH
+      // K-halves; the U loads of item it+1 are in flight while item it is
+      // multiplied
+      const int ntile = (sb1 - b1 + 63) / 64;
+      const int myt = ntile > w ? (ntile - w + 3) / 4 : 0;
+      const int nitem = myt * NH;
+      auto load_item = [&](int it, f32x4 (&ub)[KH]) {
+        const int c0 = b1 + 64 * (w + 4 * (it / NH)), h = it % NH;
+        const int col = c0 + 4 * li;
+        const bool full = uvec && col + 4 <= sb1;
+#pragma unroll
+        for (int kk = 0; kk < KH; ++kk) {
+          const float* src = ly.U + (size_t)(b0 + KQ * g + KH * h + kk) * nt + col;
+          if (full) {
+            ub[kk] = *(const __attribute__((address_space(1))) f32x4*)src;
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ub[kk][u] = (col + u < sb1) ? src[u] : 0.f;
+          }
+        }
+      };
+      f32x4 ubA[KH], ubB[KH];
+      f32x4 acc[4];
+      if (nitem > 0) load_item(0, ubA);
+      for (int it = 0; it < nitem; it += 2) {
+        // two items per trip (register sets A and B alternate)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int cur = it + half;
+          if (cur >= nitem) break;
+          f32x4 (&ubc)[KH] = half ? ubB : ubA;
+          f32x4 (&ubn)[KH] = half ? ubA : ubB;
+          if (cur + 1 < nitem) load_item(cur + 1, ubn);
+          const int c0 = b1 + 64 * (w + 4 * (cur / NH)), h = cur % NH;
+          const int col = c0 + 4 * li;
+          if (h == 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          float ea[KH];
+#pragma unroll
+          for (int k4 = 0; k4 < KH / 4; ++k4) {
+            const f32x4 v = *(const f32x4*)&lds.es[li * LD::EP + KQ * g + KH * h + 4 * k4];
+            ea[4 * k4] = v[0];
+            ea[4 * k4 + 1] = v[1];
+            ea[4 * k4 + 2] = v[2];
+            ea[4 * k4 + 3] = v[3];
+          }
+#pragma unroll
+          for (int kk = 0; kk < KH; ++kk)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kk], ubc[kk][u], acc[u], 0, 0, 0);
+          if (h == NH - 1) {
+            // lane: rows 4 g + q, columns col + u
+            const bool full = col + 4 <= sb1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float* wr = &lds.ws[(4 * g + q) * LD::WP + col - sb0];
+              if (full) {
+                f32x4 v = *(f32x4*)wr;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] -= acc[u][q];
+                *(f32x4*)wr = v;
+              } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                  if (col + u < sb1) wr[u] -= acc[u][q];
+              }
+            }
+          }
+        }
+      }
+    }
+    if (more && !dma) load_u(nb0, nbw, nb0, nbw, B);
+    __builtin_amdgcn_s_waitcnt(0);  // the next diagonal block has landed
+    __syncthreads();                // the updated columns and that block are visible
   }
+
 #pragma unroll
   for (int m = 8; m > 0; m >>= 1) {
     se += __shfl_xor(se, m, 16);
     sd += __shfl_xor(sd, m, 16);
   }
   if (rv && l16 == 0) {
-    // per-row sums, accumulated over the blocks in block order
+    // per-row sums, accumulated over the super-blocks in order
     double* op = ly.objp + (size_t)row * 2;
     op[0] = obj_e + se;
     op[1] = obj_d + sd;
@@ -354,7 +545,9 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
   constexpr int MB = TS / 64;        // 32x32 blocks per wave side
   constexpr int TPR = 256 / TS;      // threads per E row
   constexpr int VA = KC / TPR;       // E values per thread (multiple of 4)
-  constexpr int VB = TS / 8;         // U values per thread (8 threads per k row)
+  constexpr int TPK = 256 / KC;      // threads per U row (k)
+  constexpr int VB = TS / TPK;       // U values per thread (multiple of 4)
+  static_assert(VA % 4 == 0 && VB % 4 == 0 && VB >= 4, "load split");
   __shared__ float As[2][TS][KC + 1];
   __shared__ __attribute__((aligned(16))) float Bs[2][KC][TS + 4];
   // tiles vt = blockIdx.x, blockIdx.x + gridDim.x, ... < ntot (persistent when
@@ -379,7 +572,7 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int ar = tid / TPR, ak = (tid % TPR) * VA;  // E: row, first k
-  const int bk = tid >> 3, bj = (tid & 7) * VB;     // U: k row, first column
+  const int bk = tid / TPK, bj = (tid % TPK) * VB;  // U: k row, first column
   const bool arow_ok = ar < mt;
   const float* ap = ly.Eb + (size_t)(i0 + (arow_ok ? ar : 0)) * ly.ldE + eoff;
   const bool evec = (ly.ldE % 4) == 0 && (eoff % 4) == 0;
