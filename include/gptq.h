@@ -136,6 +136,24 @@ int gptq_lora(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const uint16
               int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
               uint8_t* zeros, float* L, float* R, double* obj, int32_t* info);
 
+/* gptq_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, checks, kernels and results (codes, scales, zeros, err
+ * and obj bit-identical to gptq_quantize on the same inputs), but every
+ * intermediate lives in a fixed array of about 8.5 MB of device memory that
+ * the library holds for the process's lifetime, one copy per device, and
+ * the pinned host staging it uses is made when the context is created.  The
+ * call performs no hipMalloc, hipFree, hipHostMalloc or event creation.
+ * Limits: out <= 1024, n <= 4096, out * n <= 2^20; beyond them
+ * GPTQ_ERR_UNSUPPORTED with a message.  All contexts on one device share its array, whose
+ * contents persist from call to call (the parts that must start at zero are
+ * cleared by the call's own kernels): calls that overlap on one device race
+ * and give undefined results; serialise them.  Per-kernel timing is off for
+ * this call.  SYNC (objective read back). */
+int gptq_quantize_noalloc(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const float* U,
+                          int32_t bits, int32_t group, int32_t block, double lam,
+                          uint8_t* codes, float* scales, uint8_t* zeros, float* err, double* obj);
+
 /* Gram matrix accurate to float64 rounding, H = X^T X in fp64 (the products
  * of bf16 values are exact in fp64 and the sums run in fp64 on fp64 MFMA).  X
  * as gptq_hessian; H[n][n] fp64, device, caller-owned, fully written.  The

@@ -93,6 +93,7 @@ def load_library(path: str | None = None):
     L.gptq_factor.argtypes = [vp, vp, i32, d, d, vp, ctypes.POINTER(i32), ctypes.POINTER(d)]
     L.gptq_quantize.argtypes = [vp, vp, i32, i32, vp, i32, i32, i32, d, vp, vp, vp, vp,
                                 ctypes.POINTER(d)]
+    L.gptq_quantize_noalloc.argtypes = L.gptq_quantize.argtypes
     L.gptq_lora.argtypes = [vp, vp, i32, i32, vp, i64, i64, i32, i32, i32, i32, d, d,
                             vp, vp, vp, vp, vp, ctypes.POINTER(d), ctypes.POINTER(i32)]
     L.gptq_lora_refine.argtypes = [vp, vp, i32, i32, vp, i64, i64, i32, i32, i32, i32, d, d, i32,
@@ -113,7 +114,7 @@ def load_library(path: str | None = None):
     L.gptq_timing.argtypes = [vp, ctypes.c_char_p]
     L.gptq_kernel_time.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(d), ctypes.POINTER(i64)]
     for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
-                 "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up", "gptq_round_2d",
+                 "gptq_quantize_noalloc", "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up", "gptq_round_2d",
                  "gptq_quantize_qronos", "gptq_cross_gram", "gptq_pack_codes", "gptq_unpack_codes",
                  "gptq_quantize_lowrank", "gptq_gemm_w4a16",
                  "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
@@ -261,6 +262,22 @@ class Context:
         self._check(self.lib.gptq_quantize(self.handle, _ptr(W), o, n, _ptr(U), int(bits), int(group), int(block),
                                            float(lam), _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["zeros"]),
                                            _ptr(out.get("err")), obj))
+        res = dict(out)
+        res["J"], res["J_lam"] = obj[0], obj[1]
+        return res
+
+    def quantize_noalloc(self, W, U, bits: int, group: int, block: int, lam: float, out, want_err: bool = False):
+        """quantize() through the entry point that allocates nothing: the outputs are
+        caller-provided tensors in ``out`` (codes, scales, zeros and optionally err)."""
+        torch = self.torch
+        self._dev(W, torch.float32, "W")
+        self._dev(U, torch.float32, "U")
+        o, n = W.shape
+        obj = (ctypes.c_double * 2)()
+        self._check(self.lib.gptq_quantize_noalloc(self.handle, _ptr(W), o, n, _ptr(U), int(bits), int(group),
+                                                   int(block), float(lam), _ptr(out["codes"]), _ptr(out["scales"]),
+                                                   _ptr(out["zeros"]), _ptr(out.get("err") if want_err else None),
+                                                   obj))
         res = dict(out)
         res["J"], res["J_lam"] = obj[0], obj[1]
         return res

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <mutex>
 #include <vector>
 
 #include "../../include/gptq.h"
@@ -41,6 +42,8 @@ struct gptq_ctx_s {
   size_t hsmall_cap = 0;
   hipEvent_t blob_ev = nullptr;
   bool blob_pending = false;
+  // this device's copy of the no-allocation scratch array (device address)
+  uint8_t* na_base = nullptr;
   // second stream (default priority) for the factor's trailing updates that
   // run beside its serial chain; fork / join events order it against stream
   hipStream_t side = nullptr;
@@ -204,6 +207,60 @@ int upload(gptq_ctx c, const Blob& b, uint8_t** dbase) {
   HIPCHK(c, hipEventRecord(c->blob_ev, c->stream));
   c->blob_pending = true;
   *dbase = (uint8_t*)c->blob.p;
+  return GPTQ_OK;
+}
+
+// ------------------------------------------- no-allocation scratch ------
+// gptq_quantize_noalloc works entirely inside this array (one copy per
+// device, held until the process ends): the device slot, the task tables, the
+// working weights, the errors of two super-blocks, the per-row sums and the
+// error scales.  Limits: out <= NA_MAX_OUT, n <= NA_MAX_N, out * n <= NA_MAX_ELEMS.
+constexpr int NA_MAX_OUT = 1024;
+constexpr int NA_MAX_N = 4096;
+constexpr long long NA_MAX_ELEMS = 1LL << 20;
+constexpr size_t NA_SLOT = 256;
+constexpr size_t NA_BLOB = 64 << 10;
+constexpr size_t NA_WW = (size_t)NA_MAX_ELEMS * sizeof(float);
+constexpr size_t NA_EB = (size_t)2 * NA_MAX_OUT * 512 * sizeof(float);
+constexpr size_t NA_OBJP = (size_t)NA_MAX_OUT * 2 * sizeof(double);
+constexpr size_t NA_DINV = (size_t)(NA_MAX_N + 64) * sizeof(float);
+constexpr size_t NA_BYTES = NA_SLOT + NA_BLOB + NA_WW + NA_EB + NA_OBJP + NA_DINV;
+
+// Pointers into the scratch array of one device.
+struct NoAlloc {
+  Slot* slot;
+  uint8_t* blob;
+  float* ww;
+  float* eb;
+  double* objp;
+  float* dinv;
+};
+NoAlloc noalloc_view(uint8_t* base) {
+  NoAlloc v;
+  v.slot = (Slot*)base;
+  v.blob = base + NA_SLOT;
+  v.ww = (float*)(v.blob + NA_BLOB);
+  v.eb = (float*)((uint8_t*)v.ww + NA_WW);
+  v.objp = (double*)((uint8_t*)v.eb + NA_EB);
+  v.dinv = (float*)((uint8_t*)v.objp + NA_OBJP);
+  return v;
+}
+
+// Upload a blob into the scratch array through the context's pinned staging
+// (allocated when the context was created); never allocates.
+int upload_noalloc(gptq_ctx c, const Blob& b, uint8_t* dst, uint8_t** dbase) {
+  const size_t bytes = b.h.size();
+  if (bytes > NA_BLOB || bytes > c->hblob_cap)
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "task tables of %zu bytes exceed the no-allocation limit", bytes);
+  if (c->blob_pending) {
+    HIPCHK(c, hipEventSynchronize(c->blob_ev));
+    c->blob_pending = false;
+  }
+  memcpy(c->hblob, b.h.data(), bytes);
+  HIPCHK(c, hipMemcpyAsync(dst, c->hblob, bytes, hipMemcpyHostToDevice, c->stream));
+  HIPCHK(c, hipEventRecord(c->blob_ev, c->stream));
+  c->blob_pending = true;
+  *dbase = dst;
   return GPTQ_OK;
 }
 
@@ -667,7 +724,10 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
 }
 
 // ----------------------------------------------------------- quantize plan --
-int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<float*>* Ww_out = nullptr) {
+// na: run inside the no-allocation scratch array (single layer within the
+// limits, checked by the caller); nothing is allocated.
+int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<float*>* Ww_out = nullptr,
+                 const NoAlloc* na = nullptr) {
   const int nl = (int)jobs.size();
   // Super-blocks: each block's errors reach the rest of its super-block right
   // away, the columns past it only at the super-block's end (one product with
@@ -692,25 +752,43 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     totD += (size_t)(J.nt + 63) / 64 * 64;
   }
   int rc;
-  if ((rc = ensure(c, c->work, totW * sizeof(float)))) return rc;
-  if ((rc = ensure(c, c->eblk, totE * sizeof(float)))) return rc;
-  if ((rc = ensure(c, c->objp, totO * sizeof(double)))) return rc;
-  if ((rc = ensure(c, c->dinv, totD * sizeof(float)))) return rc;
+  float* work_p;
+  float* eblk_p;
+  double* objp_p;
+  float* dinv_p;
+  if (na) {
+    if (totW * sizeof(float) > NA_WW || totE * sizeof(float) > NA_EB || totO * sizeof(double) > NA_OBJP ||
+        totD * sizeof(float) > NA_DINV)
+      return set_err(c, GPTQ_ERR_UNSUPPORTED, "layer exceeds the no-allocation limits");
+    work_p = na->ww;
+    eblk_p = na->eb;
+    objp_p = na->objp;
+    dinv_p = na->dinv;
+  } else {
+    if ((rc = ensure(c, c->work, totW * sizeof(float)))) return rc;
+    if ((rc = ensure(c, c->eblk, totE * sizeof(float)))) return rc;
+    if ((rc = ensure(c, c->objp, totO * sizeof(double)))) return rc;
+    if ((rc = ensure(c, c->dinv, totD * sizeof(float)))) return rc;
+    work_p = (float*)c->work.p;
+    eblk_p = (float*)c->eblk.p;
+    objp_p = (double*)c->objp.p;
+    dinv_p = (float*)c->dinv.p;
+  }
   std::vector<QLayer> L(nl);
   int maxblk = 0;
   for (int p = 0; p < nl; ++p) {
     const QuantJob& J = jobs[p];
     QLayer q;
     q.W = J.W;
-    q.Ww = J.Ww_ext ? J.Ww_ext : (float*)c->work.p + oW[p];
+    q.Ww = J.Ww_ext ? J.Ww_ext : work_p + oW[p];
     q.U = J.U;
     q.codes = J.codes;
     q.scales = J.scales;
     q.zeros = J.zeros;
     q.err = J.err;
-    q.Eb = (float*)c->eblk.p + oE[p];
-    q.objp = (double*)c->objp.p + oO[p];
-    q.dinv = (const float*)c->dinv.p + oD[p];
+    q.Eb = eblk_p + oE[p];
+    q.objp = objp_p + oO[p];
+    q.dinv = dinv_p + oD[p];
     q.obj = J.obj;
     q.lam = J.lam;
     q.out = J.out;
@@ -807,7 +885,7 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
   }
   if (side_busy) add_sync(7);
   uint8_t* d = nullptr;
-  if ((rc = upload(c, b, &d))) return rc;
+  if ((rc = na ? upload_noalloc(c, b, na->blob, &d) : upload(c, b, &d))) return rc;
   const QLayer* dL = (const QLayer*)(d + o_L);
   for (const Lc& l : launches) {
     const Seg* sg = (const Seg*)(d + l.off);
@@ -860,6 +938,15 @@ int ensure_small(gptq_ctx c, size_t bytes) { return ensure_pinned(c, c->hsmall, 
 
 }  // namespace
 
+// The no-allocation scratch array (see NoAlloc) and each device's address of
+// its copy, looked up once per device (with that device current) when the
+// first context on it is created.  Host code must use these addresses, never
+// the array's name (a host-side stand-in).
+static __device__ __align__(256) uint8_t scratch[NA_BYTES];
+static std::mutex g_na_mu;
+static uint8_t* g_na_ptr[64];
+static int g_na_state[64];  // 0: not looked up, 1: found, 2: lookup failed
+
 // ================================================================ C ABI ====
 GPTQ_API const char* gptq_strerror(int status) {
   switch (status) {
@@ -898,6 +985,22 @@ GPTQ_API int gptq_create(gptq_ctx* ctx, int device, void* stream) {
     delete c;
     return GPTQ_ERR_HIP;
   }
+  {
+    // this device's copy of the no-allocation scratch array
+    std::lock_guard<std::mutex> lk(g_na_mu);
+    if (device < 64 && g_na_state[device] == 0) {
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) (void)hipGetLastError();
+      g_na_state[device] = (e == hipSuccess && ptr) ? 1 : 2;
+      g_na_ptr[device] = (uint8_t*)ptr;
+    }
+    c->na_base = (device < 64 && g_na_state[device] == 1) ? g_na_ptr[device] : nullptr;
+  }
+  // pinned host staging that gptq_quantize_noalloc uses (it allocates nothing itself)
+  (void)ensure_pinned(c, c->hblob, c->hblob_cap, NA_BLOB);
+  (void)ensure_pinned(c, c->hsmall, c->hsmall_cap, 4096);
+  c->err.clear();
   *ctx = c;
   return GPTQ_OK;
 }
@@ -1041,6 +1144,50 @@ GPTQ_API int gptq_quantize(gptq_ctx c, const float* W, int32_t out, int32_t n, c
   const Slot s = *(const Slot*)c->hsmall;
   obj[0] = s.obj[0];
   obj[1] = s.obj[1];
+  return GPTQ_OK;
+}
+
+GPTQ_API int gptq_quantize_noalloc(gptq_ctx c, const float* W, int32_t out, int32_t n, const float* U,
+                                   int32_t bits, int32_t group, int32_t block, double lam, uint8_t* codes,
+                                   float* scales, uint8_t* zeros, float* err, double* obj) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  c->err.clear();
+  int rc = check_quant_args(c, out, n, bits, group, block);
+  if (rc) return rc;
+  if (!obj) return set_err(c, GPTQ_ERR_INVALID_ARG, "obj is null");
+  obj[0] = obj[1] = 0.0;
+  if (out == 0 || n == 0) return GPTQ_OK;
+  if (!W || !U || !codes || !scales || !zeros) return set_err(c, GPTQ_ERR_INVALID_ARG, "null pointer");
+  if (out > NA_MAX_OUT || n > NA_MAX_N || (long long)out * n > NA_MAX_ELEMS)
+    return set_err(c, GPTQ_ERR_UNSUPPORTED,
+                   "layer %d x %d exceeds the no-allocation limits (out <= %d, n <= %d, out * n <= %lld)", out, n,
+                   NA_MAX_OUT, NA_MAX_N, NA_MAX_ELEMS);
+  if (!c->na_base) return set_err(c, GPTQ_ERR_HIP, "the no-allocation scratch array is unavailable on device %d", c->device);
+  if (c->hblob_cap < NA_BLOB || c->hsmall_cap < 2 * sizeof(Slot))
+    return set_err(c, GPTQ_ERR_NO_MEMORY, "the context's pinned staging was not allocated");
+  DeviceGuard g(c->device);
+  const NoAlloc na = noalloc_view(c->na_base);
+  // per-kernel timing would create event pairs: off for this call
+  struct TimingOff {
+    gptq_ctx c;
+    bool was;
+    ~TimingOff() { c->timing = was; }
+  } toff{c, c->timing};
+  c->timing = false;
+  Slot* hs = (Slot*)c->hsmall;  // [0]: the slot sent, [1]: the slot read back
+  if (c->blob_pending) {  // an earlier upload may still read the pinned staging
+    HIPCHK(c, hipEventSynchronize(c->blob_ev));
+    c->blob_pending = false;
+  }
+  hs[0] = Slot{};
+  hs[0].lam = lam;
+  HIPCHK(c, hipMemcpyAsync(na.slot, &hs[0], sizeof(Slot), hipMemcpyHostToDevice, c->stream));
+  QuantJob J{W, out, n, n, U, bits, group, block, codes, scales, zeros, err, &na.slot->lam, na.slot->obj, nullptr};
+  if ((rc = run_quantize(c, {J}, nullptr, &na))) return rc;
+  HIPCHK(c, hipMemcpyAsync(&hs[1], na.slot, sizeof(Slot), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  obj[0] = hs[1].obj[0];
+  obj[1] = hs[1].obj[1];
   return GPTQ_OK;
 }
 
