@@ -45,7 +45,9 @@ typedef enum {
   GPTQ_ERR_NONFINITE = 3,   /* non-finite entry in H */
   GPTQ_ERR_UNSUPPORTED = 4, /* valid but unsupported shape or alignment */
   GPTQ_ERR_HIP = 5,         /* HIP runtime error (text in gptq_last_error) */
-  GPTQ_ERR_NO_MEMORY = 6    /* workspace allocation failed */
+  GPTQ_ERR_NO_MEMORY = 6,   /* workspace allocation failed */
+  GPTQ_ERR_NOT_CONVERGED = 7 /* a subspace iteration stopped at its step cap; every
+                                output is written, from its last iterate */
 } gptq_status;
 
 typedef struct gptq_ctx_s* gptq_ctx;
@@ -125,12 +127,17 @@ int gptq_quantize(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const fl
  * columns absorb the error.  Outputs codes/scales/zeros as gptq_quantize (W^T
  * ~ Q + L R in the pages' convention, i.e. W ~ What + R^T L^T):
  *   L[n][r] fp32: an orthonormal basis of the top-r eigenspace of H (found by
- *                 subspace iteration in fp64; any basis gives the same Q and
- *                 the same product L R);
+ *                 subspace iteration in fp64 on min(128, n, max(2r, 64))
+ *                 columns with a Rayleigh-Ritz check every 4 steps, stopping
+ *                 when ||H L - L diag(theta)||_F <= 1e-11 ||theta||; any basis
+ *                 gives the same Q and the same product L R);
  *   R[r][out] fp32;
  *   obj[2] [host] = {J, J_lam}, J = ||X (W - What - R^T L^T)^T||^2.
  * X as gptq_hessian; 1 <= r <= min(128, n); requirements on bits/group/block as
- * gptq_quantize.  SYNC.  *info semantics as gptq_factor (may be NULL). */
+ * gptq_quantize.  SYNC.  *info semantics as gptq_factor (may be NULL).
+ * GPTQ_ERR_NOT_CONVERGED: the iteration reached its cap of 600 steps (the
+ * r-th and (r+1)-th eigenvalues too close for it); every output is written,
+ * from the last Ritz vectors. */
 int gptq_lora(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const uint16_t* X,
               int64_t tokens, int64_t ldx, int32_t r, int32_t bits, int32_t group,
               int32_t block, double lam_abs, double lam_rel, uint8_t* codes, float* scales,
@@ -168,10 +175,9 @@ int gptq_hessian64(gptq_ctx ctx, const uint16_t* X, int64_t tokens, int32_t n, i
  *
  * gptq_olrc: for the given codes, the rank-r correction C minimising J is
  * C = P P^T E with E = W - What and P the top-r eigenvectors of E H E^T
- * (found by subspace iteration in fp64, Cholesky-QR once per step and twice
- * on the last; where
- * the r-th and (r+1)-th eigenvalues are close, any near-optimal subspace may
- * come out).  Writes L[n][r] = E^T P and R[r][out] = P^T (fp32, device) and
+ * (found by the checked subspace iteration gptq_lora uses for L, in
+ * dimension out; GPTQ_ERR_NOT_CONVERGED, with every output written, when it
+ * reaches its cap).  Writes L[n][r] = E^T P and R[r][out] = P^T (fp32, device) and
  * J (host, the objective with that correction).  codes/scales/zeros as
  * gptq_quantize's outputs (read only); bits is checked only.
  *

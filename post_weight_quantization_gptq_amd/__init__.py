@@ -33,7 +33,9 @@ STATUS = {
     4: "GPTQ_ERR_UNSUPPORTED",
     5: "GPTQ_ERR_HIP",
     6: "GPTQ_ERR_NO_MEMORY",
+    7: "GPTQ_ERR_NOT_CONVERGED",
 }
+NOT_CONVERGED = 7
 
 
 class GPTQError(RuntimeError):
@@ -192,6 +194,14 @@ class Context:
                 msg = self.lib.gptq_strerror(rc).decode()
             raise GPTQError(rc, msg)
 
+    def _check_conv(self, rc) -> bool:
+        """_check, except that a subspace iteration stopped at its cap (every
+        output written) gives False instead of raising."""
+        if rc == NOT_CONVERGED:
+            return False
+        self._check(rc)
+        return True
+
     def _dev(self, t, dtype, name):
         torch = self.torch
         if t.device != self.device:
@@ -284,7 +294,8 @@ class Context:
 
     def lora(self, W, X, r: int, bits: int, group: int, block: int, lam_abs: float = 0.0,
              lam_rel: float = 1e-4):
-        """GPTQ-intrinsic LoRA.  Returns dict(codes, scales, zeros, L [n, r], R [r, out], J, J_lam)."""
+        """GPTQ-intrinsic LoRA.  Returns dict(codes, scales, zeros, L [n, r], R [r, out], J, J_lam, info,
+        converged); converged is False when the top-r subspace iteration stopped at its cap."""
         torch = self.torch
         self._dev(W, torch.float32, "W")
         X = self._xbits(X)
@@ -297,11 +308,12 @@ class Context:
                    R=torch.empty((r, o), dtype=torch.float32, device=self.device))
         obj = (ctypes.c_double * 2)()
         info = ctypes.c_int32(0)
-        self._check(self.lib.gptq_lora(self.handle, _ptr(W), o, n, _ptr(X), X.shape[0], X.stride(0), int(r),
-                                       int(bits), int(group), int(block), float(lam_abs), float(lam_rel),
-                                       _ptr(res["codes"]), _ptr(res["scales"]), _ptr(res["zeros"]),
-                                       _ptr(res["L"]), _ptr(res["R"]), obj, ctypes.byref(info)))
-        res["J"], res["J_lam"], res["info"] = obj[0], obj[1], info.value
+        conv = self._check_conv(self.lib.gptq_lora(self.handle, _ptr(W), o, n, _ptr(X), X.shape[0], X.stride(0),
+                                                   int(r), int(bits), int(group), int(block), float(lam_abs),
+                                                   float(lam_rel), _ptr(res["codes"]), _ptr(res["scales"]),
+                                                   _ptr(res["zeros"]), _ptr(res["L"]), _ptr(res["R"]), obj,
+                                                   ctypes.byref(info)))
+        res["J"], res["J_lam"], res["info"], res["converged"] = obj[0], obj[1], info.value, conv
         return res
 
     def lora_refine(self, W, X, r: int, bits: int, group: int, block: int, rounds: int = 1,
@@ -320,12 +332,11 @@ class Context:
                    R=torch.empty((r, o), dtype=torch.float32, device=self.device))
         tr = (ctypes.c_double * (2 * int(rounds) + 2))()
         info = ctypes.c_int32(0)
-        self._check(self.lib.gptq_lora_refine(self.handle, _ptr(W), o, n, _ptr(X), X.shape[0], X.stride(0), int(r),
-                                              int(bits), int(group), int(block), float(lam_abs), float(lam_rel),
-                                              int(rounds), _ptr(res["codes"]), _ptr(res["scales"]),
-                                              _ptr(res["zeros"]), _ptr(res["L"]), _ptr(res["R"]), tr,
-                                              ctypes.byref(info)))
-        res["trace"], res["info"] = list(tr), info.value
+        conv = self._check_conv(self.lib.gptq_lora_refine(
+            self.handle, _ptr(W), o, n, _ptr(X), X.shape[0], X.stride(0), int(r), int(bits), int(group), int(block),
+            float(lam_abs), float(lam_rel), int(rounds), _ptr(res["codes"]), _ptr(res["scales"]), _ptr(res["zeros"]),
+            _ptr(res["L"]), _ptr(res["R"]), tr, ctypes.byref(info)))
+        res["trace"], res["info"], res["converged"] = list(tr), info.value, conv
         return res
 
     def hessian64(self, X, n: int | None = None, H=None):
@@ -340,7 +351,7 @@ class Context:
         return H
 
     def olrc(self, W, H, r: int, bits: int, group: int, codes, scales, zeros):
-        """Optimal rank-r compensation for fixed codes.  Returns dict(L [n, r], R [r, out], J)."""
+        """Optimal rank-r compensation for fixed codes.  Returns dict(L [n, r], R [r, out], J, converged)."""
         torch = self.torch
         self._dev(W, torch.float32, "W")
         self._dev(H, torch.float64, "H")
@@ -351,10 +362,10 @@ class Context:
         res = dict(L=torch.empty((n, r), dtype=torch.float32, device=self.device),
                    R=torch.empty((r, o), dtype=torch.float32, device=self.device))
         J = ctypes.c_double(0.0)
-        self._check(self.lib.gptq_olrc(self.handle, _ptr(W), o, n, _ptr(H), int(r), int(bits), int(group),
-                                       _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(res["L"]), _ptr(res["R"]),
-                                       ctypes.byref(J)))
-        res["J"] = J.value
+        conv = self._check_conv(self.lib.gptq_olrc(self.handle, _ptr(W), o, n, _ptr(H), int(r), int(bits),
+                                                   int(group), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(res["L"]),
+                                                   _ptr(res["R"]), ctypes.byref(J)))
+        res["J"], res["converged"] = J.value, conv
         return res
 
     def bid_up(self, W, H, L, R, bits: int, group: int, block: int, codes, scales, zeros):

@@ -44,6 +44,8 @@ struct gptq_ctx_s {
   bool blob_pending = false;
   // this device's copy of the no-allocation scratch array (device address)
   uint8_t* na_base = nullptr;
+  // set when a subspace iteration of the current call stopped at its cap
+  bool not_converged = false;
   // second stream (default priority) for the factor's trailing updates that
   // run beside its serial chain; fork / join events order it against stream
   hipStream_t side = nullptr;
@@ -957,6 +959,7 @@ GPTQ_API const char* gptq_strerror(int status) {
     case GPTQ_ERR_UNSUPPORTED: return "unsupported shape or alignment";
     case GPTQ_ERR_HIP: return "HIP runtime error";
     case GPTQ_ERR_NO_MEMORY: return "out of device memory";
+    case GPTQ_ERR_NOT_CONVERGED: return "subspace iteration stopped at its cap; outputs are from the last iterate";
     default: return "unknown status";
   }
 }
@@ -1311,6 +1314,15 @@ LoraHooks lora_hooks(gptq_ctx c) {
   hooks.gemm_nt = [c](const double* A, const double* B, double* C, int M, int N, int K, int ld) {
     return run_gemm_nt(c, A, B, C, M, N, K, ld);
   };
+  hooks.read = [c](const void* dev, void* host, size_t bytes) -> int {
+    int rc2 = ensure_small(c, bytes);
+    if (rc2) return rc2;
+    HIPCHK(c, hipMemcpyAsync(c->hsmall, dev, bytes, hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    memcpy(host, c->hsmall, bytes);
+    return GPTQ_OK;
+  };
+  hooks.not_converged = [c]() { c->not_converged = true; };
   return hooks;
 }
 
@@ -1336,6 +1348,7 @@ int lora_impl(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t
   LoraIO io{W, out, n, X, tokens, ldx, r, bits, group, block, lam_abs, lam_rel, codes, scales, zeros, L, R};
   io.rounds = rounds;
   const LoraHooks hooks = lora_hooks(c);
+  c->not_converged = false;
   rc = run_lora(c->stream, io, hooks);
   if (rc) return rc;
   const size_t bytes = sizeof(Slot) + (rounds > 0 ? (size_t)nres * sizeof(double) : 0);
@@ -1353,6 +1366,8 @@ int lora_impl(gptq_ctx c, const float* W, int32_t out, int32_t n, const uint16_t
     res[0] = s.obj[0];
     res[1] = s.obj[1];
   }
+  if (c->not_converged)
+    return set_err(c, GPTQ_ERR_NOT_CONVERGED, "a top-%d subspace iteration stopped at its cap", (int)r);
   return GPTQ_OK;
 }
 
@@ -1374,12 +1389,15 @@ int refine_step(gptq_ctx c, bool bid, const float* W, int32_t out, int32_t n, co
   double* dJ = (double*)c->slots.p;
   RefineIO io{W, out, n, H, r, bits, group, block, codes, scales, zeros, L, R};
   const LoraHooks hooks = lora_hooks(c);
+  c->not_converged = false;
   rc = bid ? run_bid_up(c->stream, io, hooks, dJ) : run_olrc(c->stream, io, hooks, dJ);
   if (rc) return rc;
   if ((rc = ensure_small(c, sizeof(double)))) return rc;
   HIPCHK(c, hipMemcpyAsync(c->hsmall, dJ, sizeof(double), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
   *J = *(const double*)c->hsmall;
+  if (c->not_converged)
+    return set_err(c, GPTQ_ERR_NOT_CONVERGED, "the top-%d subspace iteration stopped at its cap", (int)r);
   return GPTQ_OK;
 }
 

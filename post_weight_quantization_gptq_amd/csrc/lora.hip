@@ -11,10 +11,11 @@
 // here, in fp64 (the damped matrix stays positive definite, and fp64 keeps
 // the condition number of ~1e6 at lam = 1e-4 mean(diag H) harmless).
 //
-// V_r comes from subspace iteration in fp64 (V <- orth(H V) by Cholesky-QR;
-// an intermediate basis only has to stay well conditioned, so one pass per
-// step, and a second pass on the last iterate makes it orthonormal to
-// rounding), started from a fixed hash-generated block.
+// V_r comes from subspace iteration in fp64 on m >= r columns (Q <- orth(H Q)
+// by one Cholesky-QR pass per step, from a fixed hash-generated block), with
+// a Rayleigh-Ritz step every few steps that rotates Q onto the Ritz vectors
+// and stops on a residual test (see top_subspace); a last Cholesky-QR pass
+// on the r Ritz vectors makes V_r orthonormal to rounding.
 // Only span(V_r) matters: Q and the product L R do not depend on the basis.
 #include <algorithm>
 #include <utility>
@@ -28,7 +29,12 @@
 
 namespace {
 
-constexpr int kIters = 12;
+// Subspace iterations: a Rayleigh-Ritz check every kCheck steps, at most
+// kMaxIters steps, stop when the top-r residual is below kTol ||theta_r||
+// (about a hundred times the rounding floor of the fp64 products at n = 4096).
+constexpr int kCheck = 4;
+constexpr int kMaxIters = 600;
+constexpr double kTol = 1e-11;
 
 // C(i,j) = alpha * sum_k A(i,k) B(k,j) over the split's k range, written to
 // P + z*M*N (split-K partial).  A(i,k) = A[i*sai + k*sak], B(k,j) = B[k*sbk + j*sbj].
@@ -377,6 +383,167 @@ __global__ __launch_bounds__(256) void k_apply(const double* __restrict__ Z, int
   });
 }
 
+// --------------------------------------------- Rayleigh-Ritz pieces -----
+// The subspace iterations run on m >= r columns; every few steps the basis Q
+// (orthonormal, dim x m) is rotated onto the Ritz vectors of the operator A
+// in span(Q): with M = Q^T A Q = Y diag(theta) Y^T (theta descending), Q <- Q Y
+// and Z = A Q <- Z Y.  The first r columns then hold the current estimate of
+// the top-r eigenvectors, and the iteration stops once their residual
+// ||A Q_r - Q_r diag(theta_r)||_F falls below a tolerance relative to
+// ||theta_r||: by the sin-theta theorem the distance of span(Q_r) from the
+// top-r eigenspace is at most that residual over the gap theta_r - lambda_{r+1}.
+// The extra m - r columns make the subspace converge at the rate
+// lambda_{m+1} / lambda_r instead of lambda_{r+1} / lambda_r.
+
+constexpr int kRitzMax = 128;  // widest subspace
+constexpr int kRitzPitch = kRitzMax + 1;
+
+// Eigenpairs of a symmetric positive semidefinite m x m matrix (m <= 128) by
+// one-sided (Hestenes) Jacobi on B = M: rotations of column pairs until all
+// columns are mutually orthogonal, B J = U diag(sigma); for M = M^T >= 0 the
+// singular values are the eigenvalues and U holds the eigenvectors, so no
+// rotation needs to be accumulated.  Sweeps visit all pairs in round-robin
+// rounds of m/2 disjoint pairs (4 lanes per pair, columns in LDS); a pair is
+// rotated when |b_p . b_q| > 1e-15 ||b_p|| ||b_q||; sweeps stop when none is
+// (at most 40).  Writes Y[i][k] (m x m row-major, column k the eigenvector
+// of the k-th largest eigenvalue) and theta[k].  One workgroup of 256.
+__global__ __launch_bounds__(256) void k_ritz(const double* __restrict__ M, int m, double* __restrict__ Y,
+                                              double* __restrict__ theta) {
+  __shared__ double Bc[kRitzMax][kRitzPitch];  // Bc[c][i] = B[i][c]
+  __shared__ double sig[kRitzMax];
+  __shared__ int rotated;
+  const int tid = threadIdx.x;
+  const int mp = (m + 1) & ~1;  // even number of columns (a zero column pads)
+  for (int e = tid; e < mp * kRitzMax; e += 256) {
+    const int c = e / kRitzMax, i = e % kRitzMax;
+    Bc[c][i] = (c < m && i < m) ? 0.5 * (M[(size_t)i * m + c] + M[(size_t)c * m + i]) : 0.0;
+  }
+  if (tid == 0) rotated = 0;
+  __syncthreads();
+  const int j = tid >> 2, sub = tid & 3;
+  const bool act = j < mp / 2;
+  constexpr int RT = kRitzMax / 4;  // rows per lane
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    for (int k = 0; k < mp - 1; ++k) {
+      if (act) {
+        int p = j == 0 ? 0 : 1 + ((j - 1 + k) % (mp - 1));
+        int q = 1 + ((mp - 2 - j + k) % (mp - 1));
+        if (p > q) {
+          const int t = p;
+          p = q;
+          q = t;
+        }
+        double bp[RT], bq[RT];
+        double al = 0.0, be = 0.0, ga = 0.0;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int i = sub + 4 * t;
+          bp[t] = i < m ? Bc[p][i] : 0.0;
+          bq[t] = i < m ? Bc[q][i] : 0.0;
+          al = fma(bp[t], bp[t], al);
+          be = fma(bq[t], bq[t], be);
+          ga = fma(bp[t], bq[t], ga);
+        }
+#pragma unroll
+        for (int o = 1; o < 4; o <<= 1) {
+          al += __shfl_xor(al, o);
+          be += __shfl_xor(be, o);
+          ga += __shfl_xor(ga, o);
+        }
+        if (fabs(ga) > 1e-15 * sqrt(al) * sqrt(be)) {
+          const double zeta = (be - al) / (2.0 * ga);
+          const double t = fabs(zeta) > 1e100 ? 0.5 / zeta
+                                              : (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+          const double cs = 1.0 / sqrt(1.0 + t * t), sn = cs * t;
+#pragma unroll
+          for (int u = 0; u < RT; ++u) {
+            const int i = sub + 4 * u;
+            if (i < m) {
+              Bc[p][i] = cs * bp[u] - sn * bq[u];
+              Bc[q][i] = sn * bp[u] + cs * bq[u];
+            }
+          }
+          if (sub == 0) rotated = 1;
+        }
+      }
+      __syncthreads();
+    }
+    const bool again = rotated != 0;
+    __syncthreads();
+    if (!again) break;
+    if (tid == 0) rotated = 0;
+    __syncthreads();
+  }
+  if (tid < m) {
+    double s = 0.0;
+    for (int i = 0; i < m; ++i) s = fma(Bc[tid][i], Bc[tid][i], s);
+    sig[tid] = sqrt(s);
+  }
+  __syncthreads();
+  if (tid < m) {
+    const double sc = sig[tid];
+    int rank = 0;
+    for (int d = 0; d < m; ++d) rank += (sig[d] > sc || (sig[d] == sc && d < tid)) ? 1 : 0;
+    theta[rank] = sc;
+    const double inv = sc > 0.0 ? 1.0 / sc : 0.0;
+    for (int i = 0; i < m; ++i) Y[(size_t)i * m + rank] = Bc[tid][i] * inv;
+  }
+}
+
+// part[b] = this block's share of sum over i < dim, c < r of
+// (Z[i][c] - theta[c] Q[i][c])^2 (Q, Z of pitch m), fixed order per block
+__global__ __launch_bounds__(256) void k_ritz_resid(const double* __restrict__ Q, const double* __restrict__ Z,
+                                                    const double* __restrict__ theta, int dim, int m, int r,
+                                                    double* __restrict__ part) {
+  __shared__ double red[256];
+  const long long cnt = (long long)dim * r, stride = (long long)gridDim.x * 256;
+  double acc = 0.0;
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < cnt; e += stride) {
+    const long long i = e / r;
+    const int c = (int)(e % r);
+    const double v = Z[i * m + c] - theta[c] * Q[i * m + c];
+    acc = fma(v, v, acc);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// conv[0] = 1 if the residual meets the tolerance (else 0), conv[1] = the
+// squared residual, conv[2] = ||theta_r||^2
+__global__ __launch_bounds__(256) void k_ritz_conv(const double* __restrict__ part, int np,
+                                                   const double* __restrict__ theta, int r, double tol,
+                                                   double* __restrict__ conv) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < np; i += 256) acc += part[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double t2 = 0.0;
+    for (int c = 0; c < r; ++c) t2 = fma(theta[c], theta[c], t2);
+    conv[0] = red[0] <= tol * tol * t2 ? 1.0 : 0.0;
+    conv[1] = red[0];
+    conv[2] = t2;
+  }
+}
+
+// V[i][c] = Q[i][c] for c < r (Q of pitch m, V of pitch r)
+__global__ void k_cols(const double* __restrict__ Q, int dim, int m, int r, double* __restrict__ V) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (long long)dim * r) return;
+  const long long i = e / r;
+  V[e] = Q[i * m + (int)(e % r)];
+}
+
 // lam = lam_abs + lam_rel * mean(diag H); clears the slot's flags and the
 // Gram kernels' arrival counter.
 __global__ __launch_bounds__(256) void k_lora_lambda(const double* __restrict__ H, int n, double lam_abs,
@@ -469,6 +636,81 @@ int orth(hipStream_t st, const LoraHooks& hk, const double* Zin, double* Vout, i
   return 0;
 }
 
+// Width of the iterated subspace for the top-r eigenvectors in dimension dim.
+inline int sub_width(int dim, int r) { return std::max(r, std::min({kRitzMax, dim, std::max(2 * r, 64)})); }
+
+// Buffers of one top-subspace computation (dim x m unless noted).
+struct SubBufs {
+  double *Q, *Z, *Qn, *Zn;
+  double *M, *Y, *theta;  // m x m, m x m, m
+  double *parts, *conv;   // kParts, 4
+  double *S;              // split-K partials: ksplit_for(dim) * m * m at least
+  double *Gp, *Li;
+  unsigned* cnt;
+};
+
+constexpr int kResidParts = 256;
+
+// Orthonormal V[dim][r] spanning the top-r eigenvectors of the symmetric
+// positive semidefinite operator op (op(Q, Z): Z = A Q for dim x m blocks),
+// by subspace iteration with Cholesky-QR on m columns from a fixed start, a
+// Rayleigh-Ritz check every kCheck steps (see k_ritz), and a final
+// Cholesky-QR pass on the r Ritz vectors.  *converged = whether the residual
+// test passed before kMaxIters; V holds the last Ritz vectors either way.
+// Vtmp: dim x r scratch.  Each check reads one flag back (a host wait).
+int top_subspace(hipStream_t st, const LoraHooks& hk, const std::function<int(const double*, double*)>& op, int dim,
+                 int m, int r, const SubBufs& b, double* V, double* Vtmp, bool* converged) {
+  int rc;
+  double *Q = b.Q, *Z = b.Z, *Qn = b.Qn, *Zn = b.Zn;
+  LLAUNCH("k_start_block", k_start_block, dim3(cdivl((long long)dim * m, 256)), dim3(256), 0, st, Q, dim, m);
+  *converged = false;
+  for (int it = 0; it < kMaxIters; ++it) {
+    if ((rc = op(Q, Z))) return rc;
+    const bool last = it == kMaxIters - 1;
+    if (it >= 1 && (it % kCheck == kCheck - 1 || last)) {  // Q is orthonormal from step 1 on
+      DGemm g{Q, 1, m, Z, m, 1, nullptr, m, m, dim, ksplit_for(dim)};  // M = Q^T Z
+      if ((rc = dgemm(st, hk, g, b.M, b.S))) return rc;
+      LLAUNCH("k_ritz", k_ritz, dim3(1), dim3(256), 0, st, (const double*)b.M, m, b.Y, b.theta);
+      DGemm gq{Q, m, 1, b.Y, m, 1, nullptr, dim, m, m, 1};  // Qn = Q Y
+      if ((rc = dgemm(st, hk, gq, Qn, b.S))) return rc;
+      DGemm gz{Z, m, 1, b.Y, m, 1, nullptr, dim, m, m, 1};  // Zn = Z Y
+      if ((rc = dgemm(st, hk, gz, Zn, b.S))) return rc;
+      LLAUNCH("k_ritz_resid", k_ritz_resid, dim3(kResidParts), dim3(256), 0, st, (const double*)Qn,
+              (const double*)Zn, (const double*)b.theta, dim, m, r, b.parts);
+      LLAUNCH("k_ritz_conv", k_ritz_conv, dim3(1), dim3(256), 0, st, (const double*)b.parts, kResidParts,
+              (const double*)b.theta, r, kTol, b.conv);
+      double hc[3];
+      if ((rc = hk.read(b.conv, hc, sizeof(hc)))) return rc;
+      std::swap(Q, Qn);
+      std::swap(Z, Zn);
+      if (hc[0] != 0.0) {
+        *converged = true;
+        break;
+      }
+      if (last) break;
+    }
+    if ((rc = orth(st, hk, Z, Q, dim, m, b.Gp, b.Li, b.cnt))) return rc;
+  }
+  LLAUNCH("k_cols", k_cols, dim3(cdivl((long long)dim * r, 256)), dim3(256), 0, st, (const double*)Q, dim, m, r,
+          Vtmp);
+  return orth(st, hk, Vtmp, V, dim, r, b.Gp, b.Li, b.cnt);
+}
+
+// Lays a SubBufs out with take(bytes) -> pointer.
+template <class Take>
+void sub_layout(int dim, int m, Take&& take, SubBufs* b) {
+  const size_t dm = (size_t)dim * m * 8;
+  b->Q = (double*)take(dm);
+  b->Z = (double*)take(dm);
+  b->Qn = (double*)take(dm);
+  b->Zn = (double*)take(dm);
+  b->M = (double*)take((size_t)m * m * 8);
+  b->Y = (double*)take((size_t)m * m * 8);
+  b->theta = (double*)take((size_t)m * 8);
+  b->parts = (double*)take((size_t)kResidParts * 8);
+  b->conv = (double*)take(4 * 8);
+}
+
 // ----------------------------------------------- refinement: OLrC, Bid-Up -----
 // (GPTQ-intrinsic LoRA technical summary, section 4: OLrC re-fits L, R for a
 // fixed Q, Bid-Up moves Q on its fixed grid for fixed L, R; they alternate
@@ -477,9 +719,9 @@ int orth(hipStream_t st, const LoraHooks& hk, const double* Zin, double* Vout, i
 // OLrC: with E = W - What, the rank-r correction C minimising
 // tr((E - C) H (E - C)^T) is C = P P^T E, P the top-r eigenvectors of
 // E H E^T (Eckart-Young on E F for any H = F F^T), so no square root or
-// inverse of H is needed.  P comes from subspace iteration in fp64,
-// P <- orth(EH (E^T P)) with EH = E H formed once (one Cholesky-QR pass per
-// step, a second on the last iterate); then L = E^T P, R = P^T (C = R^T L^T).  Its objective is
+// inverse of H is needed.  P comes from the same checked subspace iteration
+// as V_r, on the operator Q -> EH (E^T Q) with EH = E H formed once; then
+// L = E^T P, R = P^T (C = R^T L^T).  Its objective is
 // J = sum(g * E) with g = (E - C) H = EH - P (P^T EH), which is also the
 // gradient Bid-Up starts from.
 // Bid-Up: one pass of the column sweep in its Bid-Up mode, on g (fp32) with
@@ -568,9 +810,10 @@ __global__ void k_ref_init(unsigned* __restrict__ cnt, double* __restrict__ dev)
 constexpr int kParts = 512;  // partial sums of the objective dot product
 
 struct RefBufs {
-  double *E, *EH, *Y, *P, *Pz, *T, *X, *S, *Gp, *Li, *parts, *Ld, *Rd, *dev;
+  double *E, *EH, *Y, *P, *Pt, *T, *X, *S, *Gp, *Li, *parts, *Ld, *Rd, *dev;
   unsigned* cnt;
   float *g32, *H32;
+  SubBufs sb;  // the top-r subspace of E H E^T (dimension out)
 };
 
 // Lay the refinement buffers out from offset off of base (base may be null
@@ -583,16 +826,17 @@ size_t ref_layout(int out, int n, int r, uint8_t* base, size_t off, RefBufs* b) 
   };
   const size_t on = (size_t)out * n;
   const int ks = std::max(ksplit_for(n), ksplit_for(out));
+  const int m = sub_width(out, r);
   b->E = (double*)take(on * 8);
   b->EH = (double*)take(on * 8);
   b->Y = (double*)take(on * 8);
   b->P = (double*)take((size_t)out * r * 8);
-  b->Pz = (double*)take((size_t)out * r * 8);
-  b->T = (double*)take((size_t)n * r * 8);
+  b->Pt = (double*)take((size_t)out * r * 8);
+  b->T = (double*)take((size_t)n * m * 8);
   b->X = (double*)take((size_t)r * n * 8);
-  b->S = (double*)take((size_t)ks * std::max(out, n) * r * 8);
+  b->S = (double*)take((size_t)ks * std::max(out, n) * m * 8);
   b->Gp = (double*)take((size_t)kGramParts * 3 * 64 * 64 * 8);
-  b->Li = (double*)take((size_t)r * r * 8);
+  b->Li = (double*)take((size_t)m * m * 8);
   b->parts = (double*)take((size_t)kParts * 8);
   b->Ld = (double*)take((size_t)n * r * 8);
   b->Rd = (double*)take((size_t)r * out * 8);
@@ -600,6 +844,11 @@ size_t ref_layout(int out, int n, int r, uint8_t* base, size_t off, RefBufs* b) 
   b->cnt = (unsigned*)take(sizeof(unsigned));
   b->g32 = (float*)take(on * 4);
   b->H32 = (float*)take((size_t)n * n * 4);
+  sub_layout(out, m, take, &b->sb);
+  b->sb.S = b->S;
+  b->sb.Gp = b->Gp;
+  b->sb.Li = b->Li;
+  b->sb.cnt = b->cnt;
   return off;
 }
 
@@ -630,17 +879,19 @@ int olrc(hipStream_t st, const RefineIO& io, const LoraHooks& hk, const RefBufs&
   LLAUNCH("k_resid", k_resid, dim3(cdivl(on, 256)), dim3(256), 0, st, io.W, io.codes, io.scales, io.zeros, out, n,
           io.group, (const double*)nullptr, b.E);
   if ((rc = e_times_h(st, hk, b.E, io.H64, b.EH, b.S, out, n))) return rc;  // EH = E H
-  double *P = b.P, *Pz = b.Pz;
-  LLAUNCH("k_start_block", k_start_block, dim3(cdivl((long long)out * r, 256)), dim3(256), 0, st, P, out, r);
-  for (int it = 0; it < kIters; ++it) {
-    DGemm t{b.E, 1, n, P, r, 1, nullptr, n, r, out, ksplit_for(out)};  // T = E^T P
-    if ((rc = dgemm(st, hk, t, b.T, b.S))) return rc;
-    DGemm z{b.EH, n, 1, b.T, r, 1, nullptr, out, r, n, ksplit_for(n)};  // Z = EH T
-    if ((rc = dgemm(st, hk, z, Pz, b.S))) return rc;
-    if ((rc = orth(st, hk, Pz, P, out, r, b.Gp, b.Li, b.cnt))) return rc;
-  }
-  if ((rc = orth(st, hk, P, Pz, out, r, b.Gp, b.Li, b.cnt))) return rc;  // second pass on the last iterate
-  std::swap(P, Pz);
+  const int m = sub_width(out, r);
+  // A = E H E^T applied as EH (E^T Q)
+  auto op = [&](const double* Q, double* Z) -> int {
+    int rc2;
+    DGemm t{b.E, 1, n, Q, m, 1, nullptr, n, m, out, ksplit_for(out)};  // T = E^T Q
+    if ((rc2 = dgemm(st, hk, t, b.T, b.S))) return rc2;
+    DGemm z{b.EH, n, 1, b.T, m, 1, nullptr, out, m, n, ksplit_for(n)};  // Z = EH T
+    return dgemm(st, hk, z, Z, b.S);
+  };
+  double* P = b.P;
+  bool conv = false;
+  if ((rc = top_subspace(st, hk, op, out, m, r, b.sb, P, b.Pt, &conv))) return rc;
+  if (!conv) hk.not_converged();
   {
     DGemm t{b.E, 1, n, P, r, 1, nullptr, n, r, out, ksplit_for(out)};  // L = E^T P
     if ((rc = dgemm(st, hk, t, b.T, b.S))) return rc;
@@ -732,12 +983,16 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
     return o;
   };
   const int ks_n = ksplit_for(n);  // split-K for K = n products
+  const int m = sub_width(n, r);    // columns of the subspace iteration
   const size_t oH64 = take((size_t)n * n * 8), oV = take((size_t)n * r * 8),
-               oZ = take((size_t)n * r * 8), oLi = take((size_t)r * r * 8),
+               oZ = take((size_t)n * r * 8), oLi = take((size_t)m * m * 8),
                oM = take((size_t)r * r * 8), oHV = take((size_t)n * r * 8),
-               oS = take((size_t)std::max(ks_n * n * r, ks_n * r * r) * 8),
+               oS = take((size_t)ks_n * n * m * 8),
                oGp = take((size_t)kGramParts * 3 * 64 * 64 * 8), oCnt = take(sizeof(unsigned)),
                oA = take((size_t)nt * nt * 8), oU = take((size_t)nt * nt * 4), oW = take((size_t)out * nt * 4);
+  SubBufs sb;
+  std::vector<size_t> sub_off;
+  sub_layout(n, m, [&](size_t bytes) { sub_off.push_back(take(bytes)); return (void*)nullptr; }, &sb);
   RefBufs rb;
   const size_t oRef = off;
   if (io.rounds > 0) off = ref_layout(out, n, r, nullptr, off, &rb);
@@ -754,6 +1009,14 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
   unsigned* cnt = (unsigned*)(base + oCnt);
   float* U = (float*)(base + oU);
   float* Ww = (float*)(base + oW);
+  {
+    size_t k = 0;
+    sub_layout(n, m, [&](size_t) { return (void*)(base + sub_off[k++]); }, &sb);
+    sb.S = S;
+    sb.Gp = Gp;
+    sb.Li = Li;
+    sb.cnt = cnt;
+  }
 
   // H accurate to float64 rounding: the Schur complement below cancels the
   // top-r eigen-directions of H against a damping far below their size
@@ -761,14 +1024,15 @@ int run_lora(hipStream_t st, const LoraIO& io, const LoraHooks& hk) {
   if (rc) return rc;
   LLAUNCH("k_lora_lambda", k_lora_lambda, dim3(1), dim3(256), 0, st, (const double*)H64, n, io.lam_abs, io.lam_rel,
           slot, cnt);
-  LLAUNCH("k_start_block", k_start_block, dim3(cdivl((long long)n * r, 256)), dim3(256), 0, st, V, n, r);
-  for (int it = 0; it < kIters; ++it) {
-    DGemm g{H64, n, 1, V, r, 1, nullptr, n, r, n, ks_n};  // Z = H V
-    if ((rc = dgemm(st, hk, g, Z, S))) return rc;
-    if ((rc = orth(st, hk, Z, V, n, r, Gp, Li, cnt))) return rc;
+  {
+    auto op = [&](const double* Q, double* Zq) -> int {
+      DGemm g{H64, n, 1, Q, m, 1, nullptr, n, m, n, ks_n};  // Zq = H Q
+      return dgemm(st, hk, g, Zq, S);
+    };
+    bool conv = false;
+    if ((rc = top_subspace(st, hk, op, n, m, r, sb, V, Z, &conv))) return rc;
+    if (!conv) hk.not_converged();
   }
-  if ((rc = orth(st, hk, V, Z, n, r, Gp, Li, cnt))) return rc;  // second pass on the last iterate
-  std::swap(V, Z);
   {
     DGemm g{H64, n, 1, V, r, 1, nullptr, n, r, n, ks_n};  // HV = H V
     if ((rc = dgemm(st, hk, g, HV, S))) return rc;

@@ -75,6 +75,10 @@ struct LoraHooks {
   // C[M][N] = A[M][K] B[N][K]^T in fp64, all of pitch ld, on the factor's
   // fp64 MFMA ring (needs K % 16 == 0, even ld and 16-byte aligned bases)
   std::function<int(const double*, const double*, double*, int, int, int, int)> gemm_nt;
+  // copy bytes from device to host after the context's stream has drained
+  std::function<int(const void*, void*, size_t)> read;
+  // note that a subspace iteration stopped at its cap (reported by the call)
+  std::function<void()> not_converged;
 };
 
 // With io.rounds > 0 the slots hold, after the Slot, the objective trace

@@ -223,7 +223,16 @@ LORA_SPECS = [synth.SMALL["lora"][0],
               # ragged last row block (400 = 6 * 64 + 16)
               synth.LayerSpec("lora96", 160, 400, 8192, 3, 0, 128, 1e-4, kind="lowrank", rank=96, seed=5),
               # rank at the limit, two full 64-blocks
-              synth.LayerSpec("lora128", 96, 640, 8192, 3, 0, 128, 1e-4, kind="lowrank", rank=128, seed=6)]
+              synth.LayerSpec("lora128", 96, 640, 8192, 3, 0, 128, 1e-4, kind="lowrank", rank=128, seed=6),
+              # power-law spectra (eigenvalue ratio lambda_r / lambda_{r+1} of a few percent or
+              # less): the top-r subspace is still unique, but a plain r-column iteration
+              # would need thousands of steps to find it
+              synth.LayerSpec("pow16", 160, 384, 8192, 3, 0, 128, 1e-4, decay=0.5, rank=16, seed=7),
+              synth.LayerSpec("pow48", 120, 256, 6000, 4, 64, 64, 1e-4, decay=0.5, rank=48, seed=8),
+              # damping a hundred times below the pages' smallest (the augmented Hessian
+              # is singular without it): the Cholesky route against the oracle's eig + QR
+              synth.LayerSpec("lam1e-6", 160, 384, 8192, 3, 0, 128, 1e-6, kind="lowrank", rank=16, seed=4),
+              synth.LayerSpec("pow16-lam1e-6", 160, 384, 8192, 3, 0, 128, 1e-6, decay=0.5, rank=16, seed=7)]
 
 
 @pytest.mark.parametrize("spec", LORA_SPECS, ids=lambda s: s.name)
@@ -245,8 +254,10 @@ def test_lora_matches_oracle(ctx, spec):
     # L spans the top-r eigenspace: same projector as the oracle's
     P_g = L @ L.T
     P_r = ref["L"] @ ref["L"].T
-    print(dict(agree=agree, forced=rep["forced_codes"], J=res["J"], J_ref=ref["J"],
-               proj=float(np.abs(P_g - P_r).max())))
+    ev = np.sort(np.linalg.eigvalsh(Hr))[::-1]
+    print(dict(agree=agree, forced=rep["forced_codes"], J=res["J"], J_ref=ref["J"], converged=res["converged"],
+               gap=float(ev[spec.rank - 1] / ev[spec.rank]), proj=float(np.abs(P_g - P_r).max())))
+    assert res["converged"]
     assert np.abs(L.T @ L - np.eye(spec.rank)).max() < 1e-5
     assert np.abs(P_g - P_r).max() < 1e-5
     assert agree >= 0.995
@@ -256,6 +267,30 @@ def test_lora_matches_oracle(ctx, spec):
     assert np.linalg.norm(LR_g - LR_r) <= 1e-3 * np.linalg.norm(LR_r)
     assert abs(res["J"] - ref["J"]) <= 5e-3 * ref["J"]
     # the intrinsic correction lowers the objective against plain GPTQ (expected)
+    Hl, _ = o.damp(Hr, lam_rel=spec.lam_rel)
+    g = o.gptq_sweep(Wn, o.factor_u(Hl), spec.bits, spec.group, spec.block)
+    assert res["J"] < o.objective(Wn, g["What"], Hr)
+
+
+def test_lora_reports_an_iteration_that_stopped_at_its_cap(ctx):
+    # r = 128 on a power-law spectrum: the subspace cannot be wider than r, so it
+    # converges at lambda_129 / lambda_128 per step and stops at its cap; every
+    # output is still written from the last Ritz vectors
+    spec = synth.LayerSpec("pow128", 96, 384, 4096, 3, 0, 128, 1e-4, decay=0.5, rank=128, seed=9)
+    lay = synth.layer(spec)
+    res = ctx.lora(lay["W"].cuda(), lay["X"].cuda(), spec.rank, spec.bits, spec.group, spec.block,
+                   lam_rel=spec.lam_rel)
+    assert not res["converged"]
+    L = np32(res["L"]).astype(np.float64)
+    assert np.all(np.isfinite(L)) and np.all(np.isfinite(np32(res["R"])))
+    assert np.abs(L.T @ L - np.eye(spec.rank)).max() < 1e-5
+    Hr = o.hessian(_bits(lay["X"]))
+    ev = np.sort(np.linalg.eigvalsh(Hr))[::-1]
+    # a near-top subspace: its Rayleigh quotient sum is within 1e-3 of the optimum
+    ritz = float(np.trace(L.T @ Hr @ L))
+    print(dict(J=res["J"], ritz=ritz, opt=float(ev[:spec.rank].sum())), flush=True)
+    assert ritz >= (1 - 1e-3) * ev[:spec.rank].sum()
+    Wn = lay["W"].numpy().astype(np.float64)
     Hl, _ = o.damp(Hr, lam_rel=spec.lam_rel)
     g = o.gptq_sweep(Wn, o.factor_u(Hl), spec.bits, spec.group, spec.block)
     assert res["J"] < o.objective(Wn, g["What"], Hr)

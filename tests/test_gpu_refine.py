@@ -78,10 +78,10 @@ def test_olrc_matches_oracle_with_a_spectral_gap(ctx):
 
 
 @pytest.mark.parametrize("spec,r", [(SPEC_LR, 16), (SPEC_FULL, 8)], ids=["lr-gptq", "flat"])
-def test_olrc_without_a_gap_is_near_optimal(ctx, spec, r):
-    # from plain GPTQ codes the error spectrum is flat: the subspace is not
-    # unique, the objective is; the GPU's must sit between the optimum and
-    # the uncorrected objective, within 2% of the gain of its optimum
+def test_olrc_with_a_narrow_gap_is_optimal(ctx, spec, r):
+    # from plain GPTQ codes the error spectrum is flat (eigenvalue ratios of a
+    # few percent): the objective the GPU's correction reaches must be the
+    # optimum, and where the r-th gap is a percent or more, its subspace too
     lay, H, W = _layer(spec)
     g = _gptq_start(ctx, lay, spec)
     H64 = ctx.hessian64(lay["X"].cuda())
@@ -93,9 +93,17 @@ def test_olrc_without_a_gap_is_near_optimal(ctx, spec, r):
     R = np32(res["R"]).astype(np.float64)
     D = W - What - R.T @ L.T
     J_eval = float(np.sum((D @ H) * D))
-    print(dict(J=res["J"], J_eval=J_eval, J_opt=ref["J"], J0=J0, gap=ref["eig"][r - 1] / ref["eig"][r]), flush=True)
+    gap = ref["eig"][r - 1] / ref["eig"][r]
+    proj = float(np.abs(R.T @ R - ref["R_out"] @ ref["R_out"].T).max())
+    print(dict(J=res["J"], J_eval=J_eval, J_opt=ref["J"], J0=J0, gap=gap, proj=proj, converged=res["converged"]),
+          flush=True)
     assert abs(res["J"] - J_eval) <= 1e-5 * J_eval
-    assert ref["J"] * (1 - 1e-9) <= J_eval <= ref["J"] + 0.02 * (J0 - ref["J"])
+    # the iteration stops on its residual test here, so it lands on the optimum up to
+    # fp32 outputs; with a gap of a percent or more its subspace is the oracle's
+    assert res["converged"]
+    assert ref["J"] * (1 - 1e-9) <= J_eval <= ref["J"] + 1e-5 * (J0 - ref["J"])
+    if gap > 1.01:
+        assert proj <= 1e-5
 
 
 def _rtn(W, scales, zeros, bits, group):
