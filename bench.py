@@ -68,10 +68,23 @@ def cpu_baseline(spec, lay, max_rows=512, tok_sample=32768):
     except Exception:
         cores = os.cpu_count()
     return {"value": round(total_ms, 1), "unit": "ms/layer", "cores": cores, "kind": "oracle",
+            "blas": blas_vendor(),
             "sample": "Hessian on %d of %d tokens (x%.0f), full damping+factor (n=%d), sweep on %d of %d rows (x%.0f);"
                       " measured %.1f s + %.1f s + %.1f s" % (tok_sample, spec.tokens, spec.tokens / tok_sample,
                                                                spec.n, max_rows, spec.out, spec.out / max_rows,
                                                                t_h, t_f, t_s)}
+
+
+def blas_vendor():
+    """The BLAS numpy calls (name, version, and the library's own configuration line)."""
+    import numpy as np
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return "%s %s (%s); threads %s" % (b.get("name"), b.get("version"), b.get("openblas configuration", "").strip(),
+                                           os.environ.get("OMP_NUM_THREADS", os.environ.get("OPENBLAS_NUM_THREADS",
+                                                                                            "default")))
+    except Exception as e:  # pragma: no cover
+        return "unknown (%s)" % e
 
 
 def code_digest(path):
@@ -106,6 +119,7 @@ def syrk_traffic(workload):
 
 PEAK_FP32_MATRIX_TFLOPS = 157.3  # dense fp32 MFMA, MI355X
 PEAK_FP64_MATRIX_TFLOPS = 78.6   # dense fp64 MFMA, MI355X
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # fp32 vector, MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2 (packed) x 2 (FMA) x 2.4 GHz
 R2D_KERNELS = ["k_damp_lambda", "k_damp_fill", "k_chol_panel", "k_chol_panel2", "k_gemm64", "k_gemm_ring64",
                "k_gemm_ring128", "k_make_u", "k_r2d_unit", "k_r2d_fill", "k_r2d_tile", "k_r2d_push", "k_r2d_obj"]
 
@@ -173,6 +187,16 @@ def bench_r2d(args, torch, Context, synth, dev):
     pairs = sum((TM - I - 1) + (TN - J - 1) for I in range(TM) for J in range(TN))
     push_flops = pairs * 2 * 64 ** 3
     ach = push_flops * args.steps / (push_ms * 1e-3) / 1e12 if push_ms else 0.0
+    # the in-tile walks: entry (k, l) of a tile pushes its delta down the
+    # rows below it and its final C along the columns right of it, inside
+    # the tile (2 flops per multiply-add), 2 * 64 * 2 * (0 + ... + 63) flops
+    # per full tile; a launch walks the tiles of one anti-diagonal stage
+    def tile_fl(mt, nt):
+        return 2 * (nt * mt * (mt - 1) // 2 + mt * nt * (nt - 1) // 2)
+    tile_flops = sum(tile_fl(min(64, m - 64 * I), min(64, n - 64 * J)) for I in range(TM) for J in range(TN))
+    tile_launches = TM + TN - 1
+    tile_avg_ms = tile_ms / max(tile_n, 1)
+    tile_ach = tile_flops / tile_launches / (tile_avg_ms * 1e-3) / 1e12 if tile_n else 0.0
     line = {"metric": "ms per layer, two-sided rounding (GPTQ-2D) of a 4096x4096 layer", "value": round(ms_step, 4),
             "unit": "ms/layer", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
@@ -181,13 +205,23 @@ def bench_r2d(args, torch, Context, synth, dev):
                                    "H from X[262144,4096], lam 0.01 mean diag"},
             "stages_ms": {"factors": round(fac, 4), "round_2d": round(rnd, 4)},
             "kernels_one_step": breakdown,
-            "roofline": {"kernel": "k_r2d_push", "bound": "mfma", "achieved": round(ach, 2),
-                         "peak": PEAK_FP32_MATRIX_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ach / PEAK_FP32_MATRIX_TFLOPS, 4), "traffic": None,
-                         "avg_launch_ms": round(push_ms / max(push_n, 1), 4),
-                         "flops_per_step": push_flops},
-            "tile_kernel": {"launches_per_step": tile_n // max(args.steps, 1),
-                            "avg_launch_ms": round(tile_ms / max(tile_n, 1), 4)},
+            # the walk is a chain of 2 * 64 - 1 dependent steps per tile (each an
+            # LDS read, the rounding, the pushes and a barrier), not limited by
+            # any throughput: its fraction of the fp32 vector peak is small by
+            # construction, and the per-step time is the figure that moves
+            "roofline": {"kernel": "k_r2d_tile", "bound": "alu", "achieved": round(tile_ach, 4),
+                         "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tile_ach / PEAK_FP32_VECTOR_TFLOPS, 6), "traffic": None,
+                         "avg_launch_ms": round(tile_avg_ms, 4),
+                         "flops_per_launch": tile_flops / tile_launches,
+                         "latency": {"dependent_steps_per_launch": 2 * 64 - 1,
+                                     "ns_per_step": round(tile_avg_ms * 1e6 / (2 * 64 - 1), 1),
+                                     "launches_per_step": tile_n // max(args.steps, 1)}},
+            "secondary": {"k_r2d_push": {"bound": "mfma", "achieved": round(ach, 2),
+                                         "peak": PEAK_FP32_MATRIX_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": round(ach / PEAK_FP32_MATRIX_TFLOPS, 4),
+                                         "avg_launch_ms": round(push_ms / max(push_n, 1), 4),
+                                         "flops_per_step": push_flops}},
             "objective": {"J": last["J"]}}
     ctx.close()
     print(json.dumps(line), flush=True)
@@ -511,6 +545,14 @@ def main():
                         "frac": round(trail_fl / t_tr / 1e12 / PEAK_FP32_MATRIX_TFLOPS, 4)},
             "k_sweep": {"gb_s": round(sweep_bytes / t_sw / 1e9, 1), "peak": PEAK_HBM_GBS,
                         "frac": round(sweep_bytes / t_sw / 1e9 / PEAK_HBM_GBS, 4), "bound": "latency"}}
+    if "stages_ms" in line and line["stages_ms"]["factor"] > 0:
+        # the factor stage (damping, Cholesky and inverse: 2 n^3 / 3 flops per
+        # distinct Hessian) against the fp64 matrix roof, from the timed steps
+        fac_fl = sum(f["factor"] for f in fl) / nlayers
+        rate = fac_fl / (line["stages_ms"]["factor"] * 1e-3) / 1e12
+        line.setdefault("secondary", {})["factor"] = {
+            "tflops": round(rate, 2), "peak": PEAK_FP64_MATRIX_TFLOPS, "frac": round(rate / PEAK_FP64_MATRIX_TFLOPS, 4),
+            "flops_per_layer": fac_fl}
     if dom_launches:
         # algorithmic flops of one launch (mean over the step's launches): the
         # triangle X^T X of every layer the launch covers

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
-SOURCES = ["syrk.hip", "factor.hip", "sweep.hip", "lora.hip", "round2d.hip", "qronos.hip", "deploy.hip", "api.cpp"]
+SOURCES = ["syrk.hip", "factor.hip", "sweep.hip", "lora.hip", "round2d.hip", "qronos.hip", "deploy.hip", "planner.cpp", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

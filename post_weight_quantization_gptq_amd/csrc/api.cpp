@@ -17,6 +17,7 @@
 #include "common.h"
 #include "launch.h"
 #include "plan.h"
+#include "planner.h"
 
 #define GPTQ_API extern "C" __attribute__((visibility("default")))
 
@@ -278,168 +279,17 @@ struct DeviceGuard {
   }
 };
 
-inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
-inline long long cdiv64(long long a, long long b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------ Hessian plan --
-struct HessJob {
-  const uint16_t* X;
-  long long tokens, ldx;
-  int n;
-  float* H;
-  int accumulate;
-  // non-null: the cross Gram X^T Y (Y as X: [tokens][ldx]; direct layout
-  // only), written in full
-  const uint16_t* Y = nullptr;
-};
-
-struct HessPlan {
-  std::vector<XposeProb> xprobs;
-  std::vector<Seg> xsegs;
-  std::vector<SyrkProb> probs;
-  std::vector<SyrkTask> tasks;
-  std::vector<RedProb> rprobs;
-  std::vector<RedTask> rtasks;
-  std::vector<int> partlist;
-  int nparts = 0;
-};
-
-// The tiles can read X directly (no transposed copy) when its rows are
-// 16-byte aligned and n is a multiple of 8 (16-byte feature chunks never
-// cross the end of a row).  A stage's per-lane byte offsets (32 rows of the
-// pitch) are 32-bit, which bounds the pitch.
-static bool hess_direct(const HessJob& J) {
-  return J.tokens > 0 && (J.ldx % 8) == 0 && (((uintptr_t)J.X) & 15) == 0 && (J.n % 8) == 0 &&
-         J.ldx < (1LL << 25);
-}
-
-// Interleaved bit order of (i, j): tiles close in this order share rows of X.
-static int morton2(int i, int j) {
-  int m = 0;
-  for (int b = 0; b < 10; ++b) m |= (((i >> b) & 1) << (2 * b + 1)) | (((j >> b) & 1) << (2 * b));
-  return m;
-}
-
-// Number of token slices for one layer's tiles: whole rounds of the chip at
-// one tile per CU, each task also paying for writing its partial (about ten
-// 32-token steps of time).  Depends on the layer alone.
-static int hess_slices(int ntile, long long chunks, int ncu) {
-  int best_s = 1;
-  long long best = -1;
-  for (int s = 1; s <= 64 && s <= std::max(1LL, chunks); ++s) {
-    const long long rounds = cdiv((long long)ntile * s, (long long)ncu);
-    const long long cost = rounds * (cdiv(chunks, (long long)s) + 10);
-    if (best < 0 || cost < best) {
-      best = cost;
-      best_s = s;
-    }
-  }
-  return best_s;
-}
-
-// Tasks of every layer: its upper 256x256 tiles times S token slices, slice
-// by slice, so that the whole chip streams one window of tokens at a time and
-// re-reads of X hit the L2/MALL.  Inside a slice the tiles go in Morton order,
-// cut into 8 groups that are dealt out in turn: consecutive workgroups land
-// on the 8 XCDs in turn, so each XCD works on one compact group of tiles that
-// shares rows of X in its own L2.  The cut points of a layer depend on that
-// layer alone, so a layer gets the same bits alone or in a batch.  The rows of
-// the transposed copy are padded by 256 tokens so that rows at the same token
-// offset spread over the L2 channels.
-void plan_hessian(const std::vector<HessJob>& jobs, int ncu, int nxcd, uint16_t* xt, HessPlan& P) {
-  for (size_t p = 0; p < jobs.size(); ++p) {
-    const HessJob& J = jobs[p];
-    const int vec = (J.ldx % 8 == 0) && (((uintptr_t)J.X & 15) == 0);
-    const int nt = cdiv(J.n, 256);
-    const long long chunks = cdiv(J.tokens, 64);
-    const int n_pad = nt * 256, t_pad = (int)(chunks * 64);
-    if (hess_direct(J)) {
-      // the tiles read X itself (transposing LDS reads); no copy
-      P.xprobs.push_back(XposeProb{J.X, J.ldx, nullptr, J.n, (int)J.tokens, n_pad, t_pad, vec, 0});
-      P.probs.push_back(SyrkProb{J.X, J.ldx, 1, (int)J.tokens, J.n, 0, J.Y});
-    } else {
-      const int ldt = t_pad > 0 ? t_pad + 256 : 0;
-      P.xprobs.push_back(XposeProb{J.X, J.ldx, xt, J.n, (int)J.tokens, n_pad, t_pad, vec, ldt});
-      if (t_pad > 0) P.xsegs.push_back(Seg{(int)p, 0, (t_pad / 64) * (n_pad / 64), 0, 0, 0, 0, 0});
-      P.probs.push_back(SyrkProb{xt, ldt, 0, (int)J.tokens, J.n, 0, nullptr});
-      xt += (size_t)n_pad * ldt;
-    }
-    const bool full = J.Y != nullptr;
-    P.rprobs.push_back(RedProb{J.H, J.n, J.accumulate, full ? 1 : 0, 0});
-    if (J.n <= 0) continue;
-    std::vector<std::pair<int, int>> tl;  // upper tiles, or every tile of a cross Gram
-    for (int ti = 0; ti < nt; ++ti)
-      for (int tj = full ? 0 : ti; tj < nt; ++tj) tl.push_back({ti, tj});
-    const int ntile = (int)tl.size();
-    if (J.tokens > 0) {
-      std::vector<std::pair<int, int>> mo = tl;
-      std::stable_sort(mo.begin(), mo.end(), [](const std::pair<int, int>& x, const std::pair<int, int>& y) {
-        return morton2(x.first, x.second) < morton2(y.first, y.second);
-      });
-      std::vector<int> ord;  // dealt order, indices into mo
-      const int G = std::max(1, std::min(nxcd, ntile)), base = ntile / G, rem = ntile % G;
-      for (int idx = 0; idx <= base; ++idx)
-        for (int g = 0; g < G; ++g)
-          if (idx < base + (g < rem ? 1 : 0)) ord.push_back(g * base + std::min(g, rem) + idx);
-      const long long c32 = t_pad / 32;
-      const int S = hess_slices(ntile, c32, ncu);
-      const int first = (int)P.tasks.size();
-      std::vector<int> pos(ntile);  // tile (canonical index) -> position inside a slice
-      for (int q = 0; q < ntile; ++q) {
-        const std::pair<int, int> t = mo[ord[q]];
-        const int ci = full ? t.first * nt + t.second
-                            : t.first * nt - t.first * (t.first - 1) / 2 + (t.second - t.first);
-        pos[ci] = q;
-      }
-      for (int sl = 0; sl < S; ++sl) {
-        const int k0 = (int)(32 * (c32 * sl / S)), k1 = (int)(32 * (c32 * (sl + 1) / S));
-        for (int q = 0; q < ntile; ++q) {
-          const std::pair<int, int> t = mo[ord[q]];
-          P.tasks.push_back(SyrkTask{(int)p, t.first, t.second, k0, k1, (int)P.tasks.size(), 0, 0});
-        }
-      }
-      for (int ci = 0; ci < ntile; ++ci) {
-        const int ti = tl[ci].first, tj = tl[ci].second;
-        const int part0 = (int)P.partlist.size();
-        for (int sl = 0; sl < S; ++sl) P.partlist.push_back(first + sl * ntile + pos[ci]);
-        for (int a = 0; a < 4; ++a)
-          for (int b = 0; b < 4; ++b) {
-            if (ti == tj && a > b && !full) continue;
-            const int r0 = ti * 256 + 64 * a, c0 = tj * 256 + 64 * b;
-            if (r0 >= J.n || c0 >= J.n) continue;
-            P.rtasks.push_back(RedTask{(int)p, r0, c0, part0, S, 0, 0, 0});
-          }
-      }
-    } else {
-      // no tokens: every sub-block sums zero partials (H = 0, or H unchanged)
-      for (int ci = 0; ci < ntile; ++ci) {
-        const int ti = tl[ci].first, tj = tl[ci].second;
-        for (int a = 0; a < 4; ++a)
-          for (int b = 0; b < 4; ++b) {
-            const int r0 = ti * 256 + 64 * a, c0 = tj * 256 + 64 * b;
-            if ((ti == tj && a > b && !full) || r0 >= J.n || c0 >= J.n) continue;
-            P.rtasks.push_back(RedTask{(int)p, r0, c0, 0, 0, 0, 0, 0});
-          }
-      }
-    }
-  }
-  P.nparts = (int)P.tasks.size();
-}
-
 int run_hessian(gptq_ctx c, const std::vector<HessJob>& jobs) {
-  size_t xt_elems = 0;
-  for (const HessJob& J : jobs)
-    if (J.tokens > 0 && !hess_direct(J)) xt_elems += (size_t)cdiv(J.n, 256) * 256 * ((size_t)cdiv(J.tokens, 64) * 64 + 256);
+  const size_t xt_elems = hess_xt_elems(jobs);
   int rc = ensure(c, c->xt, xt_elems * sizeof(uint16_t));
   if (rc) return rc;
   HessPlan P;
   plan_hessian(jobs, c->ncu, c->nxcd, (uint16_t*)c->xt.p, P);
   if ((rc = ensure(c, c->partials, (size_t)std::max(P.nparts, 1) * 65536 * sizeof(float)))) return rc;
   int nxwg = 0;
-  for (auto& sg : P.xsegs) {
-    sg.wg0 = nxwg;
-    nxwg += sg.nwg;
-  }
+  for (const auto& sg : P.xsegs) nxwg += sg.nwg;
   Blob b;
   const size_t o_xprobs = b.add(P.xprobs), o_xsegs = b.add(P.xsegs);
   const size_t o_probs = b.add(P.probs), o_tasks = b.add(P.tasks), o_rprobs = b.add(P.rprobs),
@@ -476,54 +326,11 @@ int run_hessian64(gptq_ctx c, const uint16_t* X, long long tokens, long long ldx
   const int nwx = xsegs.empty() ? 0 : xsegs[0].nwg;
   std::vector<SyrkProb> probs{SyrkProb{xt, t_pad, 0, (int)tokens, n, 0}};
   std::vector<RedProb64> rprobs{RedProb64{H, n, 0}};
-  const int nt = cdiv(n, 128);
-  const int ntile = nt * (nt + 1) / 2;
-  const long long chunks = t_pad / 32;
-  // slices: minimise rounds x slice length
-  int S = 1;
-  long long best = -1;
-  for (int k = 1; k <= 64 && k <= std::max(1LL, chunks); ++k) {
-    const long long rounds = cdiv((long long)ntile * k, (long long)c->ncu);
-    const long long cost = rounds * cdiv(chunks, (long long)k);
-    if (best < 0 || cost < best) {
-      best = cost;
-      S = k;
-    }
-  }
-  std::vector<SyrkTask> tasks;
-  std::vector<int> partlist;
-  std::vector<RedTask> rtasks;
-  if (chunks > 0) {
-    for (int sl = 0; sl < S; ++sl) {
-      const int k0 = (int)(32 * (chunks * sl / S)), k1 = (int)(32 * (chunks * (sl + 1) / S));
-      int t = 0;
-      for (int ti = 0; ti < nt; ++ti)
-        for (int tj = ti; tj < nt; ++tj, ++t) tasks.push_back(SyrkTask{0, ti, tj, k0, k1, (int)tasks.size(), 0, 0});
-    }
-    int t = 0;
-    for (int ti = 0; ti < nt; ++ti)
-      for (int tj = ti; tj < nt; ++tj, ++t) {
-        const int part0 = (int)partlist.size();
-        for (int sl = 0; sl < S; ++sl) partlist.push_back(sl * ntile + t);
-        for (int a = 0; a < 2; ++a)
-          for (int b = 0; b < 2; ++b) {
-            if (ti == tj && a > b) continue;
-            const int r0 = ti * 128 + 64 * a, c0 = tj * 128 + 64 * b;
-            if (r0 >= n || c0 >= n) continue;
-            rtasks.push_back(RedTask{0, r0, c0, part0, S, 0, 0, 0});
-          }
-      }
-  } else {
-    // no tokens: H = 0 (every sub-block sums zero partials)
-    for (int ti = 0; ti < nt; ++ti)
-      for (int tj = ti; tj < nt; ++tj)
-        for (int a = 0; a < 2; ++a)
-          for (int b = 0; b < 2; ++b) {
-            const int r0 = ti * 128 + 64 * a, c0 = tj * 128 + 64 * b;
-            if ((ti == tj && a > b) || r0 >= n || c0 >= n) continue;
-            rtasks.push_back(RedTask{0, r0, c0, 0, 0, 0, 0, 0});
-          }
-  }
+  Hess64Plan P;
+  plan_hessian64(n, tokens, c->ncu, P);
+  const std::vector<SyrkTask>& tasks = P.tasks;
+  const std::vector<RedTask>& rtasks = P.rtasks;
+  const std::vector<int>& partlist = P.partlist;
   if ((rc = ensure(c, c->partials, std::max<size_t>(tasks.size(), 1) * 16384 * sizeof(double)))) return rc;
   Blob b;
   const size_t o_xprobs = b.add(xprobs), o_xsegs = b.add(xsegs), o_probs = b.add(probs), o_tasks = b.add(tasks),
@@ -565,7 +372,6 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   }
   if ((rc = ensure(c, c->facY, totA * sizeof(double)))) return rc;
   std::vector<FacProb> probs(np);
-  int maxnb = 0, maxn = 0;
   for (int p = 0; p < np; ++p) {
     const FacJob& J = jobs[p];
     FacProb f;
@@ -583,113 +389,16 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
     f.info = &dslots[p].info;
     f.nonfinite = &dslots[p].nonfinite;
     probs[p] = f;
-    maxnb = std::max(maxnb, cdiv(J.n, 64));
-    maxn = std::max(maxn, J.n);
     if (A_out) A_out[p] = f.A;
   }
   Blob b;
   const size_t o_probs = b.add(probs);
-  struct L {
-    int kind;  // 0 fill, 1 panel, 2 gemm (general, 64 tiles), 3 ring gemm 64, 4 ring gemm 128, 5 makeu,
-               // 6 fork (side stream waits for the main stream), 7 join (main waits for the side stream),
-               // 8 panel pair
-    bool side;  // launch on the side stream
-    size_t off;
-    int nseg, nwg;
-  };
-  std::vector<L> launches;
-  auto add_launch = [&](int kind, std::vector<Seg>& segs, bool side = false) {
-    int nwg = 0;
-    for (auto& s : segs) {
-      s.wg0 = nwg;
-      nwg += s.nwg;
-    }
-    if (nwg == 0) return;
-    launches.push_back(L{kind, side, b.add(segs), (int)segs.size(), nwg});
-  };
-  auto add_sync = [&](int kind) { launches.push_back(L{kind, false, 0, 0, 0}); };
-  // The ring-staged products need every K range and row pitch to be a
-  // multiple of 64 (16-byte aligned chunks of 16 doubles).
-  bool ring = true;
-  for (const FacJob& J : jobs) ring = ring && (J.n % 64) == 0;
-  {
-    std::vector<Seg> s;
-    for (int p = 0; p < np; ++p)
-      if (jobs[p].H) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 4), 0, 0, 0, 0, 0});
-    add_launch(0, s);
-  }
-  // Cholesky and Y = L^{-1}: outer panels of 256 columns, four 64-column
-  // steps each.  Step k: the panel launch (every 64-block of the problem),
-  // then the updates of the rest of the outer panel (L columns [c0, P1) of
-  // every row below; Y rows [c0, P1)).  At the end of an outer panel the
-  // trailing updates with K = P1 - P0 split in two: the part the next outer
-  // panel reads (L columns [P1, S), S = P1 + 256; Y rows [P1, S)) on the main
-  // stream, and the rest (L's trailing triangle from S on; Y rows from S on)
-  // on the side stream, where it overlaps the next outer panel's steps (which
-  // neither read nor write it) and is joined before the next outer update.
-  // With the general products (n % 64 != 0) everything stays on one stream.
-  bool side_busy = false;
-  // Steps go in pairs (k, k+1) inside an outer panel: one launch of
-  // k_chol_panel2 (kind 8) does both; a last block without a partner takes
-  // the single-step k_chol_panel.
-  for (int k = 0; k < maxnb; k += 2) {
-    std::vector<Seg> pan, pan2, inner, crit, bulk;
-    int bulk_rows = 0;
-    for (int p = 0; p < np; ++p) {
-      const int n = jobs[p].n, nb = cdiv(n, 64);
-      if (k >= nb) continue;
-      const bool pair = k + 1 < nb;
-      (pair ? pan2 : pan).push_back(Seg{p, 0, nb, k, 0, 0, 0, 0});
-      const int k0 = 64 * k, pw = std::min(pair ? 128 : 64, n - k0);
-      const int P0 = (k0 / 256) * 256, P1 = std::min(P0 + 256, n);
-      const int c0 = k0 + pw;
-      if (c0 < P1) {  // rest of the outer panel
-        const int nrow = cdiv(n - c0, 64), ncol = cdiv(P1 - c0, 64);
-        inner.push_back(Seg{p, 0, ncol * nrow - ncol * (ncol - 1) / 2, GK_CHOL_TRAIL, k0, pw, c0, P1});
-        inner.push_back(Seg{p, 0, cdiv(P1 - c0, 64) * cdiv(c0, 64), GK_ZUPD, k0, pw, c0, P1});
-      } else if (P1 < n) {  // end of the outer panel: trailing updates with K = P1 - P0
-        const int S = ring ? std::min(P1 + 256, n) : n;
-        {
-          const int nrow = cdiv(n - P1, 64), ncol = cdiv(S - P1, 64);
-          crit.push_back(Seg{p, 0, ncol * nrow - ncol * (ncol - 1) / 2, GK_CHOL_TRAIL, P0, P1 - P0, P1, S});
-          crit.push_back(Seg{p, 0, cdiv(S - P1, 64) * cdiv(P1, 64), GK_ZUPD, P0, P1 - P0, P1, S});
-        }
-        if (S < n) {
-          const int m = cdiv(n - S, 128);
-          bulk.push_back(Seg{p, 0, m * (m + 1) / 2, GK_CHOL_TRAIL, P0, P1 - P0, S, n});
-          bulk.push_back(Seg{p, 0, m * cdiv(P1, 128), GK_ZUPD, P0, P1 - P0, S, n});
-          bulk_rows = std::max(bulk_rows, n - S);
-        }
-      }
-    }
-    add_launch(8, pan2);
-    add_launch(1, pan);
-    add_launch(ring ? 3 : 2, inner);
-    if (!crit.empty()) {
-      if (side_busy) add_sync(7);  // the previous bulk update touches the columns updated now
-      side_busy = false;
-      if (!bulk.empty()) {
-        if (bulk_rows < 1024) {  // small: 64-wide tiles, on the main stream
-          for (Seg& sg : bulk) {
-            const int n = jobs[sg.prob].n, m = cdiv(n - sg.d, 64);
-            sg.nwg = (sg.a == GK_CHOL_TRAIL) ? m * (m + 1) / 2 : m * cdiv(sg.b + sg.c, 64);
-          }
-          for (Seg& sg : bulk) crit.push_back(sg);
-        } else {
-          add_sync(6);
-          add_launch(4, bulk, true);
-          side_busy = true;
-        }
-      }
-      add_launch(ring ? 3 : 2, crit);
-    }
-  }
-  if (side_busy) add_sync(7);
-  {
-    std::vector<Seg> s;
-    for (int p = 0; p < np; ++p) s.push_back(Seg{p, 0, cdiv(jobs[p].n, 4), 0, 0, 0, 0, 0});
-    add_launch(5, s);
-  }
+  std::vector<FacShape> shapes(np);
+  for (int p = 0; p < np; ++p) shapes[p] = FacShape{jobs[p].n, jobs[p].H != nullptr};
+  const std::vector<PlanLaunch> launches = plan_factor(shapes);
+  std::vector<size_t> offs(launches.size());
+  for (size_t i = 0; i < launches.size(); ++i)
+    if (!launches[i].segs.empty()) offs[i] = b.add(launches[i].segs);
   uint8_t* d = nullptr;
   if ((rc = upload(c, b, &d))) return rc;
   const FacProb* dp = (const FacProb*)(d + o_probs);
@@ -699,24 +408,26 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   // the 64 panel workgroups of a 4096-wide problem and its narrow updates
   // (measured best at n = 4096 among caps of 128 to 256 CUs)
   const int side_wg = std::max(1, c->ncu - std::min(96, c->ncu / 2));
-  for (const L& l : launches) {
-    const Seg* sg = (const Seg*)(d + l.off);
+  for (size_t i = 0; i < launches.size(); ++i) {
+    const PlanLaunch& l = launches[i];
+    const Seg* sg = (const Seg*)(d + offs[i]);
+    const int nseg = (int)l.segs.size();
     hipStream_t st = l.side ? c->side : c->stream;
     switch (l.kind) {
-      case 0: LAUNCH(c, "k_damp_fill", launch_damp_fill(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 1: LAUNCH(c, "k_chol_panel", launch_chol_panel(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 8: LAUNCH(c, "k_chol_panel2", launch_chol_panel2(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 2: LAUNCH(c, "k_gemm64", launch_gemm64(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3: LAUNCH_ON(c, st, "k_gemm_ring64", launch_gemm_ring(64, dp, sg, l.nseg, l.nwg, 0, st)); break;
-      case 4:
-        LAUNCH_ON(c, st, "k_gemm_ring128", launch_gemm_ring(128, dp, sg, l.nseg, l.nwg, l.side ? side_wg : 0, st));
+      case FK_FILL: LAUNCH(c, "k_damp_fill", launch_damp_fill(dp, sg, nseg, l.nwg, c->stream)); break;
+      case FK_PANEL: LAUNCH(c, "k_chol_panel", launch_chol_panel(dp, sg, nseg, l.nwg, c->stream)); break;
+      case FK_PANEL2: LAUNCH(c, "k_chol_panel2", launch_chol_panel2(dp, sg, nseg, l.nwg, c->stream)); break;
+      case FK_GEMM64: LAUNCH(c, "k_gemm64", launch_gemm64(dp, sg, nseg, l.nwg, c->stream)); break;
+      case FK_RING64: LAUNCH_ON(c, st, "k_gemm_ring64", launch_gemm_ring(64, dp, sg, nseg, l.nwg, 0, st)); break;
+      case FK_RING128:
+        LAUNCH_ON(c, st, "k_gemm_ring128", launch_gemm_ring(128, dp, sg, nseg, l.nwg, l.side ? side_wg : 0, st));
         break;
-      case 5: LAUNCH(c, "k_make_u", launch_make_u(dp, sg, l.nseg, l.nwg, c->stream)); break;
-      case 6:
+      case FK_MAKEU: LAUNCH(c, "k_make_u", launch_make_u(dp, sg, nseg, l.nwg, c->stream)); break;
+      case PL_FORK:
         HIPCHK(c, hipEventRecord(c->fork_ev, c->stream));
         HIPCHK(c, hipStreamWaitEvent(c->side, c->fork_ev, 0));
         break;
-      case 7:
+      case PL_JOIN:
         HIPCHK(c, hipEventRecord(c->join_ev, c->side));
         HIPCHK(c, hipStreamWaitEvent(c->stream, c->join_ev, 0));
         break;
@@ -731,28 +442,17 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
 int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<float*>* Ww_out = nullptr,
                  const NoAlloc* na = nullptr) {
   const int nl = (int)jobs.size();
-  // Super-blocks: each block's errors reach the rest of its super-block right
-  // away, the columns past it only at the super-block's end (one product with
-  // K = the super-block width), so the far columns of W are rewritten once
-  // per super-block instead of once per block.  Groups must nest in it.
-  std::vector<int> sbk(nl);
-  size_t totW = 0, totE = 0, totO = 0, totD = 0;
-  std::vector<size_t> oW(nl), oE(nl), oO(nl), oD(nl);
+  std::vector<QuantShape> shapes(nl);
   for (int p = 0; p < nl; ++p) {
     const QuantJob& J = jobs[p];
-    int sb = std::max(1, 512 / J.block);
-    const int sbw = sb * J.block;
-    if (J.group && !(sbw % J.group == 0 || J.group % sbw == 0)) sb = 1;
-    sbk[p] = sb;
-    oW[p] = totW;
-    if (!J.Ww_ext) totW += (size_t)J.out * J.nt;
-    oE[p] = totE;
-    totE += 2 * (size_t)J.out * sb * J.block;  // two super-blocks: one swept while the other's far update runs
-    oO[p] = totO;
-    totO += (size_t)J.out * 2;
-    oD[p] = totD;
-    totD += (size_t)(J.nt + 63) / 64 * 64;
+    shapes[p] = QuantShape{J.out, J.n, J.nt, J.block, J.group, J.mode, J.Ww_ext != nullptr};
   }
+  QuantLayout QLy;
+  std::vector<PlanLaunch> launches;
+  plan_quantize(shapes, &QLy, &launches);
+  const std::vector<int>& sbk = QLy.sbk;
+  const size_t totW = QLy.totW, totE = QLy.totE, totO = QLy.totO, totD = QLy.totD;
+  const std::vector<size_t>&oW = QLy.oW, &oE = QLy.oE, &oO = QLy.oO, &oD = QLy.oD;
   int rc;
   float* work_p;
   float* eblk_p;
@@ -777,7 +477,6 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     dinv_p = (float*)c->dinv.p;
   }
   std::vector<QLayer> L(nl);
-  int maxblk = 0;
   for (int p = 0; p < nl; ++p) {
     const QuantJob& J = jobs[p];
     QLayer q;
@@ -806,104 +505,33 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
     q.sbk = sbk[p];
     q.mode = J.mode;
     L[p] = q;
-    maxblk = std::max(maxblk, q.nblk);
     if (Ww_out) Ww_out->push_back(q.Ww);
   }
   Blob b;
   const size_t o_L = b.add(L);
-  struct Lc {
-    int kind;  // 0 init, 1 rowfit, 2 sweep, 3 trail, 6 fork, 7 join (as in the factor)
-    int block;
-    bool side;
-    size_t off;
-    int nseg, nwg;
-    int mode;  // sweeps: 0 GPTQ, 1 Bid-Up
-  };
-  std::vector<Lc> launches;
-  auto add_launch = [&](int kind, int block, std::vector<Seg>& segs, bool side = false, int mode = 0) {
-    int nwg = 0;
-    for (auto& s : segs) {
-      s.wg0 = nwg;
-      nwg += s.nwg;
-    }
-    if (nwg == 0) return;
-    launches.push_back(Lc{kind, block, side, b.add(segs), (int)segs.size(), nwg, mode});
-  };
-  auto add_sync = [&](int kind) { launches.push_back(Lc{kind, 0, false, 0, 0, 0, 0}); };
-  {
-    std::vector<Seg> s, f;
-    for (int p = 0; p < nl; ++p) {
-      s.push_back(Seg{p, 0, cdiv(jobs[p].out, 4), 0, 0, 0, 0, 0});
-      if (jobs[p].group == 0 && !jobs[p].mode) f.push_back(Seg{p, 0, cdiv(jobs[p].out, 4), 0, 0, 0, 0, 0});
-    }
-    add_launch(0, 0, s);
-    add_launch(1, 0, f);
-  }
-  std::vector<int> blocks;
-  for (auto& J : jobs)
-    if (std::find(blocks.begin(), blocks.end(), J.block) == blocks.end()) blocks.push_back(J.block);
-  // At a super-block's end, the next super-block's columns are updated on
-  // the main stream (its sweeps read them); the columns past it on the side
-  // stream, beside the next super-block's sweeps (which neither read nor
-  // write them; the errors sit in the other half of the two-super-block
-  // buffer), joined before the next far update.  Needs the groups to nest in
-  // a super-block (a group fit reads its whole group).
-  bool side_busy = false;
-  // One sweep launch per super-block (the sweep kernel applies each block's
-  // errors to the rest of its super-block itself).
-  for (int k = 0; k < maxblk; ++k) {
-    for (int B : blocks)
-      for (int mode = 0; mode < 2; ++mode) {
-        std::vector<Seg> s;
-        for (int p = 0; p < nl; ++p)
-          if (jobs[p].block == B && jobs[p].mode == mode && k < L[p].nblk && k % sbk[p] == 0)
-            s.push_back(Seg{p, 0, cdiv(jobs[p].out, 16), k / sbk[p], 0, 0, 0, 0});
-        add_launch(2, B, s, false, mode);
-      }
-    std::vector<Seg> crit, bulk;  // past the super-block (64 / 128 tiles)
-    for (int p = 0; p < nl; ++p) {
-      if (k >= L[p].nblk) continue;
-      const int B = jobs[p].block, n = jobs[p].n, nt = jobs[p].nt, sb = sbk[p], sbw = sb * B;
-      const int b0 = k * B, b1 = std::min(b0 + B, n);
-      const int sb0 = (k / sb) * sbw, sb1 = std::min(sb0 + sbw, n);
-      const int par = ((k / sb) & 1) * jobs[p].out * L[p].ldE;  // this super-block's half of the error buffer
-      if (b1 == sb1 && sb1 < nt) {  // end of the super-block: all columns past it
-        const bool nest = jobs[p].group == 0 || sbw % jobs[p].group == 0;
-        const int S = nest ? std::min(sb1 + sbw, nt) : nt;
-        crit.push_back(Seg{p, 0, cdiv(jobs[p].out, 64) * cdiv(S - sb1, 64), par, sb0, sb1 - sb0, sb1, S});
-        if (S < nt) bulk.push_back(Seg{p, 0, cdiv(jobs[p].out, 128) * cdiv(nt - S, 128), par, sb0, sb1 - sb0, S, nt});
-      }
-    }
-    if (!crit.empty()) {
-      if (side_busy) add_sync(7);  // the previous far update covers the columns updated now
-      side_busy = false;
-      if (!bulk.empty()) {
-        add_sync(6);
-        add_launch(3, 128, bulk, true);
-        side_busy = true;
-      }
-      add_launch(3, 64, crit);
-    }
-  }
-  if (side_busy) add_sync(7);
+  std::vector<size_t> offs(launches.size());
+  for (size_t i = 0; i < launches.size(); ++i)
+    if (!launches[i].segs.empty()) offs[i] = b.add(launches[i].segs);
   uint8_t* d = nullptr;
   if ((rc = na ? upload_noalloc(c, b, na->blob, &d) : upload(c, b, &d))) return rc;
   const QLayer* dL = (const QLayer*)(d + o_L);
-  for (const Lc& l : launches) {
-    const Seg* sg = (const Seg*)(d + l.off);
+  for (size_t i = 0; i < launches.size(); ++i) {
+    const PlanLaunch& l = launches[i];
+    const Seg* sg = (const Seg*)(d + offs[i]);
+    const int nseg = (int)l.segs.size();
     hipStream_t st = l.side ? c->side : c->stream;
     switch (l.kind) {
-      case 0: LAUNCH(c, "k_init_work", launch_init_work(dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 1: LAUNCH(c, "k_rowfit", launch_rowfit(dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 2: LAUNCH(c, "k_sweep", launch_sweep(l.block, l.mode, dL, sg, l.nseg, l.nwg, c->stream)); break;
-      case 3:  // beside the sweeps: one workgroup per CU, which leaves room on each CU for a sweep's
-        LAUNCH_ON(c, st, "k_trail", launch_trail(l.block, dL, sg, l.nseg, l.nwg, l.side ? c->ncu : 0, st));
+      case QK_INIT: LAUNCH(c, "k_init_work", launch_init_work(dL, sg, nseg, l.nwg, c->stream)); break;
+      case QK_ROWFIT: LAUNCH(c, "k_rowfit", launch_rowfit(dL, sg, nseg, l.nwg, c->stream)); break;
+      case QK_SWEEP: LAUNCH(c, "k_sweep", launch_sweep(l.block, l.mode, dL, sg, nseg, l.nwg, c->stream)); break;
+      case QK_TRAIL:  // beside the sweeps: one workgroup per CU, which leaves room on each CU for a sweep's
+        LAUNCH_ON(c, st, "k_trail", launch_trail(l.block, dL, sg, nseg, l.nwg, l.side ? c->ncu : 0, st));
         break;
-      case 6:
+      case PL_FORK:
         HIPCHK(c, hipEventRecord(c->fork_ev, c->stream));
         HIPCHK(c, hipStreamWaitEvent(c->side, c->fork_ev, 0));
         break;
-      case 7:
+      case PL_JOIN:
         HIPCHK(c, hipEventRecord(c->join_ev, c->side));
         HIPCHK(c, hipStreamWaitEvent(c->stream, c->join_ev, 0));
         break;
