@@ -387,6 +387,10 @@ def main():
                     choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d", "qronos", "w4a16",
                              "w4a16_decode"])
     ap.add_argument("--rounds", type=int, default=1, help="refinement rounds of the lora_refine workload")
+    ap.add_argument("--pipeline", choices=["batched", "separate"], default="batched",
+                    help="square / single / mlp: one gptq_quantize_batched call per step (Hessian, factor and "
+                         "sweep enqueued together, one host wait at the end), or one call per stage (the factor "
+                         "waits for its pivot status before the sweep is enqueued)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), the reference kernel for "
@@ -466,8 +470,29 @@ def main():
             results.append(r)
         return results
 
+    # the whole-layer entry: every stage of the step's layers enqueued at once;
+    # layers fed by the same input pass it once and share its H and U
+    blayers, firsts = [], {}
+    for s, l in zip(specs, lays):
+        d = dict(W=l["W"], bits=s.bits, group=s.group, block=s.block, lam_rel=s.lam_rel)
+        if s.x_key and s.x_key in firsts:
+            d["H"], d["U"] = firsts[s.x_key]["H"], firsts[s.x_key]["U"]
+        else:
+            d["X"] = l["X"]
+            d["H"] = torch.empty((s.n, s.n), dtype=torch.float32, device=dev)
+            d["U"] = torch.empty((s.n, s.n), dtype=torch.float32, device=dev)
+            if s.x_key:
+                firsts[s.x_key] = d
+        blayers.append(d)
+    batched = args.pipeline == "batched" and args.workload in ("square", "single", "mlp")
+
+    def batched_step(evl=None):
+        ctx.quantize_batched(blayers)
+        return blayers
+
+    step = batched_step if batched else one_step
     for _ in range(args.warmup):
-        one_step()
+        step()
     torch.cuda.synchronize()
     # the Gram dominates every path: bf16 MFMA, or fp64 MFMA for the LoRA paths
     dominant = "k_syrk64" if args.workload in ("lora", "lora_refine") else "k_syrk"
@@ -478,10 +503,16 @@ def main():
     t0 = time.perf_counter()
     last = None
     for k in range(args.steps):
-        last = one_step(evs[k] if args.workload in ("square", "single", "mlp") else None)
+        last = step(evs[k] if args.workload in ("square", "single", "mlp") and not batched else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dom_ms, dom_launches = ctx.kernel_time(dominant)
+    if batched:
+        # stage times from separate calls with events between the stages (untimed steps)
+        ctx.timing(None)
+        for k in range(args.steps):
+            one_step(evs[k])
+        torch.cuda.synchronize()
     # per-kernel breakdown from one more (untimed) step with every launch bracketed
     ctx.timing("*")
     one_step()
@@ -519,7 +550,9 @@ def main():
             "data": "synthetic (seeded; shapes, spectra and outliers of the pages' layers)",
             "config": {"workload": "%s: %s" % (args.workload, ", ".join(
                 "%s W[%d,%d] X[%d,%d] %d-bit g%d B%d" % (s.name, s.out, s.n, s.tokens, s.n, s.bits, s.group, s.block)
-                for s in specs[:4]) + (" ... (%d layers)" % len(specs) if len(specs) > 4 else ""))},
+                for s in specs[:4]) + (" ... (%d layers)" % len(specs) if len(specs) > 4 else "")),
+                       "pipeline": ("one gptq_quantize_batched call per step" if batched else
+                                    "one call per stage")},
             "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "dtypes": "X bf16 -> H fp32 (bf16 MFMA, fp32 accumulate); factor fp64; sweep and trailing fp32"}
     if args.workload in ("square", "single", "mlp"):

@@ -572,7 +572,9 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int ar = tid / TPR, ak = (tid % TPR) * VA;  // E: row, first k
-  const int bk = tid / TPK, bj = (tid % TPK) * VB;  // U: k row, first column
+  // U: k row; the thread's 16-byte chunks are 4 (tid % TPK) + 4 TPK q, so the
+  // TPK threads of a row write consecutive chunks (no bank conflicts)
+  const int bk = tid / TPK, bj = (tid % TPK) * 4;
   const bool arow_ok = ar < mt;
   const float* ap = ly.Eb + (size_t)(i0 + (arow_ok ? ar : 0)) * ly.ldE + eoff;
   const bool evec = (ly.ldE % 4) == 0 && (eoff % 4) == 0;
@@ -614,7 +616,7 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
     const float* bp = ly.U + (size_t)(kb + (kok ? k : 0)) * nt + jj0;
 #pragma unroll
     for (int q = 0; q < VB / 4; ++q) {
-      const int j = bj + 4 * q;
+      const int j = bj + 4 * TPK * q;
       if (uvec && kok && j + 4 <= ntc) {
         rb[q] = *(const f32x4*)(bp + j);
       } else {
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
 #pragma unroll
       for (int u = 0; u < 4; ++u) As[buf][ar][ak + 4 * q + u] = ra[q][u];
 #pragma unroll
-    for (int q = 0; q < VB / 4; ++q) *(f32x4*)&Bs[buf][bk][bj + 4 * q] = rb[q];
+    for (int q = 0; q < VB / 4; ++q) *(f32x4*)&Bs[buf][bk][bj + 4 * TPK * q] = rb[q];
   };
   if (K > 0) {
     load(0);
