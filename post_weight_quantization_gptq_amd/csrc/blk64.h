@@ -27,10 +27,11 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 // step (the estimate is good to about 2^-26, so one step reaches double
 // precision), l = a_j * rs on every lane (lane j: sqrt of the pivot; lanes
 // below: the multipliers; lanes above: values above the diagonal that
-// nothing reads); lane j+1 forms the next pivot from its own multiplier (the
-// same fma as the rank-1 update performs there) and hands it over by
-// readlane, so the serial chain never waits for LDS; the multipliers reach
-// the other lanes through LDS (two alternating rows of broadcast reads).
+// nothing reads).  The multipliers of the next two rows reach every lane by
+// readlane and lane j+1's updated entry is the next pivot (also by
+// readlane), so the serial chain never waits for LDS; the other multipliers
+// go through LDS (two alternating rows of broadcast reads) and their part of
+// the update lands one step later.
 // The steps contain no branch: a failed pivot (not positive or not finite) is
 // recorded and replaced by 1, so the rest stays finite and is discarded.  A
 // scheduling fence ends every step, so the compiler interleaves the next
@@ -43,8 +44,16 @@ struct PanelWave {
   double a[16];
   double dvr;
   int fail;
+  double pl;       // the previous step's multiplier
+  double plk[16];  // its broadcast multipliers of columns >= its column + 3
 };
 
+// Column step C of the sub-panel at c0.  The rank-1 update of columns C+1 and
+// C+2 takes the multipliers of rows J+1 and J+2 by readlane, so the next
+// pivot (lane J+1's updated a[C+1], also by readlane) and the next step's
+// multipliers never wait for LDS.  Columns from C+3 on take theirs through
+// LDS, and that part of the update is applied one step later (the column is
+// first read two steps on), so the LDS latency stays off the serial chain.
 template <int C>
 __device__ __forceinline__ double sub_step(PanelWave& st, double* lb, int r, int c0, double rs) {
   const int J = c0 + C;
@@ -52,22 +61,32 @@ __device__ __forceinline__ double sub_step(PanelWave& st, double* lb, int r, int
   st.a[C] = l;
   st.dvr = (r == J) ? rs : st.dvr;
   double rsn = 0.0;
+  double lk[16];
   if constexpr (C + 1 < 16) {
-    // next pivot from lane J+1's own update (same fma as the rank-1 update)
-    const int J1 = J + 1;
-    const double dn = readlane_f64(st.a[C + 1] - l * l, J1);
+    st.a[C + 1] -= l * readlane_f64(l, J + 1);
+    if constexpr (C + 2 < 16) st.a[C + 2] -= l * readlane_f64(l, J + 2);
+    const double dn = readlane_f64(st.a[C + 1], J + 1);
     const bool ok = dn > 0.0 && __builtin_isfinite(dn);
-    st.fail = (st.fail < 0 && !ok) ? J1 : st.fail;
+    st.fail = (st.fail < 0 && !ok) ? J + 1 : st.fail;
     const double dd = ok ? dn : 1.0;
     rsn = __builtin_amdgcn_rsq(dd);
     rsn = rsn * (1.5 - 0.5 * dd * rsn * rsn);
-    double* row = lb + NB * (C & 1);
-    row[r] = l;
-    double lk[16];
+    if constexpr (C + 3 < 16) {
+      double* row = lb + NB * (C & 1);
+      row[r] = l;
 #pragma unroll
-    for (int t = C + 1; t < 16; ++t) lk[t] = row[c0 + t];
+      for (int t = C + 3; t < 16; ++t) lk[t] = row[c0 + t];
+    }
+  }
+  // the deferred part of the previous step's update (columns >= C + 2)
+  if constexpr (C >= 1 && C + 2 < 16) {
 #pragma unroll
-    for (int t = C + 1; t < 16; ++t) st.a[t] -= l * lk[t];
+    for (int t = C + 2; t < 16; ++t) st.a[t] -= st.pl * st.plk[t];
+  }
+  if constexpr (C + 3 < 16) {
+    st.pl = l;
+#pragma unroll
+    for (int t = C + 3; t < 16; ++t) st.plk[t] = lk[t];
   }
   __builtin_amdgcn_sched_barrier(0);
   return rsn;
