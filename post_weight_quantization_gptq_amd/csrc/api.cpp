@@ -524,8 +524,8 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
       case QK_INIT: LAUNCH(c, "k_init_work", launch_init_work(dL, sg, nseg, l.nwg, c->stream)); break;
       case QK_ROWFIT: LAUNCH(c, "k_rowfit", launch_rowfit(dL, sg, nseg, l.nwg, c->stream)); break;
       case QK_SWEEP: LAUNCH(c, "k_sweep", launch_sweep(l.block, l.mode, dL, sg, nseg, l.nwg, c->stream)); break;
-      case QK_TRAIL:  // beside the sweeps: one workgroup per CU, which leaves room on each CU for a sweep's
-        LAUNCH_ON(c, st, "k_trail", launch_trail(l.block, dL, sg, nseg, l.nwg, l.side ? c->ncu : 0, st));
+      case QK_TRAIL:  // beside the sweeps: a persistent grid of two workgroups per CU
+        LAUNCH_ON(c, st, "k_trail", launch_trail(l.block, dL, sg, nseg, l.nwg, l.side ? 2 * c->ncu : 0, st));
         break;
       case PL_FORK:
         HIPCHK(c, hipEventRecord(c->fork_ev, c->stream));

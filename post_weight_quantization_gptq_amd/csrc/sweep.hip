@@ -537,9 +537,11 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
 // (TS = 128 for the products past a super-block, 64 for the narrow ones
 // inside it), on v_mfma_f32_32x32x2f32 (4 waves of TS/2 x TS/2).  K chunks of
 // 32 go through registers into a double-buffered LDS pair, so the loads of
-// chunk c+1 are in flight while chunk c is multiplied.
+// chunk c+1 are in flight while chunk c is multiplied.  The tile's W is read
+// after the K loop, which keeps the 128-wide tile within 256 registers, so
+// two workgroups share a CU and cover each other's stalls.
 template <int TS>
-__global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, const Seg* __restrict__ segs, int nseg,
+__global__ __launch_bounds__(256, 2) void k_trail(const QLayer* __restrict__ L, const Seg* __restrict__ segs, int nseg,
                                                int ntot) {
   constexpr int KC = 32;
   constexpr int MB = TS / 64;        // 32x32 blocks per wave side
@@ -584,17 +586,6 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
   // the compiler knows, so interleaving them would cost one memory round
   // trip per element).  Global-space loads: they count only against vmcnt.
   float* wbase = ly.Ww + (size_t)i0 * nt + jj0;
-  float cur[MB][MB][16];
-#pragma unroll
-  for (int mi = 0; mi < MB; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < MB; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
-        cur[mi][ni][r] = (i < mt && j < ntc) ? ((const gfloat*)wbase)[(size_t)i * nt + j] : 0.f;
-      }
   f32x4 ra[VA / 4], rb[VB / 4];
   auto load = [&](int kc) {
 #pragma unroll
@@ -666,13 +657,21 @@ __global__ __launch_bounds__(256) void k_trail(const QLayer* __restrict__ L, con
 #pragma unroll
   for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < MB; ++ni)
+    for (int ni = 0; ni < MB; ++ni) {
+      float cur[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
-        if (i < mt && j < ntc) wbase[(size_t)i * nt + j] = cur[mi][ni][r] - acc[mi][ni][r];
+        cur[r] = (i < mt && j < ntc) ? ((const gfloat*)wbase)[(size_t)i * nt + j] : 0.f;
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
+        if (i < mt && j < ntc) wbase[(size_t)i * nt + j] = cur[r] - acc[mi][ni][r];
+      }
+    }
   __syncthreads();  // the next tile refills the LDS pair
   }
 }
