@@ -536,8 +536,8 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
 // pitch is then a multiple of 64): one TS x TS tile per workgroup (TS = 128
 // on 8 waves of 64 x 32, or TS = 64 on 4 waves of 32 x 32), fp64 MFMA
 // 16x16x4.  K chunks of 16 go from global memory straight into an LDS ring
-// (global_load_lds, 16 B per lane; 3 stages for 128-wide tiles, 6 for 64-wide
-// ones), so no register staging and no load latency on the critical path.
+// (global_load_lds, 16 B per lane; 3 stages), so no register staging and no
+// load latency on the critical path.
 //   - k-contiguous operands (L always, and L again as B in the Cholesky
 //     update) sit row-major, 128 B per row and chunk, the 16-byte k-pairs
 //     XOR-swizzled by (row / 2) % 8: a lane reads its two k values with one
@@ -568,9 +568,10 @@ struct RingCfg {
   static constexpr int WGC = NW / 2;            // wave grid 2 x WGC
   static constexpr int WM = TS / 2, WN = TS / WGC;
   static constexpr int MI = WM / 16, NI = WN / 16;
-  // 64-wide tiles compute a stage in about 1000 cycles, 128-wide ones in
-  // about 4000: the narrow ring keeps five stages in flight, the wide one two
-  static constexpr int KC = 16, NST = TS == 128 ? 3 : 6;
+  // three stages (two in flight): for 64-wide tiles that is 48 KB of LDS, so
+  // two workgroups share a CU and cover each other's waits (measured faster
+  // than one workgroup with six stages)
+  static constexpr int KC = 16, NST = 3;
   static constexpr int OPB = TS * KC * 8;       // bytes per operand per stage
   static constexpr int STB = 2 * OPB;
   static constexpr int NQ = OPB / 1024 / NW;    // global_load_lds per operand per wave per stage
