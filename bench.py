@@ -521,7 +521,7 @@ def main():
              "k_gemm64", "k_gemm_ring64", "k_gemm_ring128", "k_make_u", "k_init_work", "k_rowfit", "k_sweep", "k_trail", "k_objective",
              "k_lora_lambda", "k_start_block", "k_dgemm", "k_dsum", "k_gram_chol", "k_apply", "k_lora_assemble",
              "k_lora_extract", "k_ref_init", "k_resid", "k_gfinal", "k_sum_parts", "k_f32_to_f64", "k_f64_to_f32",
-             "k_olrc_out"]
+             "k_olrc_out", "k_ritz", "k_ritz_resid", "k_ritz_conv", "k_cols"]
     breakdown = {}
     for nm in names:
         ms, cnt = ctx.kernel_time(nm)

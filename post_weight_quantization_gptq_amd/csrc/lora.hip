@@ -396,33 +396,49 @@ __global__ __launch_bounds__(256) void k_apply(const double* __restrict__ Z, int
 // lambda_{m+1} / lambda_r instead of lambda_{r+1} / lambda_r.
 
 constexpr int kRitzMax = 128;  // widest subspace
-constexpr int kRitzPitch = kRitzMax + 1;
+constexpr int kRitzPitch = kRitzMax + 2;  // even: 16-byte aligned row pairs
+
+// 1/x, 1/sqrt(x) and sqrt(x) for x > 0 from the hardware estimates and two
+// Newton steps each (the estimates are good to about 2^-23), double precision
+// to a few ulp without the long IEEE sequences on the rotation's serial path
+__device__ __forceinline__ double rcp_f64(double x) {
+  double y = __builtin_amdgcn_rcp(x);
+  y = fma(y, fma(-x, y, 1.0), y);
+  return fma(y, fma(-x, y, 1.0), y);
+}
+__device__ __forceinline__ double rsq_f64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * fma(-0.5 * x * y, y, 1.5);
+  return y * fma(-0.5 * x * y, y, 1.5);
+}
+__device__ __forceinline__ double sqrt_f64(double x) { return x * rsq_f64(x); }
 
 // Eigenpairs of a symmetric positive semidefinite m x m matrix (m <= 128) by
 // one-sided (Hestenes) Jacobi on B = M: rotations of column pairs until all
 // columns are mutually orthogonal, B J = U diag(sigma); for M = M^T >= 0 the
 // singular values are the eigenvalues and U holds the eigenvectors, so no
 // rotation needs to be accumulated.  Sweeps visit all pairs in round-robin
-// rounds of m/2 disjoint pairs (4 lanes per pair, columns in LDS); a pair is
-// rotated when |b_p . b_q| > 1e-15 ||b_p|| ||b_q||; sweeps stop when none is
-// (at most 40).  Writes Y[i][k] (m x m row-major, column k the eigenvector
-// of the k-th largest eigenvalue) and theta[k].  One workgroup of 256.
-__global__ __launch_bounds__(256) void k_ritz(const double* __restrict__ M, int m, double* __restrict__ Y,
-                                              double* __restrict__ theta) {
-  __shared__ double Bc[kRitzMax][kRitzPitch];  // Bc[c][i] = B[i][c]
+// rounds of m/2 disjoint pairs, 16 lanes per pair (8 rows each, read as
+// 16-byte row pairs), the columns in LDS; a pair is rotated when
+// |b_p . b_q| > 1e-15 ||b_p|| ||b_q||; sweeps stop when none is (at most 40).
+// Writes Y[i][k] (m x m row-major, column k the eigenvector of the k-th
+// largest eigenvalue) and theta[k].  One workgroup of 1024.
+__global__ __launch_bounds__(1024) void k_ritz(const double* __restrict__ M, int m, double* __restrict__ Y,
+                                               double* __restrict__ theta) {
+  __shared__ __attribute__((aligned(16))) double Bc[kRitzMax][kRitzPitch];  // Bc[c][i] = B[i][c]
   __shared__ double sig[kRitzMax];
   __shared__ int rotated;
   const int tid = threadIdx.x;
   const int mp = (m + 1) & ~1;  // even number of columns (a zero column pads)
-  for (int e = tid; e < mp * kRitzMax; e += 256) {
+  for (int e = tid; e < mp * kRitzMax; e += 1024) {
     const int c = e / kRitzMax, i = e % kRitzMax;
     Bc[c][i] = (c < m && i < m) ? 0.5 * (M[(size_t)i * m + c] + M[(size_t)c * m + i]) : 0.0;
   }
   if (tid == 0) rotated = 0;
   __syncthreads();
-  const int j = tid >> 2, sub = tid & 3;
+  const int j = tid >> 4, sub = tid & 15;
   const bool act = j < mp / 2;
-  constexpr int RT = kRitzMax / 4;  // rows per lane
+  constexpr int RP = kRitzMax / 32;  // row pairs per lane: rows 2 sub + 32 t, +1
   for (int sweep = 0; sweep < 40; ++sweep) {
     for (int k = 0; k < mp - 1; ++k) {
       if (act) {
@@ -433,35 +449,42 @@ __global__ __launch_bounds__(256) void k_ritz(const double* __restrict__ M, int 
           p = q;
           q = t;
         }
-        double bp[RT], bq[RT];
+        f64x2 bp[RP], bq[RP];
         double al = 0.0, be = 0.0, ga = 0.0;
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          const int i = sub + 4 * t;
-          bp[t] = i < m ? Bc[p][i] : 0.0;
-          bq[t] = i < m ? Bc[q][i] : 0.0;
-          al = fma(bp[t], bp[t], al);
-          be = fma(bq[t], bq[t], be);
-          ga = fma(bp[t], bq[t], ga);
+        for (int t = 0; t < RP; ++t) {
+          // rows past m are zero in LDS (never written), so they add nothing
+          bp[t] = *(const f64x2*)&Bc[p][2 * sub + 32 * t];
+          bq[t] = *(const f64x2*)&Bc[q][2 * sub + 32 * t];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            al = fma(bp[t][u], bp[t][u], al);
+            be = fma(bq[t][u], bq[t][u], be);
+            ga = fma(bp[t][u], bq[t][u], ga);
+          }
         }
 #pragma unroll
-        for (int o = 1; o < 4; o <<= 1) {
+        for (int o = 1; o < 16; o <<= 1) {
           al += __shfl_xor(al, o);
           be += __shfl_xor(be, o);
           ga += __shfl_xor(ga, o);
         }
-        if (fabs(ga) > 1e-15 * sqrt(al) * sqrt(be)) {
-          const double zeta = (be - al) / (2.0 * ga);
-          const double t = fabs(zeta) > 1e100 ? 0.5 / zeta
-                                              : (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-          const double cs = 1.0 / sqrt(1.0 + t * t), sn = cs * t;
+        if (ga * ga > 1e-30 * al * be) {  // |ga| > 1e-15 ||b_p|| ||b_q||
+          const double zeta = (be - al) * rcp_f64(2.0 * ga);
+          const double az = fabs(zeta);
+          const double t = az > 1e100 ? 0.5 * rcp_f64(zeta)
+                                      : (zeta >= 0.0 ? 1.0 : -1.0) * rcp_f64(az + sqrt_f64(1.0 + zeta * zeta));
+          const double cs = rsq_f64(1.0 + t * t), sn = cs * t;
 #pragma unroll
-          for (int u = 0; u < RT; ++u) {
-            const int i = sub + 4 * u;
-            if (i < m) {
-              Bc[p][i] = cs * bp[u] - sn * bq[u];
-              Bc[q][i] = sn * bp[u] + cs * bq[u];
+          for (int u = 0; u < RP; ++u) {
+            f64x2 np, nq;
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+              np[v] = cs * bp[u][v] - sn * bq[u][v];
+              nq[v] = sn * bp[u][v] + cs * bq[u][v];
             }
+            *(f64x2*)&Bc[p][2 * sub + 32 * u] = np;
+            *(f64x2*)&Bc[q][2 * sub + 32 * u] = nq;
           }
           if (sub == 0) rotated = 1;
         }
@@ -670,7 +693,7 @@ int top_subspace(hipStream_t st, const LoraHooks& hk, const std::function<int(co
     if (it >= 1 && (it % kCheck == kCheck - 1 || last)) {  // Q is orthonormal from step 1 on
       DGemm g{Q, 1, m, Z, m, 1, nullptr, m, m, dim, ksplit_for(dim)};  // M = Q^T Z
       if ((rc = dgemm(st, hk, g, b.M, b.S))) return rc;
-      LLAUNCH("k_ritz", k_ritz, dim3(1), dim3(256), 0, st, (const double*)b.M, m, b.Y, b.theta);
+      LLAUNCH("k_ritz", k_ritz, dim3(1), dim3(1024), 0, st, (const double*)b.M, m, b.Y, b.theta);
       DGemm gq{Q, m, 1, b.Y, m, 1, nullptr, dim, m, m, 1};  // Qn = Q Y
       if ((rc = dgemm(st, hk, gq, Qn, b.S))) return rc;
       DGemm gz{Z, m, 1, b.Y, m, 1, nullptr, dim, m, m, 1};  // Zn = Z Y
