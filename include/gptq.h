@@ -127,7 +127,7 @@ int gptq_quantize(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const fl
  * columns absorb the error.  Outputs codes/scales/zeros as gptq_quantize (W^T
  * ~ Q + L R in the pages' convention, i.e. W ~ What + R^T L^T):
  *   L[n][r] fp32: an orthonormal basis of the top-r eigenspace of H (found by
- *                 subspace iteration in fp64 on min(128, n, max(2r, 64))
+ *                 subspace iteration in fp64 on min(128, n, max(r + 32, 64))
  *                 columns with a Rayleigh-Ritz check every 4 steps, stopping
  *                 when ||H L - L diag(theta)||_F <= 1e-11 ||theta||; any basis
  *                 gives the same Q and the same product L R);

@@ -660,7 +660,7 @@ int orth(hipStream_t st, const LoraHooks& hk, const double* Zin, double* Vout, i
 }
 
 // Width of the iterated subspace for the top-r eigenvectors in dimension dim.
-inline int sub_width(int dim, int r) { return std::max(r, std::min({kRitzMax, dim, std::max(2 * r, 64)})); }
+inline int sub_width(int dim, int r) { return std::max(r, std::min({kRitzMax, dim, std::max(r + 32, 64)})); }
 
 // Buffers of one top-subspace computation (dim x m unless noted).
 struct SubBufs {
