@@ -18,11 +18,13 @@
 // on the r Ritz vectors makes V_r orthonormal to rounding.
 // Only span(V_r) matters: Q and the product L R do not depend on the basis.
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
 #include "../../include/gptq.h"
 #include "blk64.h"
+#include "jacobi_order.h"
 #include "common.h"
 #include "launch.h"
 #include "plan.h"
@@ -396,7 +398,10 @@ __global__ __launch_bounds__(256) void k_apply(const double* __restrict__ Z, int
 // lambda_{m+1} / lambda_r instead of lambda_{r+1} / lambda_r.
 
 constexpr int kRitzMax = 128;  // widest subspace
-constexpr int kRitzPitch = kRitzMax + 2;  // even: 16-byte aligned row pairs
+// LDS pitch of a column: even (16-byte aligned row pairs) and 64 bytes off
+// a multiple of 128, so two 4-lane units reading 64 bytes of two columns in
+// one 8-lane phase of a 16-byte read hit disjoint banks
+constexpr int kRitzPitch = kRitzMax + 8;
 
 // 1/x, 1/sqrt(x) and sqrt(x) for x > 0 from the hardware estimates and two
 // Newton steps each (the estimates are good to about 2^-23), double precision
@@ -413,103 +418,218 @@ __device__ __forceinline__ double rsq_f64(double x) {
 }
 __device__ __forceinline__ double sqrt_f64(double x) { return x * rsq_f64(x); }
 
+// Sum over the L (4 or 8) lanes of an aligned group, the same bits on every
+// lane (pairwise sums: lane pairs, quads, then the two quads of a group of 8).
+template <int L>
+__device__ __forceinline__ double lane_sum(double x) {
+  auto mv = [](double v, auto ctrl) {
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)b, decltype(ctrl)::value, 0xF, 0xF, true);
+    const unsigned hi =
+        (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(b >> 32), decltype(ctrl)::value, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+  };
+  x += mv(x, std::integral_constant<int, 0xB1>{});  // quad_perm [1,0,3,2]
+  x += mv(x, std::integral_constant<int, 0x4E>{});  // quad_perm [2,3,0,1]
+  if constexpr (L == 8) x += mv(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  return x;
+}
+
+// This lane's part of ||x||^2 over its T row pairs (even and odd rows
+// summed apart, then added).
+template <int T>
+__device__ __forceinline__ double sqnorm(const f64x2 (&x)[T]) {
+  double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    s0 = fma(x[t][0], x[t][0], s0);
+    s1 = fma(x[t][1], x[t][1], s1);
+  }
+  return s0 + s1;
+}
+
 // Eigenpairs of a symmetric positive semidefinite m x m matrix (m <= 128) by
 // one-sided (Hestenes) Jacobi on B = M: rotations of column pairs until all
 // columns are mutually orthogonal, B J = U diag(sigma); for M = M^T >= 0 the
 // singular values are the eigenvalues and U holds the eigenvectors, so no
-// rotation needs to be accumulated.  Sweeps visit all pairs in round-robin
-// rounds of m/2 disjoint pairs, 16 lanes per pair (8 rows each, read as
-// 16-byte row pairs), the columns in LDS; a pair is rotated when
-// |b_p . b_q| > 1e-15 ||b_p|| ||b_q||; sweeps stop when none is (at most 40).
-// Writes Y[i][k] (m x m row-major, column k the eigenvector of the k-th
-// largest eigenvalue) and theta[k].  One workgroup of 1024.
-__global__ __launch_bounds__(1024) void k_ritz(const double* __restrict__ M, int m, double* __restrict__ Y,
-                                               double* __restrict__ theta) {
+// rotation needs to be accumulated.  Each unit of L lanes holds its two
+// columns in registers (lane sub: rows 2 sub + 2 L t and the next, t < T);
+// between rounds a column that changes units goes through its home slot in
+// LDS, written only when it was rotated since it was read, and the schedule
+// above keeps that to about one column per unit and round (one barrier per
+// round).  A pair is rotated when |b_p . b_q| > 1e-15 ||b_p|| ||b_q||
+// (p < q); sweeps stop when none is (at most 40).  Writes Y[i][k] (m x m
+// row-major, column k the eigenvector of the k-th largest eigenvalue) and
+// theta[k].  One workgroup of L lanes per column pair (at most 512).
+constexpr int kRitzSweeps = 40;
+template <int L, int T>
+__global__ __launch_bounds__(512) void k_ritz(const double* __restrict__ M, int m, double* __restrict__ Y,
+                                              double* __restrict__ theta) {
   __shared__ __attribute__((aligned(16))) double Bc[kRitzMax][kRitzPitch];  // Bc[c][i] = B[i][c]
   __shared__ double sig[kRitzMax];
-  __shared__ int rotated;
-  const int tid = threadIdx.x;
+  __shared__ int rank_of[kRitzMax];
+  __shared__ int rotated[kRitzSweeps];
+  // the sweep's schedule, [round][unit] = a | b << 8 (0xffff: idle); at most
+  // mp <= kRitzMax rounds of mp / 2 units
+  __shared__ unsigned short sched[kRitzMax * kRitzMax / 2];
+  const int tid = threadIdx.x, nth = blockDim.x;
   const int mp = (m + 1) & ~1;  // even number of columns (a zero column pads)
-  for (int e = tid; e < mp * kRitzMax; e += 1024) {
+  const int h = mp / 2, R = ritz_rounds(mp);
+  for (int e = tid; e < mp * kRitzMax; e += nth) {
     const int c = e / kRitzMax, i = e % kRitzMax;
     Bc[c][i] = (c < m && i < m) ? 0.5 * (M[(size_t)i * m + c] + M[(size_t)c * m + i]) : 0.0;
   }
-  if (tid == 0) rotated = 0;
+  for (int e = tid; e < R * h; e += nth) {
+    int sa, sb;
+    ritz_assign(mp, e / h, e % h, sa, sb);
+    sched[e] = sa < 0 ? 0xffff : (unsigned short)(sa | sb << 8);
+  }
+  if (tid < kRitzSweeps) rotated[tid] = 0;
   __syncthreads();
-  const int j = tid >> 4, sub = tid & 15;
-  const bool act = j < mp / 2;
-  constexpr int RP = kRitzMax / 32;  // row pairs per lane: rows 2 sub + 32 t, +1
-  for (int sweep = 0; sweep < 40; ++sweep) {
-    for (int k = 0; k < mp - 1; ++k) {
-      if (act) {
-        int p = j == 0 ? 0 : 1 + ((j - 1 + k) % (mp - 1));
-        int q = 1 + ((mp - 2 - j + k) % (mp - 1));
-        if (p > q) {
-          const int t = p;
-          p = q;
-          q = t;
+  const int u = tid / L, sub = tid % L;
+  f64x2 x0[T] = {}, x1[T] = {};  // the unit's columns a (x0) and b (x1)
+  auto slot = [&](int ri, int& sa, int& sb) {
+    const unsigned v = u < h ? sched[ri * h + u] : 0xffffu;
+    sa = v == 0xffffu ? -1 : (int)(v & 0xff);
+    sb = v == 0xffffu ? -1 : (int)(v >> 8);
+  };
+  int a, b;
+  slot(0, a, b);
+  bool d0 = false, d1 = false;  // the column differs from its home copy
+  if (a >= 0) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      x0[t] = *(const f64x2*)&Bc[a][2 * sub + 2 * L * t];
+      x1[t] = *(const f64x2*)&Bc[b][2 * sub + 2 * L * t];
+    }
+  }
+  double n0 = 0.0;     // ||x0||^2, carried into the next round when x0 stays
+  bool n0ok = false;
+  for (int sweep = 0; sweep < kRitzSweeps; ++sweep) {
+    for (int ri = 0; ri < R; ++ri) {
+      if (a >= 0) {
+        // two accumulators per sum (rows 2 sub + 2 L t and the next) halve
+        // the dependent chain
+        double n1a = 0.0, n1b = 0.0, gaa = 0.0, gab = 0.0;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          n1a = fma(x1[t][0], x1[t][0], n1a);
+          n1b = fma(x1[t][1], x1[t][1], n1b);
+          gaa = fma(x0[t][0], x1[t][0], gaa);
+          gab = fma(x0[t][1], x1[t][1], gab);
         }
-        f64x2 bp[RP], bq[RP];
-        double al = 0.0, be = 0.0, ga = 0.0;
+        if (!n0ok) n0 = lane_sum<L>(sqnorm<T>(x0));
+        const double n1 = lane_sum<L>(n1a + n1b);
+        const double ga = lane_sum<L>(gaa + gab);
+        if (ga * ga > 1e-30 * n0 * n1) {  // |ga| > 1e-15 ||b_a|| ||b_b||
+          // rotation of (p, q) = (min, max) of (a, b): b_p' = c b_p - s b_q,
+          // b_q' = s b_p + c b_q, with tan = t zeroing their product
+          // t = 2 ga sign(d) / (|d| + sqrt(d^2 + 4 ga^2)), d = be - al: the
+          // smaller root of t^2 + 2 zeta t - 1 = 0, zeta = d / (2 ga).  t needs
+          // only near double precision (a slightly-off angle is fixed by the
+          // next sweep); c = 1/sqrt(1 + t^2) is exact to rounding, so (c, s)
+          // stays an orthogonal rotation and no column is rescaled.
+          const bool ap = a < b;
+          const double d = ap ? n1 - n0 : n0 - n1, g2 = 2.0 * ga;
+          const double rr = fma(d, d, g2 * g2);
+          double y = __builtin_amdgcn_rsq(rr);
+          y = y * fma(-0.5 * rr * y, y, 1.5);
+          const double den = fabs(d) + rr * y;
+          double w = __builtin_amdgcn_rcp(den);
+          w = fma(w, fma(-den, w, 1.0), w);
+          const double tn = (d >= 0.0 ? g2 : -g2) * w;
+          const double cs = rsq_f64(fma(tn, tn, 1.0)), sn = cs * tn, s0 = ap ? sn : -sn;
 #pragma unroll
-        for (int t = 0; t < RP; ++t) {
-          // rows past m are zero in LDS (never written), so they add nothing
-          bp[t] = *(const f64x2*)&Bc[p][2 * sub + 32 * t];
-          bq[t] = *(const f64x2*)&Bc[q][2 * sub + 32 * t];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            al = fma(bp[t][u], bp[t][u], al);
-            be = fma(bq[t][u], bq[t][u], be);
-            ga = fma(bp[t][u], bq[t][u], ga);
-          }
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          al += __shfl_xor(al, o);
-          be += __shfl_xor(be, o);
-          ga += __shfl_xor(ga, o);
-        }
-        if (ga * ga > 1e-30 * al * be) {  // |ga| > 1e-15 ||b_p|| ||b_q||
-          const double zeta = (be - al) * rcp_f64(2.0 * ga);
-          const double az = fabs(zeta);
-          const double t = az > 1e100 ? 0.5 * rcp_f64(zeta)
-                                      : (zeta >= 0.0 ? 1.0 : -1.0) * rcp_f64(az + sqrt_f64(1.0 + zeta * zeta));
-          const double cs = rsq_f64(1.0 + t * t), sn = cs * t;
-#pragma unroll
-          for (int u = 0; u < RP; ++u) {
-            f64x2 np, nq;
+          for (int t = 0; t < T; ++t)
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
-              np[v] = cs * bp[u][v] - sn * bq[u][v];
-              nq[v] = sn * bp[u][v] + cs * bq[u][v];
+              const double p = x0[t][v], q = x1[t][v];
+              x0[t][v] = cs * p - s0 * q;
+              x1[t][v] = cs * q + s0 * p;
             }
-            *(f64x2*)&Bc[p][2 * sub + 32 * u] = np;
-            *(f64x2*)&Bc[q][2 * sub + 32 * u] = nq;
-          }
-          if (sub == 0) rotated = 1;
+          d0 = d1 = true;
+          n0ok = false;
+          if (sub == 0) rotated[sweep] = 1;
         }
       }
+      // hand over: changed columns leaving the unit go home, then the
+      // arrivals are read.  Inside a cross level a unit keeps x0 and swaps
+      // x1 (the common case, no selects); level changes take the general way.
+      int na, nb;
+      slot(ri + 1 < R ? ri + 1 : 0, na, nb);
+      const bool same0 = a >= 0 && na == a && nb != b;
+      if (same0) {
+        if (d1)
+#pragma unroll
+          for (int t = 0; t < T; ++t) *(f64x2*)&Bc[b][2 * sub + 2 * L * t] = x1[t];
+        if (!n0ok) n0 = lane_sum<L>(sqnorm<T>(x0));  // overlaps the wait below
+        n0ok = true;
+      } else if (a >= 0) {
+        const bool keep0 = a == na || a == nb, keep1 = b == na || b == nb;
+        if (!keep0 && d0)
+#pragma unroll
+          for (int t = 0; t < T; ++t) *(f64x2*)&Bc[a][2 * sub + 2 * L * t] = x0[t];
+        if (!keep1 && d1)
+#pragma unroll
+          for (int t = 0; t < T; ++t) *(f64x2*)&Bc[b][2 * sub + 2 * L * t] = x1[t];
+      }
       __syncthreads();
+      if (same0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) x1[t] = *(const f64x2*)&Bc[nb][2 * sub + 2 * L * t];
+        d1 = false;
+      } else if (na >= 0) {
+        // new x0 = column na, new x1 = column nb, each kept or read
+        const bool s0a = na == a, s1a = na == b, s0b = nb == a, s1b = nb == b;
+        const bool e0 = s0a ? d0 : s1a && d1, e1 = s0b ? d0 : s1b && d1;
+        d0 = e0;
+        d1 = e1;
+        n0ok = false;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const f64x2 o0 = x0[t], o1 = x1[t];
+          x0[t] = s0a ? o0 : s1a ? o1 : *(const f64x2*)&Bc[na][2 * sub + 2 * L * t];
+          x1[t] = s0b ? o0 : s1b ? o1 : *(const f64x2*)&Bc[nb][2 * sub + 2 * L * t];
+        }
+      }
+      a = na;
+      b = nb;
     }
-    const bool again = rotated != 0;
-    __syncthreads();
-    if (!again) break;
-    if (tid == 0) rotated = 0;
-    __syncthreads();
+    if (rotated[sweep] == 0) break;  // read after the last round's barrier; set before it
   }
-  if (tid < m) {
-    double s = 0.0;
-    for (int i = 0; i < m; ++i) s = fma(Bc[tid][i], Bc[tid][i], s);
-    sig[tid] = sqrt(s);
+  // the units hold every column (round 0 pairs them all): norms and home copies
+  if (a >= 0) {
+    double n0 = 0.0, n1 = 0.0;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        n0 = fma(x0[t][v], x0[t][v], n0);
+        n1 = fma(x1[t][v], x1[t][v], n1);
+      }
+      if (d0) *(f64x2*)&Bc[a][2 * sub + 2 * L * t] = x0[t];
+      if (d1) *(f64x2*)&Bc[b][2 * sub + 2 * L * t] = x1[t];
+    }
+    n0 = lane_sum<L>(n0);
+    n1 = lane_sum<L>(n1);
+    if (sub == 0) {
+      if (a < m) sig[a] = sqrt(n0);
+      if (b < m) sig[b] = sqrt(n1);
+    }
   }
   __syncthreads();
   if (tid < m) {
     const double sc = sig[tid];
     int rank = 0;
     for (int d = 0; d < m; ++d) rank += (sig[d] > sc || (sig[d] == sc && d < tid)) ? 1 : 0;
+    rank_of[tid] = rank;
     theta[rank] = sc;
-    const double inv = sc > 0.0 ? 1.0 / sc : 0.0;
-    for (int i = 0; i < m; ++i) Y[(size_t)i * m + rank] = Bc[tid][i] * inv;
+  }
+  __syncthreads();
+  for (int e = tid; e < m * m; e += nth) {
+    const int i = e / m, c = e % m;
+    const double sc = sig[c];
+    Y[(size_t)i * m + rank_of[c]] = sc > 0.0 ? Bc[c][i] / sc : 0.0;
   }
 }
 
@@ -659,6 +779,29 @@ int orth(hipStream_t st, const LoraHooks& hk, const double* Zin, double* Vout, i
   return 0;
 }
 
+// k_ritz<L, T> for m <= kRitzMax: L lanes per column pair, T = ceil(m / 2L)
+// row pairs per lane.
+template <int L, int T>
+int ritz_launch(hipStream_t st, const LoraHooks& hk, const double* M, int m, double* Y, double* theta, int t) {
+  if constexpr (T > kRitzMax / (2 * L)) {
+    return GPTQ_ERR_UNSUPPORTED;
+  } else {
+    if (t != T) return ritz_launch<L, T + 1>(st, hk, M, m, Y, theta, t);
+    const int nth = 64 * cdivl(L * ((m + 1) / 2), 64);
+    const auto kern = k_ritz<L, T>;
+    int rc;
+    LLAUNCH("k_ritz", kern, dim3(1), dim3(nth), 0, st, M, m, Y, theta);
+    return 0;
+  }
+}
+#ifndef RITZ_LANES
+#define RITZ_LANES 8
+#endif
+int ritz(hipStream_t st, const LoraHooks& hk, const double* M, int m, double* Y, double* theta) {
+  constexpr int L = RITZ_LANES;
+  return ritz_launch<L, 1>(st, hk, M, m, Y, theta, cdivl(m, 2 * L));
+}
+
 // Width of the iterated subspace for the top-r eigenvectors in dimension dim.
 inline int sub_width(int dim, int r) { return std::max(r, std::min({kRitzMax, dim, std::max(r + 32, 64)})); }
 
@@ -693,7 +836,7 @@ int top_subspace(hipStream_t st, const LoraHooks& hk, const std::function<int(co
     if (it >= 1 && (it % kCheck == kCheck - 1 || last)) {  // Q is orthonormal from step 1 on
       DGemm g{Q, 1, m, Z, m, 1, nullptr, m, m, dim, ksplit_for(dim)};  // M = Q^T Z
       if ((rc = dgemm(st, hk, g, b.M, b.S))) return rc;
-      LLAUNCH("k_ritz", k_ritz, dim3(1), dim3(1024), 0, st, (const double*)b.M, m, b.Y, b.theta);
+      if ((rc = ritz(st, hk, b.M, m, b.Y, b.theta))) return rc;
       DGemm gq{Q, m, 1, b.Y, m, 1, nullptr, dim, m, m, 1};  // Qn = Q Y
       if ((rc = dgemm(st, hk, gq, Qn, b.S))) return rc;
       DGemm gz{Z, m, 1, b.Y, m, 1, nullptr, dim, m, m, 1};  // Zn = Z Y
