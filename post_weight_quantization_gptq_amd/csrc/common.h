@@ -112,6 +112,23 @@ struct QLayer {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+// Typed global and LDS views of generic pointers (for pointers read out of
+// descriptors, which the compiler cannot prove global): accesses through a
+// global view compile to global_* instructions, whose completion is counted
+// by vmcnt alone, so waits for LDS results stay precise.
+template <class T>
+using gptr = __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ gptr<T> glb(T* p) {
+  return (gptr<T>)p;
+}
+template <class T>
+using lptr = __attribute__((address_space(3))) T*;
+template <class T>
+__device__ __forceinline__ lptr<T> lds_view(T* p) {
+  return (lptr<T>)p;
+}
+
 // global-memory views: loads through them count only against vmcnt (a
 // generic pointer's flat loads also count against lgkmcnt, which LDS waits
 // would then have to drain)

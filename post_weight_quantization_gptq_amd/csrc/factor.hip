@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
   const bool yrole = g >= nb - k;                 // Y_kj for column block j
   const int i = yrole ? k : k + g, j = yrole ? g - (nb - k) : 0;
   const int tid = threadIdx.x;
-  double* A = pb.A;
+  gptr<double> A = glb(pb.A);
   const int r0 = i * NB, mr = yrole ? m : ((i == k) ? 0 : min(NB, n - r0));
   {
     // both 64x64 blocks: 16 + 16 loads per thread, all in flight together
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
       const int e = tid + 256 * q, r = e >> 6, c = e & 63;  // coalesced over c
       ta[q] = (r < m && c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
       if (yrole)
-        tr[q] = (r < m) ? pb.Y[(size_t)(k0 + r) * n + NB * j + c] : 0.0;
+        tr[q] = (r < m) ? glb(pb.Y)[(size_t)(k0 + r) * n + NB * j + c] : 0.0;
       else
         tr[q] = (r < mr && c < m) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0;
     }
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
     const int wz = P1 - k0;  // 64 .. 256 columns
     for (int e = tid; e < NB * wz; e += 256) {
       const int r = e / wz, c = e % wz;
-      if (r < m) pb.Y[(size_t)(k0 + r) * n + k0 + c] = (c < m && c <= r) ? Ys[r][c] : 0.0;
+      if (r < m) glb(pb.Y)[(size_t)(k0 + r) * n + k0 + c] = (c < m && c <= r) ? Ys[r][c] : 0.0;
     }
     return;
   }
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
     blk_mma<false>(acc, Ys, Rs);
   else
     blk_mma<true>(acc, Rs, Ys);
-  double* out = yrole ? pb.Y + (size_t)k0 * n + NB * j : A + (size_t)r0 * n + k0;
+  gptr<double> out = yrole ? glb(pb.Y) + (size_t)k0 * n + NB * j : A + (size_t)r0 * n + k0;
   const int mc = yrole ? NB : m;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -198,8 +198,8 @@ __global__ __launch_bounds__(256) void k_chol_panel2(const FacProb* __restrict__
   const bool yrole = g >= nb - k;
   const int i = yrole ? k : k + g, j = yrole ? g - (nb - k) : 0;
   const int tid = threadIdx.x;
-  double* A = pb.A;
-  double* Y = pb.Y;
+  gptr<double> A = glb(pb.A);
+  gptr<double> Y = glb(pb.Y);
   const int r0 = i * NB, mr = min(NB, n - r0);
   const bool own = yrole || i >= k + 2;
   // loads: the pair's diagonal region and this group's two blocks
@@ -357,9 +357,9 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
   if (*pb.info != 0 || *pb.nonfinite != 0) return;
   const int n = pb.n;
   const int t = blockIdx.x - sg.wg0;
-  const double* A;
-  const double* B;
-  double* C;
+  gptr<const double> A;
+  gptr<const double> B;
+  gptr<double> C;
   long long lda, sbk, sbj, ldc;
   int mt, nt, kb, ke;
   double alpha, beta;
@@ -375,12 +375,12 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
     }
     const int a = b + tt;
     const int i0 = c0 + TS * a, j0 = c0 + TS * b;
-    A = pb.A + (size_t)i0 * n + kb0;
+    A = glb((const double*)pb.A) + (size_t)i0 * n + kb0;
     lda = n;
-    B = pb.A + (size_t)j0 * n + kb0;
+    B = glb((const double*)pb.A) + (size_t)j0 * n + kb0;
     sbk = 1;
     sbj = n;
-    C = pb.A + (size_t)i0 * n + j0;
+    C = glb(pb.A) + (size_t)i0 * n + j0;
     ldc = n;
     mt = min(TS, n - i0);
     nt = min(TS, c1 - j0);
@@ -393,12 +393,12 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
     const int kb0 = sg.b, kw = sg.c, r0 = sg.d, r1 = sg.e;
     const int ncol = (kb0 + kw + TS - 1) / TS;
     const int i0 = r0 + TS * (t / ncol), j0 = TS * (t % ncol);
-    A = pb.A + (size_t)i0 * n + kb0;
+    A = glb((const double*)pb.A) + (size_t)i0 * n + kb0;
     lda = n;
-    B = pb.Y + (size_t)kb0 * n + j0;
+    B = glb((const double*)pb.Y) + (size_t)kb0 * n + j0;
     sbk = n;
     sbj = 1;
-    C = pb.Y + (size_t)i0 * n + j0;
+    C = glb(pb.Y) + (size_t)i0 * n + j0;
     ldc = n;
     mt = min(TS, r1 - i0);
     nt = min(TS, kb0 + kw - j0);
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
   const int kr = tid / TPK, jq = (tid % TPK) * 4;
   auto load = [&](int k0) {
     const bool rok = lr < mt;
-    const double* ap = A + (size_t)(rok ? lr : 0) * lda;
+    gptr<const double> ap = A + (size_t)(rok ? lr : 0) * lda;
 #pragma unroll
     for (int h = 0; h < NQ; ++h)
 #pragma unroll
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
     if (sbj == 1) {
       const int kk = k0 + kr;
       const bool kok = kk < ke;
-      const double* bp = B + (size_t)(kok ? kk : kb) * sbk;
+      gptr<const double> bp = B + (size_t)(kok ? kk : kb) * sbk;
 #pragma unroll
       for (int h = 0; h < NQ; ++h)
 #pragma unroll
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void k_gemm(const FacProb* __restrict__ probs,
         }
     } else {
       const bool jok = lr < nt;
-      const double* bp = B + (size_t)(jok ? lr : 0) * sbj;
+      gptr<const double> bp = B + (size_t)(jok ? lr : 0) * sbj;
 #pragma unroll
       for (int h = 0; h < NQ; ++h)
 #pragma unroll
@@ -591,7 +591,7 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
   const int t = vt - sg.wg0;
   const double* A;
   const double* B;
-  double* C;
+  gptr<double> C;  // a global view: its accesses stay off lgkmcnt
   long long lda, ldb, ldc;  // ldb: pitch between B's k-contiguous rows (j) or k rows
   bool bkc;                 // B k-contiguous
   int mt, nt, kb, ke;
@@ -609,7 +609,7 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
     B = pb.A + (size_t)j0 * n + kb0;
     lda = ldb = n;
     bkc = true;
-    C = pb.A + (size_t)i0 * n + j0;
+    C = glb(pb.A) + (size_t)i0 * n + j0;
     ldc = n;
     mt = min(TS, n - i0);
     nt = min(TS, c1 - j0);
@@ -625,7 +625,7 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
     B = pb.Y + (size_t)j0 * n;
     lda = ldb = n;
     bkc = true;
-    C = pb.C + (size_t)i0 * n + j0;
+    C = glb(pb.C) + (size_t)i0 * n + j0;
     ldc = n;
     mt = min(TS, M - i0);
     nt = min(TS, N - j0);
@@ -645,7 +645,7 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
     B = pb.Y + (size_t)kb0 * n + j0;
     ldb = n;
     bkc = false;
-    C = pb.Y + (size_t)i0 * n + j0;
+    C = glb(pb.Y) + (size_t)i0 * n + j0;
     ldc = n;
     mt = min(TS, r1 - i0);
     nt = min(TS, kb0 + kw - j0);
@@ -707,7 +707,7 @@ __device__ __forceinline__ void ring_tile(const FacProb* __restrict__ probs, con
       for (int r = 0; r < 4; ++r) {
         const int i = wr * C_::WM + 16 * mi + g + 4 * r;
         const int j = wc * C_::WN + 16 * ni + li;
-        cur[mi][ni][r] = (beta != 0.0 && i < mt && j < nt) ? ((const gdouble*)C)[(size_t)i * ldc + j] : 0.0;
+        cur[mi][ni][r] = (beta != 0.0 && i < mt && j < nt) ? C[(size_t)i * ldc + j] : 0.0;
       }
 #pragma unroll
   for (int q = 0; q < NST - 1; ++q)

@@ -81,14 +81,14 @@ struct SweepState {
 };
 
 struct SweepCtx {
-  const float* Us;     // LDS U block
-  const float* Wwrow;  // working row (global), columns past the super-block
-  const float* Wsrow;  // the row's columns of the super-block in LDS, indexed by column - sb0
+  lptr<const float> Us;     // LDS U block
+  gptr<const float> Wwrow;  // working row (global), columns past the super-block
+  lptr<const float> Wsrow;  // the row's columns of the super-block in LDS, indexed by column - sb0
   float maxq;
   int B, bw, b0, G, l16, rv;
   int sb0, sb1;        // the super-block's columns [sb0, sb1)
-  float* scales;
-  uint8_t* zeros;
+  gptr<float> scales;
+  gptr<uint8_t> zeros;
   size_t grow;  // row offset into scales/zeros
 };
 
@@ -166,7 +166,7 @@ __device__ __forceinline__ void sweep_owner(SweepState<CPL>& st, const SweepCtx&
     const int j = O * CPL + c;
     float unext[CPL];
     if (j + 1 < B) {
-      const float* un = cx.Us + (j + 1) * B + CPL * cx.l16;
+      lptr<const float> un = cx.Us + (j + 1) * B + CPL * cx.l16;
 #pragma unroll
       for (int v = 0; v < CPL; ++v) unext[v] = un[v];
     }
@@ -277,9 +277,9 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
       const int j = idx / (B / 4), k4 = (idx % (B / 4)) * 4;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (idx < B * B / 4 && j < bwr) {
-        const float* src = ly.U + (size_t)(b0r + j) * nt + c0 + k4;
+        gptr<const float> src = glb(ly.U) + (size_t)(b0r + j) * nt + c0 + k4;
         if (vec) {
-          v = *(const f32x4*)src;
+          v = *(gptr<const f32x4>)src;
         } else {
 #pragma unroll
           for (int u = 0; u < 4; ++u) v[u] = (k4 + u < cw) ? src[u] : 0.f;
@@ -305,9 +305,9 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
       const int gr = r0 + r;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (gr < ly.out) {
-        const float* src = ly.Ww + (size_t)gr * nt + sb0 + c4;
+        gptr<const float> src = glb((const float*)ly.Ww) + (size_t)gr * nt + sb0 + c4;
         if (vec) {
-          v = *(const f32x4*)src;
+          v = *(gptr<const f32x4>)src;
         } else {
 #pragma unroll
           for (int u = 0; u < 4; ++u) v[u] = (c4 + u < sbw) ? src[u] : 0.f;
@@ -319,22 +319,22 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   load_u(sb0, min(B, ly.n - sb0), sb0, min(B, ly.n - sb0), B);
   double obj_e = 0.0, obj_d = 0.0;
   if (rv && l16 == 0) {
-    obj_e = ly.objp[(size_t)row * 2];
-    obj_d = ly.objp[(size_t)row * 2 + 1];
+    obj_e = glb(ly.objp)[(size_t)row * 2];
+    obj_d = glb(ly.objp)[(size_t)row * 2 + 1];
   }
   SweepState<CPL> st;
   st.g = Grid{1.f, 1.f, 0.f};
   if (rv && (G == 0 || (sb0 % G) != 0)) {
     // the row's grid, or the grid of a group that began in an earlier super-block
     const size_t gi = (size_t)row * ly.ng + (G ? sb0 / G : 0);
-    st.g.s = ly.scales[gi];
+    st.g.s = glb(ly.scales)[gi];
     st.g.r = 1.f / st.g.s;
-    st.g.z = (float)ly.zeros[gi];
+    st.g.z = (float)glb(ly.zeros)[gi];
   }
   SweepCtx cx;
-  cx.Us = Us;
-  cx.Wwrow = ly.Ww + (size_t)(rv ? row : 0) * nt;
-  cx.Wsrow = lds.ws + rr * LD::WP;
+  cx.Us = lds_view((const float*)Us);
+  cx.Wwrow = glb((const float*)ly.Ww) + (size_t)(rv ? row : 0) * nt;
+  cx.Wsrow = lds_view((const float*)lds.ws) + rr * LD::WP;
   cx.maxq = (float)((1 << ly.bits) - 1);
   cx.B = B;
   cx.G = G;
@@ -342,8 +342,8 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   cx.rv = rv;
   cx.sb0 = sb0;
   cx.sb1 = sb1;
-  cx.scales = ly.scales;
-  cx.zeros = ly.zeros;
+  cx.scales = glb(ly.scales);
+  cx.zeros = glb(ly.zeros);
   cx.grow = (size_t)(rv ? row : 0) * ly.ng;
   double se = 0.0, sd = 0.0;  // this lane's sums over the super-block, in block order
   // the next block's per-column inputs, loaded ahead (their latency hides
@@ -355,9 +355,9 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
     for (int c = 0; c < CPL; ++c) {
       const int lc = CPL * l16 + c;
       const bool in = rv && lc < bw;
-      pdv[c] = (lc < bw) ? ly.dinv[b0 + lc] : 0.f;
-      pwo[c] = (in && !BID) ? ly.W[(size_t)row * ly.n + b0 + lc] : 0.f;
-      pqv[c] = (in && BID) ? (float)ly.codes[(size_t)row * ly.n + b0 + lc] : 0.f;
+      pdv[c] = (lc < bw) ? glb(ly.dinv)[b0 + lc] : 0.f;
+      pwo[c] = (in && !BID) ? glb(ly.W)[(size_t)row * ly.n + b0 + lc] : 0.f;
+      pqv[c] = (in && BID) ? (float)glb(ly.codes)[(size_t)row * ly.n + b0 + lc] : 0.f;
     }
   };
   // a whole B x B diagonal block of U straight into LDS (pitch B), 1 KB per
@@ -407,9 +407,9 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
       const int lc = CPL * l16 + c;
       lds.es[rr * LD::EP + lc] = st.ev[c];  // zero past bw (the sweep leaves ev = 0 there)
       if (rv && lc < bw) {
-        ly.codes[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
-        ly.Eb[((size_t)((blk / ly.sbk) & 1) * ly.out + row) * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
-        if (ly.err) ly.err[(size_t)row * ly.n + b0 + lc] = st.ev[c];
+        glb(ly.codes)[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
+        glb(ly.Eb)[((size_t)((blk / ly.sbk) & 1) * ly.out + row) * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
+        if (ly.err) glb(ly.err)[(size_t)row * ly.n + b0 + lc] = st.ev[c];
         if (BID) {
           se += (double)st.hv[c];
         } else {
@@ -453,9 +453,9 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
         const bool full = uvec && col + 4 <= sb1;
 #pragma unroll
         for (int kk = 0; kk < KH; ++kk) {
-          const float* src = ly.U + (size_t)(b0 + KQ * g + KH * h + kk) * nt + col;
+          gptr<const float> src = glb(ly.U) + (size_t)(b0 + KQ * g + KH * h + kk) * nt + col;
           if (full) {
-            ub[kk] = *(const __attribute__((address_space(1))) f32x4*)src;
+            ub[kk] = *(gptr<const f32x4>)src;
           } else {
 #pragma unroll
             for (int u = 0; u < 4; ++u) ub[kk][u] = (col + u < sb1) ? src[u] : 0.f;
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   }
   if (rv && l16 == 0) {
     // per-row sums, accumulated over the super-blocks in order
-    double* op = ly.objp + (size_t)row * 2;
+    gptr<double> op = glb(ly.objp) + (size_t)row * 2;
     op[0] = obj_e + se;
     op[1] = obj_d + sd;
   }
@@ -578,21 +578,23 @@ __global__ __launch_bounds__(256, 2) void k_trail(const QLayer* __restrict__ L, 
   // TPK threads of a row write consecutive chunks (no bank conflicts)
   const int bk = tid / TPK, bj = (tid % TPK) * 4;
   const bool arow_ok = ar < mt;
-  const float* ap = ly.Eb + (size_t)(i0 + (arow_ok ? ar : 0)) * ly.ldE + eoff;
+  gptr<const float> ap = glb((const float*)ly.Eb) + (size_t)(i0 + (arow_ok ? ar : 0)) * ly.ldE + eoff;
   const bool evec = (ly.ldE % 4) == 0 && (eoff % 4) == 0;
   const bool uvec = (nt % 4) == 0 && (jj0 % 4) == 0 && (((uintptr_t)ly.U) & 15) == 0;
   // The tile's W, loaded first so its latency hides behind the K loop, and
   // all of it before any store (the stores could alias the loads as far as
   // the compiler knows, so interleaving them would cost one memory round
-  // trip per element).  Global-space loads: they count only against vmcnt.
-  float* wbase = ly.Ww + (size_t)i0 * nt + jj0;
+  // trip per element).  Every global access goes through a global view: a
+  // generic pointer's flat accesses also count against lgkmcnt, so the LDS
+  // waits of the K loop would drain the next chunk's loads with them.
+  gptr<float> wbase = glb(ly.Ww) + (size_t)i0 * nt + jj0;
   f32x4 ra[VA / 4], rb[VB / 4];
   auto load = [&](int kc) {
 #pragma unroll
     for (int q = 0; q < VA / 4; ++q) {
       const int k = kc + ak + 4 * q;
       if (evec && arow_ok && k + 4 <= K) {
-        ra[q] = *(const f32x4*)(ap + k);
+        ra[q] = *(gptr<const f32x4>)(ap + k);
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -604,12 +606,12 @@ __global__ __launch_bounds__(256, 2) void k_trail(const QLayer* __restrict__ L, 
     }
     const int k = kc + bk;
     const bool kok = k < K;
-    const float* bp = ly.U + (size_t)(kb + (kok ? k : 0)) * nt + jj0;
+    gptr<const float> bp = glb(ly.U) + (size_t)(kb + (kok ? k : 0)) * nt + jj0;
 #pragma unroll
     for (int q = 0; q < VB / 4; ++q) {
       const int j = bj + 4 * TPK * q;
       if (uvec && kok && j + 4 <= ntc) {
-        rb[q] = *(const f32x4*)(bp + j);
+        rb[q] = *(gptr<const f32x4>)(bp + j);
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -663,7 +665,7 @@ __global__ __launch_bounds__(256, 2) void k_trail(const QLayer* __restrict__ L, 
       for (int r = 0; r < 16; ++r) {
         const int i = (TS / 2) * wr + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int j = (TS / 2) * wc + 32 * ni + (lane & 31);
-        cur[r] = (i < mt && j < ntc) ? ((const gfloat*)wbase)[(size_t)i * nt + j] : 0.f;
+        cur[r] = (i < mt && j < ntc) ? wbase[(size_t)i * nt + j] : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
