@@ -156,8 +156,9 @@ def test_lora_refine_full_oracle(ctx):
 @pytest.mark.timeout(900)
 def test_mlp_layers_full(ctx):
     """MLP of a 1.7B-class decoder: gate/up (6144x2048, one shared Hessian)
-    against the whole oracle; down (2048x6144, 6144-wide Hessian) by sampled
-    blocks of H and the properties of U and the sweep."""
+    against the whole oracle; down (2048x6144, 6144-wide Hessian): H by
+    sampled blocks, U and the sweep by their properties, then damping, factor
+    and every code against the whole oracle fed the GPU's own H."""
     specs = synth.FULL["mlp"]
     gate, up, down = specs
     print("mlp: generating gate/up input", flush=True)
@@ -196,13 +197,23 @@ def test_mlp_layers_full(ctx):
     E = np32(rd["err"]).astype(np.float64)
     assert rd["J_lam"] == pytest.approx(float(np.sum(E * E)), rel=1e-6)
     print("mlp: down H block err %.2e, U ratio %.3f, recurrence %s" % (e, ratio, w), flush=True)
+    del Xb, E
+    print("mlp: oracle down on the GPU's H", flush=True)
+    Hd = Hn.astype(np.float64)
+    Hl, lam_r = o.damp(Hd, lam_rel=down.lam_rel)
+    assert lam == pytest.approx(lam_r, rel=1e-6)
+    Ur = o.factor_u(Hl)
+    rep = {}
+    check_sweep(rd, np32(ld["W"]).astype(np.float64), Ur, down.bits, down.group, down.block, Hd, lam_r, report=rep)
+    print("mlp: down", rep, flush=True)
 
 
 @pytest.mark.timeout(900)
 def test_vit_batched_full(ctx):
     """48 ViT-Base layers in one batched call: two layers (a 768-wide and a
-    3072-wide one) against the whole oracle, every layer by sampled blocks of
-    H and the properties of U and the sweep."""
+    3072-wide one) against the whole oracle from X; every other layer by
+    sampled blocks of H and the properties of U and the sweep, then damping,
+    factor and every code against the whole oracle fed the GPU's own H."""
     specs = synth.FULL["vit"]
     print("vit: generating %d layers" % len(specs), flush=True)
     lays = [synth.layer(s, "cuda") for s in specs]
@@ -231,6 +242,9 @@ def test_vit_batched_full(ctx):
         rows = _rows(s.out, 8, 200 + i)
         check_sweep_recurrence(np32(l["W"])[rows], Un, np32(b["codes"])[rows], np32(b["scales"])[rows],
                                np32(b["zeros"])[rows], np32(b["err"])[rows], s.bits, s.group)
+        Hd = Hn.astype(np.float64)
+        Hl, lam_r = o.damp(Hd, lam_rel=s.lam_rel)
+        check_sweep(b, np32(l["W"]).astype(np.float64), o.factor_u(Hl), s.bits, s.group, s.block, Hd, lam_r)
     print("vit: all layers checked", flush=True)
 
 
