@@ -370,7 +370,9 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
     rc = ensure(c, c->facA, totA * sizeof(double));
     if (rc) return rc;
   }
-  if ((rc = ensure(c, c->facY, totA * sizeof(double)))) return rc;
+  // Y matrices, then one 3 x 64 x 64 block per problem for the pair chains
+  // of batched plans
+  if ((rc = ensure(c, c->facY, (totA + (size_t)np * 3 * 64 * 64) * sizeof(double)))) return rc;
   std::vector<FacProb> probs(np);
   for (int p = 0; p < np; ++p) {
     const FacJob& J = jobs[p];
@@ -378,6 +380,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
     f.H = J.H;
     f.A = (double*)c->facA.p + oA[p];
     f.Y = (double*)c->facY.p + oA[p];
+    f.D = (double*)c->facY.p + totA + (size_t)p * 3 * 64 * 64;
     f.U = J.U;
     f.n = J.n;
     f.ldh = J.ldh;
@@ -395,7 +398,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   const size_t o_probs = b.add(probs);
   std::vector<FacShape> shapes(np);
   for (int p = 0; p < np; ++p) shapes[p] = FacShape{jobs[p].n, jobs[p].H != nullptr};
-  const std::vector<PlanLaunch> launches = plan_factor(shapes);
+  const std::vector<PlanLaunch> launches = plan_factor(shapes, c->ncu);
   std::vector<size_t> offs(launches.size());
   for (size_t i = 0; i < launches.size(); ++i)
     if (!launches[i].segs.empty()) offs[i] = b.add(launches[i].segs);
@@ -406,8 +409,12 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   // the side stream's updates take at most this many CUs (one workgroup per
   // CU, whose registers fill the CU), leaving about 96 to the serial chain:
   // the 64 panel workgroups of a 4096-wide problem and its narrow updates
-  // (measured best at n = 4096 among caps of 128 to 256 CUs)
-  const int side_wg = std::max(1, c->ncu - std::min(96, c->ncu / 2));
+  // (measured best at n = 4096 among caps of 128 to 256 CUs).  Batched plans,
+  // whose panel launches outnumber the CUs anyway (they run the diagonal
+  // chains first), give the updates the whole chip: there they set the pace.
+  bool batched = false;
+  for (const PlanLaunch& l : launches) batched = batched || l.kind == FK_DIAG2;
+  const int side_wg = batched ? c->ncu : std::max(1, c->ncu - std::min(96, c->ncu / 2));
   for (size_t i = 0; i < launches.size(); ++i) {
     const PlanLaunch& l = launches[i];
     const Seg* sg = (const Seg*)(d + offs[i]);
@@ -417,6 +424,7 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
       case FK_FILL: LAUNCH(c, "k_damp_fill", launch_damp_fill(dp, sg, nseg, l.nwg, c->stream)); break;
       case FK_PANEL: LAUNCH(c, "k_chol_panel", launch_chol_panel(dp, sg, nseg, l.nwg, c->stream)); break;
       case FK_PANEL2: LAUNCH(c, "k_chol_panel2", launch_chol_panel2(dp, sg, nseg, l.nwg, c->stream)); break;
+      case FK_DIAG2: LAUNCH(c, "k_chol_diag2", launch_chol_diag2(dp, sg, nseg, l.nwg, c->stream)); break;
       case FK_GEMM64: LAUNCH(c, "k_gemm64", launch_gemm64(dp, sg, nseg, l.nwg, c->stream)); break;
       case FK_RING64: LAUNCH_ON(c, st, "k_gemm_ring64", launch_gemm_ring(64, dp, sg, nseg, l.nwg, 0, st)); break;
       case FK_RING128:

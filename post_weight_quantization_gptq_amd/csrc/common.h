@@ -31,6 +31,7 @@ struct FacProb {
   double* Y;       // [n][n]: L^{-1}, built row block by row block
   float* U;        // output [n][ldu]
   double* C;       // GK_NT only: the product's output
+  double* D;       // [3][64][64]: Y0, Y1, L10 of the current pair from k_chol_diag2 (batched plans)
   int n;
   int ldh;
   int ldu;

@@ -165,73 +165,21 @@ __global__ __launch_bounds__(256) void k_chol_panel(const FacProb* __restrict__ 
       }
 }
 
-// Two 64-column steps k, k+1 of one outer panel in a single launch.  Every
-// workgroup first runs the pair's diagonal chain itself: the leaf Cholesky
-// and inverse of D0 = A_kk, L10 = A_{k+1,k} L_kk^{-T}, D1 = A_{k+1,k+1} -
-// L10 L10^T, its leaf and inverse; then its own part:
-//   - row block i >= k+2: L_ik = A_ik L_kk^{-T}, then
-//     L_{i,k+1} = (A_{i,k+1} - L_ik L10^T) L_{k+1,k+1}^{-T};
-//   - row block k: writes Y_kk = L_kk^{-1}, Y_{k+1,k} = -Y_{k+1,k+1} L10 Y_kk,
-//     Y_{k+1,k+1}, and zeros to the end of the 256-wide diagonal block;
-//   - row block k+1: nothing (L10 is read by no later step, and writing it
-//     would race with the other groups' loads of A_{k+1,k});
-//   - column block j < k: Y_kj = Y_kk B_kj, then
-//     Y_{k+1,j} = Y_{k+1,k+1} (B_{k+1,j} - L10 Y_kj).
-// This replaces two panel launches and the narrow update between them; the
-// repeated diagonal work is parallel and costs less than the launches.
-// Needs k + 1 < nb (block k is then full; block k+1 may be partial).
-__global__ __launch_bounds__(256) void k_chol_panel2(const FacProb* __restrict__ probs,
-                                                     const Seg* __restrict__ segs, int nseg) {
-  __shared__ __attribute__((aligned(16))) double LT[NB][LDP];   // leaf workspace (D0, then D1), then the operand stage
-  __shared__ __attribute__((aligned(16))) double Y0[NB][LDP];   // L_kk^{-1}
-  __shared__ __attribute__((aligned(16))) double Y1[NB][LDP];   // L_{k+1,k+1}^{-1}
-  __shared__ __attribute__((aligned(16))) double L10[NB][LDP];  // A_{k+1,k}, then L10
-  __shared__ double Tm[32][33];
-  __shared__ double lb[2 * NB];
-  __shared__ double dv[NB];
-  __shared__ int flag;
-  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
-  const FacProb pb = probs[sg.prob];
-  if (*pb.info != 0 || *pb.nonfinite != 0) return;
-  const int n = pb.n, k = sg.a, nb = (n + NB - 1) / NB, g = blockIdx.x - sg.wg0;
-  const int k0 = k * NB, k1 = k0 + NB, m1 = min(NB, n - k1);
-  const bool yrole = g >= nb - k;
-  const int i = yrole ? k : k + g, j = yrole ? g - (nb - k) : 0;
-  const int tid = threadIdx.x;
-  gptr<double> A = glb(pb.A);
-  gptr<double> Y = glb(pb.Y);
-  const int r0 = i * NB, mr = min(NB, n - r0);
-  const bool own = yrole || i >= k + 2;
-  // loads: the pair's diagonal region and this group's two blocks
-  f64x4 d1[2][2], x1[2][2];  // D1 and (A_{i,k+1} or B_{k+1,j}), accumulator layout
-  double tx[16];             // A_ik or B_kj, row-major by thread
-  {
-    double ta[16], tb[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = tid + 256 * q, r = e >> 6, c = e & 63;
-      ta[q] = (c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
-      tb[q] = (r < m1) ? A[(size_t)(k1 + r) * n + k0 + c] : 0.0;
-      tx[q] = !own ? 0.0 : yrole ? Y[(size_t)(k0 + r) * n + NB * j + c]
-                                 : ((r < mr) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0);
-    }
-    blk_each([&](int mi, int ni, int q, int r, int c) {
-      d1[mi][ni][q] = (r < m1 && c <= r) ? A[(size_t)(k1 + r) * n + k1 + c] : 0.0;
-      x1[mi][ni][q] = !own ? 0.0 : yrole ? ((r < m1) ? Y[(size_t)(k1 + r) * n + NB * j + c] : 0.0)
-                                         : ((r < mr && c < m1) ? A[(size_t)(r0 + r) * n + k1 + c] : 0.0);
-    });
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = tid + 256 * q, r = e >> 6, c = e & 63;
-      LT[r][c] = ta[q];
-      L10[r][c] = tb[q];
-    }
-  }
-  __syncthreads();
-  int bad = chol64_blocked(LT, dv, lb, &flag);
+// The diagonal chain of the pair of 64-column steps k, k+1: the leaf
+// Cholesky and inverse of D0 = A_kk (Y0 = L_kk^{-1}), L10 = A_{k+1,k} Y0^T,
+// D1 = A_{k+1,k+1} - L10 L10^T, its leaf and inverse (Y1 = L_{k+1,k+1}^{-1}).
+// In: LT = A_kk (lower), L10 = A_{k+1,k}, d1 = A_{k+1,k+1} (lower, in the
+// product accumulator layout, zero past m1).  Out: Y0, Y1, L10 in LDS; LT is
+// free.  Returns false (after recording the failing pivot) when a leaf fails.
+__device__ __forceinline__ bool pair_diag(const FacProb& pb, int k0, int m1, bool report,
+                                          double (&LT)[NB][LDP], double (&Y0)[NB][LDP], double (&Y1)[NB][LDP],
+                                          double (&L10)[NB][LDP], double (&Tm)[32][33], double* lb, double* dv,
+                                          int* flag, f64x4 (&d1)[2][2]) {
+  const int n = pb.n, k1 = k0 + NB;
+  int bad = chol64_blocked(LT, dv, lb, flag);
   if (bad >= 0) {
-    if (tid == 0 && g == 0) atomicMax(pb.info, n - (k0 + bad));
-    return;
+    if (report && threadIdx.x == 0) atomicMax(pb.info, n - (k0 + bad));
+    return false;
   }
   inv64_waves(LT, dv, Y0, Tm);
   f64x4 acc[2][2];
@@ -249,12 +197,139 @@ __global__ __launch_bounds__(256) void k_chol_panel2(const FacProb* __restrict__
     LT[r][c] = (r < m1 && c < m1) ? d1[mi][ni][q] : ((r == c) ? 1.0 : 0.0);
   });
   __syncthreads();
-  bad = chol64_blocked(LT, dv, lb, &flag);
+  bad = chol64_blocked(LT, dv, lb, flag);
   if (bad >= 0) {
-    if (tid == 0 && g == 0) atomicMax(pb.info, n - (k1 + bad));
-    return;
+    if (report && threadIdx.x == 0) atomicMax(pb.info, n - (k1 + bad));
+    return false;
   }
-  inv64_waves(LT, dv, Y1, Tm);  // LT is free from here on
+  inv64_waves(LT, dv, Y1, Tm);
+  return true;
+}
+
+// Loads of the pair's diagonal region for pair_diag: A_kk and A_{k+1,k} into
+// LT and L10 (row-major), A_{k+1,k+1} into d1.
+__device__ __forceinline__ void pair_diag_loads(gptr<double> A, int n, int k0, int m1, double (&LT)[NB][LDP],
+                                                double (&L10)[NB][LDP], f64x4 (&d1)[2][2]) {
+  const int tid = threadIdx.x, k1 = k0 + NB;
+  double ta[16], tb[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q, r = e >> 6, c = e & 63;
+    ta[q] = (c <= r) ? A[(size_t)(k0 + r) * n + k0 + c] : 0.0;
+    tb[q] = (r < m1) ? A[(size_t)(k1 + r) * n + k0 + c] : 0.0;
+  }
+  blk_each([&](int mi, int ni, int q, int r, int c) {
+    d1[mi][ni][q] = (r < m1 && c <= r) ? A[(size_t)(k1 + r) * n + k1 + c] : 0.0;
+  });
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q, r = e >> 6, c = e & 63;
+    LT[r][c] = ta[q];
+    L10[r][c] = tb[q];
+  }
+}
+
+// Batched problems: the diagonal chain of pair k once per problem (one
+// workgroup per segment), Y0, Y1 and L10 stored to the problem's D
+// (3 x 64 x 64, row-major) for k_chol_panel2's rows, instead of every one of
+// its workgroups repeating it.  Same code and order as the repeated chain,
+// so the results are the same bits.
+__global__ __launch_bounds__(256) void k_chol_diag2(const FacProb* __restrict__ probs,
+                                                    const Seg* __restrict__ segs, int nseg) {
+  __shared__ __attribute__((aligned(16))) double LT[NB][LDP];
+  __shared__ __attribute__((aligned(16))) double Y0[NB][LDP];
+  __shared__ __attribute__((aligned(16))) double Y1[NB][LDP];
+  __shared__ __attribute__((aligned(16))) double L10[NB][LDP];
+  __shared__ double Tm[32][33];
+  __shared__ double lb[2 * NB];
+  __shared__ double dv[NB];
+  __shared__ int flag;
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  const int n = pb.n, k0 = sg.a * NB, m1 = min(NB, n - k0 - NB);
+  f64x4 d1[2][2];
+  pair_diag_loads(glb(pb.A), n, k0, m1, LT, L10, d1);
+  __syncthreads();
+  if (!pair_diag(pb, k0, m1, true, LT, Y0, Y1, L10, Tm, lb, dv, &flag, d1)) return;
+  gptr<double> D = glb(pb.D);
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    D[e] = Y0[r][c];
+    D[NB * NB + e] = Y1[r][c];
+    D[2 * NB * NB + e] = L10[r][c];
+  }
+}
+
+// Two 64-column steps k, k+1 of one outer panel in a single launch.  Every
+// workgroup first runs the pair's diagonal chain itself (pair_diag), or, when
+// the segment's b is 1, loads its results from k_chol_diag2; then its own
+// part:
+//   - row block i >= k+2: L_ik = A_ik L_kk^{-T}, then
+//     L_{i,k+1} = (A_{i,k+1} - L_ik L10^T) L_{k+1,k+1}^{-T};
+//   - row block k: writes Y_kk = L_kk^{-1}, Y_{k+1,k} = -Y_{k+1,k+1} L10 Y_kk,
+//     Y_{k+1,k+1}, and zeros to the end of the 256-wide diagonal block;
+//   - row block k+1: nothing (L10 is read by no later step, and writing it
+//     would race with the other groups' loads of A_{k+1,k});
+//   - column block j < k: Y_kj = Y_kk B_kj, then
+//     Y_{k+1,j} = Y_{k+1,k+1} (B_{k+1,j} - L10 Y_kj).
+// This replaces two panel launches and the narrow update between them; the
+// repeated diagonal work is parallel and costs less than the launches while
+// the workgroups fit the chip in one round.
+// Needs k + 1 < nb (block k is then full; block k+1 may be partial).
+__global__ __launch_bounds__(256) void k_chol_panel2(const FacProb* __restrict__ probs,
+                                                     const Seg* __restrict__ segs, int nseg) {
+  __shared__ __attribute__((aligned(16))) double LT[NB][LDP];   // leaf workspace (D0, then D1), then the operand stage
+  __shared__ __attribute__((aligned(16))) double Y0[NB][LDP];   // L_kk^{-1}
+  __shared__ __attribute__((aligned(16))) double Y1[NB][LDP];   // L_{k+1,k+1}^{-1}
+  __shared__ __attribute__((aligned(16))) double L10[NB][LDP];  // A_{k+1,k}, then L10
+  __shared__ double Tm[32][33];
+  __shared__ double lb[2 * NB];
+  __shared__ double dv[NB];
+  __shared__ int flag;
+  const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
+  const FacProb pb = probs[sg.prob];
+  if (*pb.info != 0 || *pb.nonfinite != 0) return;
+  const int n = pb.n, k = sg.a, nb = (n + NB - 1) / NB, g = blockIdx.x - sg.wg0;
+  const bool pre = sg.b != 0;  // the diagonal chain's results are in pb.D
+  const int k0 = k * NB, k1 = k0 + NB, m1 = min(NB, n - k1);
+  const bool yrole = g >= nb - k;
+  const int i = yrole ? k : k + g, j = yrole ? g - (nb - k) : 0;
+  const int tid = threadIdx.x;
+  gptr<double> A = glb(pb.A);
+  gptr<double> Y = glb(pb.Y);
+  const int r0 = i * NB, mr = min(NB, n - r0);
+  const bool own = yrole || i >= k + 2;
+  // this group's two blocks (A_ik or B_kj in tx, row-major by thread; the
+  // second in x1, accumulator layout), loaded with the diagonal region's
+  f64x4 x1[2][2];
+  double tx[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q, r = e >> 6, c = e & 63;
+    tx[q] = !own ? 0.0 : yrole ? Y[(size_t)(k0 + r) * n + NB * j + c]
+                               : ((r < mr) ? A[(size_t)(r0 + r) * n + k0 + c] : 0.0);
+  }
+  blk_each([&](int mi, int ni, int q, int r, int c) {
+    x1[mi][ni][q] = !own ? 0.0 : yrole ? ((r < m1) ? Y[(size_t)(k1 + r) * n + NB * j + c] : 0.0)
+                                       : ((r < mr && c < m1) ? A[(size_t)(r0 + r) * n + k1 + c] : 0.0);
+  });
+  if (pre) {
+    gptr<const double> D = glb((const double*)pb.D);
+    for (int e = tid; e < NB * NB; e += 256) {
+      const int r = e >> 6, c = e & 63;
+      Y0[r][c] = D[e];
+      Y1[r][c] = D[NB * NB + e];
+      L10[r][c] = D[2 * NB * NB + e];
+    }
+    __syncthreads();
+  } else {
+    f64x4 d1[2][2];
+    pair_diag_loads(A, n, k0, m1, LT, L10, d1);
+    __syncthreads();
+    if (!pair_diag(pb, k0, m1, g == 0, LT, Y0, Y1, L10, Tm, lb, dv, &flag, d1)) return;
+  }
+  f64x4 acc[2][2];
   const int P1 = min((k0 / 256) * 256 + 256, n);
   if (!yrole && i == k) {
     // Y rows of the pair: Y_kk, Y_{k+1,k} = -Y1 (L10 Y0), Y_{k+1,k+1}, zeros
@@ -810,6 +885,7 @@ hipError_t launch_damp_lambda(const FacProb* probs, int nprob, hipStream_t st) {
 SEG_LAUNCH(launch_damp_fill, k_damp_fill, 256)
 SEG_LAUNCH(launch_chol_panel, k_chol_panel, 256)
 SEG_LAUNCH(launch_chol_panel2, k_chol_panel2, 256)
+SEG_LAUNCH(launch_chol_diag2, k_chol_diag2, 256)
 SEG_LAUNCH(launch_gemm64, k_gemm<64>, 256)
 hipError_t launch_gemm_ring(int ts, const FacProb* probs, const Seg* segs, int nseg, int ntot, int maxwg,
                             hipStream_t st) {

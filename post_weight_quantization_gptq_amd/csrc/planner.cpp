@@ -206,7 +206,7 @@ void plan_hessian64(int n, long long tokens, int ncu, Hess64Plan& P) {
 // stream, where it overlaps the next outer panel's steps (which neither read
 // nor write it) and is joined before the next outer update.  With the
 // general products (n % 64 != 0) everything stays on one stream.
-std::vector<PlanLaunch> plan_factor(const std::vector<FacShape>& jobs) {
+std::vector<PlanLaunch> plan_factor(const std::vector<FacShape>& jobs, int ncu) {
   const int np = (int)jobs.size();
   std::vector<PlanLaunch> launches;
   auto add_launch = [&](int kind, std::vector<Seg>& segs, bool side = false) {
@@ -261,6 +261,19 @@ std::vector<PlanLaunch> plan_factor(const std::vector<FacShape>& jobs) {
           bulk_rows = std::max(bulk_rows, n - S);
         }
       }
+    }
+    int pan2_wg = 0;
+    for (const Seg& sg : pan2) pan2_wg += sg.nwg;
+    if (pan2_wg > ncu) {
+      // more panel workgroups than CUs (batched layers): every workgroup
+      // repeating its problem's diagonal chain would cost one chain per round
+      // of the chip, so the chain runs once per problem first
+      std::vector<Seg> dg;
+      for (Seg& sg : pan2) {
+        dg.push_back(Seg{sg.prob, 0, 1, sg.a, 0, 0, 0, 0});
+        sg.b = 1;
+      }
+      add_launch(FK_DIAG2, dg);
     }
     add_launch(FK_PANEL2, pan2);
     add_launch(FK_PANEL, pan);

@@ -74,13 +74,16 @@ enum FacKind {
   FK_RING64 = 3,   // k_gemm_ring<64> (n % 64 == 0)
   FK_RING128 = 4,  // k_gemm_ring<128>
   FK_MAKEU = 5,    // k_make_u: U from Y
-  FK_PANEL2 = 8    // k_chol_panel2: two 64-column steps
+  FK_PANEL2 = 8,   // k_chol_panel2: two 64-column steps (segment b = 1: diagonal chain from FK_DIAG2)
+  FK_DIAG2 = 9     // k_chol_diag2: a pair's diagonal chain, once per problem
 };
 struct FacShape {
   int n;
   bool fill;  // A is built from H by k_damp_fill (else assembled beforehand)
 };
-std::vector<PlanLaunch> plan_factor(const std::vector<FacShape>& jobs);
+// ncu: CUs of the chip; a pair step whose panel workgroups exceed it runs
+// its problems' diagonal chains once each first (FK_DIAG2).
+std::vector<PlanLaunch> plan_factor(const std::vector<FacShape>& jobs, int ncu);
 
 // ----------------------------------------------------------- quantise -----
 enum QuantKind { QK_INIT = 0, QK_ROWFIT = 1, QK_SWEEP = 2, QK_TRAIL = 3 };

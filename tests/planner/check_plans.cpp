@@ -186,12 +186,14 @@ static void check_hessian64(int n, long long tokens) {
 // -------------------------------------------------------------- factor -----
 // L: lower 64-blocks (I >= J) with a count per contributing K-block t < J;
 // Y: blocks (I > J) with a count per t in [J, I).  Resources for the stream
-// check: 0 = L block I * nb + J, 1 = Y block I * nb + J.
+// check: 0 = L block I * nb + J, 1 = Y block I * nb + J, 2 = the problem's
+// stored diagonal chain (k_chol_diag2 -> k_chol_panel2).
 struct FacState {
   int n, nb;
   bool filled = false;
   std::vector<uint8_t> cl, cy;  // [I][J][t]
   std::vector<bool> finL, finY;
+  int diag_k = -1;  // pair whose diagonal chain is stored (FK_DIAG2)
   explicit FacState(int n_) : n(n_), nb(cdiv(n_, 64)) {
     cl.assign((size_t)nb * nb * nb, 0);
     cy.assign((size_t)nb * nb * nb, 0);
@@ -276,8 +278,8 @@ static void fac_gemm(FacState& F, int p, const Seg& s, int TS, std::vector<Acc>&
   }
 }
 
-static void check_factor(const std::vector<FacShape>& jobs) {
-  const std::vector<PlanLaunch> L = plan_factor(jobs);
+static void check_factor(const std::vector<FacShape>& jobs, int ncu = 256) {
+  const std::vector<PlanLaunch> L = plan_factor(jobs, ncu);
   std::vector<FacState> F;
   for (const FacShape& j : jobs) F.emplace_back(j.n);
   for (size_t p = 0; p < jobs.size(); ++p) F[p].filled = !jobs[p].fill;
@@ -308,9 +310,29 @@ static void check_factor(const std::vector<FacShape>& jobs) {
           f.filled = true;
           add_blocks(acc, s.prob, 0, nb, 0, nb, 0, nb, true);
           break;
+        case FK_DIAG2: {
+          // the pair's diagonal region must have every earlier update
+          const int k = s.a;
+          CHECK(s.nwg == 1 && k + 1 < nb, "problem %d diagonal chain launch", s.prob);
+          for (int I = k; I < k + 2 && I < nb; ++I)
+            for (int c = k; c <= I; ++c)
+              for (int t = 0; t < c; ++t) {
+                const int want = (c == k + 1 && t == k) ? 0 : 1;
+                CHECK(f.L(I, c, t) == want, "problem %d diagonal chain %d: L(%d,%d) has panel %d applied %d times",
+                      s.prob, k, I, c, t, f.L(I, c, t));
+              }
+          f.diag_k = k;
+          add_blocks(acc, s.prob, 0, nb, k, std::min(k + 2, nb), k, std::min(k + 2, nb), false);
+          acc.push_back(Acc{s.prob, 2, 0, 1, true});
+          break;
+        }
         case FK_PANEL:
         case FK_PANEL2:
           CHECK(s.nwg == nb, "panel workgroups");
+          if (l.kind == FK_PANEL2 && s.b != 0) {
+            CHECK(f.diag_k == s.a, "problem %d panel %d reads the diagonal chain of step %d", s.prob, s.a, f.diag_k);
+            acc.push_back(Acc{s.prob, 2, 0, 1, false});
+          }
           panel_step(f, s.prob, s.a, l.kind == FK_PANEL2, acc);
           break;
         case FK_GEMM64:
@@ -515,6 +537,12 @@ int main() {
   g_case = "factor-mixed";
   check_factor({FacShape{4096, true}, FacShape{768, true}, FacShape{3072, true}, FacShape{200, true}});
   check_factor({FacShape{100, true}, FacShape{37, true}});
+  // small chips: every pair step with more panel workgroups than CUs runs its
+  // diagonal chains first
+  g_case = "factor-diag-split";
+  check_factor({FacShape{4096, true}, FacShape{768, true}, FacShape{3072, true}, FacShape{200, true}}, 8);
+  check_factor({FacShape{4096, true}}, 32);
+  check_factor({FacShape{100, true}, FacShape{37, true}, FacShape{520, false}}, 1);
   if (g_fail) {
     fprintf(stderr, "%d planner check(s) failed\n", g_fail);
     return 1;

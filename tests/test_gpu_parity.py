@@ -330,10 +330,11 @@ def test_batched_matches_oracle(ctx):
 
 def test_batched_factor_more_groups_than_cus(ctx):
     """24 layers of n = 768 in one batched call: each step's panel launch has
-    24 x 12 = 288 workgroups (one per CU), so late groups start after early
-    ones have finished and written their outputs.  Every U must match the
-    oracle's factor of its own H (a group reading another group's output of
-    the same launch would break this)."""
+    24 x 12 = 288 workgroups (one per CU), more than the chip's CUs, so the
+    plan runs each pair's diagonal chain once per problem first and the panel
+    groups load it.  Every U must match the oracle's factor of its own H, and
+    the same bits as the single-layer factor (12 groups, each repeating the
+    chain itself)."""
     n, out, tokens = 768, 32, 1536
     layers = []
     for i in range(24):
@@ -349,3 +350,6 @@ def test_batched_factor_more_groups_than_cus(ctx):
         Ur = o.factor_u(Hl)
         Ug = np32(b["U"]).astype(np.float64)
         assert np.abs(Ug - Ur).max() <= 2e-6 * np.abs(Ur).max(), i
+    for i in (0, 11, 23):
+        U1, info, _ = ctx.factor(layers[i]["H"], lam_rel=0.01)
+        assert info == 0 and torch.equal(U1, layers[i]["U"]), i

@@ -74,6 +74,8 @@ MISTAKES = [
      "        add_launch(QK_TRAIL, 128, bulk, true);",
      "        add_launch(QK_TRAIL, 128, bulk, true);\n        add_launch(QK_TRAIL, 128, bulk, true);",
      "after [0,"),
+    ("factor-diag-launch-dropped",
+     "      add_launch(FK_DIAG2, dg);\n", "", "reads the diagonal chain"),
     ("hessian-slice-gap",
      "const int k0 = (int)(32 * (c32 * sl / S)), k1 = (int)(32 * (c32 * (sl + 1) / S));",
      "const int k0 = (int)(32 * (c32 * sl / S)), k1 = (int)(32 * (c32 * (sl + 1) / S)) - (sl + 1 < S ? 32 : 0);",
