@@ -418,8 +418,9 @@ __device__ __forceinline__ double rsq_f64(double x) {
 }
 __device__ __forceinline__ double sqrt_f64(double x) { return x * rsq_f64(x); }
 
-// Sum over the L (4 or 8) lanes of an aligned group, the same bits on every
-// lane (pairwise sums: lane pairs, quads, then the two quads of a group of 8).
+// Sum over the L (4, 8 or 16) lanes of an aligned group, the same bits on
+// every lane (pairwise sums: lane pairs, quads, the two quads of a group of 8,
+// then the two halves of a group of 16).
 template <int L>
 __device__ __forceinline__ double lane_sum(double x) {
   auto mv = [](double v, auto ctrl) {
@@ -431,7 +432,8 @@ __device__ __forceinline__ double lane_sum(double x) {
   };
   x += mv(x, std::integral_constant<int, 0xB1>{});  // quad_perm [1,0,3,2]
   x += mv(x, std::integral_constant<int, 0x4E>{});  // quad_perm [2,3,0,1]
-  if constexpr (L == 8) x += mv(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (L >= 8) x += mv(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  if constexpr (L == 16) x += mv(x, std::integral_constant<int, 0x140>{});  // row_mirror
   return x;
 }
 
@@ -460,10 +462,10 @@ __device__ __forceinline__ double sqnorm(const f64x2 (&x)[T]) {
 // round).  A pair is rotated when |b_p . b_q| > 1e-15 ||b_p|| ||b_q||
 // (p < q); sweeps stop when none is (at most 40).  Writes Y[i][k] (m x m
 // row-major, column k the eigenvector of the k-th largest eigenvalue) and
-// theta[k].  One workgroup of L lanes per column pair (at most 512).
+// theta[k].  One workgroup of L lanes per column pair (at most 64 L).
 constexpr int kRitzSweeps = 40;
 template <int L, int T>
-__global__ __launch_bounds__(512) void k_ritz(const double* __restrict__ M, int m, double* __restrict__ Y,
+__global__ __launch_bounds__(L * 64) void k_ritz(const double* __restrict__ M, int m, double* __restrict__ Y,
                                               double* __restrict__ theta) {
   __shared__ __attribute__((aligned(16))) double Bc[kRitzMax][kRitzPitch];  // Bc[c][i] = B[i][c]
   __shared__ double sig[kRitzMax];
