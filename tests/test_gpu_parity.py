@@ -328,6 +328,32 @@ def test_batched_matches_oracle(ctx):
         check_sweep(b, l["W"].numpy().astype(np.float64), o.factor_u(Hl), s.bits, s.group, s.block, Hr, lam)
 
 
+def test_batched_factor_ragged_more_groups_than_cus(ctx):
+    """40 layers of n = 450 (blocks of 64, the last one 2 wide, so the
+    products take the general path): each pair step's panel launch has
+    40 x 8 = 320 workgroups, more than the CUs, so the diagonal chains run
+    once per problem first, the last pair's second block partial.  U must
+    match the oracle and the single-layer factor bit for bit."""
+    n, out, tokens = 450, 16, 1200
+    layers = []
+    for i in range(40):
+        X = _rand_x(tokens, n, 700 + i)
+        W = torch.from_numpy(np.random.default_rng(800 + i).normal(0.0, 0.02, size=(out, n)).astype(np.float32))
+        layers.append(dict(W=W.cuda(), X=X.cuda(), bits=4, group=0, block=32, lam_rel=0.01))
+    ctx.quantize_batched(layers)
+    torch.cuda.synchronize()
+    for i, b in enumerate(layers):
+        assert b["info"] == 0, i
+        Hn = np32(b["H"]).astype(np.float64)
+        Hl, lam = o.damp(Hn, lam_rel=0.01)
+        Ur = o.factor_u(Hl)
+        Ug = np32(b["U"]).astype(np.float64)
+        assert np.abs(Ug - Ur).max() <= 2e-6 * np.abs(Ur).max(), i
+    for i in (0, 17, 39):
+        U1, info, _ = ctx.factor(layers[i]["H"], lam_rel=0.01)
+        assert info == 0 and torch.equal(U1, layers[i]["U"]), i
+
+
 def test_batched_factor_more_groups_than_cus(ctx):
     """24 layers of n = 768 in one batched call: each step's panel launch has
     24 x 12 = 288 workgroups (one per CU), more than the chip's CUs, so the
