@@ -147,7 +147,7 @@ int gptq_lora(gptq_ctx ctx, const float* W, int32_t out, int32_t n, const uint16
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments, checks, kernels and results (codes, scales, zeros, err
  * and obj bit-identical to gptq_quantize on the same inputs), but every
- * intermediate lives in a fixed array of about 8.5 MB of device memory that
+ * intermediate lives in a fixed array of about 12.7 MB of device memory that
  * the library holds for the process's lifetime, one copy per device, and
  * the pinned host staging it uses is made when the context is created.  The
  * call performs no hipMalloc, hipFree, hipHostMalloc or event creation.

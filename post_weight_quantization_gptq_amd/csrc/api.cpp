@@ -224,7 +224,7 @@ constexpr long long NA_MAX_ELEMS = 1LL << 20;
 constexpr size_t NA_SLOT = 256;
 constexpr size_t NA_BLOB = 64 << 10;
 constexpr size_t NA_WW = (size_t)NA_MAX_ELEMS * sizeof(float);
-constexpr size_t NA_EB = (size_t)2 * NA_MAX_OUT * 512 * sizeof(float);
+constexpr size_t NA_EB = (size_t)2 * NA_MAX_OUT * 1024 * sizeof(float);  // two 1024-column super-blocks
 constexpr size_t NA_OBJP = (size_t)NA_MAX_OUT * 2 * sizeof(double);
 constexpr size_t NA_DINV = (size_t)(NA_MAX_N + 64) * sizeof(float);
 constexpr size_t NA_BYTES = NA_SLOT + NA_BLOB + NA_WW + NA_EB + NA_OBJP + NA_DINV;
@@ -459,6 +459,11 @@ int run_quantize(gptq_ctx c, const std::vector<QuantJob>& jobs, std::vector<floa
   std::vector<PlanLaunch> launches;
   plan_quantize(shapes, &QLy, &launches);
   const std::vector<int>& sbk = QLy.sbk;
+  // the sweep keeps a super-block's columns of its rows in LDS: at most 1024
+  // columns for 128-wide blocks, 512 for narrower ones
+  for (size_t p = 0; p < shapes.size(); ++p)
+    if (sbk[p] * shapes[p].block > (shapes[p].block >= 128 ? 1024 : 512))
+      return set_err(c, GPTQ_ERR_UNSUPPORTED, "super-block wider than the sweep's LDS row buffer");
   const size_t totW = QLy.totW, totE = QLy.totE, totO = QLy.totO, totD = QLy.totD;
   const std::vector<size_t>&oW = QLy.oW, &oE = QLy.oE, &oO = QLy.oO, &oD = QLy.oD;
   int rc;

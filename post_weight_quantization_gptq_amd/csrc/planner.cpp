@@ -329,7 +329,12 @@ void plan_quantize(const std::vector<QuantShape>& jobs, QuantLayout* lay, std::v
   int maxblk = 0;
   for (int p = 0; p < nl; ++p) {
     const QuantShape& J = jobs[p];
-    int sb = std::max(1, 512 / J.block);
+    // 1024 columns for 128-wide blocks (more of the trailing update on the
+    // sweep workgroups' own MFMAs, less beside the sweeps on the second
+    // stream: faster while the sweep workgroups fit the chip in few rounds),
+    // 512 for narrower blocks (K = B products, and batched small layers whose
+    // sweep workgroups take many rounds, where the update kernels do better)
+    int sb = std::max(1, (J.block >= 128 ? 1024 : 512) / J.block);
     const int sbw = sb * J.block;
     if (J.group && !(sbw % J.group == 0 || J.group % sbw == 0)) sb = 1;
     Ly.sbk[p] = sb;

@@ -236,10 +236,17 @@ struct SweepAll<16, CPL, BID> {
 // BID: one Bid-Up pass instead of the GPTQ sweep (codes are read as the
 // starting point, the grid is the one given, and the per-row sums are the
 // objective changes of the moves).
-#define SWEEP_SBW 512  // widest super-block (blocks x block width)
+// Widest super-block for blocks of B columns (the planner keeps to it):
+// 1024 columns at B = 128 (138 KB of LDS, one workgroup per CU either way),
+// 512 below (at B = 64, 53 KB: three workgroups per CU, which the batched
+// small layers need)
+template <int B>
+constexpr int sweep_sbw() {
+  return B >= 128 ? 1024 : 512;
+}
 template <int B>
 struct SweepLds {
-  static constexpr int WP = SWEEP_SBW + 4;
+  static constexpr int WP = sweep_sbw<B>() + 4;
   static constexpr int EP = B + 4;
   float us[B * B];   // the diagonal block of U
   float ws[16 * WP];  // the rows' columns of the super-block
