@@ -8,14 +8,18 @@
 // U = P C^{-1} P, so one Cholesky and one triangular inverse suffice
 // (2n^3/3 flops instead of 4n^3/3 for Cholesky -> inverse -> Cholesky).
 //
-// Cholesky: right-looking over 256-wide outer panels, each factored in four
-// 64-wide steps.  A step factors its 64x64 diagonal block inside one wave
-// with the block's rows in registers (no barriers), inverts it on all four
-// waves (16x16 forward substitutions, then doubling on fp64 MFMA), then
-// computes the panel rows below as A_ik L_kk^{-T} on fp64 MFMA and updates
-// the rest of the outer panel; after the outer panel, one fp64 MFMA update
-// with K = 256 reaches the trailing lower triangle (four times less traffic
-// over the trailing matrix than updating it after every 64 columns).
+// Cholesky: right-looking over 256-wide outer panels, each factored as two
+// pairs of 64-wide steps (k_chol_panel2; k_chol_panel for an unpaired last
+// block).  A pair launch factors both 64x64 diagonal blocks with the
+// four-wave blocked leaf and inverts them (blk64.h), then each workgroup
+// computes its panel rows below as A_ik L_kk^{-T} on fp64 MFMA.  Between the
+// pairs, a narrow update brings the second pair's columns up to date; after
+// the outer panel, one update with K = 256 reaches the next outer panel's
+// columns on the main stream and the rest of the trailing lower triangle on
+// the second stream (four times less traffic over the trailing matrix than
+// updating it after every 64 columns).  When a pair's panel launch would
+// outnumber the CUs (batched layers), k_chol_diag2 first runs the pair's
+// diagonal chain once per problem and the panel workgroups load it.
 // Inverse: Y = L^{-1} by blocked forward substitution of L Y = I run in step
 // with the factorization.  Step k finishes block row k of Y
 // (Y_kj = L_kk^{-1} B_kj, B_kj = -sum_{t<k} L_kt Y_tj) in the same launch as
