@@ -135,6 +135,13 @@ def test_factor_nonfinite(ctx):
     (57, 512, 3, 128, 32),
     (50, 200, 8, 0, 16),
     (70, 256, 2, 16, 32),
+    # several super-blocks (1024 columns at B = 128, 512 below): the next
+    # super-block's update, the far update beside the sweeps, the two-buffer
+    # errors, a ragged last super-block, and groups wider than a super-block
+    (48, 2688, 4, 128, 128),
+    (40, 2560, 3, 0, 128),
+    (32, 4096, 4, 2048, 128),
+    (36, 1600, 4, 64, 64),
 ])
 def test_sweep_matches_oracle(ctx, out, n, bits, group, block):
     print("sweep", out, n, bits, group, block, flush=True)
