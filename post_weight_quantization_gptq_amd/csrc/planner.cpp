@@ -23,13 +23,16 @@ static int morton2(int i, int j) {
 
 // Number of token slices for one layer's tiles: whole rounds of the chip at
 // one tile per CU, each task also paying for writing its partial (about ten
-// 32-token steps of time).  Depends on the layer alone.
+// 32-token steps of time), and the reduction reading every partial back
+// (256 KB each, about 1/19 of a step of the chip's time at HBM speed).
+// Depends on the layer alone, so a layer gets the same bits alone or batched.
 static int hess_slices(int ntile, long long chunks, int ncu) {
   int best_s = 1;
   long long best = -1;
   for (int s = 1; s <= 64 && s <= std::max(1LL, chunks); ++s) {
     const long long rounds = cdiv((long long)ntile * s, (long long)ncu);
-    const long long cost = rounds * (cdiv(chunks, (long long)s) + 10);
+    // in 1/19 steps
+    const long long cost = 19 * rounds * (cdiv(chunks, (long long)s) + 10) + (long long)s * ntile;
     if (best < 0 || cost < best) {
       best = cost;
       best_s = s;

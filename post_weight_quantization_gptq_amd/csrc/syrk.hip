@@ -382,33 +382,55 @@ __global__ __launch_bounds__(256) void k_syrk_reduce(const RedProb* __restrict__
   __shared__ float S[64][65];
   const RedTask tk = tasks[blockIdx.x];
   const RedProb pb = probs[tk.prob];
+  const gptr<float> Hg = glb(pb.H);  // global view: H's accesses stay off lgkmcnt
   const int tid = threadIdx.x, n = pb.n;
   const int lr0 = tk.r0 & 255, lc0 = tk.c0 & 255;
   const int cc = tid & 63;
-  float sum[16];
+  // summing: thread t takes rows 4 (t / 16) .. +3 at columns 4 (t % 16) .. +3,
+  // one 16-byte load per row and part (parts in list order)
+  const int sr = 4 * (tid >> 4), sc = 4 * (tid & 15);
+  f32x4 sum[4];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) sum[q] = 0.f;
-  for (int p = 0; p < tk.nparts; ++p) {  // parts in list order, 16 loads in flight
-    const float* src = partials + (size_t)partlist[tk.part0 + p] * 65536 + (lr0 + (tid >> 6)) * 256 + lc0 + cc;
-    float v[16];
+  for (int u = 0; u < 4; ++u) sum[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // four parts per trip: their list entries, then their 16 loads, all in
+  // flight together; the sums still run part by part in list order
+  const float* base = partials + (lr0 + sr) * 256 + lc0 + sc;
+  for (int p0 = 0; p0 < tk.nparts; p0 += 4) {
+    const int np = min(4, tk.nparts - p0);
+    int pid[4];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = src[4 * q * 256];
+    for (int k = 0; k < 4; ++k) pid[k] = k < np ? partlist[tk.part0 + p0 + k] : 0;
+    f32x4 v[4][4];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) sum[q] += v[q];
+    for (int k = 0; k < 4; ++k) {
+      gptr<const f32x4> src = (gptr<const f32x4>)(base + (size_t)pid[k] * 65536);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[k][u] = k < np ? src[u * 64] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < np)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sum[u] += v[k][u];
   }
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int rr = (tid >> 6) + 4 * q;
-    const int i = tk.r0 + rr, j = tk.c0 + cc;
-    float s = sum[q];
-    if (pb.accumulate && i < n && j < n && (i <= j || pb.full)) s += pb.H[(size_t)i * n + j];
-    S[rr][cc] = s;
-  }
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) S[sr + u][sc + w] = sum[u][w];
   __syncthreads();
+  if (pb.accumulate) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int rr = (tid >> 6) + 4 * q;
+      const int i = tk.r0 + rr, j = tk.c0 + cc;
+      if (i < n && j < n && (i <= j || pb.full)) S[rr][cc] += Hg[(size_t)i * n + j];
+    }
+    __syncthreads();
+  }
   for (int q = 0; q < 16; ++q) {
     const int rr = (tid >> 6) + 4 * q;
     const int i = tk.r0 + rr, j = tk.c0 + cc;
-    if (i < n && j < n && (i <= j || pb.full)) pb.H[(size_t)i * n + j] = S[rr][cc];
+    if (i < n && j < n && (i <= j || pb.full)) Hg[(size_t)i * n + j] = S[rr][cc];
   }
   if (pb.full) return;  // a cross Gram has no mirror
   // mirror: H[j][i] = S[i][j] for i < j, written along contiguous rows of H
@@ -416,7 +438,7 @@ __global__ __launch_bounds__(256) void k_syrk_reduce(const RedProb* __restrict__
     const int ci = (tid >> 6) + 4 * q;  // column index inside the sub-block
     const int ri = tid & 63;            // row index inside the sub-block
     const int i = tk.r0 + ri, j = tk.c0 + ci;
-    if (i < n && j < n && i < j) pb.H[(size_t)j * n + i] = S[ri][ci];
+    if (i < n && j < n && i < j) Hg[(size_t)j * n + i] = S[ri][ci];
   }
 }
 
@@ -549,33 +571,58 @@ __global__ __launch_bounds__(256) void k_syrk64_reduce(const RedProb64* __restri
   __shared__ double S[64][65];
   const RedTask tk = tasks[blockIdx.x];
   const RedProb64 pb = probs[tk.prob];
+  const gptr<double> Hg = glb(pb.H);  // global view: H's accesses stay off lgkmcnt
   const int tid = threadIdx.x, n = pb.n;
   const int lr0 = tk.r0 & 127, lc0 = tk.c0 & 127;
-  const int cc = tid & 63;
-  double sum[16];
+  // summing: thread t takes rows 4 (t / 16) .. +3 at columns 4 (t % 16) .. +3,
+  // two 16-byte loads per row and part (parts in list order)
+  const int sr = 4 * (tid >> 4), sc = 4 * (tid & 15);
+  f64x2 sum[4][2];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) sum[q] = 0.0;
-  for (int p = 0; p < tk.nparts; ++p) {
-    const double* src = partials + (size_t)partlist[tk.part0 + p] * 16384 + (lr0 + (tid >> 6)) * 128 + lc0 + cc;
-    double v[16];
+  for (int u = 0; u < 4; ++u) sum[u][0] = sum[u][1] = f64x2{0.0, 0.0};
+  // two parts per trip: their list entries, then their 16 loads, all in
+  // flight together; the sums still run part by part in list order
+  const double* base = partials + (lr0 + sr) * 128 + lc0 + sc;
+  for (int p0 = 0; p0 < tk.nparts; p0 += 2) {
+    const int np = min(2, tk.nparts - p0);
+    int pid[2];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = src[4 * q * 128];
+    for (int k = 0; k < 2; ++k) pid[k] = k < np ? partlist[tk.part0 + p0 + k] : 0;
+    f64x2 v[2][4][2];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) sum[q] += v[q];
+    for (int k = 0; k < 2; ++k) {
+      gptr<const f64x2> src = (gptr<const f64x2>)(base + (size_t)pid[k] * 16384);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[k][u][0] = k < np ? src[u * 64] : f64x2{0.0, 0.0};
+        v[k][u][1] = k < np ? src[u * 64 + 1] : f64x2{0.0, 0.0};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (k < np)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sum[u][0] += v[k][u][0];
+          sum[u][1] += v[k][u][1];
+        }
   }
 #pragma unroll
-  for (int q = 0; q < 16; ++q) S[(tid >> 6) + 4 * q][cc] = sum[q];
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) S[sr + u][sc + w] = sum[u][w >> 1][w & 1];
   __syncthreads();
+  const int cc = tid & 63;
   for (int q = 0; q < 16; ++q) {
     const int rr = (tid >> 6) + 4 * q;
     const int i = tk.r0 + rr, j = tk.c0 + cc;
-    if (i < n && j < n && i <= j) pb.H[(size_t)i * n + j] = S[rr][cc];
+    if (i < n && j < n && i <= j) Hg[(size_t)i * n + j] = S[rr][cc];
   }
   for (int q = 0; q < 16; ++q) {
     const int ci = (tid >> 6) + 4 * q;
     const int ri = tid & 63;
     const int i = tk.r0 + ri, j = tk.c0 + ci;
-    if (i < n && j < n && i < j) pb.H[(size_t)j * n + i] = S[ri][ci];
+    if (i < n && j < n && i < j) Hg[(size_t)j * n + i] = S[ri][ci];
   }
 }
 
