@@ -411,10 +411,13 @@ int run_factor(gptq_ctx c, const std::vector<FacJob>& jobs, Slot* dslots, bool a
   // the 64 panel workgroups of a 4096-wide problem and its narrow updates
   // (measured best at n = 4096 among caps of 128 to 256 CUs).  Batched plans,
   // whose panel launches outnumber the CUs anyway (they run the diagonal
-  // chains first), give the updates the whole chip: there they set the pace.
+  // chains first), give the updates all but 64 CUs: there the updates set the
+  // pace, and the 64 keep the diagonal chains from waiting for them (ViT:
+  // caps of 160, 192, 208 and 256 measured; 192 best, within about 1%).
   bool batched = false;
   for (const PlanLaunch& l : launches) batched = batched || l.kind == FK_DIAG2;
-  const int side_wg = batched ? c->ncu : std::max(1, c->ncu - std::min(96, c->ncu / 2));
+  const int side_wg = batched ? std::max(1, c->ncu - std::min(64, c->ncu / 2))
+                              : std::max(1, c->ncu - std::min(96, c->ncu / 2));
   for (size_t i = 0; i < launches.size(); ++i) {
     const PlanLaunch& l = launches[i];
     const Seg* sg = (const Seg*)(d + offs[i]);
