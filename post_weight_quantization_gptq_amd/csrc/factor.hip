@@ -39,8 +39,11 @@ __global__ __launch_bounds__(256) void k_damp_lambda(const FacProb* __restrict__
   if (p >= nprob) return;
   const FacProb pb = probs[p];
   if (pb.H == nullptr) return;  // assembled elsewhere (lam already set)
+  // each thread sums its entries in index order; unrolled so that the loads
+  // of several entries are in flight at once
   double s = 0.0;
-  for (int i = threadIdx.x; i < pb.n; i += 256) s += (double)pb.H[(size_t)i * pb.ldh + i];
+#pragma unroll 8
+  for (int i = threadIdx.x; i < pb.n; i += 256) s += (double)glb(pb.H)[(size_t)i * pb.ldh + i];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int k = 128; k > 0; k >>= 1) {
@@ -56,7 +59,9 @@ __global__ __launch_bounds__(256) void k_damp_lambda(const FacProb* __restrict__
 }
 
 // A[i][j] = H[n-1-i][n-1-j] + lam delta_ij, lower triangle only (j <= i).
-// Segment: one workgroup per 4 rows.
+// Segment: one workgroup per 4 rows, one wave per row.  With 16-byte aligned
+// rows each lane moves 4 entries per step (a reversed float4 in, two double2
+// out), several steps in flight at once; otherwise one entry per lane.
 __global__ __launch_bounds__(256) void k_damp_fill(const FacProb* __restrict__ probs,
                                                    const Seg* __restrict__ segs, int nseg) {
   const Seg sg = segs[find_seg(segs, nseg, blockIdx.x)];
@@ -64,14 +69,39 @@ __global__ __launch_bounds__(256) void k_damp_fill(const FacProb* __restrict__ p
   const int n = pb.n;
   const int i = (blockIdx.x - sg.wg0) * 4 + (threadIdx.x >> 6);
   if (i >= n) return;
+  const int lane = threadIdx.x & 63;
   const double lam = *pb.lam;
-  const float* hrow = pb.H + (size_t)(n - 1 - i) * pb.ldh;
-  double* arow = pb.A + (size_t)i * n;
+  gptr<const float> hrow = glb(pb.H) + (size_t)(n - 1 - i) * pb.ldh;
+  gptr<double> arow = glb(pb.A) + (size_t)i * n;
   bool bad = false;
-  for (int j = threadIdx.x & 63; j <= i; j += 64) {
-    const float h = hrow[n - 1 - j];
-    bad |= !__builtin_isfinite(h);
-    arow[j] = (double)h + (i == j ? lam : 0.0);
+  const bool vec = (n % 4) == 0 && (pb.ldh % 4) == 0 && (((uintptr_t)pb.H) & 15) == 0 && (((uintptr_t)pb.A) & 15) == 0;
+  if (vec) {
+#pragma unroll 4
+    for (int j4 = 4 * lane; j4 <= i; j4 += 256) {
+      // columns j4 .. j4+3 of A are columns n-1-j4 .. n-4-j4 of H
+      const f32x4 v = *(gptr<const f32x4>)(hrow + (n - 4 - j4));
+      double d[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float h = v[3 - t];
+        bad |= (j4 + t <= i) && !__builtin_isfinite(h);
+        d[t] = (double)h + (i == j4 + t ? lam : 0.0);
+      }
+      if (j4 + 3 <= i) {
+        *(gptr<f64x2>)(arow + j4) = f64x2{d[0], d[1]};
+        *(gptr<f64x2>)(arow + j4 + 2) = f64x2{d[2], d[3]};
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (j4 + t <= i) arow[j4 + t] = d[t];
+      }
+    }
+  } else {
+    for (int j = lane; j <= i; j += 64) {
+      const float h = hrow[n - 1 - j];
+      bad |= !__builtin_isfinite(h);
+      arow[j] = (double)h + (i == j ? lam : 0.0);
+    }
   }
   if (bad) atomicOr(pb.nonfinite, 1);
 }

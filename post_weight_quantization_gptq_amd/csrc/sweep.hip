@@ -32,9 +32,18 @@ __global__ __launch_bounds__(256) void k_init_work(const QLayer* __restrict__ L,
     ((float*)ly.dinv)[c] = 1.f / ly.U[(size_t)c * ly.nt + c];
   const int row = wi * 4 + (threadIdx.x >> 6);
   if (row >= ly.out) return;
-  for (int c = threadIdx.x & 63; c < ly.nt; c += 64)
-    ly.Ww[(size_t)row * ly.nt + c] = c < ly.n ? ly.W[(size_t)row * ly.n + c] : 0.f;
-  if ((threadIdx.x & 63) < 2) ly.objp[(size_t)row * 2 + (threadIdx.x & 63)] = 0.0;
+  const int lane = threadIdx.x & 63;
+  gptr<const float> src = glb(ly.W) + (size_t)row * ly.n;
+  gptr<float> dst = glb(ly.Ww) + (size_t)row * ly.nt;
+  if ((ly.n % 4) == 0 && (ly.nt % 4) == 0 && ((((uintptr_t)ly.W) | ((uintptr_t)ly.Ww)) & 15) == 0) {
+    // 16 bytes per lane per step, several steps in flight
+#pragma unroll 4
+    for (int c = 4 * lane; c < ly.nt; c += 256)
+      *(gptr<f32x4>)(dst + c) = c < ly.n ? *(gptr<const f32x4>)(src + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    for (int c = lane; c < ly.nt; c += 64) dst[c] = c < ly.n ? src[c] : 0.f;
+  }
+  if (lane < 2) ly.objp[(size_t)row * 2 + lane] = 0.0;
 }
 
 // One grid per row on the original row (group == 0).  One wave per row.
