@@ -117,6 +117,50 @@ def syrk_traffic(workload):
     return kernel_traffic("k_syrk", workload, "syrk.hip")
 
 
+def counter_rates(workload):
+    """Counter-based rates of the layer's kernels from the committed rocprofv3
+    records (profiles/*_<workload>_counters.json and the sweep's traffic
+    record), each only while its source file's code is the one the counters
+    were taken on.  Matrix-pipe shares are SQ_VALU_MFMA_BUSY_CYCLES over the
+    cycles of the SIMDs (or, for the factor, of the CUs the kernel occupies);
+    the clock is GRBM_GUI_ACTIVE per XCD over the kernel's duration."""
+    out = {}
+
+    def load(name, source):
+        try:
+            rec = json.load(open(os.path.join(ROOT, "profiles", name)))
+            src = os.path.join(ROOT, "post_weight_quantization_gptq_amd", "csrc", source)
+            return rec if rec.get("source_code_sha256") == code_digest(src) else None
+        except Exception:
+            return None
+
+    def mean(xs):
+        return round(sum(xs) / len(xs), 4) if xs else None
+
+    rec = load("k_syrk_%s_counters.json" % workload, "syrk.hip")
+    if rec:
+        d = rec["dispatches"]
+        out["k_syrk"] = {"mfma_busy": mean([x["mfma_busy"] for x in d]), "clock_GHz": mean([x["clock_GHz"] for x in d]),
+                         "lds_active": mean([x["lds_active"] for x in d])}
+    rec = load("k_trail_%s_counters.json" % workload, "sweep.hip")
+    if rec:
+        for ts in ("64", "128"):
+            d = [x for x in rec["dispatches"] if x["kernel"].endswith("<%s>" % ts)]
+            if d:
+                out["k_trail<%s>" % ts] = {"mfma_busy": mean([x["mfma_busy"] for x in d]),
+                                           "clock_GHz": mean([x["clock_GHz"] for x in d])}
+    rec = load("k_sweep_%s_traffic.json" % workload, "sweep.hip")
+    if rec:
+        gbs = rec["hbm_GBps_under_profiler"]
+        out["k_sweep"] = {"bytes_per_launch": rec["bytes_per_launch"], "gb_s": gbs, "peak": PEAK_HBM_GBS,
+                          "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    rec = load("factor_%s_counters.json" % workload, "factor.hip")
+    if rec:
+        for k, v in rec["per_kernel"].items():
+            out[k] = {"mfma_busy_of_busy_cus": v["mfma_busy_of_busy_cus"]}
+    return out or None
+
+
 PEAK_FP32_MATRIX_TFLOPS = 157.3  # dense fp32 MFMA, MI355X
 PEAK_FP64_MATRIX_TFLOPS = 78.6   # dense fp64 MFMA, MI355X
 PEAK_FP32_VECTOR_TFLOPS = 157.3  # fp32 vector, MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2 (packed) x 2 (FMA) x 2.4 GHz
@@ -597,6 +641,10 @@ def main():
                             "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                             "traffic": syrk_traffic(args.workload) if dominant == "k_syrk" else None,
                             "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": per_launch}
+    if args.workload == "square":
+        rates = counter_rates(args.workload)
+        if rates:
+            line["counters"] = rates
     if args.workload == "lora":
         line["objective"] = {"J": last[0]["J"], "J_lam": last[0]["J_lam"]}
     if args.workload == "lora_refine":
