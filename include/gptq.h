@@ -337,6 +337,18 @@ int gptq_gemm_w4a16(gptq_ctx ctx, const uint16_t* X, int64_t M, int64_t ldx, con
                     const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group, float* Y,
                     int64_t ldy);
 
+/* The same product for the other widths the layers are quantised at (GPTQ
+ * encyclopedia entry, technical approach and performance and accuracy: 2 to
+ * 4 bits; GPTQ-intrinsic LoRA technical summary, results: 3-bit layers, L
+ * and R at 4 and 8 bits): bits in {2, 3, 4, 8}, packed[N][K bits/32] from
+ * gptq_pack_codes at that width (each row one bitstream, so 32 codes fill
+ * `bits` whole words).  Everything else, rounding and requirements included,
+ * as gptq_gemm_w4a16, which is this call with bits = 4.  Other widths:
+ * GPTQ_ERR_UNSUPPORTED. */
+int gptq_gemm_wqa16(gptq_ctx ctx, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
+                    const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group, int32_t bits,
+                    float* Y, int64_t ldy);
+
 /* Measurement support (not part of the method).  gptq_timing(ctx, kernels)
  * clears the totals and from then on brackets each launch of the named
  * kernels with a pair of HIP events on the context's stream.  kernels [host]
@@ -352,7 +364,8 @@ int gptq_gemm_w4a16(gptq_ctx ctx, const uint16_t* X, int64_t M, int64_t ldx, con
  * two-sided rounding k_r2d_unit, k_r2d_fill, k_r2d_tile, k_r2d_push, k_r2d_obj,
  * and for the quantised-input target k_qr_prep, k_qr_out, and for the
  * deployable outputs k_pack, k_unpack, k_lr_quant, k_gemm_w4a16,
- * k_gemv_w4a16.  gptq_kernel_time
+ * k_gemv_w4a16 (4-bit codes), k_gemm_wqa16, k_gemv_wqa16 (other widths).
+ * gptq_kernel_time
  * waits for the recorded events and returns the summed elapsed milliseconds
  * and the number of timed launches of kernel `name` (0 and 0 if none).  Each
  * timed launch costs two event records on the stream. */

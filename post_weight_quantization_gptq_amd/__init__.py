@@ -112,13 +112,14 @@ def load_library(path: str | None = None):
     L.gptq_unpack_codes.argtypes = [vp, vp, i32, i32, i32, vp]
     L.gptq_quantize_lowrank.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gptq_gemm_w4a16.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, vp, i64]
+    L.gptq_gemm_wqa16.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, vp, i64]
     L.gptq_quantize_batched.argtypes = [vp, i32, ctypes.POINTER(_Layer)]
     L.gptq_timing.argtypes = [vp, ctypes.c_char_p]
     L.gptq_kernel_time.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(d), ctypes.POINTER(i64)]
     for name in ("gptq_create", "gptq_destroy", "gptq_hessian", "gptq_factor", "gptq_quantize",
                  "gptq_quantize_noalloc", "gptq_lora", "gptq_lora_refine", "gptq_hessian64", "gptq_olrc", "gptq_bid_up", "gptq_round_2d",
                  "gptq_quantize_qronos", "gptq_cross_gram", "gptq_pack_codes", "gptq_unpack_codes",
-                 "gptq_quantize_lowrank", "gptq_gemm_w4a16",
+                 "gptq_quantize_lowrank", "gptq_gemm_w4a16", "gptq_gemm_wqa16",
                  "gptq_quantize_batched", "gptq_timing", "gptq_kernel_time"):
         getattr(L, name).restype = ctypes.c_int
     if path is None:
@@ -502,6 +503,26 @@ class Context:
         self._dev(Y, torch.float32, "Y")
         self._check(self.lib.gptq_gemm_w4a16(self.handle, _ptr(X), M, X.stride(0), _ptr(packed), _ptr(scales),
                                              _ptr(zeros), N, K, int(group), _ptr(Y), Y.stride(0)))
+        return Y
+
+    def gemm_wqa16(self, X, packed, scales, zeros, group: int, bits: int, K: int | None = None, Y=None):
+        """Y = X What^T (fp32 [M, N]) from bf16 X [M, K] and codes of `bits` bits (2, 3, 4 or 8) packed
+        [N, K bits/32]."""
+        torch = self.torch
+        X = self._xbits(X)
+        self._dev(packed, torch.int32, "packed")
+        self._dev(scales, torch.float32, "scales")
+        self._dev(zeros, torch.uint8, "zeros")
+        M = X.shape[0]
+        K = int(K if K is not None else X.shape[1])
+        N = packed.shape[0]
+        if K % 32 == 0 and packed.shape[1] != K * int(bits) // 32:
+            raise ValueError("packed must hold K*bits/32 words per row")
+        if Y is None:
+            Y = torch.empty((M, N), dtype=torch.float32, device=self.device)
+        self._dev(Y, torch.float32, "Y")
+        self._check(self.lib.gptq_gemm_wqa16(self.handle, _ptr(X), M, X.stride(0), _ptr(packed), _ptr(scales),
+                                             _ptr(zeros), N, K, int(group), int(bits), _ptr(Y), Y.stride(0)))
         return Y
 
     def quantize_batched(self, layers):

@@ -1269,12 +1269,14 @@ GPTQ_API int gptq_quantize_lowrank(gptq_ctx c, const float* L, const float* R, i
   return GPTQ_OK;
 }
 
-GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
-                             const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group,
-                             float* Y, int64_t ldy) {
+static int gemm_wq(gptq_ctx c, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
+                   const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group, int32_t bits,
+                   float* Y, int64_t ldy) {
   if (!c) return GPTQ_ERR_INVALID_ARG;
   c->err.clear();
   if (M < 0 || N < 0 || K < 0 || group < 0) return set_err(c, GPTQ_ERR_INVALID_ARG, "negative size");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "the product takes codes of 2, 3, 4 or 8 bits");
   if (M > INT32_MAX - 512) return set_err(c, GPTQ_ERR_UNSUPPORTED, "M too large");
   if (M == 0 || N == 0) return GPTQ_OK;
   if (!Y || (K > 0 && (!X || !packed || !scales || !zeros))) return set_err(c, GPTQ_ERR_INVALID_ARG, "null buffer");
@@ -1285,13 +1287,13 @@ GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t l
     return GPTQ_OK;
   }
   if (K % 32 != 0 || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0 || ((uintptr_t)packed & 15) != 0)
-    return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs K %% 32 == 0 and 16-byte aligned rows of X and codes");
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "the product needs K %% 32 == 0 and 16-byte aligned rows of X and codes");
   if ((long long)cdiv64(M, 256) * cdiv64(N, 128) > INT32_MAX)
-    return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 product too large for one launch");
+    return set_err(c, GPTQ_ERR_UNSUPPORTED, "product too large for one launch");
   int gshift = 31;
   if (group != 0 && group != K) {
     if (group < 8 || (group & (group - 1)) != 0 || K % group != 0)
-      return set_err(c, GPTQ_ERR_UNSUPPORTED, "W4A16 needs group 0 or a power of two >= 8 dividing K");
+      return set_err(c, GPTQ_ERR_UNSUPPORTED, "the product needs group 0 or a power of two >= 8 dividing K");
     gshift = __builtin_ctz((unsigned)group);
   }
   DeviceGuard g(c->device);
@@ -1309,11 +1311,23 @@ GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t l
   p.G = gshift == 31 ? 1 : K / group;
   p.gshift = gshift;
   if (M <= 128) {  // decode-sized: split K over 16 x 16 blocks, bound by reading the codes
-    LAUNCH(c, "k_gemv_w4a16", launch_gemv_w4a16(p, c->stream));
+    LAUNCH(c, bits == 4 ? "k_gemv_w4a16" : "k_gemv_wqa16", launch_gemv_w4a16(p, bits, c->stream));
     return GPTQ_OK;
   }
   // 512-row tiles (8 waves: each dequantised code tile feeds twice the
   // MFMAs) once X has more than 256 rows, else 256 x 128 (4 waves)
-  LAUNCH(c, "k_gemm_w4a16", launch_gemm_w4a16(p, M > 256 ? 1 : 0, c->stream));
+  LAUNCH(c, bits == 4 ? "k_gemm_w4a16" : "k_gemm_wqa16", launch_gemm_w4a16(p, M > 256 ? 1 : 0, bits, c->stream));
   return GPTQ_OK;
+}
+
+GPTQ_API int gptq_gemm_w4a16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
+                             const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group,
+                             float* Y, int64_t ldy) {
+  return gemm_wq(c, X, M, ldx, packed, scales, zeros, N, K, group, 4, Y, ldy);
+}
+
+GPTQ_API int gptq_gemm_wqa16(gptq_ctx c, const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* packed,
+                             const float* scales, const uint8_t* zeros, int32_t N, int32_t K, int32_t group,
+                             int32_t bits, float* Y, int64_t ldy) {
+  return gemm_wq(c, X, M, ldx, packed, scales, zeros, N, K, group, bits, Y, ldy);
 }

@@ -78,10 +78,12 @@ struct LrProb {
   int pad0;
 };
 
-// Y[M][N] = X[M][K] What^T with What = s (q - z) from packed 4-bit codes.
+// Y[M][N] = X[M][K] What^T with What = s (q - z) from packed codes (4 bits,
+// or 2, 3 and 8 in the general entry; the kernels take the width as a
+// template parameter).
 struct W4Prob {
   const uint16_t* X;  // bf16 bits, row pitch ldx
-  const uint32_t* P;  // [N][K/8] code words (code k at bits 4(k%8) of word k/8)
+  const uint32_t* P;  // [N][K bits/32] row bitstreams (code k at stream bits [k bits, (k+1) bits))
   const float* S;     // [N][G]
   const uint8_t* Z;   // [N][G]
   float* Y;           // row pitch ldy

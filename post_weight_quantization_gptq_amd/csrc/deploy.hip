@@ -141,7 +141,36 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float z) {
   return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-template <int BM, int BN>
+// The same for BITS-bit codes: code i of the eight at bits BITS i of v (the
+// chunk's stretch of the row's bitstream, shifted down to bit 0).
+template <int BITS>
+__device__ __forceinline__ u32x4 dequant8b(uint64_t v, float s, float z) {
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x2 t;
+    t.x = __fmul_rn((float)((uint32_t)(v >> (BITS * (2 * j))) & mask) - z, s);
+    t.y = __fmul_rn((float)((uint32_t)(v >> (BITS * (2 * j + 1))) & mask) - z, s);
+    o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(t, bf16x2));
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// Chunk cu (codes 8 cu .. 8 cu + 7) of a 32-code step of a BITS-bit row
+// stream starts at bit 8 BITS cu of the step's BITS words: word (BITS cu) / 4,
+// bit 8 ((BITS cu) % 4).  It reaches into the next word only when it does not
+// fit in the rest of its own, and that word is then still one of the step's.
+template <int BITS>
+__device__ __forceinline__ uint64_t chunk_bits(const __attribute__((address_space(1))) uint32_t* step_words, int cu) {
+  const int wi = (BITS * cu) >> 2, sh = 8 * ((BITS * cu) & 3);
+  const bool two = sh + 8 * BITS > 32;
+  const uint32_t lo = step_words[wi];
+  const uint32_t hi = step_words[two ? wi + 1 : wi];
+  return (((uint64_t)hi << 32) | lo) >> sh;
+}
+
+template <int BM, int BN, int BITS>
 __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4Prob p) {
   constexpr int WN = BN / 64;               // waves across the codes (each 128 x 64)
   constexpr int NW = (BM / 128) * WN;       // waves
@@ -185,10 +214,12 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
   const int nl = tid / TPR, c0 = WPT * (tid % TPR);
   const int nrow = min(n0 + nl, p.N - 1);
   gu32* gb = (gu32*)(p.P + (size_t)nrow * (p.K >> 3) + c0);
+  gu32* grow = (gu32*)(p.P + (size_t)nrow * ((p.K >> 5) * BITS));  // BITS != 4: the row's stream
   gfloat* gs = (gfloat*)(p.S + (size_t)nrow * p.G);
   gu8* gz = (gu8*)(p.Z + (size_t)nrow * p.G);
   const int bsw = (nl >> 2) & 3;
-  uint32_t bw[WPT];
+  uint32_t bw[WPT];  // BITS == 4: one word per chunk
+  uint64_t bv[WPT];  // other BITS: the chunk's bits
   float bsc[WPT], bzp[WPT];
   // s, z are reloaded only where a group starts (every step for groups
   // shorter than a step); they stay in registers in between
@@ -197,7 +228,10 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
     const bool fresh = p.gshift < 5 || ((unsigned)(step * W4_KS) & gmask) == 0;  // uniform
 #pragma unroll
     for (int u = 0; u < WPT; ++u) {
-      bw[u] = gb[4 * step + u];
+      if constexpr (BITS == 4)
+        bw[u] = gb[4 * step + u];
+      else
+        bv[u] = chunk_bits<BITS>(grow + (size_t)BITS * step, c0 + u);
       if (fresh) {
         const int g = (step * W4_KS + 8 * (c0 + u)) >> p.gshift;
         bsc[u] = gs[g];
@@ -208,7 +242,8 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
   auto store_b = [&](int stage) {
 #pragma unroll
     for (int u = 0; u < WPT; ++u)
-      *(u32x4*)(Bs + stage * BST + nl * 64 + (((c0 + u) ^ bsw) << 4)) = dequant8(bw[u], bsc[u], bzp[u]);
+      *(u32x4*)(Bs + stage * BST + nl * 64 + (((c0 + u) ^ bsw) << 4)) =
+          BITS == 4 ? dequant8(bw[u], bsc[u], bzp[u]) : dequant8b<BITS>(bv[u], bsc[u], bzp[u]);
   };
 
   // fragments: wave w owns rows 128 (w / WN) and columns 64 (w % WN) of the
@@ -310,13 +345,14 @@ __global__ __launch_bounds__(BM * BN / 8192 * 64, 1) void k_gemm_w4a16(const W4P
 // (bf16 weights, exact products, fp32 sums); only the order of the sums
 // differs.
 #define W4V_NW 8
+template <int BITS>
 __global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
   __shared__ f32x4 red[W4V_NW][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;  // code rows; rows of X
   const int j = lane & 15, c = lane >> 4;
   const int nrow = min(n0 + j, p.N - 1);
-  const uint32_t* crow = p.P + (size_t)nrow * (p.K >> 3);
+  const uint32_t* crow = p.P + (size_t)nrow * (BITS == 4 ? (p.K >> 3) : (p.K >> 5) * BITS);
   gfloat* gs = (gfloat*)(p.S + (size_t)nrow * p.G);
   gu8* gz = (gu8*)(p.Z + (size_t)nrow * p.G);
   const uint16_t* xrow = p.X + (size_t)min(m0 + j, p.M - 1) * p.ldx;
@@ -339,7 +375,26 @@ __global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
   float sc = 0.f, zp = 0.f;
   for (int t = t0; t < t1; ++t) {
     const int kb = 128 * t + 32 * c;
-    const u32x4 wq = *(const gu32x4*)(crow + (kb >> 3));
+    // the 32 codes of k = kb .. kb + 31: BITS words; chunk u = the 8 at kb + 8 u
+    u32x4 wq = {0u, 0u, 0u, 0u};
+    uint64_t cv[4] = {0, 0, 0, 0};
+    if constexpr (BITS == 4) {
+      wq = *(const gu32x4*)(crow + (kb >> 3));
+    } else {
+      gu32* sw = (gu32*)(crow + (size_t)BITS * (kb >> 5));
+      uint32_t wv[BITS];
+#pragma unroll
+      for (int e = 0; e < BITS; ++e) wv[e] = sw[e];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int wi = (BITS * u) >> 2, sh = 8 * ((BITS * u) & 3);
+        const uint32_t hi = (sh + 8 * BITS > 32) ? wv[wi + 1 < BITS ? wi + 1 : wi] : wv[wi];
+        cv[u] = (((uint64_t)hi << 32) | wv[wi]) >> sh;
+      }
+    }
+    auto deq = [&](int u, float s_, float z_) {
+      return BITS == 4 ? dequant8(wq[u], s_, z_) : dequant8b<BITS>(cv[u], s_, z_);
+    };
     u32x4 xa[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) xa[u] = *(const u32x4*)(xrow + kb + 8 * u);
@@ -350,12 +405,12 @@ __global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
         zp = (float)gz[g];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) mma(xa[u], dequant8(wq[u], sc, zp));
+      for (int u = 0; u < 4; ++u) mma(xa[u], deq(u, sc, zp));
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int g = (kb + 8 * u) >> p.gshift;
-        mma(xa[u], dequant8(wq[u], gs[g], (float)gz[g]));
+        mma(xa[u], deq(u, gs[g], (float)gz[g]));
       }
     }
   }
@@ -365,7 +420,10 @@ __global__ __launch_bounds__(64 * W4V_NW) void k_gemv_w4a16(const W4Prob p) {
   if (s_tail < (p.K >> 5)) {  // uniform
     const int k = 32 * s_tail + 8 * c;
     const int g = k >> p.gshift;
-    mma(*(const u32x4*)(xrow + k), dequant8(((const gu32*)crow)[k >> 3], gs[g], (float)gz[g]));
+    const u32x4 wt = BITS == 4 ? dequant8(((const gu32*)crow)[k >> 3], gs[g], (float)gz[g])
+                               : dequant8b<BITS>(chunk_bits<BITS>((gu32*)crow + (size_t)BITS * s_tail, c), gs[g],
+                                                 (float)gz[g]);
+    mma(*(const u32x4*)(xrow + k), wt);
   }
   red[w][lane] = acc;
   __syncthreads();
@@ -407,23 +465,41 @@ hipError_t launch_lr_quant(const LrProb& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_w4a16(W4Prob p, hipStream_t st) {
+template <int BITS>
+static void gemv_bits(const W4Prob& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_gemv_w4a16<BITS>, dim3(p.tiles_n, p.tiles_m), dim3(64 * W4V_NW), 0, st, p);
+}
+
+hipError_t launch_gemv_w4a16(W4Prob p, int bits, hipStream_t st) {
   p.tiles_m = (p.M + 15) / 16;
   p.tiles_n = (p.N + 15) / 16;
-  hipLaunchKernelGGL(k_gemv_w4a16, dim3(p.tiles_n, p.tiles_m), dim3(64 * W4V_NW), 0, st, p);
+  switch (bits) {
+    case 2: gemv_bits<2>(p, st); break;
+    case 3: gemv_bits<3>(p, st); break;
+    case 8: gemv_bits<8>(p, st); break;
+    default: gemv_bits<4>(p, st); break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_w4a16(W4Prob p, int shape, hipStream_t st) {
-  const int bm = shape == 1 ? 512 : 256, bn = shape == 2 ? 256 : 128;
-  p.tiles_m = (p.M + bm - 1) / bm;
-  p.tiles_n = (p.N + bn - 1) / bn;
+template <int BITS>
+static void gemm_bits(const W4Prob& p, int shape, hipStream_t st) {
   const dim3 grid(p.tiles_m * p.tiles_n);
   if (shape == 1)
-    hipLaunchKernelGGL((k_gemm_w4a16<512, 128>), grid, dim3(512), 0, st, p);
-  else if (shape == 2)
-    hipLaunchKernelGGL((k_gemm_w4a16<256, 256>), grid, dim3(512), 0, st, p);
+    hipLaunchKernelGGL((k_gemm_w4a16<512, 128, BITS>), grid, dim3(512), 0, st, p);
   else
-    hipLaunchKernelGGL((k_gemm_w4a16<256, 128>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_gemm_w4a16<256, 128, BITS>), grid, dim3(256), 0, st, p);
+}
+
+hipError_t launch_gemm_w4a16(W4Prob p, int shape, int bits, hipStream_t st) {
+  const int bm = shape == 1 ? 512 : 256, bn = 128;
+  p.tiles_m = (p.M + bm - 1) / bm;
+  p.tiles_n = (p.N + bn - 1) / bn;
+  switch (bits) {
+    case 2: gemm_bits<2>(p, shape, st); break;
+    case 3: gemm_bits<3>(p, shape, st); break;
+    case 8: gemm_bits<8>(p, shape, st); break;
+    default: gemm_bits<4>(p, shape, st); break;
+  }
   return hipGetLastError();
 }

@@ -53,8 +53,8 @@ hipError_t launch_qr_out(const double* a, float* b, long long cnt, hipStream_t s
 hipError_t launch_pack(const uint8_t* codes, int rows, int n, int bits, uint32_t* out, hipStream_t st);
 hipError_t launch_unpack(const uint32_t* packed, int rows, int n, int bits, uint8_t* codes, hipStream_t st);
 hipError_t launch_lr_quant(const LrProb& p, hipStream_t st);
-// sets the tile counts itself; K % 32 == 0
-// tile shape 0: 256 x 128 (4 waves), 1: 512 x 128 (8 waves), 2: 256 x 256 (8 waves)
-hipError_t launch_gemm_w4a16(W4Prob p, int shape, hipStream_t st);
+// sets the tile counts itself; K % 32 == 0; codes of 2, 3, 4 or 8 bits
+// tile shape 0: 256 x 128 (4 waves), 1: 512 x 128 (8 waves)
+hipError_t launch_gemm_w4a16(W4Prob p, int shape, int bits, hipStream_t st);
 // few rows of X (up to 128): split-K product on 16 x 16 MFMA blocks
-hipError_t launch_gemv_w4a16(W4Prob p, hipStream_t st);
+hipError_t launch_gemv_w4a16(W4Prob p, int bits, hipStream_t st);

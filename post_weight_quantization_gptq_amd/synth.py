@@ -29,7 +29,8 @@ columns sign-fixed by sign(diag R)):
             0..15, per-(row, group of 128) scales U(0.005, 0.01) and zero
             points uniform on 0..15, the ranges a min-max grid gives on
             N(0, 0.02^2) weights) applied to 8192 tokens of the square layer's
-            input recipe
+            input recipe; the same stand-in at 2, 3 and 8 bits (codes and
+            zero points uniform on 0..2^bits - 1) for the other widths
 where Z has i.i.d. N(0, 1) entries and i = 1..n indexes the input channels.
 """
 from __future__ import annotations
@@ -215,6 +216,18 @@ def w4_stored(N: int, K: int, group: int, seed: int):
     codes = torch.randint(0, 16, (N, K), generator=g, dtype=torch.int64).to(torch.uint8)
     scales = (0.005 + 0.005 * torch.rand((N, G), generator=g, dtype=torch.float64)).to(torch.float32)
     zeros = torch.randint(0, 16, (N, G), generator=g, dtype=torch.int64).to(torch.uint8)
+    return codes, scales, zeros
+
+
+def wq_stored(N: int, K: int, group: int, bits: int, seed: int):
+    """The same stand-in for a layer stored at `bits` bits: codes and zero
+    points uniform on 0..2^bits - 1, scales U(0.005, 0.01)."""
+    g = torch.Generator().manual_seed(71_000 + 97 * bits + seed)
+    G = K // group if group else 1
+    top = 1 << bits
+    codes = torch.randint(0, top, (N, K), generator=g, dtype=torch.int64).to(torch.uint8)
+    scales = (0.005 + 0.005 * torch.rand((N, G), generator=g, dtype=torch.float64)).to(torch.float32)
+    zeros = torch.randint(0, top, (N, G), generator=g, dtype=torch.int64).to(torch.uint8)
     return codes, scales, zeros
 
 

@@ -176,6 +176,61 @@ def test_gemm_w4a16_of_a_gptq_layer(ctx):
     _check_gemm(np32(Y), synth.bits_to_numpy(lay["X"][:1000]), codes, scales, zeros, 128)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 8])
+@pytest.mark.parametrize("M,N,K,group", [(1, 1, 32, 0), (100, 70, 96, 32), (300, 200, 256, 128), (513, 384, 1024, 64),
+                                         (600, 130, 64, 8), (129, 64, 128, 0), (200, 129, 160, 16),
+                                         # up to 128 rows: the split-K few-row kernel, K % 128 tails included
+                                         (5, 129, 256, 8), (16, 100, 64, 0), (17, 64, 128, 64), (4, 48, 416, 32),
+                                         (128, 96, 352, 16), (16, 1024, 4096, 128)])
+def test_gemm_wqa16_matches_oracle(ctx, M, N, K, group, bits):
+    # codes of 2, 3 and 8 bits: every 8-code chunk position of a 32-code step
+    # (the 3-bit chunks straddle words), groups from 8 codes to the whole row
+    print("gemm_wq", M, N, K, group, bits, flush=True)
+    X = synth.w4a16_inputs(M, K, M + N + K + bits)
+    codes, scales, zeros = (t.numpy() for t in synth.wq_stored(N, K, group, bits, M + N + K))
+    P = torch.from_numpy(o.pack_codes(codes, bits).view(np.int32)).cuda()
+    assert P.shape[1] == K * bits // 32
+    Y = ctx.gemm_wqa16(X.cuda(), P, torch.from_numpy(scales).cuda(), torch.from_numpy(zeros).cuda(), group, bits)
+    _check_gemm(np32(Y), synth.bits_to_numpy(X), codes, scales, zeros, group)
+
+
+@pytest.mark.parametrize("M", [16, 600])
+def test_gemm_wqa16_at_4_bits_is_the_w4a16_product(ctx, M):
+    # the general entry at 4 bits runs the W4A16 kernels: the same bits
+    X, codes, scales, zeros = _gemm_case(M, 200, 512, 128, 11)
+    P = torch.from_numpy(o.pack_codes(codes, 4).view(np.int32)).cuda()
+    S, Z, Xd = torch.from_numpy(scales).cuda(), torch.from_numpy(zeros).cuda(), X.cuda()
+    assert torch.equal(ctx.gemm_wqa16(Xd, P, S, Z, 128, 4), ctx.gemm_w4a16(Xd, P, S, Z, 128))
+
+
+@pytest.mark.parametrize("bits,group", [(3, 128), (2, 64)])
+def test_gemm_wqa16_of_a_gptq_layer(ctx, bits, group):
+    # the widths of the MLP (3-bit g128) and ViT (2-bit g64) layers, end to
+    # end on the GPU: the sweep's codes packed by the library, then the product
+    spec = synth.LayerSpec("wq_e2e", 160, 512, 4096, bits, group, 128, 0.01, decay=1.0, outlier_channels=0,
+                           seed=92 + bits)
+    lay = synth.layer(spec)
+    X = lay["X"].cuda()
+    H = ctx.hessian(X)
+    U, _, lam = ctx.factor(H, lam_rel=spec.lam_rel)
+    q = ctx.quantize(lay["W"].cuda(), U, bits, group, 128, lam)
+    P = ctx.pack_codes(q["codes"], bits)
+    for M in (40, 1000):  # the few-row and the tiled kernel
+        Y = ctx.gemm_wqa16(X[:M], P, q["scales"], q["zeros"], group, bits)
+        codes, scales, zeros = np32(q["codes"]), np32(q["scales"]), np32(q["zeros"])
+        _check_gemm(np32(Y), synth.bits_to_numpy(lay["X"][:M]), codes, scales, zeros, group)
+
+
+def test_gemm_wqa16_rejects_other_widths(ctx):
+    X = torch.zeros((8, 64), dtype=torch.int16, device="cuda")
+    S = torch.ones((4, 1), device="cuda")
+    Z = torch.zeros((4, 1), dtype=torch.uint8, device="cuda")
+    for bits in (1, 5, 6, 7, 9):
+        P = torch.zeros((4, 64 * bits // 32), dtype=torch.int32, device="cuda")
+        with pytest.raises(GPTQError):
+            ctx.gemm_wqa16(X, P, S, Z, 0, bits)
+
+
 @pytest.mark.parametrize("M", [16, 100, 600])
 def test_gemm_w4a16_is_bitwise_repeatable(ctx, M):
     # fixed summation orders in both kernels (no atomics): repeated calls
