@@ -339,7 +339,9 @@ def bench_w4a16(args, torch, Context, synth, dev):
     a [4096, 4096] 4-bit g128 layer (seeded codes, scales, zero points), packed
     by the library before timing.  A step is one gptq_gemm_w4a16 call.  The
     w4a16_decode workload applies the same layer to 16 tokens (the few-row
-    kernel), reported in microseconds against the HBM roof."""
+    kernel), reported in microseconds against the HBM roof.  With --bits 2, 3
+    or 8 the layer is stored at that width and the step is one
+    gptq_gemm_wqa16 call (kernels k_gemm_wqa16 / k_gemv_wqa16)."""
     cfg = synth.W4A16
     M, N, K, group = cfg["M"], cfg["N"], cfg["K"], cfg["group"]
     decode = args.workload == "w4a16_decode"
@@ -347,58 +349,71 @@ def bench_w4a16(args, torch, Context, synth, dev):
         M = synth.W4A16_DECODE_M
     print("# generating w4a16 inputs", file=sys.stderr, flush=True)
     X = synth.w4a16_inputs(M, K, 92, dev)
-    codes, scales, zeros = synth.w4_stored(N, K, group, 92)
+    bits = args.bits
+    if bits == 4:
+        codes, scales, zeros = synth.w4_stored(N, K, group, 92)
+    else:
+        codes, scales, zeros = synth.wq_stored(N, K, group, bits, 92)
     ctx = Context(dev)
-    P = ctx.pack_codes(codes.to(dev), 4)
+    P = ctx.pack_codes(codes.to(dev), bits)
     S, Z = scales.to(dev), zeros.to(dev)
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def one_step():
-        ctx.gemm_w4a16(X, P, S, Z, group, Y=Y)
+        if bits == 4:
+            ctx.gemm_w4a16(X, P, S, Z, group, Y=Y)
+        else:
+            ctx.gemm_wqa16(X, P, S, Z, group, bits, Y=Y)
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    ctx.timing("k_gemv_w4a16" if decode else "k_gemm_w4a16")
+    wq = "w4a16" if bits == 4 else "wqa16"
+    kname = ("k_gemv_" if decode else "k_gemm_") + wq
+    ctx.timing(kname)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         one_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kname = "k_gemv_w4a16" if decode else "k_gemm_w4a16"
     k_ms, k_n = ctx.kernel_time(kname)
     ctx.timing(None)
     ms_step = 1e3 * wall / args.steps
     flops = 2.0 * M * N * K
     avg = k_ms / max(k_n, 1)
     ach = flops / (avg * 1e-3) / 1e12
-    alg_bytes = M * K * 2 + N * K // 2 + N * (K // group) * 5 + M * N * 4
+    alg_bytes = M * K * 2 + N * K * bits // 8 + N * (K // group) * 5 + M * N * 4
+    wname = "W%dA16" % bits
+    label = "w4a16" if bits == 4 else "w%da16" % bits  # traffic records: profiles/<kernel>_<label>[_decode]_traffic.json
     if decode:
         gbs = alg_bytes / (avg * 1e-3) / 1e9
-        line = {"metric": "us per W4A16 product at decode size, X [%d, 4096] bf16, 4-bit g128 [4096, 4096]" % M,
+        line = {"metric": "us per %s product at decode size, X [%d, 4096] bf16, %d-bit g128 [4096, 4096]"
+                          % (wname, M, bits),
                 "value": round(ms_step * 1e3, 2), "unit": "us/product", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": False, "scaling": "weak",
                 "vs_baseline": None, "dtype": "bf16",
-                "data": "synthetic (seeded; X from the square layer's input recipe, uniform 4-bit codes)",
-                "config": {"workload": "w4a16_decode: X[%d,4096] bf16 x W[4096,4096] 4-bit g128 -> Y fp32" % M},
+                "data": "synthetic (seeded; X from the square layer's input recipe, uniform %d-bit codes)" % bits,
+                "config": {"workload": "w4a16_decode: X[%d,4096] bf16 x W[4096,4096] %d-bit g128 -> Y fp32"
+                                       % (M, bits)},
                 "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                             "traffic": kernel_traffic(kname, "w4a16_decode", "deploy.hip"),
+                             "traffic": kernel_traffic(kname, label + "_decode", "deploy.hip"),
                              "avg_launch_ms": round(avg, 5), "bytes_per_launch": alg_bytes}}
         ctx.close()
         print(json.dumps(line), flush=True)
         return
-    line = {"metric": "TFLOP/s of the W4A16 product Y = X What^T, X [8192, 4096] bf16, 4-bit g128 [4096, 4096]",
+    line = {"metric": "TFLOP/s of the %s product Y = X What^T, X [8192, 4096] bf16, %d-bit g128 [4096, 4096]"
+                      % (wname, bits),
             "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic (seeded; X from the square layer's input recipe, uniform 4-bit codes)",
-            "config": {"workload": "w4a16: X[8192,4096] bf16 x W[4096,4096] 4-bit g128 -> Y fp32"},
-            "roofline": {"kernel": "k_gemm_w4a16", "bound": "mfma", "achieved": round(ach, 2),
+            "data": "synthetic (seeded; X from the square layer's input recipe, uniform %d-bit codes)" % bits,
+            "config": {"workload": "w4a16: X[8192,4096] bf16 x W[4096,4096] %d-bit g128 -> Y fp32" % bits},
+            "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(ach, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                         "traffic": kernel_traffic("k_gemm_w4a16", "w4a16", "deploy.hip"),
+                         "traffic": kernel_traffic(kname, label, "deploy.hip"),
                          "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
                          "algorithmic_bytes_per_launch": alg_bytes}}
     if not args.no_cpu_baseline:
@@ -431,6 +446,8 @@ def main():
                     choices=["square", "single", "lora", "lora_refine", "mlp", "vit", "r2d", "qronos", "w4a16",
                              "w4a16_decode"])
     ap.add_argument("--rounds", type=int, default=1, help="refinement rounds of the lora_refine workload")
+    ap.add_argument("--bits", type=int, default=4, choices=[2, 3, 4, 8],
+                    help="code width of the w4a16 and w4a16_decode workloads")
     ap.add_argument("--pipeline", choices=["batched", "separate"], default="batched",
                     help="square / single / mlp: one gptq_quantize_batched call per step (Hessian, factor and "
                          "sweep enqueued together, one host wait at the end), or one call per stage (the factor "
