@@ -221,6 +221,32 @@ def test_gemm_wqa16_of_a_gptq_layer(ctx, bits, group):
         _check_gemm(np32(Y), synth.bits_to_numpy(lay["X"][:M]), codes, scales, zeros, group)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 8])
+def test_gemm_wqa16_pitched_repeatable_and_empty(ctx, bits):
+    # pitched X and Y, repeated calls bitwise equal, and K = 0 writing zeros,
+    # at each width the general entry adds
+    M, N, K, group = 300, 130, 256, 64
+    X, _, _, _ = _gemm_case(M, N, K, group, 5 + bits)
+    codes, scales, zeros = (t.numpy() for t in synth.wq_stored(N, K, group, bits, 5))
+    P = torch.from_numpy(o.pack_codes(codes, bits).view(np.int32)).cuda()
+    S, Z = torch.from_numpy(scales).cuda(), torch.from_numpy(zeros).cuda()
+    Xw = torch.zeros((M, K + 24), dtype=torch.int16, device="cuda")
+    Xw[:, :K] = X.cuda()
+    Yw = torch.full((M, N + 7), 5.0, device="cuda")
+    for rows in (M, 40):  # the tiled and the few-row kernel
+        ctx.gemm_wqa16(Xw[:rows], P, S, Z, group, bits, K=K, Y=Yw[:rows])
+        assert torch.all(Yw[:rows, N:] == 5.0)  # nothing written past N
+        _check_gemm(np32(Yw[:rows, :N]), synth.bits_to_numpy(X[:rows]), codes, scales, zeros, group)
+        Y1 = Yw[:rows, :N].clone()
+        for _ in range(2):
+            assert torch.equal(ctx.gemm_wqa16(Xw[:rows, :K], P, S, Z, group, bits), Y1)
+    Y0 = torch.full((5, 3), 9.0, device="cuda")
+    ctx.gemm_wqa16(torch.zeros((5, 8), dtype=torch.int16, device="cuda"), torch.zeros((3, 0), dtype=torch.int32,
+                   device="cuda"), torch.ones((3, 1), device="cuda"), torch.zeros((3, 1), dtype=torch.uint8,
+                   device="cuda"), 0, bits, K=0, Y=Y0)
+    assert torch.count_nonzero(Y0).item() == 0
+
+
 def test_gemm_wqa16_rejects_other_widths(ctx):
     X = torch.zeros((8, 64), dtype=torch.int16, device="cuda")
     S = torch.ones((4, 1), device="cuda")
