@@ -234,13 +234,23 @@ struct SweepAll<16, CPL, BID> {
 
 // One super-block of sbk consecutive blocks for 16 rows per workgroup (4
 // rows per wave, 16 lanes per row).  The rows' columns of the super-block
-// stay in LDS for the whole launch; after each block is swept, the block's
-// errors reach the rest of the super-block at once, W[rows, b1:sb1] -=
-// E[rows, blk] U[blk, b1:sb1], on the workgroup's own fp32 MFMAs
-// (v_mfma_f32_16x16x4f32, one 16-column tile per wave at a time), with U
-// staged through LDS one B x B chunk at a time.  Columns past the
-// super-block get one product per super-block afterwards (k_trail), from
-// the errors stored in the super-block's half of the error buffer.
+// stay in LDS for the whole launch; the errors of each swept block reach the
+// rest of the super-block, W[rows, b1:sb1] -= E[rows, blk] U[blk, b1:sb1], on
+// the workgroup's own fp32 MFMAs (v_mfma_f32_16x16x4f32, 64-column tiles,
+// U read from L2 one work item ahead).  Columns past the super-block get one
+// product per super-block afterwards (k_trail), from the errors stored in the
+// super-block's half of the error buffer.
+//
+// 128-wide blocks take eight waves: four sweep, and four apply the updates.
+// Right after a block is swept, the update waves apply its errors to the next
+// block's columns only; the rest of that product (the columns past the next
+// block) runs while the next block is swept, beside the sweeping waves on the
+// same SIMDs, with the errors double-buffered by block parity.  Every column
+// still takes the blocks' products in block order, each summed in the same
+// order as by one pass per block.  A group fit reads columns past its block,
+// which that overlapped product may still be writing, so layers whose groups
+// do not nest in a block keep one pass per block.  Narrower blocks: four
+// waves, which sweep and then apply each block's product.
 //
 // BID: one Bid-Up pass instead of the GPTQ sweep (codes are read as the
 // starting point, the grid is the one given, and the per-row sums are the
@@ -259,13 +269,20 @@ struct SweepLds {
   static constexpr int EP = B + 4;
   float us[B * B];   // the diagonal block of U
   float ws[16 * WP];  // the rows' columns of the super-block
-  float es[16 * EP];  // the block's errors
+  // the errors of a block (by block parity for the 128-wide blocks, whose
+  // far update runs during the next block's sweep)
+  static constexpr int NE = B >= 128 ? 2 : 1;
+  float es[NE][16 * EP];
 };
 
 template <int CPL, bool BID>
-__global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
-                                               const Seg* __restrict__ segs, int nseg) {
+__global__ __launch_bounds__(CPL == 8 ? 512 : 256) void k_sweep(const QLayer* __restrict__ L,
+                                                                const Seg* __restrict__ segs, int nseg) {
   constexpr int B = 16 * CPL;
+  // 128-wide blocks: four more waves apply the previous block's errors to the
+  // super-block's far columns while the first four sweep the current block
+  constexpr bool SPLIT = CPL == 8;
+  constexpr int NTH = SPLIT ? 512 : 256;
   using LD = SweepLds<B>;
   __shared__ __attribute__((aligned(16))) LD lds;
   float* Us = lds.us;
@@ -275,11 +292,17 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   const int kb0 = sbi * ly.sbk, kb1 = min(kb0 + ly.sbk, ly.nblk);
   const int sb0 = kb0 * B, sb1 = min(kb1 * B, ly.n), sbw = sb1 - sb0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15, rr = w * 4 + (lane >> 4);
+  const bool chain = w < 4;             // sweeps the rows (all waves unless SPLIT)
+  const int uw = SPLIT ? (w & 3) : w;   // index among the waves that apply updates
+  const int l16 = lane & 15, rr = (w & 3) * 4 + (lane >> 4);
   const int r0 = (blockIdx.x - sg.wg0) * 16;
   const int row = r0 + rr;
-  const bool rv = row < ly.out;
+  const bool rv = chain && row < ly.out;
   const int nt = ly.nt, G = ly.group;
+  // overlap the far update with the next block's sweep only where no group
+  // fit reads past its block (a fit reads columns the overlapped update is
+  // still writing): Bid-Up, per-row grids, or groups that nest in a block
+  const bool ovl = SPLIT && (BID || G == 0 || (B % G) == 0);
 
   // the diagonal block U[b0r:b0r+bwr, c0:c0+cw] (c0 = b0r, cw = bwr) -> LDS at
   // pitch B, zero past the ragged edge; all loads of a thread in flight at once
@@ -316,7 +339,7 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
   {
     const bool vec = (nt % 4) == 0 && (sbw % 4) == 0;
     const int per_row = (sbw + 3) / 4;
-    for (int e = tid; e < 16 * per_row; e += 256) {
+    for (int e = tid; e < 16 * per_row; e += NTH) {
       const int r = e / per_row, c4 = (e % per_row) * 4;
       const int gr = r0 + r;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -332,7 +355,7 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
       *(f32x4*)&lds.ws[r * LD::WP + c4] = v;
     }
   }
-  load_u(sb0, min(B, ly.n - sb0), sb0, min(B, ly.n - sb0), B);
+  if (tid < 256) load_u(sb0, min(B, ly.n - sb0), sb0, min(B, ly.n - sb0), B);
   double obj_e = 0.0, obj_d = 0.0;
   if (rv && l16 == 0) {
     obj_e = glb(ly.objp)[(size_t)row * 2];
@@ -393,56 +416,10 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
       }
     }
   };
-  prefetch(kb0);
-  __syncthreads();
+  if (chain) prefetch(kb0);
 
-  for (int blk = kb0; blk < kb1; ++blk) {
-    const int b0 = blk * B, b1 = min(b0 + B, ly.n), bw = b1 - b0;
-    cx.bw = bw;
-    cx.b0 = b0;
-    float wo[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int lc = CPL * l16 + c;
-      st.wv[c] = lc < bw ? lds.ws[rr * LD::WP + b0 - sb0 + lc] : 0.f;
-      st.dv[c] = pdv[c];
-      wo[c] = pwo[c];
-      st.qv[c] = pqv[c];
-      st.hv[c] = 0.f;
-      st.ev[c] = 0.f;
-    }
-    st.nextg = (G == 0) ? (1 << 30) : ((b0 % G) == 0 ? 0 : G - (b0 % G));
-
-    float ucur[CPL];
-#pragma unroll
-    for (int v = 0; v < CPL; ++v) ucur[v] = Us[CPL * l16 + v];
-    SweepAll<0, CPL, BID>::run(st, cx, ucur);
-
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int lc = CPL * l16 + c;
-      lds.es[rr * LD::EP + lc] = st.ev[c];  // zero past bw (the sweep leaves ev = 0 there)
-      if (rv && lc < bw) {
-        glb(ly.codes)[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
-        glb(ly.Eb)[((size_t)((blk / ly.sbk) & 1) * ly.out + row) * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
-        if (ly.err) glb(ly.err)[(size_t)row * ly.n + b0 + lc] = st.ev[c];
-        if (BID) {
-          se += (double)st.hv[c];
-        } else {
-          const double d = (double)wo[c] - (double)st.hv[c];
-          sd += d * d;
-          se += (double)st.ev[c] * (double)st.ev[c];
-        }
-      }
-    }
-    __syncthreads();  // the errors are in LDS; the diagonal U block is free
-    const bool more = blk + 1 < kb1;
-    const int nb0 = b1, nbw = more ? min(B, ly.n - nb0) : 0;
-    const bool dma = more && u_dma && nbw == B;
-    if (more) {
-      prefetch(blk + 1);
-      if (dma) dma_u(nb0);
-    }
+  // W[rows, b1:sb1) -= E U[b0:b0+B, b1:sb1) with the errors of the block at
+  // b0 (error buffer eb), by the update waves (index uw of four)
     // The block's errors reach the rest of the super-block:
     // W[rows, b1:sb1] -= E[rows, blk] U[blk, b1:sb1] on v_mfma_f32_16x16x4f32,
     // one tile of 16 rows x 64 columns per wave at a time.  K order: lane
@@ -451,20 +428,20 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
     // MFMAs of a step take columns 4 (lane % 16) + u, u = 0..3, of the tile,
     // so a lane's U values are one 16-byte load per step.  bw == B whenever
     // columns follow the block (only the layer's last block is ragged).
-    {
+  auto apply = [&](int eb, int b0, int b1, int sb1) {
       constexpr int KQ = B / 4;
       constexpr int KH = KQ > 8 ? 8 : KQ;  // K steps per work item
       constexpr int NH = KQ / KH;          // items per 64-column tile
       const int li = lane & 15, g = lane >> 4;
       const bool uvec = (nt % 4) == 0 && (((uintptr_t)ly.U) & 15) == 0;
-      // this wave's work items: tiles c0 = b1 + 64 (w + 4 i), each in NH
+      // this wave's work items: tiles c0 = b1 + 64 (uw + 4 i), each in NH
       // K-halves; the U loads of item it+1 are in flight while item it is
       // multiplied
       const int ntile = (sb1 - b1 + 63) / 64;
-      const int myt = ntile > w ? (ntile - w + 3) / 4 : 0;
+      const int myt = ntile > uw ? (ntile - uw + 3) / 4 : 0;
       const int nitem = myt * NH;
       auto load_item = [&](int it, f32x4 (&ub)[KH]) {
-        const int c0 = b1 + 64 * (w + 4 * (it / NH)), h = it % NH;
+        const int c0 = b1 + 64 * (uw + 4 * (it / NH)), h = it % NH;
         const int col = c0 + 4 * li;
         const bool full = uvec && col + 4 <= sb1;
 #pragma unroll
@@ -490,7 +467,7 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
           f32x4 (&ubc)[KH] = half ? ubB : ubA;
           f32x4 (&ubn)[KH] = half ? ubA : ubB;
           if (cur + 1 < nitem) load_item(cur + 1, ubn);
-          const int c0 = b1 + 64 * (w + 4 * (cur / NH)), h = cur % NH;
+          const int c0 = b1 + 64 * (uw + 4 * (cur / NH)), h = cur % NH;
           const int col = c0 + 4 * li;
           if (h == 0) {
 #pragma unroll
@@ -499,7 +476,7 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
           float ea[KH];
 #pragma unroll
           for (int k4 = 0; k4 < KH / 4; ++k4) {
-            const f32x4 v = *(const f32x4*)&lds.es[li * LD::EP + KQ * g + KH * h + 4 * k4];
+            const f32x4 v = *(const f32x4*)&lds.es[eb][li * LD::EP + KQ * g + KH * h + 4 * k4];
             ea[4 * k4] = v[0];
             ea[4 * k4 + 1] = v[1];
             ea[4 * k4 + 2] = v[2];
@@ -530,8 +507,66 @@ __global__ __launch_bounds__(256) void k_sweep(const QLayer* __restrict__ L,
           }
         }
       }
+    };
+  __syncthreads();
+  for (int blk = kb0; blk < kb1; ++blk) {
+    const int b0 = blk * B, b1 = min(b0 + B, ly.n), bw = b1 - b0;
+    if (chain) {
+    cx.bw = bw;
+    cx.b0 = b0;
+    float wo[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int lc = CPL * l16 + c;
+      st.wv[c] = lc < bw ? lds.ws[rr * LD::WP + b0 - sb0 + lc] : 0.f;
+      st.dv[c] = pdv[c];
+      wo[c] = pwo[c];
+      st.qv[c] = pqv[c];
+      st.hv[c] = 0.f;
+      st.ev[c] = 0.f;
     }
-    if (more && !dma) load_u(nb0, nbw, nb0, nbw, B);
+    st.nextg = (G == 0) ? (1 << 30) : ((b0 % G) == 0 ? 0 : G - (b0 % G));
+
+    float ucur[CPL];
+#pragma unroll
+    for (int v = 0; v < CPL; ++v) ucur[v] = Us[CPL * l16 + v];
+    SweepAll<0, CPL, BID>::run(st, cx, ucur);
+
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int lc = CPL * l16 + c;
+      lds.es[(blk & 1) % LD::NE][rr * LD::EP + lc] = st.ev[c];  // zero past bw (the sweep leaves ev = 0 there)
+      if (rv && lc < bw) {
+        glb(ly.codes)[(size_t)row * ly.n + b0 + lc] = (uint8_t)st.qv[c];
+        glb(ly.Eb)[((size_t)((blk / ly.sbk) & 1) * ly.out + row) * ly.ldE + ly.eoff_blk * (blk % ly.sbk) + lc] = st.ev[c];
+        if (ly.err) glb(ly.err)[(size_t)row * ly.n + b0 + lc] = st.ev[c];
+        if (BID) {
+          se += (double)st.hv[c];
+        } else {
+          const double d = (double)wo[c] - (double)st.hv[c];
+          sd += d * d;
+          se += (double)st.ev[c] * (double)st.ev[c];
+        }
+      }
+    }
+    } else if (ovl && blk > kb0) {
+      // the previous block's errors on the columns past this block (this
+      // block's own columns took them before its sweep)
+      apply(((blk - 1) & 1) % LD::NE, b0 - B, b1, sb1);
+    }
+    __syncthreads();  // the errors are in LDS; the diagonal U block is free
+    const bool more = blk + 1 < kb1;
+    const int nb0 = b1, nbw = more ? min(B, ly.n - nb0) : 0;
+    const bool dma = more && u_dma && nbw == B;
+    if (more && chain) {
+      prefetch(blk + 1);
+      if (dma) dma_u(nb0);
+    }
+    // this block's errors: on the next block's columns only when the far ones
+    // are left to the update waves during the next sweep, else on every
+    // column past the block
+    if (!SPLIT || !chain) apply((blk & 1) % LD::NE, b0, b1, ovl ? min(b1 + B, sb1) : sb1);
+    if (more && !dma && tid < 256) load_u(nb0, nbw, nb0, nbw, B);
     __builtin_amdgcn_s_waitcnt(0);  // the next diagonal block has landed
     __syncthreads();                // the updated columns and that block are visible
   }
@@ -758,7 +793,7 @@ hipError_t launch_sweep_t(int block, const QLayer* L, const Seg* segs, int nseg,
     case 16: hipLaunchKernelGGL((k_sweep<1, BID>), dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
     case 32: hipLaunchKernelGGL((k_sweep<2, BID>), dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
     case 64: hipLaunchKernelGGL((k_sweep<4, BID>), dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
-    case 128: hipLaunchKernelGGL((k_sweep<8, BID>), dim3(nwg), dim3(256), 0, st, L, segs, nseg); break;
+    case 128: hipLaunchKernelGGL((k_sweep<8, BID>), dim3(nwg), dim3(512), 0, st, L, segs, nseg); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
